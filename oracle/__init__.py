@@ -1,0 +1,227 @@
+"""CPU oracle for the verify pass -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package.  It wraps ``oracle.c`` (plain C, double precision, no fast-math),
+which shares no code with the HIP library.  What each function computes, and which
+passage of the pages it follows, is stated in ``oracle.c``.
+
+The stage-composition check of a full decode pass (each stage's input is the
+RMS-normalised previous output, the MLP input is silu(gate) * up) is written here in
+terms of the C primitives.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FMT_Q4, FMT_Q4_MIN, FMT_MXFP4 = 0, 1, 2
+MODE_GREEDY, MODE_SAMPLE = 0, 1
+DRAFT_GIVEN, DRAFT_Q_ARGMAX, DRAFT_Q_SAMPLE, DRAFT_AGREE = 0, 1, 2, 3
+NEAR_RATIO, NEAR_CAT, NEAR_TOP_P, NEAR_MIN_P, NEAR_DRAFT_CAT = 1, 2, 4, 8, 16
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (-O2, IEEE semantics, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+                        "-ffp-contract=off", "-Wall", "-o", tmp, _SRC, "-lm", "-lpthread"],
+                       check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P, I64, I32, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.or_half.restype = D
+        L.or_half.argtypes = [ctypes.c_uint16]
+        L.or_half_array.argtypes = [P, P, I64]
+        L.or_e2m1.restype = D
+        L.or_e2m1.argtypes = [I32]
+        L.or_e8m0.restype = D
+        L.or_e8m0.argtypes = [ctypes.c_uint8]
+        L.or_dequant.argtypes = [I32, P, P, P, I64, I64, P]
+        L.or_linear.restype = I32
+        L.or_linear.argtypes = [I32, P, P, P, I64, I64, P, I32, P, P, I32]
+        L.or_rho.argtypes = [P, I32, I64, P]
+        L.or_silu_mul.argtypes = [P, P, I64, P]
+        L.or_philox4x64.argtypes = [P, P, P]
+        L.or_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, P]
+        L.or_warp.restype = I32
+        L.or_warp.argtypes = [P, I64, D, D, D, P, P]
+        L.or_argmax.restype = I64
+        L.or_argmax.argtypes = [P, I64]
+        L.or_cat.restype = I64
+        L.or_cat.argtypes = [P, I64, D, P]
+        L.or_accept.restype = I32
+        L.or_accept.argtypes = [P, I32]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def half(h: int) -> float:
+    return lib().or_half(h)
+
+
+def half_array(h: np.ndarray) -> np.ndarray:
+    h = np.ascontiguousarray(h).view(np.uint16)
+    out = np.empty(h.shape, np.float64)
+    lib().or_half_array(_p(h), _p(out), h.size)
+    return out
+
+
+def e2m1(code: int) -> float:
+    return lib().or_e2m1(code)
+
+
+def e8m0(e: int) -> float:
+    return lib().or_e8m0(e)
+
+
+def dequant(m) -> np.ndarray:
+    """Dequantised weights [rows][cols] in double for a synth.Q4Matrix."""
+    out = np.empty((m.rows, m.cols), np.float64)
+    qs = np.ascontiguousarray(m.qs)
+    sc = np.ascontiguousarray(m.scales)
+    mn = None if m.mins is None else np.ascontiguousarray(m.mins)
+    lib().or_dequant(m.fmt, _p(qs), _p(sc), _p(mn), m.rows, m.cols, _p(out))
+    return out
+
+
+def linear(m, x: np.ndarray, threads: int = 1):
+    """y[K][rows] = W x (double) and the row tolerance base A[K][rows] = sum |w x|."""
+    x = np.ascontiguousarray(x, dtype=np.float16)
+    K = x.shape[0]
+    assert x.shape[1] == m.cols
+    y = np.empty((K, m.rows), np.float64)
+    a = np.empty((K, m.rows), np.float64)
+    qs = np.ascontiguousarray(m.qs)
+    sc = np.ascontiguousarray(m.scales)
+    mn = None if m.mins is None else np.ascontiguousarray(m.mins)
+    rc = lib().or_linear(m.fmt, _p(qs), _p(sc), _p(mn), m.rows, m.cols, _p(x), K,
+                         _p(y), _p(a), threads)
+    if rc:
+        raise RuntimeError(f"or_linear failed ({rc})")
+    return y, a
+
+
+def rho(v: np.ndarray) -> np.ndarray:
+    """Per activation column (row of v [K][n]): v / sqrt(mean(v^2)), in double."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.float64)
+    lib().or_rho(_p(v), v.shape[0], v.shape[1], _p(out))
+    return out
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    out = np.empty(g.shape, np.float64)
+    lib().or_silu_mul(_p(g), _p(u), g.size, _p(out))
+    return out
+
+
+def philox4x64(counter, key) -> np.ndarray:
+    c = np.asarray(counter, dtype=np.uint64).copy()
+    k = np.asarray(key, dtype=np.uint64).copy()
+    out = np.empty(4, np.uint64)
+    lib().or_philox4x64(_p(c), _p(k), _p(out))
+    return out
+
+
+def uniforms(seed: int, window: int, position: int) -> np.ndarray:
+    out = np.empty(4, np.float64)
+    lib().or_uniforms(seed, window, position, _p(out))
+    return out
+
+
+class WarpInfo(ctypes.Structure):
+    _fields_ = [("n_keep", ctypes.c_int64), ("m_p", ctypes.c_int64), ("m_m", ctypes.c_int64),
+                ("near_top_p", ctypes.c_int), ("near_min_p", ctypes.c_int),
+                ("nonfinite", ctypes.c_int), ("argmax", ctypes.c_int64)]
+
+
+def warp(logits: np.ndarray, T: float, top_p: float = 1.0, min_p: float = 0.0):
+    """Warped distribution p[V] (double) and the WarpInfo of one logits row."""
+    l = np.ascontiguousarray(logits, dtype=np.float32)
+    p = np.empty(l.shape[0], np.float64)
+    info = WarpInfo()
+    lib().or_warp(_p(l), l.shape[0], T, top_p, min_p, _p(p), ctypes.byref(info))
+    return p, info
+
+
+def argmax(logits: np.ndarray) -> int:
+    l = np.ascontiguousarray(logits, dtype=np.float32)
+    return int(lib().or_argmax(_p(l), l.shape[0]))
+
+
+def cat(w: np.ndarray, u: float):
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    near = ctypes.c_int(0)
+    j = lib().or_cat(_p(w), w.shape[0], u, ctypes.byref(near))
+    return int(j), bool(near.value)
+
+
+class _AcceptArgs(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int), ("draft_mode", ctypes.c_int),
+                ("W", ctypes.c_int64), ("K", ctypes.c_int64), ("V", ctypes.c_int64),
+                ("target", ctypes.c_void_p), ("draft", ctypes.c_void_p),
+                ("draft_tokens", ctypes.c_void_p),
+                ("T", ctypes.c_double), ("top_p", ctypes.c_double),
+                ("min_p", ctypes.c_double), ("alpha", ctypes.c_double),
+                ("seed", ctypes.c_uint64), ("window_base", ctypes.c_uint64),
+                ("n_accepted", ctypes.c_void_p), ("tokens", ctypes.c_void_p),
+                ("status", ctypes.c_void_p), ("near", ctypes.c_void_p)]
+
+
+def accept(mode: int, target: np.ndarray, draft: np.ndarray | None = None,
+           draft_tokens: np.ndarray | None = None, draft_mode: int = DRAFT_GIVEN,
+           T: float = 1.0, top_p: float = 1.0, min_p: float = 0.0, alpha: float = 0.0,
+           seed: int = 0, window_base: int = 0, threads: int = 1) -> dict:
+    """Acceptance of W windows.  target [W][K][V] f32, draft [W][K-1][V] f32.
+
+    Returns n_accepted [W], tokens [W][K] (-1 padded), status [W], near [W] (bits of
+    decisions within 1e-6 of a threshold) and draft_tokens [W][K-1] (drafted or given).
+    """
+    target = np.ascontiguousarray(target, dtype=np.float32)
+    W, K, V = target.shape
+    if draft is not None:
+        draft = np.ascontiguousarray(draft, dtype=np.float32)
+        assert draft.shape == (W, K - 1, V)
+    if draft_tokens is None:
+        draft_tokens = np.full((W, max(K - 1, 0)), -1, np.int32)
+    else:
+        draft_tokens = np.ascontiguousarray(draft_tokens, dtype=np.int32).copy()
+    n_acc = np.zeros(W, np.int32)
+    tokens = np.full((W, K), -1, np.int32)
+    status = np.zeros(W, np.int32)
+    near = np.zeros(W, np.int32)
+    args = _AcceptArgs(mode, draft_mode, W, K, V, _p(target).value if W else None,
+                       None if draft is None else _p(draft).value,
+                       _p(draft_tokens).value if draft_tokens.size else None,
+                       T, top_p, min_p, alpha, seed, window_base,
+                       _p(n_acc).value, _p(tokens).value, _p(status).value, _p(near).value)
+    rc = lib().or_accept(ctypes.byref(args), threads)
+    if rc:
+        raise RuntimeError(f"or_accept failed ({rc})")
+    return dict(n_accepted=n_acc, tokens=tokens, status=status, near=near,
+                draft_tokens=draft_tokens)
+

@@ -1,0 +1,216 @@
+"""Seeded synthetic inputs for the speculative-decoding verify pass.
+
+Both the HIP path and the CPU oracle consume the bytes this module produces.  It holds
+only random draws and their packing into the byte layouts the library reads; none of
+the method's arithmetic (no dequantisation, no dot products, no softmax, no sampling)
+lives here.
+
+Every array is a pure function of (seed, what it is, where it is), drawn from numpy's
+``default_rng`` seeded by a ``SeedSequence`` built from those integers, so any matrix,
+any 256-row chunk of a matrix and any acceptance window can be regenerated on its own.
+
+Layouts (all row-major, C order):
+  * 4-bit weights ``qs``: uint8 ``[rows][cols/2]``; byte ``j//2`` of a row holds column
+    ``j`` in its low nibble when ``j`` is even and in its high nibble when ``j`` is odd.
+  * Q4 block scales / mins: float16 ``[rows][cols/32]`` (one per 32 consecutive columns).
+  * MXFP4 block scales: uint8 E8M0 ``[rows][cols/32]``.
+  * Activations: float16 ``[K][cols]`` (column k of the verify window is row k here).
+  * Logits: float32, target ``[W][K][V]`` and drafter ``[W][K-1][V]``.
+"""
+from __future__ import annotations
+
+import dataclasses
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+FMT_Q4 = 0          # 4-bit code + fp16 block scale
+FMT_Q4_MIN = 1      # 4-bit code + fp16 block scale + fp16 block min
+FMT_MXFP4 = 2       # E2M1 code + E8M0 block scale
+
+BLOCK = 32
+ROW_CHUNK = 256     # rows per independently seeded chunk of a weight matrix
+
+_TAG_WEIGHT = 1
+_TAG_ACT = 2
+_TAG_LOGITS = 3
+
+# Matrix ids inside one decoder layer, in stage order.
+MAT_Q, MAT_K, MAT_V, MAT_O, MAT_GATE, MAT_UP, MAT_DOWN, MAT_LM_HEAD = range(8)
+LAYER_MATS = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def _rng(*keys: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(k) for k in keys]))
+
+
+@dataclasses.dataclass(frozen=True)
+class ModelShape:
+    """Shapes of a dense decoder's weight stack (no attention/norm weights)."""
+    n_layers: int
+    hidden: int
+    kv_dim: int
+    ffn: int
+    vocab: int
+
+    def mat_shape(self, mat: int) -> tuple[int, int]:
+        h, kv, ff = self.hidden, self.kv_dim, self.ffn
+        return {MAT_Q: (h, h), MAT_K: (kv, h), MAT_V: (kv, h), MAT_O: (h, h),
+                MAT_GATE: (ff, h), MAT_UP: (ff, h), MAT_DOWN: (h, ff),
+                MAT_LM_HEAD: (self.vocab, h)}[mat]
+
+    def n_weights(self) -> int:
+        per_layer = sum(r * c for r, c in (self.mat_shape(m) for m in range(7)))
+        r, c = self.mat_shape(MAT_LM_HEAD)
+        return self.n_layers * per_layer + r * c
+
+
+# The 27B-class stack: 64 layers of hidden 5120, kv 1024, ffn 17408, vocab 151936.
+SHAPE_27B = ModelShape(n_layers=64, hidden=5120, kv_dim=1024, ffn=17408, vocab=151936)
+# A small stack with the same structure, for full (every row, every stage) parity.
+SHAPE_MINI = ModelShape(n_layers=2, hidden=256, kv_dim=64, ffn=512, vocab=1000)
+
+
+def bytes_per_weight(fmt: int) -> float:
+    return {FMT_Q4: 0.5 + 2 / 32, FMT_Q4_MIN: 0.5 + 4 / 32, FMT_MXFP4: 0.5 + 1 / 32}[fmt]
+
+
+@dataclasses.dataclass
+class Q4Matrix:
+    fmt: int
+    rows: int
+    cols: int
+    qs: np.ndarray                 # uint8 [rows][cols/2]
+    scales: np.ndarray             # float16 (Q4) or uint8 E8M0 (MXFP4) [rows][cols/32]
+    mins: np.ndarray | None        # float16 [rows][cols/32] or None
+
+    @property
+    def nbytes(self) -> int:
+        n = self.qs.nbytes + self.scales.nbytes
+        return n + (self.mins.nbytes if self.mins is not None else 0)
+
+
+def _chunk_arrays(fmt: int, seed: int, layer: int, mat: int, chunk: int,
+                  nrows: int, cols: int, scale_lo: float, scale_hi: float):
+    rng = _rng(seed, _TAG_WEIGHT, layer, mat, chunk)
+    nb = cols // BLOCK
+    qs = rng.integers(0, 256, size=(nrows, cols // 2), dtype=np.uint8)
+    if fmt == FMT_MXFP4:
+        scales = rng.integers(119, 124, size=(nrows, nb), dtype=np.uint8)
+        mins = None
+    else:
+        scales = rng.uniform(scale_lo, scale_hi, size=(nrows, nb)).astype(np.float16)
+        mins = (rng.uniform(-0.01, 0.01, size=(nrows, nb)).astype(np.float16)
+                if fmt == FMT_Q4_MIN else None)
+    return qs, scales, mins
+
+
+def weight_matrix(fmt: int, seed: int, layer: int, mat: int, rows: int, cols: int,
+                  row_begin: int = 0, row_end: int | None = None,
+                  scale_lo: float = 0.005, scale_hi: float = 0.02,
+                  threads: int = 1) -> Q4Matrix:
+    """Rows [row_begin, row_end) of weight matrix (layer, mat), in chunks of ROW_CHUNK rows.
+
+    Q4 / Q4_MIN: nibble bytes uniform over 0..255 (both nibbles uniform on 16 codes),
+    fp16 scales ~U(scale_lo, scale_hi), fp16 mins ~U(-0.01, 0.01).
+    MXFP4: nibble bytes uniform (E2M1 codes uniform on 16 codes), E8M0 bytes uniform on
+    {119..123}, i.e. block scales 2^-8 .. 2^-4.
+    """
+    if cols % BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    row_end = rows if row_end is None else row_end
+    c0, c1 = row_begin // ROW_CHUNK, (row_end + ROW_CHUNK - 1) // ROW_CHUNK
+    nb = cols // BLOCK
+    n = row_end - row_begin
+    qs = np.empty((n, cols // 2), np.uint8)
+    scales = np.empty((n, nb), np.uint8 if fmt == FMT_MXFP4 else np.float16)
+    mins = np.empty((n, nb), np.float16) if fmt == FMT_Q4_MIN else None
+
+    def work(ci: int):
+        r0 = ci * ROW_CHUNK
+        nr = min(ROW_CHUNK, rows - r0)
+        q, s, m = _chunk_arrays(fmt, seed, layer, mat, ci, nr, cols, scale_lo, scale_hi)
+        a, b = max(r0, row_begin), min(r0 + nr, row_end)
+        qs[a - row_begin:b - row_begin] = q[a - r0:b - r0]
+        scales[a - row_begin:b - row_begin] = s[a - r0:b - r0]
+        if mins is not None:
+            mins[a - row_begin:b - row_begin] = m[a - r0:b - r0]
+
+    if threads > 1 and c1 - c0 > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, range(c0, c1)))
+    else:
+        for ci in range(c0, c1):
+            work(ci)
+    return Q4Matrix(fmt, n, cols, qs, scales, mins)
+
+
+def weight_rows(fmt: int, seed: int, layer: int, mat: int, rows: int, cols: int,
+                row_ids) -> Q4Matrix:
+    """Only the listed rows of a matrix (regenerating just their chunks)."""
+    row_ids = np.asarray(row_ids, dtype=np.int64)
+    parts = [weight_matrix(fmt, seed, layer, mat, rows, cols, int(r), int(r) + 1) for r in row_ids]
+    return Q4Matrix(fmt, len(row_ids), cols,
+                    np.concatenate([p.qs for p in parts]),
+                    np.concatenate([p.scales for p in parts]),
+                    None if parts[0].mins is None else np.concatenate([p.mins for p in parts]))
+
+
+def activations(seed: int, K: int, cols: int, tag: int = 0) -> np.ndarray:
+    """K activation columns ~N(0,1), rounded to fp16: array [K][cols]."""
+    rng = _rng(seed, _TAG_ACT, tag, K, cols)
+    return rng.standard_normal((K, cols), dtype=np.float32).astype(np.float16)
+
+
+@dataclasses.dataclass(frozen=True)
+class LogitSpec:
+    seed: int
+    K: int
+    vocab: int
+    target_sigma: float
+    noise_sigma: float
+
+
+def window_logits(spec: LogitSpec, window: int):
+    """Target [K][V] ~N(0, target_sigma) and drafter [K-1][V] = target rows 0..K-2 + N(0, noise_sigma).
+
+    Drafter row i (0-based) scores the same position as target row i; target row K-1 is
+    the bonus position, which no draft covers.
+    """
+    rng = _rng(spec.seed, _TAG_LOGITS, window)
+    t = rng.standard_normal((spec.K, spec.vocab), dtype=np.float32) * np.float32(spec.target_sigma)
+    n = rng.standard_normal((spec.K - 1, spec.vocab), dtype=np.float32) * np.float32(spec.noise_sigma)
+    return t, (t[: spec.K - 1] + n).astype(np.float32)
+
+
+def logits_batch(spec: LogitSpec, w0: int, w1: int, threads: int = 1):
+    """Windows [w0, w1): target [W][K][V] and drafter [W][K-1][V] float32."""
+    W = w1 - w0
+    tgt = np.empty((W, spec.K, spec.vocab), np.float32)
+    drf = np.empty((W, max(spec.K - 1, 0), spec.vocab), np.float32)
+
+    def work(i):
+        t, d = window_logits(spec, w0 + i)
+        tgt[i] = t
+        drf[i] = d
+
+    if threads > 1 and W > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, range(W)))
+    else:
+        for i in range(W):
+            work(i)
+    return tgt, drf
+
+
+# The five workloads: sizes, formats, seeds and sampler settings.
+C1 = dict(name="tiny-1024x1024-q4-K4-V256", seed=0, rows=1024, cols=1024, fmt=FMT_Q4, K=4,
+          logits=LogitSpec(seed=0, K=4, vocab=256, target_sigma=2.0, noise_sigma=0.5),
+          windows=10_000, T=1.0, top_p=1.0, min_p=0.0, philox_seed=0)
+C2 = dict(name="27b-q4min-K1-decode", seed=0, shape=SHAPE_27B, fmt=FMT_Q4_MIN, K=1)
+C3 = dict(name="27b-q4min-K4-greedy", seed=0, shape=SHAPE_27B, fmt=FMT_Q4_MIN, K=4,
+          alpha=0.7, philox_seed=0)
+C4 = dict(name="27b-q4min-K8-sample", seed=0, shape=SHAPE_27B, fmt=FMT_Q4_MIN, K=8,
+          logits=LogitSpec(seed=1, K=8, vocab=151936, target_sigma=3.0, noise_sigma=1.0),
+          windows=1000, T=0.6, top_p=0.95, min_p=0.05, philox_seed=1)
+C5 = dict(name="27b-mxfp4-K16", seed=0, shape=SHAPE_27B, fmt=FMT_MXFP4, K=16)

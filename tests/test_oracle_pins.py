@@ -1,0 +1,530 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (no GPU).
+
+Each test ties an oracle function to something outside the oracle: a value the pages
+print, a closed form, an independent library routine (numpy, scipy), an invariant, or
+a brute-force count on a tiny input.
+"""
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line)
+    return rows
+
+
+# ----------------------------------------------------------------- formats
+
+def test_half_matches_numpy_all_bit_patterns():
+    """fp16 decode vs numpy's float16 -> float64 conversion, all 65536 encodings."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = oracle.half_array(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+
+
+def test_e2m1_table_ocp_mx():
+    """The 16 E2M1 code points of the OCP Microscaling Formats spec v1.0 (FP4 table)."""
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(8):
+        assert oracle.e2m1(c) == mags[c]
+        assert oracle.e2m1(c + 8) == -mags[c]
+        assert np.signbit(oracle.e2m1(c + 8))
+
+
+def test_e8m0_scale():
+    """E8M0: 2^(E-127), E = 255 is NaN (OCP MX v1.0)."""
+    assert oracle.e8m0(127) == 1.0
+    assert oracle.e8m0(119) == 2.0 ** -8
+    assert oracle.e8m0(123) == 2.0 ** -4
+    assert oracle.e8m0(254) == 2.0 ** 127
+    assert oracle.e8m0(0) == 2.0 ** -127
+    assert np.isnan(oracle.e8m0(255))
+
+
+def _pack_q4(q):
+    """Encode signed codes q in [-8, 7] ([rows][cols]) as bytes: low nibble = even column."""
+    n = (np.asarray(q) + 8).astype(np.uint8)
+    return (n[:, 0::2] | (n[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_q4_roundtrip_from_encoding():
+    """Codes written by the inverse map (n = q + 8, even column low nibble) decode to d*q + m."""
+    rng = np.random.default_rng(3)
+    rows, cols = 5, 96
+    q = rng.integers(-8, 8, size=(rows, cols))
+    # scales and mins that are exact in fp16 (k / 1024), so d*q + m is exact in double
+    d = (rng.integers(1, 64, size=(rows, cols // 32)) / 1024.0).astype(np.float16)
+    m = (rng.integers(-16, 17, size=(rows, cols // 32)) / 1024.0).astype(np.float16)
+    for fmt, mins in ((synth.FMT_Q4, None), (synth.FMT_Q4_MIN, m)):
+        W = synth.Q4Matrix(fmt, rows, cols, _pack_q4(q), d, mins)
+        got = oracle.dequant(W)
+        dd = np.repeat(d.astype(np.float64), 32, axis=1)
+        mm = 0.0 if mins is None else np.repeat(m.astype(np.float64), 32, axis=1)
+        assert np.array_equal(got, dd * q + mm)
+
+
+def test_q4_nibble_order_single_byte():
+    """Byte 0x8F: column 0 has code 15 (q = 7), column 1 has code 8 (q = 0)."""
+    qs = np.zeros((1, 16), np.uint8)
+    qs[0, 0] = 0x8F
+    qs[0, 1:] = 0x88
+    W = synth.Q4Matrix(synth.FMT_Q4, 1, 32, qs, np.array([[1.0]], np.float16), None)
+    w = oracle.dequant(W)[0]
+    assert w[0] == 7.0 and w[1] == 0.0 and np.all(w[2:] == 0.0)
+
+
+def test_mxfp4_roundtrip():
+    """MXFP4 codes decode to e2m1(code) * 2^(E-127); low nibble = even column."""
+    rng = np.random.default_rng(4)
+    codes = rng.integers(0, 16, size=(3, 64)).astype(np.uint8)
+    qs = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    E = rng.integers(119, 124, size=(3, 2)).astype(np.uint8)
+    W = synth.Q4Matrix(synth.FMT_MXFP4, 3, 64, qs, E, None)
+    got = oracle.dequant(W)
+    mags = np.array([0, .5, 1, 1.5, 2, 3, 4, 6] * 2) * np.repeat([1.0, -1.0], 8)
+    ref = mags[codes] * np.repeat(2.0 ** (E.astype(np.float64) - 127), 32, axis=1)
+    assert np.array_equal(got, ref)
+
+
+def test_mxfp4_values_exact_in_fp16():
+    """Every C5 weight (|code| <= 6, scale 2^-8..2^-4) is exactly representable in fp16."""
+    mags = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    for e in range(119, 124):
+        v = mags * 2.0 ** (e - 127)
+        assert np.array_equal(v.astype(np.float16).astype(np.float64), v)
+
+
+# ------------------------------------------------------------------ linear
+
+def _small_matrix(fmt=synth.FMT_Q4_MIN, rows=40, cols=128, seed=7):
+    return synth.weight_matrix(fmt, seed, 0, 0, rows, cols)
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_Q4, synth.FMT_Q4_MIN, synth.FMT_MXFP4])
+def test_linear_vs_numpy_matmul(fmt):
+    """W x agrees with numpy's float64 matmul of the dequantised matrix (library routine)."""
+    W = _small_matrix(fmt)
+    x = synth.activations(1, 3, W.cols)
+    y, a = oracle.linear(W, x)
+    ref = x.astype(np.float64) @ oracle.dequant(W).T
+    assert np.all(np.abs(y - ref) <= 1e-12 * a + 1e-300)
+    assert np.all(a >= np.abs(y))
+
+
+def test_linear_unit_vectors_recover_columns():
+    """x = e_j returns column j of W exactly."""
+    W = _small_matrix(rows=17, cols=64)
+    Wd = oracle.dequant(W)
+    x = np.zeros((64, 64), np.float16)
+    x[np.arange(64), np.arange(64)] = 1.0
+    y, _ = oracle.linear(W, x)
+    assert np.array_equal(y, Wd.T)
+
+
+def test_linear_hand_cases():
+    """One block: q = 7, d = 0.5, m = 0 gives 3.5 * sum(x); q = 0 gives m * sum(x)."""
+    x = synth.activations(2, 2, 32)
+    xs = x.astype(np.float64).sum(axis=1)
+    W7 = synth.Q4Matrix(synth.FMT_Q4, 1, 32, np.full((1, 16), 0xFF, np.uint8),
+                        np.array([[0.5]], np.float16), None)
+    y, _ = oracle.linear(W7, x)
+    assert np.allclose(y[:, 0], 3.5 * xs, rtol=1e-15, atol=1e-15)
+    m = np.float16(0.0078125)
+    W0 = synth.Q4Matrix(synth.FMT_Q4_MIN, 1, 32, np.full((1, 16), 0x88, np.uint8),
+                        np.array([[0.5]], np.float16), np.array([[m]], np.float16))
+    y, _ = oracle.linear(W0, x)
+    assert np.allclose(y[:, 0], float(m) * xs, rtol=1e-15, atol=1e-15)
+
+
+def test_linear_linearity_and_zero_row():
+    """y(x1 + x2) = y(x1) + y(x2) (inputs chosen so the fp16 sum is exact); zero rows give 0."""
+    W = _small_matrix(rows=9, cols=96)
+    qs = W.qs.copy()
+    qs[4] = 0x88                                # row 4: every code q = 0
+    mins = W.mins.copy()
+    mins[4] = 0
+    W = synth.Q4Matrix(W.fmt, W.rows, W.cols, qs, W.scales, mins)
+    rng = np.random.default_rng(5)
+    x1 = (rng.integers(-64, 64, size=(2, 96)) / 64).astype(np.float16)
+    x2 = (rng.integers(-64, 64, size=(2, 96)) / 64).astype(np.float16)
+    y1, _ = oracle.linear(W, x1)
+    y2, _ = oracle.linear(W, x2)
+    y12, a12 = oracle.linear(W, (x1.astype(np.float32) + x2).astype(np.float16))
+    assert np.allclose(y12, y1 + y2, rtol=0, atol=1e-12)
+    assert np.all(y12[:, 4] == 0.0) and np.all(a12[:, 4] == 0.0)
+
+
+# -------------------------------------------------------------------- glue
+
+def test_rho_unit_rms_and_scale_invariance():
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((3, 1000)).astype(np.float32) * np.float32(7.5)
+    r = oracle.rho(v)
+    assert np.allclose(np.sqrt((r ** 2).mean(axis=1)), 1.0, rtol=1e-14)
+    r2 = oracle.rho(v * np.float32(4.0))      # power-of-two scaling is exact in fp32
+    assert np.allclose(r, r2, rtol=1e-14)
+
+
+def test_silu_mul_vs_scipy():
+    rng = np.random.default_rng(7)
+    g = rng.standard_normal(1000).astype(np.float32) * 4
+    u = rng.standard_normal(1000).astype(np.float32)
+    ref = g.astype(np.float64) * scipy.special.expit(g.astype(np.float64)) * u
+    assert np.allclose(oracle.silu_mul(g, u), ref, rtol=1e-13, atol=1e-300)
+
+
+# ------------------------------------------------------------------ Philox
+
+def test_philox_matches_numpy_philox():
+    """Philox4x64-10 vs numpy.random.Philox, an independent implementation of Salmon et al.
+
+    numpy increments the 256-bit counter before each block, so starting it at c - 1
+    yields the block for counter c.
+    """
+    rng = np.random.default_rng(8)
+    for _ in range(200):
+        key = rng.integers(0, 2 ** 63, size=2, dtype=np.uint64) * np.uint64(2) + \
+            rng.integers(0, 2, size=2, dtype=np.uint64)
+        ctr = rng.integers(1, 2 ** 63, size=4, dtype=np.uint64)
+        prev = ctr.copy()
+        prev[0] -= np.uint64(1)
+        bg = np.random.Philox(key=key, counter=prev)
+        assert np.array_equal(bg.random_raw(4).astype(np.uint64), oracle.philox4x64(ctr, key))
+    for w in (0, 1, 9999, 2 ** 40 + 3):
+        for i in (1, 2, 8, 16):
+            prev = np.array([w - 1 if w else 2 ** 64 - 1, i if w else i - 1, 0, 0], np.uint64)
+            bg = np.random.Philox(key=np.array([5, 0], np.uint64), counter=prev)
+            ref = bg.random_raw(4).astype(np.uint64)
+            assert np.array_equal(ref, oracle.philox4x64([w, i, 0, 0], [5, 0]))
+
+
+def test_uniforms_definition_and_chi_square():
+    """u = top 24 bits * 2^-24 in [0, 1); 2^16 draws pass a 64-bin chi-square at 1e-3."""
+    r = oracle.philox4x64([17, 3, 0, 0], [11, 0])
+    u = oracle.uniforms(11, 17, 3)
+    assert np.array_equal(u, (r >> np.uint64(40)).astype(np.float64) / 2.0 ** 24)
+    draws = np.concatenate([oracle.uniforms(2, w, 1) for w in range(16384)])
+    assert draws.min() >= 0.0 and draws.max() < 1.0
+    counts = np.histogram(draws, bins=64, range=(0, 1))[0]
+    assert scipy.stats.chisquare(counts).pvalue > 1e-3
+    assert len(set(map(tuple, [oracle.philox4x64([w, 1, 0, 0], [2, 0]) for w in range(64)]))) == 64
+
+
+# -------------------------------------------------------------------- warp
+
+def test_warp_no_filters_is_softmax():
+    rng = np.random.default_rng(9)
+    l = rng.standard_normal(300).astype(np.float32) * 3
+    for T in (1.0, 0.6, 2.5):
+        p, info = oracle.warp(l, T)
+        ref = scipy.special.softmax(l.astype(np.float64) / T)
+        assert np.allclose(p, ref, rtol=1e-12, atol=1e-300)
+        assert info.n_keep == 300
+
+
+def test_warp_hand_case():
+    """pi = (.5, .3, .15, .05), top_p .75, min_p .2: top-p keeps 2, min-p keeps 3 -> keep 2."""
+    pi = np.array([0.5, 0.3, 0.15, 0.05])
+    l = np.log(pi).astype(np.float32)
+    p, info = oracle.warp(l, 1.0, top_p=0.75, min_p=0.2)
+    assert info.m_p == 2 and info.m_m == 3 and info.n_keep == 2
+    assert np.allclose(p, [0.625, 0.375, 0, 0], rtol=1e-6)
+    # min-p alone at 0.35 keeps pi >= .175: 2 tokens; top-p alone at 0.9 keeps 3
+    assert oracle.warp(l, 1.0, min_p=0.35)[1].n_keep == 2
+    assert oracle.warp(l, 1.0, top_p=0.9)[1].n_keep == 3
+
+
+def test_warp_invariants_and_monotone_subsets():
+    rng = np.random.default_rng(10)
+    for _ in range(20):
+        l = rng.standard_normal(500).astype(np.float32) * 3
+        prev = None
+        for top_p, min_p in ((1.0, 0.0), (0.99, 0.0), (0.95, 0.01), (0.9, 0.05), (0.5, 0.2)):
+            p, info = oracle.warp(l, 0.6, top_p, min_p)
+            keep = p > 0
+            assert abs(p.sum() - 1) < 1e-12
+            assert keep[np.argmax(l)]
+            if prev is not None:
+                assert np.all(prev | ~keep)           # subset of the looser setting
+            prev = keep
+            # the kept set is a prefix of the (logit desc, index asc) order
+            order = np.lexsort((np.arange(500), -l.astype(np.float64)))
+            assert np.all(keep[order][:info.n_keep]) and not np.any(keep[order][info.n_keep:])
+
+
+def test_warp_zero_temperature_and_ties():
+    l = np.array([1.0, 3.0, 3.0, -2.0], np.float32)
+    p, info = oracle.warp(l, 0.0)
+    assert np.array_equal(p, [0, 1, 0, 0]) and info.argmax == 1
+    assert oracle.argmax(l) == 1
+    p, _ = oracle.warp(l, 1e-3, top_p=0.4)            # the tie breaks to the lower index
+    assert p[1] == 1.0
+
+
+def test_warp_top_p_matches_brute_force():
+    """Shortest prefix of the sorted order with mass >= top_p, by exhaustive count."""
+    rng = np.random.default_rng(11)
+    for _ in range(50):
+        l = rng.standard_normal(40).astype(np.float32) * 2
+        top_p = float(rng.uniform(0.05, 0.99))
+        p, info = oracle.warp(l, 1.0, top_p=top_p)
+        pi = scipy.special.softmax(l.astype(np.float64))
+        order = np.lexsort((np.arange(40), -pi))
+        m = next(m for m in range(1, 41) if pi[order[:m]].sum() >= top_p)
+        assert info.n_keep == m
+
+
+# --------------------------------------------------------------- categorical
+
+def test_cat_inverse_cdf_brute_force():
+    w = np.array([0.0, 0.25, 0.0, 0.5, 0.25])
+    assert oracle.cat(w, 0.0)[0] == 1
+    assert oracle.cat(w, 0.2499)[0] == 1
+    assert oracle.cat(w, 0.25)[0] == 3            # C_j > u*S is strict
+    assert oracle.cat(w, 0.7499)[0] == 3
+    assert oracle.cat(w, 0.9999)[0] == 4
+    rng = np.random.default_rng(12)
+    draws = np.array([oracle.cat(w, u)[0] for u in rng.random(20000)])
+    counts = np.bincount(draws, minlength=5)
+    assert counts[0] == 0 and counts[2] == 0
+    assert scipy.stats.chisquare(counts[[1, 3, 4]], 20000 * w[[1, 3, 4]]).pvalue > 1e-3
+
+
+# ------------------------------------------------------------------ greedy
+
+def test_greedy_worked_example():
+    """The "D E F" example (Hacker News thread 49596054), tokens A..H = 0..7, V = 8."""
+    tok = {c: i for i, c in enumerate("ABCDEFGH")}
+    for line in _golden_rows("greedy_worked_example.txt"):
+        drafts, target, emitted = (s.split() for s in line.split("|"))
+        K = len(drafts) + 1
+        logits = np.zeros((1, K, 8), np.float32)
+        for i, c in enumerate(target + ["A"]):       # bonus position: unrelated token
+            logits[0, i, tok[c]] = 5.0
+        out = oracle.accept(oracle.MODE_GREEDY, logits,
+                            draft_tokens=np.array([[tok[c] for c in drafts]], np.int32))
+        n = int(out["n_accepted"][0])
+        got = [ "ABCDEFGH"[t] for t in out["tokens"][0, : n + 1]]
+        assert got == emitted
+        assert np.all(out["tokens"][0, n + 1:] == -1)
+
+
+def test_greedy_invariants():
+    """1 <= emitted <= K; emitted tokens are the target argmaxes; full accept emits K."""
+    rng = np.random.default_rng(13)
+    W, K, V = 500, 5, 16
+    t = rng.standard_normal((W, K, V)).astype(np.float32)
+    am = t.argmax(axis=2)
+    drafts = np.where(rng.random((W, K - 1)) < 0.6, am[:, : K - 1],
+                      rng.integers(0, V, size=(W, K - 1))).astype(np.int32)
+    out = oracle.accept(oracle.MODE_GREEDY, t, draft_tokens=drafts)
+    for w in range(W):
+        n = out["n_accepted"][w]
+        assert 0 <= n <= K - 1
+        assert np.array_equal(out["tokens"][w, : n + 1], am[w, : n + 1])
+        match = drafts[w] == am[w, : K - 1]
+        expect_n = K - 1 if match.all() else int(np.argmin(match))
+        assert n == expect_n
+
+
+def _tau(alpha, k):
+    return (1 - alpha ** (k + 1)) / (1 - alpha)
+
+
+def test_tau_formula_matches_printed_table():
+    """The closed form reproduces the printed 18-cell table to its 2 decimals."""
+    for line in _golden_rows("tau_table.txt"):
+        a, *vals = map(float, line.split())
+        for k, v in zip((1, 3, 5), vals):
+            assert abs(_tau(a, k) - v) <= 0.005 + 1e-12
+
+
+def test_ceilings_and_inverse_checks_printed_on_the_pages():
+    """Ceiling = bandwidth / bytes per pass; 82 tok/s over a 59 passes/s ceiling is >= 1.4
+    tokens/pass; 1.8-2 tokens at k = 3 puts acceptance at about 0.47-0.54."""
+    for line in _golden_rows("ceilings.txt"):
+        bw, gb, printed = map(float, line.split())
+        assert abs(bw / gb - printed) < 1.0
+    assert abs(82 / 59 - 1.4) < 0.05
+    from scipy.optimize import brentq
+    a18 = brentq(lambda a: _tau(a, 3) - 1.8, 0.01, 0.99)
+    a20 = brentq(lambda a: _tau(a, 3) - 2.0, 0.01, 0.99)
+    assert abs(a18 - 0.47) < 0.01 and abs(a20 - 0.54) < 0.01
+
+
+@pytest.mark.parametrize("alpha,k", [(0.9, 5), (0.7, 3), (0.5, 1), (0.35, 5), (0.8, 3)])
+def test_greedy_monte_carlo_tokens_per_pass(alpha, k):
+    """Drafts agreeing independently with prob alpha give mean (1 - alpha^(k+1))/(1 - alpha)
+    tokens per pass (4.69 at alpha 0.9, k 5)."""
+    K, V, W = k + 1, 32, 40000
+    rng = np.random.default_rng(14)
+    t = rng.standard_normal((W, K, V)).astype(np.float32)
+    out = oracle.accept(oracle.MODE_GREEDY, t, draft_mode=oracle.DRAFT_AGREE,
+                        alpha=alpha, seed=3, threads=8)
+    emitted = out["n_accepted"] + 1
+    se = emitted.std() / np.sqrt(W)
+    assert abs(emitted.mean() - _tau(alpha, k)) < 4.5 * se
+    # every pass emits at least one token
+    assert emitted.min() >= 1
+    # the per-position agreement rate is alpha
+    am = t.argmax(axis=2)[:, :k]
+    agree = (out["draft_tokens"] == am).mean()
+    assert abs(agree - alpha) < 4.5 * np.sqrt(alpha * (1 - alpha) / (W * k))
+
+
+# ---------------------------------------------------------------- sampling
+
+def _fixed_rows(V, K, rng, sigma=1.5, noise=0.8):
+    t = (rng.standard_normal((K, V)) * sigma).astype(np.float32)
+    d = (t[: K - 1] + rng.standard_normal((K - 1, V)) * noise).astype(np.float32)
+    return t, d
+
+
+def _tile(a, W):
+    return np.ascontiguousarray(np.broadcast_to(a, (W,) + a.shape))
+
+
+def test_sampling_acceptance_rate_is_overlap():
+    """P(accept x_1) = sum_x min(p(x), q(x)), x_1 ~ q (99.9% binomial interval)."""
+    rng = np.random.default_rng(15)
+    V, K, W = 8, 2, 200000
+    t, d = _fixed_rows(V, K, rng)
+    for T, top_p, min_p in ((1.0, 1.0, 0.0), (0.6, 0.95, 0.05)):
+        out = oracle.accept(oracle.MODE_SAMPLE, _tile(t, W), _tile(d, W),
+                            draft_mode=oracle.DRAFT_Q_SAMPLE, T=T, top_p=top_p, min_p=min_p,
+                            seed=21, threads=8)
+        p, _ = oracle.warp(t[0], T, top_p, min_p)
+        q, _ = oracle.warp(d[0], T, top_p, min_p)
+        beta = np.minimum(p, q).sum()
+        rate = (out["n_accepted"] >= 1).mean()
+        assert abs(rate - beta) < 3.3 * np.sqrt(beta * (1 - beta) / W)
+
+
+def test_sampling_one_hot_drafter_accepts_with_p():
+    """A greedy (one-hot) drafter at x is accepted with probability p(x)."""
+    rng = np.random.default_rng(16)
+    V, W = 8, 200000
+    t, _ = _fixed_rows(V, 2, rng)
+    d = np.zeros((1, V), np.float32)
+    x = 3
+    d[0, x] = 200.0                                  # q is one-hot at x in double
+    out = oracle.accept(oracle.MODE_SAMPLE, _tile(t, W), _tile(d, W),
+                        draft_mode=oracle.DRAFT_Q_SAMPLE, seed=5, threads=8)
+    assert np.all(out["draft_tokens"] == x)
+    p, _ = oracle.warp(t[0], 1.0)
+    rate = (out["n_accepted"] >= 1).mean()
+    assert abs(rate - p[x]) < 3.3 * np.sqrt(p[x] * (1 - p[x]) / W)
+
+
+def test_sampling_lossless_chi_square():
+    """The token at output index j is distributed as p_{j+1} (target-only sampling):
+    V = 8, K = 4, fixed p and q, 10^6 windows, chi-square per index, Bonferroni 1e-3."""
+    rng = np.random.default_rng(17)
+    V, K, W = 8, 4, 1_000_000
+    t, d = _fixed_rows(V, K, rng)
+    out = oracle.accept(oracle.MODE_SAMPLE, _tile(t, W), _tile(d, W),
+                        draft_mode=oracle.DRAFT_Q_SAMPLE, seed=9, threads=8)
+    n = out["n_accepted"]
+    assert n.min() >= 0 and n.max() <= K - 1
+    for j in range(K):
+        sel = n >= j
+        toks = out["tokens"][sel, j]
+        counts = np.bincount(toks, minlength=V)
+        p, _ = oracle.warp(t[j], 1.0)
+        assert scipy.stats.chisquare(counts, counts.sum() * p).pvalue > 1e-3 / K
+
+
+def test_sampling_lossless_pit_on_fresh_windows():
+    """C1-like windows (fresh p per window): the randomized probability-integral transform
+    of the first emitted token under p_1 is U(0,1) (chi-square over 20 bins)."""
+    spec = synth.LogitSpec(seed=0, K=4, vocab=256, target_sigma=2.0, noise_sigma=0.5)
+    t, d = synth.logits_batch(spec, 0, 20000, threads=8)
+    out = oracle.accept(oracle.MODE_SAMPLE, t, d, draft_mode=oracle.DRAFT_Q_SAMPLE,
+                        seed=0, threads=8)
+    rng = np.random.default_rng(18)
+    v = np.empty(len(t))
+    for w in range(len(t)):
+        p, _ = oracle.warp(t[w, 0], 1.0)
+        tok = out["tokens"][w, 0]
+        F = np.cumsum(p)
+        lo = F[tok - 1] if tok else 0.0
+        v[w] = lo + rng.random() * (F[tok] - lo)
+    counts = np.histogram(v, bins=20, range=(0, 1))[0]
+    assert scipy.stats.chisquare(counts).pvalue > 1e-3
+
+
+def test_sampling_q_equals_p_accepts_all_and_disjoint_accepts_none():
+    rng = np.random.default_rng(19)
+    V, K, W = 8, 4, 20000
+    t, _ = _fixed_rows(V, K, rng)
+    out = oracle.accept(oracle.MODE_SAMPLE, _tile(t, W), _tile(t[: K - 1], W),
+                        draft_mode=oracle.DRAFT_Q_SAMPLE, seed=4, threads=8)
+    assert np.all(out["n_accepted"] == K - 1)
+    # disjoint supports: p lives on tokens 0..3, q on 4..7
+    tp = np.full((K, V), -1e4, np.float32)
+    tp[:, :4] = rng.standard_normal((K, 4))
+    dq = np.full((K - 1, V), -1e4, np.float32)
+    dq[:, 4:] = rng.standard_normal((K - 1, 4))
+    out = oracle.accept(oracle.MODE_SAMPLE, _tile(tp, W), _tile(dq, W),
+                        draft_mode=oracle.DRAFT_Q_SAMPLE, seed=4, threads=8)
+    assert np.all(out["n_accepted"] == 0)
+    p, _ = oracle.warp(tp[0], 1.0)
+    counts = np.bincount(out["tokens"][:, 0], minlength=V)
+    assert counts[4:].sum() == 0
+    assert scipy.stats.chisquare(counts[:4], W * p[:4]).pvalue > 1e-3
+
+
+def test_sampling_mean_tokens_is_product_of_overlaps():
+    """Mean tokens per pass = sum_{j<K} prod_{i<=j} beta_i with beta_i = sum min(p_i, q_i)."""
+    rng = np.random.default_rng(20)
+    V, K, W = 8, 5, 300000
+    t, d = _fixed_rows(V, K, rng, noise=0.5)
+    out = oracle.accept(oracle.MODE_SAMPLE, _tile(t, W), _tile(d, W),
+                        draft_mode=oracle.DRAFT_Q_SAMPLE, seed=6, threads=8)
+    beta = [np.minimum(oracle.warp(t[i], 1.0)[0], oracle.warp(d[i], 1.0)[0]).sum()
+            for i in range(K - 1)]
+    expect = sum(np.prod(beta[:j]) for j in range(K))
+    emitted = out["n_accepted"] + 1
+    assert abs(emitted.mean() - expect) < 4.5 * emitted.std() / np.sqrt(W)
+
+
+def test_accept_status_codes():
+    rng = np.random.default_rng(21)
+    t = rng.standard_normal((3, 3, 8)).astype(np.float32)
+    t[1, 2, 5] = np.nan
+    drafts = np.array([[1, 2], [1, 2], [1, 9]], np.int32)
+    out = oracle.accept(oracle.MODE_GREEDY, t, draft_tokens=drafts)
+    assert list(out["status"]) == [0, 1, 2]
+    assert np.all(out["tokens"][1:] == -1) and np.all(out["n_accepted"][1:] == 0)
+
+
+def test_k1_is_plain_decode():
+    """K = 1: no drafts; greedy emits the argmax, sampling one draw from p_1."""
+    rng = np.random.default_rng(22)
+    V, W = 8, 100000
+    t = (rng.standard_normal((1, V)) * 1.5).astype(np.float32)
+    g = oracle.accept(oracle.MODE_GREEDY, _tile(t, 3))
+    assert np.all(g["tokens"][:, 0] == t[0].argmax()) and np.all(g["n_accepted"] == 0)
+    s = oracle.accept(oracle.MODE_SAMPLE, _tile(t, W), np.zeros((W, 0, V), np.float32),
+                      seed=2, threads=8)
+    p, _ = oracle.warp(t[0], 1.0)
+    counts = np.bincount(s["tokens"][:, 0], minlength=V)
+    assert scipy.stats.chisquare(counts, W * p).pvalue > 1e-3
