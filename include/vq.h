@@ -1,0 +1,232 @@
+/*
+ * vq.h -- C ABI of libvq, the speculative-decoding verify pass on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The pass has two parts, both described on the page "100 tokens per second from a
+ * 27B model on a 24 GB AMD card" (section "How speculative decoding gets past a
+ * per-token wall") and on the Hacker News thread 49596054:
+ *   1. every block-quantised weight matrix of a dense decoder is read from HBM once and
+ *      applied to a K-wide batch of drafted-token activations, layer by layer
+ *      (vq_verify_linear for one matrix, vq_decode_pass for the whole stack);
+ *   2. a lossless acceptance rule turns the [K][vocab] logits into emitted tokens
+ *      (vq_verify_accept).
+ *
+ * Conventions for every entry point:
+ *   - Buffers are caller-owned DEVICE pointers unless stated otherwise; descriptors are
+ *     HOST structs, read only during the call.  The library never allocates device or
+ *     host memory; scratch space is a caller-provided workspace sized by
+ *     vq_workspace_bytes().
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).  No call
+ *     synchronises the host, copies to the host or allocates.  Buffers must stay alive
+ *     until the stream has executed the work.
+ *   - Return value: VQ_OK (0) or a negative VQ_ERR_* code.  Arguments are validated on
+ *     the host before anything is launched; on an argument error nothing is enqueued.
+ *     vq_last_error() returns a thread-local text for the last failure.
+ *   - No C++ exception crosses this interface; the library keeps no global mutable
+ *     state besides that thread-local text.
+ *   - Calls that share a workspace must not overlap on the device.
+ */
+#ifndef VQ_H
+#define VQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VQ_ABI_VERSION 1
+
+/* ------------------------------------------------------------------ status */
+#define VQ_OK 0
+#define VQ_ERR_ARG (-1)          /* invalid argument (NULL, size, range, alignment)     */
+#define VQ_ERR_UNSUPPORTED (-2)  /* valid but not instantiated (format / K / path)      */
+#define VQ_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than vq_workspace_bytes() */
+#define VQ_ERR_HIP (-4)          /* a HIP launch or runtime call failed                 */
+
+/* ------------------------------------------------------------ weight format */
+/* Block-quantised weights, row-major, blocks of 32 consecutive input columns.
+ *   qs     : uint8 [rows][cols/2]; byte j/2 of a row holds column j in its low nibble
+ *            when j is even, in its high nibble when j is odd.
+ *   VQ_FMT_Q4      : code n in 0..15, q = n - 8, w = d * q          (d: fp16 scale)
+ *   VQ_FMT_Q4_MIN  : w = d * q + m                                   (m: fp16 block min)
+ *   VQ_FMT_MXFP4   : w = e2m1(n) * 2^(E - 127)  (OCP Microscaling v1.0: E2M1 code, E8M0 E)
+ *   scales : fp16 [rows][cols/32] (Q4, Q4_MIN) or uint8 E8M0 [rows][cols/32] (MXFP4)
+ *   mins   : fp16 [rows][cols/32] for Q4_MIN, NULL otherwise
+ * Alignment: qs 16-byte aligned; scales and mins 16-byte aligned.
+ * The pages name 4-bit block formats (Q4_K_M, UD-Q4_K_XL, q4_0) and MXFP4 without
+ * defining them; this is the block-32 layout the library implements. */
+#define VQ_FMT_Q4 0
+#define VQ_FMT_Q4_MIN 1
+#define VQ_FMT_MXFP4 2
+
+typedef struct vq_matrix {
+    int32_t format;       /* VQ_FMT_*                                   */
+    int32_t rows;         /* output features, >= 0                      */
+    int32_t cols;         /* input features, > 0, multiple of 32        */
+    int32_t reserved;     /* must be 0                                  */
+    const void* qs;       /* device */
+    const void* scales;   /* device */
+    const void* mins;     /* device or NULL */
+} vq_matrix;
+
+/* Output element type of vq_verify_linear. */
+#define VQ_DTYPE_F32 0
+#define VQ_DTYPE_F16 1
+
+/* Kernel choice.  AUTO picks by K; VALU and MFMA force one (for measurement). */
+#define VQ_PATH_AUTO 0
+#define VQ_PATH_VALU 1        /* VALU dot2 kernel, K <= 8 */
+#define VQ_PATH_MFMA 2        /* MFMA 16x16x32 f16 kernel, K <= 16 */
+
+#define VQ_MAX_K 16
+
+/*
+ * vq_verify_linear -- y = W x for K activation columns, each weight byte read once.
+ *
+ * "Hand the target model K drafted tokens and it scores all of them in a single forward
+ * pass, because the weight matrices get read once and applied to a K wide batch of
+ * activations instead of a single vector" (page "100 tokens per second ...", section
+ * "How speculative decoding gets past a per-token wall"); the weights are streamed out
+ * of memory once per pass (same page, section "The wall").
+ *
+ *   W       : host descriptor of a device matrix (see above)
+ *   x_f16   : device fp16 [K][cols]  (row k = activation column k of the window)
+ *   K       : 1..16
+ *   y       : device [K][rows], fp32 or fp16 (y_dtype); y[k][r] = sum_j w[r][j] x[k][j]
+ *   path    : VQ_PATH_*
+ *   ws      : device workspace of at least vq_workspace_bytes(VQ_OP_LINEAR, W, K) bytes
+ * Errors: VQ_ERR_ARG for NULL pointers (except ws when the size query is 0), K outside
+ * 1..16, cols not a positive multiple of 32, rows < 0, misaligned pointers, an unknown
+ * format/dtype/path or mins inconsistent with the format; VQ_ERR_UNSUPPORTED for
+ * VQ_PATH_VALU with K > 8; VQ_ERR_WORKSPACE; VQ_ERR_HIP.
+ * rows == 0 is valid and enqueues nothing.
+ */
+int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y,
+                     int32_t y_dtype, int32_t path, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- acceptance */
+#define VQ_MODE_GREEDY 0      /* accept x_i while it equals the target argmax            */
+#define VQ_MODE_SAMPLE 1      /* accept x_i with prob. min(1, p(x_i)/q(x_i)), else resample */
+
+/* Where the drafted tokens come from.  GIVEN reads draft_tokens; the others are
+ * synthetic drafters that write the tokens they draw into draft_tokens. */
+#define VQ_DRAFT_GIVEN 0      /* draft_tokens is an input                                */
+#define VQ_DRAFT_Q_ARGMAX 1   /* x_i = argmax of drafter row i                           */
+#define VQ_DRAFT_Q_SAMPLE 2   /* x_i ~ q_i (warped drafter row i) with uniform u_D       */
+#define VQ_DRAFT_AGREE 3      /* x_i = target argmax if u_D < alpha, else another token
+                                 uniform over the other V-1 via u_X                      */
+
+typedef struct vq_accept_desc {
+    int32_t mode;              /* VQ_MODE_*                                              */
+    int32_t draft_mode;        /* VQ_DRAFT_*                                             */
+    int32_t W;                 /* windows, >= 0                                          */
+    int32_t K;                 /* positions per window (K-1 drafts + 1 bonus), 1..16     */
+    int32_t V;                 /* vocabulary size, 1 .. 2^24                             */
+    int32_t reserved;          /* must be 0                                              */
+    const float* target_logits;/* device f32 [W][K][V]: row i scores position i+1        */
+    const float* draft_logits; /* device f32 [W][K-1][V], or NULL when not needed        */
+    int32_t* draft_tokens;     /* device i32 [W][K-1]: input (GIVEN) or output           */
+    float temperature;         /* > 0; 0 with VQ_MODE_SAMPLE is rejected                 */
+    float top_p;               /* (0, 1]; 1 disables the top-p cut                        */
+    float min_p;               /* [0, 1); 0 disables the min-p cut                        */
+    float alpha;               /* [0, 1]: agreement rate of VQ_DRAFT_AGREE                */
+    uint64_t seed;             /* Philox key                                              */
+    uint64_t window_base;      /* counter offset: window w uses counter window_base + w   */
+    int32_t* n_accepted;       /* device i32 [W]: accepted drafts n (tokens emitted n+1)  */
+    int32_t* tokens;           /* device i32 [W][K]: emitted tokens, -1 padded            */
+    int32_t* status;           /* device i32 [W]: 0 ok, 1 non-finite logit, 2 draft token
+                                  outside [0, V); on status != 0 nothing is emitted       */
+} vq_accept_desc;
+
+/*
+ * vq_verify_accept -- the lossless acceptance rule over W independent windows.
+ *
+ * GREEDY: "accept xi while it equals the target's argmax" (page "100 tokens per second
+ * ...", section "How speculative decoding gets past a per-token wall"); argmax ties go
+ * to the lowest index; the target's own token at the first disagreement (or at the
+ * bonus position K when every draft is accepted) caps the window (page "Decode is
+ * memory-bound ...", section "Speculative decoding").
+ * SAMPLE: p_i and q_i are the target and drafter rows after the sampler warp
+ * (temperature, softmax, top-p and min-p cuts over the order probability-descending /
+ * index-ascending, renormalised; page "Decode is memory-bound ...", section "Two things
+ * the math says to do").  For i = 1..K-1: accept x_i iff u_A < p_i(x_i)/q_i(x_i); on the
+ * first rejection draw from the normalised positive part of p_i - q_i (p_i itself if
+ * that part is zero) and stop; if all are accepted draw the bonus from p_K.  Draws are
+ * inverse-CDF over vocabulary order.
+ * Uniforms: Philox4x64-10 (Salmon et al., SC'11), key (seed, 0), counter
+ * (window_base + w, position, 0, 0); u = (r >> 40) * 2^-24 of output lanes
+ * 0 (u_A), 1 (u_R: residual / bonus), 2 (u_D: drafting), 3 (u_X: "other token").
+ * Errors: VQ_ERR_ARG for NULL pointers, sizes or sampler settings out of range;
+ * VQ_ERR_WORKSPACE; VQ_ERR_HIP.  Data errors never abort: they go to status[w].
+ */
+int vq_verify_accept(const vq_accept_desc* d, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------- decode pass */
+typedef struct vq_layer {
+    vq_matrix q, k, v, o, gate, up, down;
+} vq_layer;
+
+typedef struct vq_model {
+    int32_t n_layers;          /* >= 1                                                  */
+    int32_t reserved;          /* must be 0                                             */
+    const vq_layer* layers;    /* HOST array [n_layers] of device-matrix descriptors    */
+    vq_matrix lm_head;         /* [vocab][hidden]                                       */
+} vq_model;
+
+/*
+ * vq_decode_pass -- one verify pass of the whole weight stack for K columns.
+ *
+ * The window goes through layer 1, then layer 2, and so on, reading each layer's weights
+ * once (Hacker News thread 49596054); the output is a [K][vocab] logits tensor.  Per
+ * layer four dependent stages run: S1 q|k|v = W_qkv x_attn, S2 o = W_o x_o,
+ * S3 gate|up = W_gu x_mlp, S4 down = W_down x_down, then logits = W_lm x_final.
+ * The stack has no attention, norm weights or residuals; each stage input is the
+ * previous output normalised to unit RMS per column and rounded to fp16:
+ * x_o = rho(q), x_mlp = rho(o), x_down = rho(silu(gate) * up), next x_attn = rho(down),
+ * x_final = rho(last down), with rho(v) = v / sqrt(mean(v^2)).  The first x_attn is x0.
+ *
+ *   M      : host model descriptor; hidden = q.cols, every layer the same shapes;
+ *            q: [H][H], k, v: [KV][H], o: [H][H], gate, up: [FF][H], down: [H][FF],
+ *            lm_head: [V][H]; all matrices of one format
+ *   x0_f16 : device fp16 [K][H]
+ *   logits : device f32 [K][V]
+ *   ws     : device workspace >= vq_workspace_bytes(VQ_OP_DECODE, M, K); after the call
+ *            it holds every stage's fp16 input and fp32 output (see vq_decode_stage_ptr)
+ * Errors: as vq_verify_linear, plus VQ_ERR_ARG for inconsistent layer shapes.
+ */
+int vq_decode_pass(const vq_model* M, const void* x0_f16, int32_t K, float* logits,
+                   int32_t path, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * vq_decode_stage_ptr -- where a decode pass left stage s's tensors inside ws.
+ * Stage s = 4*layer + j (j: 0 qkv, 1 o, 2 gate|up, 3 down), s = 4*n_layers is the
+ * lm_head.  *in_f16 receives the device address of the fp16 input [K][cols] and
+ * *out_f32 of the fp32 output [K][rows] (rows of the fused stage: qkv = H + 2 KV,
+ * gate|up = 2 FF with gate first).  Host-only arithmetic; no device access.
+ */
+int vq_decode_stage_ptr(const vq_model* M, int32_t K, void* ws, int32_t stage,
+                        void** in_f16, void** out_f32);
+
+/* ---------------------------------------------------------------- queries */
+#define VQ_OP_LINEAR 0         /* desc = const vq_matrix*       */
+#define VQ_OP_ACCEPT 1         /* desc = const vq_accept_desc*  */
+#define VQ_OP_DECODE 2         /* desc = const vq_model*        */
+
+/* Workspace bytes needed by an op for the given descriptor and K (0 on bad input). */
+size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K);
+
+/* Static text for a status code. */
+const char* vq_status_string(int32_t status);
+
+/* Thread-local text of the last error raised on this thread ("" if none). */
+const char* vq_last_error(void);
+
+/* VQ_ABI_VERSION of the built library. */
+int32_t vq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VQ_H */

@@ -124,8 +124,9 @@ def linear(m, x: np.ndarray, threads: int = 1):
 
 
 def rho(v: np.ndarray) -> np.ndarray:
-    """Per activation column (row of v [K][n]): v / sqrt(mean(v^2)), in double."""
-    v = np.ascontiguousarray(v, dtype=np.float32)
+    """Per activation column (row of v [K][n]): v / sqrt(mean(v^2)), in double.
+    float32 input (a stage output) converts to double exactly."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
     out = np.empty(v.shape, np.float64)
     lib().or_rho(_p(v), v.shape[0], v.shape[1], _p(out))
     return out

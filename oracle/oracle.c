@@ -172,13 +172,13 @@ int or_linear(int fmt, const uint8_t* qs, const void* scales, const uint16_t* mi
 /* ------------------------------------------------------------------ stage glue */
 
 /* rho: out[k][j] = v[k][j] / sqrt(mean_j v[k][j]^2), per activation column k. */
-void or_rho(const float* v, int K, int64_t n, double* out) {
+void or_rho(const double* v, int K, int64_t n, double* out) {
     for (int k = 0; k < K; ++k) {
-        const float* vk = v + (int64_t)k * n;
+        const double* vk = v + (int64_t)k * n;
         double ss = 0.0;
-        for (int64_t j = 0; j < n; ++j) ss += (double)vk[j] * (double)vk[j];
+        for (int64_t j = 0; j < n; ++j) ss += vk[j] * vk[j];
         double rms = sqrt(ss / (double)n);
-        for (int64_t j = 0; j < n; ++j) out[(int64_t)k * n + j] = (double)vk[j] / rms;
+        for (int64_t j = 0; j < n; ++j) out[(int64_t)k * n + j] = vk[j] / rms;
     }
 }
 

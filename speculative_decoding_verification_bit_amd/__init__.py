@@ -1,0 +1,255 @@
+"""Python binding of libvq, the speculative-decoding verify pass for MI355X (gfx950).
+
+Argument marshalling only: every step of the pass runs in the HIP kernels of libvq.so;
+PyTorch supplies device memory and the stream.  Importing this package loads the
+library and fails loudly if it has not been built (``python
+speculative_decoding_verification_bit_amd/build.py``); there is no CPU fallback.
+
+Entry points (same names as the C ABI, without the ``vq_`` prefix):
+  verify_linear(W, x, ...)   y[K][rows] = W x, every weight byte read once
+  verify_accept(...)         greedy / sampling acceptance over W windows
+  decode_pass(model, x0)     the whole weight stack for a K-wide window -> logits
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libvq.so")
+
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+FMT_Q4, FMT_Q4_MIN, FMT_MXFP4 = 0, 1, 2
+DTYPE_F32, DTYPE_F16 = 0, 1
+PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+MODE_GREEDY, MODE_SAMPLE = 0, 1
+DRAFT_GIVEN, DRAFT_Q_ARGMAX, DRAFT_Q_SAMPLE, DRAFT_AGREE = 0, 1, 2, 3
+OP_LINEAR, OP_ACCEPT, OP_DECODE = 0, 1, 2
+MAX_K = 16
+
+_P = ctypes.c_void_p
+
+
+class VqMatrix(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("qs", _P), ("scales", _P), ("mins", _P)]
+
+
+class VqLayer(ctypes.Structure):
+    _fields_ = [(n, VqMatrix) for n in ("q", "k", "v", "o", "gate", "up", "down")]
+
+
+class VqModel(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("layers", ctypes.POINTER(VqLayer)), ("lm_head", VqMatrix)]
+
+
+class VqAcceptDesc(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("draft_mode", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("target_logits", _P), ("draft_logits", _P), ("draft_tokens", _P),
+                ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
+                ("min_p", ctypes.c_float), ("alpha", ctypes.c_float),
+                ("seed", ctypes.c_uint64), ("window_base", ctypes.c_uint64),
+                ("n_accepted", _P), ("tokens", _P), ("status", _P)]
+
+
+EXPORTS = ("vq_verify_linear", "vq_verify_accept", "vq_decode_pass", "vq_decode_stage_ptr",
+           "vq_workspace_bytes", "vq_status_string", "vq_last_error", "vq_abi_version")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libvq.so not built at {path}; run "
+                          "`python speculative_decoding_verification_bit_amd/build.py`")
+    L = ctypes.CDLL(path)
+    I32, SZ = ctypes.c_int32, ctypes.c_size_t
+    L.vq_verify_linear.restype = I32
+    L.vq_verify_linear.argtypes = [ctypes.POINTER(VqMatrix), _P, I32, _P, I32, I32, _P, SZ, _P]
+    L.vq_verify_accept.restype = I32
+    L.vq_verify_accept.argtypes = [ctypes.POINTER(VqAcceptDesc), _P, SZ, _P]
+    L.vq_decode_pass.restype = I32
+    L.vq_decode_pass.argtypes = [ctypes.POINTER(VqModel), _P, I32, _P, I32, _P, SZ, _P]
+    L.vq_decode_stage_ptr.restype = I32
+    L.vq_decode_stage_ptr.argtypes = [ctypes.POINTER(VqModel), I32, _P, I32,
+                                      ctypes.POINTER(_P), ctypes.POINTER(_P)]
+    L.vq_workspace_bytes.restype = SZ
+    L.vq_workspace_bytes.argtypes = [I32, _P, I32]
+    L.vq_status_string.restype = ctypes.c_char_p
+    L.vq_status_string.argtypes = [I32]
+    L.vq_last_error.restype = ctypes.c_char_p
+    L.vq_last_error.argtypes = []
+    L.vq_abi_version.restype = I32
+    L.vq_abi_version.argtypes = []
+    return L
+
+
+lib = load_library()
+
+
+class VqError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = lib.vq_last_error().decode() or lib.vq_status_string(code).decode()
+        super().__init__(f"{where}: {lib.vq_status_string(code).decode()} ({code}): {msg}")
+
+
+def _check(rc: int, where: str):
+    if rc != OK:
+        raise VqError(rc, where)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _empty(nbytes: int, device):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+class DeviceMatrix:
+    """A block-quantised matrix in device memory (torch tensors) and its descriptor."""
+
+    def __init__(self, fmt: int, rows: int, cols: int, qs, scales, mins=None):
+        self.fmt, self.rows, self.cols = fmt, rows, cols
+        self.qs, self.scales, self.mins = qs, scales, mins
+        self.desc = VqMatrix(fmt, rows, cols, 0, _ptr(qs), _ptr(scales), _ptr(mins))
+
+    @classmethod
+    def from_host(cls, m, device="cuda"):
+        """Upload a synth.Q4Matrix (numpy arrays)."""
+        import torch
+        qs = torch.from_numpy(np.ascontiguousarray(m.qs)).to(device)
+        sc = np.ascontiguousarray(m.scales)
+        scales = torch.from_numpy(sc.view(np.uint16) if sc.dtype == np.float16 else sc).to(device)
+        mins = None
+        if m.mins is not None:
+            mins = torch.from_numpy(np.ascontiguousarray(m.mins).view(np.uint16)).to(device)
+        return cls(m.fmt, m.rows, m.cols, qs, scales, mins)
+
+    @property
+    def nbytes(self) -> int:
+        n = self.qs.numel() + self.scales.numel() * self.scales.element_size()
+        return n + (0 if self.mins is None else self.mins.numel() * 2)
+
+
+def workspace_bytes(op: int, desc, K: int) -> int:
+    return int(lib.vq_workspace_bytes(op, ctypes.cast(ctypes.pointer(desc), _P), K))
+
+
+def verify_linear(W: DeviceMatrix, x, y=None, y_dtype: int = DTYPE_F32, path: int = PATH_AUTO,
+                  ws=None, stream=None):
+    """y[K][rows] = W x for fp16 x [K][cols] on the device."""
+    import torch
+    K = x.shape[0]
+    if y is None:
+        y = torch.empty((K, W.rows), dtype=torch.float32 if y_dtype == DTYPE_F32 else torch.float16,
+                        device=x.device)
+    need = int(lib.vq_workspace_bytes(OP_LINEAR, ctypes.byref(W.desc), K))
+    if ws is None:
+        ws = _empty(need, x.device)
+    _check(lib.vq_verify_linear(ctypes.byref(W.desc), _ptr(x), K, _ptr(y), y_dtype, path,
+                                _ptr(ws), ws.numel(), _stream(stream)), "vq_verify_linear")
+    return y
+
+
+def accept_desc(mode, target, draft=None, draft_tokens=None, draft_mode=DRAFT_GIVEN, T=1.0,
+                top_p=1.0, min_p=0.0, alpha=0.0, seed=0, window_base=0, n_accepted=None,
+                tokens=None, status=None) -> VqAcceptDesc:
+    W, K, V = target.shape
+    return VqAcceptDesc(mode, draft_mode, W, K, V, 0, _ptr(target), _ptr(draft), _ptr(draft_tokens),
+                        T, top_p, min_p, alpha, seed, window_base, _ptr(n_accepted), _ptr(tokens),
+                        _ptr(status))
+
+
+def verify_accept(mode: int, target, draft=None, draft_tokens=None, draft_mode: int = DRAFT_GIVEN,
+                  T: float = 1.0, top_p: float = 1.0, min_p: float = 0.0, alpha: float = 0.0,
+                  seed: int = 0, window_base: int = 0, ws=None, out=None, stream=None) -> dict:
+    """Acceptance over W windows of fp32 target [W][K][V] / drafter [W][K-1][V] logits."""
+    import torch
+    W, K, V = target.shape
+    dev = target.device
+    if out is None:
+        out = dict(n_accepted=torch.empty(W, dtype=torch.int32, device=dev),
+                   tokens=torch.empty((W, K), dtype=torch.int32, device=dev),
+                   status=torch.empty(W, dtype=torch.int32, device=dev))
+    if draft_tokens is None and K > 1:
+        draft_tokens = torch.full((W, K - 1), -1, dtype=torch.int32, device=dev)
+    d = accept_desc(mode, target, draft, draft_tokens, draft_mode, T, top_p, min_p, alpha, seed,
+                    window_base, out["n_accepted"], out["tokens"], out["status"])
+    need = int(lib.vq_workspace_bytes(OP_ACCEPT, ctypes.byref(d), K))
+    if ws is None:
+        ws = _empty(need, dev)
+    _check(lib.vq_verify_accept(ctypes.byref(d), _ptr(ws), ws.numel(), _stream(stream)),
+           "vq_verify_accept")
+    out["draft_tokens"] = draft_tokens
+    return out
+
+
+class DeviceModel:
+    """A dense decoder's weight stack on the device (synth.ModelShape layout)."""
+
+    def __init__(self, layers: list[dict], lm_head: DeviceMatrix):
+        self.layers = layers
+        self.lm_head = lm_head
+        arr = (VqLayer * len(layers))()
+        for i, L in enumerate(layers):
+            for n in ("q", "k", "v", "o", "gate", "up", "down"):
+                setattr(arr[i], n, L[n].desc)
+        self._arr = arr
+        self.desc = VqModel(len(layers), 0, ctypes.cast(arr, ctypes.POINTER(VqLayer)), lm_head.desc)
+
+    @property
+    def hidden(self) -> int:
+        return self.layers[0]["q"].cols
+
+    @property
+    def vocab(self) -> int:
+        return self.lm_head.rows
+
+    @property
+    def nbytes(self) -> int:
+        n = self.lm_head.nbytes
+        for L in self.layers:
+            n += sum(m.nbytes for m in L.values())
+        return n
+
+    def workspace_bytes(self, K: int) -> int:
+        return int(lib.vq_workspace_bytes(OP_DECODE, ctypes.byref(self.desc), K))
+
+    def stage_ptrs(self, K: int, ws, stage: int):
+        a, b = _P(), _P()
+        _check(lib.vq_decode_stage_ptr(ctypes.byref(self.desc), K, _ptr(ws), stage,
+                                       ctypes.byref(a), ctypes.byref(b)), "vq_decode_stage_ptr")
+        return a.value, b.value
+
+
+def decode_pass(model: DeviceModel, x0, logits=None, path: int = PATH_AUTO, ws=None, stream=None):
+    """logits[K][V] of one verify pass over the whole stack; ws keeps every stage's tensors."""
+    import torch
+    K = x0.shape[0]
+    if logits is None:
+        logits = torch.empty((K, model.vocab), dtype=torch.float32, device=x0.device)
+    if ws is None:
+        ws = _empty(model.workspace_bytes(K), x0.device)
+    _check(lib.vq_decode_pass(ctypes.byref(model.desc), _ptr(x0), K, _ptr(logits), path, _ptr(ws),
+                              ws.numel(), _stream(stream)), "vq_decode_pass")
+    return logits, ws
+
+
+def stage_tensor(ws, addr: int, shape, dtype):
+    """A view of a tensor inside the decode workspace at device address addr."""
+    import torch
+    off = addr - ws.data_ptr()
+    n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+    return ws[off:off + n].view(dtype).view(*shape)

@@ -1,0 +1,541 @@
+// Lossless acceptance of drafted tokens against the target's [K][vocab] logits.
+//
+// Greedy: a draft is kept while it equals the target argmax; sampling: draft x is
+// accepted with probability min(1, p(x)/q(x)) and on rejection a token is drawn from
+// the normalised positive part of p - q (page "100 tokens per second from a 27B model
+// on a 24 GB AMD card", section "How speculative decoding gets past a per-token wall";
+// page "Decode is memory-bound ...", section "Speculative decoding").  p and q are the
+// rows after the sampler warp: temperature, softmax, then the top-p and min-p cuts
+// (page "Decode is memory-bound ...", section "Two things the math says to do").
+//
+// Kernels:
+//  * k_row_stats: one 512-thread workgroup per logits row.  Pass 1 finds the maximum,
+//    the first argmax and non-finite entries.  For sampling rows, pass 2 sums
+//    e_j = exp((l_j - l_max) / T) in 2^-44 fixed point (integer sums are exact and
+//    order-independent, so every run is bitwise identical), pass 3 locates the top-p
+//    cut exactly by a three-level radix select on the order-preserving bit pattern of
+//    the logit (12 + 12 + 8 bits, histograms of probability mass in LDS) and then
+//    resolves equal logits by index, pass 4 sums the kept mass.  The kept set is then
+//    "min-p test passes and (key, index) ranks at or before the cut".
+//  * k_accept: one 512-thread workgroup per window.  Thread 0 runs the sequential
+//    rule; inverse-CDF draws are block-wide: each thread owns a contiguous slice of
+//    the vocabulary, slice masses are scanned, and the slice holding the crossing is
+//    walked in index order.
+// Uniforms come from Philox4x64-10 (Salmon et al., SC'11) keyed by the seed, with the
+// counter (window, position, 0, 0); u = top 24 bits * 2^-24, exact in fp32 and fp64.
+#include <hip/hip_runtime.h>
+
+#include "vq_internal.h"
+
+namespace vq {
+namespace {
+
+constexpr int NT = 512;                        // threads per workgroup
+constexpr double FX = 17592186044416.0;        // 2^44, fixed-point unit of mass
+constexpr float FXF = 17592186044416.0f;
+
+struct RowStat {
+    int32_t argmax;
+    int32_t nonfinite;
+    float lmax;
+    uint32_t thr_key;    // top-p cut: keys above are kept, equal keys up to thr_idx
+    int32_t thr_idx;
+    int32_t n_keep;
+    uint64_t z_fx;       // sum of e over the row
+    uint64_t keep_fx;    // sum of e over the kept set
+};
+
+// Order-preserving map of a finite float to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t fkey(float v) {
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float e_of(float l, float lmax, float T) {
+    return expf(__fdiv_rn(l - lmax, T));
+}
+
+__device__ __forceinline__ uint64_t to_fx(float e) { return (uint64_t)(e * FXF); }
+
+__device__ __forceinline__ bool kept(const RowStat& s, float l, float e, int j, float min_p) {
+    if (min_p > 0.f && !(e >= min_p)) return false;
+    const uint32_t k = fkey(l);
+    return k > s.thr_key || (k == s.thr_key && j <= s.thr_idx);
+}
+
+// ---------------------------------------------------------------- block helpers
+
+__device__ uint64_t block_sum_u64(uint64_t v, uint64_t* sh) {
+    sh[threadIdx.x] = v;
+    __syncthreads();
+    for (int s = NT / 2; s > 0; s >>= 1) {
+        if (threadIdx.x < (unsigned)s) sh[threadIdx.x] += sh[threadIdx.x + s];
+        __syncthreads();
+    }
+    const uint64_t r = sh[0];
+    __syncthreads();
+    return r;
+}
+
+// Exclusive prefix sum over threads 0..NT-1 in thread order; *total gets the sum.
+__device__ uint64_t block_excl_scan_u64(uint64_t v, uint64_t* sh, uint64_t* total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    uint64_t x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) sh[wv] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t run = 0;
+        for (int w = 0; w < NT / 64; ++w) {
+            const uint64_t t = sh[w];
+            sh[w] = run;
+            run += t;
+        }
+        sh[NT / 64] = run;
+    }
+    __syncthreads();
+    const uint64_t r = sh[wv] + x - v;
+    *total = sh[NT / 64];
+    __syncthreads();
+    return r;
+}
+
+// Highest bin b of hist[0..n) (n = 256 or 4096) with sum_{b' >= b} hist >= tgt; also the
+// mass strictly above b.  Requires sum(hist) >= tgt.
+__device__ void find_bin(const uint64_t* hist, int n, uint64_t tgt, uint64_t* sh, int* bin,
+                         uint64_t* above, int* sbin, uint64_t* sabove) {
+    const int bpt = n >= NT ? n / NT : 1;
+    const int active = n / bpt;
+    const int t = threadIdx.x;
+    uint64_t local = 0;
+    if (t < active)
+        for (int i = 0; i < bpt; ++i) local += hist[n - 1 - (t * bpt + i)];
+    uint64_t tot;
+    const uint64_t before = block_excl_scan_u64(local, sh, &tot);
+    if (t < active && before < tgt && tgt <= before + local) {
+        uint64_t c = before;
+        for (int i = 0; i < bpt; ++i) {
+            const int b = n - 1 - (t * bpt + i);
+            if (c + hist[b] >= tgt) {
+                *sbin = b;
+                *sabove = c;
+                break;
+            }
+            c += hist[b];
+        }
+    }
+    __syncthreads();
+    *bin = *sbin;
+    *above = *sabove;
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------ row stats
+
+struct StatArgs {
+    const float* logits;   // rows of length V
+    int nrows;
+    int V;
+    int full;              // 0: argmax and non-finite only
+    float T, top_p, min_p;
+    RowStat* out;
+};
+
+__global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
+    __shared__ uint64_t hist[4096];
+    __shared__ uint64_t sh[NT + 1];
+    __shared__ float shf[NT];
+    __shared__ int shi[NT];
+    __shared__ int s_bin;
+    __shared__ uint64_t s_above;
+    const int row = blockIdx.x;
+    const int V = A.V;
+    const float* l = A.logits + (size_t)row * V;
+    const int t = threadIdx.x;
+
+    // pass 1: maximum, first argmax, non-finite entries
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    int nf = 0;
+    for (int j = t; j < V; j += NT) {
+        const float v = l[j];
+        if (!isfinite(v)) nf = 1;
+        else if (v > best) { best = v; bi = j; }
+    }
+    shf[t] = best;
+    shi[t] = bi;
+    __syncthreads();
+    for (int s = NT / 2; s > 0; s >>= 1) {
+        if (t < s) {
+            const float ob = shf[t + s];
+            const int oi = shi[t + s];
+            if (ob > shf[t] || (ob == shf[t] && oi < shi[t])) { shf[t] = ob; shi[t] = oi; }
+        }
+        __syncthreads();
+    }
+    const float lmax = shf[0];
+    const int amax = shi[0];
+    __syncthreads();
+    const int anynf = __syncthreads_or(nf);
+    RowStat st;
+    st.argmax = amax == 0x7fffffff ? 0 : amax;
+    st.nonfinite = anynf ? 1 : 0;
+    st.lmax = lmax;
+    st.thr_key = 0u;
+    st.thr_idx = 0x7fffffff;
+    st.n_keep = 0;
+    st.z_fx = 0;
+    st.keep_fx = 0;
+    if (anynf || !A.full) {
+        if (t == 0) A.out[row] = st;
+        return;
+    }
+    const float T = A.T;
+
+    // pass 2: total mass
+    uint64_t z = 0;
+    for (int j = t; j < V; j += NT) z += to_fx(e_of(l[j], lmax, T));
+    st.z_fx = block_sum_u64(z, sh);
+
+    // pass 3: top-p cut
+    if (A.top_p < 1.f) {
+        uint64_t tgt = (uint64_t)ceil((double)A.top_p * (double)st.z_fx);
+        if (tgt < 1) tgt = 1;
+        uint32_t prefix = 0;
+        int shift_hi = 32;      // bits already fixed: key >> shift_hi == prefix
+        uint64_t above = 0;
+        const int levels[3] = {12, 12, 8};
+        for (int lv = 0; lv < 3; ++lv) {
+            const int nbits = levels[lv];
+            const int nbins = 1 << nbits;
+            const int shift = shift_hi - nbits;
+            for (int i = t; i < nbins; i += NT) hist[i] = 0;
+            __syncthreads();
+            for (int j = t; j < V; j += NT) {
+                const float v = l[j];
+                const uint32_t k = fkey(v);
+                if (shift_hi == 32 || (k >> shift_hi) == prefix)
+                    atomicAdd((unsigned long long*)&hist[(k >> shift) & (nbins - 1)],
+                              (unsigned long long)to_fx(e_of(v, lmax, T)));
+            }
+            __syncthreads();
+            int b;
+            uint64_t ab;
+            find_bin(hist, nbins, tgt - above, sh, &b, &ab, &s_bin, &s_above);
+            above += ab;
+            prefix = (shift_hi == 32 ? 0u : (prefix << nbits)) | (uint32_t)b;
+            shift_hi = shift;
+        }
+        const uint32_t kstar = prefix;
+        // equal keys: the c-th smallest index among them crosses the target
+        const float lstar = __uint_as_float((kstar & 0x80000000u) ? (kstar & 0x7fffffffu) : ~kstar);
+        const uint64_t estar = to_fx(e_of(lstar, lmax, T));
+        const uint64_t need = tgt - above;
+        const uint64_t c = estar ? (need + estar - 1) / estar : 1;
+        const int chunk = (V + NT - 1) / NT;
+        const int j0 = t * chunk, j1 = min(V, j0 + chunk);
+        uint64_t cnt = 0;
+        for (int j = j0; j < j1; ++j) cnt += fkey(l[j]) == kstar;
+        uint64_t tot;
+        const uint64_t before = block_excl_scan_u64(cnt, sh, &tot);
+        const uint64_t cc = c > tot ? tot : c;
+        if (before < cc && cc <= before + cnt) {
+            uint64_t seen = before;
+            for (int j = j0; j < j1; ++j)
+                if (fkey(l[j]) == kstar && ++seen == cc) { s_bin = j; break; }
+        }
+        __syncthreads();
+        st.thr_key = kstar;
+        st.thr_idx = s_bin;
+        __syncthreads();
+    }
+
+    // pass 4: kept mass and size
+    uint64_t kf = 0, kn = 0;
+    for (int j = t; j < V; j += NT) {
+        const float v = l[j];
+        const float e = e_of(v, lmax, T);
+        if (kept(st, v, e, j, A.min_p)) { kf += to_fx(e); ++kn; }
+    }
+    st.keep_fx = block_sum_u64(kf, sh);
+    st.n_keep = (int)block_sum_u64(kn, sh);
+    if (t == 0) A.out[row] = st;
+}
+
+// ------------------------------------------------------------------ Philox
+
+__device__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+        const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+        const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0;
+        c[1] = lo1;
+        c[2] = n2;
+        c[3] = lo0;
+        k0 += W0;
+        k1 += W1;
+    }
+}
+
+// Top 24 bits of the four Philox lanes of (window, position).
+__device__ void uniforms24(uint64_t seed, uint64_t window, uint64_t pos, uint32_t (&u)[4]) {
+    uint64_t c[4] = {window, pos, 0, 0};
+    philox4x64_10(c, seed, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = (uint32_t)(c[i] >> 40);
+}
+
+// ------------------------------------------------------------------ accept
+
+struct AcceptArgs {
+    int mode, draft_mode, W, K, V;
+    const float* tgt;          // [W][K][V]
+    const float* drf;          // [W][K-1][V]
+    int32_t* draft_tokens;
+    float T, top_p, min_p;
+    uint32_t alpha24;          // ceil(alpha * 2^24)
+    uint64_t seed, window_base;
+    const RowStat* st_t;       // [W*K]
+    const RowStat* st_d;       // [W*(K-1)]
+    int32_t *n_acc, *tokens, *status;
+};
+
+// C * 2^24 > u24 * S with 128-bit integers.
+__device__ __forceinline__ bool cross(uint64_t C, uint32_t u24, uint64_t S) {
+    const uint64_t ahi = C >> 40, alo = C << 24;
+    const uint64_t bhi = __umul64hi((uint64_t)u24, S), blo = (uint64_t)u24 * S;
+    return ahi > bhi || (ahi == bhi && alo > blo);
+}
+
+// Smallest j with prefix_j(w) * 2^24 > u24 * sum(w) (vocabulary order); -1 if sum is 0.
+template <class WF>
+__device__ int block_cat(WF wf, int V, uint32_t u24, uint64_t* sh, int* sres) {
+    const int chunk = (V + NT - 1) / NT;
+    const int j0 = threadIdx.x * chunk, j1 = min(V, j0 + chunk);
+    uint64_t local = 0;
+    for (int j = j0; j < j1; ++j) local += wf(j);
+    uint64_t S;
+    const uint64_t before = block_excl_scan_u64(local, sh, &S);
+    if (threadIdx.x == 0) *sres = -1;
+    __syncthreads();
+    if (S > 0 && local > 0 && !cross(before, u24, S) && cross(before + local, u24, S)) {
+        uint64_t C = before;
+        for (int j = j0; j < j1; ++j) {
+            C += wf(j);
+            if (cross(C, u24, S)) { *sres = j; break; }
+        }
+    }
+    __syncthreads();
+    const int r = *sres;
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ double prob_of(const RowStat& s, const float* l, int x, float T, float min_p) {
+    const float v = l[x];
+    const float e = e_of(v, s.lmax, T);
+    if (!kept(s, v, e, x, min_p)) return 0.0;
+    return (double)e / ((double)s.keep_fx / FX);
+}
+
+__global__ __launch_bounds__(NT) void k_accept(AcceptArgs A) {
+    __shared__ uint64_t sh[NT + 1];
+    __shared__ int sres;
+    __shared__ int x[VQ_MAX_K + 1];
+    __shared__ int s_status, s_n, s_stop;
+    __shared__ uint32_t s_u[4];
+    const int w = blockIdx.x;
+    const int K = A.K, V = A.V;
+    const float T = A.T, min_p = A.min_p;
+    const uint64_t win = A.window_base + (uint64_t)w;
+    const RowStat* stt = A.st_t + (size_t)w * K;
+    const RowStat* std_ = A.st_d ? A.st_d + (size_t)w * (K - 1) : nullptr;
+    const float* tl = A.tgt + (size_t)w * K * V;
+    const float* dl = A.drf ? A.drf + (size_t)w * (K - 1) * V : nullptr;
+    int32_t* out = A.tokens + (size_t)w * K;
+    int32_t* dtok = A.draft_tokens ? A.draft_tokens + (size_t)w * (K - 1) : nullptr;
+    const bool uses_drafter = A.mode == VQ_MODE_SAMPLE || A.draft_mode == VQ_DRAFT_Q_ARGMAX ||
+                              A.draft_mode == VQ_DRAFT_Q_SAMPLE;
+
+    if (threadIdx.x == 0) {
+        int st = 0;
+        for (int i = 0; i < K; ++i) st |= stt[i].nonfinite;
+        if (uses_drafter)
+            for (int i = 0; i + 1 < K; ++i) st |= std_[i].nonfinite;
+        s_status = st ? 1 : 0;
+    }
+    __syncthreads();
+
+    // drafts x_1..x_{K-1}
+    for (int i = 1; i < K && s_status == 0; ++i) {
+        if (threadIdx.x == 0) {
+            uint32_t u[4];
+            uniforms24(A.seed, win, (uint64_t)i, u);
+            for (int q = 0; q < 4; ++q) s_u[q] = u[q];
+        }
+        __syncthreads();
+        if (A.draft_mode == VQ_DRAFT_Q_SAMPLE) {
+            const RowStat sq = std_[i - 1];
+            const float* lq = dl + (size_t)(i - 1) * V;
+            auto wf = [&](int j) -> uint64_t {
+                const float v = lq[j];
+                const float e = e_of(v, sq.lmax, T);
+                return kept(sq, v, e, j, min_p) ? to_fx(e) : 0ull;
+            };
+            const int r = block_cat(wf, V, s_u[2], sh, &sres);
+            if (threadIdx.x == 0) x[i] = r >= 0 ? r : sq.argmax;   // the argmax always has mass
+        } else if (threadIdx.x == 0) {
+            int xi;
+            if (A.draft_mode == VQ_DRAFT_GIVEN) {
+                xi = dtok[i - 1];
+                if (xi < 0 || xi >= V) s_status = 2;
+            } else if (A.draft_mode == VQ_DRAFT_Q_ARGMAX) {
+                xi = std_[i - 1].argmax;
+            } else {
+                const int a = stt[i - 1].argmax;
+                if (s_u[2] < A.alpha24) {
+                    xi = a;
+                } else {
+                    const int o = (int)(((uint64_t)s_u[3] * (uint64_t)(V - 1)) >> 24);
+                    xi = o < a ? o : o + 1;
+                }
+            }
+            x[i] = xi;
+        }
+        __syncthreads();
+    }
+
+    if (s_status != 0) {
+        for (int i = threadIdx.x; i < K; i += NT) out[i] = -1;
+        if (dtok && A.draft_mode != VQ_DRAFT_GIVEN)
+            for (int i = threadIdx.x; i + 1 < K; i += NT) dtok[i] = -1;
+        if (threadIdx.x == 0) {
+            A.n_acc[w] = 0;
+            A.status[w] = s_status;
+        }
+        return;
+    }
+    if (dtok && A.draft_mode != VQ_DRAFT_GIVEN)
+        for (int i = threadIdx.x + 1; i < K; i += NT) dtok[i - 1] = x[i];
+    for (int i = threadIdx.x; i < K; i += NT) out[i] = -1;
+    __syncthreads();
+
+    if (A.mode == VQ_MODE_GREEDY) {
+        if (threadIdx.x == 0) {
+            int n = 0;
+            while (n < K - 1 && x[n + 1] == stt[n].argmax) {
+                out[n] = x[n + 1];
+                ++n;
+            }
+            out[n] = stt[n].argmax;
+            A.n_acc[w] = n;
+            A.status[w] = 0;
+        }
+        return;
+    }
+
+    // sampling: ratio tests at positions 1..K-1 (thread 0), then one draw
+    if (threadIdx.x == 0) {
+        int n = 0, stop = K;          // stop: position of the draw (K = bonus)
+        for (int i = 1; i < K; ++i) {
+            uint32_t u[4];
+            uniforms24(A.seed, win, (uint64_t)i, u);
+            const double p = prob_of(stt[i - 1], tl + (size_t)(i - 1) * V, x[i], T, min_p);
+            const double q = prob_of(std_[i - 1], dl + (size_t)(i - 1) * V, x[i], T, min_p);
+            const double r = p / q;
+            const double uA = (double)u[0] * (1.0 / 16777216.0);
+            if (uA < r) {
+                out[i - 1] = x[i];
+                n = i;
+            } else {
+                stop = i;
+                break;
+            }
+        }
+        uint32_t u[4];
+        uniforms24(A.seed, win, (uint64_t)stop, u);
+        s_u[1] = u[1];
+        s_n = n;
+        s_stop = stop;
+    }
+    __syncthreads();
+    const int stop = s_stop;
+    const RowStat sp = stt[stop - 1];
+    const float* lp = tl + (size_t)(stop - 1) * V;
+    auto wp = [&](int j) -> uint64_t {
+        const float v = lp[j];
+        const float e = e_of(v, sp.lmax, T);
+        return kept(sp, v, e, j, min_p) ? to_fx(e) : 0ull;
+    };
+    int tok;
+    if (stop == K) {
+        tok = block_cat(wp, V, s_u[1], sh, &sres);
+    } else {
+        const RowStat sq = std_[stop - 1];
+        const float* lq = dl + (size_t)(stop - 1) * V;
+        const double Sp = (double)sp.keep_fx / FX, Sq = (double)sq.keep_fx / FX;
+        auto wr = [&](int j) -> uint64_t {
+            const float v = lp[j];
+            const float e = e_of(v, sp.lmax, T);
+            if (!kept(sp, v, e, j, min_p)) return 0ull;
+            const double pj = (double)e / Sp;
+            const float vq = lq[j];
+            const float eq = e_of(vq, sq.lmax, T);
+            const double qj = kept(sq, vq, eq, j, min_p) ? (double)eq / Sq : 0.0;
+            const double d = pj - qj;
+            return d > 0.0 ? (uint64_t)(d * FX) : 0ull;
+        };
+        tok = block_cat(wr, V, s_u[1], sh, &sres);
+        if (tok < 0) tok = block_cat(wp, V, s_u[1], sh, &sres);
+    }
+    if (threadIdx.x == 0) {
+        out[stop - 1] = tok;
+        A.n_acc[w] = s_n;
+        A.status[w] = 0;
+    }
+}
+
+}  // namespace
+
+size_t accept_ws_bytes(const vq_accept_desc* d) {
+    const size_t rows = (size_t)d->W * d->K + (size_t)d->W * (d->K > 1 ? d->K - 1 : 0);
+    return align_up(rows * sizeof(RowStat), 256);
+}
+
+hipError_t launch_accept(const vq_accept_desc* d, void* ws, hipStream_t st) {
+    if (d->W == 0) return hipSuccess;
+    RowStat* st_t = (RowStat*)ws;
+    RowStat* st_d = st_t + (size_t)d->W * d->K;
+    const bool sample = d->mode == VQ_MODE_SAMPLE;
+    const bool drafter = sample || d->draft_mode == VQ_DRAFT_Q_ARGMAX || d->draft_mode == VQ_DRAFT_Q_SAMPLE;
+    const float T = d->temperature;
+    StatArgs sa{d->target_logits, d->W * d->K, d->V, sample ? 1 : 0, T, d->top_p, d->min_p, st_t};
+    k_row_stats<<<dim3(sa.nrows), NT, 0, st>>>(sa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (drafter && d->K > 1) {
+        const int full = (sample || d->draft_mode == VQ_DRAFT_Q_SAMPLE) ? 1 : 0;
+        StatArgs sd{d->draft_logits, d->W * (d->K - 1), d->V, full, T, d->top_p, d->min_p, st_d};
+        k_row_stats<<<dim3(sd.nrows), NT, 0, st>>>(sd);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    double a24 = ceil((double)d->alpha * 16777216.0);
+    if (a24 < 0) a24 = 0;
+    if (a24 > 16777216.0) a24 = 16777216.0;
+    AcceptArgs aa{d->mode, d->draft_mode, d->W, d->K, d->V, d->target_logits,
+                  drafter ? d->draft_logits : nullptr, d->draft_tokens, T, d->top_p, d->min_p,
+                  (uint32_t)a24, d->seed, d->window_base, st_t, drafter ? st_d : nullptr,
+                  d->n_accepted, d->tokens, d->status};
+    k_accept<<<dim3(d->W), NT, 0, st>>>(aa);
+    return hipGetLastError();
+}
+
+}  // namespace vq

@@ -1,0 +1,381 @@
+// C ABI of libvq: argument validation, workspace layout, dispatch and the decode-pass
+// stage sequence.  Every check runs on the host before anything is enqueued.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "vq_internal.h"
+
+namespace vq {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(VQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_matrix(const vq_matrix* W, const char* name) {
+    if (!W) return fail(VQ_ERR_ARG, "%s: NULL matrix descriptor", name);
+    if (W->format < VQ_FMT_Q4 || W->format > VQ_FMT_MXFP4)
+        return fail(VQ_ERR_ARG, "%s: unknown format %d", name, W->format);
+    if (W->reserved != 0) return fail(VQ_ERR_ARG, "%s: reserved field must be 0", name);
+    if (W->rows < 0) return fail(VQ_ERR_ARG, "%s: rows %d < 0", name, W->rows);
+    if (W->cols <= 0 || W->cols % 32)
+        return fail(VQ_ERR_ARG, "%s: cols %d is not a positive multiple of 32", name, W->cols);
+    if (W->rows == 0) return VQ_OK;
+    if (!W->qs || !W->scales) return fail(VQ_ERR_ARG, "%s: NULL qs or scales", name);
+    if ((W->format == VQ_FMT_Q4_MIN) != (W->mins != nullptr))
+        return fail(VQ_ERR_ARG, "%s: mins must be given exactly for VQ_FMT_Q4_MIN", name);
+    if (!aligned(W->qs, 16) || !aligned(W->scales, 16) || (W->mins && !aligned(W->mins, 16)))
+        return fail(VQ_ERR_ARG, "%s: qs, scales and mins must be 16-byte aligned", name);
+    return VQ_OK;
+}
+
+bool use_mfma(int K, int path) {
+    if (path == VQ_PATH_MFMA) return true;
+    if (path == VQ_PATH_VALU) return false;
+    return K > 8;
+}
+
+int check_path(int K, int path) {
+    if (path < VQ_PATH_AUTO || path > VQ_PATH_MFMA) return fail(VQ_ERR_ARG, "unknown path %d", path);
+    if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
+    if (path == VQ_PATH_VALU && K > 8)
+        return fail(VQ_ERR_UNSUPPORTED, "the VALU path is instantiated for K <= 8 (K = %d)", K);
+    return VQ_OK;
+}
+
+size_t lin_ws(const vq_matrix* W, int K) {
+    // Sized for either path so one workspace serves both.
+    return std::max(lin_scratch_bytes(W->format, W->rows, W->cols, K, false),
+                    lin_scratch_bytes(W->format, W->rows, W->cols, K, true));
+}
+
+// ---------------------------------------------------------------- decode layout
+
+struct Shapes {
+    int H, KV, FF, V, L, fmt;
+};
+
+int check_model(const vq_model* M, Shapes* s) {
+    if (!M) return fail(VQ_ERR_ARG, "NULL model");
+    if (M->n_layers < 1 || !M->layers) return fail(VQ_ERR_ARG, "model needs n_layers >= 1 and layers");
+    if (M->reserved != 0) return fail(VQ_ERR_ARG, "model reserved field must be 0");
+    const vq_layer& l0 = M->layers[0];
+    s->H = l0.q.cols;
+    s->KV = l0.k.rows;
+    s->FF = l0.gate.rows;
+    s->V = M->lm_head.rows;
+    s->L = M->n_layers;
+    s->fmt = l0.q.format;
+    if (s->H % 64 || s->KV % 64 || s->FF % 64 || s->H <= 0 || s->KV <= 0 || s->FF <= 0)
+        return fail(VQ_ERR_UNSUPPORTED, "decode pass needs hidden, kv and ffn sizes that are multiples of 64");
+    if (s->V < 1) return fail(VQ_ERR_ARG, "lm_head needs rows >= 1");
+    for (int l = 0; l < M->n_layers; ++l) {
+        const vq_layer& y = M->layers[l];
+        const vq_matrix* ms[7] = {&y.q, &y.k, &y.v, &y.o, &y.gate, &y.up, &y.down};
+        const int rr[7] = {s->H, s->KV, s->KV, s->H, s->FF, s->FF, s->H};
+        const int cc[7] = {s->H, s->H, s->H, s->H, s->H, s->H, s->FF};
+        static const char* nm[7] = {"q", "k", "v", "o", "gate", "up", "down"};
+        for (int i = 0; i < 7; ++i) {
+            char buf[48];
+            snprintf(buf, sizeof buf, "layer %d %s", l, nm[i]);
+            int rc = check_matrix(ms[i], buf);
+            if (rc) return rc;
+            if (ms[i]->rows != rr[i] || ms[i]->cols != cc[i] || ms[i]->format != s->fmt)
+                return fail(VQ_ERR_ARG, "%s: shape %dx%d fmt %d, expected %dx%d fmt %d", buf, ms[i]->rows,
+                            ms[i]->cols, ms[i]->format, rr[i], cc[i], s->fmt);
+        }
+    }
+    int rc = check_matrix(&M->lm_head, "lm_head");
+    if (rc) return rc;
+    if (M->lm_head.cols != s->H || M->lm_head.format != s->fmt)
+        return fail(VQ_ERR_ARG, "lm_head: shape or format inconsistent with the layers");
+    return VQ_OK;
+}
+
+// Stage s of a pass: 4 per layer (qkv, o, gate|up, down) + lm_head.
+struct StageShape {
+    int rows, cols;
+};
+
+StageShape stage_shape(const Shapes& s, int st) {
+    if (st == 4 * s.L) return {s.V, s.H};
+    switch (st % 4) {
+        case 0: return {s.H + 2 * s.KV, s.H};
+        case 1: return {s.H, s.H};
+        case 2: return {2 * s.FF, s.H};
+        default: return {s.H, s.FF};
+    }
+}
+
+struct DecodeLayout {
+    size_t in_off[4], out_off[4];  // per stage kind within a layer block
+    size_t layer_bytes;            // retention bytes per layer
+    size_t final_in_off;           // x_final fp16 [K][H]
+    size_t stats_off, scratch_off, total;
+};
+
+DecodeLayout decode_layout(const Shapes& s, int K) {
+    DecodeLayout d{};
+    size_t p = 0;
+    for (int j = 0; j < 4; ++j) {
+        const StageShape ss = stage_shape(s, j);
+        d.in_off[j] = p;
+        p += align_up((size_t)K * ss.cols * 2, 256);
+        d.out_off[j] = p;
+        p += align_up((size_t)K * ss.rows * 4, 256);
+    }
+    d.layer_bytes = p;
+    p = d.layer_bytes * s.L;
+    d.final_in_off = p;
+    p += align_up((size_t)K * s.H * 2, 256);
+    d.stats_off = p;
+    const int nst = std::max(finalize_stats_blocks(2 * s.FF, 1),
+                             std::max(finalize_stats_blocks(s.H + 2 * s.KV, 0), finalize_stats_blocks(s.H, 0)));
+    p += align_up((size_t)nst * K * 4, 256);
+    d.scratch_off = p;
+    size_t sc = 0;
+    for (int j = 0; j <= 4; ++j) {
+        const StageShape ss = stage_shape(s, j == 4 ? 4 * s.L : j);
+        sc = std::max(sc, std::max(lin_scratch_bytes(s.fmt, ss.rows, ss.cols, K, false),
+                                   lin_scratch_bytes(s.fmt, ss.rows, ss.cols, K, true)));
+    }
+    p += sc;
+    d.total = p;
+    return d;
+}
+
+Mat mat_cat(const vq_matrix* const* ms, int n) {
+    Mat r = mat_from(*ms[0]);
+    r.nseg = n;
+    int end = 0;
+    for (int i = 0; i < n; ++i) {
+        end += ms[i]->rows;
+        r.seg_end[i] = end;
+        r.qs[i] = (const uint8_t*)ms[i]->qs;
+        r.scales[i] = ms[i]->scales;
+        r.mins[i] = (const uint16_t*)ms[i]->mins;
+    }
+    r.rows = end;
+    return r;
+}
+
+}  // namespace
+}  // namespace vq
+
+using namespace vq;
+
+extern "C" {
+
+int32_t vq_abi_version(void) { return VQ_ABI_VERSION; }
+
+const char* vq_last_error(void) { return vq::g_err; }
+
+const char* vq_status_string(int32_t status) {
+    switch (status) {
+        case VQ_OK: return "ok";
+        case VQ_ERR_ARG: return "invalid argument";
+        case VQ_ERR_UNSUPPORTED: return "unsupported configuration";
+        case VQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case VQ_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K) {
+    if (!desc) return 0;
+    if (op == VQ_OP_LINEAR) {
+        const vq_matrix* W = (const vq_matrix*)desc;
+        if (check_matrix(W, "W") || K < 1 || K > VQ_MAX_K) return 0;
+        return W->rows == 0 ? 0 : lin_ws(W, K);
+    }
+    if (op == VQ_OP_ACCEPT) {
+        const vq_accept_desc* d = (const vq_accept_desc*)desc;
+        if (d->W < 0 || d->K < 1 || d->K > VQ_MAX_K) return 0;
+        return accept_ws_bytes(d);
+    }
+    if (op == VQ_OP_DECODE) {
+        Shapes s;
+        if (check_model((const vq_model*)desc, &s) || K < 1 || K > VQ_MAX_K) return 0;
+        return decode_layout(s, K).total;
+    }
+    return 0;
+}
+
+int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype,
+                     int32_t path, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = check_matrix(W, "W");
+    if (rc) return rc;
+    rc = check_path(K, path);
+    if (rc) return rc;
+    if (y_dtype != VQ_DTYPE_F32 && y_dtype != VQ_DTYPE_F16) return fail(VQ_ERR_ARG, "unknown y_dtype %d", y_dtype);
+    if (W->rows == 0) return VQ_OK;
+    if (!x_f16 || !y) return fail(VQ_ERR_ARG, "NULL x or y");
+    if (!aligned(x_f16, 16)) return fail(VQ_ERR_ARG, "x must be 16-byte aligned");
+    if (!aligned(y, y_dtype == VQ_DTYPE_F32 ? 4 : 2)) return fail(VQ_ERR_ARG, "y is misaligned");
+    const size_t need = lin_ws(W, K);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+        return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
+    const bool mfma = use_mfma(K, path);
+    const Mat M = mat_from(*W);
+    LinScratch s;
+    lin_scratch_carve(ws, W->format, W->rows, W->cols, K, mfma, &s);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_prep_plain(M, (const uint16_t*)x_f16, K, mfma, s, nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "prep launch");
+    e = launch_linear_main(M, K, mfma, s, st);
+    if (e != hipSuccess) return hip_fail(e, "linear launch");
+    e = launch_finalize(M, K, s, y, y_dtype, st);
+    if (e != hipSuccess) return hip_fail(e, "finalize launch");
+    return VQ_OK;
+}
+
+int vq_verify_accept(const vq_accept_desc* d, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!d) return fail(VQ_ERR_ARG, "NULL descriptor");
+    if (d->reserved != 0) return fail(VQ_ERR_ARG, "reserved field must be 0");
+    if (d->mode != VQ_MODE_GREEDY && d->mode != VQ_MODE_SAMPLE) return fail(VQ_ERR_ARG, "unknown mode %d", d->mode);
+    if (d->draft_mode < VQ_DRAFT_GIVEN || d->draft_mode > VQ_DRAFT_AGREE)
+        return fail(VQ_ERR_ARG, "unknown draft_mode %d", d->draft_mode);
+    if (d->W < 0) return fail(VQ_ERR_ARG, "W %d < 0", d->W);
+    if (d->K < 1 || d->K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", d->K, VQ_MAX_K);
+    if (d->V < 1 || d->V > (1 << 19)) return fail(VQ_ERR_ARG, "V %d outside 1..524288", d->V);
+    if (d->draft_mode == VQ_DRAFT_AGREE && d->V < 2) return fail(VQ_ERR_ARG, "VQ_DRAFT_AGREE needs V >= 2");
+    const bool needs_warp = d->mode == VQ_MODE_SAMPLE || d->draft_mode == VQ_DRAFT_Q_SAMPLE;
+    if (needs_warp) {
+        if (!(d->temperature > 0.f) || !isfinite(d->temperature))
+            return fail(VQ_ERR_ARG, "temperature must be finite and > 0 for sampling (T = 0 means greedy)");
+        if (!(d->top_p > 0.f && d->top_p <= 1.f)) return fail(VQ_ERR_ARG, "top_p must be in (0, 1]");
+        if (!(d->min_p >= 0.f && d->min_p < 1.f)) return fail(VQ_ERR_ARG, "min_p must be in [0, 1)");
+    }
+    if (d->draft_mode == VQ_DRAFT_AGREE && !(d->alpha >= 0.f && d->alpha <= 1.f))
+        return fail(VQ_ERR_ARG, "alpha must be in [0, 1]");
+    if (d->W == 0) return VQ_OK;
+    const bool drafter = d->mode == VQ_MODE_SAMPLE || d->draft_mode == VQ_DRAFT_Q_ARGMAX ||
+                         d->draft_mode == VQ_DRAFT_Q_SAMPLE;
+    if (!d->target_logits || !d->n_accepted || !d->tokens || !d->status)
+        return fail(VQ_ERR_ARG, "NULL logits or output pointer");
+    if (d->K > 1 && drafter && !d->draft_logits) return fail(VQ_ERR_ARG, "draft_logits required by this mode");
+    if (d->K > 1 && !d->draft_tokens) return fail(VQ_ERR_ARG, "draft_tokens required when K > 1");
+    if (!aligned(d->target_logits, 4) || (d->draft_logits && !aligned(d->draft_logits, 4)))
+        return fail(VQ_ERR_ARG, "logits must be 4-byte aligned");
+    const size_t need = accept_ws_bytes(d);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+        return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
+    hipError_t e = launch_accept(d, ws, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "accept launch");
+    return VQ_OK;
+}
+
+int vq_decode_stage_ptr(const vq_model* M, int32_t K, void* ws, int32_t stage, void** in_f16,
+                        void** out_f32) {
+    g_err[0] = 0;
+    Shapes s;
+    int rc = check_model(M, &s);
+    if (rc) return rc;
+    if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
+    if (stage < 0 || stage > 4 * s.L) return fail(VQ_ERR_ARG, "stage %d outside 0..%d", stage, 4 * s.L);
+    if (!ws || !in_f16 || !out_f32) return fail(VQ_ERR_ARG, "NULL pointer");
+    const DecodeLayout d = decode_layout(s, K);
+    char* base = (char*)ws;
+    if (stage == 4 * s.L) {
+        *in_f16 = base + d.final_in_off;
+        *out_f32 = nullptr;
+    } else {
+        const size_t lb = (size_t)(stage / 4) * d.layer_bytes;
+        *in_f16 = base + lb + d.in_off[stage % 4];
+        *out_f32 = base + lb + d.out_off[stage % 4];
+    }
+    return VQ_OK;
+}
+
+int vq_decode_pass(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
+                   void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    Shapes s;
+    int rc = check_model(M, &s);
+    if (rc) return rc;
+    rc = check_path(K, path);
+    if (rc) return rc;
+    if (!x0_f16 || !logits) return fail(VQ_ERR_ARG, "NULL x0 or logits");
+    if (!aligned(x0_f16, 16) || !aligned(logits, 4)) return fail(VQ_ERR_ARG, "x0 or logits misaligned");
+    const DecodeLayout d = decode_layout(s, K);
+    if (!ws || ws_bytes < d.total || !aligned(ws, 256))
+        return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", d.total, ws_bytes);
+    const bool mfma = use_mfma(K, path);
+    hipStream_t st = (hipStream_t)stream;
+    char* base = (char*)ws;
+    float* stats = (float*)(base + d.stats_off);
+    void* scratch = base + d.scratch_off;
+    int nstats = 0;
+    const float* prev = nullptr;   // raw output of the previous stage
+    int prev_ld = 0;
+    hipError_t e;
+    for (int l = 0; l <= s.L; ++l) {
+        for (int j = 0; j < 4; ++j) {
+            const bool lm = (l == s.L);
+            if (lm && j > 0) break;
+            Mat W;
+            if (lm) {
+                W = mat_from(M->lm_head);
+            } else {
+                const vq_layer& y = M->layers[l];
+                if (j == 0) {
+                    const vq_matrix* m3[3] = {&y.q, &y.k, &y.v};
+                    W = mat_cat(m3, 3);
+                } else if (j == 1) {
+                    W = mat_from(y.o);
+                } else if (j == 2) {
+                    const vq_matrix* m2[2] = {&y.gate, &y.up};
+                    W = mat_cat(m2, 2);
+                } else {
+                    W = mat_from(y.down);
+                }
+            }
+            LinScratch sc;
+            lin_scratch_carve(scratch, s.fmt, W.rows, W.cols, K, mfma, &sc);
+            uint16_t* keep = (uint16_t*)(lm ? base + d.final_in_off
+                                            : base + (size_t)l * d.layer_bytes + d.in_off[j]);
+            float* out = lm ? logits : (float*)(base + (size_t)l * d.layer_bytes + d.out_off[j]);
+            // input: x0, rho(previous output) or rho(silu(gate) * up)
+            if (l == 0 && j == 0) {
+                e = launch_prep_plain(W, (const uint16_t*)x0_f16, K, mfma, sc, keep, st);
+            } else if (j == 3) {
+                e = launch_prep_glue(W, prev, prev_ld, s.FF, GLUE_RHO_SILU, stats, nstats, K, mfma, keep, sc, st);
+            } else {
+                e = launch_prep_glue(W, prev, prev_ld, 0, GLUE_RHO, stats, nstats, K, mfma, keep, sc, st);
+            }
+            if (e != hipSuccess) return hip_fail(e, "prep launch");
+            e = launch_linear_main(W, K, mfma, sc, st);
+            if (e != hipSuccess) return hip_fail(e, "linear launch");
+            if (lm) {
+                e = launch_finalize(W, K, sc, out, VQ_DTYPE_F32, st);
+            } else {
+                const int silu = (j == 2) ? 1 : 0;
+                const int nstat = (j == 0) ? s.H : W.rows;
+                e = launch_finalize_stats(W, K, sc, out, nstat, silu, stats, st);
+                nstats = finalize_stats_blocks(W.rows, silu);
+            }
+            if (e != hipSuccess) return hip_fail(e, "finalize launch");
+            prev = out;
+            prev_ld = W.rows;
+        }
+    }
+    return VQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+"""The C-ABI library loads, exports what include/vq.h declares, and rejects bad arguments
+on the host before anything is enqueued.  No GPU: every call here either fails
+validation or has nothing to launch, so no device pointer is ever dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verification_bit_amd as vq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "vq.h")
+FAKE = 0x10000          # a 256-byte aligned non-NULL address that is never dereferenced
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_exports():
+    assert set(_declared()) == set(vq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(vq.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define VQ_ABI_VERSION (\d+)", open(HEADER).read())
+    assert vq.lib.vq_abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    for code in (vq.OK, vq.ERR_ARG, vq.ERR_UNSUPPORTED, vq.ERR_WORKSPACE, vq.ERR_HIP):
+        assert vq.lib.vq_status_string(code)
+    assert vq.lib.vq_status_string(-99) == b"unknown status"
+
+
+def _mat(fmt=vq.FMT_Q4_MIN, rows=64, cols=256, qs=FAKE, scales=FAKE, mins=FAKE):
+    return vq.VqMatrix(fmt, rows, cols, 0, qs, scales, mins if fmt == vq.FMT_Q4_MIN else None)
+
+
+def _lin(W, K=4, x=FAKE, y=FAKE, dtype=vq.DTYPE_F32, path=vq.PATH_AUTO, ws=None, nbytes=0):
+    return vq.lib.vq_verify_linear(ctypes.byref(W), x, K, y, dtype, path, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(K=0), vq.ERR_ARG),
+    (dict(K=17), vq.ERR_ARG),
+    (dict(K=9, path=vq.PATH_VALU), vq.ERR_UNSUPPORTED),
+    (dict(path=7), vq.ERR_ARG),
+    (dict(dtype=5), vq.ERR_ARG),
+    (dict(x=None), vq.ERR_ARG),
+    (dict(y=None), vq.ERR_ARG),
+    (dict(x=FAKE + 8), vq.ERR_ARG),
+    (dict(), vq.ERR_WORKSPACE),
+    (dict(ws=FAKE, nbytes=16), vq.ERR_WORKSPACE),
+])
+def test_linear_argument_errors(kw, code):
+    assert _lin(_mat(), **kw) == code
+    assert vq.lib.vq_last_error()
+
+
+@pytest.mark.parametrize("W", [
+    _mat(cols=48), _mat(cols=0), _mat(rows=-1), _mat(fmt=3), _mat(qs=None), _mat(scales=None),
+    _mat(qs=FAKE + 4), _mat(fmt=vq.FMT_Q4, mins=FAKE), vq.VqMatrix(vq.FMT_Q4_MIN, 64, 256, 0, FAKE, FAKE, None),
+])
+def test_linear_bad_matrix(W):
+    if W.format == vq.FMT_Q4 and W.mins is None:
+        W.mins = FAKE
+    assert _lin(W) == vq.ERR_ARG
+
+
+def test_linear_zero_rows_is_a_no_op():
+    W = _mat(rows=0, qs=None, scales=None, mins=None)
+    assert _lin(W, x=None, y=None) == vq.OK
+    assert vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), 4) == 0
+
+
+def test_linear_workspace_query():
+    W = _mat(rows=5120, cols=5120)
+    n = vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), 4)
+    # at least the split-K partials: 5 chunks x K x rows floats
+    assert n >= 5 * 4 * 5120 * 4
+    assert vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), 0) == 0
+    assert vq.lib.vq_workspace_bytes(9, ctypes.byref(W), 4) == 0
+
+
+def _acc(**kw):
+    base = dict(mode=vq.MODE_SAMPLE, draft_mode=vq.DRAFT_GIVEN, W=4, K=4, V=256, reserved=0,
+                target_logits=FAKE, draft_logits=FAKE, draft_tokens=FAKE, temperature=1.0, top_p=1.0,
+                min_p=0.0, alpha=0.0, seed=0, window_base=0, n_accepted=FAKE, tokens=FAKE, status=FAKE)
+    base.update(kw)
+    return vq.VqAcceptDesc(**base)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(mode=2), dict(draft_mode=4), dict(W=-1), dict(K=0), dict(K=17), dict(V=0),
+    dict(V=(1 << 19) + 1), dict(temperature=0.0), dict(temperature=-1.0), dict(top_p=0.0),
+    dict(top_p=1.5), dict(min_p=1.0), dict(min_p=-0.1), dict(target_logits=None),
+    dict(draft_logits=None), dict(draft_tokens=None), dict(tokens=None), dict(status=None),
+    dict(n_accepted=None), dict(reserved=1), dict(draft_mode=vq.DRAFT_AGREE, mode=vq.MODE_GREEDY, V=1),
+    dict(draft_mode=vq.DRAFT_AGREE, mode=vq.MODE_GREEDY, alpha=1.5),
+    dict(temperature=float("nan")),
+])
+def test_accept_argument_errors(kw):
+    d = _acc(**kw)
+    assert vq.lib.vq_verify_accept(ctypes.byref(d), FAKE, 1 << 30, None) == vq.ERR_ARG
+
+
+def test_accept_workspace_errors_and_empty():
+    d = _acc()
+    assert vq.lib.vq_verify_accept(ctypes.byref(d), None, 0, None) == vq.ERR_WORKSPACE
+    need = vq.lib.vq_workspace_bytes(vq.OP_ACCEPT, ctypes.byref(d), 4)
+    assert need > 0
+    assert vq.lib.vq_verify_accept(ctypes.byref(d), FAKE, need - 1, None) == vq.ERR_WORKSPACE
+    e = _acc(W=0, target_logits=None, n_accepted=None, tokens=None, status=None)
+    assert vq.lib.vq_verify_accept(ctypes.byref(e), None, 0, None) == vq.OK
+    # greedy with given drafts ignores the sampler settings and needs no drafter logits
+    g = _acc(mode=vq.MODE_GREEDY, temperature=0.0, top_p=0.0, draft_logits=None)
+    assert vq.lib.vq_verify_accept(ctypes.byref(g), None, 0, None) == vq.ERR_WORKSPACE
+
+
+def _model(L=2, H=256, KV=64, FF=512, V=1000, fmt=vq.FMT_Q4_MIN, bad=None):
+    shapes = dict(q=(H, H), k=(KV, H), v=(KV, H), o=(H, H), gate=(FF, H), up=(FF, H), down=(H, FF))
+    arr = (vq.VqLayer * L)()
+    for i in range(L):
+        for n, (r, c) in shapes.items():
+            if bad == (i, n):
+                r += 64
+            setattr(arr[i], n, _mat(fmt, r, c))
+    return vq.VqModel(L, 0, ctypes.cast(arr, ctypes.POINTER(vq.VqLayer)), _mat(fmt, V, H)), arr
+
+
+def test_decode_validation_and_layout():
+    M, keep = _model()
+    n1 = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 1)
+    n4 = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 4)
+    assert 0 < n1 < n4
+    assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, 4, FAKE, 0, None, 0, None) == vq.ERR_WORKSPACE
+    assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, 0, FAKE, 0, FAKE, n4, None) == vq.ERR_ARG
+    assert vq.lib.vq_decode_pass(ctypes.byref(M), None, 4, FAKE, 0, FAKE, n4, None) == vq.ERR_ARG
+    Mb, kb = _model(bad=(1, "down"))
+    assert vq.lib.vq_decode_pass(ctypes.byref(Mb), FAKE, 4, FAKE, 0, FAKE, n4, None) == vq.ERR_ARG
+    assert vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(Mb), 4) == 0
+    Mu, ku = _model(H=96 * 4 + 32)   # hidden not a multiple of 64
+    assert vq.lib.vq_decode_pass(ctypes.byref(Mu), FAKE, 4, FAKE, 0, FAKE, n4, None) == vq.ERR_UNSUPPORTED
+    # stage pointers: distinct, ordered, inside the workspace
+    seen = []
+    for s in range(9):
+        a, b = ctypes.c_void_p(), ctypes.c_void_p()
+        assert vq.lib.vq_decode_stage_ptr(ctypes.byref(M), 4, FAKE, s, ctypes.byref(a), ctypes.byref(b)) == vq.OK
+        assert FAKE <= a.value < FAKE + n4
+        seen.append(a.value)
+        if s < 8:
+            assert a.value < b.value < FAKE + n4
+        else:
+            assert b.value is None
+    assert seen == sorted(seen) and len(set(seen)) == 9
+    a, b = ctypes.c_void_p(), ctypes.c_void_p()
+    assert vq.lib.vq_decode_stage_ptr(ctypes.byref(M), 4, FAKE, 9, ctypes.byref(a), ctypes.byref(b)) == vq.ERR_ARG

@@ -1,0 +1,131 @@
+"""GPU parity of vq_decode_pass: every stage's output against the oracle's linear map of
+the GPU's own stage input (the per-stage tolerance 1e-3 * sum|w x|), and every stage input
+against the oracle's glue of the previous GPU output (within one fp16 ulp)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import check_rows, need_gpu, say, upload_model
+
+pytestmark = pytest.mark.gpu
+
+
+def _stage_mats(shape, fmt, seed, stage, rows_pick=None):
+    """Host copy of stage s's (fused) weight matrix, optionally only some rows."""
+    L = shape.n_layers
+    if stage == 4 * L:
+        parts = [(L, synth.MAT_LM_HEAD)]
+    else:
+        l, j = divmod(stage, 4)
+        parts = [[(l, synth.MAT_Q), (l, synth.MAT_K), (l, synth.MAT_V)], [(l, synth.MAT_O)],
+                 [(l, synth.MAT_GATE), (l, synth.MAT_UP)], [(l, synth.MAT_DOWN)]][j]
+    mats = []
+    for (l, mid) in parts:
+        r, c = shape.mat_shape(mid)
+        mats.append(synth.weight_matrix(fmt, seed, l, mid, r, c, threads=16))
+    qs = np.concatenate([m.qs for m in mats])
+    sc = np.concatenate([m.scales for m in mats])
+    mn = None if mats[0].mins is None else np.concatenate([m.mins for m in mats])
+    if rows_pick is not None:
+        qs, sc = qs[rows_pick], sc[rows_pick]
+        mn = None if mn is None else mn[rows_pick]
+    return synth.Q4Matrix(fmt, qs.shape[0], mats[0].cols, qs, sc, mn)
+
+
+def _stage_io(model, shape, K, ws, logits, stage):
+    import torch
+    import speculative_decoding_verification_bit_amd as vq
+    L, H, KV, FF = shape.n_layers, shape.hidden, shape.kv_dim, shape.ffn
+    if stage == 4 * L:
+        rows, cols = shape.vocab, H
+    else:
+        rows, cols = [(H + 2 * KV, H), (H, H), (2 * FF, H), (H, FF)][stage % 4]
+    a, b = model.stage_ptrs(K, ws, stage)
+    xin = vq.stage_tensor(ws, a, (K, cols), torch.float16).cpu().numpy()
+    out = logits.cpu().numpy() if b is None else vq.stage_tensor(ws, b, (K, rows), torch.float32).cpu().numpy()
+    return xin, out
+
+
+def _expected_input(shape, stage, prev_out):
+    """The oracle's glue applied to the previous stage's GPU output (double)."""
+    H, FF = shape.hidden, shape.ffn
+    j = stage % 4 if stage < 4 * shape.n_layers else 0
+    if j == 1:                                   # rho(q part of q|k|v)
+        return oracle.rho(prev_out[:, :H])
+    if j == 3:                                   # rho(silu(gate) * up)
+        K = prev_out.shape[0]
+        s = np.stack([oracle.silu_mul(prev_out[k, :FF], prev_out[k, FF:]) for k in range(K)])
+        return oracle.rho(s)
+    return oracle.rho(prev_out)                  # rho(o), rho(down)
+
+
+def _check_glue(xin, expect, what):
+    e16 = expect.astype(np.float16)
+    diff = np.abs(xin.astype(np.float64) - e16.astype(np.float64))
+    ulp = np.spacing(np.abs(e16)).astype(np.float64)
+    bad = diff > ulp
+    say(f"{what}: glue inputs off the rounded oracle value: {int((diff > 0).sum())} "
+        f"(one ulp), beyond one ulp: {int(bad.sum())}")
+    assert not bad.any()
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_MXFP4])
+@pytest.mark.parametrize("K,path", [(1, 1), (4, 1), (8, 1), (4, 2), (16, 2)])
+def test_mini_model_every_stage(fmt, K, path):
+    """A 2-layer stack (hidden 256, kv 64, ffn 512, vocab 1000): all rows of all stages."""
+    torch = need_gpu()
+    import speculative_decoding_verification_bit_amd as vq
+    shape, seed = synth.SHAPE_MINI, 4
+    model = upload_model(shape, fmt, seed)
+    x0 = synth.activations(seed, K, shape.hidden)
+    logits, ws = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=path)
+    torch.cuda.synchronize()
+    prev = None
+    for s in range(4 * shape.n_layers + 1):
+        xin, out = _stage_io(model, shape, K, ws, logits, s)
+        if s == 0:
+            assert np.array_equal(xin.view(np.uint16), x0.view(np.uint16))
+        else:
+            _check_glue(xin, _expected_input(shape, s, prev), f"stage {s}")
+        W = _stage_mats(shape, fmt, seed, s)
+        y_ref, a_ref = oracle.linear(W, xin, threads=8)
+        check_rows(out, y_ref, a_ref, f"fmt {fmt} K {K} path {path} stage {s}")
+        prev = out
+    assert np.isfinite(logits.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("fmt,Ks", [(synth.FMT_Q4_MIN, (1, 4, 8)), (synth.FMT_MXFP4, (16,))])
+def test_27b_stack_sampled_rows(fmt, Ks):
+    """The full 27B-class stack (64 layers, 5120 / 1024 / 17408, vocab 151936) in one pass;
+    stages of layers 0, 31, 63 and the lm_head checked on 24 sampled rows each, every
+    checked stage's input against the glue of the previous output."""
+    torch = need_gpu()
+    import speculative_decoding_verification_bit_amd as vq
+    shape, seed = synth.SHAPE_27B, 0
+    model = upload_model(shape, fmt, seed)
+    say(f"27B stack fmt {fmt} uploaded: {model.nbytes / 1e9:.3f} GB")
+    L = shape.n_layers
+    stages = [0, 1, 2, 3, 4 * 31, 4 * 31 + 1, 4 * 31 + 2, 4 * 31 + 3, 4 * 63 + 3, 4 * L]
+    rng = np.random.default_rng(1)
+    picks, mats = {}, {}
+    for s in stages:
+        full = _stage_mats(shape, fmt, seed, s)
+        pick = np.unique(np.concatenate([rng.integers(0, full.rows, 22), [0, full.rows - 1]]))
+        picks[s] = pick
+        mats[s] = synth.Q4Matrix(fmt, len(pick), full.cols, full.qs[pick], full.scales[pick],
+                                 None if full.mins is None else full.mins[pick])
+        del full
+    for K in Ks:
+        x0 = synth.activations(seed, K, shape.hidden)
+        logits, ws = vq.decode_pass(model, torch.from_numpy(x0).cuda())
+        torch.cuda.synchronize()
+        for s in stages:
+            xin, out = _stage_io(model, shape, K, ws, logits, s)
+            if s > 0:
+                _, prev = _stage_io(model, shape, K, ws, logits, s - 1)
+                _check_glue(xin, _expected_input(shape, s, prev), f"K {K} stage {s}")
+            y_ref, a_ref = oracle.linear(mats[s], xin, threads=8)
+            check_rows(out[:, picks[s]], y_ref, a_ref, f"27B fmt {fmt} K {K} stage {s}")
+        del ws, logits
+        torch.cuda.empty_cache()
