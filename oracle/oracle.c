@@ -312,6 +312,11 @@ int or_warp(const float* l, int64_t V, double T, double top_p, double min_p,
         if (m_m < V && fabs(ord[m_m].pi - thr) < 1e-6 * pi_max) info->near_min_p = 1;
     }
     int64_t n_keep = m_p < m_m ? m_p : m_m;
+    /* A near-threshold cut matters only where it decides the kept set: moving the
+     * top-p cut by one token changes min(m_p, m_m) only when m_p <= m_m, and the
+     * min-p cut only when m_m <= m_p. */
+    if (m_p > m_m) info->near_top_p = 0;
+    if (m_m > m_p) info->near_min_p = 0;
     /* (4) renormalise over the kept set */
     double S = 0.0;
     for (int64_t m = 0; m < n_keep; ++m) S += ord[m].pi;

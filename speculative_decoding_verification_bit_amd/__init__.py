@@ -16,6 +16,9 @@ import ctypes
 import os
 
 import numpy as np
+# torch first: its HIP runtime (soname libamdhip64.so.7) is then the one libvq.so binds
+# to, so device memory, streams and kernels share a single runtime in the process.
+import torch  # noqa: F401
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libvq.so")
