@@ -75,10 +75,17 @@ typedef struct vq_matrix {
 #define VQ_DTYPE_F32 0
 #define VQ_DTYPE_F16 1
 
-/* Kernel choice.  AUTO picks by K; VALU and MFMA force one (for measurement). */
+/* Kernel choice.  AUTO picks by K (VALU up to K = 4, MFMA above); VALU and MFMA force
+   one (for measurement). */
 #define VQ_PATH_AUTO 0
 #define VQ_PATH_VALU 1        /* VALU dot2 kernel, K <= 8 */
 #define VQ_PATH_MFMA 2        /* MFMA 16x16x32 f16 kernel, K <= 16 */
+
+/* Launch strategy of vq_decode_pass, OR-ed into `path` (vq_verify_linear takes 0). */
+#define VQ_LAUNCH_AUTO 0        /* the faster of the two on MI355X: staged */
+#define VQ_LAUNCH_STAGED 4      /* one launch per stage */
+#define VQ_LAUNCH_PERSISTENT 8  /* one cooperative launch per 8 layers; grid barriers
+                                   between the stages inside a launch */
 
 #define VQ_MAX_K 16
 
@@ -123,7 +130,7 @@ typedef struct vq_accept_desc {
     int32_t draft_mode;        /* VQ_DRAFT_*                                             */
     int32_t W;                 /* windows, >= 0                                          */
     int32_t K;                 /* positions per window (K-1 drafts + 1 bonus), 1..16     */
-    int32_t V;                 /* vocabulary size, 1 .. 2^24                             */
+    int32_t V;                 /* vocabulary size, 1 .. 2^19 (fixed-point mass sums)     */
     int32_t reserved;          /* must be 0                                              */
     const float* target_logits;/* device f32 [W][K][V]: row i scores position i+1        */
     const float* draft_logits; /* device f32 [W][K-1][V], or NULL when not needed        */
@@ -192,12 +199,39 @@ typedef struct vq_model {
  *            lm_head: [V][H]; all matrices of one format
  *   x0_f16 : device fp16 [K][H]
  *   logits : device f32 [K][V]
+ *   path   : VQ_PATH_* | VQ_LAUNCH_*
  *   ws     : device workspace >= vq_workspace_bytes(VQ_OP_DECODE, M, K); after the call
  *            it holds every stage's fp16 input and fp32 output (see vq_decode_stage_ptr)
+ * Persistent launches need every workgroup resident (a cooperative launch; the runtime
+ * refuses it otherwise and the call returns VQ_ERR_HIP).  Their grid barriers wait at
+ * most about a second; a barrier that times out sets an error word in ws (never expected
+ * on a resident grid), after which the pass's results are not meaningful.
  * Errors: as vq_verify_linear, plus VQ_ERR_ARG for inconsistent layer shapes.
  */
 int vq_decode_pass(const vq_model* M, const void* x0_f16, int32_t K, float* logits,
                    int32_t path, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * vq_decode_error_word -- where a decode pass in `ws` keeps its grid-barrier error word.
+ *   *word : DEVICE address of an int32 that is 0 after a pass whose grid barriers all
+ *           completed and 1 if one timed out (read it after the pass has finished)
+ * Pure host arithmetic: no GPU call.  Errors: VQ_ERR_ARG for a bad model, K or NULL.
+ */
+int vq_decode_error_word(const vq_model* M, int32_t K, void* ws, int32_t** word);
+
+/*
+ * vq_decode_pass_timed -- measurement hook: exactly the work of vq_decode_pass, plus
+ * hipEventRecord(events[2i]) before and hipEventRecord(events[2i+1]) after the i-th
+ * weight-streaming launch (one per stage when staged, one per 8 layers when persistent),
+ * on `stream`, so the caller can time those launches (hipEventElapsedTime).
+ *   events     : HOST array of n_events caller-created hipEvent_t handles (timing enabled)
+ *   n_events   : >= 2 * (4 * n_layers + 1)
+ *   n_launches : HOST out, the number of launches bracketed (may be NULL)
+ * Errors: as vq_decode_pass, plus VQ_ERR_ARG for a short or NULL-holding events array.
+ */
+int vq_decode_pass_timed(const vq_model* M, const void* x0_f16, int32_t K, float* logits,
+                         int32_t path, void* ws, size_t ws_bytes, void* stream,
+                         void* const* events, int32_t n_events, int32_t* n_launches);
 
 /*
  * vq_decode_stage_ptr -- where a decode pass left stage s's tensors inside ws.

@@ -27,6 +27,7 @@ OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 FMT_Q4, FMT_Q4_MIN, FMT_MXFP4 = 0, 1, 2
 DTYPE_F32, DTYPE_F16 = 0, 1
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+LAUNCH_AUTO, LAUNCH_STAGED, LAUNCH_PERSISTENT = 0, 4, 8
 MODE_GREEDY, MODE_SAMPLE = 0, 1
 DRAFT_GIVEN, DRAFT_Q_ARGMAX, DRAFT_Q_SAMPLE, DRAFT_AGREE = 0, 1, 2, 3
 OP_LINEAR, OP_ACCEPT, OP_DECODE = 0, 1, 2
@@ -59,7 +60,8 @@ class VqAcceptDesc(ctypes.Structure):
                 ("n_accepted", _P), ("tokens", _P), ("status", _P)]
 
 
-EXPORTS = ("vq_verify_linear", "vq_verify_accept", "vq_decode_pass", "vq_decode_stage_ptr",
+EXPORTS = ("vq_verify_linear", "vq_verify_accept", "vq_decode_pass", "vq_decode_pass_timed",
+           "vq_decode_stage_ptr", "vq_decode_error_word",
            "vq_workspace_bytes", "vq_status_string", "vq_last_error", "vq_abi_version")
 
 
@@ -75,9 +77,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.vq_verify_accept.argtypes = [ctypes.POINTER(VqAcceptDesc), _P, SZ, _P]
     L.vq_decode_pass.restype = I32
     L.vq_decode_pass.argtypes = [ctypes.POINTER(VqModel), _P, I32, _P, I32, _P, SZ, _P]
+    L.vq_decode_pass_timed.restype = I32
+    L.vq_decode_pass_timed.argtypes = [ctypes.POINTER(VqModel), _P, I32, _P, I32, _P, SZ, _P,
+                                       ctypes.POINTER(_P), I32, ctypes.POINTER(I32)]
     L.vq_decode_stage_ptr.restype = I32
     L.vq_decode_stage_ptr.argtypes = [ctypes.POINTER(VqModel), I32, _P, I32,
                                       ctypes.POINTER(_P), ctypes.POINTER(_P)]
+    L.vq_decode_error_word.restype = I32
+    L.vq_decode_error_word.argtypes = [ctypes.POINTER(VqModel), I32, _P, ctypes.POINTER(_P)]
     L.vq_workspace_bytes.restype = SZ
     L.vq_workspace_bytes.argtypes = [I32, _P, I32]
     L.vq_status_string.restype = ctypes.c_char_p
@@ -236,6 +243,14 @@ class DeviceModel:
                                        ctypes.byref(a), ctypes.byref(b)), "vq_decode_stage_ptr")
         return a.value, b.value
 
+    def barrier_error(self, K: int, ws) -> int:
+        """The grid-barrier error word of the last pass in ws (0: every barrier completed)."""
+        import torch
+        a = _P()
+        _check(lib.vq_decode_error_word(ctypes.byref(self.desc), K, _ptr(ws), ctypes.byref(a)),
+               "vq_decode_error_word")
+        return int(stage_tensor(ws, a.value, (1,), torch.int32).item())
+
 
 def decode_pass(model: DeviceModel, x0, logits=None, path: int = PATH_AUTO, ws=None, stream=None):
     """logits[K][V] of one verify pass over the whole stack; ws keeps every stage's tensors."""
@@ -248,6 +263,21 @@ def decode_pass(model: DeviceModel, x0, logits=None, path: int = PATH_AUTO, ws=N
     _check(lib.vq_decode_pass(ctypes.byref(model.desc), _ptr(x0), K, _ptr(logits), path, _ptr(ws),
                               ws.numel(), _stream(stream)), "vq_decode_pass")
     return logits, ws
+
+
+def decode_pass_timed(model: DeviceModel, x0, events, logits, ws, path: int = PATH_AUTO, stream=None):
+    """decode_pass plus HIP events around each weight-streaming launch; returns the number
+    of launches bracketed.
+
+    events: a list of 2 * n_stages torch.cuda.Event(enable_timing=True), already recorded
+    once (so that their HIP handles exist); events[2 i] / events[2 i + 1] bracket launch i."""
+    K = x0.shape[0]
+    arr = (_P * len(events))(*[ev.cuda_event for ev in events])
+    n = ctypes.c_int32(0)
+    _check(lib.vq_decode_pass_timed(ctypes.byref(model.desc), _ptr(x0), K, _ptr(logits), path, _ptr(ws),
+                                    ws.numel(), _stream(stream), arr, len(events), ctypes.byref(n)),
+           "vq_decode_pass_timed")
+    return n.value
 
 
 def stage_tensor(ws, addr: int, shape, dtype):

@@ -46,22 +46,18 @@ int check_matrix(const vq_matrix* W, const char* name) {
 bool use_mfma(int K, int path) {
     if (path == VQ_PATH_MFMA) return true;
     if (path == VQ_PATH_VALU) return false;
-    return K > 8;
+    return K > 4;          // measured: VALU and MFMA about even at K = 4, MFMA 2x at K = 8
 }
 
 int check_path(int K, int path) {
-    if (path < VQ_PATH_AUTO || path > VQ_PATH_MFMA) return fail(VQ_ERR_ARG, "unknown path %d", path);
+    if (path < VQ_PATH_AUTO || path > VQ_PATH_MFMA) return fail(VQ_ERR_ARG, "unknown kernel path %d", path);
     if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
     if (path == VQ_PATH_VALU && K > 8)
         return fail(VQ_ERR_UNSUPPORTED, "the VALU path is instantiated for K <= 8 (K = %d)", K);
     return VQ_OK;
 }
 
-size_t lin_ws(const vq_matrix* W, int K) {
-    // Sized for either path so one workspace serves both.
-    return std::max(lin_scratch_bytes(W->format, W->rows, W->cols, K, false),
-                    lin_scratch_bytes(W->format, W->rows, W->cols, K, true));
-}
+size_t lin_ws(const vq_matrix* W, int K) { return stage_scratch_bytes(W->rows, W->cols, K, 0, 0); }
 
 // ---------------------------------------------------------------- decode layout
 
@@ -125,8 +121,25 @@ struct DecodeLayout {
     size_t in_off[4], out_off[4];  // per stage kind within a layer block
     size_t layer_bytes;            // retention bytes per layer
     size_t final_in_off;           // x_final fp16 [K][H]
-    size_t stats_off, scratch_off, total;
+    size_t stats_off;              // per-tile sums of squares, stats_stride floats per stage
+    size_t stats_stride;
+    size_t sbuf_off;               // silu(gate) * up, f32 [K][FF], sbuf_stride floats per layer
+    size_t sbuf_stride;
+    size_t scratch_off;            // split-K partials (sized for the largest stage)
+    size_t counters_off;           // sync words: tile arrival counters [max_tiles], error
+                                   // flag, stage completion counters [stages][DONE_WORDS]
+    int max_tiles;
+    int err_word;                  // index of the error flag among the sync words
+    int done_word;                 // index of the first completion counter
+    int sync_words;
+    size_t total;
 };
+
+int stage_tiles(const Shapes& s, int st) {
+    const StageShape ss = stage_shape(s, st);
+    const int paired = (st < 4 * s.L && st % 4 == 2);
+    return stage_geom(ss.rows, ss.cols, paired, paired ? s.FF : 0).ntiles;
+}
 
 DecodeLayout decode_layout(const Shapes& s, int K) {
     DecodeLayout d{};
@@ -142,18 +155,32 @@ DecodeLayout decode_layout(const Shapes& s, int K) {
     p = d.layer_bytes * s.L;
     d.final_in_off = p;
     p += align_up((size_t)K * s.H * 2, 256);
-    d.stats_off = p;
-    const int nst = std::max(finalize_stats_blocks(2 * s.FF, 1),
-                             std::max(finalize_stats_blocks(s.H + 2 * s.KV, 0), finalize_stats_blocks(s.H, 0)));
-    p += align_up((size_t)nst * K * 4, 256);
-    d.scratch_off = p;
+    int mt = 0;
     size_t sc = 0;
     for (int j = 0; j <= 4; ++j) {
-        const StageShape ss = stage_shape(s, j == 4 ? 4 * s.L : j);
-        sc = std::max(sc, std::max(lin_scratch_bytes(s.fmt, ss.rows, ss.cols, K, false),
-                                   lin_scratch_bytes(s.fmt, ss.rows, ss.cols, K, true)));
+        const int st = j == 4 ? 4 * s.L : j;
+        const StageShape ss = stage_shape(s, st);
+        const int paired = (j == 2);
+        mt = std::max(mt, stage_tiles(s, st));
+        sc = std::max(sc, stage_scratch_bytes(ss.rows, ss.cols, K, paired, paired ? s.FF : 0));
     }
+    d.max_tiles = mt;
+    // Every buffer a later stage reads is written once per pass at its own 256-byte
+    // aligned place (no reuse between stages or layers): the persistent pass reads them
+    // through the caches while other XCDs may still be writing their neighbours.
+    d.stats_off = p;
+    d.stats_stride = align_up((size_t)mt * K * 4, 256) / 4;
+    p += d.stats_stride * 4 * (size_t)(4 * s.L);
+    d.sbuf_off = p;
+    d.sbuf_stride = align_up((size_t)K * s.FF * 4, 256) / 4;
+    p += d.sbuf_stride * 4 * (size_t)s.L;
+    d.scratch_off = p;
     p += sc;
+    d.counters_off = p;
+    d.err_word = mt;
+    d.done_word = (int)align_up((size_t)mt + 1, DONE_STRIDE);
+    d.sync_words = d.done_word + (4 * s.L + 1) * DONE_WORDS;
+    p += align_up((size_t)d.sync_words * 4, 256);
     d.total = p;
     return d;
 }
@@ -231,16 +258,19 @@ int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y, 
     if (!ws || ws_bytes < need || !aligned(ws, 256))
         return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
     const bool mfma = use_mfma(K, path);
-    const Mat M = mat_from(*W);
-    LinScratch s;
-    lin_scratch_carve(ws, W->format, W->rows, W->cols, K, mfma, &s);
+    StageArgs A{};
+    A.W = mat_from(*W);
+    A.K = K;
+    A.glue = GLUE_NONE;
+    A.x16 = (const uint16_t*)x_f16;
+    A.y = y;
+    A.y_dtype = y_dtype;
+    stage_scratch_carve(ws, W->rows, W->cols, K, 0, 0, &A);
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_prep_plain(M, (const uint16_t*)x_f16, K, mfma, s, nullptr, st);
-    if (e != hipSuccess) return hip_fail(e, "prep launch");
-    e = launch_linear_main(M, K, mfma, s, st);
+    hipError_t e = launch_zero_u32(A.counters, stage_geom(W->rows, W->cols, 0, 0).ntiles, st);
+    if (e != hipSuccess) return hip_fail(e, "counter reset launch");
+    e = launch_stage(A, mfma, st);
     if (e != hipSuccess) return hip_fail(e, "linear launch");
-    e = launch_finalize(M, K, s, y, y_dtype, st);
-    if (e != hipSuccess) return hip_fail(e, "finalize launch");
     return VQ_OK;
 }
 
@@ -303,79 +333,127 @@ int vq_decode_stage_ptr(const vq_model* M, int32_t K, void* ws, int32_t stage, v
     return VQ_OK;
 }
 
-int vq_decode_pass(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
-                   void* ws, size_t ws_bytes, void* stream) {
+int vq_decode_error_word(const vq_model* M, int32_t K, void* ws, int32_t** word) {
     g_err[0] = 0;
     Shapes s;
     int rc = check_model(M, &s);
     if (rc) return rc;
-    rc = check_path(K, path);
+    if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
+    if (!ws || !word) return fail(VQ_ERR_ARG, "NULL pointer");
+    const DecodeLayout d = decode_layout(s, K);
+    *word = (int32_t*)((char*)ws + d.counters_off) + d.err_word;
+    return VQ_OK;
+}
+
+static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
+                       void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t n_events,
+                       int32_t* n_launches) {
+    g_err[0] = 0;
+    Shapes s;
+    int rc = check_model(M, &s);
+    if (rc) return rc;
+    const int kern = path & 3, launch = path & ~3;
+    if (launch != VQ_LAUNCH_AUTO && launch != VQ_LAUNCH_STAGED && launch != VQ_LAUNCH_PERSISTENT)
+        return fail(VQ_ERR_ARG, "unknown launch mode in path %d", path);
+    rc = check_path(K, kern);
     if (rc) return rc;
     if (!x0_f16 || !logits) return fail(VQ_ERR_ARG, "NULL x0 or logits");
     if (!aligned(x0_f16, 16) || !aligned(logits, 4)) return fail(VQ_ERR_ARG, "x0 or logits misaligned");
     const DecodeLayout d = decode_layout(s, K);
     if (!ws || ws_bytes < d.total || !aligned(ws, 256))
         return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", d.total, ws_bytes);
-    const bool mfma = use_mfma(K, path);
+    const bool mfma = use_mfma(K, kern);
+    const bool persistent = launch == VQ_LAUNCH_PERSISTENT;     // AUTO: staged (measured faster)
     hipStream_t st = (hipStream_t)stream;
     char* base = (char*)ws;
-    float* stats = (float*)(base + d.stats_off);
-    void* scratch = base + d.scratch_off;
-    int nstats = 0;
-    const float* prev = nullptr;   // raw output of the previous stage
-    int prev_ld = 0;
-    hipError_t e;
-    for (int l = 0; l <= s.L; ++l) {
-        for (int j = 0; j < 4; ++j) {
-            const bool lm = (l == s.L);
-            if (lm && j > 0) break;
-            Mat W;
-            if (lm) {
-                W = mat_from(M->lm_head);
-            } else {
-                const vq_layer& y = M->layers[l];
-                if (j == 0) {
-                    const vq_matrix* m3[3] = {&y.q, &y.k, &y.v};
-                    W = mat_cat(m3, 3);
-                } else if (j == 1) {
-                    W = mat_from(y.o);
-                } else if (j == 2) {
-                    const vq_matrix* m2[2] = {&y.gate, &y.up};
-                    W = mat_cat(m2, 2);
-                } else {
-                    W = mat_from(y.down);
+    unsigned* sync = (unsigned*)(base + d.counters_off);
+    hipError_t e = launch_zero_u32(sync, d.sync_words, st);     // counters, error flag
+    if (e != hipSuccess) return hip_fail(e, "sync reset launch");
+    PassPlan P{};
+    P.fmt = s.fmt;
+    P.K = K;
+    P.H = s.H;
+    P.KV = s.KV;
+    P.FF = s.FF;
+    P.V = s.V;
+    P.L = s.L;
+    P.x0 = (const uint16_t*)x0_f16;
+    P.logits = logits;
+    P.base = base;
+    P.layer_bytes = d.layer_bytes;
+    for (int j = 0; j < 4; ++j) {
+        P.in_off[j] = d.in_off[j];
+        P.out_off[j] = d.out_off[j];
+    }
+    P.final_in_off = d.final_in_off;
+    P.stats = (float*)(base + d.stats_off);
+    P.stats_stride = d.stats_stride;
+    P.sbuf = (float*)(base + d.sbuf_off);
+    P.sbuf_stride = d.sbuf_stride;
+    P.part = (float*)(base + d.scratch_off);
+    P.counters = sync;
+    P.err = (int*)(sync + d.err_word);
+    P.done = persistent ? sync + d.done_word : nullptr;
+    P.coh = persistent ? 1 : 0;
+    P.lm = MatPtrs{M->lm_head.qs, M->lm_head.scales, M->lm_head.mins};
+    int nl = 0;
+    for (int l0 = 0; l0 < s.L; l0 += PASS_LAYERS) {
+        P.layer0 = l0;
+        P.nlayers = std::min(PASS_LAYERS, s.L - l0);
+        P.with_lm = (l0 + P.nlayers == s.L) ? 1 : 0;
+        for (int i = 0; i < P.nlayers; ++i) {
+            const vq_layer& y = M->layers[l0 + i];
+            const vq_matrix* ms[7] = {&y.q, &y.k, &y.v, &y.o, &y.gate, &y.up, &y.down};
+            for (int m = 0; m < 7; ++m) P.m[i][m] = MatPtrs{ms[m]->qs, ms[m]->scales, ms[m]->mins};
+        }
+        const int s0 = 4 * l0, s1 = 4 * (l0 + P.nlayers) + P.with_lm;
+        if (persistent) {
+            if (events && 2 * nl + 1 < n_events) {
+                e = hipEventRecord((hipEvent_t)events[2 * nl], st);
+                if (e != hipSuccess) return hip_fail(e, "event record");
+            }
+            e = launch_pass_segment(P, mfma, st);
+            if (e != hipSuccess) return hip_fail(e, "persistent pass launch");
+            if (events && 2 * nl + 1 < n_events) {
+                e = hipEventRecord((hipEvent_t)events[2 * nl + 1], st);
+                if (e != hipSuccess) return hip_fail(e, "event record");
+            }
+            ++nl;
+        } else {
+            for (int stage = s0; stage < s1; ++stage) {
+                StageArgs A;
+                build_stage(P, stage, A);
+                if (events && 2 * nl + 1 < n_events) {
+                    e = hipEventRecord((hipEvent_t)events[2 * nl], st);
+                    if (e != hipSuccess) return hip_fail(e, "event record");
                 }
+                e = launch_stage(A, mfma, st);
+                if (e != hipSuccess) return hip_fail(e, "stage launch");
+                if (events && 2 * nl + 1 < n_events) {
+                    e = hipEventRecord((hipEvent_t)events[2 * nl + 1], st);
+                    if (e != hipSuccess) return hip_fail(e, "event record");
+                }
+                ++nl;
             }
-            LinScratch sc;
-            lin_scratch_carve(scratch, s.fmt, W.rows, W.cols, K, mfma, &sc);
-            uint16_t* keep = (uint16_t*)(lm ? base + d.final_in_off
-                                            : base + (size_t)l * d.layer_bytes + d.in_off[j]);
-            float* out = lm ? logits : (float*)(base + (size_t)l * d.layer_bytes + d.out_off[j]);
-            // input: x0, rho(previous output) or rho(silu(gate) * up)
-            if (l == 0 && j == 0) {
-                e = launch_prep_plain(W, (const uint16_t*)x0_f16, K, mfma, sc, keep, st);
-            } else if (j == 3) {
-                e = launch_prep_glue(W, prev, prev_ld, s.FF, GLUE_RHO_SILU, stats, nstats, K, mfma, keep, sc, st);
-            } else {
-                e = launch_prep_glue(W, prev, prev_ld, 0, GLUE_RHO, stats, nstats, K, mfma, keep, sc, st);
-            }
-            if (e != hipSuccess) return hip_fail(e, "prep launch");
-            e = launch_linear_main(W, K, mfma, sc, st);
-            if (e != hipSuccess) return hip_fail(e, "linear launch");
-            if (lm) {
-                e = launch_finalize(W, K, sc, out, VQ_DTYPE_F32, st);
-            } else {
-                const int silu = (j == 2) ? 1 : 0;
-                const int nstat = (j == 0) ? s.H : W.rows;
-                e = launch_finalize_stats(W, K, sc, out, nstat, silu, stats, st);
-                nstats = finalize_stats_blocks(W.rows, silu);
-            }
-            if (e != hipSuccess) return hip_fail(e, "finalize launch");
-            prev = out;
-            prev_ld = W.rows;
         }
     }
+    if (n_launches) *n_launches = nl;
     return VQ_OK;
+}
+
+int vq_decode_pass(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
+                   void* ws, size_t ws_bytes, void* stream) {
+    return decode_impl(M, x0_f16, K, logits, path, ws, ws_bytes, stream, nullptr, 0, nullptr);
+}
+
+int vq_decode_pass_timed(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
+                         void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t n_events,
+                         int32_t* n_launches) {
+    if (!events || n_events < 2 * (4 * (M ? M->n_layers : 0) + 1))
+        return fail(VQ_ERR_ARG, "events must hold two HIP events per stage (begin, end)");
+    for (int i = 0; i < n_events; ++i)
+        if (!events[i]) return fail(VQ_ERR_ARG, "event %d is NULL", i);
+    return decode_impl(M, x0_f16, K, logits, path, ws, ws_bytes, stream, events, n_events, n_launches);
 }
 
 }  // extern "C"

@@ -3,28 +3,38 @@
 // Decode reads every weight once per pass and multiplies it against the activation
 // vector (page "100 tokens per second from a 27B model on a 24 GB AMD card", section
 // "The wall"); verification applies the same single read to K activation columns
-// (same page, section "How speculative decoding gets past a per-token wall").
+// (same page, section "How speculative decoding gets past a per-token wall"), layer by
+// layer (Hacker News thread 49596054).
 //
-// Two kernels share one work decomposition: a workgroup of 4 waves owns a 64-row tile
-// and a chunk of 4 groups of 8 blocks (256 input columns per wave).  Each wave reads
-// its 64 rows x 256 columns of 4-bit codes exactly once, with 16-byte loads, and the
-// four waves' partial sums are combined in LDS in a fixed order.  Chunks of one tile
-// are written as split-K partials and summed in fixed order by the finalize kernel,
-// so results are bitwise reproducible.
+// One launch per stage.  A workgroup of 4 waves owns a 64-row tile and a chunk of 4
+// groups of 8 quantisation blocks (one group of 256 input columns per wave):
+//  * prologue: the wave issues all of its weight loads first (unconditional loads from
+//    clamped addresses, so they are all in flight at once), then builds its K activation
+//    columns in registers -- either the fp16 input, or the previous stage's raw output
+//    scaled to unit RMS per column and rounded to fp16 (the RMS comes from per-tile sums
+//    of squares the previous stage wrote);
+//  * the dot products (VALU or MFMA, below);
+//  * epilogue: the four waves' partials are combined in LDS in a fixed order; with more
+//    than one chunk per tile, each chunk writes its partial and the last workgroup to
+//    arrive at the tile's counter sums the chunks in chunk order, writes y and the tile's
+//    sums of squares, and resets the counter.  Results are bitwise reproducible.
 //
-//  * VALU kernel (K <= 8): lane = weight row, all 64 lanes at the same input columns,
-//    so the activations are wave-uniform and feed v_dot2_f32_f16 from scalar
-//    registers.  Codes are widened to exact fp16 q = n - 8 with the 0x6400 exponent
-//    trick (two nibbles per instruction); the block scale and min are applied once
-//    per 32 columns: y += d * sum(q x) + m * sum(x).
-//  * MFMA kernel (K <= 16): v_mfma_f32_16x16x32_f16 with the weights as the B operand
-//    (16 rows x 32 columns = one quantisation block per instruction) and the K
-//    activation columns, zero-padded to 16, as A.  A lane loads a whole block of one
-//    row (16 bytes); permlane32/permlane16 swaps transpose 4 lanes' blocks into the
-//    k-quarters the MFMA expects.  Each block's product is scaled by its fp16 scale
-//    on the accumulator; the min term sum_b m_b * sum(x_b) is one more MFMA per
-//    8 blocks with the block sums split into fp16 hi + lo parts.
+//  * VALU kernel (K <= 8): lane 8s + c owns block c of the wave's group for rows
+//    8i + s (i = 0..7): each load instruction covers 8 rows x 128 contiguous bytes.  The
+//    lane keeps its block's activations in VGPRs; codes are widened to exact fp16
+//    q = n - 8 (0x6400 exponent trick, two nibbles per instruction) and fed to
+//    v_dot2_f32_f16; per block y += d * sum(q x) + m * sum(x); the 8 block partials of a
+//    row are summed across lanes with DPP.
+//  * MFMA kernel (K <= 16): v_mfma_f32_16x16x32_f16 with the weights as B (16 rows x 32
+//    columns = one quantisation block per instruction) and the K activation columns,
+//    zero-padded to 16, as A.  A lane loads a whole block of one row (16 bytes);
+//    permlane32/permlane16 swaps transpose 4 lanes' blocks into the k-quarters the MFMA
+//    expects.  Each block's product is scaled by its scale on the accumulator; the min
+//    term sum_b m_b * sum(x_b) is one more MFMA per 8 blocks with the block sums split
+//    into fp16 hi + lo parts.
 #include <hip/hip_fp16.h>
+
+#include <type_traits>
 
 #include "vq_internal.h"
 
@@ -37,10 +47,14 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
-__device__ __forceinline__ uint32_t h2_bits(h2_t h) { return __builtin_bit_cast(uint32_t, h); }
+__device__ __forceinline__ h8_t as_h8(u4_t v) { return __builtin_bit_cast(h8_t, v); }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ uint32_t f2h_bits(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);   // round to nearest even
 }
 
 // E8M0 (OCP MX v1.0): 2^(E-127); E = 0 is 2^-127 (an fp32 subnormal), E = 255 NaN.
@@ -84,156 +98,413 @@ __device__ __forceinline__ void unpack8(uint32_t w, h2_t (&p)[4]) {
     else unpack_q4(w, p);
 }
 
-// Position of column c (0..7) of an 8-column group in the widened order above.
-__host__ __device__ __forceinline__ int q4_slot(int c) { return (c & 3) * 2 + (c >> 2); }
+// Column held by slot p (0..7) of an 8-column group in the widened order above.
+template <int FMT>
+__device__ __forceinline__ int slot_col(int p) {
+    if constexpr (FMT == VQ_FMT_MXFP4) return p;
+    else return (p >> 1) + 4 * (p & 1);
+}
 
-// Scales (and mins) of blocks [rb, rb + nvb) of one row; rb = row * nb + b0.
-template <int FMT, bool AL>
-__device__ __forceinline__ void load_scales(const void* scales, const uint16_t* mins, size_t rb,
-                                            int nvb, float (&d)[8], float (&m)[8]) {
-    if constexpr (FMT == VQ_FMT_MXFP4) {
-        const uint8_t* s = (const uint8_t*)scales + rb;
-        if (AL) {
-            const uint2 v = *reinterpret_cast<const uint2*>(s);
+// Work item of workgroup `id` in a 1-D grid of n items.  Workgroups are dealt to the
+// 8 XCDs round-robin by id; id -> (id % 8) * (n / 8) + id / 8 gives each XCD a run of
+// consecutive items, so the chunks of one row tile (which share the lines holding the
+// tile's block scales and mins) meet in one L2 and are in flight together.
+__device__ __forceinline__ int xcd_item(int id, int n) {
+    const int full = n & ~7;
+    if (id >= full) return id;
+    return (id & 7) * (full >> 3) + (id >> 3);
+}
+
+// Sum over the 8 lanes 8s..8s+7 (a fixed butterfly: every lane gets the same result).
+__device__ __forceinline__ float sum8(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    return v;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Data one workgroup writes and another reads within the same launch (the persistent
+// pass) is stored with device-scope relaxed atomics, which write through to memory past
+// the XCD's own L2.  The readers use plain loads: every such buffer is written once per
+// pass at an address no workgroup has read since the launch began (the launch starts
+// with clean caches), so a load cannot hit a stale line, and after the first miss the
+// XCD's other workgroups find the line in their L2.
+__device__ __forceinline__ void st_shared_f32(float* p, float v, bool coh) {
+    if (coh) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *p = v;
+}
+
+// ------------------------------------------------------------------ rows of a tile
+
+// Output row of local row r (0..63) of tile t.  Paired stages (gate|up) put rows
+// [32t, 32t + 32) of segment 0 in r < 32 and the same rows of segment 1 in r >= 32, so
+// one tile holds both factors of silu(gate) * up.
+__device__ __forceinline__ int out_row(const StageArgs& A, int t, int r) {
+    if (A.paired) return (r < 32 ? 0 : A.W.seg_end[0]) + 32 * t + (r & 31);
+    return 64 * t + r;
+}
+
+__device__ __forceinline__ bool row_ok(const StageArgs& A, int t, int r) {
+    if (A.paired) return 32 * t + (r & 31) < A.W.seg_end[0];
+    return 64 * t + r < A.W.rows;
+}
+
+// A valid row standing in for (t, r): r itself, or the last row of its segment range.
+__device__ __forceinline__ int clamp_row(const StageArgs& A, int t, int r) {
+    if (A.paired) return (r < 32 ? 0 : A.W.seg_end[0]) + min(32 * t + (r & 31), A.W.seg_end[0] - 1);
+    return min(64 * t + r, A.W.rows - 1);
+}
+
+struct RowPtr {
+    const uint8_t* qs;       // start of the row's codes
+    const uint8_t* sc8;      // start of the row's scales (bytes)
+    const uint16_t* mn;      // start of the row's mins (or NULL)
+};
+
+// Segment of the rows that local row r of tile t reads: uniform over a wave, because the
+// boundaries of a multi-segment matrix are multiples of 64 rows and a paired tile takes
+// rows r < 32 from segment 0 and r >= 32 from segment 1.
+__device__ __forceinline__ int tile_seg(const StageArgs& A, int t, int r) {
+    if (A.paired) return r < 32 ? 0 : 1;
+    const int row0 = 64 * t;
+    return __builtin_amdgcn_readfirstlane(
+        (A.W.nseg > 2 && row0 >= A.W.seg_end[1]) ? 2 : (A.W.nseg > 1 && row0 >= A.W.seg_end[0]) ? 1 : 0);
+}
+
+// Makes a value opaque to the optimiser.  The segment select below would otherwise be
+// turned into an indexed load, which forces a Mat held in registers (the persistent pass
+// builds one per stage) out to scratch memory.
+template <typename T>
+__device__ __forceinline__ T opaque(T v) {
+    asm volatile("" : "+r"(v));
+    return v;
+}
+
+// Row pointers of `row`, which lies in segment `seg` (uniform).
+__device__ __forceinline__ RowPtr row_ptr(const Mat& W, int seg, int row) {
+    const uint8_t* q[3] = {opaque(W.qs[0]), opaque(W.qs[1]), opaque(W.qs[2])};
+    const void* c[3] = {opaque(W.scales[0]), opaque(W.scales[1]), opaque(W.scales[2])};
+    const uint16_t* m[3] = {opaque(W.mins[0]), opaque(W.mins[1]), opaque(W.mins[2])};
+    const int e0 = opaque(W.seg_end[0]), e1 = opaque(W.seg_end[1]);
+    const uint8_t* qs = seg == 2 ? q[2] : seg == 1 ? q[1] : q[0];
+    const void* sc = seg == 2 ? c[2] : seg == 1 ? c[1] : c[0];
+    const uint16_t* mn = seg == 2 ? m[2] : seg == 1 ? m[1] : m[0];
+    const int r0 = seg == 2 ? e1 : seg == 1 ? e0 : 0;
+    const size_t lr = (size_t)(row - r0);
+    const size_t nb = (size_t)(W.cols >> 5);
+    RowPtr p;
+    p.qs = qs + lr * (size_t)(W.cols >> 1);
+    p.sc8 = (const uint8_t*)sc + lr * nb * (W.fmt == VQ_FMT_MXFP4 ? 1 : 2);
+    p.mn = mn ? mn + lr * nb : nullptr;
+    return p;
+}
+
+// ------------------------------------------------------------------ stage glue
+
+// rs[k] = 1 / sqrt(sum_i stats_in[i][k] / n_in): per-column inverse RMS of the previous
+// stage's output, from its per-tile sums of squares (summed in a fixed order).
+__device__ void stage_rms(const StageArgs& A, float* rs, float* sh) {
+    if (A.glue == GLUE_NONE) return;
+    const int K = A.K;
+    float acc[VQ_MAX_K];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                d[i] = e8m0_to_float((v.x >> (8 * i)) & 0xffu);
-                d[i + 4] = e8m0_to_float((v.y >> (8 * i)) & 0xffu);
-            }
-        } else {
+    for (int k = 0; k < VQ_MAX_K; ++k) acc[k] = 0.f;
+    for (int i = threadIdx.x; i < A.nstats_in; i += 256)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) d[i] = i < nvb ? e8m0_to_float(s[i]) : 0.f;
+        for (int k = 0; k < VQ_MAX_K; ++k)
+            if (k < K) acc[k] += A.stats_in[(size_t)i * K + k];
+    for (int k = 0; k < K; ++k) sh[k * 256 + threadIdx.x] = acc[k];
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+        if (threadIdx.x < (unsigned)st)
+            for (int k = 0; k < K; ++k) sh[k * 256 + threadIdx.x] += sh[k * 256 + threadIdx.x + st];
+        __syncthreads();
+    }
+    if (threadIdx.x < (unsigned)K)
+        rs[threadIdx.x] = 1.0f / __fsqrt_rn(__fdiv_rn(sh[threadIdx.x * 256], (float)A.n_in));
+    __syncthreads();
+}
+
+// Input activations (k, col .. col + 7) as fp16 bits: the fp16 input, or fp16(v * rs[k])
+// of the raw previous output v.
+__device__ __forceinline__ void load_x8(const StageArgs& A, const float* rs, int k, int col,
+                                        uint32_t (&h)[8]) {
+    if (A.glue == GLUE_NONE) {
+        const u4_t v = *reinterpret_cast<const u4_t*>(A.x16 + (size_t)k * A.W.cols + col);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h[2 * e] = v[e] & 0xffffu;
+            h[2 * e + 1] = v[e] >> 16;
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) m[i] = 0.f;
     } else {
-        const uint16_t* s = (const uint16_t*)scales + rb;
-        if (AL) {
-            const uint4 v = *reinterpret_cast<const uint4*>(s);
-            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+        const float* p = A.src + (size_t)k * A.ld + col;
+        const f4_t a = *reinterpret_cast<const f4_t*>(p), b = *reinterpret_cast<const f4_t*>(p + 4);
+        const float r = rs[k];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                d[2 * i] = half_bits_to_float(vv[i] & 0xffffu);
-                d[2 * i + 1] = half_bits_to_float(vv[i] >> 16);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) d[i] = i < nvb ? half_bits_to_float(s[i]) : 0.f;
-        }
-        if constexpr (FMT == VQ_FMT_Q4_MIN) {
-            const uint16_t* mm = mins + rb;
-            if (AL) {
-                const uint4 v = *reinterpret_cast<const uint4*>(mm);
-                const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    m[2 * i] = half_bits_to_float(vv[i] & 0xffffu);
-                    m[2 * i + 1] = half_bits_to_float(vv[i] >> 16);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) m[i] = i < nvb ? half_bits_to_float(mm[i]) : 0.f;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) m[i] = 0.f;
+        for (int e = 0; e < 4; ++e) {
+            h[e] = f2h_bits(a[e] * r);
+            h[4 + e] = f2h_bits(b[e] * r);
         }
     }
 }
 
+__device__ __forceinline__ void keep_x8(const StageArgs& A, int k, int col, const uint32_t (&h)[8]) {
+    u4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = h[2 * e] | (h[2 * e + 1] << 16);
+    *reinterpret_cast<u4_t*>(A.keep + (size_t)k * A.W.cols + col) = v;
+}
 
-// Segment of the 64-row tile starting at row r0 (tiles never straddle segments).
-struct SegRef {
-    const uint8_t* qs;
-    const void* scales;
-    const uint16_t* mins;
-    int row0;   // first row of the segment
-};
+// ------------------------------------------------------------------ epilogue
 
-__device__ __forceinline__ SegRef seg_of(const Mat& W, int r0) {
-    int s = 0;
-    if (W.nseg > 1 && r0 >= W.seg_end[0]) s = 1;
-    if (W.nseg > 2 && r0 >= W.seg_end[1]) s = 2;
-    SegRef g;
-    g.qs = W.qs[s];
-    g.scales = W.scales[s];
-    g.mins = W.mins[s];
-    g.row0 = s ? W.seg_end[s - 1] : 0;
-    return g;
+// red[w][k][l] (w < 4 waves, k < K, l < 64 local rows) holds this workgroup's partials
+// for (tile, chunk).  Writes y (and the tile's sums of squares) once all chunks of the
+// tile are in.
+__device__ void stage_epilogue(const StageArgs& A, int tile, int chunk, int nchunks,
+                               float (*red)[16][65], float (*fin)[64], int* s_last) {
+    const int K = A.K, rows = A.W.rows;
+    for (int e = threadIdx.x; e < K * 64; e += 256) {
+        const int k = e >> 6, l = e & 63;
+        fin[k][l] = ((red[0][k][l] + red[1][k][l]) + red[2][k][l]) + red[3][k][l];
+    }
+    __syncthreads();
+    if (nchunks > 1) {
+        // Partials, the counter and the last arriver's reads all use device-scope relaxed
+        // atomics, which gfx950 performs coherently across XCDs without flushing or
+        // invalidating the L2; s_waitcnt 0 makes each thread's partial stores complete
+        // before the workgroup's arrival is counted.
+        for (int e = threadIdx.x; e < K * 64; e += 256) {
+            const int k = e >> 6, l = e & 63;
+            if (row_ok(A, tile, l))
+                __hip_atomic_store(&A.part[((size_t)chunk * K + k) * rows + out_row(A, tile, l)], fin[k][l],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x == 0)
+            *s_last = __hip_atomic_fetch_add(&A.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                      (unsigned)(nchunks - 1);
+        __syncthreads();
+        if (!*s_last) return;
+        for (int e = threadIdx.x; e < K * 64; e += 256) {
+            const int k = e >> 6, l = e & 63;
+            float v = 0.f;
+            if (row_ok(A, tile, l)) {
+                const int row = out_row(A, tile, l);
+                for (int c = 0; c < nchunks; ++c)
+                    v += __hip_atomic_load(&A.part[((size_t)c * K + k) * rows + row], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            }
+            fin[k][l] = v;
+        }
+        if (threadIdx.x == 0) __hip_atomic_store(&A.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+    }
+    for (int e = threadIdx.x; e < K * 64; e += 256) {
+        const int k = e >> 6, l = e & 63;
+        if (!row_ok(A, tile, l)) continue;
+        const size_t o = (size_t)k * rows + out_row(A, tile, l);
+        if (A.y_dtype == VQ_DTYPE_F16)
+            reinterpret_cast<uint16_t*>(A.y)[o] = (uint16_t)f2h_bits(fin[k][l]);
+        else
+            st_shared_f32(reinterpret_cast<float*>(A.y) + o, fin[k][l], A.coh);
+    }
+    if (A.stats_out && threadIdx.x < (unsigned)K) {
+        const int k = threadIdx.x;
+        float ss = 0.f;
+        if (A.paired) {
+            const int half = A.W.seg_end[0];
+            for (int l = 0; l < 32; ++l) {
+                if (!row_ok(A, tile, l)) break;
+                const float v = silu_mul(fin[k][l], fin[k][32 + l]);
+                st_shared_f32(A.sbuf + (size_t)k * half + 32 * tile + l, v, A.coh);
+                ss += v * v;
+            }
+        } else {
+            for (int l = 0; l < 64; ++l) {
+                const int row = 64 * tile + l;
+                if (row < A.nstat && row < rows) ss += fin[k][l] * fin[k][l];
+            }
+        }
+        st_shared_f32(A.stats_out + (size_t)tile * K + k, ss, A.coh);
+    }
+    if (A.done) {
+        // the tile's outputs are in memory before the completion counters count it
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (threadIdx.x < (unsigned)DONE_REPL)
+            __hip_atomic_fetch_add(A.done + threadIdx.x * DONE_STRIDE, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // ------------------------------------------------------------------ VALU kernel
 
-template <int FMT, int K, bool AL>
-__global__ __launch_bounds__(256) void k_lin_valu(const Mat W, const uint32_t* __restrict__ xp,
-                                                  const float* __restrict__ bsum,
-                                                  float* __restrict__ part) {
-    __shared__ float red[4][K][64];
-    const int rows = W.rows, cols = W.cols;
-    const SegRef sg = seg_of(W, blockIdx.x * 64);
-    const int nb = cols >> 5;
-    const int ngroups = (nb + 7) >> 3;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int grp = blockIdx.y * 4 + wave;
-    const int row = blockIdx.x * 64 + lane;
-    const int hc = cols >> 1;
-    float acc[K];
+// One wave's share of a 64-row tile: 8 rows x one block per lane.
+struct WTileV {
+    u4_t w[8];
+    uint32_t sr[8], mr[8];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_tile_valu(const StageArgs& A, int tile, int s, int bcl, WTileV& T) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) acc[k] = 0.f;
-    if (grp < ngroups && row < rows) {
-        const int b0 = grp * 8;
-        const int nvb = min(8, nb - b0);
-        const int lr = row - sg.row0;
-        const u4_t* qp = reinterpret_cast<const u4_t*>(sg.qs + (size_t)lr * (size_t)hc) + b0;
-        u4_t w[8];
+    for (int i = 0; i < 8; ++i) {
+        const RowPtr rp = row_ptr(A.W, tile_seg(A, tile, 8 * i), clamp_row(A, tile, 8 * i + s));
+        T.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u4_t*>(rp.qs) + bcl);
+        if constexpr (FMT == VQ_FMT_MXFP4) {
+            T.sr[i] = rp.sc8[bcl];
+            T.mr[i] = 0u;
+        } else {
+            T.sr[i] = reinterpret_cast<const uint16_t*>(rp.sc8)[bcl];
+            T.mr[i] = FMT == VQ_FMT_Q4_MIN ? (uint32_t)rp.mn[bcl] : 0u;
+        }
+    }
+}
+
+template <int FMT, int K>
+__device__ __forceinline__ void compute_tile_valu(const StageArgs& A, int tile, int s, bool live, const WTileV& T,
+                                                  const uint32_t (&xv)[K][16], const float (&bs)[K],
+                                                  float (&out)[K][8]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (i < nvb) w[i] = __builtin_nontemporal_load(qp + i);
-        float d[8], m[8];
-        load_scales<FMT, AL>(sg.scales, sg.mins, (size_t)lr * nb + b0, nvb, d, m);
+    for (int i = 0; i < 8; ++i) {
+        float t[K];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (i < nvb) {
-                const int b = b0 + i;
-                const uint32_t wd[4] = {w[i][0], w[i][1], w[i][2], w[i][3]};
-                float t[K];
+        for (int k = 0; k < K; ++k) t[k] = 0.f;
 #pragma unroll
-                for (int k = 0; k < K; ++k) t[k] = 0.f;
+        for (int q = 0; q < 4; ++q) {
+            h2_t p[4];
+            unpack8<FMT>(T.w[i][q], p);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    h2_t p[4];
-                    unpack8<FMT>(wd[q], p);
-#pragma unroll
-                    for (int k = 0; k < K; ++k) {
-                        const uint4 xv = *reinterpret_cast<const uint4*>(
-                            xp + (size_t)k * hc + (size_t)b * 16 + q * 4);
-                        t[k] = __builtin_amdgcn_fdot2(p[0], as_h2(xv.x), t[k], false);
-                        t[k] = __builtin_amdgcn_fdot2(p[1], as_h2(xv.y), t[k], false);
-                        t[k] = __builtin_amdgcn_fdot2(p[2], as_h2(xv.z), t[k], false);
-                        t[k] = __builtin_amdgcn_fdot2(p[3], as_h2(xv.w), t[k], false);
-                    }
-                }
-#pragma unroll
-                for (int k = 0; k < K; ++k) acc[k] = fmaf(d[i], t[k], acc[k]);
-                if constexpr (FMT == VQ_FMT_Q4_MIN) {
-#pragma unroll
-                    for (int k = 0; k < K; ++k) acc[k] = fmaf(m[i], bsum[(size_t)k * nb + b], acc[k]);
-                }
+            for (int k = 0; k < K; ++k) {
+                t[k] = __builtin_amdgcn_fdot2(p[0], as_h2(xv[k][4 * q]), t[k], false);
+                t[k] = __builtin_amdgcn_fdot2(p[1], as_h2(xv[k][4 * q + 1]), t[k], false);
+                t[k] = __builtin_amdgcn_fdot2(p[2], as_h2(xv[k][4 * q + 2]), t[k], false);
+                t[k] = __builtin_amdgcn_fdot2(p[3], as_h2(xv[k][4 * q + 3]), t[k], false);
             }
         }
-    }
+        const bool ok = live && row_ok(A, tile, 8 * i + s);
+        float d = FMT == VQ_FMT_MXFP4 ? e8m0_to_float(T.sr[i]) : half_bits_to_float(T.sr[i]);
+        float m = half_bits_to_float(T.mr[i]);
+        d = ok ? d : 0.f;
+        m = ok ? m : 0.f;
 #pragma unroll
-    for (int k = 0; k < K; ++k) red[wave][k][lane] = acc[k];
-    __syncthreads();
-    for (int e = threadIdx.x; e < K * 64; e += 256) {
-        const int k = e >> 6, l = e & 63;
-        const int r = blockIdx.x * 64 + l;
-        if (r < rows) {
-            const float s = ((red[0][k][l] + red[1][k][l]) + red[2][k][l]) + red[3][k][l];
-            part[((size_t)blockIdx.y * K + k) * (size_t)rows + r] = s;
+        for (int k = 0; k < K; ++k) {
+            float v = d * t[k];
+            if constexpr (FMT == VQ_FMT_Q4_MIN) v = fmaf(m, bs[k], v);
+            out[k][i] = sum8(v);
         }
     }
+}
+
+// LDS of one stage item (a 64-row tile x one chunk).
+struct StageSmem {
+    float red[4][16][65];          // the 4 waves' partials; also the RMS reduction scratch
+    float fin[VQ_MAX_K][64];
+    float rs[VQ_MAX_K];
+    int last;
+};
+
+// One item: a 64-row tile x one chunk (4 groups of 8 blocks, one group per wave).
+// Lane 8s + c owns block c of the wave's group for rows 8i + s of the tile.
+// The weights of item (tile, chunk) for this lane: issued ahead of the item, so that
+// their latency overlaps other work (the previous item's epilogue, a wait for inputs).
+template <int FMT>
+__device__ __forceinline__ void prefetch_valu(const StageArgs& A, int tile, int chunk, WTileV& T) {
+    const int nb = A.W.cols >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int b = (chunk * 4 + wave) * 8 + (lane & 7);
+    load_tile_valu<FMT>(A, tile, lane >> 3, b < nb ? b : nb - 1, T);
+}
+
+// rs (sm.rs) must hold the stage's input scales (stage_rms); mid() runs once the item's
+// weights are consumed, before its epilogue.
+template <int FMT, int K, typename F>
+__device__ void stage_item_valu(const StageArgs& A, int tile, int chunk, int nchunks, StageSmem& sm,
+                                uint2 (&xs)[4][K][8][8], const WTileV& cur, F&& mid) {
+    float (*red)[16][65] = sm.red;
+    float (*fin)[64] = sm.fin;
+    const float* rs = sm.rs;
+    const int nb = A.W.cols >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int s = lane >> 3, c = lane & 7;
+    const int b = (chunk * 4 + wave) * 8 + c;
+    const bool live = b < nb;
+    const int bcl = live ? b : nb - 1;
+
+    // The K activation columns of the wave's 8 blocks: lane (s, c) converts elements
+    // 4s..4s+3 of block c and the wave shares them through LDS; each lane then holds its
+    // block's 32 activations per column in the widened pair order.
+    const bool keeper = A.keep && tile == 0 && live;
+    float bs[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        uint32_t h[4];
+        const int col = 32 * bcl + 4 * s;
+        if (A.glue == GLUE_NONE) {
+            const uint2 v = *reinterpret_cast<const uint2*>(A.x16 + (size_t)k * A.W.cols + col);
+            h[0] = v.x & 0xffffu; h[1] = v.x >> 16; h[2] = v.y & 0xffffu; h[3] = v.y >> 16;
+        } else {
+            const f4_t v = *reinterpret_cast<const f4_t*>(A.src + (size_t)k * A.ld + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = f2h_bits(v[e] * rs[k]);
+        }
+        const uint2 pk = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        xs[wave][k][c][s] = pk;
+        if (keeper) *reinterpret_cast<uint2*>(A.keep + (size_t)k * A.W.cols + col) = pk;
+        float sum = (half_bits_to_float(h[0]) + half_bits_to_float(h[1])) +
+                    (half_bits_to_float(h[2]) + half_bits_to_float(h[3]));
+        sum += __shfl_xor(sum, 8, 64);
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        bs[k] = live ? sum : 0.f;
+    }
+    __syncthreads();
+    uint32_t xv[K][16];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        uint32_t h[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint2 v = xs[wave][k][c][q];
+            h[4 * q] = v.x & 0xffffu; h[4 * q + 1] = v.x >> 16;
+            h[4 * q + 2] = v.y & 0xffffu; h[4 * q + 3] = v.y >> 16;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t lo = h[8 * g + slot_col<FMT>(2 * t)], hi = h[8 * g + slot_col<FMT>(2 * t + 1)];
+                xv[k][4 * g + t] = live ? (lo | (hi << 16)) : 0u;
+            }
+    }
+    float out[K][8];
+    compute_tile_valu<FMT, K>(A, tile, s, live, cur, xv, bs, out);
+    if (c == 0) {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) red[wave][k][8 * i + s] = out[k][i];
+    }
+    mid();
+    __syncthreads();
+    stage_epilogue(A, tile, chunk, nchunks, red, fin, &sm.last);
+}
+
+template <int FMT, int K>
+__global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, int nchunks) {
+    __shared__ StageSmem sm;
+    __shared__ uint2 xs[4][K][8][8];          // [wave][column][block][quarter of 4 fp16]
+    const int item = xcd_item(blockIdx.x, gridDim.x);
+    const int tile = item / nchunks, chunk = item - tile * nchunks;
+    WTileV cur;
+    prefetch_valu<FMT>(A, tile, chunk, cur);
+    stage_rms(A, sm.rs, &sm.red[0][0][0]);
+    stage_item_valu<FMT, K>(A, tile, chunk, nchunks, sm, xs, cur, [] {});
 }
 
 // ------------------------------------------------------------------ MFMA kernel
@@ -269,465 +540,371 @@ __device__ __forceinline__ h8_t widen_block_quarter(uint32_t w) {
     return r;
 }
 
-__device__ __forceinline__ h8_t as_h8(uint4 v) { return __builtin_bit_cast(h8_t, v); }
+// One wave's share of a 64-row tile: 4 sub-tiles of 16 rows x 8 blocks.
+struct WTileM {
+    u4_t n0[4], n1[4];       // blocks b0 + g and b0 + 4 + g of row j of each sub-tile
+    uint32_t sv[4][4];       // scales of blocks b0..b0+7 (8 fp16 or 8 E8M0 bytes)
+    uint32_t mv[4][4];       // mins of blocks b0..b0+7 (8 fp16)
+};
 
-template <int FMT, bool AL>
-__global__ __launch_bounds__(256) void k_lin_mfma(const Mat W, const uint4* __restrict__ afrag,
-                                                  const uint4* __restrict__ mfrag,
-                                                  float* __restrict__ part, int K) {
-    __shared__ float red[4][16][65];
-    const int rows = W.rows, cols = W.cols;
-    const SegRef sg = seg_of(W, blockIdx.x * 64);
-    const int nb = cols >> 5;
-    const int ngroups = (nb + 7) >> 3;
+template <int FMT>
+__device__ __forceinline__ void load_tile_mfma(const StageArgs& A, int tile, int j, int gq, int b0, int nvb,
+                                               bool al, WTileM& T) {
+    const int nb = A.W.cols >> 5;
+    const int bb0 = min(b0, nb - 1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const RowPtr rp = row_ptr(A.W, tile_seg(A, tile, 16 * t), clamp_row(A, tile, 16 * t + j));
+        T.n0[t] = reinterpret_cast<const u4_t*>(rp.qs)[min(b0 + gq, nb - 1)];
+        T.n1[t] = reinterpret_cast<const u4_t*>(rp.qs)[min(b0 + 4 + gq, nb - 1)];
+        if (al && nvb == 8) {
+            if constexpr (FMT == VQ_FMT_MXFP4) {
+                const uint2 v = *reinterpret_cast<const uint2*>(rp.sc8 + b0);
+                T.sv[t][0] = v.x;
+                T.sv[t][1] = v.y;
+                T.sv[t][2] = T.sv[t][3] = 0u;
+            } else {
+                const u4_t v = *reinterpret_cast<const u4_t*>(rp.sc8 + 2 * b0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) T.sv[t][e] = v[e];
+            }
+            if constexpr (FMT == VQ_FMT_Q4_MIN) {
+                const u4_t v = *reinterpret_cast<const u4_t*>(rp.mn + b0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) T.mv[t][e] = v[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) T.mv[t][e] = 0u;
+            }
+        } else {
+            // ragged group: one element load per block
+            uint32_t sb[8], mb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int bb = min(bb0 + i, nb - 1);
+                if constexpr (FMT == VQ_FMT_MXFP4) sb[i] = rp.sc8[bb];
+                else sb[i] = reinterpret_cast<const uint16_t*>(rp.sc8)[bb];
+                mb[i] = FMT == VQ_FMT_Q4_MIN ? (uint32_t)rp.mn[bb] : 0u;
+                if (i >= nvb) sb[i] = mb[i] = 0u;
+            }
+            if constexpr (FMT == VQ_FMT_MXFP4) {
+                T.sv[t][0] = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
+                T.sv[t][1] = sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24);
+                T.sv[t][2] = T.sv[t][3] = 0u;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) T.sv[t][e] = sb[2 * e] | (sb[2 * e + 1] << 16);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) T.mv[t][e] = mb[2 * e] | (mb[2 * e + 1] << 16);
+        }
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void compute_tile_mfma(const WTileM& T, int gq, int nvb, const h8_t (&a)[8], h8_t am,
+                                                  f4_t (&acc)[4]) {
+    const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        acc[t] = zero;
+        uint32_t T0[4] = {T.n0[t][0], T.n0[t][1], T.n0[t][2], T.n0[t][3]};
+        uint32_t T1[4] = {T.n1[t][0], T.n1[t][1], T.n1[t][2], T.n1[t][3]};
+        transpose4(T0);
+        transpose4(T1);
+        float d[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if constexpr (FMT == VQ_FMT_MXFP4) d[i] = e8m0_to_float((T.sv[t][i >> 2] >> (8 * (i & 3))) & 0xffu);
+            else d[i] = half_bits_to_float((T.sv[t][i >> 1] >> (16 * (i & 1))) & 0xffffu);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            if (tt < nvb) {
+                const h8_t B = widen_block_quarter<FMT>(tt < 4 ? T0[tt] : T1[tt - 4]);
+                const f4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], B, zero, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(d[tt], D[v], acc[t][v]);
+            }
+        }
+        if constexpr (FMT == VQ_FMT_Q4_MIN) {
+            u4_t mm;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mm[e] = gq < 2 ? T.mv[t][e] : 0u;
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, as_h8(mm), acc[t], 0, 0, 0);
+        }
+    }
+}
+
+// One item: a 64-row tile (4 sub-tiles of 16 rows) x one chunk (4 groups of 8 blocks,
+// one per wave).  Lane (j = lane % 16, g = lane / 16): weight row j of a sub-tile and
+// k-quarter g of each block; as the A operand, activation column j.
+template <int FMT>
+__device__ __forceinline__ void prefetch_mfma(const StageArgs& A, int tile, int chunk, WTileM& T) {
+    const int nb = A.W.cols >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int b0 = (chunk * 4 + wave) * 8;
+    load_tile_mfma<FMT>(A, tile, lane & 15, lane >> 4, b0, max(0, min(8, nb - b0)), (nb & 7) == 0, T);
+}
+
+// As stage_item_valu: sm.rs holds the input scales, mid() runs before the epilogue.
+template <int FMT, typename F>
+__device__ void stage_item_mfma(const StageArgs& A, int tile, int chunk, int nchunks, StageSmem& sm,
+                                const WTileM& cur, F&& mid) {
+    float (*red)[16][65] = sm.red;
+    float (*fin)[64] = sm.fin;
+    const float* rs = sm.rs;
+    const int K = A.K;
+    const int nb = A.W.cols >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int j = lane & 15, gq = lane >> 4;
-    const int grp = blockIdx.y * 4 + wave;
-    const int rbase = blockIdx.x * 64;
-    const int hc = cols >> 1;
-    f4_t acc[4];
+    const int b0 = (chunk * 4 + wave) * 8;
+    const int nvb = max(0, min(8, nb - b0));          // blocks of this group (wave-uniform)
+    const bool al = (nb & 7) == 0;
+    const int bb0 = min(b0, nb - 1);
+    (void)al;
+
+    // A operands: activation column j, k-quarter gq of each block of the group
+    h8_t a[8];
+    float bsum[8];
+    const bool col_live = j < K;
+    const int kk = col_live ? j : 0;
+    const bool keeper = A.keep && tile == 0 && col_live;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
-    if (grp < ngroups) {
-        const int b0 = grp * 8;
-        const int nvb = min(8, nb - b0);
-        h8_t a[8];
+    for (int tt = 0; tt < 8; ++tt) {
+        const int blk = min(bb0 + tt, nb - 1);
+        uint32_t h[8];
+        load_x8(A, rs, kk, 32 * blk + 8 * gq, h);
+        if (keeper && tt < nvb) keep_x8(A, kk, 32 * blk + 8 * gq, h);
+        float sum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            a[i] = h8_t{};
-            if (i < nvb) a[i] = as_h8(afrag[(size_t)(b0 + i) * 64 + lane]);
-        }
-        h8_t am = h8_t{};
-        if constexpr (FMT == VQ_FMT_Q4_MIN) am = as_h8(mfrag[(size_t)grp * 64 + lane]);
-        const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 8; ++e) sum += half_bits_to_float(h[e]);
+        h8_t v;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int row = rbase + 16 * t + j;
-            const bool rv = row < rows;
-            const int lr = row - sg.row0;
-            const u4_t* qp = reinterpret_cast<const u4_t*>(sg.qs + (size_t)lr * (size_t)hc) + b0;
-            u4_t n0 = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-            u4_t n1 = n0;
-            if (rv && gq < nvb) n0 = __builtin_nontemporal_load(qp + gq);
-            if (rv && 4 + gq < nvb) n1 = __builtin_nontemporal_load(qp + 4 + gq);
-            float d[8], m[8];
-            if (rv) {
-                load_scales<FMT, AL>(sg.scales, sg.mins, (size_t)lr * nb + b0, nvb, d, m);
-            } else {
+        for (int p = 0; p < 8; ++p) v[p] = __builtin_bit_cast(_Float16, (uint16_t)h[slot_col<FMT>(p)]);
+        const bool use = col_live && tt < nvb;
+        a[tt] = use ? v : h8_t{};
+        bsum[tt] = use ? sum : 0.f;
+    }
+    h8_t am = h8_t{};
+    if constexpr (FMT == VQ_FMT_Q4_MIN) {
+        // block sums over the 4 k-quarters (lanes j, j+16, j+32, j+48), then fp16 hi / lo
 #pragma unroll
-                for (int i = 0; i < 8; ++i) d[i] = m[i] = 0.f;
-            }
-            uint32_t T0[4] = {n0[0], n0[1], n0[2], n0[3]};
-            uint32_t T1[4] = {n1[0], n1[1], n1[2], n1[3]};
-            transpose4(T0);
-            transpose4(T1);
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) {
-                if (tt < nvb) {
-                    const h8_t B = widen_block_quarter<FMT>(tt < 4 ? T0[tt] : T1[tt - 4]);
-                    const f4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], B, zero, 0, 0, 0);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(d[tt], D[v], acc[t][v]);
-                }
-            }
-            if constexpr (FMT == VQ_FMT_Q4_MIN) {
-                h8_t Bm = h8_t{};
-                if (rv && gq < 2) {
-                    const uint16_t* mp = sg.mins + (size_t)lr * nb + b0;
-                    if (AL) {
-                        Bm = as_h8(*reinterpret_cast<const uint4*>(mp));
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            if (i < nvb) Bm[i] = __builtin_bit_cast(_Float16, mp[i]);
-                    }
-                }
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, Bm, acc[t], 0, 0, 0);
-            }
+        for (int tt = 0; tt < 8; ++tt) {
+            float v = bsum[tt];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            const _Float16 hi = (_Float16)v;
+            const _Float16 lo = (_Float16)(v - (float)hi);
+            am[tt] = gq == 0 ? hi : (gq == 1 ? lo : (_Float16)0.0f);
         }
     }
-    // lane (j, gq) holds D[4 gq + v][j]: activation column 4 gq + v, weight row 16 t + j
+    f4_t acc[4];
+    compute_tile_mfma<FMT>(cur, gq, nvb, a, am, acc);
+    // lane (j, gq) holds D[4 gq + v][j] = column 4 gq + v of row 16 t + j
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave][4 * gq + v][16 * t + j] = acc[t][v];
+    mid();
     __syncthreads();
-    for (int e = threadIdx.x; e < K * 64; e += 256) {
-        const int k = e >> 6, l = e & 63;
-        const int r = rbase + l;
-        if (r < rows) {
-            const float s = ((red[0][k][l] + red[1][k][l]) + red[2][k][l]) + red[3][k][l];
-            part[((size_t)blockIdx.y * K + k) * (size_t)rows + r] = s;
-        }
-    }
+    stage_epilogue(A, tile, chunk, nchunks, red, fin, &sm.last);
 }
 
-// ------------------------------------------------------------- activation layouts
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
-// Source of activation (k, c) for the prep kernels.
-struct XSrc {
-    const uint16_t* x16;   // plain fp16 input [K][cols], or NULL
-    const float* src;      // raw fp32 stage output
-    int ld, up_off, mode;
-    const float* stats;
-    int nstats;
-    uint16_t* keep;        // fp16 copy of the prepared input [K][cols], or NULL
-};
-
-// Inverse RMS of each activation column from per-block partial sums of squares.
-__device__ void glue_scales(const XSrc& S, int K, int n, float* rs) {
-    if (S.mode != GLUE_NONE && threadIdx.x < (unsigned)K) {
-        float ss = 0.f;
-        for (int i = 0; i < S.nstats; ++i) ss += S.stats[(size_t)i * K + threadIdx.x];
-        rs[threadIdx.x] = 1.0f / __fsqrt_rn(__fdiv_rn(ss, (float)n));
-    }
-    __syncthreads();
-}
-
-// Loads the 32 activations of block b of column k as fp16 bits, applying the glue.
-__device__ __forceinline__ void load_block_x(const XSrc& S, int cols, int k, int b, float r,
-                                             uint16_t (&h)[32]) {
-    if (S.mode == GLUE_NONE) {
-        const uint4* p = reinterpret_cast<const uint4*>(S.x16 + (size_t)k * cols + (size_t)b * 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 v = p[i];
-            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                h[i * 8 + 2 * e] = vv[e] & 0xffffu;
-                h[i * 8 + 2 * e + 1] = vv[e] >> 16;
-            }
-            if (S.keep)
-                reinterpret_cast<uint4*>(S.keep + (size_t)k * cols + (size_t)b * 32)[i] = v;
-        }
-        return;
-    }
-    const float* src = S.src + (size_t)k * S.ld + (size_t)b * 32;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) {
-        float v = src[c];
-        if (S.mode == GLUE_RHO_SILU) v = silu_mul(v, src[S.up_off + c]);
-        h[c] = __builtin_bit_cast(uint16_t, (_Float16)(v * r));
-    }
-    if (S.keep) {
-        uint4* kp = reinterpret_cast<uint4*>(S.keep + (size_t)k * cols + (size_t)b * 32);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = h[i * 8 + 2 * e] | ((uint32_t)h[i * 8 + 2 * e + 1] << 16);
-            kp[i] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-    }
-}
-
-// VALU layout: xp[k][b*16 + g*4 + t] = half2 pair t of 8-column group g of block b
-// (Q4: (x[8g+t], x[8g+4+t]); MXFP4: (x[8g+2t], x[8g+2t+1])) and bsum[k][b] = sum x.
 template <int FMT>
-__global__ __launch_bounds__(256) void k_prep_valu(XSrc S, int K, int cols, uint32_t* __restrict__ xp,
-                                                   float* __restrict__ bsum) {
-    __shared__ float rs[VQ_MAX_K];
-    const int nb = cols >> 5;
-    glue_scales(S, K, S.mode == GLUE_NONE ? 1 : cols, rs);
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= K * nb) return;
-    const int k = idx / nb, b = idx % nb;
-    uint16_t h[32];
-    load_block_x(S, cols, k, b, S.mode == GLUE_NONE ? 1.f : rs[k], h);
-    uint32_t out[16];
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            uint32_t lo, hi;
-            if (FMT == VQ_FMT_MXFP4) {
-                lo = h[8 * g + 2 * t];
-                hi = h[8 * g + 2 * t + 1];
-            } else {
-                lo = h[8 * g + t];
-                hi = h[8 * g + 4 + t];
-            }
-            out[g * 4 + t] = lo | (hi << 16);
-        }
-    uint4* dst = reinterpret_cast<uint4*>(xp + (size_t)k * (cols >> 1) + (size_t)b * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-    if (bsum) {
-        float s = 0.f;
-#pragma unroll
-        for (int c = 0; c < 32; ++c) s += (float)__builtin_bit_cast(_Float16, h[c]);
-        bsum[(size_t)k * nb + b] = s;
-    }
+__global__ __launch_bounds__(256) void k_stage_mfma(const StageArgs A, int nchunks) {
+    __shared__ StageSmem sm;
+    const int item = xcd_item(blockIdx.x, gridDim.x);
+    const int tile = item / nchunks, chunk = item - tile * nchunks;
+    WTileM cur;
+    prefetch_mfma<FMT>(A, tile, chunk, cur);
+    stage_rms(A, sm.rs, &sm.red[0][0][0]);
+    stage_item_mfma<FMT>(A, tile, chunk, nchunks, sm, cur, [] {});
 }
 
-// MFMA layout: afrag[b][16 g + i] = the 8 activations of column i (0 when i >= K) at
-// block b, columns 8g..8g+7 in the widened order; mfrag[grp][16 g + i] holds, for g = 0
-// and 1, the fp16 hi and lo parts of the block sums of column i over blocks 8 grp..+7
-// (zero for g = 2, 3, for i >= K and for blocks past the row end).
-template <int FMT>
-__global__ __launch_bounds__(256) void k_prep_mfma(XSrc S, int K, int cols, uint4* __restrict__ afrag,
-                                                   uint16_t* __restrict__ mfrag) {
-    __shared__ float rs[VQ_MAX_K];
-    const int nb = cols >> 5;
-    const int ngroups = (nb + 7) >> 3;
-    glue_scales(S, K, S.mode == GLUE_NONE ? 1 : cols, rs);
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= 16 * ngroups * 8) return;
-    const int i = idx & 15, b = idx >> 4;
-    uint16_t h[32];
-    const bool live = i < K && b < nb;
-    if (live) {
-        load_block_x(S, cols, i, b, S.mode == GLUE_NONE ? 1.f : rs[i], h);
-    } else {
-#pragma unroll
-        for (int c = 0; c < 32; ++c) h[c] = 0;
-    }
-    if (b < nb) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            uint32_t w[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                uint32_t lo, hi;
-                if (FMT == VQ_FMT_MXFP4) {
-                    lo = h[8 * g + 2 * s];
-                    hi = h[8 * g + 2 * s + 1];
-                } else {
-                    // widened order: slot 2s holds column s, slot 2s+1 column s+4
-                    lo = h[8 * g + s];
-                    hi = h[8 * g + s + 4];
+
+// ------------------------------------------------------------------ persistent pass
+
+// Waits until *cnt reaches `target`: thread 0 polls, the workgroup waits at the barrier
+// behind it.  The wait is bounded: after about a second without progress the error flag
+// is raised and the workgroup proceeds, so a launch always ends.
+__device__ void wait_count(const unsigned* cnt, unsigned target, int* err) {
+    if (threadIdx.x == 0) {
+        unsigned spins = 0;
+        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(1);
+            if ((++spins & 1023u) == 0) {
+                // another workgroup gave up: do not wait either
+                if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
+                if (spins >= (1u << 20)) {
+                    __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
                 }
-                w[s] = lo | (hi << 16);
-            }
-            afrag[(size_t)b * 64 + 16 * g + i] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-    }
-    if (mfrag) {
-        float s = 0.f;
-#pragma unroll
-        for (int c = 0; c < 32; ++c) s += (float)__builtin_bit_cast(_Float16, h[c]);
-        const _Float16 hi = (_Float16)s;
-        const _Float16 lo = (_Float16)(s - (float)hi);
-        uint16_t* base = mfrag + ((size_t)(b >> 3) * 64) * 8 + (b & 7);
-        base[(size_t)(0 * 16 + i) * 8] = __builtin_bit_cast(uint16_t, hi);
-        base[(size_t)(1 * 16 + i) * 8] = __builtin_bit_cast(uint16_t, lo);
-        base[(size_t)(2 * 16 + i) * 8] = 0;
-        base[(size_t)(3 * 16 + i) * 8] = 0;
-    }
-}
-
-// ------------------------------------------------------------------ finalize
-
-__global__ __launch_bounds__(256) void k_finalize(const float* __restrict__ part, int C, int K,
-                                                  int rows, void* __restrict__ y, int y_dtype) {
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)K * rows) return;
-    const int k = (int)(idx / rows);
-    const int r = (int)(idx % rows);
-    float s = 0.f;
-    for (int c = 0; c < C; ++c) s += part[((size_t)c * K + k) * rows + r];
-    if (y_dtype == VQ_DTYPE_F16)
-        reinterpret_cast<uint16_t*>(y)[idx] = __builtin_bit_cast(uint16_t, (_Float16)s);
-    else
-        reinterpret_cast<float*>(y)[idx] = s;
-}
-
-__device__ float block_sum_256(float v, float* sh) {
-    sh[threadIdx.x] = v;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (threadIdx.x < (unsigned)s) sh[threadIdx.x] += sh[threadIdx.x + s];
-        __syncthreads();
-    }
-    const float r = sh[0];
-    __syncthreads();
-    return r;
-}
-
-__global__ __launch_bounds__(256) void k_finalize_stats(const float* __restrict__ part, int C, int K,
-                                                        int rows, float* __restrict__ y, int nstat,
-                                                        int silu, float* __restrict__ stats) {
-    __shared__ float sh[256];
-    const int half = silu ? rows / 2 : rows;
-    const int r = blockIdx.x * 256 + threadIdx.x;
-    for (int k = 0; k < K; ++k) {
-        float sq = 0.f;
-        if (r < half) {
-            float s = 0.f;
-            for (int c = 0; c < C; ++c) s += part[((size_t)c * K + k) * rows + r];
-            y[(size_t)k * rows + r] = s;
-            if (silu) {
-                float u = 0.f;
-                for (int c = 0; c < C; ++c) u += part[((size_t)c * K + k) * rows + half + r];
-                y[(size_t)k * rows + half + r] = u;
-                const float v = silu_mul(s, u);
-                sq = v * v;
-            } else if (r < nstat) {
-                sq = s * s;
             }
         }
-        const float t = block_sum_256(sq, sh);
-        if (threadIdx.x == 0) stats[(size_t)blockIdx.x * K + k] = t;
+    }
+    __syncthreads();
+}
+
+// The stages of a plan segment in one launch.  A stage's items are dealt round-robin to
+// the workgroups (those of one XCD take consecutive items, so a tile's chunks meet in one
+// L2).  There is no grid-wide barrier: a workgroup with items in stage s issues its first
+// item's weight loads, then waits until every tile of stage s - 1 has counted itself
+// complete, then reads that stage's outputs.  Workgroups without items in a stage go
+// straight on to the next one, and every item's epilogue overlaps the next item's loads.
+template <int FMT, int K, bool MFMA>
+__global__ __launch_bounds__(256) void k_pass(const PassPlan P) {
+    __shared__ StageSmem sm;
+    __shared__ uint2 xs[4][MFMA ? 1 : K][8][8];
+    using Tile = typename std::conditional<MFMA, WTileM, WTileV>::type;
+    const int nwg = gridDim.x;                // a multiple of 8
+    const int grp = blockIdx.x & 7;
+    const int vid = grp * (nwg >> 3) + (blockIdx.x >> 3);
+    const int s0 = 4 * P.layer0;
+    const int s1 = 4 * (P.layer0 + P.nlayers) + (P.with_lm ? 1 : 0);
+    int prev_tiles = 0;
+    for (int stage = s0; stage < s1; ++stage) {
+        StageArgs A;
+        build_stage(P, stage, A);
+        const StageGeom g = stage_geom(A.W.rows, A.W.cols, A.paired, A.paired ? A.W.seg_end[0] : 0);
+        const int nitems = g.ntiles * g.nchunks;
+        const int wait_tiles = prev_tiles;
+        prev_tiles = g.ntiles;
+        if (vid >= nitems) continue;
+        auto fetch = [&](int it, Tile& T) {
+            const int tile = it / g.nchunks;
+            if constexpr (MFMA) prefetch_mfma<FMT>(A, tile, it - tile * g.nchunks, T);
+            else prefetch_valu<FMT>(A, tile, it - tile * g.nchunks, T);
+        };
+        Tile cur;
+        fetch(vid, cur);
+        if (stage > s0)
+            wait_count(P.done + (size_t)(stage - 1) * DONE_WORDS + grp * DONE_STRIDE, (unsigned)wait_tiles, P.err);
+        stage_rms(A, sm.rs, &sm.red[0][0][0]);
+        for (int it = vid; it < nitems; it += nwg) {
+            const int tile = it / g.nchunks;
+            Tile nxt;
+            const bool more = it + nwg < nitems;
+            auto mid = [&] {
+                if (more) fetch(it + nwg, nxt);
+            };
+            if constexpr (MFMA) stage_item_mfma<FMT>(A, tile, it - tile * g.nchunks, g.nchunks, sm, cur, mid);
+            else stage_item_valu<FMT, K>(A, tile, it - tile * g.nchunks, g.nchunks, sm, xs, cur, mid);
+            __syncthreads();                  // LDS is reused by the next item
+            if (more) cur = nxt;
+        }
     }
 }
 
-template <typename F>
-hipError_t launch_checked(F f) {
-    f();
-    return hipGetLastError();
+template <int FMT, int K, bool MFMA>
+const void* pass_fn() {
+    return reinterpret_cast<const void*>(&k_pass<FMT, K, MFMA>);
+}
+
+template <int FMT>
+const void* pass_fn_k(int K, bool mfma) {
+    if (mfma) return pass_fn<FMT, 1, true>();
+    switch (K) {
+        case 1: return pass_fn<FMT, 1, false>();
+        case 2: return pass_fn<FMT, 2, false>();
+        case 3: return pass_fn<FMT, 3, false>();
+        case 4: return pass_fn<FMT, 4, false>();
+        case 5: return pass_fn<FMT, 5, false>();
+        case 6: return pass_fn<FMT, 6, false>();
+        case 7: return pass_fn<FMT, 7, false>();
+        default: return pass_fn<FMT, 8, false>();
+    }
+}
+
+constexpr int PERSIST_WGS_PER_CU = 4;
+
+__global__ void k_zero_u32(unsigned* p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+template <int FMT, int K>
+void launch_valu_k(const StageArgs& A, int tg, const StageGeom& g, hipStream_t st) {
+    k_stage_valu<FMT, K><<<dim3(tg * g.nchunks), 256, 0, st>>>(A, g.nchunks);
+}
+
+template <int FMT>
+void launch_valu_f(const StageArgs& A, int tg, const StageGeom& g, hipStream_t st) {
+    switch (A.K) {
+        case 1: launch_valu_k<FMT, 1>(A, tg, g, st); break;
+        case 2: launch_valu_k<FMT, 2>(A, tg, g, st); break;
+        case 3: launch_valu_k<FMT, 3>(A, tg, g, st); break;
+        case 4: launch_valu_k<FMT, 4>(A, tg, g, st); break;
+        case 5: launch_valu_k<FMT, 5>(A, tg, g, st); break;
+        case 6: launch_valu_k<FMT, 6>(A, tg, g, st); break;
+        case 7: launch_valu_k<FMT, 7>(A, tg, g, st); break;
+        default: launch_valu_k<FMT, 8>(A, tg, g, st); break;
+    }
 }
 
 }  // namespace
 
 // ------------------------------------------------------------------ host side
 
-size_t lin_scratch_bytes(int fmt, int rows, int cols, int K, bool mfma) {
-    const LinGeom g = lin_geom(rows, cols);
-    size_t n = 0;
-    if (mfma) {
-        n += align_up((size_t)g.nb * 64 * 16, 256);
-        if (fmt == VQ_FMT_Q4_MIN) n += align_up((size_t)g.ngroups * 64 * 16, 256);
-    } else {
-        n += align_up((size_t)K * cols * 2, 256);
-        if (fmt == VQ_FMT_Q4_MIN) n += align_up((size_t)K * g.nb * 4, 256);
-    }
-    n += align_up((size_t)g.nchunks * K * rows * 4, 256);
-    return n;
+size_t stage_scratch_bytes(int rows, int cols, int K, int paired, int half) {
+    const StageGeom g = stage_geom(rows, cols, paired, half);
+    return align_up((size_t)g.nchunks * K * rows * 4, 256) + align_up((size_t)g.ntiles * 4, 256);
 }
 
-void lin_scratch_carve(void* base, int fmt, int rows, int cols, int K, bool mfma, LinScratch* s) {
-    const LinGeom g = lin_geom(rows, cols);
-    char* p = (char*)base;
-    s->xlay = p;
-    p += mfma ? align_up((size_t)g.nb * 64 * 16, 256) : align_up((size_t)K * cols * 2, 256);
-    s->aux = nullptr;
-    if (fmt == VQ_FMT_Q4_MIN) {
-        s->aux = p;
-        p += mfma ? align_up((size_t)g.ngroups * 64 * 16, 256) : align_up((size_t)K * g.nb * 4, 256);
-    }
-    s->part = (float*)p;
+void stage_scratch_carve(void* base, int rows, int cols, int K, int paired, int half, StageArgs* A) {
+    const StageGeom g = stage_geom(rows, cols, paired, half);
+    A->part = (float*)base;
+    A->counters = (unsigned*)((char*)base + align_up((size_t)g.nchunks * K * rows * 4, 256));
 }
 
-static hipError_t launch_prep(const Mat& W, const XSrc& S, int K, bool mfma, const LinScratch& s,
-                              hipStream_t st) {
-    const LinGeom g = lin_geom(W.rows, W.cols);
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    k_zero_u32<<<dim3((n + 255) / 256), 256, 0, st>>>(p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage(const StageArgs& A, bool mfma, hipStream_t st) {
+    const StageGeom g = stage_geom(A.W.rows, A.W.cols, A.paired, A.paired ? A.W.seg_end[0] : 0);
+    // one workgroup per (tile, chunk): many independent workgroups overlap the epilogue's
+    // atomic round trips (a tile loop inside a workgroup serialises them)
+    const int tg = g.ntiles;
     if (mfma) {
-        const int n = 16 * g.ngroups * 8;
-        dim3 grid((n + 255) / 256);
-        switch (W.fmt) {
-            case VQ_FMT_Q4:
-                k_prep_mfma<VQ_FMT_Q4><<<grid, 256, 0, st>>>(S, K, W.cols, (uint4*)s.xlay, nullptr);
-                break;
-            case VQ_FMT_Q4_MIN:
-                k_prep_mfma<VQ_FMT_Q4_MIN><<<grid, 256, 0, st>>>(S, K, W.cols, (uint4*)s.xlay,
-                                                                 (uint16_t*)s.aux);
-                break;
-            default:
-                k_prep_mfma<VQ_FMT_MXFP4><<<grid, 256, 0, st>>>(S, K, W.cols, (uint4*)s.xlay, nullptr);
+        switch (A.W.fmt) {
+            case VQ_FMT_Q4: k_stage_mfma<VQ_FMT_Q4><<<dim3(tg * g.nchunks), 256, 0, st>>>(A, g.nchunks); break;
+            case VQ_FMT_Q4_MIN: k_stage_mfma<VQ_FMT_Q4_MIN><<<dim3(tg * g.nchunks), 256, 0, st>>>(A, g.nchunks); break;
+            default: k_stage_mfma<VQ_FMT_MXFP4><<<dim3(tg * g.nchunks), 256, 0, st>>>(A, g.nchunks); break;
         }
     } else {
-        const int n = K * g.nb;
-        dim3 grid((n + 255) / 256);
-        switch (W.fmt) {
-            case VQ_FMT_Q4:
-                k_prep_valu<VQ_FMT_Q4><<<grid, 256, 0, st>>>(S, K, W.cols, (uint32_t*)s.xlay, nullptr);
-                break;
-            case VQ_FMT_Q4_MIN:
-                k_prep_valu<VQ_FMT_Q4_MIN><<<grid, 256, 0, st>>>(S, K, W.cols, (uint32_t*)s.xlay,
-                                                                 (float*)s.aux);
-                break;
-            default:
-                k_prep_valu<VQ_FMT_MXFP4><<<grid, 256, 0, st>>>(S, K, W.cols, (uint32_t*)s.xlay, nullptr);
+        switch (A.W.fmt) {
+            case VQ_FMT_Q4: launch_valu_f<VQ_FMT_Q4>(A, tg, g, st); break;
+            case VQ_FMT_Q4_MIN: launch_valu_f<VQ_FMT_Q4_MIN>(A, tg, g, st); break;
+            default: launch_valu_f<VQ_FMT_MXFP4>(A, tg, g, st); break;
         }
     }
     return hipGetLastError();
 }
 
-hipError_t launch_prep_plain(const Mat& W, const uint16_t* x, int K, bool mfma, const LinScratch& s,
-                             uint16_t* x_keep, hipStream_t st) {
-    XSrc S{x, nullptr, 0, 0, GLUE_NONE, nullptr, 0, x_keep};
-    return launch_prep(W, S, K, mfma, s, st);
-}
-
-hipError_t launch_prep_glue(const Mat& W, const float* src, int ld, int up_off, int mode,
-                            const float* stats, int nstats, int K, bool mfma, uint16_t* x_keep,
-                            const LinScratch& s, hipStream_t st) {
-    XSrc S{nullptr, src, ld, up_off, mode, stats, nstats, x_keep};
-    return launch_prep(W, S, K, mfma, s, st);
-}
-
-template <int FMT, int K, bool AL>
-static void launch_valu_k(const Mat& W, const LinScratch& s, dim3 grid, hipStream_t st) {
-    k_lin_valu<FMT, K, AL><<<grid, 256, 0, st>>>(W, (const uint32_t*)s.xlay, (const float*)s.aux, s.part);
-}
-
-template <int FMT, bool AL>
-static void launch_valu_f(const Mat& W, int K, const LinScratch& s, dim3 grid, hipStream_t st) {
-    switch (K) {
-        case 1: launch_valu_k<FMT, 1, AL>(W, s, grid, st); break;
-        case 2: launch_valu_k<FMT, 2, AL>(W, s, grid, st); break;
-        case 3: launch_valu_k<FMT, 3, AL>(W, s, grid, st); break;
-        case 4: launch_valu_k<FMT, 4, AL>(W, s, grid, st); break;
-        case 5: launch_valu_k<FMT, 5, AL>(W, s, grid, st); break;
-        case 6: launch_valu_k<FMT, 6, AL>(W, s, grid, st); break;
-        case 7: launch_valu_k<FMT, 7, AL>(W, s, grid, st); break;
-        default: launch_valu_k<FMT, 8, AL>(W, s, grid, st); break;
-    }
-}
-
-template <int FMT, bool AL>
-static void launch_mfma_f(const Mat& W, int K, const LinScratch& s, dim3 grid, hipStream_t st) {
-    k_lin_mfma<FMT, AL><<<grid, 256, 0, st>>>(W, (const uint4*)s.xlay, (const uint4*)s.aux, s.part, K);
-}
-
-hipError_t launch_linear_main(const Mat& W, int K, bool mfma, const LinScratch& s, hipStream_t st) {
-    const LinGeom g = lin_geom(W.rows, W.cols);
-    dim3 grid(g.ntiles, g.nchunks);
-    const bool al = (g.nb % 8) == 0;
-    if (mfma) {
-        switch (W.fmt * 2 + (al ? 1 : 0)) {
-            case 0: launch_mfma_f<VQ_FMT_Q4, false>(W, K, s, grid, st); break;
-            case 1: launch_mfma_f<VQ_FMT_Q4, true>(W, K, s, grid, st); break;
-            case 2: launch_mfma_f<VQ_FMT_Q4_MIN, false>(W, K, s, grid, st); break;
-            case 3: launch_mfma_f<VQ_FMT_Q4_MIN, true>(W, K, s, grid, st); break;
-            case 4: launch_mfma_f<VQ_FMT_MXFP4, false>(W, K, s, grid, st); break;
-            default: launch_mfma_f<VQ_FMT_MXFP4, true>(W, K, s, grid, st); break;
-        }
-    } else {
-        switch (W.fmt * 2 + (al ? 1 : 0)) {
-            case 0: launch_valu_f<VQ_FMT_Q4, false>(W, K, s, grid, st); break;
-            case 1: launch_valu_f<VQ_FMT_Q4, true>(W, K, s, grid, st); break;
-            case 2: launch_valu_f<VQ_FMT_Q4_MIN, false>(W, K, s, grid, st); break;
-            case 3: launch_valu_f<VQ_FMT_Q4_MIN, true>(W, K, s, grid, st); break;
-            case 4: launch_valu_f<VQ_FMT_MXFP4, false>(W, K, s, grid, st); break;
-            default: launch_valu_f<VQ_FMT_MXFP4, true>(W, K, s, grid, st); break;
-        }
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_finalize(const Mat& W, int K, const LinScratch& s, void* y, int y_dtype,
-                           hipStream_t st) {
-    const LinGeom g = lin_geom(W.rows, W.cols);
-    const size_t n = (size_t)K * W.rows;
-    k_finalize<<<dim3((unsigned)((n + 255) / 256)), 256, 0, st>>>(s.part, g.nchunks, K, W.rows, y, y_dtype);
-    return hipGetLastError();
-}
-
-int finalize_stats_blocks(int rows, int silu) {
-    const int half = silu ? rows / 2 : rows;
-    return (half + 255) / 256;
-}
-
-hipError_t launch_finalize_stats(const Mat& W, int K, const LinScratch& s, float* y, int nstat,
-                                 int silu, float* stats, hipStream_t st) {
-    const LinGeom g = lin_geom(W.rows, W.cols);
-    k_finalize_stats<<<dim3(finalize_stats_blocks(W.rows, silu)), 256, 0, st>>>(
-        s.part, g.nchunks, K, W.rows, y, nstat, silu, stats);
+hipError_t launch_pass_segment(const PassPlan& P, bool mfma, hipStream_t st) {
+    const void* fn = P.fmt == VQ_FMT_Q4 ? pass_fn_k<VQ_FMT_Q4>(P.K, mfma)
+                     : P.fmt == VQ_FMT_Q4_MIN ? pass_fn_k<VQ_FMT_Q4_MIN>(P.K, mfma)
+                                              : pass_fn_k<VQ_FMT_MXFP4>(P.K, mfma);
+    int dev = 0, cus = 0, occ = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 256, 0);
+    if (e != hipSuccess) return e;
+    int nwg = cus * std::min(occ, PERSIST_WGS_PER_CU);
+    nwg -= nwg % 8;
+    if (nwg < 8) return hipErrorInvalidConfiguration;
+    void* args[] = {const_cast<PassPlan*>(&P)};
+    // cooperative: the runtime refuses the launch unless every workgroup is resident,
+    // which the grid barriers rely on
+    e = hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(256), args, 0, st);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -1,6 +1,8 @@
 // Internal declarations of libvq (not part of the C ABI).
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -35,64 +37,177 @@ inline Mat mat_from(const vq_matrix& m) {
     return r;
 }
 
-// Geometry of a linear launch: 64-row tiles x chunks of 4 groups of 8 blocks.
-struct LinGeom {
+// Geometry of one stage launch: tiles of 64 rows (paired: 32 rows of each of the two
+// segments) x chunks of 4 groups of 8 blocks (one group per wave of a workgroup).
+struct StageGeom {
     int nb;        // blocks of 32 per row
     int ngroups;   // groups of 8 blocks per row
-    int nchunks;   // chunks of 4 groups (one per wave of a 256-thread workgroup)
-    int ntiles;    // 64-row tiles
+    int nchunks;   // chunks of 4 groups
+    int ntiles;
 };
-
-inline LinGeom lin_geom(int rows, int cols) {
-    LinGeom g;
-    g.nb = cols / 32;
-    g.ngroups = (g.nb + 7) / 8;
-    g.nchunks = (g.ngroups + 3) / 4;
-    g.ntiles = (rows + 63) / 64;
-    return g;
-}
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Scratch of one linear launch: activation layout, block sums, split-K partials.
-struct LinScratch {
-    void* xlay;      // VALU: packed half2 [K][cols/2]; MFMA: uint4 [nb][64]
-    void* aux;       // VALU: float [K][nb] block sums; MFMA: uint4 [ngroups][64] min fragments
-    float* part;     // [nchunks][K][rows]
+// Glue modes: how a stage builds its input from the previous stage.
+enum GlueMode { GLUE_NONE = 0, GLUE_RHO = 1 };
+
+// Everything one stage launch reads and writes.
+struct StageArgs {
+    Mat W;
+    int K;
+    int paired;                // 1: gate|up pairing (tile t = rows [32t, 32t+32) of both segments)
+    // input: GLUE_NONE reads fp16 x16 [K][cols]; GLUE_RHO reads src[k*ld + j] and scales
+    // column k by 1/sqrt(sum(stats_in[.][k]) / n_in) before rounding to fp16
+    int glue;
+    const uint16_t* x16;
+    const float* src;
+    int ld;
+    int n_in;
+    const float* stats_in;
+    int nstats_in;
+    uint16_t* keep;            // fp16 copy of the input [K][cols] (written by tile 0), or NULL
+    // scratch
+    float* part;               // split-K partials [nchunks][K][rows]
+    unsigned* counters;        // per-tile arrival counters [ntiles], zero between launches
+    // output
+    void* y;                   // [K][rows], f32 or f16
+    int y_dtype;
+    float* stats_out;          // per-tile sums of squares [ntiles][K], or NULL
+    int nstat;                 // rows < nstat contribute to stats_out (unpaired)
+    float* sbuf;               // paired: silu(gate) * up [K][rows/2]
+    int coh;                   // 1: y / stats_out / sbuf are read by other workgroups of the
+                               // same launch: stored through to memory (device scope)
+    unsigned* done;            // NULL, or DONE_REPL completion counters DONE_STRIDE words
+                               // apart: each gets +1 when a tile's outputs are in memory
 };
 
-size_t lin_scratch_bytes(int fmt, int rows, int cols, int K, bool mfma);
-void lin_scratch_carve(void* base, int fmt, int rows, int cols, int K, bool mfma, LinScratch* s);
+// Completion counters of the persistent pass: one replica per XCD group of workgroups,
+// each on its own 128-byte line, so that waiting workgroups spread their polling.
+constexpr int DONE_REPL = 8;
+constexpr int DONE_STRIDE = 32;
+constexpr int DONE_WORDS = DONE_REPL * DONE_STRIDE;     // per stage
 
-// Prepare the activation layout from fp16 x [K][cols] (plain input).
-hipError_t launch_prep_plain(const Mat& W, const uint16_t* x, int K, bool mfma,
-                             const LinScratch& s, uint16_t* x_keep, hipStream_t st);
+// ------------------------------------------------------------- decode pass plan
 
-// Glue input modes for the decode pass.
-enum GlueMode { GLUE_NONE = 0, GLUE_RHO = 1, GLUE_RHO_SILU = 2 };
+// The stage sequence of a decode pass, in a form both the host and the device can turn
+// into StageArgs.  One launch of the persistent kernel covers up to PASS_LAYERS layers.
+constexpr int PASS_LAYERS = 8;
 
-// Prepare the activation layout from a raw fp32 stage output with rho (and silu*up):
-//   v[k][j] = src[k*ld + j]              (GLUE_RHO)
-//   v[k][j] = silu(src[k*ld + j]) * src[k*ld + up_off + j]   (GLUE_RHO_SILU)
-// x[k][j] = fp16(v[k][j] * r_k), r_k = 1/sqrt(sum(stats[.][k]) / n); x is also stored
-// to x_keep (fp16 [K][cols]).
-hipError_t launch_prep_glue(const Mat& W, const float* src, int ld, int up_off, int mode,
-                            const float* stats, int nstats, int K, bool mfma,
-                            uint16_t* x_keep, const LinScratch& s, hipStream_t st);
+struct MatPtrs {
+    const void* qs;
+    const void* sc;
+    const void* mn;
+};
 
-// The main weight-streaming kernel (writes split-K partials).
-hipError_t launch_linear_main(const Mat& W, int K, bool mfma, const LinScratch& s, hipStream_t st);
+struct PassPlan {
+    int fmt, K, H, KV, FF, V, L;   // shapes (every layer alike)
+    int layer0, nlayers;           // layers of this plan segment
+    int with_lm;                   // 1: the lm_head stage ends this segment
+    MatPtrs m[PASS_LAYERS][7];     // q, k, v, o, gate, up, down of layers layer0 + i
+    MatPtrs lm;
+    const uint16_t* x0;            // pass input fp16 [K][H]
+    float* logits;                 // [K][V]
+    char* base;                    // workspace
+    size_t layer_bytes, in_off[4], out_off[4], final_in_off;
+    float* stats;                  // per-tile sums of squares, stats_stride floats per stage
+    size_t stats_stride;
+    float* sbuf;                   // silu(gate) * up, sbuf_stride floats per layer
+    size_t sbuf_stride;
+    float* part;
+    unsigned* counters;
+    unsigned* done;                // DONE_WORDS per stage, 0 at pass start (persistent only)
+    int* err;                      // set when a wait for a stage times out
+    int coh;
+};
 
-// Sum the partials: y[k][r] (f32 or f16 with leading dim rows).
-hipError_t launch_finalize(const Mat& W, int K, const LinScratch& s, void* y, int y_dtype,
-                           hipStream_t st);
+__host__ __device__ inline int stage_tiles_of(int rows, int paired, int half) {
+    return paired ? (half + 31) / 32 : (rows + 63) / 64;
+}
 
-// Decode-pass finalize: y = sum of partials (f32, leading dim ld_out), plus per-256-row
-// partial sums of squares of y over rows < nstat (stats[blk][k]).  SILU: rows [0, half)
-// are gate, [half, 2 half) up; the statistic is of silu(gate) * up.
-int finalize_stats_blocks(int rows, int silu);
-hipError_t launch_finalize_stats(const Mat& W, int K, const LinScratch& s, float* y,
-                                 int nstat, int silu, float* stats, hipStream_t st);
+// StageArgs of global stage `stage` (4 per layer + lm_head) of a plan segment.
+__host__ __device__ inline void build_stage(const PassPlan& P, int stage, StageArgs& A) {
+    const int l = stage / 4, j = stage % 4;
+    const bool lm = (l == P.L);
+    const int li = l - P.layer0;
+    A = StageArgs{};
+    A.K = P.K;
+    A.coh = P.coh;
+    Mat& W = A.W;
+    W.fmt = P.fmt;
+    auto seg = [&](int i, const MatPtrs& mp, int rows_before) {
+        W.qs[i] = (const uint8_t*)mp.qs;
+        W.scales[i] = mp.sc;
+        W.mins[i] = (const uint16_t*)mp.mn;
+        (void)rows_before;
+    };
+    if (lm) {
+        W.rows = P.V; W.cols = P.H; W.nseg = 1; W.seg_end[0] = P.V;
+        seg(0, P.lm, 0);
+    } else if (j == 0) {
+        W.rows = P.H + 2 * P.KV; W.cols = P.H; W.nseg = 3;
+        W.seg_end[0] = P.H; W.seg_end[1] = P.H + P.KV; W.seg_end[2] = P.H + 2 * P.KV;
+        seg(0, P.m[li][0], 0); seg(1, P.m[li][1], 0); seg(2, P.m[li][2], 0);
+    } else if (j == 1) {
+        W.rows = P.H; W.cols = P.H; W.nseg = 1; W.seg_end[0] = P.H;
+        seg(0, P.m[li][3], 0);
+    } else if (j == 2) {
+        W.rows = 2 * P.FF; W.cols = P.H; W.nseg = 2; W.seg_end[0] = P.FF; W.seg_end[1] = 2 * P.FF;
+        seg(0, P.m[li][4], 0); seg(1, P.m[li][5], 0);
+        A.paired = 1;
+    } else {
+        W.rows = P.H; W.cols = P.FF; W.nseg = 1; W.seg_end[0] = P.H;
+        seg(0, P.m[li][6], 0);
+    }
+    A.keep = (uint16_t*)(lm ? P.base + P.final_in_off : P.base + (size_t)l * P.layer_bytes + P.in_off[j]);
+    if (stage == 0) {
+        A.glue = GLUE_NONE;
+        A.x16 = P.x0;
+    } else {
+        // the previous stage's raw output: q part of q|k|v, o, silu(gate) * up, down
+        const int pl = (stage - 1) / 4, pj = (stage - 1) % 4;
+        A.glue = GLUE_RHO;
+        A.n_in = W.cols;
+        A.stats_in = P.stats + (size_t)(stage - 1) * P.stats_stride;
+        if (pj == 2) {
+            A.src = P.sbuf + (size_t)pl * P.sbuf_stride;
+            A.ld = P.FF;
+            A.nstats_in = stage_tiles_of(2 * P.FF, 1, P.FF);
+        } else {
+            A.src = (const float*)(P.base + (size_t)pl * P.layer_bytes + P.out_off[pj]);
+            const int prow = pj == 0 ? P.H + 2 * P.KV : P.H;
+            A.ld = prow;
+            A.nstats_in = stage_tiles_of(prow, 0, 0);
+        }
+    }
+    A.y_dtype = VQ_DTYPE_F32;
+    if (lm) {
+        A.y = P.logits;
+    } else {
+        A.y = P.base + (size_t)l * P.layer_bytes + P.out_off[j];
+        A.stats_out = P.stats + (size_t)stage * P.stats_stride;
+        A.nstat = j == 0 ? P.H : W.rows;
+        A.sbuf = P.sbuf + (size_t)l * P.sbuf_stride;
+        A.done = P.done ? P.done + (size_t)stage * DONE_WORDS : nullptr;
+    }
+    A.part = P.part;
+    A.counters = P.counters;
+}
+
+__host__ __device__ inline StageGeom stage_geom(int rows, int cols, int paired, int half) {
+    StageGeom g;
+    g.nb = cols / 32;
+    g.ngroups = (g.nb + 7) / 8;
+    g.nchunks = (g.ngroups + 3) / 4;
+    g.ntiles = paired ? (half + 31) / 32 : (rows + 63) / 64;
+    return g;
+}
+size_t stage_scratch_bytes(int rows, int cols, int K, int paired, int half);
+void stage_scratch_carve(void* base, int rows, int cols, int K, int paired, int half, StageArgs* A);
+hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);
+hipError_t launch_stage(const StageArgs& A, bool mfma, hipStream_t st);
+// One persistent (cooperative) launch over the stages of a plan segment, separated by
+// grid barriers.  *nwg receives the grid size used.
+hipError_t launch_pass_segment(const PassPlan& P, bool mfma, hipStream_t st);
 
 // Acceptance.
 size_t accept_ws_bytes(const vq_accept_desc* d);

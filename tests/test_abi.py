@@ -163,3 +163,45 @@ def test_decode_validation_and_layout():
     assert seen == sorted(seen) and len(set(seen)) == 9
     a, b = ctypes.c_void_p(), ctypes.c_void_p()
     assert vq.lib.vq_decode_stage_ptr(ctypes.byref(M), 4, FAKE, 9, ctypes.byref(a), ctypes.byref(b)) == vq.ERR_ARG
+
+
+@pytest.mark.parametrize("path,code", [
+    (3, vq.ERR_ARG),                                              # no such kernel
+    (vq.LAUNCH_STAGED | vq.LAUNCH_PERSISTENT, vq.ERR_ARG),         # two launch modes
+    (16, vq.ERR_ARG),
+    (-4, vq.ERR_ARG),
+    (vq.PATH_VALU | vq.LAUNCH_PERSISTENT, vq.ERR_UNSUPPORTED),     # VALU stops at K = 8
+])
+def test_decode_path_and_launch_mode_errors(path, code):
+    M, keep = _model()
+    n9 = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 9)
+    assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, 9, FAKE, path, FAKE, n9, None) == code
+    assert vq.lib.vq_last_error()
+
+
+def test_decode_error_word_lies_in_the_workspace():
+    M, keep = _model()
+    for K in (1, 4, 16):
+        n = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), K)
+        w = ctypes.c_void_p()
+        assert vq.lib.vq_decode_error_word(ctypes.byref(M), K, FAKE, ctypes.byref(w)) == vq.OK
+        assert FAKE <= w.value and w.value + 4 <= FAKE + n and w.value % 4 == 0
+        a, b = ctypes.c_void_p(), ctypes.c_void_p()
+        vq.lib.vq_decode_stage_ptr(ctypes.byref(M), K, FAKE, 8, ctypes.byref(a), ctypes.byref(b))
+        assert w.value > a.value                    # after the stage tensors, not inside them
+    assert vq.lib.vq_decode_error_word(ctypes.byref(M), 0, FAKE, ctypes.byref(w)) == vq.ERR_ARG
+    assert vq.lib.vq_decode_error_word(ctypes.byref(M), 4, None, ctypes.byref(w)) == vq.ERR_ARG
+    assert vq.lib.vq_decode_error_word(ctypes.byref(M), 4, FAKE, None) == vq.ERR_ARG
+
+
+def test_decode_timed_needs_events():
+    M, keep = _model()
+    n4 = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 4)
+    ev = (ctypes.c_void_p * 17)(*([FAKE] * 17))
+    nl = ctypes.c_int32(-1)
+    assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, 0, FAKE, n4, None, ev, 17,
+                                       ctypes.byref(nl)) == vq.ERR_ARG       # 18 needed for 9 stages
+    ev2 = (ctypes.c_void_p * 18)(*([FAKE] * 17 + [None]))
+    assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, 0, FAKE, n4, None, ev2, 18,
+                                       ctypes.byref(nl)) == vq.ERR_ARG       # a NULL event
+    assert nl.value == -1

@@ -70,17 +70,22 @@ def _check_glue(xin, expect, what):
     assert not bad.any()
 
 
+LAUNCHES = [4, 8]          # staged, persistent
+
+
+@pytest.mark.parametrize("launch", LAUNCHES)
 @pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_MXFP4])
 @pytest.mark.parametrize("K,path", [(1, 1), (4, 1), (8, 1), (4, 2), (16, 2)])
-def test_mini_model_every_stage(fmt, K, path):
+def test_mini_model_every_stage(fmt, K, path, launch):
     """A 2-layer stack (hidden 256, kv 64, ffn 512, vocab 1000): all rows of all stages."""
     torch = need_gpu()
     import speculative_decoding_verification_bit_amd as vq
     shape, seed = synth.SHAPE_MINI, 4
     model = upload_model(shape, fmt, seed)
     x0 = synth.activations(seed, K, shape.hidden)
-    logits, ws = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=path)
+    logits, ws = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=path | launch)
     torch.cuda.synchronize()
+    assert model.barrier_error(K, ws) == 0
     prev = None
     for s in range(4 * shape.n_layers + 1):
         xin, out = _stage_io(model, shape, K, ws, logits, s)
@@ -120,6 +125,16 @@ def test_27b_stack_sampled_rows(fmt, Ks):
         x0 = synth.activations(seed, K, shape.hidden)
         logits, ws = vq.decode_pass(model, torch.from_numpy(x0).cuda())
         torch.cuda.synchronize()
+        # the other launch mode computes the same sums in the same order: identical bits
+        other = vq.LAUNCH_PERSISTENT
+        logits_st, ws_st = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=other)
+        torch.cuda.synchronize()
+        assert model.barrier_error(K, ws_st) == 0
+        assert torch.equal(logits, logits_st), f"K {K}: staged and persistent logits differ"
+        for s in stages:
+            assert all(np.array_equal(u.view(np.uint8), v.view(np.uint8)) for u, v in
+                       zip(_stage_io(model, shape, K, ws, logits, s), _stage_io(model, shape, K, ws_st, logits_st, s)))
+        del ws_st, logits_st
         for s in stages:
             xin, out = _stage_io(model, shape, K, ws, logits, s)
             if s > 0:
@@ -129,3 +144,72 @@ def test_27b_stack_sampled_rows(fmt, Ks):
             check_rows(out[:, picks[s]], y_ref, a_ref, f"27B fmt {fmt} K {K} stage {s}")
         del ws, logits
         torch.cuda.empty_cache()
+
+
+def test_graph_replay_matches_eager():
+    """A captured HIP graph of decode_pass + verify_accept, replayed several times with eager
+    work in between, reproduces the eager result bitwise on every replay."""
+    torch = need_gpu()
+    import speculative_decoding_verification_bit_amd as vq
+    shape, seed, K = synth.SHAPE_MINI, 6, 4
+    model = upload_model(shape, synth.FMT_Q4_MIN, seed)
+    V = shape.vocab
+    x0 = torch.from_numpy(synth.activations(seed, K, shape.hidden)).cuda()
+    logits = torch.empty((K, V), dtype=torch.float32, device="cuda")
+    ws = torch.empty(model.workspace_bytes(K), dtype=torch.uint8, device="cuda")
+    t = logits.view(1, K, V)
+    d = torch.from_numpy(synth.window_logits(synth.LogitSpec(seed, K, V, 2.0, 0.5), 0)[1][None]).cuda()
+    kw = dict(draft_mode=vq.DRAFT_Q_SAMPLE, T=0.8, top_p=0.9, min_p=0.02, seed=3)
+    out = vq.verify_accept(vq.MODE_SAMPLE, t, d, **kw)
+    aws = torch.empty(vq.workspace_bytes(vq.OP_ACCEPT, vq.accept_desc(1, t, d, out["draft_tokens"]), K),
+                      dtype=torch.uint8, device="cuda")
+
+    def step():
+        vq.decode_pass(model, x0, logits, ws=ws)
+        vq.verify_accept(vq.MODE_SAMPLE, t, d, draft_tokens=out["draft_tokens"], ws=aws, out=out, **kw)
+
+    step()
+    torch.cuda.synchronize()
+    ref_logits = logits.clone()
+    ref_tokens = out["tokens"].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        logits.fill_(float("nan"))
+        out["tokens"].fill_(-7)
+        scratch = torch.randn(1 << 20, device="cuda") * 3      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits, ref_logits), f"replay {rep}: logits differ"
+        assert torch.equal(out["tokens"], ref_tokens), f"replay {rep}: tokens differ"
+        del scratch
+
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+def test_workspace_reuse_with_new_inputs(launch):
+    """A pass over a workspace that still holds another input's pass gives the same bits
+    as a pass over a fresh workspace: nothing stale is read back from the previous pass."""
+    torch = need_gpu()
+    import speculative_decoding_verification_bit_amd as vq
+    shape, seed, K = synth.SHAPE_MINI, 7, 4
+    model = upload_model(shape, synth.FMT_Q4_MIN, seed)
+    xa = torch.from_numpy(synth.activations(seed, K, shape.hidden)).cuda()
+    xb = torch.from_numpy(synth.activations(seed + 1, K, shape.hidden)).cuda()
+    logits, ws = vq.decode_pass(model, xa, path=launch)
+    for _ in range(3):
+        vq.decode_pass(model, xb, logits, path=launch, ws=ws)
+        torch.cuda.synchronize()
+        ref, ws_ref = vq.decode_pass(model, xb, path=vq.LAUNCH_STAGED)
+        torch.cuda.synchronize()
+        assert torch.equal(logits, ref)
+        for s in range(4 * shape.n_layers + 1):
+            for u, v in zip(_stage_io(model, shape, K, ws, logits, s), _stage_io(model, shape, K, ws_ref, ref, s)):
+                assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), f"stage {s}"
+        xa, xb = xb, xa
