@@ -84,8 +84,8 @@ typedef struct vq_matrix {
 /* Launch strategy of vq_decode_pass, OR-ed into `path` (vq_verify_linear takes 0). */
 #define VQ_LAUNCH_AUTO 0        /* the faster of the two on MI355X: staged */
 #define VQ_LAUNCH_STAGED 4      /* one launch per stage */
-#define VQ_LAUNCH_PERSISTENT 8  /* one cooperative launch per 8 layers; grid barriers
-                                   between the stages inside a launch */
+#define VQ_LAUNCH_PERSISTENT 8  /* one cooperative launch per 8 layers; inside it, a
+                                   stage waits on the completion counts of the previous one */
 
 #define VQ_MAX_K 16
 
@@ -107,7 +107,8 @@ typedef struct vq_matrix {
  * Errors: VQ_ERR_ARG for NULL pointers (except ws when the size query is 0), K outside
  * 1..16, cols not a positive multiple of 32, rows < 0, misaligned pointers, an unknown
  * format/dtype/path or mins inconsistent with the format; VQ_ERR_UNSUPPORTED for
- * VQ_PATH_VALU with K > 8; VQ_ERR_WORKSPACE; VQ_ERR_HIP.
+ * VQ_PATH_VALU with K > 8 or a matrix whose codes take 2 GiB or more; VQ_ERR_WORKSPACE;
+ * VQ_ERR_HIP.
  * rows == 0 is valid and enqueues nothing.
  */
 int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y,

@@ -35,6 +35,8 @@ int check_matrix(const vq_matrix* W, const char* name) {
     if (W->cols <= 0 || W->cols % 32)
         return fail(VQ_ERR_ARG, "%s: cols %d is not a positive multiple of 32", name, W->cols);
     if (W->rows == 0) return VQ_OK;
+    if ((int64_t)W->rows * (W->cols / 2) >= ((int64_t)1 << 31))
+        return fail(VQ_ERR_UNSUPPORTED, "%s: codes of %d x %d exceed 2 GiB", name, W->rows, W->cols);
     if (!W->qs || !W->scales) return fail(VQ_ERR_ARG, "%s: NULL qs or scales", name);
     if ((W->format == VQ_FMT_Q4_MIN) != (W->mins != nullptr))
         return fail(VQ_ERR_ARG, "%s: mins must be given exactly for VQ_FMT_Q4_MIN", name);
@@ -396,6 +398,11 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
     P.done = persistent ? sync + d.done_word : nullptr;
     P.coh = persistent ? 1 : 0;
     P.lm = MatPtrs{M->lm_head.qs, M->lm_head.scales, M->lm_head.mins};
+    for (int j = 0; j < 5; ++j) {
+        const int st = j == 4 ? 4 * s.L : j;
+        const StageShape ss = stage_shape(s, st);
+        P.cpw[j] = stage_geom(ss.rows, ss.cols, j == 2, j == 2 ? s.FF : 0).cpw;
+    }
     int nl = 0;
     for (int l0 = 0; l0 < s.L; l0 += PASS_LAYERS) {
         P.layer0 = l0;

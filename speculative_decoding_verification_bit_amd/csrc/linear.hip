@@ -45,6 +45,7 @@ typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 __device__ __forceinline__ h8_t as_h8(u4_t v) { return __builtin_bit_cast(h8_t, v); }
@@ -157,15 +158,29 @@ __device__ __forceinline__ int clamp_row(const StageArgs& A, int t, int r) {
     return min(64 * t + r, A.W.rows - 1);
 }
 
-struct RowPtr {
-    const uint8_t* qs;       // start of the row's codes
-    const uint8_t* sc8;      // start of the row's scales (bytes)
-    const uint16_t* mn;      // start of the row's mins (or NULL)
+// Loads through global (not flat) pointers.  The compiler cannot always prove that a
+// weight pointer is global; a flat load would also count against the LDS / scalar-load
+// counter, so every LDS wait would wait for the weights in flight as well.
+#define GLOBAL_AS __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ T ld_global(const void* p) {
+    return *(const GLOBAL_AS T*)p;          // an address-space cast (no instruction)
+}
+template <typename T>
+__device__ __forceinline__ T ld_global_nt(const void* p) {
+    return __builtin_nontemporal_load((const GLOBAL_AS T*)p);
+}
+
+// Base addresses of one segment (uniform); a row's data lies at 32-bit offsets from them
+// (a matrix's codes stay below 2 GiB), which lets the loads take the base in scalar
+// registers and only the offset in a vector register.
+struct SegRef {
+    const uint8_t* qs;       // codes, rows of cols / 2 bytes
+    const uint8_t* sc8;      // scales, rows of nb fp16 (nb bytes for E8M0)
+    const uint16_t* mn;      // mins, rows of nb fp16 (or NULL)
+    int r0;                  // first row of the segment
 };
 
-// Segment of the rows that local row r of tile t reads: uniform over a wave, because the
-// boundaries of a multi-segment matrix are multiples of 64 rows and a paired tile takes
-// rows r < 32 from segment 0 and r >= 32 from segment 1.
 __device__ __forceinline__ int tile_seg(const StageArgs& A, int t, int r) {
     if (A.paired) return r < 32 ? 0 : 1;
     const int row0 = 64 * t;
@@ -178,27 +193,22 @@ __device__ __forceinline__ int tile_seg(const StageArgs& A, int t, int r) {
 // builds one per stage) out to scratch memory.
 template <typename T>
 __device__ __forceinline__ T opaque(T v) {
-    asm volatile("" : "+r"(v));
+    asm volatile("" : "+s"(v));
     return v;
 }
 
-// Row pointers of `row`, which lies in segment `seg` (uniform).
-__device__ __forceinline__ RowPtr row_ptr(const Mat& W, int seg, int row) {
+// Segment `seg` (uniform) of W.
+__device__ __forceinline__ SegRef seg_ref(const Mat& W, int seg) {
     const uint8_t* q[3] = {opaque(W.qs[0]), opaque(W.qs[1]), opaque(W.qs[2])};
     const void* c[3] = {opaque(W.scales[0]), opaque(W.scales[1]), opaque(W.scales[2])};
     const uint16_t* m[3] = {opaque(W.mins[0]), opaque(W.mins[1]), opaque(W.mins[2])};
     const int e0 = opaque(W.seg_end[0]), e1 = opaque(W.seg_end[1]);
-    const uint8_t* qs = seg == 2 ? q[2] : seg == 1 ? q[1] : q[0];
-    const void* sc = seg == 2 ? c[2] : seg == 1 ? c[1] : c[0];
-    const uint16_t* mn = seg == 2 ? m[2] : seg == 1 ? m[1] : m[0];
-    const int r0 = seg == 2 ? e1 : seg == 1 ? e0 : 0;
-    const size_t lr = (size_t)(row - r0);
-    const size_t nb = (size_t)(W.cols >> 5);
-    RowPtr p;
-    p.qs = qs + lr * (size_t)(W.cols >> 1);
-    p.sc8 = (const uint8_t*)sc + lr * nb * (W.fmt == VQ_FMT_MXFP4 ? 1 : 2);
-    p.mn = mn ? mn + lr * nb : nullptr;
-    return p;
+    SegRef r;
+    r.qs = seg == 2 ? q[2] : seg == 1 ? q[1] : q[0];
+    r.sc8 = (const uint8_t*)(seg == 2 ? c[2] : seg == 1 ? c[1] : c[0]);
+    r.mn = seg == 2 ? m[2] : seg == 1 ? m[1] : m[0];
+    r.r0 = seg == 2 ? e1 : seg == 1 ? e0 : 0;
+    return r;
 }
 
 // ------------------------------------------------------------------ stage glue
@@ -227,29 +237,6 @@ __device__ void stage_rms(const StageArgs& A, float* rs, float* sh) {
     __syncthreads();
 }
 
-// Input activations (k, col .. col + 7) as fp16 bits: the fp16 input, or fp16(v * rs[k])
-// of the raw previous output v.
-__device__ __forceinline__ void load_x8(const StageArgs& A, const float* rs, int k, int col,
-                                        uint32_t (&h)[8]) {
-    if (A.glue == GLUE_NONE) {
-        const u4_t v = *reinterpret_cast<const u4_t*>(A.x16 + (size_t)k * A.W.cols + col);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            h[2 * e] = v[e] & 0xffffu;
-            h[2 * e + 1] = v[e] >> 16;
-        }
-    } else {
-        const float* p = A.src + (size_t)k * A.ld + col;
-        const f4_t a = *reinterpret_cast<const f4_t*>(p), b = *reinterpret_cast<const f4_t*>(p + 4);
-        const float r = rs[k];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            h[e] = f2h_bits(a[e] * r);
-            h[4 + e] = f2h_bits(b[e] * r);
-        }
-    }
-}
-
 __device__ __forceinline__ void keep_x8(const StageArgs& A, int k, int col, const uint32_t (&h)[8]) {
     u4_t v;
 #pragma unroll
@@ -260,9 +247,9 @@ __device__ __forceinline__ void keep_x8(const StageArgs& A, int k, int col, cons
 // ------------------------------------------------------------------ epilogue
 
 // red[w][k][l] (w < 4 waves, k < K, l < 64 local rows) holds this workgroup's partials
-// for (tile, chunk).  Writes y (and the tile's sums of squares) once all chunks of the
+// for (tile, part).  Writes y (and the tile's sums of squares) once all parts of the
 // tile are in.
-__device__ void stage_epilogue(const StageArgs& A, int tile, int chunk, int nchunks,
+__device__ void stage_epilogue(const StageArgs& A, int tile, int part, int nparts,
                                float (*red)[16][65], float (*fin)[64], int* s_last) {
     const int K = A.K, rows = A.W.rows;
     for (int e = threadIdx.x; e < K * 64; e += 256) {
@@ -270,7 +257,7 @@ __device__ void stage_epilogue(const StageArgs& A, int tile, int chunk, int nchu
         fin[k][l] = ((red[0][k][l] + red[1][k][l]) + red[2][k][l]) + red[3][k][l];
     }
     __syncthreads();
-    if (nchunks > 1) {
+    if (nparts > 1) {
         // Partials, the counter and the last arriver's reads all use device-scope relaxed
         // atomics, which gfx950 performs coherently across XCDs without flushing or
         // invalidating the L2; s_waitcnt 0 makes each thread's partial stores complete
@@ -278,14 +265,14 @@ __device__ void stage_epilogue(const StageArgs& A, int tile, int chunk, int nchu
         for (int e = threadIdx.x; e < K * 64; e += 256) {
             const int k = e >> 6, l = e & 63;
             if (row_ok(A, tile, l))
-                __hip_atomic_store(&A.part[((size_t)chunk * K + k) * rows + out_row(A, tile, l)], fin[k][l],
+                __hip_atomic_store(&A.part[((size_t)part * K + k) * rows + out_row(A, tile, l)], fin[k][l],
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (threadIdx.x == 0)
             *s_last = __hip_atomic_fetch_add(&A.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                      (unsigned)(nchunks - 1);
+                      (unsigned)(nparts - 1);
         __syncthreads();
         if (!*s_last) return;
         for (int e = threadIdx.x; e < K * 64; e += 256) {
@@ -293,7 +280,7 @@ __device__ void stage_epilogue(const StageArgs& A, int tile, int chunk, int nchu
             float v = 0.f;
             if (row_ok(A, tile, l)) {
                 const int row = out_row(A, tile, l);
-                for (int c = 0; c < nchunks; ++c)
+                for (int c = 0; c < nparts; ++c)
                     v += __hip_atomic_load(&A.part[((size_t)c * K + k) * rows + row], __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -350,24 +337,29 @@ struct WTileV {
 
 template <int FMT>
 __device__ __forceinline__ void load_tile_valu(const StageArgs& A, int tile, int s, int bcl, WTileV& T) {
+    tile = opaque(tile);          // row addresses are recomputed per chunk, not kept live
+    const uint32_t rowq = (uint32_t)A.W.cols >> 1, nb = (uint32_t)A.W.cols >> 5;
+    const uint32_t b = (uint32_t)bcl;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const RowPtr rp = row_ptr(A.W, tile_seg(A, tile, 8 * i), clamp_row(A, tile, 8 * i + s));
-        T.w[i] = __builtin_nontemporal_load(reinterpret_cast<const u4_t*>(rp.qs) + bcl);
+        const SegRef R = seg_ref(A.W, tile_seg(A, tile, 8 * i));
+        const uint32_t lr = (uint32_t)(clamp_row(A, tile, 8 * i + s) - R.r0);
+        T.w[i] = ld_global_nt<u4_t>(R.qs + (lr * rowq + 16u * b));
         if constexpr (FMT == VQ_FMT_MXFP4) {
-            T.sr[i] = rp.sc8[bcl];
+            T.sr[i] = ld_global<uint8_t>(R.sc8 + (lr * nb + b));
             T.mr[i] = 0u;
         } else {
-            T.sr[i] = reinterpret_cast<const uint16_t*>(rp.sc8)[bcl];
-            T.mr[i] = FMT == VQ_FMT_Q4_MIN ? (uint32_t)rp.mn[bcl] : 0u;
+            T.sr[i] = ld_global<uint16_t>(R.sc8 + 2u * (lr * nb + b));
+            T.mr[i] = FMT == VQ_FMT_Q4_MIN ? (uint32_t)ld_global<uint16_t>(R.mn + (lr * nb + b)) : 0u;
         }
     }
 }
 
+// acc[k][i] += this lane's block term for row 8i + s (summed over the 8 block lanes later).
 template <int FMT, int K>
 __device__ __forceinline__ void compute_tile_valu(const StageArgs& A, int tile, int s, bool live, const WTileV& T,
                                                   const uint32_t (&xv)[K][16], const float (&bs)[K],
-                                                  float (&out)[K][8]) {
+                                                  float (&acc)[K][8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float t[K];
@@ -394,7 +386,7 @@ __device__ __forceinline__ void compute_tile_valu(const StageArgs& A, int tile, 
         for (int k = 0; k < K; ++k) {
             float v = d * t[k];
             if constexpr (FMT == VQ_FMT_Q4_MIN) v = fmaf(m, bs[k], v);
-            out[k][i] = sum8(v);
+            acc[k][i] += v;
         }
     }
 }
@@ -407,10 +399,11 @@ struct StageSmem {
     int last;
 };
 
-// One item: a 64-row tile x one chunk (4 groups of 8 blocks, one group per wave).
-// Lane 8s + c owns block c of the wave's group for rows 8i + s of the tile.
-// The weights of item (tile, chunk) for this lane: issued ahead of the item, so that
-// their latency overlaps other work (the previous item's epilogue, a wait for inputs).
+// One item: a 64-row tile x a run of chunks [part * cpw, part * cpw + cpw) (a chunk is
+// 4 groups of 8 blocks, one group per wave).  Lane 8s + c owns block c of the wave's
+// group for rows 8i + s of the tile.
+//
+// The weights of one chunk for this lane.
 template <int FMT>
 __device__ __forceinline__ void prefetch_valu(const StageArgs& A, int tile, int chunk, WTileV& T) {
     const int nb = A.W.cols >> 5;
@@ -420,91 +413,133 @@ __device__ __forceinline__ void prefetch_valu(const StageArgs& A, int tile, int 
     load_tile_valu<FMT>(A, tile, lane >> 3, b < nb ? b : nb - 1, T);
 }
 
-// rs (sm.rs) must hold the stage's input scales (stage_rms); mid() runs once the item's
-// weights are consumed, before its epilogue.
-template <int FMT, int K, typename F>
-__device__ void stage_item_valu(const StageArgs& A, int tile, int chunk, int nchunks, StageSmem& sm,
-                                uint2 (&xs)[4][K][8][8], const WTileV& cur, F&& mid) {
+// Whether a chunk's compute overlaps the loads of the next weights (two register tiles
+// per lane), or the next weights are loaded after it (one tile, more workgroups per CU).
+#ifndef VQ_PREFETCH_NEXT
+#define VQ_PREFETCH_NEXT 0
+#endif
+constexpr bool PREFETCH_NEXT = VQ_PREFETCH_NEXT != 0;
+
+// Orders one wave's LDS writes before its later LDS reads (the wave's own region only).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// On entry `cur` holds the item's first chunk and sm.rs the stage's input scales.  Each
+// chunk's activations are loaded and converted, then the next weights are issued (the
+// next chunk, else the first chunk of item (ntile, npart) unless ntile < 0), then the
+// chunk is computed; on return `cur` holds those next weights.
+template <int FMT, int K, bool MULTI>
+__device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile, int part, StageSmem& sm,
+                                uint2 (&xs)[4][K][8][8], WTileV& cur, int ntile, int npart) {
     float (*red)[16][65] = sm.red;
     float (*fin)[64] = sm.fin;
     const float* rs = sm.rs;
-    const int nb = A.W.cols >> 5;
+    const int nb = g.nb;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int s = lane >> 3, c = lane & 7;
-    const int b = (chunk * 4 + wave) * 8 + c;
-    const bool live = b < nb;
-    const int bcl = live ? b : nb - 1;
-
-    // The K activation columns of the wave's 8 blocks: lane (s, c) converts elements
-    // 4s..4s+3 of block c and the wave shares them through LDS; each lane then holds its
-    // block's 32 activations per column in the widened pair order.
-    const bool keeper = A.keep && tile == 0 && live;
-    float bs[K];
+    // MULTI = false: one chunk per item (cpw == 1), compiled without the loop, which
+    // keeps far fewer registers live
+    const int c0 = part * g.cpw, c1 = MULTI ? min(g.nchunks, c0 + g.cpw) : c0 + 1;
+    float acc[K][8];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        uint32_t h[4];
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[k][i] = 0.f;
+    for (int ch = c0; ch < c1; ++ch) {
+        const int b = (ch * 4 + wave) * 8 + c;
+        const bool live = b < nb;
+        const int bcl = live ? b : nb - 1;
         const int col = 32 * bcl + 4 * s;
-        if (A.glue == GLUE_NONE) {
-            const uint2 v = *reinterpret_cast<const uint2*>(A.x16 + (size_t)k * A.W.cols + col);
-            h[0] = v.x & 0xffffu; h[1] = v.x >> 16; h[2] = v.y & 0xffffu; h[3] = v.y >> 16;
-        } else {
-            const f4_t v = *reinterpret_cast<const f4_t*>(A.src + (size_t)k * A.ld + col);
+        // this chunk's activations: lane (s, c) takes elements 4s..4s+3 of block c
+        uint2 r16[K];
+        f4_t r32[K];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) h[e] = f2h_bits(v[e] * rs[k]);
+        for (int k = 0; k < K; ++k) {
+            if (A.glue == GLUE_NONE) r16[k] = *reinterpret_cast<const uint2*>(A.x16 + (size_t)k * A.W.cols + col);
+            else r32[k] = *reinterpret_cast<const f4_t*>(A.src + (size_t)k * A.ld + col);
         }
-        const uint2 pk = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        xs[wave][k][c][s] = pk;
-        if (keeper) *reinterpret_cast<uint2*>(A.keep + (size_t)k * A.W.cols + col) = pk;
-        float sum = (half_bits_to_float(h[0]) + half_bits_to_float(h[1])) +
-                    (half_bits_to_float(h[2]) + half_bits_to_float(h[3]));
-        sum += __shfl_xor(sum, 8, 64);
-        sum += __shfl_xor(sum, 16, 64);
-        sum += __shfl_xor(sum, 32, 64);
-        bs[k] = live ? sum : 0.f;
-    }
-    __syncthreads();
-    uint32_t xv[K][16];
+        // fp16 inputs; the wave shares them through LDS, so that each lane then holds its
+        // block's 32 activations per column in the widened pair order
+        const bool keeper = A.keep && tile == 0 && live;
+        float bs[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        uint32_t h[32];
+        for (int k = 0; k < K; ++k) {
+            uint32_t h[4];
+            if (A.glue == GLUE_NONE) {
+                h[0] = r16[k].x & 0xffffu; h[1] = r16[k].x >> 16; h[2] = r16[k].y & 0xffffu; h[3] = r16[k].y >> 16;
+            } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint2 v = xs[wave][k][c][q];
-            h[4 * q] = v.x & 0xffffu; h[4 * q + 1] = v.x >> 16;
-            h[4 * q + 2] = v.y & 0xffffu; h[4 * q + 3] = v.y >> 16;
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint32_t lo = h[8 * g + slot_col<FMT>(2 * t)], hi = h[8 * g + slot_col<FMT>(2 * t + 1)];
-                xv[k][4 * g + t] = live ? (lo | (hi << 16)) : 0u;
+                for (int e = 0; e < 4; ++e) h[e] = f2h_bits(r32[k][e] * rs[k]);
             }
-    }
-    float out[K][8];
-    compute_tile_valu<FMT, K>(A, tile, s, live, cur, xv, bs, out);
-    if (c == 0) {
+            const uint2 pk = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+            xs[wave][k][c][s] = pk;
+            if (keeper) *reinterpret_cast<uint2*>(A.keep + (size_t)k * A.W.cols + col) = pk;
+            float sum = (half_bits_to_float(h[0]) + half_bits_to_float(h[1])) +
+                        (half_bits_to_float(h[2]) + half_bits_to_float(h[3]));
+            sum += __shfl_xor(sum, 8, 64);
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            bs[k] = live ? sum : 0.f;
+        }
+        wave_lds_sync();
+        uint32_t xv[K][16];
 #pragma unroll
-        for (int k = 0; k < K; ++k)
+        for (int k = 0; k < K; ++k) {
+            uint32_t h[32];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) red[wave][k][8 * i + s] = out[k][i];
+            for (int q = 0; q < 8; ++q) {
+                const uint2 v = xs[wave][k][c][q];
+                h[4 * q] = v.x & 0xffffu; h[4 * q + 1] = v.x >> 16;
+                h[4 * q + 2] = v.y & 0xffffu; h[4 * q + 3] = v.y >> 16;
+            }
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t lo = h[8 * gg + slot_col<FMT>(2 * t)], hi = h[8 * gg + slot_col<FMT>(2 * t + 1)];
+                    xv[k][4 * gg + t] = live ? (lo | (hi << 16)) : 0u;
+                }
+        }
+        wave_lds_sync();
+        if constexpr (PREFETCH_NEXT) {
+            // the next weights load while this chunk is computed (issued only now: a wait
+            // for the activations above would otherwise also wait for them)
+            WTileV nxt;
+            if (ch + 1 < c1) prefetch_valu<FMT>(A, tile, ch + 1, nxt);
+            else if (ntile >= 0) prefetch_valu<FMT>(A, ntile, npart * g.cpw, nxt);
+            compute_tile_valu<FMT, K>(A, tile, s, live, cur, xv, bs, acc);
+            cur = nxt;
+        } else {
+            compute_tile_valu<FMT, K>(A, tile, s, live, cur, xv, bs, acc);
+            if (ch + 1 < c1) prefetch_valu<FMT>(A, tile, ch + 1, cur);
+            else if (ntile >= 0) prefetch_valu<FMT>(A, ntile, npart * g.cpw, cur);
+        }
     }
-    mid();
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = sum8(acc[k][i]);
+            if (c == 0) red[wave][k][8 * i + s] = v;
+        }
     __syncthreads();
-    stage_epilogue(A, tile, chunk, nchunks, red, fin, &sm.last);
+    stage_epilogue(A, tile, part, g.nparts, red, fin, &sm.last);
 }
 
-template <int FMT, int K>
-__global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, int nchunks) {
+template <int FMT, int K, bool MULTI>
+__global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, const StageGeom g) {
     __shared__ StageSmem sm;
     __shared__ uint2 xs[4][K][8][8];          // [wave][column][block][quarter of 4 fp16]
     const int item = xcd_item(blockIdx.x, gridDim.x);
-    const int tile = item / nchunks, chunk = item - tile * nchunks;
+    const int tile = item / g.nparts, part = item - tile * g.nparts;
     WTileV cur;
-    prefetch_valu<FMT>(A, tile, chunk, cur);
+    prefetch_valu<FMT>(A, tile, part * g.cpw, cur);
     stage_rms(A, sm.rs, &sm.red[0][0][0]);
-    stage_item_valu<FMT, K>(A, tile, chunk, nchunks, sm, xs, cur, [] {});
+    stage_item_valu<FMT, K, MULTI>(A, g, tile, part, sm, xs, cur, -1, 0);
 }
 
 // ------------------------------------------------------------------ MFMA kernel
@@ -551,25 +586,29 @@ template <int FMT>
 __device__ __forceinline__ void load_tile_mfma(const StageArgs& A, int tile, int j, int gq, int b0, int nvb,
                                                bool al, WTileM& T) {
     const int nb = A.W.cols >> 5;
+    const uint32_t rowq = (uint32_t)A.W.cols >> 1, unb = (uint32_t)nb;
     const int bb0 = min(b0, nb - 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const RowPtr rp = row_ptr(A.W, tile_seg(A, tile, 16 * t), clamp_row(A, tile, 16 * t + j));
-        T.n0[t] = reinterpret_cast<const u4_t*>(rp.qs)[min(b0 + gq, nb - 1)];
-        T.n1[t] = reinterpret_cast<const u4_t*>(rp.qs)[min(b0 + 4 + gq, nb - 1)];
+        const SegRef R = seg_ref(A.W, tile_seg(A, tile, 16 * t));
+        const uint32_t lr = (uint32_t)(clamp_row(A, tile, 16 * t + j) - R.r0);
+        const uint32_t qrow = lr * rowq;
+        T.n0[t] = ld_global_nt<u4_t>(R.qs + (qrow + 16u * (uint32_t)min(b0 + gq, nb - 1)));
+        T.n1[t] = ld_global_nt<u4_t>(R.qs + (qrow + 16u * (uint32_t)min(b0 + 4 + gq, nb - 1)));
+        const uint32_t srow = lr * unb * (FMT == VQ_FMT_MXFP4 ? 1u : 2u), mrow = 2u * lr * unb;
         if (al && nvb == 8) {
             if constexpr (FMT == VQ_FMT_MXFP4) {
-                const uint2 v = *reinterpret_cast<const uint2*>(rp.sc8 + b0);
-                T.sv[t][0] = v.x;
-                T.sv[t][1] = v.y;
+                const u2_t v = ld_global<u2_t>(R.sc8 + (srow + (uint32_t)b0));
+                T.sv[t][0] = v[0];
+                T.sv[t][1] = v[1];
                 T.sv[t][2] = T.sv[t][3] = 0u;
             } else {
-                const u4_t v = *reinterpret_cast<const u4_t*>(rp.sc8 + 2 * b0);
+                const u4_t v = ld_global<u4_t>(R.sc8 + (srow + 2u * (uint32_t)b0));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) T.sv[t][e] = v[e];
             }
             if constexpr (FMT == VQ_FMT_Q4_MIN) {
-                const u4_t v = *reinterpret_cast<const u4_t*>(rp.mn + b0);
+                const u4_t v = ld_global<u4_t>(reinterpret_cast<const uint8_t*>(R.mn) + (mrow + 2u * (uint32_t)b0));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) T.mv[t][e] = v[e];
             } else {
@@ -581,10 +620,13 @@ __device__ __forceinline__ void load_tile_mfma(const StageArgs& A, int tile, int
             uint32_t sb[8], mb[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int bb = min(bb0 + i, nb - 1);
-                if constexpr (FMT == VQ_FMT_MXFP4) sb[i] = rp.sc8[bb];
-                else sb[i] = reinterpret_cast<const uint16_t*>(rp.sc8)[bb];
-                mb[i] = FMT == VQ_FMT_Q4_MIN ? (uint32_t)rp.mn[bb] : 0u;
+                const uint32_t bb = (uint32_t)min(bb0 + i, nb - 1);
+                if constexpr (FMT == VQ_FMT_MXFP4) sb[i] = ld_global<uint8_t>(R.sc8 + (srow + bb));
+                else sb[i] = ld_global<uint16_t>(R.sc8 + (srow + 2u * bb));
+                if constexpr (FMT == VQ_FMT_Q4_MIN)
+                    mb[i] = ld_global<uint16_t>(reinterpret_cast<const uint8_t*>(R.mn) + (mrow + 2u * bb));
+                else
+                    mb[i] = 0u;
                 if (i >= nvb) sb[i] = mb[i] = 0u;
             }
             if constexpr (FMT == VQ_FMT_MXFP4) {
@@ -607,7 +649,6 @@ __device__ __forceinline__ void compute_tile_mfma(const WTileM& T, int gq, int n
     const f4_t zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        acc[t] = zero;
         uint32_t T0[4] = {T.n0[t][0], T.n0[t][1], T.n0[t][2], T.n0[t][3]};
         uint32_t T1[4] = {T.n1[t][0], T.n1[t][1], T.n1[t][2], T.n1[t][3]};
         transpose4(T0);
@@ -648,80 +689,120 @@ __device__ __forceinline__ void prefetch_mfma(const StageArgs& A, int tile, int 
     load_tile_mfma<FMT>(A, tile, lane & 15, lane >> 4, b0, max(0, min(8, nb - b0)), (nb & 7) == 0, T);
 }
 
-// As stage_item_valu: sm.rs holds the input scales, mid() runs before the epilogue.
-template <int FMT, typename F>
-__device__ void stage_item_mfma(const StageArgs& A, int tile, int chunk, int nchunks, StageSmem& sm,
-                                const WTileM& cur, F&& mid) {
+// As stage_item_valu (the same chunk run, load order and next-weights contract); the
+// MFMA accumulators carry the sums across the run.
+template <int FMT, bool MULTI>
+__device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile, int part, StageSmem& sm,
+                                WTileM& cur, int ntile, int npart) {
     float (*red)[16][65] = sm.red;
     float (*fin)[64] = sm.fin;
     const float* rs = sm.rs;
     const int K = A.K;
-    const int nb = A.W.cols >> 5;
+    const int nb = g.nb;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int j = lane & 15, gq = lane >> 4;
-    const int b0 = (chunk * 4 + wave) * 8;
-    const int nvb = max(0, min(8, nb - b0));          // blocks of this group (wave-uniform)
-    const bool al = (nb & 7) == 0;
-    const int bb0 = min(b0, nb - 1);
-    (void)al;
-
-    // A operands: activation column j, k-quarter gq of each block of the group
-    h8_t a[8];
-    float bsum[8];
     const bool col_live = j < K;
     const int kk = col_live ? j : 0;
     const bool keeper = A.keep && tile == 0 && col_live;
-#pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-        const int blk = min(bb0 + tt, nb - 1);
-        uint32_t h[8];
-        load_x8(A, rs, kk, 32 * blk + 8 * gq, h);
-        if (keeper && tt < nvb) keep_x8(A, kk, 32 * blk + 8 * gq, h);
-        float sum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sum += half_bits_to_float(h[e]);
-        h8_t v;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) v[p] = __builtin_bit_cast(_Float16, (uint16_t)h[slot_col<FMT>(p)]);
-        const bool use = col_live && tt < nvb;
-        a[tt] = use ? v : h8_t{};
-        bsum[tt] = use ? sum : 0.f;
-    }
-    h8_t am = h8_t{};
-    if constexpr (FMT == VQ_FMT_Q4_MIN) {
-        // block sums over the 4 k-quarters (lanes j, j+16, j+32, j+48), then fp16 hi / lo
+    const float r = A.glue == GLUE_NONE ? 1.f : rs[kk];
+    const int c0 = part * g.cpw, c1 = MULTI ? min(g.nchunks, c0 + g.cpw) : c0 + 1;
+    const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+    f4_t acc[4] = {zero, zero, zero, zero};
+    for (int ch = c0; ch < c1; ++ch) {
+        const int b0 = (ch * 4 + wave) * 8;
+        const int nvb = max(0, min(8, nb - b0));      // blocks of this group (wave-uniform)
+        const int bb0 = min(b0, nb - 1);
+        // A operands: activation column j, k-quarter gq of each block of the group (raw
+        // values first: 8 fp16 of the input, or 8 f32 of the previous output)
+        f4_t raw[8][2];
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
-            float v = bsum[tt];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            const _Float16 hi = (_Float16)v;
-            const _Float16 lo = (_Float16)(v - (float)hi);
-            am[tt] = gq == 0 ? hi : (gq == 1 ? lo : (_Float16)0.0f);
+            const int col = 32 * min(bb0 + tt, nb - 1) + 8 * gq;
+            if (A.glue == GLUE_NONE) {
+                raw[tt][0] = __builtin_bit_cast(f4_t, *reinterpret_cast<const u4_t*>(A.x16 + (size_t)kk * A.W.cols + col));
+                raw[tt][1] = raw[tt][0];
+            } else {
+                const float* p = A.src + (size_t)kk * A.ld + col;
+                raw[tt][0] = *reinterpret_cast<const f4_t*>(p);
+                raw[tt][1] = *reinterpret_cast<const f4_t*>(p + 4);
+            }
+        }
+        h8_t a[8];
+        float bsum[8];
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            uint32_t h[8];
+            if (A.glue == GLUE_NONE) {
+                const u4_t v = __builtin_bit_cast(u4_t, raw[tt][0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[2 * e] = v[e] & 0xffffu;
+                    h[2 * e + 1] = v[e] >> 16;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = f2h_bits(raw[tt][0][e] * r);
+                    h[4 + e] = f2h_bits(raw[tt][1][e] * r);
+                }
+            }
+            if (keeper && tt < nvb) keep_x8(A, kk, 32 * (bb0 + tt) + 8 * gq, h);
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum += half_bits_to_float(h[e]);
+            h8_t v;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) v[p] = __builtin_bit_cast(_Float16, (uint16_t)h[slot_col<FMT>(p)]);
+            const bool use = col_live && tt < nvb;
+            a[tt] = use ? v : h8_t{};
+            bsum[tt] = use ? sum : 0.f;
+        }
+        h8_t am = h8_t{};
+        if constexpr (FMT == VQ_FMT_Q4_MIN) {
+            // block sums over the 4 k-quarters (lanes j, j+16, j+32, j+48), then fp16 hi / lo
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+                float v = bsum[tt];
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                const _Float16 hi = (_Float16)v;
+                const _Float16 lo = (_Float16)(v - (float)hi);
+                am[tt] = gq == 0 ? hi : (gq == 1 ? lo : (_Float16)0.0f);
+            }
+        }
+        if constexpr (PREFETCH_NEXT) {
+            // the next weights load while this chunk is computed (issued only now: a wait
+            // for the activations above would otherwise also wait for them)
+            WTileM nxt;
+            if (ch + 1 < c1) prefetch_mfma<FMT>(A, tile, ch + 1, nxt);
+            else if (ntile >= 0) prefetch_mfma<FMT>(A, ntile, npart * g.cpw, nxt);
+            compute_tile_mfma<FMT>(cur, gq, nvb, a, am, acc);
+            cur = nxt;
+        } else {
+            compute_tile_mfma<FMT>(cur, gq, nvb, a, am, acc);
+            if (ch + 1 < c1) prefetch_mfma<FMT>(A, tile, ch + 1, cur);
+            else if (ntile >= 0) prefetch_mfma<FMT>(A, ntile, npart * g.cpw, cur);
         }
     }
-    f4_t acc[4];
-    compute_tile_mfma<FMT>(cur, gq, nvb, a, am, acc);
     // lane (j, gq) holds D[4 gq + v][j] = column 4 gq + v of row 16 t + j
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave][4 * gq + v][16 * t + j] = acc[t][v];
-    mid();
     __syncthreads();
-    stage_epilogue(A, tile, chunk, nchunks, red, fin, &sm.last);
+    stage_epilogue(A, tile, part, g.nparts, red, fin, &sm.last);
 }
 
-template <int FMT>
-__global__ __launch_bounds__(256) void k_stage_mfma(const StageArgs A, int nchunks) {
+template <int FMT, bool MULTI>
+__global__ __launch_bounds__(256) void k_stage_mfma(const StageArgs A, const StageGeom g) {
     __shared__ StageSmem sm;
     const int item = xcd_item(blockIdx.x, gridDim.x);
-    const int tile = item / nchunks, chunk = item - tile * nchunks;
+    const int tile = item / g.nparts, part = item - tile * g.nparts;
     WTileM cur;
-    prefetch_mfma<FMT>(A, tile, chunk, cur);
+    prefetch_mfma<FMT>(A, tile, part * g.cpw, cur);
     stage_rms(A, sm.rs, &sm.red[0][0][0]);
-    stage_item_mfma<FMT>(A, tile, chunk, nchunks, sm, cur, [] {});
+    stage_item_mfma<FMT, MULTI>(A, g, tile, part, sm, cur, -1, 0);
 }
 
 
@@ -749,11 +830,12 @@ __device__ void wait_count(const unsigned* cnt, unsigned target, int* err) {
 }
 
 // The stages of a plan segment in one launch.  A stage's items are dealt round-robin to
-// the workgroups (those of one XCD take consecutive items, so a tile's chunks meet in one
+// the workgroups (those of one XCD take consecutive items, so a tile's parts meet in one
 // L2).  There is no grid-wide barrier: a workgroup with items in stage s issues its first
 // item's weight loads, then waits until every tile of stage s - 1 has counted itself
 // complete, then reads that stage's outputs.  Workgroups without items in a stage go
-// straight on to the next one, and every item's epilogue overlaps the next item's loads.
+// straight on to the next one, and each item's last chunk issues the loads of the
+// workgroup's next item in the stage.
 template <int FMT, int K, bool MFMA>
 __global__ __launch_bounds__(256) void k_pass(const PassPlan P) {
     __shared__ StageSmem sm;
@@ -768,32 +850,29 @@ __global__ __launch_bounds__(256) void k_pass(const PassPlan P) {
     for (int stage = s0; stage < s1; ++stage) {
         StageArgs A;
         build_stage(P, stage, A);
-        const StageGeom g = stage_geom(A.W.rows, A.W.cols, A.paired, A.paired ? A.W.seg_end[0] : 0);
-        const int nitems = g.ntiles * g.nchunks;
+        const StageGeom g = stage_geom_cpw(A.W.rows, A.W.cols, A.paired, A.paired ? A.W.seg_end[0] : 0,
+                                           P.cpw[stage == 4 * P.L ? 4 : stage & 3]);
+        const int nitems = g.ntiles * g.nparts;
         const int wait_tiles = prev_tiles;
         prev_tiles = g.ntiles;
         if (vid >= nitems) continue;
-        auto fetch = [&](int it, Tile& T) {
-            const int tile = it / g.nchunks;
-            if constexpr (MFMA) prefetch_mfma<FMT>(A, tile, it - tile * g.nchunks, T);
-            else prefetch_valu<FMT>(A, tile, it - tile * g.nchunks, T);
-        };
         Tile cur;
-        fetch(vid, cur);
+        {
+            const int tile = vid / g.nparts, part = vid - tile * g.nparts;
+            if constexpr (MFMA) prefetch_mfma<FMT>(A, tile, part * g.cpw, cur);
+            else prefetch_valu<FMT>(A, tile, part * g.cpw, cur);
+        }
         if (stage > s0)
             wait_count(P.done + (size_t)(stage - 1) * DONE_WORDS + grp * DONE_STRIDE, (unsigned)wait_tiles, P.err);
         stage_rms(A, sm.rs, &sm.red[0][0][0]);
         for (int it = vid; it < nitems; it += nwg) {
-            const int tile = it / g.nchunks;
-            Tile nxt;
-            const bool more = it + nwg < nitems;
-            auto mid = [&] {
-                if (more) fetch(it + nwg, nxt);
-            };
-            if constexpr (MFMA) stage_item_mfma<FMT>(A, tile, it - tile * g.nchunks, g.nchunks, sm, cur, mid);
-            else stage_item_valu<FMT, K>(A, tile, it - tile * g.nchunks, g.nchunks, sm, xs, cur, mid);
+            const int tile = it / g.nparts, part = it - tile * g.nparts;
+            const int nx = it + nwg;
+            const int ntile = nx < nitems ? nx / g.nparts : -1;
+            const int npart = nx < nitems ? nx - ntile * g.nparts : 0;
+            if constexpr (MFMA) stage_item_mfma<FMT, true>(A, g, tile, part, sm, cur, ntile, npart);
+            else stage_item_valu<FMT, K, true>(A, g, tile, part, sm, xs, cur, ntile, npart);
             __syncthreads();                  // LDS is reused by the next item
-            if (more) cur = nxt;
         }
     }
 }
@@ -827,7 +906,14 @@ __global__ void k_zero_u32(unsigned* p, int n) {
 
 template <int FMT, int K>
 void launch_valu_k(const StageArgs& A, int tg, const StageGeom& g, hipStream_t st) {
-    k_stage_valu<FMT, K><<<dim3(tg * g.nchunks), 256, 0, st>>>(A, g.nchunks);
+    if (g.cpw > 1) k_stage_valu<FMT, K, true><<<dim3(tg * g.nparts), 256, 0, st>>>(A, g);
+    else k_stage_valu<FMT, K, false><<<dim3(tg * g.nparts), 256, 0, st>>>(A, g);
+}
+
+template <int FMT>
+void launch_mfma_f(const StageArgs& A, const dim3& grid, const StageGeom& g, hipStream_t st) {
+    if (g.cpw > 1) k_stage_mfma<FMT, true><<<grid, 256, 0, st>>>(A, g);
+    else k_stage_mfma<FMT, false><<<grid, 256, 0, st>>>(A, g);
 }
 
 template <int FMT>
@@ -850,13 +936,13 @@ void launch_valu_f(const StageArgs& A, int tg, const StageGeom& g, hipStream_t s
 
 size_t stage_scratch_bytes(int rows, int cols, int K, int paired, int half) {
     const StageGeom g = stage_geom(rows, cols, paired, half);
-    return align_up((size_t)g.nchunks * K * rows * 4, 256) + align_up((size_t)g.ntiles * 4, 256);
+    return align_up((size_t)g.nparts * K * rows * 4, 256) + align_up((size_t)g.ntiles * 4, 256);
 }
 
 void stage_scratch_carve(void* base, int rows, int cols, int K, int paired, int half, StageArgs* A) {
     const StageGeom g = stage_geom(rows, cols, paired, half);
     A->part = (float*)base;
-    A->counters = (unsigned*)((char*)base + align_up((size_t)g.nchunks * K * rows * 4, 256));
+    A->counters = (unsigned*)((char*)base + align_up((size_t)g.nparts * K * rows * 4, 256));
 }
 
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st) {
@@ -867,14 +953,14 @@ hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st) {
 
 hipError_t launch_stage(const StageArgs& A, bool mfma, hipStream_t st) {
     const StageGeom g = stage_geom(A.W.rows, A.W.cols, A.paired, A.paired ? A.W.seg_end[0] : 0);
-    // one workgroup per (tile, chunk): many independent workgroups overlap the epilogue's
-    // atomic round trips (a tile loop inside a workgroup serialises them)
+    // one workgroup per item (a tile and a run of its chunks, sized by stage_geom)
     const int tg = g.ntiles;
+    const dim3 grid(tg * g.nparts);
     if (mfma) {
         switch (A.W.fmt) {
-            case VQ_FMT_Q4: k_stage_mfma<VQ_FMT_Q4><<<dim3(tg * g.nchunks), 256, 0, st>>>(A, g.nchunks); break;
-            case VQ_FMT_Q4_MIN: k_stage_mfma<VQ_FMT_Q4_MIN><<<dim3(tg * g.nchunks), 256, 0, st>>>(A, g.nchunks); break;
-            default: k_stage_mfma<VQ_FMT_MXFP4><<<dim3(tg * g.nchunks), 256, 0, st>>>(A, g.nchunks); break;
+            case VQ_FMT_Q4: launch_mfma_f<VQ_FMT_Q4>(A, grid, g, st); break;
+            case VQ_FMT_Q4_MIN: launch_mfma_f<VQ_FMT_Q4_MIN>(A, grid, g, st); break;
+            default: launch_mfma_f<VQ_FMT_MXFP4>(A, grid, g, st); break;
         }
     } else {
         switch (A.W.fmt) {

@@ -44,7 +44,24 @@ struct StageGeom {
     int ngroups;   // groups of 8 blocks per row
     int nchunks;   // chunks of 4 groups
     int ntiles;
+    int cpw;       // chunks per item (one workgroup's share of a tile)
+    int nparts;    // items per tile = split-K partials per output
 };
+
+// Work-splitting model: a tile's chunks are dealt out in runs of cpw chunks per item.
+// Longer runs stream more weights per workgroup between epilogues (partial exchange,
+// arrival counting), shorter runs give more items to spread over the chip.  The cost of
+// a choice is the number of rounds of ITEM_SLOTS concurrent items times a round's
+// length, counting an epilogue as EPI_COST chunks; the cheapest run length wins (ties go
+// to the shorter run).
+#ifndef VQ_ITEM_SLOTS
+#define VQ_ITEM_SLOTS 512
+#endif
+#ifndef VQ_EPI_COST
+#define VQ_EPI_COST 2
+#endif
+constexpr int ITEM_SLOTS = VQ_ITEM_SLOTS;
+constexpr int EPI_COST = VQ_EPI_COST;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -67,7 +84,7 @@ struct StageArgs {
     int nstats_in;
     uint16_t* keep;            // fp16 copy of the input [K][cols] (written by tile 0), or NULL
     // scratch
-    float* part;               // split-K partials [nchunks][K][rows]
+    float* part;               // split-K partials [nparts][K][rows]
     unsigned* counters;        // per-tile arrival counters [ntiles], zero between launches
     // output
     void* y;                   // [K][rows], f32 or f16
@@ -105,6 +122,7 @@ struct PassPlan {
     int with_lm;                   // 1: the lm_head stage ends this segment
     MatPtrs m[PASS_LAYERS][7];     // q, k, v, o, gate, up, down of layers layer0 + i
     MatPtrs lm;
+    int cpw[5];                    // chunks per item of stages q|k|v, o, gate|up, down, lm_head
     const uint16_t* x0;            // pass input fp16 [K][H]
     float* logits;                 // [K][V]
     char* base;                    // workspace
@@ -193,12 +211,33 @@ __host__ __device__ inline void build_stage(const PassPlan& P, int stage, StageA
     A.counters = P.counters;
 }
 
-__host__ __device__ inline StageGeom stage_geom(int rows, int cols, int paired, int half) {
+// Geometry with a given run length (cheap: the kernels call it).
+__host__ __device__ inline StageGeom stage_geom_cpw(int rows, int cols, int paired, int half, int cpw) {
     StageGeom g;
-    g.nb = cols / 32;
-    g.ngroups = (g.nb + 7) / 8;
-    g.nchunks = (g.ngroups + 3) / 4;
-    g.ntiles = paired ? (half + 31) / 32 : (rows + 63) / 64;
+    g.nb = cols >> 5;
+    g.ngroups = (g.nb + 7) >> 3;
+    g.nchunks = (g.ngroups + 3) >> 2;
+    g.ntiles = paired ? (half + 31) >> 5 : (rows + 63) >> 6;
+    g.cpw = cpw;
+    g.nparts = (g.nchunks + cpw - 1) / cpw;
+    return g;
+}
+
+// Geometry with the run length the work-splitting model picks (host side).
+inline StageGeom stage_geom(int rows, int cols, int paired, int half) {
+    StageGeom g = stage_geom_cpw(rows, cols, paired, half, 1);
+    long best = -1;
+    for (int c = 1; c <= g.nchunks; ++c) {
+        const int parts = (g.nchunks + c - 1) / c;
+        if (c > 1 && parts == (g.nchunks + c - 2) / (c - 1)) continue;   // same split, longer run
+        const long items = (long)g.ntiles * parts;
+        const long cost = (items + ITEM_SLOTS - 1) / ITEM_SLOTS * (long)(c + EPI_COST);
+        if (best < 0 || cost < best) {
+            best = cost;
+            g.cpw = c;
+        }
+    }
+    g.nparts = (g.nchunks + g.cpw - 1) / g.cpw;
     return g;
 }
 size_t stage_scratch_bytes(int rows, int cols, int K, int paired, int half);
