@@ -228,11 +228,15 @@ int vq_decode_error_word(const vq_model* M, int32_t K, void* ws, int32_t** word)
  *   events     : HOST array of n_events caller-created hipEvent_t handles (timing enabled)
  *   n_events   : >= 2 * (4 * n_layers + 1)
  *   n_launches : HOST out, the number of launches bracketed (may be NULL)
+ *   runs       : HOST out [n_events / 2] (may be NULL): per launch, the chunks of 1024
+ *                columns each workgroup item covers (a staged launch runs the multi-chunk
+ *                kernel when this is above 1); 0 for a persistent launch
  * Errors: as vq_decode_pass, plus VQ_ERR_ARG for a short or NULL-holding events array.
  */
 int vq_decode_pass_timed(const vq_model* M, const void* x0_f16, int32_t K, float* logits,
                          int32_t path, void* ws, size_t ws_bytes, void* stream,
-                         void* const* events, int32_t n_events, int32_t* n_launches);
+                         void* const* events, int32_t n_events, int32_t* n_launches,
+                         int32_t* runs);
 
 /*
  * vq_decode_stage_ptr -- where a decode pass left stage s's tensors inside ws.

@@ -79,7 +79,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.vq_decode_pass.argtypes = [ctypes.POINTER(VqModel), _P, I32, _P, I32, _P, SZ, _P]
     L.vq_decode_pass_timed.restype = I32
     L.vq_decode_pass_timed.argtypes = [ctypes.POINTER(VqModel), _P, I32, _P, I32, _P, SZ, _P,
-                                       ctypes.POINTER(_P), I32, ctypes.POINTER(I32)]
+                                       ctypes.POINTER(_P), I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     L.vq_decode_stage_ptr.restype = I32
     L.vq_decode_stage_ptr.argtypes = [ctypes.POINTER(VqModel), I32, _P, I32,
                                       ctypes.POINTER(_P), ctypes.POINTER(_P)]
@@ -266,18 +266,20 @@ def decode_pass(model: DeviceModel, x0, logits=None, path: int = PATH_AUTO, ws=N
 
 
 def decode_pass_timed(model: DeviceModel, x0, events, logits, ws, path: int = PATH_AUTO, stream=None):
-    """decode_pass plus HIP events around each weight-streaming launch; returns the number
-    of launches bracketed.
+    """decode_pass plus HIP events around each weight-streaming launch.  Returns the list
+    of the bracketed launches' run lengths (chunks per workgroup item; 0 for a persistent
+    launch), one per launch.
 
     events: a list of 2 * n_stages torch.cuda.Event(enable_timing=True), already recorded
     once (so that their HIP handles exist); events[2 i] / events[2 i + 1] bracket launch i."""
     K = x0.shape[0]
     arr = (_P * len(events))(*[ev.cuda_event for ev in events])
     n = ctypes.c_int32(0)
+    runs = (ctypes.c_int32 * (len(events) // 2))()
     _check(lib.vq_decode_pass_timed(ctypes.byref(model.desc), _ptr(x0), K, _ptr(logits), path, _ptr(ws),
-                                    ws.numel(), _stream(stream), arr, len(events), ctypes.byref(n)),
+                                    ws.numel(), _stream(stream), arr, len(events), ctypes.byref(n), runs),
            "vq_decode_pass_timed")
-    return n.value
+    return list(runs[:n.value])
 
 
 def stage_tensor(ws, addr: int, shape, dtype):

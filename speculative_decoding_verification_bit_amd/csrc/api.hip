@@ -349,7 +349,7 @@ int vq_decode_error_word(const vq_model* M, int32_t K, void* ws, int32_t** word)
 
 static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
                        void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t n_events,
-                       int32_t* n_launches) {
+                       int32_t* n_launches, int32_t* runs) {
     g_err[0] = 0;
     Shapes s;
     int rc = check_model(M, &s);
@@ -419,6 +419,7 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
                 e = hipEventRecord((hipEvent_t)events[2 * nl], st);
                 if (e != hipSuccess) return hip_fail(e, "event record");
             }
+            if (runs && nl < n_events / 2) runs[nl] = 0;
             e = launch_pass_segment(P, mfma, st);
             if (e != hipSuccess) return hip_fail(e, "persistent pass launch");
             if (events && 2 * nl + 1 < n_events) {
@@ -434,6 +435,7 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
                     e = hipEventRecord((hipEvent_t)events[2 * nl], st);
                     if (e != hipSuccess) return hip_fail(e, "event record");
                 }
+                if (runs && nl < n_events / 2) runs[nl] = P.cpw[stage == 4 * s.L ? 4 : stage & 3];
                 e = launch_stage(A, mfma, st);
                 if (e != hipSuccess) return hip_fail(e, "stage launch");
                 if (events && 2 * nl + 1 < n_events) {
@@ -450,17 +452,17 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
 
 int vq_decode_pass(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
                    void* ws, size_t ws_bytes, void* stream) {
-    return decode_impl(M, x0_f16, K, logits, path, ws, ws_bytes, stream, nullptr, 0, nullptr);
+    return decode_impl(M, x0_f16, K, logits, path, ws, ws_bytes, stream, nullptr, 0, nullptr, nullptr);
 }
 
 int vq_decode_pass_timed(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
                          void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t n_events,
-                         int32_t* n_launches) {
+                         int32_t* n_launches, int32_t* runs) {
     if (!events || n_events < 2 * (4 * (M ? M->n_layers : 0) + 1))
         return fail(VQ_ERR_ARG, "events must hold two HIP events per stage (begin, end)");
     for (int i = 0; i < n_events; ++i)
         if (!events[i]) return fail(VQ_ERR_ARG, "event %d is NULL", i);
-    return decode_impl(M, x0_f16, K, logits, path, ws, ws_bytes, stream, events, n_events, n_launches);
+    return decode_impl(M, x0_f16, K, logits, path, ws, ws_bytes, stream, events, n_events, n_launches, runs);
 }
 
 }  // extern "C"

@@ -200,8 +200,8 @@ def test_decode_timed_needs_events():
     ev = (ctypes.c_void_p * 17)(*([FAKE] * 17))
     nl = ctypes.c_int32(-1)
     assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, 0, FAKE, n4, None, ev, 17,
-                                       ctypes.byref(nl)) == vq.ERR_ARG       # 18 needed for 9 stages
+                                       ctypes.byref(nl), None) == vq.ERR_ARG   # 18 needed for 9 stages
     ev2 = (ctypes.c_void_p * 18)(*([FAKE] * 17 + [None]))
     assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, 0, FAKE, n4, None, ev2, 18,
-                                       ctypes.byref(nl)) == vq.ERR_ARG       # a NULL event
+                                       ctypes.byref(nl), None) == vq.ERR_ARG   # a NULL event
     assert nl.value == -1
