@@ -102,20 +102,20 @@ KERNEL_SOURCES = [os.path.join(ROOT, "speculative_decoding_verification_bit_amd"
                   for f in ("linear.hip", "vq_internal.h")]
 
 
-def profiled_traffic():
+def profiled_traffic(kernel_key):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel
-    sources have changed since the counters were taken."""
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the summary
+    covers another kernel or the kernel sources have changed since the counters were taken."""
     import hashlib
     try:
         fields = dict(line.split(": ", 1) for line in open(PROFILE).read().splitlines()
-                      if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
+                      if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ", "kernel_key: ")))
     except OSError:
         return None
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         h.update(open(f, "rb").read())
-    if fields.get("source_sha256") != h.hexdigest():
+    if fields.get("source_sha256") != h.hexdigest() or fields.get("kernel_key") != kernel_key:
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -145,7 +145,7 @@ def time_stream_kernel(torch, vq, model, x0, logits, ws, passes, path, stage_byt
         torch.cuda.synchronize()
         n = len(runs)
         for i, r in enumerate(runs):
-            key = "persistent" if r == 0 else ("multi" if r > 1 else "single")
+            key = "persistent" if r == 0 else "rows" if r < 0 else "multi" if r > 1 else "single"
             ms = events[2 * i].elapsed_time(events[2 * i + 1])
             b = stage_bytes[i] if r else sum(stage_bytes) / n
             c, t, bb = groups.get(key, (0, 0.0, 0.0))
@@ -263,6 +263,7 @@ def main():
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
     kname = {"single": "k_stage_valu<1, 1, false> (Q4_MIN, K 1, one chunk per item)",
              "multi": "k_stage_valu<1, 1, true> (Q4_MIN, K 1, chunk runs per item)",
+             "rows": "k_rows_s<1, 1, NSG> (Q4_MIN, K 1, row strips)",
              "persistent": "k_pass<1, 1, false> (Q4_MIN, K 1, persistent)"}[dom]
     value = wbytes / (ms1 * 1e-3) / 1e9
     log(f"K=1 step {ms1:.3f} ms ({value:.0f} GB/s), eager {eager1:.3f} ms; launches per pass {n_launch}; "
@@ -290,7 +291,7 @@ def main():
         ("persistent_pass_ms" if n_launch > 16 else "staged_pass_ms"): other1 and round(other1, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": profiled_traffic() if dom == "multi" else None,
+                     "traffic": profiled_traffic(dom),
                      "kernel": kname, "launches_per_pass": round(n_dom),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 3),
                      "bytes_per_launch": round(bytes_per_launch)},

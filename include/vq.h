@@ -6,7 +6,7 @@
  * 27B model on a 24 GB AMD card" (section "How speculative decoding gets past a
  * per-token wall") and on the Hacker News thread 49596054:
  *   1. every block-quantised weight matrix of a dense decoder is read from HBM once and
- *      applied to a K-wide batch of drafted-token activations, layer by layer
+ *      multiplied into the K drafted-token activation columns, layer by layer
  *      (vq_verify_linear for one matrix, vq_decode_pass for the whole stack);
  *   2. a lossless acceptance rule turns the [K][vocab] logits into emitted tokens
  *      (vq_verify_accept).
@@ -75,28 +75,33 @@ typedef struct vq_matrix {
 #define VQ_DTYPE_F32 0
 #define VQ_DTYPE_F16 1
 
-/* Kernel choice.  AUTO picks by K (VALU up to K = 4, MFMA above); VALU and MFMA force
-   one (for measurement). */
+/* Kernel choice.  AUTO picks by K (VALU up to K = 4, MFMA above); the others force one
+   (for measurement). */
 #define VQ_PATH_AUTO 0
-#define VQ_PATH_VALU 1        /* VALU dot2 kernel, K <= 8 */
+#define VQ_PATH_VALU 1        /* VALU dot2 kernel on 64-row x 1024-column tiles, K <= 8 */
 #define VQ_PATH_MFMA 2        /* MFMA 16x16x32 f16 kernel, K <= 16 */
+#define VQ_PATH_ROWS 3        /* VALU row-strip kernel (whole rows per workgroup, no split-K
+                                 exchange), K <= 4; stages whose K x cols activations do not
+                                 fit 36 KB of LDS run the VALU tile kernel */
 
 /* Launch strategy of vq_decode_pass, OR-ed into `path` (vq_verify_linear takes 0). */
 #define VQ_LAUNCH_AUTO 0        /* the faster of the two on MI355X: staged */
 #define VQ_LAUNCH_STAGED 4      /* one launch per stage */
 #define VQ_LAUNCH_PERSISTENT 8  /* one cooperative launch per 8 layers; inside it, a
-                                   stage waits on the completion counts of the previous one */
+                                   stage waits on the completion counts of the previous one.
+                                   Tile kernels only: with VQ_PATH_ROWS the pass returns
+                                   VQ_ERR_UNSUPPORTED */
 
 #define VQ_MAX_K 16
 
 /*
  * vq_verify_linear -- y = W x for K activation columns, each weight byte read once.
  *
- * "Hand the target model K drafted tokens and it scores all of them in a single forward
- * pass, because the weight matrices get read once and applied to a K wide batch of
- * activations instead of a single vector" (page "100 tokens per second ...", section
- * "How speculative decoding gets past a per-token wall"); the weights are streamed out
- * of memory once per pass (same page, section "The wall").
+ * The target model scores all K drafted tokens in one forward pass: each weight matrix
+ * is fetched from memory a single time and multiplied into the K activation columns
+ * together, not into one column per pass (page "100 tokens per second ...", section
+ * "How speculative decoding gets past a per-token wall"); streaming the weights is what
+ * bounds the pass (same page, section "The wall").
  *
  *   W       : host descriptor of a device matrix (see above)
  *   x_f16   : device fp16 [K][cols]  (row k = activation column k of the window)
@@ -151,8 +156,9 @@ typedef struct vq_accept_desc {
 /*
  * vq_verify_accept -- the lossless acceptance rule over W independent windows.
  *
- * GREEDY: "accept xi while it equals the target's argmax" (page "100 tokens per second
- * ...", section "How speculative decoding gets past a per-token wall"); argmax ties go
+ * GREEDY: draft x_i is kept as long as it matches the target's most likely token at its
+ * position, and the first mismatch ends the run (page "100 tokens per second ...",
+ * section "How speculative decoding gets past a per-token wall"); argmax ties go
  * to the lowest index; the target's own token at the first disagreement (or at the
  * bonus position K when every draft is accepted) caps the window (page "Decode is
  * memory-bound ...", section "Speculative decoding").
@@ -228,9 +234,10 @@ int vq_decode_error_word(const vq_model* M, int32_t K, void* ws, int32_t** word)
  *   events     : HOST array of n_events caller-created hipEvent_t handles (timing enabled)
  *   n_events   : >= 2 * (4 * n_layers + 1)
  *   n_launches : HOST out, the number of launches bracketed (may be NULL)
- *   runs       : HOST out [n_events / 2] (may be NULL): per launch, the chunks of 1024
- *                columns each workgroup item covers (a staged launch runs the multi-chunk
- *                kernel when this is above 1); 0 for a persistent launch
+ *   runs       : HOST out [n_events / 2] (may be NULL): per launch, which kernel ran:
+ *                -R for the row-strip kernel (R whole rows per workgroup item), c >= 1
+ *                for the tile kernel with items of c chunks of 1024 columns (c > 1 is its
+ *                multi-chunk variant), 0 for a persistent launch
  * Errors: as vq_decode_pass, plus VQ_ERR_ARG for a short or NULL-holding events array.
  */
 int vq_decode_pass_timed(const vq_model* M, const void* x0_f16, int32_t K, float* logits,

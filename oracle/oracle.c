@@ -15,8 +15,8 @@
  *    min(1, p_target(x)/p_draft(x)) and on rejection resamples from the normalised
  *    positive part of p_target - p_draft; the target's own token caps the window).
  *  - "Decode is memory-bound: the ~59 tok/s ceiling on an RTX 4090 ...", sections
- *    "Speculative decoding" (at the first disagreement the large model's own token is
- *    used, so every pass yields at least one token) and "Two things the math says to do"
+ *    "Speculative decoding" (at the first disagreement the target's own token is
+ *    taken, so no pass ends with zero new tokens) and "Two things the math says to do"
  *    (the production sampler: temperature 0.6, top-p 0.95, min-p 0.05).
  *  - Hacker News thread 49596054: the target runs the whole window through each layer
  *    once, and outputs a [n_tokens, vocab] logits tensor; the "D E F" worked example.

@@ -1,7 +1,7 @@
 // Lossless acceptance of drafted tokens against the target's [K][vocab] logits.
 //
-// Greedy: a draft is kept while it equals the target argmax; sampling: draft x is
-// accepted with probability min(1, p(x)/q(x)) and on rejection a token is drawn from
+// Greedy: a draft is kept while it equals the target argmax; sampling: draft x
+// survives with probability min(1, p(x)/q(x)) and on rejection a token is drawn from
 // the normalised positive part of p - q (page "100 tokens per second from a 27B model
 // on a 24 GB AMD card", section "How speculative decoding gets past a per-token wall";
 // page "Decode is memory-bound ...", section "Speculative decoding").  p and q are the

@@ -45,17 +45,20 @@ int check_matrix(const vq_matrix* W, const char* name) {
     return VQ_OK;
 }
 
-bool use_mfma(int K, int path) {
-    if (path == VQ_PATH_MFMA) return true;
-    if (path == VQ_PATH_VALU) return false;
-    return K > 4;          // measured: VALU and MFMA about even at K = 4, MFMA 2x at K = 8
+Kern kernel_of(int K, int path) {
+    if (path == VQ_PATH_MFMA) return KERN_MFMA;
+    if (path == VQ_PATH_VALU) return KERN_VALU;
+    if (path == VQ_PATH_ROWS) return KERN_ROWS;
+    return K > 4 ? KERN_MFMA : KERN_VALU;   // measured: about even at K = 4, MFMA 2x at K = 8
 }
 
 int check_path(int K, int path) {
-    if (path < VQ_PATH_AUTO || path > VQ_PATH_MFMA) return fail(VQ_ERR_ARG, "unknown kernel path %d", path);
+    if (path < VQ_PATH_AUTO || path > VQ_PATH_ROWS) return fail(VQ_ERR_ARG, "unknown kernel path %d", path);
     if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
     if (path == VQ_PATH_VALU && K > 8)
         return fail(VQ_ERR_UNSUPPORTED, "the VALU path is instantiated for K <= 8 (K = %d)", K);
+    if (path == VQ_PATH_ROWS && K > ROWS_MAX_K)
+        return fail(VQ_ERR_UNSUPPORTED, "the row-strip path is instantiated for K <= %d (K = %d)", ROWS_MAX_K, K);
     return VQ_OK;
 }
 
@@ -171,7 +174,14 @@ DecodeLayout decode_layout(const Shapes& s, int K) {
     // aligned place (no reuse between stages or layers): the persistent pass reads them
     // through the caches while other XCDs may still be writing their neighbours.
     d.stats_off = p;
-    d.stats_stride = align_up((size_t)mt * K * 4, 256) / 4;
+    // sums of squares: one per tile (tile kernel) or per item (row-strip kernel)
+    int mstat = mt;
+    for (int j = 0; j <= 4; ++j) {
+        const int st = j == 4 ? 4 * s.L : j;
+        const StageShape ss = stage_shape(s, st);
+        mstat = std::max(mstat, rows_geom(ss.rows, ss.cols, j == 2, j == 2 ? s.FF : 0, std::min(K, ROWS_MAX_K)).nitems);
+    }
+    d.stats_stride = align_up((size_t)mstat * K * 4, 256) / 4;
     p += d.stats_stride * 4 * (size_t)(4 * s.L);
     d.sbuf_off = p;
     d.sbuf_stride = align_up((size_t)K * s.FF * 4, 256) / 4;
@@ -259,7 +269,8 @@ int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y, 
     const size_t need = lin_ws(W, K);
     if (!ws || ws_bytes < need || !aligned(ws, 256))
         return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
-    const bool mfma = use_mfma(K, path);
+    const Kern kern = kernel_of(K, path);
+    const bool mfma = kern == KERN_MFMA;
     StageArgs A{};
     A.W = mat_from(*W);
     A.K = K;
@@ -269,9 +280,10 @@ int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y, 
     A.y_dtype = y_dtype;
     stage_scratch_carve(ws, W->rows, W->cols, K, 0, 0, &A);
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_zero_u32(A.counters, stage_geom(W->rows, W->cols, 0, 0).ntiles, st);
+    const StageGeom g = plan_geom(W->rows, W->cols, 0, 0, K, kern);
+    hipError_t e = g.rk ? hipSuccess : launch_zero_u32(A.counters, g.ntiles, st);
     if (e != hipSuccess) return hip_fail(e, "counter reset launch");
-    e = launch_stage(A, mfma, st);
+    e = launch_stage(A, g, mfma, st);
     if (e != hipSuccess) return hip_fail(e, "linear launch");
     return VQ_OK;
 }
@@ -359,12 +371,15 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
         return fail(VQ_ERR_ARG, "unknown launch mode in path %d", path);
     rc = check_path(K, kern);
     if (rc) return rc;
+    if (launch == VQ_LAUNCH_PERSISTENT && kern == VQ_PATH_ROWS)
+        return fail(VQ_ERR_UNSUPPORTED, "the persistent launch does not run the row-strip kernel");
     if (!x0_f16 || !logits) return fail(VQ_ERR_ARG, "NULL x0 or logits");
     if (!aligned(x0_f16, 16) || !aligned(logits, 4)) return fail(VQ_ERR_ARG, "x0 or logits misaligned");
     const DecodeLayout d = decode_layout(s, K);
     if (!ws || ws_bytes < d.total || !aligned(ws, 256))
         return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", d.total, ws_bytes);
-    const bool mfma = use_mfma(K, kern);
+    const Kern kind = kernel_of(K, kern);
+    const bool mfma = kind == KERN_MFMA;
     const bool persistent = launch == VQ_LAUNCH_PERSISTENT;     // AUTO: staged (measured faster)
     hipStream_t st = (hipStream_t)stream;
     char* base = (char*)ws;
@@ -401,7 +416,7 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
     for (int j = 0; j < 5; ++j) {
         const int st = j == 4 ? 4 * s.L : j;
         const StageShape ss = stage_shape(s, st);
-        P.cpw[j] = stage_geom(ss.rows, ss.cols, j == 2, j == 2 ? s.FF : 0).cpw;
+        P.geo[j] = plan_geom(ss.rows, ss.cols, j == 2, j == 2 ? s.FF : 0, K, kind);
     }
     int nl = 0;
     for (int l0 = 0; l0 < s.L; l0 += PASS_LAYERS) {
@@ -435,8 +450,9 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
                     e = hipEventRecord((hipEvent_t)events[2 * nl], st);
                     if (e != hipSuccess) return hip_fail(e, "event record");
                 }
-                if (runs && nl < n_events / 2) runs[nl] = P.cpw[stage == 4 * s.L ? 4 : stage & 3];
-                e = launch_stage(A, mfma, st);
+                const StageGeom& g = P.geo[stage == 4 * s.L ? 4 : stage & 3];
+                if (runs && nl < n_events / 2) runs[nl] = g.rk ? -g.R : g.cpw;
+                e = launch_stage(A, g, mfma, st);
                 if (e != hipSuccess) return hip_fail(e, "stage launch");
                 if (events && 2 * nl + 1 < n_events) {
                     e = hipEventRecord((hipEvent_t)events[2 * nl + 1], st);

@@ -34,7 +34,10 @@
 //    into fp16 hi + lo parts.
 #include <hip/hip_fp16.h>
 
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "vq_internal.h"
 
@@ -188,13 +191,17 @@ __device__ __forceinline__ int tile_seg(const StageArgs& A, int t, int r) {
         (A.W.nseg > 2 && row0 >= A.W.seg_end[1]) ? 2 : (A.W.nseg > 1 && row0 >= A.W.seg_end[0]) ? 1 : 0);
 }
 
-// Makes a value opaque to the optimiser.  The segment select below would otherwise be
-// turned into an indexed load, which forces a Mat held in registers (the persistent pass
-// builds one per stage) out to scratch memory.
+// Pins a uniform value (a segment's base or bound) into scalar registers.  Besides
+// keeping the value scalar, the intrinsic stops the compiler from folding the segment
+// select below into an indexed load, which would force a Mat held in registers (the
+// persistent pass builds one per stage) out to scratch memory.
+__device__ __forceinline__ int opaque(int v) { return __builtin_amdgcn_readfirstlane(v); }
 template <typename T>
-__device__ __forceinline__ T opaque(T v) {
-    asm volatile("" : "+s"(v));
-    return v;
+__device__ __forceinline__ T* opaque(T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T*>((uint64_t)lo | ((uint64_t)hi << 32));
 }
 
 // Segment `seg` (uniform) of W.
@@ -318,11 +325,11 @@ __device__ void stage_epilogue(const StageArgs& A, int tile, int part, int npart
         st_shared_f32(A.stats_out + (size_t)tile * K + k, ss, A.coh);
     }
     if (A.done) {
-        // the tile's outputs are in memory before the completion counters count it
+        // the tile's outputs are in memory before its XCD group's counter counts it
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (threadIdx.x < (unsigned)DONE_REPL)
-            __hip_atomic_fetch_add(A.done + threadIdx.x * DONE_STRIDE, 1u, __ATOMIC_RELAXED,
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(A.done + (blockIdx.x & 7) * DONE_STRIDE, 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -806,15 +813,353 @@ __global__ __launch_bounds__(256) void k_stage_mfma(const StageArgs A, const Sta
 }
 
 
+// ------------------------------------------------------------------ row-strip VALU kernel
+//
+// One item = R consecutive output rows (gate|up: rows h of both halves for R / 2 values
+// of h) over all columns, so no partial sum leaves the workgroup.  The whole row's
+// activations (K x cols fp16) sit in LDS, converted once per stage and workgroup, in the
+// widened pair order (quarters swizzled against bank conflicts).  Wave w computes the
+// item's local rows 4j + w (j < RW); lane l takes block 64s + l of each of the row's NSG
+// 64-block segments, so a wave reads 1 KB of one row's codes per load instruction.  The
+// code is specialised on NSG so that all loads and block terms are straight-line, which
+// lets the compiler wait for exactly the item being computed while the next item's
+// loads are in flight (lanes past the row's last block re-read that block, which the
+// wave's load merges, and drop the term).  A block term is d * sum q x (+ m * sum x),
+// with q widened exactly to fp16 as in the tile kernel, so a row of zero codes or zero
+// scales gives exactly 0.
+
+struct RowSmem {
+    u4_t xs[ROWS_X_BYTES / 16];      // [k][block][quarter] fp16 x, quarters swizzled
+    float scratch[ROWS_X_BYTES / 16 > ROWS_MAX_K * 256 ? ROWS_X_BYTES / 16 : ROWS_MAX_K * 256];
+                                     // RMS reduction (K x 256) / quarter sums (K x xwb x 4)
+    float xb[ROWS_X_BYTES / 64];     // [k][block] sums of x (Q4 with mins)
+    float fin[16][ROWS_MAX_K];       // the item's outputs [R][K]
+    float rs[VQ_MAX_K];
+};
+
+// Local row lr of an item: its matrix row, whether it exists, and its segment.
+struct RowRef {
+    int row;
+    bool ok;
+    int seg;
+};
+
+__device__ __forceinline__ RowRef rows_ref(const StageArgs& A, const StageGeom& g, int item, int lr) {
+    RowRef r;
+    if (A.paired) {
+        const int hr = g.R >> 1, half = A.W.seg_end[0];
+        const int up = lr >= hr;
+        const int h = item * hr + (up ? lr - hr : lr);
+        r.ok = h < half;
+        r.row = (up ? half : 0) + min(h, half - 1);
+        r.seg = up;
+    } else {
+        const int row = item * g.R + lr;
+        r.ok = row < A.W.rows;
+        r.row = min(row, A.W.rows - 1);
+        const int row0 = item * g.R;        // items never straddle a segment boundary
+        r.seg = (A.W.nseg > 2 && row0 >= A.W.seg_end[1]) ? 2 : (A.W.nseg > 1 && row0 >= A.W.seg_end[0]) ? 1 : 0;
+    }
+    return r;
+}
+
+// The stage's (up to three) segment bases, pinned in scalar registers once per stage.
+struct StageSegs {
+    SegRef s[MAX_SEG];
+    __device__ __forceinline__ const SegRef& get(int seg) const { return seg == 2 ? s[2] : seg == 1 ? s[1] : s[0]; }
+};
+
+__device__ __forceinline__ StageSegs stage_segs(const StageArgs& A) {
+    StageSegs r;
+#pragma unroll
+    for (int i = 0; i < MAX_SEG; ++i) r.s[i] = seg_ref(A.W, i);
+    return r;
+}
+
+// Converts the activations into LDS (and, for item 0's owner, the fp16 copy of the stage
+// input), with the sum of every block (for the min term).  Thread t takes quarters t,
+// t + 256, ... (8 columns each).
+template <int FMT, int K>
+__device__ void rows_stage_x(const StageArgs& A, const StageGeom& g, bool keeper, RowSmem& sm) {
+    constexpr int QMAX = ROWS_X_BYTES / 16 / 256;      // quarters per thread at most
+    constexpr bool Q4F = FMT == VQ_FMT_Q4_MIN;
+    const int nb = g.nb;
+    const int nq = K * nb * 4;
+    f4_t ra[QMAX], rb[QMAX];
+#pragma unroll
+    for (int i = 0; i < QMAX; ++i) {
+        const int qi = threadIdx.x + 256 * i;
+        if (qi < nq) {
+            const int k = qi / (nb * 4), rem = qi - k * nb * 4;
+            const int col = 8 * rem;
+            if (A.glue == GLUE_NONE) {
+                ra[i] = __builtin_bit_cast(f4_t, *reinterpret_cast<const u4_t*>(A.x16 + (size_t)k * A.W.cols + col));
+            } else {
+                const float* p = A.src + (size_t)k * A.ld + col;
+                ra[i] = *reinterpret_cast<const f4_t*>(p);
+                rb[i] = *reinterpret_cast<const f4_t*>(p + 4);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < QMAX; ++i) {
+        const int qi = threadIdx.x + 256 * i;
+        if (qi < nq) {
+            const int k = qi / (nb * 4), rem = qi - k * nb * 4;
+            const int b = rem >> 2, q = rem & 3;
+            uint32_t h[8];
+            if (A.glue == GLUE_NONE) {
+                const u4_t v = __builtin_bit_cast(u4_t, ra[i]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[2 * e] = v[e] & 0xffffu;
+                    h[2 * e + 1] = v[e] >> 16;
+                }
+            } else {
+                const float r = sm.rs[k];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = f2h_bits(ra[i][e] * r);
+                    h[4 + e] = f2h_bits(rb[i][e] * r);
+                }
+            }
+            if (keeper) {
+                u4_t v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = h[2 * e] | (h[2 * e + 1] << 16);
+                *reinterpret_cast<u4_t*>(A.keep + (size_t)k * A.W.cols + 8 * rem) = v;
+            }
+            u4_t pk;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) pk[t] = h[slot_col<FMT>(2 * t)] | (h[slot_col<FMT>(2 * t + 1)] << 16);
+            sm.xs[(k * g.xwb + b) * 4 + (q ^ ((b >> 2) & 3))] = pk;
+            if constexpr (Q4F) {
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = half_bits_to_float(h[e]);
+                sm.scratch[(k * g.xwb + b) * 4 + q] = ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
+            }
+        }
+    }
+    __syncthreads();
+    if constexpr (Q4F) {
+        for (int t = threadIdx.x; t < K * nb; t += 256) {
+            const int k = t / nb, b = t - k * nb;
+            const float* q4 = &sm.scratch[(k * g.xwb + b) * 4];
+            sm.xb[k * g.xwb + b] = (q4[0] + q4[1]) + (q4[2] + q4[3]);
+        }
+        __syncthreads();
+    }
+}
+
+template <int N>
+struct WRowN {
+    u4_t w[N];
+    uint32_t sr[N], mr[N];
+};
+
+template <int NSG>
+struct RowShape {
+    static constexpr int RW = rows_per_wave(NSG);      // rows per wave
+    static constexpr int N = RW * NSG;                 // loads per lane
+};
+
+// The weights of item `item` for this lane; idle = true issues the same loads, all lanes
+// of a wave on the first block of each row (a cheap stand-in when there is no next
+// item, which keeps the compiler's load-counter waits exact).
+template <int FMT, int NSG>
+__device__ __forceinline__ void rows_load_s(const StageArgs& A, const StageGeom& g, const StageSegs& S, int item,
+                                            WRowN<RowShape<NSG>::N>& T, bool idle) {
+    constexpr int RW = RowShape<NSG>::RW;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const uint32_t rowq = (uint32_t)A.W.cols >> 1, nb = (uint32_t)g.nb;
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        const RowRef rr = rows_ref(A, g, item, 4 * j + wave);
+        const SegRef& R = S.get(__builtin_amdgcn_readfirstlane(rr.seg));
+        const uint32_t lr = (uint32_t)(rr.row - R.r0);
+#pragma unroll
+        for (int sg = 0; sg < NSG; ++sg) {
+            const int u = j * NSG + sg;
+            const uint32_t b = idle ? 0u : min((uint32_t)(64 * sg + lane), nb - 1u);
+            T.w[u] = ld_global_nt<u4_t>(R.qs + (lr * rowq + 16u * b));
+            if constexpr (FMT == VQ_FMT_MXFP4) {
+                T.sr[u] = ld_global<uint8_t>(R.sc8 + (lr * nb + b));
+                T.mr[u] = 0u;
+            } else {
+                T.sr[u] = ld_global<uint16_t>(R.sc8 + 2u * (lr * nb + b));
+                T.mr[u] = FMT == VQ_FMT_Q4_MIN ? (uint32_t)ld_global<uint16_t>(R.mn + (lr * nb + b)) : 0u;
+            }
+        }
+    }
+}
+
+// acc[j][k] += this lane's block terms of local row 4j + wave.
+template <int FMT, int K, int NSG>
+__device__ __forceinline__ void rows_compute_s(const StageArgs& A, const StageGeom& g, int item,
+                                               const WRowN<RowShape<NSG>::N>& T, const RowSmem& sm,
+                                               float (&acc)[RowShape<NSG>::RW][K]) {
+    constexpr int RW = RowShape<NSG>::RW;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    bool ok[RW];
+#pragma unroll
+    for (int j = 0; j < RW; ++j) ok[j] = rows_ref(A, g, item, 4 * j + wave).ok;
+#pragma unroll
+    for (int sg = 0; sg < NSG; ++sg) {
+        // the segment's activations serve all RW rows of the wave
+        const int bl = 64 * sg + lane;
+        const bool in = bl < g.nb;
+        const int blc = min(bl, g.nb - 1);
+        const int sw = (blc >> 2) & 3;
+        // 1 for a lane's own block of an existing row, 0 for a repeated one (a factor,
+        // not a branch: every lane computes a finite term either way)
+        float msk[RW];
+#pragma unroll
+        for (int j = 0; j < RW; ++j) msk[j] = (in && ok[j]) ? 1.f : 0.f;
+        u4_t xq[K][4];
+        float xs[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int xb = (k * g.xwb + blc) * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xq[k][i] = sm.xs[xb + (i ^ sw)];
+            xs[k] = FMT == VQ_FMT_Q4_MIN ? sm.xb[k * g.xwb + blc] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < RW; ++j) {
+            const int u = j * NSG + sg;
+            const float d = FMT == VQ_FMT_MXFP4 ? e8m0_to_float(T.sr[u]) : half_bits_to_float(T.sr[u]);
+            const float m = FMT == VQ_FMT_Q4_MIN ? half_bits_to_float(T.mr[u]) : 0.f;
+            h2_t p[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unpack8<FMT>(T.w[u][i], p[i]);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                float t = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) t = __builtin_amdgcn_fdot2(p[i][e], as_h2(xq[k][i][e]), t, false);
+                float v = d * t;
+                if constexpr (FMT == VQ_FMT_Q4_MIN) v = fmaf(m, xs[k], v);
+                acc[j][k] = fmaf(v, msk[j], acc[j][k]);
+            }
+        }
+    }
+}
+
+// Sum over the 64 lanes of a wave, the same in every lane (a fixed order: DPP sums over
+// 8 and 16 lanes, then the four 16-lane rows).
+__device__ __forceinline__ float wave_sum(float v) {
+    v = sum8(v);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return ((r0 + r1) + r2) + r3;
+}
+
+// Outputs, sums of squares and silu(gate) * up of an item whose results are in sm.fin.
+template <int K>
+__device__ __forceinline__ void rows_epilogue(const StageArgs& A, const StageGeom& g, int item, RowSmem& sm) {
+    const int rows = A.W.rows;
+    for (int e = threadIdx.x; e < g.R * K; e += 256) {
+        const int lr = e / K, k = e - lr * K;
+        const RowRef rr = rows_ref(A, g, item, lr);
+        if (!rr.ok) continue;
+        const size_t o = (size_t)k * rows + rr.row;
+        if (A.y_dtype == VQ_DTYPE_F16)
+            reinterpret_cast<uint16_t*>(A.y)[o] = (uint16_t)f2h_bits(sm.fin[lr][k]);
+        else
+            st_shared_f32(reinterpret_cast<float*>(A.y) + o, sm.fin[lr][k], A.coh);
+    }
+    if (A.stats_out && threadIdx.x < (unsigned)K) {
+        const int k = threadIdx.x;
+        float ss = 0.f;
+        if (A.paired) {
+            const int hr = g.R >> 1, half = A.W.seg_end[0];
+            for (int l = 0; l < hr; ++l) {
+                const int h = item * hr + l;
+                if (h >= half) break;
+                const float v = silu_mul(sm.fin[l][k], sm.fin[hr + l][k]);
+                st_shared_f32(A.sbuf + (size_t)k * half + h, v, A.coh);
+                ss += v * v;
+            }
+        } else {
+            for (int l = 0; l < g.R; ++l) {
+                const int row = item * g.R + l;
+                if (row < A.nstat && row < rows) ss += sm.fin[l][k] * sm.fin[l][k];
+            }
+        }
+        st_shared_f32(A.stats_out + (size_t)item * K + k, ss, A.coh);
+    }
+}
+
+// Items vid, vid + nwg, ... of a stage; `cur` holds the first one's weights, already
+// issued.  The stage's input scales and activations are prepared once; each item's
+// weights are issued before the previous item is computed.
+template <int FMT, int K, int NSG>
+__device__ void rows_run_s(const StageArgs& A, const StageGeom& g, const StageSegs& S, int vid, int nwg,
+                           RowSmem& sm, WRowN<RowShape<NSG>::N>& cur) {
+    constexpr int RW = RowShape<NSG>::RW;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    stage_rms(A, sm.rs, sm.scratch);
+    rows_stage_x<FMT, K>(A, g, A.keep && vid == 0, sm);
+    for (int it = vid; it < g.nitems; it += nwg) {
+        const int nx = it + nwg;
+        const bool more = nx < g.nitems;
+        WRowN<RowShape<NSG>::N> nxt;
+        rows_load_s<FMT, NSG>(A, g, S, more ? nx : it, nxt, !more);
+        float acc[RW][K];
+#pragma unroll
+        for (int j = 0; j < RW; ++j)
+#pragma unroll
+            for (int k = 0; k < K; ++k) acc[j][k] = 0.f;
+        rows_compute_s<FMT, K, NSG>(A, g, it, cur, sm, acc);
+#pragma unroll
+        for (int j = 0; j < RW; ++j)
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const float v = wave_sum(acc[j][k]);
+                if (lane == 0) sm.fin[4 * j + wave][k] = v;
+            }
+        __syncthreads();
+        rows_epilogue<K>(A, g, it, sm);
+        cur = nxt;
+        __syncthreads();                      // fin is reused by the next item
+    }
+}
+
+template <int FMT, int K, int NSG>
+__global__ __launch_bounds__(256) void k_rows_s(const StageArgs A, const StageGeom g) {
+    __shared__ RowSmem sm;
+    const int nwg = gridDim.x;
+    const int vid = xcd_item(blockIdx.x, nwg);
+    const StageSegs S = stage_segs(A);
+    WRowN<RowShape<NSG>::N> cur;
+    rows_load_s<FMT, NSG>(A, g, S, vid, cur, false);
+    rows_run_s<FMT, K, NSG>(A, g, S, vid, nwg, sm, cur);
+}
+
 // ------------------------------------------------------------------ persistent pass
 
-// Waits until *cnt reaches `target`: thread 0 polls, the workgroup waits at the barrier
-// behind it.  The wait is bounded: after about a second without progress the error flag
-// is raised and the workgroup proceeds, so a launch always ends.
+// Waits until the DONE_REPL group counters at cnt (DONE_STRIDE words apart) sum to
+// `target`: thread 0 polls, the workgroup waits at the barrier behind it.  The wait is
+// bounded: after about a second without completion the error flag is raised and the
+// workgroup proceeds, so a launch always ends.
 __device__ void wait_count(const unsigned* cnt, unsigned target, int* err) {
     if (threadIdx.x == 0) {
         unsigned spins = 0;
-        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        for (;;) {
+            unsigned sum = 0;
+#pragma unroll
+            for (int r = 0; r < DONE_REPL; ++r)
+                sum += __hip_atomic_load(cnt + r * DONE_STRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (sum >= target) break;
             __builtin_amdgcn_s_sleep(1);
             if ((++spins & 1023u) == 0) {
                 // another workgroup gave up: do not wait either
@@ -829,33 +1174,32 @@ __device__ void wait_count(const unsigned* cnt, unsigned target, int* err) {
     __syncthreads();
 }
 
-// The stages of a plan segment in one launch.  A stage's items are dealt round-robin to
-// the workgroups (those of one XCD take consecutive items, so a tile's parts meet in one
-// L2).  There is no grid-wide barrier: a workgroup with items in stage s issues its first
-// item's weight loads, then waits until every tile of stage s - 1 has counted itself
-// complete, then reads that stage's outputs.  Workgroups without items in a stage go
-// straight on to the next one, and each item's last chunk issues the loads of the
-// workgroup's next item in the stage.
+// The stages of a plan segment in one launch, with the plan's geometry (the same items
+// as one launch per stage, so the same sums in the same order).  A stage's items are
+// dealt round-robin to the workgroups (those of one XCD take consecutive items, so a
+// tile's parts meet in one L2).  There is no grid-wide barrier: a workgroup with items in
+// stage s issues its first item's weight loads, then waits until every tile of stage
+// s - 1 has counted itself complete, then reads that stage's outputs.  Workgroups without items in a stage go straight on to the next one.
 template <int FMT, int K, bool MFMA>
 __global__ __launch_bounds__(256) void k_pass(const PassPlan P) {
-    __shared__ StageSmem sm;
-    __shared__ uint2 xs[4][MFMA ? 1 : K][8][8];
-    using Tile = typename std::conditional<MFMA, WTileM, WTileV>::type;
+    struct Smem {
+        StageSmem st;
+        uint2 xs[4][MFMA ? 1 : K][8][8];
+    };
+    __shared__ Smem sm;
     const int nwg = gridDim.x;                // a multiple of 8
     const int grp = blockIdx.x & 7;
     const int vid = grp * (nwg >> 3) + (blockIdx.x >> 3);
     const int s0 = 4 * P.layer0;
     const int s1 = 4 * (P.layer0 + P.nlayers) + (P.with_lm ? 1 : 0);
-    int prev_tiles = 0;
+    auto kind = [&](int stage) { return stage == 4 * P.L ? 4 : stage & 3; };
     for (int stage = s0; stage < s1; ++stage) {
         StageArgs A;
         build_stage(P, stage, A);
-        const StageGeom g = stage_geom_cpw(A.W.rows, A.W.cols, A.paired, A.paired ? A.W.seg_end[0] : 0,
-                                           P.cpw[stage == 4 * P.L ? 4 : stage & 3]);
+        const StageGeom& g = P.geo[kind(stage)];
+        if (vid >= g.nitems) continue;
+        using Tile = typename std::conditional<MFMA, WTileM, WTileV>::type;
         const int nitems = g.ntiles * g.nparts;
-        const int wait_tiles = prev_tiles;
-        prev_tiles = g.ntiles;
-        if (vid >= nitems) continue;
         Tile cur;
         {
             const int tile = vid / g.nparts, part = vid - tile * g.nparts;
@@ -863,15 +1207,15 @@ __global__ __launch_bounds__(256) void k_pass(const PassPlan P) {
             else prefetch_valu<FMT>(A, tile, part * g.cpw, cur);
         }
         if (stage > s0)
-            wait_count(P.done + (size_t)(stage - 1) * DONE_WORDS + grp * DONE_STRIDE, (unsigned)wait_tiles, P.err);
-        stage_rms(A, sm.rs, &sm.red[0][0][0]);
+            wait_count(P.done + (size_t)(stage - 1) * DONE_WORDS, (unsigned)P.geo[kind(stage - 1)].nstat, P.err);
+        stage_rms(A, sm.st.rs, &sm.st.red[0][0][0]);
         for (int it = vid; it < nitems; it += nwg) {
             const int tile = it / g.nparts, part = it - tile * g.nparts;
             const int nx = it + nwg;
             const int ntile = nx < nitems ? nx / g.nparts : -1;
             const int npart = nx < nitems ? nx - ntile * g.nparts : 0;
-            if constexpr (MFMA) stage_item_mfma<FMT, true>(A, g, tile, part, sm, cur, ntile, npart);
-            else stage_item_valu<FMT, K, true>(A, g, tile, part, sm, xs, cur, ntile, npart);
+            if constexpr (MFMA) stage_item_mfma<FMT, true>(A, g, tile, part, sm.st, cur, ntile, npart);
+            else stage_item_valu<FMT, K, true>(A, g, tile, part, sm.st, sm.xs, cur, ntile, npart);
             __syncthreads();                  // LDS is reused by the next item
         }
     }
@@ -906,8 +1250,8 @@ __global__ void k_zero_u32(unsigned* p, int n) {
 
 template <int FMT, int K>
 void launch_valu_k(const StageArgs& A, int tg, const StageGeom& g, hipStream_t st) {
-    if (g.cpw > 1) k_stage_valu<FMT, K, true><<<dim3(tg * g.nparts), 256, 0, st>>>(A, g);
-    else k_stage_valu<FMT, K, false><<<dim3(tg * g.nparts), 256, 0, st>>>(A, g);
+    // staged VALU launches take one chunk per item (the plan never gives them runs)
+    k_stage_valu<FMT, K, false><<<dim3(tg * g.nparts), 256, 0, st>>>(A, g);
 }
 
 template <int FMT>
@@ -934,15 +1278,18 @@ void launch_valu_f(const StageArgs& A, int tg, const StageGeom& g, hipStream_t s
 
 // ------------------------------------------------------------------ host side
 
+// Split-K partials [parts][K][rows] and tile arrival counters, with room for the most
+// parts any tile geometry of the stage has: one chunk per item (parts = chunks).
 size_t stage_scratch_bytes(int rows, int cols, int K, int paired, int half) {
-    const StageGeom g = stage_geom(rows, cols, paired, half);
-    return align_up((size_t)g.nparts * K * rows * 4, 256) + align_up((size_t)g.ntiles * 4, 256);
+    const StageGeom g = stage_geom_cpw(rows, cols, paired, half, 1);
+    return align_up((size_t)max_parts(cols) * K * rows * 4, 256) + align_up((size_t)g.ntiles * 4, 256);
 }
 
 void stage_scratch_carve(void* base, int rows, int cols, int K, int paired, int half, StageArgs* A) {
-    const StageGeom g = stage_geom(rows, cols, paired, half);
+    (void)paired;
+    (void)half;
     A->part = (float*)base;
-    A->counters = (unsigned*)((char*)base + align_up((size_t)g.nparts * K * rows * 4, 256));
+    A->counters = (unsigned*)((char*)base + align_up((size_t)max_parts(cols) * K * rows * 4, 256));
 }
 
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st) {
@@ -951,9 +1298,71 @@ hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_stage(const StageArgs& A, bool mfma, hipStream_t st) {
-    const StageGeom g = stage_geom(A.W.rows, A.W.cols, A.paired, A.paired ? A.W.seg_end[0] : 0);
-    // one workgroup per item (a tile and a run of its chunks, sized by stage_geom)
+// Resident workgroups of a kernel on this device (queried once per kernel and device).
+int resident_wgs(const void* fn) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({fn, dev});
+    if (it != cache.end()) return it->second;
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 256, 0) != hipSuccess || occ < 1)
+        occ = 1, cus = cus > 0 ? cus : 256;
+    const int n = cus * occ;
+    cache[{fn, dev}] = n;
+    return n;
+}
+
+template <int FMT, int K, int NSG>
+void launch_rows_s(const StageArgs& A, const StageGeom& g, hipStream_t st) {
+    if constexpr (rows_fit(K, NSG)) {
+        // one workgroup per item while they all fit at once, else as many as fit (each
+        // then streams several items)
+        const int nwg = std::min(g.nitems, resident_wgs(reinterpret_cast<const void*>(&k_rows_s<FMT, K, NSG>)));
+        k_rows_s<FMT, K, NSG><<<dim3(nwg), 256, 0, st>>>(A, g);
+    }
+}
+
+template <int FMT, int K>
+void launch_rows_k(const StageArgs& A, const StageGeom& g, hipStream_t st) {
+    switch (g.xwb / 64) {
+        case 1: launch_rows_s<FMT, K, 1>(A, g, st); break;
+        case 2: launch_rows_s<FMT, K, 2>(A, g, st); break;
+        case 3: launch_rows_s<FMT, K, 3>(A, g, st); break;
+        case 4: launch_rows_s<FMT, K, 4>(A, g, st); break;
+        case 5: launch_rows_s<FMT, K, 5>(A, g, st); break;
+        case 6: launch_rows_s<FMT, K, 6>(A, g, st); break;
+        case 7: launch_rows_s<FMT, K, 7>(A, g, st); break;
+        case 8: launch_rows_s<FMT, K, 8>(A, g, st); break;
+        default: launch_rows_s<FMT, K, 9>(A, g, st); break;
+    }
+}
+
+template <int FMT>
+void launch_rows_f(const StageArgs& A, const StageGeom& g, hipStream_t st) {
+    switch (A.K) {
+        case 1: launch_rows_k<FMT, 1>(A, g, st); break;
+        case 2: launch_rows_k<FMT, 2>(A, g, st); break;
+        case 3: launch_rows_k<FMT, 3>(A, g, st); break;
+        default: launch_rows_k<FMT, 4>(A, g, st); break;
+    }
+}
+
+hipError_t launch_stage(const StageArgs& A, const StageGeom& g, bool mfma, hipStream_t st) {
+    if (g.rk) {
+        switch (A.W.fmt) {
+            case VQ_FMT_Q4: launch_rows_f<VQ_FMT_Q4>(A, g, st); break;
+            case VQ_FMT_Q4_MIN: launch_rows_f<VQ_FMT_Q4_MIN>(A, g, st); break;
+            default: launch_rows_f<VQ_FMT_MXFP4>(A, g, st); break;
+        }
+        return hipGetLastError();
+    }
+    // one workgroup per item (a tile and a run of its chunks); the partials were sized
+    // for at most max_parts parts
+    if (g.nparts < 1 || g.nparts > max_parts(A.W.cols) || g.cpw < 1) return hipErrorInvalidValue;
     const int tg = g.ntiles;
     const dim3 grid(tg * g.nparts);
     if (mfma) {
@@ -973,6 +1382,11 @@ hipError_t launch_stage(const StageArgs& A, bool mfma, hipStream_t st) {
 }
 
 hipError_t launch_pass_segment(const PassPlan& P, bool mfma, hipStream_t st) {
+    // tile geometries only, within the partial buffers' room
+    const int gcols[5] = {P.H, P.H, P.H, P.FF, P.H};
+    for (int j = 0; j < 5; ++j)
+        if (P.geo[j].rk || P.geo[j].nparts < 1 || P.geo[j].nparts > max_parts(gcols[j]) || P.geo[j].cpw < 1)
+            return hipErrorInvalidValue;
     const void* fn = P.fmt == VQ_FMT_Q4 ? pass_fn_k<VQ_FMT_Q4>(P.K, mfma)
                      : P.fmt == VQ_FMT_Q4_MIN ? pass_fn_k<VQ_FMT_Q4_MIN>(P.K, mfma)
                                               : pass_fn_k<VQ_FMT_MXFP4>(P.K, mfma);
@@ -988,7 +1402,7 @@ hipError_t launch_pass_segment(const PassPlan& P, bool mfma, hipStream_t st) {
     if (nwg < 8) return hipErrorInvalidConfiguration;
     void* args[] = {const_cast<PassPlan*>(&P)};
     // cooperative: the runtime refuses the launch unless every workgroup is resident,
-    // which the grid barriers rely on
+    // which the waits between stages rely on
     e = hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(256), args, 0, st);
     if (e != hipSuccess) return e;
     return hipGetLastError();

@@ -46,7 +46,21 @@ struct StageGeom {
     int ntiles;
     int cpw;       // chunks per item (one workgroup's share of a tile)
     int nparts;    // items per tile = split-K partials per output
+    // row-strip kernel (rk = 1): items of R whole rows, activations staged per window
+    int rk;
+    int R;         // rows per item (paired: R / 2 of each half); 4, 8 or 16
+    int nitems;    // items of the stage (either kernel)
+    int xwb;       // blocks per activation window (a multiple of 64)
+    int nphase;    // windows per row
+    int nstat;     // sums-of-squares entries the stage writes (row-strip: items; tile: tiles)
 };
+
+// Row-strip kernel limits: K <= ROWS_MAX_K, at most ROWS_NLD 16-byte weight loads per
+// lane per window (two items' worth are in registers at once), ROWS_X_BYTES of LDS for a
+// window's fp16 activations.
+constexpr int ROWS_MAX_K = 4;
+constexpr int ROWS_NLD = 12;
+constexpr int ROWS_X_BYTES = 36864;
 
 // Work-splitting model: a tile's chunks are dealt out in runs of cpw chunks per item.
 // Longer runs stream more weights per workgroup between epilogues (partial exchange,
@@ -95,11 +109,13 @@ struct StageArgs {
     int coh;                   // 1: y / stats_out / sbuf are read by other workgroups of the
                                // same launch: stored through to memory (device scope)
     unsigned* done;            // NULL, or DONE_REPL completion counters DONE_STRIDE words
-                               // apart: each gets +1 when a tile's outputs are in memory
+                               // apart, one per XCD group of workgroups; their sum counts
+                               // the tiles (tile kernel) or items (row-strip kernel) whose
+                               // outputs are in memory
 };
 
-// Completion counters of the persistent pass: one replica per XCD group of workgroups,
-// each on its own 128-byte line, so that waiting workgroups spread their polling.
+// Completion counters of the persistent pass: one per XCD group of workgroups (blockIdx
+// mod 8), each on its own 128-byte line, so that arrivals spread over 8 addresses.
 constexpr int DONE_REPL = 8;
 constexpr int DONE_STRIDE = 32;
 constexpr int DONE_WORDS = DONE_REPL * DONE_STRIDE;     // per stage
@@ -122,7 +138,7 @@ struct PassPlan {
     int with_lm;                   // 1: the lm_head stage ends this segment
     MatPtrs m[PASS_LAYERS][7];     // q, k, v, o, gate, up, down of layers layer0 + i
     MatPtrs lm;
-    int cpw[5];                    // chunks per item of stages q|k|v, o, gate|up, down, lm_head
+    StageGeom geo[5];              // geometry of stages q|k|v, o, gate|up, down, lm_head
     const uint16_t* x0;            // pass input fp16 [K][H]
     float* logits;                 // [K][V]
     char* base;                    // workspace
@@ -186,15 +202,13 @@ __host__ __device__ inline void build_stage(const PassPlan& P, int stage, StageA
         A.glue = GLUE_RHO;
         A.n_in = W.cols;
         A.stats_in = P.stats + (size_t)(stage - 1) * P.stats_stride;
+        A.nstats_in = P.geo[pj].nstat;
         if (pj == 2) {
             A.src = P.sbuf + (size_t)pl * P.sbuf_stride;
             A.ld = P.FF;
-            A.nstats_in = stage_tiles_of(2 * P.FF, 1, P.FF);
         } else {
             A.src = (const float*)(P.base + (size_t)pl * P.layer_bytes + P.out_off[pj]);
-            const int prow = pj == 0 ? P.H + 2 * P.KV : P.H;
-            A.ld = prow;
-            A.nstats_in = stage_tiles_of(prow, 0, 0);
+            A.ld = pj == 0 ? P.H + 2 * P.KV : P.H;
         }
     }
     A.y_dtype = VQ_DTYPE_F32;
@@ -220,10 +234,42 @@ __host__ __device__ inline StageGeom stage_geom_cpw(int rows, int cols, int pair
     g.ntiles = paired ? (half + 31) >> 5 : (rows + 63) >> 6;
     g.cpw = cpw;
     g.nparts = (g.nchunks + cpw - 1) / cpw;
+    g.rk = 0;
+    g.R = 64;
+    g.nitems = g.ntiles * g.nparts;
+    g.xwb = 0;
+    g.nphase = 0;
+    g.nstat = g.ntiles;
     return g;
 }
 
-// Geometry with the run length the work-splitting model picks (host side).
+// The most split-K parts a tile geometry of a stage with `cols` columns can have (one
+// chunk per item); the partial buffers are sized for it.
+__host__ __device__ inline int max_parts(int cols) { return stage_geom_cpw(0, cols, 0, 0, 1).nchunks; }
+
+// Row-strip geometry for K columns: the whole row's activations in one LDS window
+// (NSG 64-block segments), R = 4 * rows per wave, with rows per wave 4, 2 or 1 as the
+// segments grow (the loads per lane stay at most ROWS_NLD).  rk = 0 when the row does
+// not fit one window (the tile kernel runs those stages).
+__host__ __device__ constexpr int rows_per_wave(int nsg) { return nsg <= 3 ? 4 : nsg <= 6 ? 2 : 1; }
+__host__ __device__ constexpr bool rows_fit(int K, int nsg) {
+    return nsg >= 1 && nsg <= 9 && (long)K * nsg * 64 * 64 <= ROWS_X_BYTES;
+}
+
+inline StageGeom rows_geom(int rows, int cols, int paired, int half, int K) {
+    StageGeom g = stage_geom_cpw(rows, cols, paired, half, 1);
+    const int nsg = (g.nb + 63) / 64;
+    if (K > ROWS_MAX_K || !rows_fit(K, nsg)) return g;
+    g.rk = 1;
+    g.xwb = 64 * nsg;
+    g.nphase = 1;
+    g.R = 4 * rows_per_wave(nsg);
+    g.nitems = paired ? (half + g.R / 2 - 1) / (g.R / 2) : (rows + g.R - 1) / g.R;
+    g.nstat = g.nitems;
+    return g;
+}
+
+// Tile-kernel geometry with the run length the work-splitting model picks (host side).
 inline StageGeom stage_geom(int rows, int cols, int paired, int half) {
     StageGeom g = stage_geom_cpw(rows, cols, paired, half, 1);
     long best = -1;
@@ -237,15 +283,28 @@ inline StageGeom stage_geom(int rows, int cols, int paired, int half) {
             g.cpw = c;
         }
     }
-    g.nparts = (g.nchunks + g.cpw - 1) / g.cpw;
-    return g;
+    return stage_geom_cpw(rows, cols, paired, half, g.cpw);
+}
+
+// Which kernel streams a stage.
+enum Kern { KERN_VALU = 0, KERN_MFMA = 1, KERN_ROWS = 2 };
+
+// Geometry of a stage for its kernel: the VALU tile kernel one chunk per item (measured
+// fastest), the MFMA tile kernel with the run length of the work-splitting model, the
+// row-strip kernel where the row's activations fit (the VALU tile kernel elsewhere).
+inline StageGeom plan_geom(int rows, int cols, int paired, int half, int K, Kern kern) {
+    if (kern == KERN_ROWS && K <= ROWS_MAX_K) {
+        const StageGeom g = rows_geom(rows, cols, paired, half, K);
+        if (g.rk) return g;
+    }
+    if (kern == KERN_MFMA) return stage_geom(rows, cols, paired, half);
+    return stage_geom_cpw(rows, cols, paired, half, 1);
 }
 size_t stage_scratch_bytes(int rows, int cols, int K, int paired, int half);
 void stage_scratch_carve(void* base, int rows, int cols, int K, int paired, int half, StageArgs* A);
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);
-hipError_t launch_stage(const StageArgs& A, bool mfma, hipStream_t st);
-// One persistent (cooperative) launch over the stages of a plan segment, separated by
-// grid barriers.  *nwg receives the grid size used.
+hipError_t launch_stage(const StageArgs& A, const StageGeom& g, bool mfma, hipStream_t st);
+// One persistent (cooperative) launch over the stages of a plan segment.
 hipError_t launch_pass_segment(const PassPlan& P, bool mfma, hipStream_t st);
 
 // Acceptance.

@@ -48,3 +48,22 @@ def upload_model(shape: synth.ModelShape, fmt: int, seed: int, threads: int = 16
     lm = vq.DeviceMatrix.from_host(synth.weight_matrix(fmt, seed, shape.n_layers, synth.MAT_LM_HEAD, r, c,
                                                        threads=threads))
     return vq.DeviceModel(layers, lm)
+
+
+GUARD_BYTES = 1 << 20
+GUARD_FILL = 0xA5
+
+
+def guarded_buffer(nbytes: int):
+    """A device byte buffer of exactly nbytes followed by a 1 MiB guard band of 0xA5 bytes:
+    returns (buffer view, whole allocation)."""
+    import torch
+    whole = torch.full((nbytes + GUARD_BYTES,), GUARD_FILL, dtype=torch.uint8, device="cuda")
+    return whole[:nbytes], whole
+
+
+def check_guard(whole, nbytes: int, what: str):
+    """No byte past the first nbytes of `whole` was written."""
+    tail = whole[nbytes:]
+    bad = int((tail != GUARD_FILL).sum().item())
+    assert bad == 0, f"{what}: {bad} bytes written past the end of the {nbytes}-byte buffer"

@@ -88,6 +88,12 @@ def test_linear_workspace_query():
     assert n >= 5 * 4 * 5120 * 4
     assert vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), 0) == 0
     assert vq.lib.vq_workspace_bytes(9, ctypes.byref(W), 4) == 0
+    # one partial per 1024-column chunk and K column, whatever run length a kernel picks
+    for rows, cols in ((5120, 17408), (151936, 5120), (64, 1056)):
+        W = _mat(rows=rows, cols=cols)
+        for K in (1, 4, 16):
+            n = vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), K)
+            assert n >= -(-cols // 1024) * K * rows * 4, (rows, cols, K)
 
 
 def _acc(**kw):
@@ -166,7 +172,7 @@ def test_decode_validation_and_layout():
 
 
 @pytest.mark.parametrize("path,code", [
-    (3, vq.ERR_ARG),                                              # no such kernel
+    (vq.PATH_ROWS, vq.ERR_UNSUPPORTED),                           # row-strip stops at K = 4
     (vq.LAUNCH_STAGED | vq.LAUNCH_PERSISTENT, vq.ERR_ARG),         # two launch modes
     (16, vq.ERR_ARG),
     (-4, vq.ERR_ARG),
@@ -177,6 +183,15 @@ def test_decode_path_and_launch_mode_errors(path, code):
     n9 = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 9)
     assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, 9, FAKE, path, FAKE, n9, None) == code
     assert vq.lib.vq_last_error()
+
+
+def test_persistent_launch_rejects_the_row_strip_kernel():
+    M, keep = _model()
+    for K in (1, 4):
+        n = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), K)
+        rc = vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, K, FAKE, vq.PATH_ROWS | vq.LAUNCH_PERSISTENT, FAKE, n, None)
+        assert rc == vq.ERR_UNSUPPORTED
+        assert b"row-strip" in vq.lib.vq_last_error()
 
 
 def test_decode_error_word_lies_in_the_workspace():

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import check_rows, need_gpu, say, upload_model
+from gpu_util import check_guard, check_rows, guarded_buffer, need_gpu, say, upload_model
 
 pytestmark = pytest.mark.gpu
 
@@ -70,21 +70,23 @@ def _check_glue(xin, expect, what):
     assert not bad.any()
 
 
-LAUNCHES = [4, 8]          # staged, persistent
-
-
-@pytest.mark.parametrize("launch", LAUNCHES)
-@pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_MXFP4])
-@pytest.mark.parametrize("K,path", [(1, 1), (4, 1), (8, 1), (4, 2), (16, 2)])
-def test_mini_model_every_stage(fmt, K, path, launch):
-    """A 2-layer stack (hidden 256, kv 64, ffn 512, vocab 1000): all rows of all stages."""
+def _every_stage(shape, seed, fmt, K, path):
+    """One pass over the stack; every row of every stage checked against the oracle, the
+    workspace and the logits guarded against writes past their ends."""
     torch = need_gpu()
     import speculative_decoding_verification_bit_amd as vq
-    shape, seed = synth.SHAPE_MINI, 4
     model = upload_model(shape, fmt, seed)
     x0 = synth.activations(seed, K, shape.hidden)
-    logits, ws = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=path | launch)
+    nws = model.workspace_bytes(K)
+    ws, ws_whole = guarded_buffer(nws)
+    nlg = K * shape.vocab * 4
+    lg, lg_whole = guarded_buffer(nlg)
+    logits = lg.view(torch.float32).view(K, shape.vocab)
+    say(f"every stage: {shape} fmt {fmt} K {K} path {path}")
+    vq.decode_pass(model, torch.from_numpy(x0).cuda(), logits, path=path, ws=ws)
     torch.cuda.synchronize()
+    check_guard(ws_whole, nws, "decode workspace")
+    check_guard(lg_whole, nlg, "logits")
     assert model.barrier_error(K, ws) == 0
     prev = None
     for s in range(4 * shape.n_layers + 1):
@@ -100,8 +102,38 @@ def test_mini_model_every_stage(fmt, K, path, launch):
     assert np.isfinite(logits.cpu().numpy()).all()
 
 
-@pytest.mark.parametrize("fmt,Ks", [(synth.FMT_Q4_MIN, (1, 4, 8)), (synth.FMT_MXFP4, (16,))])
-def test_27b_stack_sampled_rows(fmt, Ks):
+LAUNCHES = [4, 8]          # staged, persistent
+
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+@pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_MXFP4])
+@pytest.mark.parametrize("K,path", [(1, 1), (4, 1), (8, 1), (4, 2), (16, 2), (1, 3), (4, 3)])
+def test_mini_model_every_stage(fmt, K, path, launch):
+    """A 2-layer stack (hidden 256, kv 64, ffn 512, vocab 1000): all rows of all stages."""
+    if path == 3 and launch == 8:
+        pytest.skip("the persistent launch rejects the row-strip kernel: run inside the cooperative "
+                    "pass kernel it made an illegal memory access at K = 4 whose cause was not found, "
+                    "so that combination is switched off (VQ_ERR_UNSUPPORTED, checked in test_abi)")
+    _every_stage(synth.SHAPE_MINI, 4, fmt, K, path | launch)
+
+
+# Two layers whose stages split into several 1024-column chunks (split-K partials, tile
+# arrival counters), small enough for every row of every stage to be checked.
+SHAPE_MID = synth.ModelShape(n_layers=2, hidden=2048, kv_dim=256, ffn=5120, vocab=4000)
+
+
+@pytest.mark.parametrize("launch", LAUNCHES)
+@pytest.mark.parametrize("K,path", [(1, 0), (4, 1), (8, 1), (8, 2), (16, 2), (2, 3)])
+def test_mid_model_every_stage_split_k(K, path, launch):
+    """hidden 2048, kv 256, ffn 5120, vocab 4000: 2 and 5 column chunks per row."""
+    if path == 3 and launch == 8:
+        pytest.skip("the persistent launch does not run the row-strip kernel")
+    _every_stage(SHAPE_MID, 9, synth.FMT_Q4_MIN, K, path | launch)
+
+
+@pytest.mark.parametrize("fmt,runs", [(synth.FMT_Q4_MIN, ((1, 0), (4, 0), (8, 0), (1, 3))),
+                                      (synth.FMT_MXFP4, ((16, 0),))])
+def test_27b_stack_sampled_rows(fmt, runs):
     """The full 27B-class stack (64 layers, 5120 / 1024 / 17408, vocab 151936) in one pass;
     stages of layers 0, 31, 63 and the lm_head checked on 24 sampled rows each, every
     checked stage's input against the glue of the previous output."""
@@ -121,28 +153,34 @@ def test_27b_stack_sampled_rows(fmt, Ks):
         mats[s] = synth.Q4Matrix(fmt, len(pick), full.cols, full.qs[pick], full.scales[pick],
                                  None if full.mins is None else full.mins[pick])
         del full
-    for K in Ks:
+    for K, path in runs:
         x0 = synth.activations(seed, K, shape.hidden)
-        logits, ws = vq.decode_pass(model, torch.from_numpy(x0).cuda())
+        nws = model.workspace_bytes(K)
+        ws, ws_whole = guarded_buffer(nws)
+        logits, _ = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=path, ws=ws)
         torch.cuda.synchronize()
-        # the other launch mode computes the same sums in the same order: identical bits
-        other = vq.LAUNCH_PERSISTENT
-        logits_st, ws_st = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=other)
-        torch.cuda.synchronize()
-        assert model.barrier_error(K, ws_st) == 0
-        assert torch.equal(logits, logits_st), f"K {K}: staged and persistent logits differ"
-        for s in stages:
-            assert all(np.array_equal(u.view(np.uint8), v.view(np.uint8)) for u, v in
-                       zip(_stage_io(model, shape, K, ws, logits, s), _stage_io(model, shape, K, ws_st, logits_st, s)))
-        del ws_st, logits_st
+        check_guard(ws_whole, nws, f"K {K} path {path}: decode workspace")
+        if path != vq.PATH_ROWS:            # the persistent launch runs tile kernels only
+            # the other launch mode computes the same sums in the same order: identical bits
+            other = vq.LAUNCH_PERSISTENT | path
+            ws_st, st_whole = guarded_buffer(nws)
+            logits_st, _ = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=other, ws=ws_st)
+            torch.cuda.synchronize()
+            check_guard(st_whole, nws, f"K {K} path {other}: decode workspace")
+            assert model.barrier_error(K, ws_st) == 0
+            assert torch.equal(logits, logits_st), f"K {K}: staged and persistent logits differ"
+            for s in stages:
+                assert all(np.array_equal(u.view(np.uint8), v.view(np.uint8)) for u, v in
+                           zip(_stage_io(model, shape, K, ws, logits, s), _stage_io(model, shape, K, ws_st, logits_st, s)))
+            del ws_st, st_whole, logits_st
         for s in stages:
             xin, out = _stage_io(model, shape, K, ws, logits, s)
             if s > 0:
                 _, prev = _stage_io(model, shape, K, ws, logits, s - 1)
                 _check_glue(xin, _expected_input(shape, s, prev), f"K {K} stage {s}")
             y_ref, a_ref = oracle.linear(mats[s], xin, threads=8)
-            check_rows(out[:, picks[s]], y_ref, a_ref, f"27B fmt {fmt} K {K} stage {s}")
-        del ws, logits
+            check_rows(out[:, picks[s]], y_ref, a_ref, f"27B fmt {fmt} K {K} path {path} stage {s}")
+        del ws, ws_whole, logits
         torch.cuda.empty_cache()
 
 
