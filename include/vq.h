@@ -91,6 +91,13 @@ typedef struct vq_matrix {
                                    stage waits on the completion counts of the previous one.
                                    Tile kernels only: with VQ_PATH_ROWS the pass returns
                                    VQ_ERR_UNSUPPORTED */
+#define VQ_LAUNCH_STREAM 16     /* (switched off in this build: VQ_ERR_UNSUPPORTED)
+                                   one cooperative launch per 8 layers, one 8-wave
+                                   workgroup per CU: every wave streams its rows' weights
+                                   through an LDS ring ahead of its arithmetic, across
+                                   stage boundaries.  K <= 2, path AUTO or VALU, hidden and
+                                   ffn widths up to 20480 (multiples of 64; of 128 for
+                                   MXFP4); otherwise VQ_ERR_UNSUPPORTED */
 
 #define VQ_MAX_K 16
 
@@ -229,7 +236,8 @@ int vq_decode_error_word(const vq_model* M, int32_t K, void* ws, int32_t** word)
 /*
  * vq_decode_pass_timed -- measurement hook: exactly the work of vq_decode_pass, plus
  * hipEventRecord(events[2i]) before and hipEventRecord(events[2i+1]) after the i-th
- * weight-streaming launch (one per stage when staged, one per 8 layers when persistent),
+ * weight-streaming launch (one per stage when staged, one per 8 layers when persistent
+ * or stream),
  * on `stream`, so the caller can time those launches (hipEventElapsedTime).
  *   events     : HOST array of n_events caller-created hipEvent_t handles (timing enabled)
  *   n_events   : >= 2 * (4 * n_layers + 1)
@@ -237,7 +245,7 @@ int vq_decode_error_word(const vq_model* M, int32_t K, void* ws, int32_t** word)
  *   runs       : HOST out [n_events / 2] (may be NULL): per launch, which kernel ran:
  *                -R for the row-strip kernel (R whole rows per workgroup item), c >= 1
  *                for the tile kernel with items of c chunks of 1024 columns (c > 1 is its
- *                multi-chunk variant), 0 for a persistent launch
+ *                multi-chunk variant), 0 for a persistent launch, -1 for a stream launch
  * Errors: as vq_decode_pass, plus VQ_ERR_ARG for a short or NULL-holding events array.
  */
 int vq_decode_pass_timed(const vq_model* M, const void* x0_f16, int32_t K, float* logits,

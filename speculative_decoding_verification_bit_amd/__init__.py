@@ -27,7 +27,7 @@ OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 FMT_Q4, FMT_Q4_MIN, FMT_MXFP4 = 0, 1, 2
 DTYPE_F32, DTYPE_F16 = 0, 1
 PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_ROWS = 0, 1, 2, 3
-LAUNCH_AUTO, LAUNCH_STAGED, LAUNCH_PERSISTENT = 0, 4, 8
+LAUNCH_AUTO, LAUNCH_STAGED, LAUNCH_PERSISTENT, LAUNCH_STREAM = 0, 4, 8, 16
 MODE_GREEDY, MODE_SAMPLE = 0, 1
 DRAFT_GIVEN, DRAFT_Q_ARGMAX, DRAFT_Q_SAMPLE, DRAFT_AGREE = 0, 1, 2, 3
 OP_LINEAR, OP_ACCEPT, OP_DECODE = 0, 1, 2

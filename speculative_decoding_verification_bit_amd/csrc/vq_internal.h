@@ -300,6 +300,16 @@ inline StageGeom plan_geom(int rows, int cols, int paired, int half, int K, Kern
     if (kern == KERN_MFMA) return stage_geom(rows, cols, paired, half);
     return stage_geom_cpw(rows, cols, paired, half, 1);
 }
+// Stream-ahead pass (LDS-direct weight rings, one 8-wave workgroup per CU): K up to
+// STREAM_MAX_K, stage widths up to VQ_STREAM_MAX_COLS columns.
+constexpr int STREAM_WAVES = 8;
+constexpr int STREAM_MAX_K = 2;
+#define VQ_STREAM_MAX_COLS 20480
+bool stream_enabled();
+size_t stream_lds_bytes(int K, int H, int FF);
+int stream_supported(int fmt, int K, int H, int KV, int FF);
+hipError_t launch_stream_segment(const PassPlan& P, hipStream_t st);
+
 size_t stage_scratch_bytes(int rows, int cols, int K, int paired, int half);
 void stage_scratch_carve(void* base, int rows, int cols, int K, int paired, int half, StageArgs* A);
 hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);

@@ -174,7 +174,7 @@ def test_decode_validation_and_layout():
 @pytest.mark.parametrize("path,code", [
     (vq.PATH_ROWS, vq.ERR_UNSUPPORTED),                           # row-strip stops at K = 4
     (vq.LAUNCH_STAGED | vq.LAUNCH_PERSISTENT, vq.ERR_ARG),         # two launch modes
-    (16, vq.ERR_ARG),
+    (32, vq.ERR_ARG),
     (-4, vq.ERR_ARG),
     (vq.PATH_VALU | vq.LAUNCH_PERSISTENT, vq.ERR_UNSUPPORTED),     # VALU stops at K = 8
 ])
@@ -183,6 +183,17 @@ def test_decode_path_and_launch_mode_errors(path, code):
     n9 = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 9)
     assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, 9, FAKE, path, FAKE, n9, None) == code
     assert vq.lib.vq_last_error()
+
+
+def test_stream_launch_limits():
+    M, keep = _model()
+    for K, path in ((3, vq.LAUNCH_STREAM), (1, vq.LAUNCH_STREAM | vq.PATH_MFMA),
+                    (1, vq.LAUNCH_STREAM | vq.PATH_ROWS), (1, vq.LAUNCH_STREAM)):
+        n = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), K)
+        assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, K, FAKE, path, FAKE, n, None) == vq.ERR_UNSUPPORTED
+    n = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 1)
+    assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, 1, FAKE, vq.LAUNCH_STREAM | vq.LAUNCH_STAGED, FAKE, n,
+                                 None) == vq.ERR_ARG
 
 
 def test_persistent_launch_rejects_the_row_strip_kernel():

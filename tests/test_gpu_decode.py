@@ -131,6 +131,45 @@ def test_mid_model_every_stage_split_k(K, path, launch):
     _every_stage(SHAPE_MID, 9, synth.FMT_Q4_MIN, K, path | launch)
 
 
+STREAM_OFF = ("the stream launch is switched off: its first GPU run (mini stack, K = 1, Q4 with mins) "
+              "made a memory fault whose cause is not found; host emulation of its addressing finds "
+              "every access in bounds")
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_MXFP4])
+@pytest.mark.parametrize("K", [1, 2])
+def test_stream_every_stage(fmt, K):
+    """The stream launch on the 2-layer mini stack and on the split-K one (hidden 2048,
+    ffn 5120): every row of every stage against the oracle."""
+    pytest.skip(STREAM_OFF)
+    import speculative_decoding_verification_bit_amd as vq
+    _every_stage(synth.SHAPE_MINI, 4, fmt, K, vq.LAUNCH_STREAM)
+    _every_stage(SHAPE_MID, 9, fmt, K, vq.LAUNCH_STREAM)
+
+
+def test_stream_reproducible_and_close_to_staged():
+    """Two stream passes give identical bits; staged and stream logits agree to rounding."""
+    pytest.skip(STREAM_OFF)
+    torch = need_gpu()
+    import speculative_decoding_verification_bit_amd as vq
+    shape, seed, K = SHAPE_MID, 11, 1
+    model = upload_model(shape, synth.FMT_Q4_MIN, seed)
+    x0 = torch.from_numpy(synth.activations(seed, K, shape.hidden)).cuda()
+    a, _ = vq.decode_pass(model, x0, path=vq.LAUNCH_STREAM)
+    b, _ = vq.decode_pass(model, x0, path=vq.LAUNCH_STREAM)
+    c, _ = vq.decode_pass(model, x0, path=vq.LAUNCH_STAGED)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    rel = float((a - c).abs().max() / c.abs().max())
+    say(f"stream vs staged logits: max |diff| / max |logit| = {rel:.2e}")
+    assert rel < 1e-3
+
+
+def test_27b_stack_stream_sampled_rows():
+    """The 27B-class stack through the stream launch, sampled rows against the oracle."""
+    pytest.skip(STREAM_OFF)
+
+
 @pytest.mark.parametrize("fmt,runs", [(synth.FMT_Q4_MIN, ((1, 0), (4, 0), (8, 0), (1, 3))),
                                       (synth.FMT_MXFP4, ((16, 0),))])
 def test_27b_stack_sampled_rows(fmt, runs):
@@ -160,7 +199,7 @@ def test_27b_stack_sampled_rows(fmt, runs):
         logits, _ = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=path, ws=ws)
         torch.cuda.synchronize()
         check_guard(ws_whole, nws, f"K {K} path {path}: decode workspace")
-        if path != vq.PATH_ROWS:            # the persistent launch runs tile kernels only
+        if path not in (vq.PATH_ROWS, vq.LAUNCH_STREAM):   # persistent: tile kernels, same sums
             # the other launch mode computes the same sums in the same order: identical bits
             other = vq.LAUNCH_PERSISTENT | path
             ws_st, st_whole = guarded_buffer(nws)
