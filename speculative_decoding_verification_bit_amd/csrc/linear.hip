@@ -115,6 +115,26 @@ __device__ __forceinline__ SegRef seg_ref(const Mat& W, int seg) {
 
 // rs[k] = 1 / sqrt(sum_i stats_in[i][k] / n_in): per-column inverse RMS of the previous
 // stage's output, from its per-tile sums of squares (summed in a fixed order).
+// The workgroup's sum of its threads' partial sums acc[k] (a fixed order: each wave's DPP
+// tree, then the four waves), turned into the input scales rs[k] = 1 / sqrt(sum / n_in).
+__device__ void rms_reduce(const StageArgs& A, const float (&acc)[VQ_MAX_K], float* rs, float* sh) {
+    const int K = A.K;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < VQ_MAX_K; ++k)
+        if (k < K) {
+            const float w = wave_sum(acc[k]);
+            if (lane == 0) sh[4 * k + wave] = w;
+        }
+    __syncthreads();
+    if (threadIdx.x < (unsigned)K) {
+        const float* t = sh + 4 * threadIdx.x;
+        rs[threadIdx.x] = 1.0f / __fsqrt_rn(__fdiv_rn((t[0] + t[1]) + (t[2] + t[3]), (float)A.n_in));
+    }
+    __syncthreads();
+}
+
+// Thread t sums entries t, t + 256, ... of the previous stage's sums of squares.
 __device__ void stage_rms(const StageArgs& A, float* rs, float* sh) {
     if (A.glue == GLUE_NONE) return;
     const int K = A.K;
@@ -125,16 +145,50 @@ __device__ void stage_rms(const StageArgs& A, float* rs, float* sh) {
 #pragma unroll
         for (int k = 0; k < VQ_MAX_K; ++k)
             if (k < K) acc[k] += A.stats_in[(size_t)i * K + k];
-    for (int k = 0; k < K; ++k) sh[k * 256 + threadIdx.x] = acc[k];
-    __syncthreads();
-    for (int st = 128; st > 0; st >>= 1) {
-        if (threadIdx.x < (unsigned)st)
-            for (int k = 0; k < K; ++k) sh[k * 256 + threadIdx.x] += sh[k * 256 + threadIdx.x + st];
-        __syncthreads();
+    rms_reduce(A, acc, rs, sh);
+}
+
+// The same sums with the loads issued early (before a workgroup's weights, so that
+// waiting for them does not wait for the weights too): at most STATS_PRE entries per
+// thread, loaded unconditionally from clamped addresses.  `ok` is false when the stage
+// has more entries (or no input scales); stats_finish then falls back to stage_rms.
+constexpr int STATS_PRE = 4;
+template <int K>
+struct StatsPre {
+    float a[STATS_PRE][K];
+    bool ok;
+};
+
+template <int K>
+__device__ __forceinline__ void stats_issue(const StageArgs& A, StatsPre<K>& S) {
+    S.ok = A.glue != GLUE_NONE && A.nstats_in <= 256 * STATS_PRE;
+    // a readable stand-in address when there is nothing to load
+    const float* p = S.ok ? A.stats_in : reinterpret_cast<const float*>(A.W.qs[0]);
+    const int last = S.ok ? A.nstats_in - 1 : 0;
+#pragma unroll
+    for (int j = 0; j < STATS_PRE; ++j) {
+        const int i = min((int)threadIdx.x + 256 * j, last);
+#pragma unroll
+        for (int k = 0; k < K; ++k) S.a[j][k] = ld_global<float>(p + (S.ok ? (size_t)i * K + k : 0));
     }
-    if (threadIdx.x < (unsigned)K)
-        rs[threadIdx.x] = 1.0f / __fsqrt_rn(__fdiv_rn(sh[threadIdx.x * 256], (float)A.n_in));
-    __syncthreads();
+}
+
+template <int K>
+__device__ void stats_finish(const StageArgs& A, const StatsPre<K>& S, float* rs, float* sh) {
+    if (A.glue == GLUE_NONE) return;
+    if (!S.ok) {
+        stage_rms(A, rs, sh);
+        return;
+    }
+    float acc[VQ_MAX_K];
+#pragma unroll
+    for (int k = 0; k < VQ_MAX_K; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int j = 0; j < STATS_PRE; ++j)
+        if ((int)threadIdx.x + 256 * j < A.nstats_in)
+#pragma unroll
+            for (int k = 0; k < K; ++k) acc[k] += S.a[j][k];
+    rms_reduce(A, acc, rs, sh);
 }
 
 __device__ __forceinline__ void keep_x8(const StageArgs& A, int k, int col, const uint32_t (&h)[8]) {
@@ -327,13 +381,37 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One lane's share of a chunk's activations (elements 4s..4s+3 of block c of the wave's
+// group, per column), before conversion.
+template <int K>
+struct XPre {
+    uint2 r16[K];
+    f4_t r32[K];
+};
+
+template <int K>
+__device__ __forceinline__ void x_issue(const StageArgs& A, int nb, int ch, XPre<K>& X) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int s = lane >> 3, c = lane & 7;
+    const int b = (ch * 4 + wave) * 8 + c;
+    const int col = 32 * (b < nb ? b : nb - 1) + 4 * s;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (A.glue == GLUE_NONE) X.r16[k] = *reinterpret_cast<const uint2*>(A.x16 + (size_t)k * A.W.cols + col);
+        else X.r32[k] = *reinterpret_cast<const f4_t*>(A.src + (size_t)k * A.ld + col);
+    }
+}
+
 // On entry `cur` holds the item's first chunk and sm.rs the stage's input scales.  Each
-// chunk's activations are loaded and converted, then the next weights are issued (the
-// next chunk, else the first chunk of item (ntile, npart) unless ntile < 0), then the
-// chunk is computed; on return `cur` holds those next weights.
+// chunk's activations are loaded (the first chunk's may come preloaded in *pre) and
+// converted, then the next weights are issued (the next chunk, else the first chunk of
+// item (ntile, npart) unless ntile < 0), then the chunk is computed; on return `cur`
+// holds those next weights.
 template <int FMT, int K, bool MULTI>
 __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile, int part, StageSmem& sm,
-                                uint2 (&xs)[4][K][8][8], WTileV& cur, int ntile, int npart) {
+                                uint2 (&xs)[4][K][8][8], WTileV& cur, int ntile, int npart,
+                                const XPre<K>* pre = nullptr) {
     float (*red)[16][65] = sm.red;
     float (*fin)[64] = sm.fin;
     const float* rs = sm.rs;
@@ -355,13 +433,11 @@ __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile
         const int bcl = live ? b : nb - 1;
         const int col = 32 * bcl + 4 * s;
         // this chunk's activations: lane (s, c) takes elements 4s..4s+3 of block c
-        uint2 r16[K];
-        f4_t r32[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            if (A.glue == GLUE_NONE) r16[k] = *reinterpret_cast<const uint2*>(A.x16 + (size_t)k * A.W.cols + col);
-            else r32[k] = *reinterpret_cast<const f4_t*>(A.src + (size_t)k * A.ld + col);
-        }
+        XPre<K> X;
+        if (pre && ch == c0) X = *pre;
+        else x_issue<K>(A, nb, ch, X);
+        const uint2 (&r16)[K] = X.r16;
+        const f4_t (&r32)[K] = X.r32;
         // fp16 inputs; the wave shares them through LDS, so that each lane then holds its
         // block's 32 activations per column in the widened pair order
         const bool keeper = A.keep && tile == 0 && live;
@@ -437,9 +513,22 @@ __global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, const Sta
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int tile = item / g.nparts, part = item - tile * g.nparts;
     WTileV cur;
-    prefetch_valu<FMT>(A, tile, part * g.cpw, cur);
-    stage_rms(A, sm.rs, &sm.red[0][0][0]);
-    stage_item_valu<FMT, K, MULTI>(A, g, tile, part, sm, xs, cur, -1, 0);
+    if constexpr (MULTI) {
+        prefetch_valu<FMT>(A, tile, part * g.cpw, cur);
+        stage_rms(A, sm.rs, &sm.red[0][0][0]);
+        stage_item_valu<FMT, K, MULTI>(A, g, tile, part, sm, xs, cur, -1, 0);
+    } else {
+        // the small loads first (input sums of squares, the chunk's activations), then the
+        // weights: loads complete in order, so the scales and activations are ready
+        // without waiting for the weights
+        StatsPre<K> sp;
+        stats_issue<K>(A, sp);
+        XPre<K> xp;
+        x_issue<K>(A, g.nb, part, xp);
+        prefetch_valu<FMT>(A, tile, part, cur);
+        stats_finish<K>(A, sp, sm.rs, &sm.red[0][0][0]);
+        stage_item_valu<FMT, K, MULTI>(A, g, tile, part, sm, xs, cur, -1, 0, &xp);
+    }
 }
 
 // ------------------------------------------------------------------ MFMA kernel
