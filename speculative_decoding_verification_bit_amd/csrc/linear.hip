@@ -134,60 +134,62 @@ __device__ void rms_reduce(const StageArgs& A, const float (&acc)[VQ_MAX_K], flo
     __syncthreads();
 }
 
-// Thread t sums entries t, t + 256, ... of the previous stage's sums of squares.
+// Thread t sums the flat entries f = t, t + 256, ... of the previous stage's sums of
+// squares ([nstats_in][K], entry f belongs to column f mod K).
 __device__ void stage_rms(const StageArgs& A, float* rs, float* sh) {
     if (A.glue == GLUE_NONE) return;
-    const int K = A.K;
+    const int K = A.K, n = A.nstats_in * K;
     float acc[VQ_MAX_K];
 #pragma unroll
     for (int k = 0; k < VQ_MAX_K; ++k) acc[k] = 0.f;
-    for (int i = threadIdx.x; i < A.nstats_in; i += 256)
+    for (int f = threadIdx.x; f < n; f += 256) {
+        const float v = A.stats_in[f];
+        const int kf = f % K;
 #pragma unroll
-        for (int k = 0; k < VQ_MAX_K; ++k)
-            if (k < K) acc[k] += A.stats_in[(size_t)i * K + k];
+        for (int k = 0; k < VQ_MAX_K; ++k) acc[k] += k == kf ? v : 0.f;
+    }
     rms_reduce(A, acc, rs, sh);
 }
 
 // The same sums with the loads issued early (before a workgroup's weights, so that
-// waiting for them does not wait for the weights too): at most STATS_PRE entries per
-// thread, loaded unconditionally from clamped addresses.  `ok` is false when the stage
-// has more entries (or no input scales); stats_finish then falls back to stage_rms.
-constexpr int STATS_PRE = 4;
-template <int K>
+// waiting for them does not wait for the weights too): at most NPRE entries per thread,
+// loaded unconditionally from clamped addresses.  `ok` is false when the stage has more
+// entries (or no input scales); stats_finish then falls back to stage_rms.
+template <int NPRE>
 struct StatsPre {
-    float a[STATS_PRE][K];
+    float a[NPRE];
     bool ok;
 };
 
-template <int K>
-__device__ __forceinline__ void stats_issue(const StageArgs& A, StatsPre<K>& S) {
-    S.ok = A.glue != GLUE_NONE && A.nstats_in <= 256 * STATS_PRE;
+template <int NPRE>
+__device__ __forceinline__ void stats_issue(const StageArgs& A, StatsPre<NPRE>& S) {
+    const int n = A.nstats_in * A.K;
+    S.ok = A.glue != GLUE_NONE && n <= 256 * NPRE;
     // a readable stand-in address when there is nothing to load
     const float* p = S.ok ? A.stats_in : reinterpret_cast<const float*>(A.W.qs[0]);
-    const int last = S.ok ? A.nstats_in - 1 : 0;
+    const int last = S.ok ? n - 1 : 0;
 #pragma unroll
-    for (int j = 0; j < STATS_PRE; ++j) {
-        const int i = min((int)threadIdx.x + 256 * j, last);
-#pragma unroll
-        for (int k = 0; k < K; ++k) S.a[j][k] = ld_global<float>(p + (S.ok ? (size_t)i * K + k : 0));
-    }
+    for (int j = 0; j < NPRE; ++j) S.a[j] = ld_global<float>(p + min((int)threadIdx.x + 256 * j, last));
 }
 
-template <int K>
-__device__ void stats_finish(const StageArgs& A, const StatsPre<K>& S, float* rs, float* sh) {
+template <int NPRE>
+__device__ void stats_finish(const StageArgs& A, const StatsPre<NPRE>& S, float* rs, float* sh) {
     if (A.glue == GLUE_NONE) return;
     if (!S.ok) {
         stage_rms(A, rs, sh);
         return;
     }
+    const int K = A.K, n = A.nstats_in * K;
     float acc[VQ_MAX_K];
 #pragma unroll
     for (int k = 0; k < VQ_MAX_K; ++k) acc[k] = 0.f;
 #pragma unroll
-    for (int j = 0; j < STATS_PRE; ++j)
-        if ((int)threadIdx.x + 256 * j < A.nstats_in)
+    for (int j = 0; j < NPRE; ++j) {
+        const int f = (int)threadIdx.x + 256 * j;
+        const int kf = f % K;
 #pragma unroll
-            for (int k = 0; k < K; ++k) acc[k] += S.a[j][k];
+        for (int k = 0; k < VQ_MAX_K; ++k) acc[k] += (f < n && k == kf) ? S.a[j] : 0.f;
+    }
     rms_reduce(A, acc, rs, sh);
 }
 
@@ -252,24 +254,24 @@ __device__ void stage_epilogue(const StageArgs& A, int tile, int part, int npart
         else
             st_shared_f32(reinterpret_cast<float*>(A.y) + o, fin[k][l], A.coh);
     }
-    if (A.stats_out && threadIdx.x < (unsigned)K) {
-        const int k = threadIdx.x;
-        float ss = 0.f;
-        if (A.paired) {
-            const int half = A.W.seg_end[0];
-            for (int l = 0; l < 32; ++l) {
-                if (!row_ok(A, tile, l)) break;
-                const float v = silu_mul(fin[k][l], fin[k][32 + l]);
-                st_shared_f32(A.sbuf + (size_t)k * half + 32 * tile + l, v, A.coh);
-                ss += v * v;
-            }
-        } else {
-            for (int l = 0; l < 64; ++l) {
+    if (A.stats_out && threadIdx.x < 64) {
+        // wave 0, one lane per row: silu(gate) * up (paired) and the tile's sums of squares
+        const int l = threadIdx.x;
+        for (int k = 0; k < K; ++k) {
+            float sq = 0.f;
+            if (A.paired) {
+                if (l < 32 && row_ok(A, tile, l)) {
+                    const float v = silu_mul(fin[k][l], fin[k][32 + l]);
+                    st_shared_f32(A.sbuf + (size_t)k * A.W.seg_end[0] + 32 * tile + l, v, A.coh);
+                    sq = v * v;
+                }
+            } else {
                 const int row = 64 * tile + l;
-                if (row < A.nstat && row < rows) ss += fin[k][l] * fin[k][l];
+                if (row < A.nstat && row < rows) sq = fin[k][l] * fin[k][l];
             }
+            const float ss = wave_sum(sq);
+            if (l == 0) st_shared_f32(A.stats_out + (size_t)tile * K + k, ss, A.coh);
         }
-        st_shared_f32(A.stats_out + (size_t)tile * K + k, ss, A.coh);
     }
     if (A.done) {
         // the tile's outputs are in memory before its XCD group's counter counts it
@@ -521,12 +523,12 @@ __global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, const Sta
         // the small loads first (input sums of squares, the chunk's activations), then the
         // weights: loads complete in order, so the scales and activations are ready
         // without waiting for the weights
-        StatsPre<K> sp;
-        stats_issue<K>(A, sp);
+        StatsPre<4 * K> sp;
+        stats_issue<4 * K>(A, sp);
         XPre<K> xp;
         x_issue<K>(A, g.nb, part, xp);
         prefetch_valu<FMT>(A, tile, part, cur);
-        stats_finish<K>(A, sp, sm.rs, &sm.red[0][0][0]);
+        stats_finish<4 * K>(A, sp, sm.rs, &sm.red[0][0][0]);
         stage_item_valu<FMT, K, MULTI>(A, g, tile, part, sm, xs, cur, -1, 0, &xp);
     }
 }
@@ -680,9 +682,36 @@ __device__ __forceinline__ void prefetch_mfma(const StageArgs& A, int tile, int 
 
 // As stage_item_valu (the same chunk run, load order and next-weights contract); the
 // MFMA accumulators carry the sums across the run.
+// One lane's raw activations of a chunk for the MFMA A operands: column j = lane mod 16,
+// k-quarter gq = lane / 16 of each of the wave's 8 blocks (8 fp16 of the input, or 8 f32
+// of the previous output).
+struct MPre {
+    f4_t raw[8][2];
+};
+
+__device__ __forceinline__ void mraw_issue(const StageArgs& A, int nb, int ch, MPre& X) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, gq = lane >> 4;
+    const int kk = j < A.K ? j : 0;
+    const int bb0 = min((ch * 4 + wave) * 8, nb - 1);
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+        const int col = 32 * min(bb0 + tt, nb - 1) + 8 * gq;
+        if (A.glue == GLUE_NONE) {
+            X.raw[tt][0] = __builtin_bit_cast(f4_t, *reinterpret_cast<const u4_t*>(A.x16 + (size_t)kk * A.W.cols + col));
+            X.raw[tt][1] = X.raw[tt][0];
+        } else {
+            const float* p = A.src + (size_t)kk * A.ld + col;
+            X.raw[tt][0] = *reinterpret_cast<const f4_t*>(p);
+            X.raw[tt][1] = *reinterpret_cast<const f4_t*>(p + 4);
+        }
+    }
+}
+
 template <int FMT, bool MULTI>
 __device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile, int part, StageSmem& sm,
-                                WTileM& cur, int ntile, int npart) {
+                                WTileM& cur, int ntile, int npart, const MPre* pre = nullptr) {
     float (*red)[16][65] = sm.red;
     float (*fin)[64] = sm.fin;
     const float* rs = sm.rs;
@@ -704,19 +733,10 @@ __device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile
         const int bb0 = min(b0, nb - 1);
         // A operands: activation column j, k-quarter gq of each block of the group (raw
         // values first: 8 fp16 of the input, or 8 f32 of the previous output)
-        f4_t raw[8][2];
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-            const int col = 32 * min(bb0 + tt, nb - 1) + 8 * gq;
-            if (A.glue == GLUE_NONE) {
-                raw[tt][0] = __builtin_bit_cast(f4_t, *reinterpret_cast<const u4_t*>(A.x16 + (size_t)kk * A.W.cols + col));
-                raw[tt][1] = raw[tt][0];
-            } else {
-                const float* p = A.src + (size_t)kk * A.ld + col;
-                raw[tt][0] = *reinterpret_cast<const f4_t*>(p);
-                raw[tt][1] = *reinterpret_cast<const f4_t*>(p + 4);
-            }
-        }
+        MPre X;
+        if (pre && ch == c0) X = *pre;
+        else mraw_issue(A, nb, ch, X);
+        const f4_t (&raw)[8][2] = X.raw;
         h8_t a[8];
         float bsum[8];
 #pragma unroll
@@ -789,9 +809,22 @@ __global__ __launch_bounds__(256) void k_stage_mfma(const StageArgs A, const Sta
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int tile = item / g.nparts, part = item - tile * g.nparts;
     WTileM cur;
-    prefetch_mfma<FMT>(A, tile, part * g.cpw, cur);
-    stage_rms(A, sm.rs, &sm.red[0][0][0]);
-    stage_item_mfma<FMT, MULTI>(A, g, tile, part, sm, cur, -1, 0);
+    // the small loads first, then the weights, as in the VALU kernel: the input sums of
+    // squares always; the first chunk's activations too for one-chunk items (with chunk
+    // runs they would hold too many registers across the weight loads)
+    StatsPre<8> sp;
+    stats_issue<8>(A, sp);
+    if constexpr (MULTI) {
+        prefetch_mfma<FMT>(A, tile, part * g.cpw, cur);
+        stats_finish<8>(A, sp, sm.rs, &sm.red[0][0][0]);
+        stage_item_mfma<FMT, MULTI>(A, g, tile, part, sm, cur, -1, 0);
+    } else {
+        MPre xp;
+        mraw_issue(A, g.nb, part, xp);
+        prefetch_mfma<FMT>(A, tile, part, cur);
+        stats_finish<8>(A, sp, sm.rs, &sm.red[0][0][0]);
+        stage_item_mfma<FMT, MULTI>(A, g, tile, part, sm, cur, -1, 0, &xp);
+    }
 }
 
 
