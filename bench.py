@@ -99,7 +99,7 @@ def time_eager(torch, step, steps):
 
 PROFILE = os.path.join(ROOT, "profiles", "k_stage_valu_q4min_k1_27b_decode.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_decoding_verification_bit_amd", "csrc", f)
-                  for f in ("linear.hip", "vq_internal.h")]
+                  for f in ("linear.hip", "vq_device.h", "vq_internal.h")]
 
 
 def profiled_traffic(kernel_key):
@@ -131,8 +131,11 @@ def stage_weight_bytes(shape, synth, fmt):
 def time_stream_kernel(torch, vq, model, x0, logits, ws, passes, path, stage_bytes):
     """Per-launch durations of the weight-streaming kernels, from HIP events that the
     library records around each launch on the stream it launches on, grouped by kernel
-    instantiation (single- or multi-chunk items).  Returns {name: (launches per pass,
-    ms per pass, weight bytes per pass)} and the launches per pass."""
+    instantiation (single- or multi-chunk items).  The event brackets themselves
+    serialise the launches (about 2 us each), so every group's time is scaled by the
+    ratio of an unbracketed pass (two events on the same stream around decode_pass) to
+    the sum of the bracketed launch times.  Returns {name: (launches per pass, ms per pass,
+    weight bytes per pass, raw bracketed ms per pass)} and the launches per pass."""
     n_st = 4 * len(model.layers) + 1
     events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_st)]
     for ev in events:
@@ -140,17 +143,29 @@ def time_stream_kernel(torch, vq, model, x0, logits, ws, passes, path, stage_byt
     torch.cuda.synchronize()
     groups = {}
     n = 0
+    bracketed = 0.0
     for _ in range(passes):
         runs = vq.decode_pass_timed(model, x0, events, logits, ws, path=path)
         torch.cuda.synchronize()
         n = len(runs)
         for i, r in enumerate(runs):
-            key = "persistent" if r == 0 else "rows" if r < 0 else "multi" if r > 1 else "single"
+            key = "persistent" if r == 0 else "stream" if r == -1 else "rows" if r < 0 else "multi" if r > 1 else "single"
             ms = events[2 * i].elapsed_time(events[2 * i + 1])
-            b = stage_bytes[i] if r else sum(stage_bytes) / n
+            bracketed += ms
+            b = stage_bytes[i] if r > 0 or r < -1 else sum(stage_bytes) / n
             c, t, bb = groups.get(key, (0, 0.0, 0.0))
             groups[key] = (c + 1, t + ms, bb + b)
-    return {k: (c / passes, t / passes, b / passes) for k, (c, t, b) in groups.items()}, n
+    # the same passes without per-launch events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    plain = 0.0
+    for _ in range(passes):
+        e0.record()
+        vq.decode_pass(model, x0, logits, path=path, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        plain += e0.elapsed_time(e1)
+    scale = min(1.0, plain / bracketed) if bracketed > 0 else 1.0
+    return {k: (c / passes, t * scale / passes, b / passes, t / passes) for k, (c, t, b) in groups.items()}, n
 
 
 def cpu_baseline(synth, oracle_mod, budget_s: float):
@@ -257,17 +272,19 @@ def main():
     groups, n_launch = time_stream_kernel(torch, vq, model, x0_1, logits1, ws1, args.steps, vq.PATH_AUTO, sbytes)
     # the dominant kernel: the instantiation with the most time per pass
     dom = max(groups, key=lambda k: groups[k][1])
-    n_dom, ms_dom, b_dom = groups[dom]
+    n_dom, ms_dom, b_dom, raw_dom = groups[dom]
     avg_launch_ms = ms_dom / n_dom
     bytes_per_launch = b_dom / n_dom
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
     kname = {"single": "k_stage_valu<1, 1, false> (Q4_MIN, K 1, one chunk per item)",
              "multi": "k_stage_valu<1, 1, true> (Q4_MIN, K 1, chunk runs per item)",
              "rows": "k_rows_s<1, 1, NSG> (Q4_MIN, K 1, row strips)",
+             "stream": "k_stream<1, 1> (Q4_MIN, K 1, stream-ahead)",
              "persistent": "k_pass<1, 1, false> (Q4_MIN, K 1, persistent)"}[dom]
     value = wbytes / (ms1 * 1e-3) / 1e9
     log(f"K=1 step {ms1:.3f} ms ({value:.0f} GB/s), eager {eager1:.3f} ms; launches per pass {n_launch}; "
-        + "; ".join(f"{k}: {c:.0f} launches {t:.3f} ms {b / t / 1e6:.0f} GB/s" for k, (c, t, b) in groups.items()))
+        + "; ".join(f"{k}: {c:.0f} launches {t:.3f} ms ({r:.3f} ms bracketed) {b / t / 1e6:.0f} GB/s"
+                    for k, (c, t, b, r) in groups.items()))
     del g1
     other1 = None
     if not args.no_compare:
@@ -294,6 +311,7 @@ def main():
                      "traffic": profiled_traffic(dom),
                      "kernel": kname, "launches_per_pass": round(n_dom),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 3),
+                     "event_bracketed_avg_launch_us": round(raw_dom / n_dom * 1e3, 3),
                      "bytes_per_launch": round(bytes_per_launch)},
     }
 

@@ -285,12 +285,10 @@ __device__ void stage_epilogue(const StageArgs& A, int tile, int part, int npart
 
 // ------------------------------------------------------------------ VALU kernel
 
-// One wave's share of a 64-row tile: 8 rows x one block per lane; sr holds the block's
-// scale (Q4 with mins: the scale in the low half, the min in the high half).
-typedef uint16_t us2_t __attribute__((ext_vector_type(2)));
+// One wave's share of a 64-row tile: 8 rows x one block per lane.
 struct WTileV {
     u4_t w[8];
-    uint32_t sr[8];
+    uint32_t sr[8], mr[8];
 };
 
 template <int FMT>
@@ -305,15 +303,10 @@ __device__ __forceinline__ void load_tile_valu(const StageArgs& A, int tile, int
         T.w[i] = ld_global_nt<u4_t>(R.qs + (lr * rowq + 16u * b));
         if constexpr (FMT == VQ_FMT_MXFP4) {
             T.sr[i] = ld_global<uint8_t>(R.sc8 + (lr * nb + b));
-        } else if constexpr (FMT == VQ_FMT_Q4_MIN) {
-            // scale in the low half, min in the high half of one register (16-bit loads
-            // into either half)
-            us2_t sm;
-            sm.x = ld_global<uint16_t>(R.sc8 + 2u * (lr * nb + b));
-            sm.y = ld_global<uint16_t>(R.mn + (lr * nb + b));
-            T.sr[i] = __builtin_bit_cast(uint32_t, sm);
+            T.mr[i] = 0u;
         } else {
             T.sr[i] = ld_global<uint16_t>(R.sc8 + 2u * (lr * nb + b));
+            T.mr[i] = FMT == VQ_FMT_Q4_MIN ? (uint32_t)ld_global<uint16_t>(R.mn + (lr * nb + b)) : 0u;
         }
     }
 }
@@ -341,8 +334,8 @@ __device__ __forceinline__ void compute_tile_valu(const StageArgs& A, int tile, 
             }
         }
         const bool ok = live && row_ok(A, tile, 8 * i + s);
-        float d = FMT == VQ_FMT_MXFP4 ? e8m0_to_float(T.sr[i]) : half_bits_to_float(T.sr[i] & 0xffffu);
-        float m = FMT == VQ_FMT_Q4_MIN ? half_bits_to_float(T.sr[i] >> 16) : 0.f;
+        float d = FMT == VQ_FMT_MXFP4 ? e8m0_to_float(T.sr[i]) : half_bits_to_float(T.sr[i]);
+        float m = half_bits_to_float(T.mr[i]);
         d = ok ? d : 0.f;
         m = ok ? m : 0.f;
 #pragma unroll
