@@ -203,71 +203,95 @@ __device__ __forceinline__ void keep_x8(const StageArgs& A, int k, int col, cons
 // ------------------------------------------------------------------ epilogue
 
 // red[w][k][l] (w < 4 waves, k < K, l < 64 local rows) holds this workgroup's partials
-// for (tile, part).  Writes y (and the tile's sums of squares) once all parts of the
-// tile are in.
-__device__ void stage_epilogue(const StageArgs& A, int tile, int part, int nparts,
-                               float (*red)[16][65], float (*fin)[64], int* s_last) {
+// for (tile, part).  Wave w finishes columns w, w + 4, ... of the item, one lane per
+// local row.  With one column the other waves return at once (in a one-item launch they
+// end, which frees their registers and wave slots while wave 0 waits on memory).  Writes
+// y (and the tile's sums of squares) once all parts of the tile are in.
+template <int KR>
+__device__ void stage_epilogue(const StageArgs& A, int tile, int part, int nparts, float (*red)[KR][65],
+                               int* s_flag) {
+    constexpr int NC = (KR + 3) / 4;                 // columns per wave, at most
     const int K = A.K, rows = A.W.rows;
-    for (int e = threadIdx.x; e < K * 64; e += 256) {
-        const int k = e >> 6, l = e & 63;
-        fin[k][l] = ((red[0][k][l] + red[1][k][l]) + red[2][k][l]) + red[3][k][l];
+    const bool solo = K == 1;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (solo && wave > 0) return;
+    const int l = threadIdx.x & 63;
+    const bool ok = row_ok(A, tile, l);
+    const int orow = ok ? out_row(A, tile, l) : 0;
+    float fv[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int k = wave + 4 * j;
+        fv[j] = k < K ? ((red[0][k][l] + red[1][k][l]) + red[2][k][l]) + red[3][k][l] : 0.f;
     }
-    __syncthreads();
     if (nparts > 1) {
         // Partials, the counter and the last arriver's reads all use device-scope relaxed
         // atomics, which gfx950 performs coherently across XCDs without flushing or
-        // invalidating the L2; s_waitcnt 0 makes each thread's partial stores complete
+        // invalidating the L2; s_waitcnt 0 makes each wave's partial stores complete
         // before the workgroup's arrival is counted.
-        for (int e = threadIdx.x; e < K * 64; e += 256) {
-            const int k = e >> 6, l = e & 63;
-            if (row_ok(A, tile, l))
-                __hip_atomic_store(&A.part[((size_t)part * K + k) * rows + out_row(A, tile, l)], fin[k][l],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int k = wave + 4 * j;
+            if (k < K && ok)
+                __hip_atomic_store(&A.part[((size_t)part * K + k) * rows + orow], fv[j], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (threadIdx.x == 0)
-            *s_last = __hip_atomic_fetch_add(&A.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                      (unsigned)(nparts - 1);
-        __syncthreads();
-        if (!*s_last) return;
-        for (int e = threadIdx.x; e < K * 64; e += 256) {
-            const int k = e >> 6, l = e & 63;
+        bool last;
+        if (solo) {
+            unsigned prev = 0u;
+            if (l == 0)
+                prev = __hip_atomic_fetch_add(&A.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = (unsigned)__builtin_amdgcn_readfirstlane((int)prev) == (unsigned)(nparts - 1);
+        } else {
+            __syncthreads();
+            if (threadIdx.x == 0)
+                *s_flag = __hip_atomic_fetch_add(&A.counters[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                          (unsigned)(nparts - 1);
+            __syncthreads();
+            last = *s_flag != 0;
+        }
+        if (!last) return;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int k = wave + 4 * j;
             float v = 0.f;
-            if (row_ok(A, tile, l)) {
-                const int row = out_row(A, tile, l);
+            if (k < K && ok)
                 for (int c = 0; c < nparts; ++c)
-                    v += __hip_atomic_load(&A.part[((size_t)c * K + k) * rows + row], __ATOMIC_RELAXED,
+                    v += __hip_atomic_load(&A.part[((size_t)c * K + k) * rows + orow], __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
-            }
-            fin[k][l] = v;
+            fv[j] = v;
         }
         if (threadIdx.x == 0) __hip_atomic_store(&A.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
     }
-    for (int e = threadIdx.x; e < K * 64; e += 256) {
-        const int k = e >> 6, l = e & 63;
-        if (!row_ok(A, tile, l)) continue;
-        const size_t o = (size_t)k * rows + out_row(A, tile, l);
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int k = wave + 4 * j;
+        if (k >= K || !ok) continue;
+        const size_t o = (size_t)k * rows + orow;
         if (A.y_dtype == VQ_DTYPE_F16)
-            reinterpret_cast<uint16_t*>(A.y)[o] = (uint16_t)f2h_bits(fin[k][l]);
+            reinterpret_cast<uint16_t*>(A.y)[o] = (uint16_t)f2h_bits(fv[j]);
         else
-            st_shared_f32(reinterpret_cast<float*>(A.y) + o, fin[k][l], A.coh);
+            st_shared_f32(reinterpret_cast<float*>(A.y) + o, fv[j], A.coh);
     }
-    if (A.stats_out && threadIdx.x < 64) {
-        // wave 0, one lane per row: silu(gate) * up (paired) and the tile's sums of squares
-        const int l = threadIdx.x;
-        for (int k = 0; k < K; ++k) {
+    if (A.stats_out) {
+        // silu(gate) * up (paired: lane l < 32 holds gate, lane l + 32 up) and the tile's
+        // sums of squares
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int k = wave + 4 * j;
+            if (k >= K) continue;
             float sq = 0.f;
             if (A.paired) {
-                if (l < 32 && row_ok(A, tile, l)) {
-                    const float v = silu_mul(fin[k][l], fin[k][32 + l]);
+                const float up = __shfl(fv[j], (l + 32) & 63, 64);
+                if (l < 32 && ok) {
+                    const float v = silu_mul(fv[j], up);
                     st_shared_f32(A.sbuf + (size_t)k * A.W.seg_end[0] + 32 * tile + l, v, A.coh);
                     sq = v * v;
                 }
             } else {
                 const int row = 64 * tile + l;
-                if (row < A.nstat && row < rows) sq = fin[k][l] * fin[k][l];
+                if (row < A.nstat && row < rows) sq = fv[j] * fv[j];
             }
             const float ss = wave_sum(sq);
             if (l == 0) st_shared_f32(A.stats_out + (size_t)tile * K + k, ss, A.coh);
@@ -276,7 +300,7 @@ __device__ void stage_epilogue(const StageArgs& A, int tile, int part, int npart
     if (A.done) {
         // the tile's outputs are in memory before its XCD group's counter counts it
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        if (!solo) __syncthreads();
         if (threadIdx.x == 0)
             __hip_atomic_fetch_add(A.done + (blockIdx.x & 7) * DONE_STRIDE, 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -348,11 +372,11 @@ __device__ __forceinline__ void compute_tile_valu(const StageArgs& A, int tile, 
 }
 
 // LDS of one stage item (a 64-row tile x one chunk).
+template <int KR>
 struct StageSmem {
-    float red[4][16][65];          // the 4 waves' partials; also the RMS reduction scratch
-    float fin[VQ_MAX_K][64];
+    float red[4][KR][65];          // the 4 waves' partials; also the RMS reduction scratch
     float rs[VQ_MAX_K];
-    int last;
+    int flag;
 };
 
 // One item: a 64-row tile x a run of chunks [part * cpw, part * cpw + cpw) (a chunk is
@@ -411,11 +435,10 @@ __device__ __forceinline__ void x_issue(const StageArgs& A, int nb, int ch, XPre
 // item (ntile, npart) unless ntile < 0), then the chunk is computed; on return `cur`
 // holds those next weights.
 template <int FMT, int K, bool MULTI>
-__device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile, int part, StageSmem& sm,
+__device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile, int part, StageSmem<K>& sm,
                                 uint2 (&xs)[4][K][8][8], WTileV& cur, int ntile, int npart,
                                 const XPre<K>* pre = nullptr) {
-    float (*red)[16][65] = sm.red;
-    float (*fin)[64] = sm.fin;
+    float (*red)[K][65] = sm.red;
     const float* rs = sm.rs;
     const int nb = g.nb;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -505,12 +528,12 @@ __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile
             if (c == 0) red[wave][k][8 * i + s] = v;
         }
     __syncthreads();
-    stage_epilogue(A, tile, part, g.nparts, red, fin, &sm.last);
+    stage_epilogue<K>(A, tile, part, g.nparts, red, &sm.flag);
 }
 
 template <int FMT, int K, bool MULTI>
 __global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, const StageGeom g) {
-    __shared__ StageSmem sm;
+    __shared__ StageSmem<K> sm;
     __shared__ uint2 xs[4][K][8][8];          // [wave][column][block][quarter of 4 fp16]
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int tile = item / g.nparts, part = item - tile * g.nparts;
@@ -710,10 +733,9 @@ __device__ __forceinline__ void mraw_issue(const StageArgs& A, int nb, int ch, M
 }
 
 template <int FMT, bool MULTI>
-__device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile, int part, StageSmem& sm,
+__device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile, int part, StageSmem<16>& sm,
                                 WTileM& cur, int ntile, int npart, const MPre* pre = nullptr) {
     float (*red)[16][65] = sm.red;
-    float (*fin)[64] = sm.fin;
     const float* rs = sm.rs;
     const int K = A.K;
     const int nb = g.nb;
@@ -800,12 +822,12 @@ __device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave][4 * gq + v][16 * t + j] = acc[t][v];
     __syncthreads();
-    stage_epilogue(A, tile, part, g.nparts, red, fin, &sm.last);
+    stage_epilogue<16>(A, tile, part, g.nparts, red, &sm.flag);
 }
 
 template <int FMT, bool MULTI>
 __global__ __launch_bounds__(256) void k_stage_mfma(const StageArgs A, const StageGeom g) {
-    __shared__ StageSmem sm;
+    __shared__ StageSmem<16> sm;
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int tile = item / g.nparts, part = item - tile * g.nparts;
     WTileM cur;
@@ -1187,7 +1209,7 @@ __device__ void wait_count(const unsigned* cnt, unsigned target, int* err) {
 template <int FMT, int K, bool MFMA>
 __global__ __launch_bounds__(256) void k_pass(const PassPlan P) {
     struct Smem {
-        StageSmem st;
+        StageSmem<MFMA ? 16 : K> st;
         uint2 xs[4][MFMA ? 1 : K][8][8];
     };
     __shared__ Smem sm;
