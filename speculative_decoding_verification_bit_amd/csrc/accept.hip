@@ -65,6 +65,22 @@ __device__ __forceinline__ bool kept(const RowStat& s, float l, float e, int j, 
 
 // ---------------------------------------------------------------- block helpers
 
+// f(v, j) for the entries j = t, t + NT, t + 2 NT, ... of a row, in increasing j per
+// thread; RU consecutive strides are loaded together so that many loads are in flight.
+constexpr int RU = 16;
+template <class F>
+__device__ __forceinline__ void row_for(const float* l, int V, F&& f) {
+    int j = threadIdx.x;
+    for (; j + (RU - 1) * NT < V; j += RU * NT) {
+        float v[RU];
+#pragma unroll
+        for (int u = 0; u < RU; ++u) v[u] = l[j + u * NT];
+#pragma unroll
+        for (int u = 0; u < RU; ++u) f(v[u], j + u * NT);
+    }
+    for (; j < V; j += NT) f(l[j], j);
+}
+
 __device__ uint64_t block_sum_u64(uint64_t v, uint64_t* sh) {
     sh[threadIdx.x] = v;
     __syncthreads();
@@ -160,11 +176,10 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
     float best = -INFINITY;
     int bi = 0x7fffffff;
     int nf = 0;
-    for (int j = t; j < V; j += NT) {
-        const float v = l[j];
+    row_for(l, V, [&](float v, int j) {
         if (!isfinite(v)) nf = 1;
         else if (v > best) { best = v; bi = j; }
-    }
+    });
     shf[t] = best;
     shi[t] = bi;
     __syncthreads();
@@ -195,15 +210,37 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
     }
     const float T = A.T;
 
-    // pass 2: total mass
-    uint64_t z = 0;
-    for (int j = t; j < V; j += NT) z += to_fx(e_of(l[j], lmax, T));
+    // pass 2: total mass, and the mass and size of the min-p set (e >= min_p).  The
+    // min-p set is a prefix of the (logit descending, index ascending) order, like every
+    // top-p prefix, and the kept set is the shorter of the two.
+    uint64_t z = 0, zm = 0, nm = 0;
+    const float min_p = A.min_p;
+    row_for(l, V, [&](float v, int) {
+        const float e = e_of(v, lmax, T);
+        const uint64_t f = to_fx(e);
+        z += f;
+        if (e >= min_p) { zm += f; ++nm; }
+    });
     st.z_fx = block_sum_u64(z, sh);
 
     // pass 3: top-p cut
     if (A.top_p < 1.f) {
         uint64_t tgt = (uint64_t)ceil((double)A.top_p * (double)st.z_fx);
         if (tgt < 1) tgt = 1;
+        if (min_p > 0.f) {
+            const uint64_t zm_fx = block_sum_u64(zm, sh);
+            const uint64_t nm_all = block_sum_u64(nm, sh);
+            if (zm_fx < tgt) {
+                // the min-p set holds less than the top-p mass, so every top-p prefix
+                // contains it: the min-p cut is the shorter one and decides alone
+                st.thr_key = 0u;
+                st.thr_idx = 0x7fffffff;
+                st.keep_fx = zm_fx;
+                st.n_keep = (int)nm_all;
+                if (t == 0) A.out[row] = st;
+                return;
+            }
+        }
         uint32_t prefix = 0;
         int shift_hi = 32;      // bits already fixed: key >> shift_hi == prefix
         uint64_t above = 0;
@@ -214,13 +251,12 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
             const int shift = shift_hi - nbits;
             for (int i = t; i < nbins; i += NT) hist[i] = 0;
             __syncthreads();
-            for (int j = t; j < V; j += NT) {
-                const float v = l[j];
+            row_for(l, V, [&](float v, int) {
                 const uint32_t k = fkey(v);
                 if (shift_hi == 32 || (k >> shift_hi) == prefix)
                     atomicAdd((unsigned long long*)&hist[(k >> shift) & (nbins - 1)],
                               (unsigned long long)to_fx(e_of(v, lmax, T)));
-            }
+            });
             __syncthreads();
             int b;
             uint64_t ab;
@@ -235,17 +271,44 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
         const uint64_t estar = to_fx(e_of(lstar, lmax, T));
         const uint64_t need = tgt - above;
         const uint64_t c = estar ? (need + estar - 1) / estar : 1;
-        const int chunk = (V + NT - 1) / NT;
-        const int j0 = t * chunk, j1 = min(V, j0 + chunk);
+        // The entries with key kstar: usually a handful.  Up to NT of them are listed in
+        // LDS and the cc-th smallest index is found by ranking; more than that (long runs
+        // of equal logits) take an ordered scan over contiguous slices.
+        if (t == 0) s_bin = 0;
+        __syncthreads();
         uint64_t cnt = 0;
-        for (int j = j0; j < j1; ++j) cnt += fkey(l[j]) == kstar;
-        uint64_t tot;
-        const uint64_t before = block_excl_scan_u64(cnt, sh, &tot);
+        row_for(l, V, [&](float v, int j) {
+            if (fkey(v) == kstar) {
+                ++cnt;
+                const int at = atomicAdd(&s_bin, 1);
+                if (at < NT) shi[at] = j;
+            }
+        });
+        const uint64_t tot = block_sum_u64(cnt, sh);
         const uint64_t cc = c > tot ? tot : c;
-        if (before < cc && cc <= before + cnt) {
-            uint64_t seen = before;
-            for (int j = j0; j < j1; ++j)
-                if (fkey(l[j]) == kstar && ++seen == cc) { s_bin = j; break; }
+        if (tot <= (uint64_t)NT) {
+            __syncthreads();
+            int pick = -1;
+            if ((uint64_t)t < tot) {
+                const int mine = shi[t];
+                uint64_t rank = 0;
+                for (int i = 0; i < (int)tot; ++i) rank += shi[i] < mine;
+                if (rank + 1 == cc) pick = mine;
+            }
+            __syncthreads();
+            if (pick >= 0) s_bin = pick;
+        } else {
+            const int chunk = (V + NT - 1) / NT;
+            const int j0 = t * chunk, j1 = min(V, j0 + chunk);
+            uint64_t cs = 0;
+            for (int j = j0; j < j1; ++j) cs += fkey(l[j]) == kstar;
+            uint64_t tot2;
+            const uint64_t before = block_excl_scan_u64(cs, sh, &tot2);
+            if (before < cc && cc <= before + cs) {
+                uint64_t seen = before;
+                for (int j = j0; j < j1; ++j)
+                    if (fkey(l[j]) == kstar && ++seen == cc) { s_bin = j; break; }
+            }
         }
         __syncthreads();
         st.thr_key = kstar;
@@ -255,11 +318,10 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
 
     // pass 4: kept mass and size
     uint64_t kf = 0, kn = 0;
-    for (int j = t; j < V; j += NT) {
-        const float v = l[j];
+    row_for(l, V, [&](float v, int j) {
         const float e = e_of(v, lmax, T);
         if (kept(st, v, e, j, A.min_p)) { kf += to_fx(e); ++kn; }
-    }
+    });
     st.keep_fx = block_sum_u64(kf, sh);
     st.n_keep = (int)block_sum_u64(kn, sh);
     if (t == 0) A.out[row] = st;
@@ -317,20 +379,51 @@ __device__ __forceinline__ bool cross(uint64_t C, uint32_t u24, uint64_t S) {
 // Smallest j with prefix_j(w) * 2^24 > u24 * sum(w) (vocabulary order); -1 if sum is 0.
 template <class WF>
 __device__ int block_cat(WF wf, int V, uint32_t u24, uint64_t* sh, int* sres) {
+    // a thread's slice is read in groups of CU entries, all loads of a group in flight
+    constexpr int CU = 8;
     const int chunk = (V + NT - 1) / NT;
     const int j0 = threadIdx.x * chunk, j1 = min(V, j0 + chunk);
     uint64_t local = 0;
-    for (int j = j0; j < j1; ++j) local += wf(j);
+    int j = j0;
+    for (; j + CU <= j1; j += CU) {
+        uint64_t w[CU];
+#pragma unroll
+        for (int u = 0; u < CU; ++u) w[u] = wf(j + u);
+#pragma unroll
+        for (int u = 0; u < CU; ++u) local += w[u];
+    }
+    for (; j < j1; ++j) local += wf(j);
     uint64_t S;
     const uint64_t before = block_excl_scan_u64(local, sh, &S);
     if (threadIdx.x == 0) *sres = -1;
     __syncthreads();
     if (S > 0 && local > 0 && !cross(before, u24, S) && cross(before + local, u24, S)) {
+        // the running sum is non-decreasing: a group whose end does not cross holds no
+        // crossing, so only the crossing group is walked entry by entry
         uint64_t C = before;
-        for (int j = j0; j < j1; ++j) {
-            C += wf(j);
-            if (cross(C, u24, S)) { *sres = j; break; }
+        int found = -1;
+        int jj = j0;
+        for (; jj + CU <= j1 && found < 0; jj += CU) {
+            uint64_t w[CU];
+#pragma unroll
+            for (int u = 0; u < CU; ++u) w[u] = wf(jj + u);
+            uint64_t s8 = 0;
+#pragma unroll
+            for (int u = 0; u < CU; ++u) s8 += w[u];
+            if (cross(C + s8, u24, S)) {
+                for (int u = 0; u < CU; ++u) {
+                    C += w[u];
+                    if (cross(C, u24, S)) { found = jj + u; break; }
+                }
+            } else {
+                C += s8;
+            }
         }
+        for (; jj < j1 && found < 0; ++jj) {
+            C += wf(jj);
+            if (cross(C, u24, S)) found = jj;
+        }
+        *sres = found;
     }
     __syncthreads();
     const int r = *sres;
