@@ -131,6 +131,8 @@ struct DecodeLayout {
     size_t sbuf_off;               // silu(gate) * up, f32 [K][FF], sbuf_stride floats per layer
     size_t sbuf_stride;
     size_t scratch_off;            // split-K partials (sized for the largest stage)
+    size_t xp_off, xp_stride;      // MFMA input conversion, per stage: [blocks][64] x 16 B,
+    size_t xpa_rel;                // then (at xpa_rel) [groups][64] x 16 B
     size_t counters_off;           // sync words: tile arrival counters [max_tiles], error
                                    // flag, stage completion counters [stages][DONE_WORDS]
     int max_tiles;
@@ -188,6 +190,15 @@ DecodeLayout decode_layout(const Shapes& s, int K) {
     p += d.sbuf_stride * 4 * (size_t)s.L;
     d.scratch_off = p;
     p += sc;
+    {
+        // one region per stage (written once per pass, like every other buffer a later
+        // reader loads through its caches): conversion slots of the widest input
+        const size_t nbm = (size_t)std::max(s.H, s.FF) / 32;
+        d.xp_stride = align_up(nbm * 64 * 16, 256) + align_up((nbm + 7) / 8 * 64 * 16, 256);
+        d.xpa_rel = align_up(nbm * 64 * 16, 256);
+        d.xp_off = p;
+        p += d.xp_stride * (size_t)(4 * s.L + 1);
+    }
     d.counters_off = p;
     d.err_word = mt;
     d.done_word = (int)align_up((size_t)mt + 1, DONE_STRIDE);
@@ -425,6 +436,14 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
     P.counters = sync;
     P.err = (int*)(sync + d.err_word);
     P.done = (persistent || streamed) ? sync + d.done_word : nullptr;
+    if (mfma && !persistent && !streamed) {
+        // staged MFMA launches convert each stage's input once (the completion counters
+        // are unused in staged launches and serve as the conversion counters)
+        P.xp = (u4_t_*)(base + d.xp_off);
+        P.xpa = (u4_t_*)(base + d.xp_off + d.xpa_rel);
+        P.xp_stride = d.xp_stride / 16;
+        P.xflag = sync + d.done_word;
+    }
     P.coh = persistent ? 1 : 0;
     P.lm = MatPtrs{M->lm_head.qs, M->lm_head.scales, M->lm_head.mins};
     for (int j = 0; j < 5; ++j) {
@@ -478,6 +497,7 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
                     if (e != hipSuccess) return hip_fail(e, "event record");
                 }
                 const StageGeom& g = P.geo[stage == 4 * s.L ? 4 : stage & 3];
+                if (P.xflag && !g.rk) A.n_prep = N_PREP;
                 if (runs && nl < n_events / 2) runs[nl] = g.rk ? -g.R : g.cpw;
                 e = launch_stage(A, g, mfma, st);
                 if (e != hipSuccess) return hip_fail(e, "stage launch");

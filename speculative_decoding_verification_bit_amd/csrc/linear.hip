@@ -474,7 +474,7 @@ __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile
                 h[0] = r16[k].x & 0xffffu; h[1] = r16[k].x >> 16; h[2] = r16[k].y & 0xffffu; h[3] = r16[k].y >> 16;
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = f2h_bits(r32[k][e] * rs[k]);
+                for (int e = 0; e < 4; ++e) h[e] = f2h_scaled(r32[k][e], rs[k]);
             }
             const uint2 pk = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             xs[wave][k][c][s] = pk;
@@ -732,7 +732,7 @@ __device__ __forceinline__ void mraw_issue(const StageArgs& A, int nb, int ch, M
     }
 }
 
-template <int FMT, bool MULTI>
+template <int FMT, bool MULTI, bool PREP = false>
 __device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile, int part, StageSmem<16>& sm,
                                 WTileM& cur, int ntile, int npart, const MPre* pre = nullptr) {
     float (*red)[16][65] = sm.red;
@@ -753,13 +753,25 @@ __device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile
         const int b0 = (ch * 4 + wave) * 8;
         const int nvb = max(0, min(8, nb - b0));      // blocks of this group (wave-uniform)
         const int bb0 = min(b0, nb - 1);
+        h8_t a[8];
+        h8_t am = h8_t{};
+        if constexpr (PREP) {
+            // operands converted once for the whole stage (prep_x_mfma)
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt)
+                a[tt] = tt < nvb ? as_h8(ld_global<u4_t>(A.xp + (size_t)(b0 + tt) * 64 + lane)) : h8_t{};
+            if constexpr (FMT == VQ_FMT_Q4_MIN) {
+                const h8_t v = nvb > 0 ? as_h8(ld_global<u4_t>(A.xpa + (size_t)(b0 >> 3) * 64 + lane)) : h8_t{};
+#pragma unroll
+                for (int tt = 0; tt < 8; ++tt) am[tt] = tt < nvb ? v[tt] : (_Float16)0.0f;
+            }
+        } else {
         // A operands: activation column j, k-quarter gq of each block of the group (raw
         // values first: 8 fp16 of the input, or 8 f32 of the previous output)
         MPre X;
         if (pre && ch == c0) X = *pre;
         else mraw_issue(A, nb, ch, X);
         const f4_t (&raw)[8][2] = X.raw;
-        h8_t a[8];
         float bsum[8];
 #pragma unroll
         for (int tt = 0; tt < 8; ++tt) {
@@ -774,8 +786,8 @@ __device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    h[e] = f2h_bits(raw[tt][0][e] * r);
-                    h[4 + e] = f2h_bits(raw[tt][1][e] * r);
+                    h[e] = f2h_scaled(raw[tt][0][e], r);
+                    h[4 + e] = f2h_scaled(raw[tt][1][e], r);
                 }
             }
             if (keeper && tt < nvb) keep_x8(A, kk, 32 * (bb0 + tt) + 8 * gq, h);
@@ -789,7 +801,6 @@ __device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile
             a[tt] = use ? v : h8_t{};
             bsum[tt] = use ? sum : 0.f;
         }
-        h8_t am = h8_t{};
         if constexpr (FMT == VQ_FMT_Q4_MIN) {
             // block sums over the 4 k-quarters (lanes j, j+16, j+32, j+48), then fp16 hi / lo
 #pragma unroll
@@ -801,6 +812,7 @@ __device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile
                 const _Float16 lo = (_Float16)(v - (float)hi);
                 am[tt] = gq == 0 ? hi : (gq == 1 ? lo : (_Float16)0.0f);
             }
+        }
         }
         if constexpr (PREFETCH_NEXT) {
             // the next weights load while this chunk is computed (issued only now: a wait
@@ -825,9 +837,109 @@ __device__ void stage_item_mfma(const StageArgs& A, const StageGeom& g, int tile
     stage_epilogue<16>(A, tile, part, g.nparts, red, &sm.flag);
 }
 
-template <int FMT, bool MULTI>
+// The input conversion of stage_item_mfma for the whole stage, done once: wave v of
+// the n_prep converting workgroups takes groups of 8 blocks v, v + 4 n_prep, ...; lane
+// (j, gq) converts k-quarter gq of column j of each block with the same arithmetic and
+// order as the inline conversion, so both give the same bits.  Every 16-byte slot of xp
+// and xpa (hence every cache line a reader loads) is written whole by one wave: a line
+// assembled from several writers could leave a partly written copy in one XCD's L2.
+// Also writes the fp16 copy of the input (if any).
+template <int FMT>
+__device__ void prep_x_mfma(const StageArgs& A, const float* rs) {
+    const int K = A.K;
+    const int nb = A.W.cols >> 5;
+    const int ngrp = (nb + 7) >> 3;
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, gq = lane >> 4;
+    const bool col_live = j < K;
+    const int kk = col_live ? j : 0;
+    const float r = A.glue == GLUE_NONE ? 1.f : rs[kk];
+    const int nwv = A.n_prep * 4;
+    for (int gi = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6); gi < ngrp; gi += nwv) {
+        const int nvb = min(8, nb - 8 * gi);
+        u4_t am = {0u, 0u, 0u, 0u};
+        for (int tt = 0; tt < nvb; ++tt) {
+            const int b = 8 * gi + tt;
+            const int col = 32 * b + 8 * gq;
+            uint32_t h[8];
+            if (A.glue == GLUE_NONE) {
+                const u4_t v = *reinterpret_cast<const u4_t*>(A.x16 + (size_t)kk * A.W.cols + col);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[2 * e] = v[e] & 0xffffu;
+                    h[2 * e + 1] = v[e] >> 16;
+                }
+            } else {
+                const float* p = A.src + (size_t)kk * A.ld + col;
+                const f4_t x0 = *reinterpret_cast<const f4_t*>(p), x1 = *reinterpret_cast<const f4_t*>(p + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h[e] = f2h_scaled(x0[e], r);
+                    h[4 + e] = f2h_scaled(x1[e], r);
+                }
+            }
+            if (A.keep && col_live) keep_x8(A, kk, col, h);
+            float sum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum += half_bits_to_float(h[e]);
+            u4_t v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                v[q] = col_live ? h[slot_col<FMT>(2 * q)] | (h[slot_col<FMT>(2 * q + 1)] << 16) : 0u;
+            A.xp[(size_t)b * 64 + lane] = v;
+            if constexpr (FMT == VQ_FMT_Q4_MIN) {
+                float t = col_live ? sum : 0.f;
+                t += __shfl_xor(t, 16, 64);
+                t += __shfl_xor(t, 32, 64);
+                const _Float16 hi = (_Float16)t;
+                const _Float16 lo = (_Float16)(t - (float)hi);
+                const uint32_t e = __builtin_bit_cast(uint16_t, gq == 0 ? hi : (gq == 1 ? lo : (_Float16)0.0f));
+                am[tt >> 1] |= e << (16 * (tt & 1));
+            }
+        }
+        if constexpr (FMT == VQ_FMT_Q4_MIN) A.xpa[(size_t)gi * 64 + lane] = am;
+    }
+}
+
+// Waits (thread 0 polls, the workgroup waits behind it) until *flag reaches target; after
+// about a second the error word is raised and the workgroup proceeds, so a launch always
+// ends.
+__device__ void wait_flag(const unsigned* flag, unsigned target, int* err) {
+    if (threadIdx.x == 0) {
+        unsigned spins = 0;
+        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins >= (1u << 22)) {
+                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+template <int FMT, bool MULTI, bool PREP = false>
 __global__ __launch_bounds__(256) void k_stage_mfma(const StageArgs A, const StageGeom g) {
     __shared__ StageSmem<16> sm;
+    if constexpr (PREP) {
+        if ((int)blockIdx.x < A.n_prep) {
+            // convert the stage's input, publish it (written back past this XCD's L2
+            // before the count), count this workgroup
+            stage_rms(A, sm.rs, &sm.red[0][0][0]);
+            prep_x_mfma<FMT>(A, sm.rs);
+            __threadfence();
+            __syncthreads();
+            if (threadIdx.x == 0) __hip_atomic_fetch_add(A.xflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        const int item = xcd_item((int)blockIdx.x - A.n_prep, (int)gridDim.x - A.n_prep);
+        const int tile = item / g.nparts, part = item - tile * g.nparts;
+        WTileM cur;
+        prefetch_mfma<FMT>(A, tile, part * g.cpw, cur);
+        wait_flag(A.xflag, (unsigned)A.n_prep, A.err);
+        stage_item_mfma<FMT, MULTI, true>(A, g, tile, part, sm, cur, -1, 0);
+        return;
+    }
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int tile = item / g.nparts, part = item - tile * g.nparts;
     WTileM cur;
@@ -956,8 +1068,8 @@ __device__ void rows_stage_x(const StageArgs& A, const StageGeom& g, bool keeper
                 const float r = sm.rs[k];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    h[e] = f2h_bits(ra[i][e] * r);
-                    h[4 + e] = f2h_bits(rb[i][e] * r);
+                    h[e] = f2h_scaled(ra[i][e], r);
+                    h[4 + e] = f2h_scaled(rb[i][e], r);
                 }
             }
             if (keeper) {
@@ -1282,7 +1394,9 @@ void launch_valu_k(const StageArgs& A, int tg, const StageGeom& g, hipStream_t s
 
 template <int FMT>
 void launch_mfma_f(const StageArgs& A, const dim3& grid, const StageGeom& g, hipStream_t st) {
-    if (g.cpw > 1) k_stage_mfma<FMT, true><<<grid, 256, 0, st>>>(A, g);
+    if (A.n_prep > 0 && g.cpw > 1) k_stage_mfma<FMT, true, true><<<dim3(grid.x + A.n_prep), 256, 0, st>>>(A, g);
+    else if (A.n_prep > 0) k_stage_mfma<FMT, false, true><<<dim3(grid.x + A.n_prep), 256, 0, st>>>(A, g);
+    else if (g.cpw > 1) k_stage_mfma<FMT, true><<<grid, 256, 0, st>>>(A, g);
     else k_stage_mfma<FMT, false><<<grid, 256, 0, st>>>(A, g);
 }
 

@@ -373,8 +373,8 @@ __device__ void stage_input(const StreamStage& A, int nbmax, bool keeper, u4_t L
                 uint32_t h[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    h[e] = f2h_bits(lo[k][i][e] * rs[k]);
-                    h[4 + e] = f2h_bits(hi[k][i][e] * rs[k]);
+                    h[e] = f2h_scaled(lo[k][i][e], rs[k]);
+                    h[4 + e] = f2h_scaled(hi[k][i][e], rs[k]);
                 }
                 if (keeper && A.keep) {
                     u4_t v;

@@ -25,6 +25,14 @@ __device__ __forceinline__ uint32_t f2h_bits(float v) {
     return __builtin_bit_cast(uint16_t, (_Float16)v);   // round to nearest even
 }
 
+// fp16(v * r) with the product rounded to fp32 first.  The explicit product keeps the
+// compiler from fusing the multiply and the narrowing into one mixed-precision FMA in
+// some kernels and not in others (a single rounding from the exact product can differ
+// from the two-step one by an fp16 ulp), so every kernel converts stage inputs alike.
+__device__ __forceinline__ uint32_t f2h_scaled(float v, float r) {
+    return f2h_bits(__fmul_rn(v, r));
+}
+
 // E8M0 (OCP MX v1.0): 2^(E-127); E = 0 is 2^-127 (an fp32 subnormal), E = 255 NaN.
 __device__ __forceinline__ float e8m0_to_float(uint32_t e) {
     if (e == 0u) return __uint_as_float(0x00400000u);

@@ -55,6 +55,9 @@ struct StageGeom {
     int nstat;     // sums-of-squares entries the stage writes (row-strip: items; tile: tiles)
 };
 
+// Workgroups that convert a stage's input for the MFMA kernel (staged launches).
+constexpr int N_PREP = 16;
+
 // Row-strip kernel limits: K <= ROWS_MAX_K, at most ROWS_NLD 16-byte weight loads per
 // lane per window (two items' worth are in registers at once), ROWS_X_BYTES of LDS for a
 // window's fp16 activations.
@@ -82,6 +85,8 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Glue modes: how a stage builds its input from the previous stage.
 enum GlueMode { GLUE_NONE = 0, GLUE_RHO = 1 };
 
+typedef uint32_t u4_t_ __attribute__((ext_vector_type(4)));
+
 // Everything one stage launch reads and writes.
 struct StageArgs {
     Mat W;
@@ -108,6 +113,15 @@ struct StageArgs {
     float* sbuf;               // paired: silu(gate) * up [K][rows/2]
     int coh;                   // 1: y / stats_out / sbuf are read by other workgroups of the
                                // same launch: stored through to memory (device scope)
+    // MFMA kernel, one-stage input conversion: with n_prep > 0 the first n_prep workgroups
+    // of the launch (a multiple of 8) convert the whole input into xp (A operands, [block]
+    // [lane] 16 bytes) and xpa (block-sum operands, [group][lane] 16 bytes), then count
+    // themselves on *xflag; the other workgroups wait for that count before reading them.
+    u4_t_* xp;
+    u4_t_* xpa;
+    unsigned* xflag;
+    int* err;                  // raised when the wait for the conversion times out
+    int n_prep;
     unsigned* done;            // NULL, or DONE_REPL completion counters DONE_STRIDE words
                                // apart, one per XCD group of workgroups; their sum counts
                                // the tiles (tile kernel) or items (row-strip kernel) whose
@@ -152,6 +166,10 @@ struct PassPlan {
     unsigned* done;                // DONE_WORDS per stage, 0 at pass start (persistent only)
     int* err;                      // set when a wait for a stage times out
     int coh;
+    u4_t_* xp;                     // staged MFMA input conversion buffers of stage 0 (or
+    u4_t_* xpa;                    // NULL); stage s's are xp_stride slots further on
+    size_t xp_stride;
+    unsigned* xflag;               // DONE_WORDS per stage, 0 at pass start
 };
 
 __host__ __device__ inline int stage_tiles_of(int rows, int paired, int half) {
@@ -223,6 +241,10 @@ __host__ __device__ inline void build_stage(const PassPlan& P, int stage, StageA
     }
     A.part = P.part;
     A.counters = P.counters;
+    A.xp = P.xp ? P.xp + (size_t)stage * P.xp_stride : nullptr;
+    A.xpa = P.xpa ? P.xpa + (size_t)stage * P.xp_stride : nullptr;
+    A.xflag = P.xflag ? P.xflag + (size_t)stage * DONE_WORDS : nullptr;
+    A.err = P.err;
 }
 
 // Geometry with a given run length (cheap: the kernels call it).
