@@ -436,9 +436,11 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
     P.counters = sync;
     P.err = (int*)(sync + d.err_word);
     P.done = (persistent || streamed) ? sync + d.done_word : nullptr;
-    if (mfma && !persistent && !streamed) {
-        // staged MFMA launches convert each stage's input once (the completion counters
-        // are unused in staged launches and serve as the conversion counters)
+    if (!persistent && !streamed) {
+        // staged launches convert a stage's input once (MFMA: every stage; VALU at K >= 4:
+        // gate|up, down and lm_head, whose many workgroups would each convert it again); the
+        // completion counters are unused in staged launches and serve as the conversion
+        // counters
         P.xp = (u4_t_*)(base + d.xp_off);
         P.xpa = (u4_t_*)(base + d.xp_off + d.xpa_rel);
         P.xp_stride = d.xp_stride / 16;
@@ -497,7 +499,10 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
                     if (e != hipSuccess) return hip_fail(e, "event record");
                 }
                 const StageGeom& g = P.geo[stage == 4 * s.L ? 4 : stage & 3];
-                if (P.xflag && !g.rk) A.n_prep = N_PREP;
+                // measured: at K = 1 the conversion's latency (input scales, conversion,
+                // write-back, count) costs more than the per-workgroup conversion it saves
+                if (P.xflag && !g.rk && (mfma || (K >= 4 && (stage == 4 * s.L || (stage & 3) >= 2))))
+                    A.n_prep = N_PREP;
                 if (runs && nl < n_events / 2) runs[nl] = g.rk ? -g.R : g.cpw;
                 e = launch_stage(A, g, mfma, st);
                 if (e != hipSuccess) return hip_fail(e, "stage launch");

@@ -307,6 +307,23 @@ __device__ void stage_epilogue(const StageArgs& A, int tile, int part, int npart
     }
 }
 
+// Waits (thread 0 polls, the workgroup waits behind it) until *flag reaches target; after
+// about a second the error word is raised and the workgroup proceeds, so a launch always
+// ends.
+__device__ void wait_flag(const unsigned* flag, unsigned target, int* err) {
+    if (threadIdx.x == 0) {
+        unsigned spins = 0;
+        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins >= (1u << 22)) {
+                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
 // ------------------------------------------------------------------ VALU kernel
 
 // One wave's share of a 64-row tile: 8 rows x one block per lane.
@@ -434,7 +451,7 @@ __device__ __forceinline__ void x_issue(const StageArgs& A, int nb, int ch, XPre
 // converted, then the next weights are issued (the next chunk, else the first chunk of
 // item (ntile, npart) unless ntile < 0), then the chunk is computed; on return `cur`
 // holds those next weights.
-template <int FMT, int K, bool MULTI>
+template <int FMT, int K, bool MULTI, bool PREP = false>
 __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile, int part, StageSmem<K>& sm,
                                 uint2 (&xs)[4][K][8][8], WTileV& cur, int ntile, int npart,
                                 const XPre<K>* pre = nullptr) {
@@ -457,6 +474,23 @@ __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile
         const bool live = b < nb;
         const int bcl = live ? b : nb - 1;
         const int col = 32 * bcl + 4 * s;
+        float bs[K];
+        uint32_t xv[K][16];
+        if constexpr (PREP) {
+            // the stage's input converted once (prep_x_valu): block c's 32 values per
+            // column in the widened pair order, and its sum
+            const float* bsum = reinterpret_cast<const float*>(A.xpa);
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u4_t v = live ? ld_global<u4_t>(A.xp + ((size_t)k * nb + b) * 4 + q) : u4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) xv[k][4 * q + e] = v[e];
+                }
+                bs[k] = live ? ld_global<float>(bsum + (size_t)k * nb + b) : 0.f;
+            }
+        } else {
         // this chunk's activations: lane (s, c) takes elements 4s..4s+3 of block c
         XPre<K> X;
         if (pre && ch == c0) X = *pre;
@@ -466,7 +500,6 @@ __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile
         // fp16 inputs; the wave shares them through LDS, so that each lane then holds its
         // block's 32 activations per column in the widened pair order
         const bool keeper = A.keep && tile == 0 && live;
-        float bs[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             uint32_t h[4];
@@ -487,7 +520,6 @@ __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile
             bs[k] = live ? sum : 0.f;
         }
         wave_lds_sync();
-        uint32_t xv[K][16];
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             uint32_t h[32];
@@ -506,6 +538,7 @@ __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile
                 }
         }
         wave_lds_sync();
+        }
         if constexpr (PREFETCH_NEXT) {
             // the next weights load while this chunk is computed (issued only now: a wait
             // for the activations above would otherwise also wait for them)
@@ -531,10 +564,80 @@ __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile
     stage_epilogue<K>(A, tile, part, g.nparts, red, &sm.flag);
 }
 
-template <int FMT, int K, bool MULTI>
+// The input conversion of stage_item_valu for the whole stage, done once: wave v of the
+// n_prep converting workgroups takes (column, group of 8 blocks) units v, v + 4 n_prep,
+// ...; lane (s, c) converts elements 4s..4s+3 of block c with the same arithmetic and
+// order as the inline conversion (the block sum by the same butterfly), so both give the
+// same bits.  Writes xp ([k][block] 64 bytes: the block's 32 values in the widened pair
+// order), the block sums ([k][block] floats at xpa) and the fp16 copy of the input.
+// Every 16-byte slot is written whole by one lane.
+template <int FMT>
+__device__ void prep_x_valu(const StageArgs& A, const float* rs) {
+    const int K = A.K;
+    const int nb = A.W.cols >> 5;
+    const int ngrp = (nb + 7) >> 3;
+    const int lane = threadIdx.x & 63;
+    const int s = lane >> 3, c = lane & 7;
+    const int nwv = A.n_prep * 4;
+    float* bsum = reinterpret_cast<float*>(A.xpa);
+    for (int u = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6); u < K * ngrp; u += nwv) {
+        const int k = u / ngrp, gi = u - k * ngrp;
+        const int b = 8 * gi + c;
+        const bool live = b < nb;
+        const int col = 32 * (live ? b : nb - 1) + 4 * s;
+        uint32_t h[4];
+        if (A.glue == GLUE_NONE) {
+            const uint2 v = *reinterpret_cast<const uint2*>(A.x16 + (size_t)k * A.W.cols + col);
+            h[0] = v.x & 0xffffu; h[1] = v.x >> 16; h[2] = v.y & 0xffffu; h[3] = v.y >> 16;
+        } else {
+            const f4_t v = *reinterpret_cast<const f4_t*>(A.src + (size_t)k * A.ld + col);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = f2h_scaled(v[e], rs[k]);
+        }
+        if (A.keep && live)
+            *reinterpret_cast<uint2*>(A.keep + (size_t)k * A.W.cols + col) =
+                make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        float sum = (half_bits_to_float(h[0]) + half_bits_to_float(h[1])) +
+                    (half_bits_to_float(h[2]) + half_bits_to_float(h[3]));
+        sum += __shfl_xor(sum, 8, 64);
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        // lane s ^ 1 holds the other half of the 8-value group s >> 1
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (uint32_t)__shfl_xor((int)h[e], 8, 64);
+        if ((s & 1) == 0 && live) {
+            const uint32_t v8[8] = {h[0], h[1], h[2], h[3], o[0], o[1], o[2], o[3]};
+            u4_t out;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) out[t] = v8[slot_col<FMT>(2 * t)] | (v8[slot_col<FMT>(2 * t + 1)] << 16);
+            A.xp[((size_t)k * nb + b) * 4 + (s >> 1)] = out;
+        }
+        if (s == 0 && live) bsum[(size_t)k * nb + b] = sum;
+    }
+}
+
+template <int FMT, int K, bool MULTI, bool PREP = false>
 __global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, const StageGeom g) {
     __shared__ StageSmem<K> sm;
     __shared__ uint2 xs[4][K][8][8];          // [wave][column][block][quarter of 4 fp16]
+    if constexpr (PREP) {
+        if ((int)blockIdx.x < A.n_prep) {
+            stage_rms(A, sm.rs, &sm.red[0][0][0]);
+            prep_x_valu<FMT>(A, sm.rs);
+            __threadfence();
+            __syncthreads();
+            if (threadIdx.x == 0) __hip_atomic_fetch_add(A.xflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        const int item = xcd_item((int)blockIdx.x - A.n_prep, (int)gridDim.x - A.n_prep);
+        const int tile = item / g.nparts, part = item - tile * g.nparts;
+        WTileV cur;
+        prefetch_valu<FMT>(A, tile, part, cur);
+        wait_flag(A.xflag, (unsigned)A.n_prep, A.err);
+        stage_item_valu<FMT, K, false, true>(A, g, tile, part, sm, xs, cur, -1, 0);
+        return;
+    }
     const int item = xcd_item(blockIdx.x, gridDim.x);
     const int tile = item / g.nparts, part = item - tile * g.nparts;
     WTileV cur;
@@ -899,23 +1002,6 @@ __device__ void prep_x_mfma(const StageArgs& A, const float* rs) {
         }
         if constexpr (FMT == VQ_FMT_Q4_MIN) A.xpa[(size_t)gi * 64 + lane] = am;
     }
-}
-
-// Waits (thread 0 polls, the workgroup waits behind it) until *flag reaches target; after
-// about a second the error word is raised and the workgroup proceeds, so a launch always
-// ends.
-__device__ void wait_flag(const unsigned* flag, unsigned target, int* err) {
-    if (threadIdx.x == 0) {
-        unsigned spins = 0;
-        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins >= (1u << 22)) {
-                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-        }
-    }
-    __syncthreads();
 }
 
 template <int FMT, bool MULTI, bool PREP = false>
@@ -1389,7 +1475,8 @@ __global__ void k_zero_u32(unsigned* p, int n) {
 template <int FMT, int K>
 void launch_valu_k(const StageArgs& A, int tg, const StageGeom& g, hipStream_t st) {
     // staged VALU launches take one chunk per item (the plan never gives them runs)
-    k_stage_valu<FMT, K, false><<<dim3(tg * g.nparts), 256, 0, st>>>(A, g);
+    if (A.n_prep > 0) k_stage_valu<FMT, K, false, true><<<dim3(tg * g.nparts + A.n_prep), 256, 0, st>>>(A, g);
+    else k_stage_valu<FMT, K, false><<<dim3(tg * g.nparts), 256, 0, st>>>(A, g);
 }
 
 template <int FMT>
