@@ -377,53 +377,115 @@ __device__ __forceinline__ bool cross(uint64_t C, uint32_t u24, uint64_t S) {
 }
 
 // Smallest j with prefix_j(w) * 2^24 > u24 * sum(w) (vocabulary order); -1 if sum is 0.
+// The row is read in tiles of NT * CU entries, thread t taking entries t * CU .. t * CU +
+// CU - 1 of a tile (so a wave reads contiguous memory) and TU tiles' loads in flight at
+// once; each wave's sum per tile goes to LDS.  One thread then walks the (tile, wave)
+// sums in vocabulary order to the one holding the crossing, and that wave alone re-reads
+// its 64 * CU entries of that tile: a wave prefix sum finds the crossing thread, which
+// walks its CU entries.  Sums are in fixed point, so any order gives the same totals.
+// Rows longer than MAX_TILES tiles use the slice walk of block_cat_slices.
+constexpr int CAT_CU = 8, CAT_TU = 4, CAT_MAX_TILES = 64;
+
 template <class WF>
-__device__ int block_cat(WF wf, int V, uint32_t u24, uint64_t* sh, int* sres) {
-    // a thread's slice is read in groups of CU entries, all loads of a group in flight
-    constexpr int CU = 8;
+__device__ int block_cat_slices(WF wf, int V, uint32_t u24, uint64_t* sh, int* sres) {
     const int chunk = (V + NT - 1) / NT;
     const int j0 = threadIdx.x * chunk, j1 = min(V, j0 + chunk);
     uint64_t local = 0;
-    int j = j0;
-    for (; j + CU <= j1; j += CU) {
-        uint64_t w[CU];
-#pragma unroll
-        for (int u = 0; u < CU; ++u) w[u] = wf(j + u);
-#pragma unroll
-        for (int u = 0; u < CU; ++u) local += w[u];
-    }
-    for (; j < j1; ++j) local += wf(j);
+    for (int j = j0; j < j1; ++j) local += wf(j);
     uint64_t S;
     const uint64_t before = block_excl_scan_u64(local, sh, &S);
     if (threadIdx.x == 0) *sres = -1;
     __syncthreads();
     if (S > 0 && local > 0 && !cross(before, u24, S) && cross(before + local, u24, S)) {
-        // the running sum is non-decreasing: a group whose end does not cross holds no
-        // crossing, so only the crossing group is walked entry by entry
         uint64_t C = before;
-        int found = -1;
-        int jj = j0;
-        for (; jj + CU <= j1 && found < 0; jj += CU) {
-            uint64_t w[CU];
+        for (int j = j0; j < j1; ++j) {
+            C += wf(j);
+            if (cross(C, u24, S)) { *sres = j; break; }
+        }
+    }
+    __syncthreads();
+    const int r = *sres;
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
-            for (int u = 0; u < CU; ++u) w[u] = wf(jj + u);
-            uint64_t s8 = 0;
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+template <class WF>
+__device__ int block_cat(WF wf, int V, uint32_t u24, uint64_t* sh, int* sres) {
+    constexpr int CU = CAT_CU, TILE = NT * CU, NW = NT / 64;
+    const int ntile = (V + TILE - 1) / TILE;
+    if (ntile > CAT_MAX_TILES) return block_cat_slices(wf, V, u24, sh, sres);
+    __shared__ uint64_t tw[CAT_MAX_TILES][NW];
+    __shared__ int s_tile, s_wave;
+    __shared__ uint64_t s_before, s_total;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    for (int tb = 0; tb < ntile; tb += CAT_TU) {
+        uint64_t w[CAT_TU][CU];
 #pragma unroll
-            for (int u = 0; u < CU; ++u) s8 += w[u];
-            if (cross(C + s8, u24, S)) {
-                for (int u = 0; u < CU; ++u) {
-                    C += w[u];
-                    if (cross(C, u24, S)) { found = jj + u; break; }
+        for (int u = 0; u < CAT_TU; ++u)
+#pragma unroll
+            for (int e = 0; e < CU; ++e) {
+                const int j = (tb + u) * TILE + t * CU + e;
+                w[u][e] = j < V ? wf(j) : 0ull;
+            }
+#pragma unroll
+        for (int u = 0; u < CAT_TU; ++u) {
+            uint64_t l = 0;
+#pragma unroll
+            for (int e = 0; e < CU; ++e) l += w[u][e];
+            l = wave_sum_u64(l);
+            if (lane == 0 && tb + u < ntile) tw[tb + u][wave] = l;
+        }
+    }
+    __syncthreads();
+    if (t == 0) {
+        uint64_t S = 0;
+        for (int i = 0; i < ntile; ++i)
+            for (int v = 0; v < NW; ++v) S += tw[i][v];
+        int ft = -1, fw = 0;
+        uint64_t C = 0;
+        if (S > 0)
+            for (int i = 0; i < ntile && ft < 0; ++i)
+                for (int v = 0; v < NW; ++v) {
+                    if (cross(C + tw[i][v], u24, S)) { ft = i; fw = v; break; }
+                    C += tw[i][v];
                 }
-            } else {
-                C += s8;
+        s_tile = ft;
+        s_wave = fw;
+        s_before = C;
+        s_total = S;
+        *sres = -1;
+    }
+    __syncthreads();
+    if (s_tile >= 0 && wave == s_wave) {
+        const uint64_t S = s_total;
+        const int base = s_tile * TILE + t * CU;
+        uint64_t w[CU], l = 0;
+#pragma unroll
+        for (int e = 0; e < CU; ++e) {
+            w[e] = base + e < V ? wf(base + e) : 0ull;
+            l += w[e];
+        }
+        // inclusive prefix over the wave's lanes, then the lane whose range crosses
+        uint64_t x = l;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint64_t y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        const uint64_t before = s_before + x - l;
+        if (l > 0 && !cross(before, u24, S) && cross(before + l, u24, S)) {
+            uint64_t C = before;
+            for (int e = 0; e < CU; ++e) {
+                C += w[e];
+                if (cross(C, u24, S)) { *sres = base + e; break; }
             }
         }
-        for (; jj < j1 && found < 0; ++jj) {
-            C += wf(jj);
-            if (cross(C, u24, S)) found = jj;
-        }
-        *sres = found;
     }
     __syncthreads();
     const int r = *sres;
