@@ -252,14 +252,27 @@ __device__ void stage_epilogue(const StageArgs& A, int tile, int part, int npart
             last = *s_flag != 0;
         }
         if (!last) return;
+        // the parts are summed in part order; their loads go out in groups of 8, so a
+        // wide stage (17 parts at 17408 columns) waits for 3 round trips, not 17
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
             const int k = wave + 4 * j;
             float v = 0.f;
-            if (k < K && ok)
-                for (int c = 0; c < nparts; ++c)
-                    v += __hip_atomic_load(&A.part[((size_t)c * K + k) * rows + orow], __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+            if (k < K && ok) {
+                const float* pp = A.part + (size_t)k * rows + orow;
+                const size_t pstride = (size_t)K * rows;
+                for (int c0 = 0; c0 < nparts; c0 += 8) {
+                    float t[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        t[u] = c0 + u < nparts ? __hip_atomic_load(pp + (size_t)(c0 + u) * pstride, __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_AGENT)
+                                               : 0.f;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (c0 + u < nparts) v += t[u];
+                }
+            }
             fv[j] = v;
         }
         if (threadIdx.x == 0) __hip_atomic_store(&A.counters[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
