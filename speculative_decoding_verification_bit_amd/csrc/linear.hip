@@ -142,11 +142,18 @@ __device__ void stage_rms(const StageArgs& A, float* rs, float* sh) {
     float acc[VQ_MAX_K];
 #pragma unroll
     for (int k = 0; k < VQ_MAX_K; ++k) acc[k] = 0.f;
-    for (int f = threadIdx.x; f < n; f += 256) {
-        const float v = A.stats_in[f];
-        const int kf = f % K;
+    // entries in the same order, loaded 8 at a time (one round trip per 8, not per entry)
+    for (int f0 = threadIdx.x; f0 < n; f0 += 8 * 256) {
+        float v[8];
 #pragma unroll
-        for (int k = 0; k < VQ_MAX_K; ++k) acc[k] += k == kf ? v : 0.f;
+        for (int u = 0; u < 8; ++u) v[u] = f0 + 256 * u < n ? A.stats_in[f0 + 256 * u] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int f = f0 + 256 * u;
+            const int kf = f % K;
+#pragma unroll
+            for (int k = 0; k < VQ_MAX_K; ++k) acc[k] += (f < n && k == kf) ? v[u] : 0.f;
+        }
     }
     rms_reduce(A, acc, rs, sh);
 }
