@@ -276,8 +276,8 @@ def main():
     avg_launch_ms = ms_dom / n_dom
     bytes_per_launch = b_dom / n_dom
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
-    kname = {"single": "k_stage_valu<1, 1, false> (Q4_MIN, K 1, one chunk per item)",
-             "multi": "k_stage_valu<1, 1, true> (Q4_MIN, K 1, chunk runs per item)",
+    kname = {"single": "k_stage_valu<1, 1, false, false> (Q4_MIN, K 1, one chunk per item)",
+             "multi": "k_stage_valu<1, 1, true, false> (Q4_MIN, K 1, chunk runs per item)",
              "rows": "k_rows_s<1, 1, NSG> (Q4_MIN, K 1, row strips)",
              "stream": "k_stream<1, 1> (Q4_MIN, K 1, stream-ahead)",
              "persistent": "k_pass<1, 1, false> (Q4_MIN, K 1, persistent)"}[dom]
