@@ -158,7 +158,117 @@ struct StatArgs {
     int full;              // 0: argmax and non-finite only
     float T, top_p, min_p;
     RowStat* out;
+    // With few rows, the first two passes run split over SPLIT_S workgroups per row
+    // (k_row_part1, k_row_part2) and k_row_stats starts from their partials; NULL: not split.
+    const struct Part1* p1;
+    const struct Part2* p2;
 };
+
+// Split row statistics: a row is cut into SPLIT_S slices, one workgroup each.  Their
+// partials combine exactly (the maximum with its first index, the or of non-finite
+// flags, integer fixed-point sums), so the statistics are the same bits as one
+// workgroup's passes.
+constexpr int SPLIT_S = 64;
+constexpr int SPLIT_MAX_ROWS = 64;
+constexpr int SPLIT_MIN_V = 16384;
+struct Part1 {
+    float m;
+    int i, nf, pad;
+};
+struct Part2 {
+    uint64_t z, zm, nm, pad;
+};
+
+__device__ __forceinline__ void slice_of(int V, int sl, int& j0, int& j1) {
+    const int chunk = (V + SPLIT_S - 1) / SPLIT_S;
+    j0 = min(V, sl * chunk);
+    j1 = min(V, j0 + chunk);
+}
+
+// Largest value with its first index over the workgroup (the pass-1 tree order).
+__device__ void block_max_first(float& best, int& bi, float* shf, int* shi) {
+    const int t = threadIdx.x;
+    shf[t] = best;
+    shi[t] = bi;
+    __syncthreads();
+    for (int s = NT / 2; s > 0; s >>= 1) {
+        if (t < s) {
+            const float ob = shf[t + s];
+            const int oi = shi[t + s];
+            if (ob > shf[t] || (ob == shf[t] && oi < shi[t])) { shf[t] = ob; shi[t] = oi; }
+        }
+        __syncthreads();
+    }
+    best = shf[0];
+    bi = shi[0];
+    __syncthreads();
+}
+
+// Pass 1 of one slice: maximum, first argmax, non-finite entries.
+__global__ __launch_bounds__(NT) void k_row_part1(const float* logits, int V, Part1* out) {
+    __shared__ float shf[NT];
+    __shared__ int shi[NT];
+    const int row = blockIdx.x / SPLIT_S, sl = blockIdx.x % SPLIT_S;
+    const float* l = logits + (size_t)row * V;
+    int j0, j1;
+    slice_of(V, sl, j0, j1);
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    int nf = 0;
+    for (int j = j0 + (int)threadIdx.x; j < j1; j += NT) {
+        const float v = l[j];
+        if (!isfinite(v)) nf = 1;
+        else if (v > best) { best = v; bi = j; }
+    }
+    block_max_first(best, bi, shf, shi);
+    const int anynf = __syncthreads_or(nf);
+    if (threadIdx.x == 0) out[blockIdx.x] = Part1{best, bi, anynf ? 1 : 0, 0};
+}
+
+// The row's maximum, first argmax and non-finite flag from its slices (slice order).
+__device__ __forceinline__ void combine_part1(const Part1* p, float& lmax, int& amax, int& nf) {
+    lmax = -INFINITY;
+    amax = 0x7fffffff;
+    nf = 0;
+    for (int i = 0; i < SPLIT_S; ++i) {
+        const Part1 q = p[i];
+        nf |= q.nf;
+        if (q.m > lmax || (q.m == lmax && q.i < amax)) { lmax = q.m; amax = q.i; }
+    }
+}
+
+
+// Pass 2 of one slice: the mass and the min-p set's mass and size.
+__global__ __launch_bounds__(NT) void k_row_part2(StatArgs A, Part2* out) {
+    __shared__ uint64_t sh[NT + 1];
+    __shared__ float s_lmax;
+    __shared__ int s_skip;
+    const int row = blockIdx.x / SPLIT_S, sl = blockIdx.x % SPLIT_S;
+    if (threadIdx.x == 0) {
+        float lmax;
+        int amax, nf;
+        combine_part1(A.p1 + (size_t)row * SPLIT_S, lmax, amax, nf);
+        s_lmax = lmax;
+        s_skip = nf || !A.full;
+    }
+    __syncthreads();
+    if (s_skip) return;
+    const float lmax = s_lmax, T = A.T, min_p = A.min_p;
+    const float* l = A.logits + (size_t)row * A.V;
+    int j0, j1;
+    slice_of(A.V, sl, j0, j1);
+    uint64_t z = 0, zm = 0, nm = 0;
+    for (int j = j0 + (int)threadIdx.x; j < j1; j += NT) {
+        const float e = e_of(l[j], lmax, T);
+        const uint64_t f = to_fx(e);
+        z += f;
+        if (e >= min_p) { zm += f; ++nm; }
+    }
+    z = block_sum_u64(z, sh);
+    zm = block_sum_u64(zm, sh);
+    nm = block_sum_u64(nm, sh);
+    if (threadIdx.x == 0) out[blockIdx.x] = Part2{z, zm, nm, 0};
+}
 
 __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
     __shared__ uint64_t hist[4096];
@@ -172,28 +282,21 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
     const float* l = A.logits + (size_t)row * V;
     const int t = threadIdx.x;
 
-    // pass 1: maximum, first argmax, non-finite entries
+    // pass 1: maximum, first argmax, non-finite entries (or their split partials)
     float best = -INFINITY;
     int bi = 0x7fffffff;
     int nf = 0;
-    row_for(l, V, [&](float v, int j) {
-        if (!isfinite(v)) nf = 1;
-        else if (v > best) { best = v; bi = j; }
-    });
-    shf[t] = best;
-    shi[t] = bi;
-    __syncthreads();
-    for (int s = NT / 2; s > 0; s >>= 1) {
-        if (t < s) {
-            const float ob = shf[t + s];
-            const int oi = shi[t + s];
-            if (ob > shf[t] || (ob == shf[t] && oi < shi[t])) { shf[t] = ob; shi[t] = oi; }
-        }
-        __syncthreads();
+    if (A.p1) {
+        if (t == 0) combine_part1(A.p1 + (size_t)row * SPLIT_S, best, bi, nf);
+    } else {
+        row_for(l, V, [&](float v, int j) {
+            if (!isfinite(v)) nf = 1;
+            else if (v > best) { best = v; bi = j; }
+        });
     }
-    const float lmax = shf[0];
-    const int amax = shi[0];
-    __syncthreads();
+    block_max_first(best, bi, shf, shi);
+    const float lmax = best;
+    const int amax = bi;
     const int anynf = __syncthreads_or(nf);
     RowStat st;
     st.argmax = amax == 0x7fffffff ? 0 : amax;
@@ -215,12 +318,21 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
     // top-p prefix, and the kept set is the shorter of the two.
     uint64_t z = 0, zm = 0, nm = 0;
     const float min_p = A.min_p;
-    row_for(l, V, [&](float v, int) {
-        const float e = e_of(v, lmax, T);
-        const uint64_t f = to_fx(e);
-        z += f;
-        if (e >= min_p) { zm += f; ++nm; }
-    });
+    if (A.p2) {
+        if (t < SPLIT_S) {
+            const Part2 q = A.p2[(size_t)row * SPLIT_S + t];
+            z = q.z;
+            zm = q.zm;
+            nm = q.nm;
+        }
+    } else {
+        row_for(l, V, [&](float v, int) {
+            const float e = e_of(v, lmax, T);
+            const uint64_t f = to_fx(e);
+            z += f;
+            if (e >= min_p) { zm += f; ++nm; }
+        });
+    }
     st.z_fx = block_sum_u64(z, sh);
 
     // pass 3: top-p cut
@@ -659,27 +771,72 @@ __global__ __launch_bounds__(NT) void k_accept(AcceptArgs A) {
 
 }  // namespace
 
-size_t accept_ws_bytes(const vq_accept_desc* d) {
-    const size_t rows = (size_t)d->W * d->K + (size_t)d->W * (d->K > 1 ? d->K - 1 : 0);
-    return align_up(rows * sizeof(RowStat), 256);
+// Workspace: row statistics of the target rows, then of the drafter rows, then (rows
+// split over workgroups) the slices' partials of each.
+struct AcceptLayout {
+    size_t st_d, p1_t, p2_t, p1_d, p2_d, total;
+    bool split_t, split_d;
+};
+
+bool split_rows(int nrows, int V) { return nrows > 0 && nrows <= SPLIT_MAX_ROWS && V >= SPLIT_MIN_V; }
+
+AcceptLayout accept_layout(const vq_accept_desc* d) {
+    AcceptLayout L{};
+    const size_t rt = (size_t)d->W * d->K, rd = (size_t)d->W * (d->K > 1 ? d->K - 1 : 0);
+    size_t p = align_up(rt * sizeof(RowStat), 256);
+    L.st_d = p;
+    p += align_up(rd * sizeof(RowStat), 256);
+    L.split_t = split_rows((int)rt, d->V);
+    L.split_d = split_rows((int)rd, d->V);
+    if (L.split_t) {
+        L.p1_t = p;
+        p += align_up(rt * SPLIT_S * sizeof(Part1), 256);
+        L.p2_t = p;
+        p += align_up(rt * SPLIT_S * sizeof(Part2), 256);
+    }
+    if (L.split_d) {
+        L.p1_d = p;
+        p += align_up(rd * SPLIT_S * sizeof(Part1), 256);
+        L.p2_d = p;
+        p += align_up(rd * SPLIT_S * sizeof(Part2), 256);
+    }
+    L.total = p;
+    return L;
+}
+
+size_t accept_ws_bytes(const vq_accept_desc* d) { return accept_layout(d).total; }
+
+// Row statistics of one set of rows: split over workgroups when the rows are few.
+hipError_t launch_row_stats(StatArgs a, bool split, char* ws, size_t p1_off, size_t p2_off, hipStream_t st) {
+    if (a.nrows == 0) return hipSuccess;
+    if (split) {
+        Part1* p1 = (Part1*)(ws + p1_off);
+        Part2* p2 = (Part2*)(ws + p2_off);
+        k_row_part1<<<dim3(a.nrows * SPLIT_S), NT, 0, st>>>(a.logits, a.V, p1);
+        a.p1 = p1;
+        k_row_part2<<<dim3(a.nrows * SPLIT_S), NT, 0, st>>>(a, p2);
+        a.p2 = a.full ? p2 : nullptr;
+    }
+    k_row_stats<<<dim3(a.nrows), NT, 0, st>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_accept(const vq_accept_desc* d, void* ws, hipStream_t st) {
     if (d->W == 0) return hipSuccess;
-    RowStat* st_t = (RowStat*)ws;
-    RowStat* st_d = st_t + (size_t)d->W * d->K;
+    const AcceptLayout L = accept_layout(d);
+    char* wsb = (char*)ws;
+    RowStat* st_t = (RowStat*)wsb;
+    RowStat* st_d = (RowStat*)(wsb + L.st_d);
     const bool sample = d->mode == VQ_MODE_SAMPLE;
     const bool drafter = sample || d->draft_mode == VQ_DRAFT_Q_ARGMAX || d->draft_mode == VQ_DRAFT_Q_SAMPLE;
     const float T = d->temperature;
-    StatArgs sa{d->target_logits, d->W * d->K, d->V, sample ? 1 : 0, T, d->top_p, d->min_p, st_t};
-    k_row_stats<<<dim3(sa.nrows), NT, 0, st>>>(sa);
-    hipError_t e = hipGetLastError();
+    StatArgs sa{d->target_logits, d->W * d->K, d->V, sample ? 1 : 0, T, d->top_p, d->min_p, st_t, nullptr, nullptr};
+    hipError_t e = launch_row_stats(sa, L.split_t, wsb, L.p1_t, L.p2_t, st);
     if (e != hipSuccess) return e;
     if (drafter && d->K > 1) {
         const int full = (sample || d->draft_mode == VQ_DRAFT_Q_SAMPLE) ? 1 : 0;
-        StatArgs sd{d->draft_logits, d->W * (d->K - 1), d->V, full, T, d->top_p, d->min_p, st_d};
-        k_row_stats<<<dim3(sd.nrows), NT, 0, st>>>(sd);
-        e = hipGetLastError();
+        StatArgs sd{d->draft_logits, d->W * (d->K - 1), d->V, full, T, d->top_p, d->min_p, st_d, nullptr, nullptr};
+        e = launch_row_stats(sd, L.split_d, wsb, L.p1_d, L.p2_d, st);
         if (e != hipSuccess) return e;
     }
     double a24 = ceil((double)d->alpha * 16777216.0);
