@@ -437,7 +437,7 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
     P.err = (int*)(sync + d.err_word);
     P.done = (persistent || streamed) ? sync + d.done_word : nullptr;
     if (!persistent && !streamed) {
-        // staged launches convert a stage's input once (MFMA: every stage; VALU at K >= 4:
+        // staged launches convert a stage's input once (MFMA: every stage; VALU at K >= 2:
         // gate|up, down and lm_head, whose many workgroups would each convert it again); the
         // completion counters are unused in staged launches and serve as the conversion
         // counters
@@ -499,9 +499,10 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
                     if (e != hipSuccess) return hip_fail(e, "event record");
                 }
                 const StageGeom& g = P.geo[stage == 4 * s.L ? 4 : stage & 3];
-                // measured: at K = 1 the conversion's latency (input scales, conversion,
-                // write-back, count) costs more than the per-workgroup conversion it saves
-                if (P.xflag && !g.rk && (mfma || (K >= 4 && (stage == 4 * s.L || (stage & 3) >= 2))))
+                // measured: at K = 1 the conversion's latency on the critical path (input
+                // scales, conversion, count) costs more than the per-workgroup conversion
+                // it saves (27B pass 4.59 -> 5.16 ms); from K = 2 it pays (7.19 -> 6.80)
+                if (P.xflag && !g.rk && (mfma || (K >= PREP_MIN_K_VALU && (stage == 4 * s.L || (stage & 3) >= 2))))
                     A.n_prep = N_PREP;
                 if (runs && nl < n_events / 2) runs[nl] = g.rk ? -g.R : g.cpw;
                 e = launch_stage(A, g, mfma, st);

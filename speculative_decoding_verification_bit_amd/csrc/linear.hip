@@ -584,6 +584,15 @@ __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile
     stage_epilogue<K>(A, tile, part, g.nparts, red, &sm.flag);
 }
 
+// A 16-byte store that other XCDs read within the same launch: two device-scope 8-byte
+// stores, written through past this XCD's L2, so that waiting for their completion
+// (s_waitcnt) is enough before the count that publishes them (no L2 write-back).
+__device__ __forceinline__ void st_through_u4(u4_t* p, const u4_t& v) {
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    __hip_atomic_store(q, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The input conversion of stage_item_valu for the whole stage, done once: wave v of the
 // n_prep converting workgroups takes (column, group of 8 blocks) units v, v + 4 n_prep,
 // ...; lane (s, c) converts elements 4s..4s+3 of block c with the same arithmetic and
@@ -631,9 +640,9 @@ __device__ void prep_x_valu(const StageArgs& A, const float* rs) {
             u4_t out;
 #pragma unroll
             for (int t = 0; t < 4; ++t) out[t] = v8[slot_col<FMT>(2 * t)] | (v8[slot_col<FMT>(2 * t + 1)] << 16);
-            A.xp[((size_t)k * nb + b) * 4 + (s >> 1)] = out;
+            st_through_u4(A.xp + ((size_t)k * nb + b) * 4 + (s >> 1), out);
         }
-        if (s == 0 && live) bsum[(size_t)k * nb + b] = sum;
+        if (s == 0 && live) __hip_atomic_store(bsum + (size_t)k * nb + b, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -645,7 +654,7 @@ __global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, const Sta
         if ((int)blockIdx.x < A.n_prep) {
             stage_rms(A, sm.rs, &sm.red[0][0][0]);
             prep_x_valu<FMT>(A, sm.rs);
-            __threadfence();
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (threadIdx.x == 0) __hip_atomic_fetch_add(A.xflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
@@ -1009,7 +1018,7 @@ __device__ void prep_x_mfma(const StageArgs& A, const float* rs) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 v[q] = col_live ? h[slot_col<FMT>(2 * q)] | (h[slot_col<FMT>(2 * q + 1)] << 16) : 0u;
-            A.xp[(size_t)b * 64 + lane] = v;
+            st_through_u4(A.xp + (size_t)b * 64 + lane, v);
             if constexpr (FMT == VQ_FMT_Q4_MIN) {
                 float t = col_live ? sum : 0.f;
                 t += __shfl_xor(t, 16, 64);
@@ -1020,7 +1029,7 @@ __device__ void prep_x_mfma(const StageArgs& A, const float* rs) {
                 am[tt >> 1] |= e << (16 * (tt & 1));
             }
         }
-        if constexpr (FMT == VQ_FMT_Q4_MIN) A.xpa[(size_t)gi * 64 + lane] = am;
+        if constexpr (FMT == VQ_FMT_Q4_MIN) st_through_u4(A.xpa + (size_t)gi * 64 + lane, am);
     }
 }
 
@@ -1033,7 +1042,7 @@ __global__ __launch_bounds__(256) void k_stage_mfma(const StageArgs A, const Sta
             // before the count), count this workgroup
             stage_rms(A, sm.rs, &sm.red[0][0][0]);
             prep_x_mfma<FMT>(A, sm.rs);
-            __threadfence();
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             if (threadIdx.x == 0) __hip_atomic_fetch_add(A.xflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;

@@ -55,8 +55,10 @@ struct StageGeom {
     int nstat;     // sums-of-squares entries the stage writes (row-strip: items; tile: tiles)
 };
 
-// Workgroups that convert a stage's input for the MFMA kernel (staged launches).
+// Workgroups that convert a stage's input (staged launches): every MFMA stage, and the
+// VALU kernel's gate|up, down and lm_head stages from K = PREP_MIN_K_VALU.
 constexpr int N_PREP = 16;
+constexpr int PREP_MIN_K_VALU = 2;
 
 // Row-strip kernel limits: K <= ROWS_MAX_K, at most ROWS_NLD 16-byte weight loads per
 // lane per window (two items' worth are in registers at once), ROWS_X_BYTES of LDS for a
