@@ -94,6 +94,28 @@ def test_top_p_radix_select_and_min_p(T, top_p, min_p):
     _compare(g, o, False, f"T {T} top-p {top_p} min-p {min_p}", max_near_frac=frac)
 
 
+def test_single_window_k1_sampled_full_vocab():
+    """One window, K = 1, V = 151936 (a sampled plain-decode step: the bonus token only);
+    the row statistics run split over many workgroups.  Eight independent windows."""
+    spec = synth.LogitSpec(seed=11, K=1, vocab=151936, target_sigma=3.0, noise_sigma=1.0)
+    t, _ = synth.logits_batch(spec, 0, 8, threads=8)
+    kw = dict(T=0.6, top_p=0.95, min_p=0.05, seed=3)
+    gs, os_ = {}, {}
+    for w in range(8):
+        g = _gpu(1, t[w:w + 1], np.zeros((1, 0, spec.vocab), np.float32), window_base=w, **kw)
+        o = _oracle(oracle.MODE_SAMPLE, t[w:w + 1], np.zeros((1, 0, spec.vocab), np.float32), window_base=w, **kw)
+        for k in o:
+            if g.get(k) is not None:
+                gs.setdefault(k, []).append(g[k])
+            os_.setdefault(k, []).append(o[k])
+    gs = {k: np.concatenate(v) for k, v in gs.items()}
+    os_ = {k: np.concatenate(v) for k, v in os_.items()}
+    _compare(gs, os_, False, "K=1 single windows, T 0.6 top-p 0.95 min-p 0.05", max_near_frac=0.25)
+    for w in range(8):
+        g = _gpu(0, t[w:w + 1])
+        assert g["tokens"][0, 0] == int(np.argmax(t[w, 0]))
+
+
 def test_top_p_ties_resolved_by_index():
     """Equal logits at the top-p cut: the lower indices are kept first."""
     V, K, W = 64, 2, 400
