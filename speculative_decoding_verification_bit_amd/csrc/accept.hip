@@ -479,7 +479,68 @@ struct AcceptArgs {
     const RowStat* st_t;       // [W*K]
     const RowStat* st_d;       // [W*(K-1)]
     int32_t *n_acc, *tokens, *status;
+    // Split draw (few windows): k_accept stops before the final draw and leaves it in
+    // rec[w]; k_draw_part sums SPLIT_S slices' weights, k_draw_final picks the token.
+    struct DrawRec* rec;
+    struct DrawPart* part;
 };
+
+// A window's final draw: at position stop (K: the bonus token from p; else the residual
+// norm(max(0, p - q)), falling back to p when it is all zero) with the 24-bit uniform u24;
+// need = 0 when the window needs no draw (greedy, or a data error).
+struct DrawRec {
+    int need, stop, n;
+    uint32_t u24;
+};
+struct DrawPart {
+    uint64_t sr, sp;           // residual and p weight sums of a slice
+};
+
+// The draw's weights in 2^-44 fixed point: p (the warped target row) and the residual.
+struct DrawRows {
+    RowStat sp, sq;
+    const float *lp, *lq;
+    double Sp, Sq;
+    float T, min_p;
+};
+
+__device__ __forceinline__ uint64_t w_p(const DrawRows& R, int j) {
+    const float v = R.lp[j];
+    const float e = e_of(v, R.sp.lmax, R.T);
+    return kept(R.sp, v, e, j, R.min_p) ? to_fx(e) : 0ull;
+}
+
+__device__ __forceinline__ uint64_t w_r(const DrawRows& R, int j) {
+    const float v = R.lp[j];
+    const float e = e_of(v, R.sp.lmax, R.T);
+    if (!kept(R.sp, v, e, j, R.min_p)) return 0ull;
+    const double pj = (double)e / R.Sp;
+    const float vq = R.lq[j];
+    const float eq = e_of(vq, R.sq.lmax, R.T);
+    const double qj = kept(R.sq, vq, eq, j, R.min_p) ? (double)eq / R.Sq : 0.0;
+    const double d = pj - qj;
+    return d > 0.0 ? (uint64_t)(d * FX) : 0ull;
+}
+
+__device__ __forceinline__ DrawRows draw_rows(const AcceptArgs& A, int w, int stop) {
+    DrawRows R;
+    const int K = A.K, V = A.V;
+    R.sp = A.st_t[(size_t)w * K + stop - 1];
+    R.lp = A.tgt + ((size_t)w * K + stop - 1) * V;
+    R.Sp = (double)R.sp.keep_fx / FX;
+    R.T = A.T;
+    R.min_p = A.min_p;
+    if (stop < K) {
+        R.sq = A.st_d[(size_t)w * (K - 1) + stop - 1];
+        R.lq = A.drf + ((size_t)w * (K - 1) + stop - 1) * V;
+        R.Sq = (double)R.sq.keep_fx / FX;
+    } else {
+        R.sq = R.sp;
+        R.lq = R.lp;
+        R.Sq = R.Sp;
+    }
+    return R;
+}
 
 // C * 2^24 > u24 * S with 128-bit integers.
 __device__ __forceinline__ bool cross(uint64_t C, uint32_t u24, uint64_t S) {
@@ -679,6 +740,7 @@ __global__ __launch_bounds__(NT) void k_accept(AcceptArgs A) {
         __syncthreads();
     }
 
+    if (A.rec && threadIdx.x == 0 && (s_status != 0 || A.mode == VQ_MODE_GREEDY)) A.rec[w] = DrawRec{0, 0, 0, 0u};
     if (s_status != 0) {
         for (int i = threadIdx.x; i < K; i += NT) out[i] = -1;
         if (dtok && A.draft_mode != VQ_DRAFT_GIVEN)
@@ -734,6 +796,11 @@ __global__ __launch_bounds__(NT) void k_accept(AcceptArgs A) {
     }
     __syncthreads();
     const int stop = s_stop;
+    if (A.rec) {
+        // the draw is left to k_draw_part / k_draw_final
+        if (threadIdx.x == 0) A.rec[w] = DrawRec{1, stop, s_n, s_u[1]};
+        return;
+    }
     const RowStat sp = stt[stop - 1];
     const float* lp = tl + (size_t)(stop - 1) * V;
     auto wp = [&](int j) -> uint64_t {
@@ -769,13 +836,95 @@ __global__ __launch_bounds__(NT) void k_accept(AcceptArgs A) {
     }
 }
 
+// Split draw, part 1: the residual and p weight sums of slice sl of window w's draw row.
+__global__ __launch_bounds__(NT) void k_draw_part(AcceptArgs A) {
+    __shared__ uint64_t sh[NT + 1];
+    const int w = blockIdx.x / SPLIT_S, sl = blockIdx.x % SPLIT_S;
+    const DrawRec rc = A.rec[w];
+    if (!rc.need) return;
+    const DrawRows R = draw_rows(A, w, rc.stop);
+    const bool resid = rc.stop < A.K;
+    int j0, j1;
+    slice_of(A.V, sl, j0, j1);
+    uint64_t sr = 0, sp = 0;
+    for (int j = j0 + (int)threadIdx.x; j < j1; j += NT) {
+        sp += w_p(R, j);
+        if (resid) sr += w_r(R, j);
+    }
+    sp = block_sum_u64(sp, sh);
+    sr = block_sum_u64(sr, sh);
+    if (threadIdx.x == 0) A.part[blockIdx.x] = DrawPart{sr, sp};
+}
+
+// Split draw, part 2: the slice holding the crossing (slice order), then the smallest
+// index in it whose running sum crosses, found as block_cat finds it within one tile.
+__global__ __launch_bounds__(NT) void k_draw_final(AcceptArgs A) {
+    __shared__ uint64_t sh[NT + 1];
+    __shared__ int s_sl, s_res, s_useq;
+    __shared__ uint64_t s_C, s_S;
+    const int w = blockIdx.x;
+    const DrawRec rc = A.rec[w];
+    if (!rc.need) return;
+    const DrawRows R = draw_rows(A, w, rc.stop);
+    const DrawPart* P = A.part + (size_t)w * SPLIT_S;
+    if (threadIdx.x == 0) {
+        uint64_t Sr = 0, Sp = 0;
+        for (int i = 0; i < SPLIT_S; ++i) {
+            Sr += P[i].sr;
+            Sp += P[i].sp;
+        }
+        const bool resid = rc.stop < A.K && Sr > 0;     // an all-zero residual falls back to p
+        const uint64_t S = resid ? Sr : Sp;
+        uint64_t C = 0;
+        int sl = -1;
+        for (int i = 0; i < SPLIT_S && S > 0; ++i) {
+            const uint64_t x = resid ? P[i].sr : P[i].sp;
+            if (cross(C + x, rc.u24, S)) { sl = i; break; }
+            C += x;
+        }
+        s_sl = sl;
+        s_C = C;
+        s_S = S;
+        s_useq = resid ? 1 : 0;
+        s_res = -1;
+    }
+    __syncthreads();
+    const int sl = s_sl;
+    if (sl >= 0) {
+        int j0, j1;
+        slice_of(A.V, sl, j0, j1);
+        const bool resid = s_useq != 0;
+        const uint64_t S = s_S;
+        // one pass over the slice: each thread a contiguous run, prefix over the threads
+        const int n = j1 - j0, per = (n + NT - 1) / NT;
+        const int a = min(j1, j0 + (int)threadIdx.x * per), b = min(j1, a + per);
+        uint64_t loc = 0;
+        for (int j = a; j < b; ++j) loc += resid ? w_r(R, j) : w_p(R, j);
+        uint64_t tot;
+        const uint64_t before = s_C + block_excl_scan_u64(loc, sh, &tot);
+        if (loc > 0 && !cross(before, rc.u24, S) && cross(before + loc, rc.u24, S)) {
+            uint64_t C = before;
+            for (int j = a; j < b; ++j) {
+                C += resid ? w_r(R, j) : w_p(R, j);
+                if (cross(C, rc.u24, S)) { s_res = j; break; }
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        A.tokens[(size_t)w * A.K + rc.stop - 1] = s_res;
+        A.n_acc[w] = rc.n;
+        A.status[w] = 0;
+    }
+}
+
 }  // namespace
 
 // Workspace: row statistics of the target rows, then of the drafter rows, then (rows
 // split over workgroups) the slices' partials of each.
 struct AcceptLayout {
-    size_t st_d, p1_t, p2_t, p1_d, p2_d, total;
-    bool split_t, split_d;
+    size_t st_d, p1_t, p2_t, p1_d, p2_d, rec, dpart, total;
+    bool split_t, split_d, split_draw;
 };
 
 bool split_rows(int nrows, int V) { return nrows > 0 && nrows <= SPLIT_MAX_ROWS && V >= SPLIT_MIN_V; }
@@ -799,6 +948,14 @@ AcceptLayout accept_layout(const vq_accept_desc* d) {
         p += align_up(rd * SPLIT_S * sizeof(Part1), 256);
         L.p2_d = p;
         p += align_up(rd * SPLIT_S * sizeof(Part2), 256);
+    }
+    // sampling with few windows: the final draws split over workgroups
+    L.split_draw = d->mode == VQ_MODE_SAMPLE && split_rows(d->W, d->V);
+    if (L.split_draw) {
+        L.rec = p;
+        p += align_up((size_t)d->W * sizeof(DrawRec), 256);
+        L.dpart = p;
+        p += align_up((size_t)d->W * SPLIT_S * sizeof(DrawPart), 256);
     }
     L.total = p;
     return L;
@@ -845,8 +1002,18 @@ hipError_t launch_accept(const vq_accept_desc* d, void* ws, hipStream_t st) {
     AcceptArgs aa{d->mode, d->draft_mode, d->W, d->K, d->V, d->target_logits,
                   drafter ? d->draft_logits : nullptr, d->draft_tokens, T, d->top_p, d->min_p,
                   (uint32_t)a24, d->seed, d->window_base, st_t, drafter ? st_d : nullptr,
-                  d->n_accepted, d->tokens, d->status};
+                  d->n_accepted, d->tokens, d->status, nullptr, nullptr};
+    if (L.split_draw) {
+        aa.rec = (DrawRec*)(wsb + L.rec);
+        aa.part = (DrawPart*)(wsb + L.dpart);
+    }
     k_accept<<<dim3(d->W), NT, 0, st>>>(aa);
+    if (L.split_draw) {
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        k_draw_part<<<dim3(d->W * SPLIT_S), NT, 0, st>>>(aa);
+        k_draw_final<<<dim3(d->W), NT, 0, st>>>(aa);
+    }
     return hipGetLastError();
 }
 
