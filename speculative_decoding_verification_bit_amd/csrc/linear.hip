@@ -1018,7 +1018,7 @@ __device__ void prep_x_mfma(const StageArgs& A, const float* rs) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 v[q] = col_live ? h[slot_col<FMT>(2 * q)] | (h[slot_col<FMT>(2 * q + 1)] << 16) : 0u;
-            st_through_u4(A.xp + (size_t)b * 64 + lane, v);
+            A.xp[(size_t)b * 64 + lane] = v;
             if constexpr (FMT == VQ_FMT_Q4_MIN) {
                 float t = col_live ? sum : 0.f;
                 t += __shfl_xor(t, 16, 64);
@@ -1029,7 +1029,7 @@ __device__ void prep_x_mfma(const StageArgs& A, const float* rs) {
                 am[tt >> 1] |= e << (16 * (tt & 1));
             }
         }
-        if constexpr (FMT == VQ_FMT_Q4_MIN) st_through_u4(A.xpa + (size_t)gi * 64 + lane, am);
+        if constexpr (FMT == VQ_FMT_Q4_MIN) A.xpa[(size_t)gi * 64 + lane] = am;
     }
 }
 
@@ -1042,7 +1042,9 @@ __global__ __launch_bounds__(256) void k_stage_mfma(const StageArgs A, const Sta
             // before the count), count this workgroup
             stage_rms(A, sm.rs, &sm.red[0][0][0]);
             prep_x_mfma<FMT>(A, sm.rs);
-            __builtin_amdgcn_s_waitcnt(0);
+            // plain stores written back by a fence before the count (measured faster here
+            // than write-through stores; the VALU conversion measured the other way)
+            __threadfence();
             __syncthreads();
             if (threadIdx.x == 0) __hip_atomic_fetch_add(A.xflag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
