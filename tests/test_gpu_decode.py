@@ -107,7 +107,7 @@ LAUNCHES = [4, 8]          # staged, persistent
 
 @pytest.mark.parametrize("launch", LAUNCHES)
 @pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_MXFP4])
-@pytest.mark.parametrize("K,path", [(1, 1), (4, 1), (8, 1), (4, 2), (16, 2), (1, 3), (4, 3)])
+@pytest.mark.parametrize("K,path", [(1, 1), (2, 1), (3, 1), (4, 1), (8, 1), (4, 2), (16, 2), (1, 3), (4, 3)])
 def test_mini_model_every_stage(fmt, K, path, launch):
     """A 2-layer stack (hidden 256, kv 64, ffn 512, vocab 1000): all rows of all stages."""
     if path == 3 and launch == 8:
@@ -123,7 +123,7 @@ SHAPE_MID = synth.ModelShape(n_layers=2, hidden=2048, kv_dim=256, ffn=5120, voca
 
 
 @pytest.mark.parametrize("launch", LAUNCHES)
-@pytest.mark.parametrize("K,path", [(1, 0), (4, 1), (8, 1), (8, 2), (16, 2), (2, 3)])
+@pytest.mark.parametrize("K,path", [(1, 0), (2, 1), (3, 0), (4, 1), (8, 1), (8, 2), (16, 2), (2, 3)])
 def test_mid_model_every_stage_split_k(K, path, launch):
     """hidden 2048, kv 256, ffn 5120, vocab 4000: 2 and 5 column chunks per row."""
     if path == 3 and launch == 8:
