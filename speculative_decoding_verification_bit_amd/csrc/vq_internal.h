@@ -313,15 +313,16 @@ inline StageGeom stage_geom(int rows, int cols, int paired, int half) {
 // Which kernel streams a stage.
 enum Kern { KERN_VALU = 0, KERN_MFMA = 1, KERN_ROWS = 2 };
 
-// Geometry of a stage for its kernel: the VALU tile kernel one chunk per item (measured
-// fastest), the MFMA tile kernel with the run length of the work-splitting model, the
+// Geometry of a stage for its kernel: the tile kernels one chunk per item (measured
+// fastest for both: a run of chunks is loaded and computed in series by one workgroup;
+// at K = 8 the work-splitting model's runs cost 10.34 against 9.41 ms per 27B pass), the
 // row-strip kernel where the row's activations fit (the VALU tile kernel elsewhere).
 inline StageGeom plan_geom(int rows, int cols, int paired, int half, int K, Kern kern) {
     if (kern == KERN_ROWS && K <= ROWS_MAX_K) {
         const StageGeom g = rows_geom(rows, cols, paired, half, K);
         if (g.rk) return g;
     }
-    if (kern == KERN_MFMA) return stage_geom(rows, cols, paired, half);
+    (void)kern;
     return stage_geom_cpw(rows, cols, paired, half, 1);
 }
 // Stream-ahead pass (LDS-direct weight rings, one 8-wave workgroup per CU): K up to
