@@ -805,19 +805,33 @@ __device__ __forceinline__ void compute_tile_mfma(const WTileM& T, int gq, int n
             if constexpr (FMT == VQ_FMT_MXFP4) d[i] = e8m0_to_float((T.sv[t][i >> 2] >> (8 * (i & 3))) & 0xffu);
             else d[i] = half_bits_to_float((T.sv[t][i >> 1] >> (16 * (i & 1))) & 0xffffu);
         }
-        // all 8 block products first (independent MFMAs, issued back to back), then the
-        // scales in block order; blocks past the row's end have zero A operands and zero
-        // scales, so they add exactly nothing
-        f4_t D[8];
+        if constexpr (FMT != VQ_FMT_Q4_MIN) {
+            // one product at a time: batched, these formats' kernels take far more
+            // registers (the E8M0 one drops from 5 waves per SIMD to 2: measured slower)
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
-            const h8_t B = widen_block_quarter<FMT>(tt < 4 ? T0[tt] : T1[tt - 4]);
-            D[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], B, zero, 0, 0, 0);
+            for (int tt = 0; tt < 8; ++tt) {
+                if (tt < nvb) {
+                    const h8_t B = widen_block_quarter<FMT>(tt < 4 ? T0[tt] : T1[tt - 4]);
+                    const f4_t D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], B, zero, 0, 0, 0);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(d[tt], D[v], acc[t][v]);
+                }
+            }
+        } else {
+            // all 8 block products first (independent MFMAs, issued back to back), then
+            // the scales in block order; blocks past the row's end have zero A operands
+            // and zero scales, so they add exactly nothing
+            f4_t D[8];
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) {
+                const h8_t B = widen_block_quarter<FMT>(tt < 4 ? T0[tt] : T1[tt - 4]);
+                D[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[tt], B, zero, 0, 0, 0);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(d[tt], D[tt][v], acc[t][v]);
         }
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[t][v] = fmaf(d[tt], D[tt][v], acc[t][v]);
         if constexpr (FMT == VQ_FMT_Q4_MIN) {
             u4_t mm;
 #pragma unroll
