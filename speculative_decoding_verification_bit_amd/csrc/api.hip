@@ -145,7 +145,7 @@ struct DecodeLayout {
 int stage_tiles(const Shapes& s, int st) {
     const StageShape ss = stage_shape(s, st);
     const int paired = (st < 4 * s.L && st % 4 == 2);
-    return stage_geom(ss.rows, ss.cols, paired, paired ? s.FF : 0).ntiles;
+    return stage_geom_cpw(ss.rows, ss.cols, paired, paired ? s.FF : 0, 1).ntiles;
 }
 
 DecodeLayout decode_layout(const Shapes& s, int K) {

@@ -67,20 +67,6 @@ constexpr int ROWS_MAX_K = 4;
 constexpr int ROWS_NLD = 12;
 constexpr int ROWS_X_BYTES = 36864;
 
-// Work-splitting model: a tile's chunks are dealt out in runs of cpw chunks per item.
-// Longer runs stream more weights per workgroup between epilogues (partial exchange,
-// arrival counting), shorter runs give more items to spread over the chip.  The cost of
-// a choice is the number of rounds of ITEM_SLOTS concurrent items times a round's
-// length, counting an epilogue as EPI_COST chunks; the cheapest run length wins (ties go
-// to the shorter run).
-#ifndef VQ_ITEM_SLOTS
-#define VQ_ITEM_SLOTS 512
-#endif
-#ifndef VQ_EPI_COST
-#define VQ_EPI_COST 2
-#endif
-constexpr int ITEM_SLOTS = VQ_ITEM_SLOTS;
-constexpr int EPI_COST = VQ_EPI_COST;
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -293,29 +279,12 @@ inline StageGeom rows_geom(int rows, int cols, int paired, int half, int K) {
     return g;
 }
 
-// Tile-kernel geometry with the run length the work-splitting model picks (host side).
-inline StageGeom stage_geom(int rows, int cols, int paired, int half) {
-    StageGeom g = stage_geom_cpw(rows, cols, paired, half, 1);
-    long best = -1;
-    for (int c = 1; c <= g.nchunks; ++c) {
-        const int parts = (g.nchunks + c - 1) / c;
-        if (c > 1 && parts == (g.nchunks + c - 2) / (c - 1)) continue;   // same split, longer run
-        const long items = (long)g.ntiles * parts;
-        const long cost = (items + ITEM_SLOTS - 1) / ITEM_SLOTS * (long)(c + EPI_COST);
-        if (best < 0 || cost < best) {
-            best = cost;
-            g.cpw = c;
-        }
-    }
-    return stage_geom_cpw(rows, cols, paired, half, g.cpw);
-}
-
 // Which kernel streams a stage.
 enum Kern { KERN_VALU = 0, KERN_MFMA = 1, KERN_ROWS = 2 };
 
 // Geometry of a stage for its kernel: the tile kernels one chunk per item (measured
 // fastest for both: a run of chunks is loaded and computed in series by one workgroup;
-// at K = 8 the work-splitting model's runs cost 10.34 against 9.41 ms per 27B pass), the
+// at K = 8 runs of several chunks per item cost 10.34 against 9.41 ms per 27B pass), the
 // row-strip kernel where the row's activations fit (the VALU tile kernel elsewhere).
 inline StageGeom plan_geom(int rows, int cols, int paired, int half, int K, Kern kern) {
     if (kern == KERN_ROWS && K <= ROWS_MAX_K) {
