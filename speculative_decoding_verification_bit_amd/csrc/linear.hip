@@ -352,17 +352,36 @@ struct WTileV {
     uint32_t sr[8], mr[8];
 };
 
-template <int FMT>
-__device__ __forceinline__ void load_tile_valu(const StageArgs& A, int tile, int s, int bcl, WTileV& T) {
+// Q4 with mins at K = 1 (PAIR): lanes c and c + 1 (c even) hold blocks p and p + 1 of the
+// same row, so the even lane loads both blocks' scales and the odd lane both blocks' mins,
+// one 4-byte load each (T.sr; T.mr unused), and compute_tile_valu swaps the halves between
+// the two lanes (measured: K = 1 pass 4.63 -> 4.60 ms; at K >= 2 it was slower).  bu is the lane's block before clamping (the pair is formed from
+// it, so the two lanes agree on it even past the row's end).
+template <int FMT, bool PAIR>
+__device__ __forceinline__ void load_tile_valu(const StageArgs& A, int tile, int s, int bcl, int bu, WTileV& T) {
     tile = opaque(tile);          // row addresses are recomputed per chunk, not kept live
     const uint32_t rowq = (uint32_t)A.W.cols >> 1, nb = (uint32_t)A.W.cols >> 5;
     const uint32_t b = (uint32_t)bcl;
+    const bool odd = (threadIdx.x & 1) != 0;
+    const uint32_t pb = (uint32_t)bu & ~1u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const SegRef R = seg_ref(A.W, tile_seg(A, tile, 8 * i));
         const uint32_t lr = (uint32_t)(clamp_row(A, tile, 8 * i + s) - R.r0);
         T.w[i] = ld_global_nt<u4_t>(R.qs + (lr * rowq + 16u * b));
-        if constexpr (FMT == VQ_FMT_MXFP4) {
+        if constexpr (FMT == VQ_FMT_Q4_MIN && PAIR) {
+            const uint8_t* src = odd ? reinterpret_cast<const uint8_t*>(R.mn) : R.sc8;
+            if ((nb & 1u) == 0u) {
+                // even row length: the pair is 4-byte aligned and inside the row
+                const uint32_t e0 = min(pb, nb - 2u);
+                T.sr[i] = ld_global<uint32_t>(src + 2u * (lr * nb + e0));
+            } else {
+                const uint32_t e0 = min(pb, nb - 1u), e1 = min(pb + 1u, nb - 1u);
+                T.sr[i] = (uint32_t)ld_global<uint16_t>(src + 2u * (lr * nb + e0)) |
+                          ((uint32_t)ld_global<uint16_t>(src + 2u * (lr * nb + e1)) << 16);
+            }
+            T.mr[i] = 0u;
+        } else if constexpr (FMT == VQ_FMT_MXFP4) {
             T.sr[i] = ld_global<uint8_t>(R.sc8 + (lr * nb + b));
             T.mr[i] = 0u;
         } else {
@@ -395,8 +414,18 @@ __device__ __forceinline__ void compute_tile_valu(const StageArgs& A, int tile, 
             }
         }
         const bool ok = live && row_ok(A, tile, 8 * i + s);
-        float d = FMT == VQ_FMT_MXFP4 ? e8m0_to_float(T.sr[i]) : half_bits_to_float(T.sr[i]);
-        float m = half_bits_to_float(T.mr[i]);
+        float d, m;
+        if constexpr (FMT == VQ_FMT_Q4_MIN && K == 1) {
+            // the pair's scales (even lane) and mins (odd lane): swap with the partner lane
+            const uint32_t own = T.sr[i];
+            const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)own, 0xB1, 0xF, 0xF, false);
+            const bool odd = (threadIdx.x & 1) != 0;
+            d = half_bits_to_float(odd ? (other >> 16) : (own & 0xffffu));
+            m = half_bits_to_float(odd ? (own >> 16) : (other & 0xffffu));
+        } else {
+            d = FMT == VQ_FMT_MXFP4 ? e8m0_to_float(T.sr[i]) : half_bits_to_float(T.sr[i]);
+            m = half_bits_to_float(T.mr[i]);
+        }
         d = ok ? d : 0.f;
         m = ok ? m : 0.f;
 #pragma unroll
@@ -421,13 +450,13 @@ struct StageSmem {
 // group for rows 8i + s of the tile.
 //
 // The weights of one chunk for this lane.
-template <int FMT>
+template <int FMT, bool PAIR>
 __device__ __forceinline__ void prefetch_valu(const StageArgs& A, int tile, int chunk, WTileV& T) {
     const int nb = A.W.cols >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int b = (chunk * 4 + wave) * 8 + (lane & 7);
-    load_tile_valu<FMT>(A, tile, lane >> 3, b < nb ? b : nb - 1, T);
+    load_tile_valu<FMT, PAIR>(A, tile, lane >> 3, b < nb ? b : nb - 1, b, T);
 }
 
 // Whether a chunk's compute overlaps the loads of the next weights (two register tiles
@@ -563,14 +592,14 @@ __device__ void stage_item_valu(const StageArgs& A, const StageGeom& g, int tile
             // the next weights load while this chunk is computed (issued only now: a wait
             // for the activations above would otherwise also wait for them)
             WTileV nxt;
-            if (ch + 1 < c1) prefetch_valu<FMT>(A, tile, ch + 1, nxt);
-            else if (ntile >= 0) prefetch_valu<FMT>(A, ntile, npart * g.cpw, nxt);
+            if (ch + 1 < c1) prefetch_valu<FMT, K == 1>(A, tile, ch + 1, nxt);
+            else if (ntile >= 0) prefetch_valu<FMT, K == 1>(A, ntile, npart * g.cpw, nxt);
             compute_tile_valu<FMT, K>(A, tile, s, live, cur, xv, bs, acc);
             cur = nxt;
         } else {
             compute_tile_valu<FMT, K>(A, tile, s, live, cur, xv, bs, acc);
-            if (ch + 1 < c1) prefetch_valu<FMT>(A, tile, ch + 1, cur);
-            else if (ntile >= 0) prefetch_valu<FMT>(A, ntile, npart * g.cpw, cur);
+            if (ch + 1 < c1) prefetch_valu<FMT, K == 1>(A, tile, ch + 1, cur);
+            else if (ntile >= 0) prefetch_valu<FMT, K == 1>(A, ntile, npart * g.cpw, cur);
         }
     }
 #pragma unroll
@@ -662,7 +691,7 @@ __global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, const Sta
         const int item = xcd_item((int)blockIdx.x - A.n_prep, (int)gridDim.x - A.n_prep);
         const int tile = item / g.nparts, part = item - tile * g.nparts;
         WTileV cur;
-        prefetch_valu<FMT>(A, tile, part, cur);
+        prefetch_valu<FMT, K == 1>(A, tile, part, cur);
         wait_flag(A.xflag, (unsigned)A.n_prep, A.err);
         stage_item_valu<FMT, K, false, true>(A, g, tile, part, sm, xs, cur, -1, 0);
         return;
@@ -671,7 +700,7 @@ __global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, const Sta
     const int tile = item / g.nparts, part = item - tile * g.nparts;
     WTileV cur;
     if constexpr (MULTI) {
-        prefetch_valu<FMT>(A, tile, part * g.cpw, cur);
+        prefetch_valu<FMT, K == 1>(A, tile, part * g.cpw, cur);
         stage_rms(A, sm.rs, &sm.red[0][0][0]);
         stage_item_valu<FMT, K, MULTI>(A, g, tile, part, sm, xs, cur, -1, 0);
     } else {
@@ -682,7 +711,7 @@ __global__ __launch_bounds__(256) void k_stage_valu(const StageArgs A, const Sta
         stats_issue<4 * K>(A, sp);
         XPre<K> xp;
         x_issue<K>(A, g.nb, part, xp);
-        prefetch_valu<FMT>(A, tile, part, cur);
+        prefetch_valu<FMT, K == 1>(A, tile, part, cur);
         stats_finish<4 * K>(A, sp, sm.rs, &sm.red[0][0][0]);
         stage_item_valu<FMT, K, MULTI>(A, g, tile, part, sm, xs, cur, -1, 0, &xp);
     }
@@ -1477,7 +1506,7 @@ __global__ __launch_bounds__(256) void k_pass(const PassPlan P) {
         {
             const int tile = vid / g.nparts, part = vid - tile * g.nparts;
             if constexpr (MFMA) prefetch_mfma<FMT>(A, tile, part * g.cpw, cur);
-            else prefetch_valu<FMT>(A, tile, part * g.cpw, cur);
+            else prefetch_valu<FMT, K == 1>(A, tile, part * g.cpw, cur);
         }
         if (stage > s0)
             wait_count(P.done + (size_t)(stage - 1) * DONE_WORDS, (unsigned)P.geo[kind(stage - 1)].nstat, P.err);
