@@ -437,8 +437,8 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
     P.err = (int*)(sync + d.err_word);
     P.done = (persistent || streamed) ? sync + d.done_word : nullptr;
     if (!persistent && !streamed) {
-        // staged launches convert a stage's input once (MFMA: every stage; VALU at K >= 2:
-        // gate|up, down and lm_head, whose many workgroups would each convert it again); the
+        // staged launches convert a stage's input once (MFMA, and VALU at K >= 2: gate|up,
+        // down and lm_head, whose many workgroups would each convert it again); the
         // completion counters are unused in staged launches and serve as the conversion
         // counters
         P.xp = (u4_t_*)(base + d.xp_off);
@@ -501,8 +501,10 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
                 const StageGeom& g = P.geo[stage == 4 * s.L ? 4 : stage & 3];
                 // measured: at K = 1 the conversion's latency on the critical path (input
                 // scales, conversion, count) costs more than the per-workgroup conversion
-                // it saves (27B pass 4.59 -> 5.16 ms); from K = 2 it pays (7.19 -> 6.80)
-                if (P.xflag && !g.rk && (mfma || (K >= PREP_MIN_K_VALU && (stage == 4 * s.L || (stage & 3) >= 2))))
+                // it saves (27B pass 4.59 -> 5.16 ms); from K = 2 it pays (7.19 -> 6.80) on
+                // the large stages; the small q|k|v and o stages keep the inline
+                // conversion on both kernels (MFMA K = 8: 9.26 -> 9.02 ms)
+                if (P.xflag && !g.rk && (mfma || K >= PREP_MIN_K_VALU) && (stage == 4 * s.L || (stage & 3) >= 2))
                     A.n_prep = N_PREP;
                 if (runs && nl < n_events / 2) runs[nl] = g.rk ? -g.R : g.cpw;
                 e = launch_stage(A, g, mfma, st);

@@ -55,8 +55,8 @@ struct StageGeom {
     int nstat;     // sums-of-squares entries the stage writes (row-strip: items; tile: tiles)
 };
 
-// Workgroups that convert a stage's input (staged launches): every MFMA stage, and the
-// VALU kernel's gate|up, down and lm_head stages from K = PREP_MIN_K_VALU.
+// Workgroups that convert a stage's input (staged launches): the gate|up, down and lm_head
+// stages of the MFMA kernel, and of the VALU kernel from K = PREP_MIN_K_VALU.
 constexpr int N_PREP = 16;
 constexpr int PREP_MIN_K_VALU = 2;
 
