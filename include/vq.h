@@ -75,7 +75,7 @@ typedef struct vq_matrix {
 #define VQ_DTYPE_F32 0
 #define VQ_DTYPE_F16 1
 
-/* Kernel choice.  AUTO picks by K (VALU up to K = 4, MFMA above); the others force one
+/* Kernel choice.  AUTO picks by K (VALU up to K = 3, MFMA from K = 4); the others force one
    (for measurement). */
 #define VQ_PATH_AUTO 0
 #define VQ_PATH_VALU 1        /* VALU dot2 kernel on 64-row x 1024-column tiles, K <= 8 */
