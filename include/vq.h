@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 1
+#define VQ_ABI_VERSION 2
 
 /* ------------------------------------------------------------------ status */
 #define VQ_OK 0
@@ -75,30 +75,6 @@ typedef struct vq_matrix {
 #define VQ_DTYPE_F32 0
 #define VQ_DTYPE_F16 1
 
-/* Kernel choice.  AUTO picks by K (VALU up to K = 3, MFMA from K = 4); the others force one
-   (for measurement). */
-#define VQ_PATH_AUTO 0
-#define VQ_PATH_VALU 1        /* VALU dot2 kernel on 64-row x 1024-column tiles, K <= 8 */
-#define VQ_PATH_MFMA 2        /* MFMA 16x16x32 f16 kernel, K <= 16 */
-#define VQ_PATH_ROWS 3        /* VALU row-strip kernel (whole rows per workgroup, no split-K
-                                 exchange), K <= 4; stages whose K x cols activations do not
-                                 fit 36 KB of LDS run the VALU tile kernel */
-
-/* Launch strategy of vq_decode_pass, OR-ed into `path` (vq_verify_linear takes 0). */
-#define VQ_LAUNCH_AUTO 0        /* the faster of the two on MI355X: staged */
-#define VQ_LAUNCH_STAGED 4      /* one launch per stage */
-#define VQ_LAUNCH_PERSISTENT 8  /* one cooperative launch per 8 layers; inside it, a
-                                   stage waits on the completion counts of the previous one.
-                                   Tile kernels only: with VQ_PATH_ROWS the pass returns
-                                   VQ_ERR_UNSUPPORTED */
-#define VQ_LAUNCH_STREAM 16     /* (switched off in this build: VQ_ERR_UNSUPPORTED)
-                                   one cooperative launch per 8 layers, one 8-wave
-                                   workgroup per CU: every wave streams its rows' weights
-                                   through an LDS ring ahead of its arithmetic, across
-                                   stage boundaries.  K <= 2, path AUTO or VALU, hidden and
-                                   ffn widths up to 20480 (multiples of 64; of 128 for
-                                   MXFP4); otherwise VQ_ERR_UNSUPPORTED */
-
 #define VQ_MAX_K 16
 
 /*
@@ -114,17 +90,17 @@ typedef struct vq_matrix {
  *   x_f16   : device fp16 [K][cols]  (row k = activation column k of the window)
  *   K       : 1..16
  *   y       : device [K][rows], fp32 or fp16 (y_dtype); y[k][r] = sum_j w[r][j] x[k][j]
- *   path    : VQ_PATH_*
- *   ws      : device workspace of at least vq_workspace_bytes(VQ_OP_LINEAR, W, K) bytes
- * Errors: VQ_ERR_ARG for NULL pointers (except ws when the size query is 0), K outside
- * 1..16, cols not a positive multiple of 32, rows < 0, misaligned pointers, an unknown
- * format/dtype/path or mins inconsistent with the format; VQ_ERR_UNSUPPORTED for
- * VQ_PATH_VALU with K > 8 or a matrix whose codes take 2 GiB or more; VQ_ERR_WORKSPACE;
- * VQ_ERR_HIP.
- * rows == 0 is valid and enqueues nothing.
+ * Arithmetic: codes widen exactly to fp16 (q = n - 8, or the E2M1 value), products with
+ * the fp16 activations are exact, sums are fp32; the block scale multiplies the fp32 sum
+ * of its block and the min the fp32 sum of the block's activations, so no weight is
+ * rounded.  The result is deterministic (fixed summation order).
+ * Needs no workspace.  Errors: VQ_ERR_ARG for NULL pointers, K outside 1..16, cols not a
+ * positive multiple of 32, rows < 0, misaligned pointers (x and qs/scales/mins 16-byte,
+ * y its element size), an unknown format/dtype or mins inconsistent with the format;
+ * VQ_ERR_HIP.  rows == 0 is valid and enqueues nothing.
  */
 int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y,
-                     int32_t y_dtype, int32_t path, void* ws, size_t ws_bytes, void* stream);
+                     int32_t y_dtype, void* stream);
 
 /* ---------------------------------------------------------------- acceptance */
 #define VQ_MODE_GREEDY 0      /* accept x_i while it equals the target argmax            */
@@ -203,62 +179,68 @@ typedef struct vq_model {
  * once (Hacker News thread 49596054); the output is a [K][vocab] logits tensor.  Per
  * layer four dependent stages run: S1 q|k|v = W_qkv x_attn, S2 o = W_o x_o,
  * S3 gate|up = W_gu x_mlp, S4 down = W_down x_down, then logits = W_lm x_final.
- * The stack has no attention, norm weights or residuals; each stage input is the
- * previous output normalised to unit RMS per column and rounded to fp16:
- * x_o = rho(q), x_mlp = rho(o), x_down = rho(silu(gate) * up), next x_attn = rho(down),
- * x_final = rho(last down), with rho(v) = v / sqrt(mean(v^2)).  The first x_attn is x0.
+ * The stack has no attention, norm weights or residuals.  Stage glue: a stage's input is
+ * the previous stage's fp32 output v rounded to fp16 (x_o = q rows of q|k|v,
+ * x_mlp = o, x_down = silu(gate) * up, the next x_attn and x_final = down), and the
+ * stage multiplies its fp32 sums by rho = 1 / sqrt(mean(v^2)) of that v per column, so
+ * that every output is what a unit-RMS input would give.  The first x_attn is x0 and
+ * stage 0 is not scaled.
  *
  *   M      : host model descriptor; hidden = q.cols, every layer the same shapes;
  *            q: [H][H], k, v: [KV][H], o: [H][H], gate, up: [FF][H], down: [H][FF],
- *            lm_head: [V][H]; all matrices of one format
+ *            lm_head: [V][H]; all matrices of one format; H, KV, FF multiples of 64
  *   x0_f16 : device fp16 [K][H]
  *   logits : device f32 [K][V]
- *   path   : VQ_PATH_* | VQ_LAUNCH_*
  *   ws     : device workspace >= vq_workspace_bytes(VQ_OP_DECODE, M, K); after the call
- *            it holds every stage's fp16 input and fp32 output (see vq_decode_stage_ptr)
- * Persistent launches need every workgroup resident (a cooperative launch; the runtime
- * refuses it otherwise and the call returns VQ_ERR_HIP).  Their grid barriers wait at
- * most about a second; a barrier that times out sets an error word in ws (never expected
- * on a resident grid), after which the pass's results are not meaningful.
- * Errors: as vq_verify_linear, plus VQ_ERR_ARG for inconsistent layer shapes.
+ *            it holds every stage's fp16 input and fp32 output (vq_decode_stage_ptr)
+ * The pass runs as one persistent launch per 16 layers (the last one also runs the
+ * lm_head): one workgroup per compute unit, every workgroup resident (a cooperative
+ * launch; the runtime refuses it otherwise and the call returns VQ_ERR_HIP).  Inside a
+ * launch a stage waits for the previous one on device-scope completion counters; a wait
+ * gives up after about a second and raises the error word (vq_decode_error_word), after
+ * which the logits are not meaningful -- callers that cannot rule out such a stall read
+ * that word after the pass before trusting the logits.
+ * Errors: as vq_verify_linear, plus VQ_ERR_ARG for inconsistent layer shapes,
+ * VQ_ERR_UNSUPPORTED for sizes that are not multiples of 64, VQ_ERR_WORKSPACE.
  */
 int vq_decode_pass(const vq_model* M, const void* x0_f16, int32_t K, float* logits,
-                   int32_t path, void* ws, size_t ws_bytes, void* stream);
+                   void* ws, size_t ws_bytes, void* stream);
 
 /*
- * vq_decode_error_word -- where a decode pass in `ws` keeps its grid-barrier error word.
- *   *word : DEVICE address of an int32 that is 0 after a pass whose grid barriers all
- *           completed and 1 if one timed out (read it after the pass has finished)
+ * vq_decode_error_word -- where a decode pass in `ws` keeps its wait-timeout word.
+ *   *word : DEVICE address of an int32 that is 0 after a pass whose waits all completed
+ *           and 1 if one timed out (read it after the pass has finished)
  * Pure host arithmetic: no GPU call.  Errors: VQ_ERR_ARG for a bad model, K or NULL.
  */
 int vq_decode_error_word(const vq_model* M, int32_t K, void* ws, int32_t** word);
 
+/* Launch modes of vq_decode_pass_timed. */
+#define VQ_LAUNCH_AUTO 0        /* what vq_decode_pass does: persistent                  */
+#define VQ_LAUNCH_STAGED 4      /* one ordinary launch per stage (257 for 64 layers); the
+                                   same per-tile arithmetic, so the same bits            */
+#define VQ_LAUNCH_PERSISTENT 8  /* one cooperative launch per 16 layers                  */
+
 /*
- * vq_decode_pass_timed -- measurement hook: exactly the work of vq_decode_pass, plus
- * hipEventRecord(events[2i]) before and hipEventRecord(events[2i+1]) after the i-th
- * weight-streaming launch (one per stage when staged, one per 8 layers when persistent
- * or stream),
- * on `stream`, so the caller can time those launches (hipEventElapsedTime).
- *   events     : HOST array of n_events caller-created hipEvent_t handles (timing enabled)
- *   n_events   : >= 2 * (4 * n_layers + 1)
- *   n_launches : HOST out, the number of launches bracketed (may be NULL)
- *   runs       : HOST out [n_events / 2] (may be NULL): per launch, which kernel ran:
- *                -R for the row-strip kernel (R whole rows per workgroup item), c >= 1
- *                for the tile kernel with items of c chunks of 1024 columns (c > 1 is its
- *                multi-chunk variant), 0 for a persistent launch, -1 for a stream launch
- * Errors: as vq_decode_pass, plus VQ_ERR_ARG for a short or NULL-holding events array.
+ * vq_decode_pass_timed -- measurement hook: the work of vq_decode_pass with a chosen
+ * launch mode, plus hipEventRecord(events[2i]) before and hipEventRecord(events[2i+1])
+ * after the i-th launch (for i < n_events / 2), on `stream`.
+ *   launch     : VQ_LAUNCH_*
+ *   events     : HOST array of n_events caller-created hipEvent_t handles
+ *   n_launches : HOST out, the number of launches of the pass (may be NULL)
+ * Errors: as vq_decode_pass, plus VQ_ERR_ARG for an unknown launch mode or a short or
+ * NULL-holding events array.
  */
 int vq_decode_pass_timed(const vq_model* M, const void* x0_f16, int32_t K, float* logits,
-                         int32_t path, void* ws, size_t ws_bytes, void* stream,
-                         void* const* events, int32_t n_events, int32_t* n_launches,
-                         int32_t* runs);
+                         int32_t launch, void* ws, size_t ws_bytes, void* stream,
+                         void* const* events, int32_t n_events, int32_t* n_launches);
 
 /*
  * vq_decode_stage_ptr -- where a decode pass left stage s's tensors inside ws.
  * Stage s = 4*layer + j (j: 0 qkv, 1 o, 2 gate|up, 3 down), s = 4*n_layers is the
- * lm_head.  *in_f16 receives the device address of the fp16 input [K][cols] and
- * *out_f32 of the fp32 output [K][rows] (rows of the fused stage: qkv = H + 2 KV,
- * gate|up = 2 FF with gate first).  Host-only arithmetic; no device access.
+ * lm_head.  *in_f16 receives the device address of the fp16 input [K][cols] (natural
+ * column order) and *out_f32 of the fp32 output [K][rows] (rows of the fused stage:
+ * qkv = H + 2 KV, gate|up = 2 FF with gate first; NULL for the lm_head, whose output is
+ * the logits).  Host-only arithmetic; no device access.
  */
 int vq_decode_stage_ptr(const vq_model* M, int32_t K, void* ws, int32_t stage,
                         void** in_f16, void** out_f32);
@@ -268,7 +250,8 @@ int vq_decode_stage_ptr(const vq_model* M, int32_t K, void* ws, int32_t stage,
 #define VQ_OP_ACCEPT 1         /* desc = const vq_accept_desc*  */
 #define VQ_OP_DECODE 2         /* desc = const vq_model*        */
 
-/* Workspace bytes needed by an op for the given descriptor and K (0 on bad input). */
+/* Workspace bytes needed by an op for the given descriptor and K (0 on bad input; 0 for
+ * VQ_OP_LINEAR, which needs none). */
 size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K);
 
 /* Static text for a status code. */

@@ -5,9 +5,10 @@ import this package.  It wraps ``oracle.c`` (plain C, double precision, no fast-
 which shares no code with the HIP library.  What each function computes, and which
 passage of the pages it follows, is stated in ``oracle.c``.
 
-The stage-composition check of a full decode pass (each stage's input is the
-RMS-normalised previous output, the MLP input is silu(gate) * up) is written here in
-terms of the C primitives.
+The stage-composition glue of a full decode pass (a stage's input is the previous
+stage's output rounded to fp16 -- the q rows of q|k|v, o, silu(gate) * up, down -- and
+the stage scales its dot products by rho = 1 / sqrt(mean(v^2)) of that output) is
+written here in terms of the C primitives.
 """
 from __future__ import annotations
 
@@ -58,6 +59,7 @@ def lib():
         L.or_linear.restype = I32
         L.or_linear.argtypes = [I32, P, P, P, I64, I64, P, I32, P, P, I32]
         L.or_rho.argtypes = [P, I32, I64, P]
+        L.or_rms_scale.argtypes = [P, I32, I64, P]
         L.or_silu_mul.argtypes = [P, P, I64, P]
         L.or_philox4x64.argtypes = [P, P, P]
         L.or_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, P]
@@ -130,6 +132,32 @@ def rho(v: np.ndarray) -> np.ndarray:
     out = np.empty(v.shape, np.float64)
     lib().or_rho(_p(v), v.shape[0], v.shape[1], _p(out))
     return out
+
+
+def rms_scale(v: np.ndarray) -> np.ndarray:
+    """Per activation column k (row of v [K][n]): 1 / sqrt(mean(v^2)), in double."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape[0], np.float64)
+    lib().or_rms_scale(_p(v), v.shape[0], v.shape[1], _p(out))
+    return out
+
+
+STAGE_QKV, STAGE_O, STAGE_GU, STAGE_DOWN = 0, 1, 2, 3
+
+
+def stage_glue(prev_out: np.ndarray, prev_kind: int, hidden: int, ffn: int):
+    """What the next stage of a decode pass gets from a stage's fp32 output prev_out
+    [K][rows]: the value v [K][n] (double) whose fp16 rounding is the next input, and the
+    scale rho [K] of the next stage's dot products.  prev_kind is the producing stage:
+    q|k|v feeds its q rows, o and down feed themselves, gate|up feeds silu(gate) * up."""
+    prev_out = np.asarray(prev_out, dtype=np.float32)
+    if prev_kind == STAGE_QKV:
+        v = prev_out[:, :hidden].astype(np.float64)
+    elif prev_kind == STAGE_GU:
+        v = np.stack([silu_mul(prev_out[k, :ffn], prev_out[k, ffn:2 * ffn]) for k in range(prev_out.shape[0])])
+    else:
+        v = prev_out.astype(np.float64)
+    return v, rms_scale(v)
 
 
 def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:

@@ -37,6 +37,10 @@
  *  - a categorical draw over weights w picks the smallest index j (in vocabulary order)
  *    whose running sum exceeds u * sum(w); when rounding leaves no such j, the last j
  *    with w_j > 0.  An all-zero residual falls back to p itself.
+ *  - the decode pass's stage glue (the pages give the layer order, not the layer
+ *    internals): a stage's input is the previous stage's output rounded to fp16 (the q
+ *    rows of q|k|v for the o stage, silu(gate) * up for the down stage) and the stage
+ *    multiplies its dot products by rho = 1 / sqrt(mean(v^2)) of that previous output v.
  *  - uniforms: u = (r >> 40) * 2^-24 from the 64-bit Philox outputs; counter
  *    (window_base + w, position, 0, 0), key (seed, 0); lanes 0..3 are u_A (ratio
  *    test), u_R (residual / bonus draw), u_D (harness draft draw), u_X (harness
@@ -179,6 +183,19 @@ void or_rho(const double* v, int K, int64_t n, double* out) {
         for (int64_t j = 0; j < n; ++j) ss += vk[j] * vk[j];
         double rms = sqrt(ss / (double)n);
         for (int64_t j = 0; j < n; ++j) out[(int64_t)k * n + j] = vk[j] / rms;
+    }
+}
+
+/* The scale a decode-pass stage applies to its dot products: rho_k = 1 / sqrt(mean_j
+ * v[k][j]^2) of the previous stage's output v, per activation column k (the stage's
+ * input is v itself rounded to fp16, so its outputs are what the unit-RMS input v * rho
+ * would give).  n > 0. */
+void or_rms_scale(const double* v, int K, int64_t n, double* rho) {
+    for (int k = 0; k < K; ++k) {
+        const double* vk = v + (int64_t)k * n;
+        double ss = 0.0;
+        for (int64_t j = 0; j < n; ++j) ss += vk[j] * vk[j];
+        rho[k] = 1.0 / sqrt(ss / (double)n);
     }
 }
 

@@ -26,8 +26,7 @@ LIB_PATH = os.path.join(HERE, "libvq.so")
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 FMT_Q4, FMT_Q4_MIN, FMT_MXFP4 = 0, 1, 2
 DTYPE_F32, DTYPE_F16 = 0, 1
-PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_ROWS = 0, 1, 2, 3
-LAUNCH_AUTO, LAUNCH_STAGED, LAUNCH_PERSISTENT, LAUNCH_STREAM = 0, 4, 8, 16
+LAUNCH_AUTO, LAUNCH_STAGED, LAUNCH_PERSISTENT = 0, 4, 8
 MODE_GREEDY, MODE_SAMPLE = 0, 1
 DRAFT_GIVEN, DRAFT_Q_ARGMAX, DRAFT_Q_SAMPLE, DRAFT_AGREE = 0, 1, 2, 3
 OP_LINEAR, OP_ACCEPT, OP_DECODE = 0, 1, 2
@@ -72,14 +71,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L = ctypes.CDLL(path)
     I32, SZ = ctypes.c_int32, ctypes.c_size_t
     L.vq_verify_linear.restype = I32
-    L.vq_verify_linear.argtypes = [ctypes.POINTER(VqMatrix), _P, I32, _P, I32, I32, _P, SZ, _P]
+    L.vq_verify_linear.argtypes = [ctypes.POINTER(VqMatrix), _P, I32, _P, I32, _P]
     L.vq_verify_accept.restype = I32
     L.vq_verify_accept.argtypes = [ctypes.POINTER(VqAcceptDesc), _P, SZ, _P]
     L.vq_decode_pass.restype = I32
-    L.vq_decode_pass.argtypes = [ctypes.POINTER(VqModel), _P, I32, _P, I32, _P, SZ, _P]
+    L.vq_decode_pass.argtypes = [ctypes.POINTER(VqModel), _P, I32, _P, _P, SZ, _P]
     L.vq_decode_pass_timed.restype = I32
     L.vq_decode_pass_timed.argtypes = [ctypes.POINTER(VqModel), _P, I32, _P, I32, _P, SZ, _P,
-                                       ctypes.POINTER(_P), I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+                                       ctypes.POINTER(_P), I32, ctypes.POINTER(I32)]
     L.vq_decode_stage_ptr.restype = I32
     L.vq_decode_stage_ptr.argtypes = [ctypes.POINTER(VqModel), I32, _P, I32,
                                       ctypes.POINTER(_P), ctypes.POINTER(_P)]
@@ -157,19 +156,15 @@ def workspace_bytes(op: int, desc, K: int) -> int:
     return int(lib.vq_workspace_bytes(op, ctypes.cast(ctypes.pointer(desc), _P), K))
 
 
-def verify_linear(W: DeviceMatrix, x, y=None, y_dtype: int = DTYPE_F32, path: int = PATH_AUTO,
-                  ws=None, stream=None):
+def verify_linear(W: DeviceMatrix, x, y=None, y_dtype: int = DTYPE_F32, stream=None):
     """y[K][rows] = W x for fp16 x [K][cols] on the device."""
     import torch
     K = x.shape[0]
     if y is None:
         y = torch.empty((K, W.rows), dtype=torch.float32 if y_dtype == DTYPE_F32 else torch.float16,
                         device=x.device)
-    need = int(lib.vq_workspace_bytes(OP_LINEAR, ctypes.byref(W.desc), K))
-    if ws is None:
-        ws = _empty(need, x.device)
-    _check(lib.vq_verify_linear(ctypes.byref(W.desc), _ptr(x), K, _ptr(y), y_dtype, path,
-                                _ptr(ws), ws.numel(), _stream(stream)), "vq_verify_linear")
+    _check(lib.vq_verify_linear(ctypes.byref(W.desc), _ptr(x), K, _ptr(y), y_dtype, _stream(stream)),
+           "vq_verify_linear")
     return y
 
 
@@ -252,7 +247,7 @@ class DeviceModel:
         return int(stage_tensor(ws, a.value, (1,), torch.int32).item())
 
 
-def decode_pass(model: DeviceModel, x0, logits=None, path: int = PATH_AUTO, ws=None, stream=None):
+def decode_pass(model: DeviceModel, x0, logits=None, ws=None, stream=None):
     """logits[K][V] of one verify pass over the whole stack; ws keeps every stage's tensors."""
     import torch
     K = x0.shape[0]
@@ -260,26 +255,35 @@ def decode_pass(model: DeviceModel, x0, logits=None, path: int = PATH_AUTO, ws=N
         logits = torch.empty((K, model.vocab), dtype=torch.float32, device=x0.device)
     if ws is None:
         ws = _empty(model.workspace_bytes(K), x0.device)
-    _check(lib.vq_decode_pass(ctypes.byref(model.desc), _ptr(x0), K, _ptr(logits), path, _ptr(ws),
-                              ws.numel(), _stream(stream)), "vq_decode_pass")
+    _check(lib.vq_decode_pass(ctypes.byref(model.desc), _ptr(x0), K, _ptr(logits), _ptr(ws), ws.numel(),
+                              _stream(stream)), "vq_decode_pass")
     return logits, ws
 
 
-def decode_pass_timed(model: DeviceModel, x0, events, logits, ws, path: int = PATH_AUTO, stream=None):
-    """decode_pass plus HIP events around each weight-streaming launch.  Returns the list
-    of the bracketed launches' run lengths (chunks per workgroup item; 0 for a persistent
-    launch), one per launch.
+def decode_pass_launch(model: DeviceModel, x0, logits=None, ws=None, launch: int = LAUNCH_AUTO, events=None,
+                       stream=None):
+    """decode_pass with a chosen launch mode (LAUNCH_STAGED: one launch per stage), and
+    optionally HIP events around each launch.  Returns (logits, ws, number of launches).
 
-    events: a list of 2 * n_stages torch.cuda.Event(enable_timing=True), already recorded
-    once (so that their HIP handles exist); events[2 i] / events[2 i + 1] bracket launch i."""
+    events: a list of torch.cuda.Event(enable_timing=True), already recorded once (so that
+    their HIP handles exist); events[2 i] / events[2 i + 1] bracket launch i."""
+    import torch
     K = x0.shape[0]
+    if logits is None:
+        logits = torch.empty((K, model.vocab), dtype=torch.float32, device=x0.device)
+    if ws is None:
+        ws = _empty(model.workspace_bytes(K), x0.device)
+    if not events:
+        sink = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for ev in sink:
+            ev.record()
+        events = sink
     arr = (_P * len(events))(*[ev.cuda_event for ev in events])
     n = ctypes.c_int32(0)
-    runs = (ctypes.c_int32 * (len(events) // 2))()
-    _check(lib.vq_decode_pass_timed(ctypes.byref(model.desc), _ptr(x0), K, _ptr(logits), path, _ptr(ws),
-                                    ws.numel(), _stream(stream), arr, len(events), ctypes.byref(n), runs),
+    _check(lib.vq_decode_pass_timed(ctypes.byref(model.desc), _ptr(x0), K, _ptr(logits), launch, _ptr(ws),
+                                    ws.numel(), _stream(stream), arr, len(events), ctypes.byref(n)),
            "vq_decode_pass_timed")
-    return list(runs[:n.value])
+    return logits, ws, n.value
 
 
 def stage_tensor(ws, addr: int, shape, dtype):

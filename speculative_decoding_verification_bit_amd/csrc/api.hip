@@ -1,5 +1,5 @@
-// C ABI of libvq: argument validation, workspace layout, dispatch and the decode-pass
-// stage sequence.  Every check runs on the host before anything is enqueued.
+// C ABI of libvq: argument validation, the decode workspace layout, and the launch
+// sequence of a pass.  Every check runs on the host before anything is enqueued.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -35,8 +35,6 @@ int check_matrix(const vq_matrix* W, const char* name) {
     if (W->cols <= 0 || W->cols % 32)
         return fail(VQ_ERR_ARG, "%s: cols %d is not a positive multiple of 32", name, W->cols);
     if (W->rows == 0) return VQ_OK;
-    if ((int64_t)W->rows * (W->cols / 2) >= ((int64_t)1 << 31))
-        return fail(VQ_ERR_UNSUPPORTED, "%s: codes of %d x %d exceed 2 GiB", name, W->rows, W->cols);
     if (!W->qs || !W->scales) return fail(VQ_ERR_ARG, "%s: NULL qs or scales", name);
     if ((W->format == VQ_FMT_Q4_MIN) != (W->mins != nullptr))
         return fail(VQ_ERR_ARG, "%s: mins must be given exactly for VQ_FMT_Q4_MIN", name);
@@ -44,25 +42,6 @@ int check_matrix(const vq_matrix* W, const char* name) {
         return fail(VQ_ERR_ARG, "%s: qs, scales and mins must be 16-byte aligned", name);
     return VQ_OK;
 }
-
-Kern kernel_of(int K, int path) {
-    if (path == VQ_PATH_MFMA) return KERN_MFMA;
-    if (path == VQ_PATH_VALU) return KERN_VALU;
-    if (path == VQ_PATH_ROWS) return KERN_ROWS;
-    return K >= 4 ? KERN_MFMA : KERN_VALU;   // measured (27B pass): K = 4 8.13 vs 8.70 ms, K = 8 9.0 vs 20.4
-}
-
-int check_path(int K, int path) {
-    if (path < VQ_PATH_AUTO || path > VQ_PATH_ROWS) return fail(VQ_ERR_ARG, "unknown kernel path %d", path);
-    if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
-    if (path == VQ_PATH_VALU && K > 8)
-        return fail(VQ_ERR_UNSUPPORTED, "the VALU path is instantiated for K <= 8 (K = %d)", K);
-    if (path == VQ_PATH_ROWS && K > ROWS_MAX_K)
-        return fail(VQ_ERR_UNSUPPORTED, "the row-strip path is instantiated for K <= %d (K = %d)", ROWS_MAX_K, K);
-    return VQ_OK;
-}
-
-size_t lin_ws(const vq_matrix* W, int K) { return stage_scratch_bytes(W->rows, W->cols, K, 0, 0); }
 
 // ---------------------------------------------------------------- decode layout
 
@@ -107,120 +86,98 @@ int check_model(const vq_model* M, Shapes* s) {
     return VQ_OK;
 }
 
-// Stage s of a pass: 4 per layer (qkv, o, gate|up, down) + lm_head.
-struct StageShape {
-    int rows, cols;
-};
-
-StageShape stage_shape(const Shapes& s, int st) {
-    if (st == 4 * s.L) return {s.V, s.H};
-    switch (st % 4) {
-        case 0: return {s.H + 2 * s.KV, s.H};
-        case 1: return {s.H, s.H};
-        case 2: return {2 * s.FF, s.H};
-        default: return {s.H, s.FF};
-    }
-}
-
+// Workspace of a decode pass.  Every buffer a later stage reads is written once per pass
+// at its own 256-byte aligned place: per layer and stage the fp16 input in natural order
+// (xn, kept for inspection), the same input in the MFMA pair order (xp, what the next
+// stage reads for the Q4 formats) and the fp32 output (y); the lm_head's input; per stage
+// the per-workgroup sums of squares; the completion counters and the error word.
 struct DecodeLayout {
-    size_t in_off[4], out_off[4];  // per stage kind within a layer block
-    size_t layer_bytes;            // retention bytes per layer
-    size_t final_in_off;           // x_final fp16 [K][H]
-    size_t stats_off;              // per-tile sums of squares, stats_stride floats per stage
-    size_t stats_stride;
-    size_t sbuf_off;               // silu(gate) * up, f32 [K][FF], sbuf_stride floats per layer
-    size_t sbuf_stride;
-    size_t scratch_off;            // split-K partials (sized for the largest stage)
-    size_t xp_off, xp_stride;      // MFMA input conversion, per stage: [blocks][64] x 16 B,
-    size_t xpa_rel;                // then (at xpa_rel) [groups][64] x 16 B
-    size_t counters_off;           // sync words: tile arrival counters [max_tiles], error
-                                   // flag, stage completion counters [stages][DONE_WORDS]
-    int max_tiles;
-    int err_word;                  // index of the error flag among the sync words
-    int done_word;                 // index of the first completion counter
-    int sync_words;
+    size_t off_xn[4], off_xp[4], off_y[4];
+    size_t layer_bytes;
+    size_t off_fxn, off_fxp;
+    size_t off_stats, stats_stride;
+    size_t off_sync;
+    int sync_words;            // completion counters, then the error word
     size_t total;
 };
-
-int stage_tiles(const Shapes& s, int st) {
-    const StageShape ss = stage_shape(s, st);
-    const int paired = (st < 4 * s.L && st % 4 == 2);
-    return stage_geom_cpw(ss.rows, ss.cols, paired, paired ? s.FF : 0, 1).ntiles;
-}
 
 DecodeLayout decode_layout(const Shapes& s, int K) {
     DecodeLayout d{};
     size_t p = 0;
+    const int rows[4] = {s.H + 2 * s.KV, s.H, 2 * s.FF, s.H};
+    const int cols[4] = {s.H, s.H, s.H, s.FF};
     for (int j = 0; j < 4; ++j) {
-        const StageShape ss = stage_shape(s, j);
-        d.in_off[j] = p;
-        p += align_up((size_t)K * ss.cols * 2, 256);
-        d.out_off[j] = p;
-        p += align_up((size_t)K * ss.rows * 4, 256);
+        d.off_xn[j] = p;
+        p += align_up((size_t)K * cols[j] * 2, 256);
+        d.off_xp[j] = p;
+        p += align_up((size_t)K * cols[j] * 2, 256);
+        d.off_y[j] = p;
+        p += align_up((size_t)K * rows[j] * 4, 256);
     }
     d.layer_bytes = p;
     p = d.layer_bytes * s.L;
-    d.final_in_off = p;
+    d.off_fxn = p;
     p += align_up((size_t)K * s.H * 2, 256);
-    int mt = 0;
-    size_t sc = 0;
-    for (int j = 0; j <= 4; ++j) {
-        const int st = j == 4 ? 4 * s.L : j;
-        const StageShape ss = stage_shape(s, st);
-        const int paired = (j == 2);
-        mt = std::max(mt, stage_tiles(s, st));
-        sc = std::max(sc, stage_scratch_bytes(ss.rows, ss.cols, K, paired, paired ? s.FF : 0));
-    }
-    d.max_tiles = mt;
-    // Every buffer a later stage reads is written once per pass at its own 256-byte
-    // aligned place (no reuse between stages or layers): the persistent pass reads them
-    // through the caches while other XCDs may still be writing their neighbours.
-    d.stats_off = p;
-    // sums of squares: one per tile (tile kernel) or per item (row-strip kernel)
-    int mstat = mt;
-    for (int j = 0; j <= 4; ++j) {
-        const int st = j == 4 ? 4 * s.L : j;
-        const StageShape ss = stage_shape(s, st);
-        mstat = std::max(mstat, rows_geom(ss.rows, ss.cols, j == 2, j == 2 ? s.FF : 0, std::min(K, ROWS_MAX_K)).nitems);
-    }
-    d.stats_stride = align_up((size_t)mstat * K * 4, 256) / 4;
+    d.off_fxp = p;
+    p += align_up((size_t)K * s.H * 2, 256);
+    d.off_stats = p;
+    d.stats_stride = align_up((size_t)FLOW_MAX_WG * K, 64);
     p += d.stats_stride * 4 * (size_t)(4 * s.L);
-    d.sbuf_off = p;
-    d.sbuf_stride = align_up((size_t)K * s.FF * 4, 256) / 4;
-    p += d.sbuf_stride * 4 * (size_t)s.L;
-    d.scratch_off = p;
-    p += sc;
-    {
-        // one region per stage (written once per pass, like every other buffer a later
-        // reader loads through its caches): conversion slots of the widest input
-        const size_t nbm = (size_t)std::max(s.H, s.FF) / 32;
-        d.xp_stride = align_up(nbm * 64 * 16, 256) + align_up((nbm + 7) / 8 * 64 * 16, 256);
-        d.xpa_rel = align_up(nbm * 64 * 16, 256);
-        d.xp_off = p;
-        p += d.xp_stride * (size_t)(4 * s.L + 1);
-    }
-    d.counters_off = p;
-    d.err_word = mt;
-    d.done_word = (int)align_up((size_t)mt + 1, DONE_STRIDE);
-    d.sync_words = d.done_word + (4 * s.L + 1) * DONE_WORDS;
+    d.off_sync = p;
+    d.sync_words = (4 * s.L + 1) * DONE_WORDS + DONE_STRIDE;
     p += align_up((size_t)d.sync_words * 4, 256);
     d.total = p;
     return d;
 }
 
-Mat mat_cat(const vq_matrix* const* ms, int n) {
-    Mat r = mat_from(*ms[0]);
-    r.nseg = n;
-    int end = 0;
-    for (int i = 0; i < n; ++i) {
-        end += ms[i]->rows;
-        r.seg_end[i] = end;
-        r.qs[i] = (const uint8_t*)ms[i]->qs;
-        r.scales[i] = ms[i]->scales;
-        r.mins[i] = (const uint16_t*)ms[i]->mins;
+int* err_word(const DecodeLayout& d, char* ws) {
+    return (int*)(ws + d.off_sync) + (d.sync_words - DONE_STRIDE);
+}
+
+// Tiles of 16 rows per stage (gate|up: 8 gate + 8 up rows).
+int stage_tiles(const Shapes& s, int st) {
+    if (st == 4 * s.L) return (s.V + 15) / 16;
+    switch (st & 3) {
+        case 0: return (s.H + 2 * s.KV) / 16;
+        case 1: return s.H / 16;
+        case 2: return s.FF / 8;
+        default: return s.H / 16;
     }
-    r.rows = end;
-    return r;
+}
+
+void fill_common(FlowArgs& A, const vq_model* M, const Shapes& s, const DecodeLayout& d, int K,
+                 const void* x0, float* logits, char* ws) {
+    A = FlowArgs{};
+    A.fmt = s.fmt;
+    A.K = K;
+    A.H = s.H; A.KV = s.KV; A.FF = s.FF; A.V = s.V; A.L = s.L;
+    A.nwg = flow_grid();
+    A.x0 = (const uint16_t*)x0;
+    A.out = logits;
+    A.ws = ws;
+    A.layer_bytes = d.layer_bytes;
+    for (int j = 0; j < 4; ++j) {
+        A.off_xn[j] = d.off_xn[j];
+        A.off_xp[j] = d.off_xp[j];
+        A.off_y[j] = d.off_y[j];
+    }
+    A.off_fxn = d.off_fxn;
+    A.off_fxp = d.off_fxp;
+    A.off_stats = d.off_stats;
+    A.stats_stride = d.stats_stride;
+    A.done = (unsigned*)(ws + d.off_sync);
+    A.err = err_word(d, ws);
+    A.lm = MatPtr{(const uint8_t*)M->lm_head.qs, M->lm_head.scales, (const uint16_t*)M->lm_head.mins};
+}
+
+void fill_layers(FlowArgs& A, const vq_model* M, int l0) {
+    A.l0 = l0;
+    for (int i = 0; i < FLOW_MAX_LAYERS && l0 + i < M->n_layers; ++i) {
+        const vq_layer& y = M->layers[l0 + i];
+        const vq_matrix* ms[7] = {&y.q, &y.k, &y.v, &y.o, &y.gate, &y.up, &y.down};
+        for (int m = 0; m < 7; ++m)
+            A.m[i][m] = MatPtr{(const uint8_t*)ms[m]->qs, ms[m]->scales, (const uint16_t*)ms[m]->mins};
+    }
 }
 
 }  // namespace
@@ -247,11 +204,7 @@ const char* vq_status_string(int32_t status) {
 
 size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K) {
     if (!desc) return 0;
-    if (op == VQ_OP_LINEAR) {
-        const vq_matrix* W = (const vq_matrix*)desc;
-        if (check_matrix(W, "W") || K < 1 || K > VQ_MAX_K) return 0;
-        return W->rows == 0 ? 0 : lin_ws(W, K);
-    }
+    if (op == VQ_OP_LINEAR) return 0;            // the linear map needs no workspace
     if (op == VQ_OP_ACCEPT) {
         const vq_accept_desc* d = (const vq_accept_desc*)desc;
         if (d->W < 0 || d->K < 1 || d->K > VQ_MAX_K) return 0;
@@ -265,36 +218,31 @@ size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K) {
     return 0;
 }
 
-int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype,
-                     int32_t path, void* ws, size_t ws_bytes, void* stream) {
+int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype, void* stream) {
     g_err[0] = 0;
     int rc = check_matrix(W, "W");
     if (rc) return rc;
-    rc = check_path(K, path);
-    if (rc) return rc;
+    if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
     if (y_dtype != VQ_DTYPE_F32 && y_dtype != VQ_DTYPE_F16) return fail(VQ_ERR_ARG, "unknown y_dtype %d", y_dtype);
     if (W->rows == 0) return VQ_OK;
     if (!x_f16 || !y) return fail(VQ_ERR_ARG, "NULL x or y");
     if (!aligned(x_f16, 16)) return fail(VQ_ERR_ARG, "x must be 16-byte aligned");
     if (!aligned(y, y_dtype == VQ_DTYPE_F32 ? 4 : 2)) return fail(VQ_ERR_ARG, "y is misaligned");
-    const size_t need = lin_ws(W, K);
-    if (!ws || ws_bytes < need || !aligned(ws, 256))
-        return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
-    const Kern kern = kernel_of(K, path);
-    const bool mfma = kern == KERN_MFMA;
-    StageArgs A{};
-    A.W = mat_from(*W);
+    FlowArgs A{};
+    A.fmt = W->format;
     A.K = K;
-    A.glue = GLUE_NONE;
-    A.x16 = (const uint16_t*)x_f16;
-    A.y = y;
+    A.V = W->rows;
+    A.H = W->cols;
+    A.L = 0;
+    A.linear = 1;
     A.y_dtype = y_dtype;
-    stage_scratch_carve(ws, W->rows, W->cols, K, 0, 0, &A);
-    hipStream_t st = (hipStream_t)stream;
-    const StageGeom g = plan_geom(W->rows, W->cols, 0, 0, K, kern);
-    hipError_t e = g.rk ? hipSuccess : launch_zero_u32(A.counters, g.ntiles, st);
-    if (e != hipSuccess) return hip_fail(e, "counter reset launch");
-    e = launch_stage(A, g, mfma, st);
+    A.s_begin = 0;
+    A.s_end = 1;
+    A.nwg = std::min(flow_grid(), (W->rows + 15) / 16);
+    A.x0 = (const uint16_t*)x_f16;
+    A.out = y;
+    A.lm = MatPtr{(const uint8_t*)W->qs, W->scales, (const uint16_t*)W->mins};
+    const hipError_t e = launch_flow(A, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "linear launch");
     return VQ_OK;
 }
@@ -348,12 +296,12 @@ int vq_decode_stage_ptr(const vq_model* M, int32_t K, void* ws, int32_t stage, v
     const DecodeLayout d = decode_layout(s, K);
     char* base = (char*)ws;
     if (stage == 4 * s.L) {
-        *in_f16 = base + d.final_in_off;
+        *in_f16 = base + d.off_fxn;
         *out_f32 = nullptr;
     } else {
         const size_t lb = (size_t)(stage / 4) * d.layer_bytes;
-        *in_f16 = base + lb + d.in_off[stage % 4];
-        *out_f32 = base + lb + d.out_off[stage % 4];
+        *in_f16 = base + lb + d.off_xn[stage % 4];
+        *out_f32 = base + lb + d.off_y[stage % 4];
     }
     return VQ_OK;
 }
@@ -365,175 +313,81 @@ int vq_decode_error_word(const vq_model* M, int32_t K, void* ws, int32_t** word)
     if (rc) return rc;
     if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
     if (!ws || !word) return fail(VQ_ERR_ARG, "NULL pointer");
-    const DecodeLayout d = decode_layout(s, K);
-    *word = (int32_t*)((char*)ws + d.counters_off) + d.err_word;
+    *word = err_word(decode_layout(s, K), (char*)ws);
     return VQ_OK;
 }
 
-static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
+static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t launch,
                        void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t n_events,
-                       int32_t* n_launches, int32_t* runs) {
+                       int32_t* n_launches) {
     g_err[0] = 0;
     Shapes s;
     int rc = check_model(M, &s);
     if (rc) return rc;
-    const int kern = path & 3, launch = path & ~3;
-    if (launch != VQ_LAUNCH_AUTO && launch != VQ_LAUNCH_STAGED && launch != VQ_LAUNCH_PERSISTENT &&
-        launch != VQ_LAUNCH_STREAM)
-        return fail(VQ_ERR_ARG, "unknown launch mode in path %d", path);
-    rc = check_path(K, kern);
-    if (rc) return rc;
-    if (launch == VQ_LAUNCH_PERSISTENT && kern == VQ_PATH_ROWS)
-        return fail(VQ_ERR_UNSUPPORTED, "the persistent launch does not run the row-strip kernel");
-    const bool streamed = launch == VQ_LAUNCH_STREAM;
-    if (streamed) {
-        // Switched off: the kernel's first run (two-layer stack, K = 1, Q4 with mins) made
-        // a GPU memory fault whose cause is not found yet; its addressing checks out on
-        // the host.
-        if (!stream_enabled())
-            return fail(VQ_ERR_UNSUPPORTED, "the stream launch is switched off (a GPU fault under investigation)");
-        if (kern != VQ_PATH_AUTO && kern != VQ_PATH_VALU)
-            return fail(VQ_ERR_UNSUPPORTED, "the stream launch runs its own VALU kernel (path %d)", kern);
-        if (!stream_supported(s.fmt, K, s.H, s.KV, s.FF))
-            return fail(VQ_ERR_UNSUPPORTED, "the stream launch takes K <= %d and widths up to %d (K = %d, %d / %d)",
-                        STREAM_MAX_K, VQ_STREAM_MAX_COLS, K, s.H, s.FF);
-    }
+    if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
+    if (launch != VQ_LAUNCH_AUTO && launch != VQ_LAUNCH_STAGED && launch != VQ_LAUNCH_PERSISTENT)
+        return fail(VQ_ERR_ARG, "unknown launch mode %d", launch);
     if (!x0_f16 || !logits) return fail(VQ_ERR_ARG, "NULL x0 or logits");
     if (!aligned(x0_f16, 16) || !aligned(logits, 4)) return fail(VQ_ERR_ARG, "x0 or logits misaligned");
     const DecodeLayout d = decode_layout(s, K);
     if (!ws || ws_bytes < d.total || !aligned(ws, 256))
         return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", d.total, ws_bytes);
-    const Kern kind = kernel_of(K, kern);
-    const bool mfma = kind == KERN_MFMA;
-    const bool persistent = launch == VQ_LAUNCH_PERSISTENT;     // AUTO: staged (measured faster)
     hipStream_t st = (hipStream_t)stream;
     char* base = (char*)ws;
-    unsigned* sync = (unsigned*)(base + d.counters_off);
-    hipError_t e = launch_zero_u32(sync, d.sync_words, st);     // counters, error flag
+    hipError_t e = launch_zero_u32((unsigned*)(base + d.off_sync), d.sync_words, st);
     if (e != hipSuccess) return hip_fail(e, "sync reset launch");
-    PassPlan P{};
-    P.fmt = s.fmt;
-    P.K = K;
-    P.H = s.H;
-    P.KV = s.KV;
-    P.FF = s.FF;
-    P.V = s.V;
-    P.L = s.L;
-    P.x0 = (const uint16_t*)x0_f16;
-    P.logits = logits;
-    P.base = base;
-    P.layer_bytes = d.layer_bytes;
-    for (int j = 0; j < 4; ++j) {
-        P.in_off[j] = d.in_off[j];
-        P.out_off[j] = d.out_off[j];
-    }
-    P.final_in_off = d.final_in_off;
-    P.stats = (float*)(base + d.stats_off);
-    P.stats_stride = d.stats_stride;
-    P.sbuf = (float*)(base + d.sbuf_off);
-    P.sbuf_stride = d.sbuf_stride;
-    P.part = (float*)(base + d.scratch_off);
-    P.counters = sync;
-    P.err = (int*)(sync + d.err_word);
-    P.done = (persistent || streamed) ? sync + d.done_word : nullptr;
-    if (!persistent && !streamed) {
-        // staged launches convert a stage's input once (MFMA, and VALU at K >= 2: gate|up,
-        // down and lm_head, whose many workgroups would each convert it again); the
-        // completion counters are unused in staged launches and serve as the conversion
-        // counters
-        P.xp = (u4_t_*)(base + d.xp_off);
-        P.xpa = (u4_t_*)(base + d.xp_off + d.xpa_rel);
-        P.xp_stride = d.xp_stride / 16;
-        P.xflag = sync + d.done_word;
-    }
-    P.coh = persistent ? 1 : 0;
-    P.lm = MatPtrs{M->lm_head.qs, M->lm_head.scales, M->lm_head.mins};
-    for (int j = 0; j < 5; ++j) {
-        const int st = j == 4 ? 4 * s.L : j;
-        const StageShape ss = stage_shape(s, st);
-        P.geo[j] = plan_geom(ss.rows, ss.cols, j == 2, j == 2 ? s.FF : 0, K, kind);
-    }
-    int nl = 0;
-    for (int l0 = 0; l0 < s.L; l0 += PASS_LAYERS) {
-        P.layer0 = l0;
-        P.nlayers = std::min(PASS_LAYERS, s.L - l0);
-        P.with_lm = (l0 + P.nlayers == s.L) ? 1 : 0;
-        for (int i = 0; i < P.nlayers; ++i) {
-            const vq_layer& y = M->layers[l0 + i];
-            const vq_matrix* ms[7] = {&y.q, &y.k, &y.v, &y.o, &y.gate, &y.up, &y.down};
-            for (int m = 0; m < 7; ++m) P.m[i][m] = MatPtrs{ms[m]->qs, ms[m]->scales, ms[m]->mins};
-        }
-        const int s0 = 4 * l0, s1 = 4 * (l0 + P.nlayers) + P.with_lm;
-        if (streamed) {
-            if (events && 2 * nl + 1 < n_events) {
-                e = hipEventRecord((hipEvent_t)events[2 * nl], st);
-                if (e != hipSuccess) return hip_fail(e, "event record");
-            }
-            if (runs && nl < n_events / 2) runs[nl] = -1;
-            e = launch_stream_segment(P, st);
-            if (e != hipSuccess) return hip_fail(e, "stream pass launch");
-            if (events && 2 * nl + 1 < n_events) {
-                e = hipEventRecord((hipEvent_t)events[2 * nl + 1], st);
-                if (e != hipSuccess) return hip_fail(e, "event record");
-            }
-            ++nl;
-        } else if (persistent) {
-            if (events && 2 * nl + 1 < n_events) {
-                e = hipEventRecord((hipEvent_t)events[2 * nl], st);
-                if (e != hipSuccess) return hip_fail(e, "event record");
-            }
-            if (runs && nl < n_events / 2) runs[nl] = 0;
-            e = launch_pass_segment(P, mfma, st);
-            if (e != hipSuccess) return hip_fail(e, "persistent pass launch");
-            if (events && 2 * nl + 1 < n_events) {
-                e = hipEventRecord((hipEvent_t)events[2 * nl + 1], st);
-                if (e != hipSuccess) return hip_fail(e, "event record");
-            }
-            ++nl;
+    FlowArgs A;
+    fill_common(A, M, s, d, K, x0_f16, logits, base);
+    const int S = 4 * s.L + 1;
+    const bool staged = launch == VQ_LAUNCH_STAGED;
+    int nl = 0, base0 = 0, s0 = 0;
+    while (s0 < S) {
+        int s1;
+        if (staged) {
+            s1 = s0 + 1;
         } else {
-            for (int stage = s0; stage < s1; ++stage) {
-                StageArgs A;
-                build_stage(P, stage, A);
-                if (events && 2 * nl + 1 < n_events) {
-                    e = hipEventRecord((hipEvent_t)events[2 * nl], st);
-                    if (e != hipSuccess) return hip_fail(e, "event record");
-                }
-                const StageGeom& g = P.geo[stage == 4 * s.L ? 4 : stage & 3];
-                // measured: at K = 1 the conversion's latency on the critical path (input
-                // scales, conversion, count) costs more than the per-workgroup conversion
-                // it saves (27B pass 4.59 -> 5.16 ms); from K = 2 it pays (7.19 -> 6.80) on
-                // the large stages; the small q|k|v and o stages keep the inline
-                // conversion on both kernels (MFMA K = 8: 9.26 -> 9.02 ms)
-                if (P.xflag && !g.rk && (mfma || K >= PREP_MIN_K_VALU) && (stage == 4 * s.L || (stage & 3) >= 2))
-                    A.n_prep = N_PREP;
-                if (runs && nl < n_events / 2) runs[nl] = g.rk ? -g.R : g.cpw;
-                e = launch_stage(A, g, mfma, st);
-                if (e != hipSuccess) return hip_fail(e, "stage launch");
-                if (events && 2 * nl + 1 < n_events) {
-                    e = hipEventRecord((hipEvent_t)events[2 * nl + 1], st);
-                    if (e != hipSuccess) return hip_fail(e, "event record");
-                }
-                ++nl;
-            }
+            // the stages of FLOW_MAX_LAYERS layers (the last launch also runs the lm_head)
+            const int l0 = s0 / 4;
+            s1 = std::min(S, 4 * (l0 + FLOW_MAX_LAYERS));
+            if (s1 == 4 * s.L) s1 = S;
         }
+        fill_layers(A, M, std::min(s0 / 4, s.L - 1));
+        A.s_begin = s0;
+        A.s_end = s1;
+        for (int t = s0, b = base0; t < s1; ++t) {
+            A.base[t - s0] = b;
+            b = (b + stage_tiles(s, t)) % A.nwg;
+        }
+        if (events && 2 * nl + 1 < n_events) {
+            e = hipEventRecord((hipEvent_t)events[2 * nl], st);
+            if (e != hipSuccess) return hip_fail(e, "event record");
+        }
+        e = launch_flow(A, st);
+        if (e != hipSuccess) return hip_fail(e, "pass launch");
+        if (events && 2 * nl + 1 < n_events) {
+            e = hipEventRecord((hipEvent_t)events[2 * nl + 1], st);
+            if (e != hipSuccess) return hip_fail(e, "event record");
+        }
+        for (int t = s0; t < s1; ++t) base0 = (base0 + stage_tiles(s, t)) % A.nwg;
+        ++nl;
+        s0 = s1;
     }
     if (n_launches) *n_launches = nl;
     return VQ_OK;
 }
 
-int vq_decode_pass(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
-                   void* ws, size_t ws_bytes, void* stream) {
-    return decode_impl(M, x0_f16, K, logits, path, ws, ws_bytes, stream, nullptr, 0, nullptr, nullptr);
+int vq_decode_pass(const vq_model* M, const void* x0_f16, int32_t K, float* logits, void* ws, size_t ws_bytes,
+                   void* stream) {
+    return decode_impl(M, x0_f16, K, logits, VQ_LAUNCH_AUTO, ws, ws_bytes, stream, nullptr, 0, nullptr);
 }
 
-int vq_decode_pass_timed(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t path,
+int vq_decode_pass_timed(const vq_model* M, const void* x0_f16, int32_t K, float* logits, int32_t launch,
                          void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t n_events,
-                         int32_t* n_launches, int32_t* runs) {
-    if (!events || n_events < 2 * (4 * (M ? M->n_layers : 0) + 1))
-        return fail(VQ_ERR_ARG, "events must hold two HIP events per stage (begin, end)");
+                         int32_t* n_launches) {
+    if (!events || n_events < 2) return fail(VQ_ERR_ARG, "events must hold at least one (begin, end) pair");
     for (int i = 0; i < n_events; ++i)
         if (!events[i]) return fail(VQ_ERR_ARG, "event %d is NULL", i);
-    return decode_impl(M, x0_f16, K, logits, path, ws, ws_bytes, stream, events, n_events, n_launches, runs);
+    return decode_impl(M, x0_f16, K, logits, launch, ws, ws_bytes, stream, events, n_events, n_launches);
 }
 
 }  // extern "C"

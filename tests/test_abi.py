@@ -44,21 +44,19 @@ def _mat(fmt=vq.FMT_Q4_MIN, rows=64, cols=256, qs=FAKE, scales=FAKE, mins=FAKE):
     return vq.VqMatrix(fmt, rows, cols, 0, qs, scales, mins if fmt == vq.FMT_Q4_MIN else None)
 
 
-def _lin(W, K=4, x=FAKE, y=FAKE, dtype=vq.DTYPE_F32, path=vq.PATH_AUTO, ws=None, nbytes=0):
-    return vq.lib.vq_verify_linear(ctypes.byref(W), x, K, y, dtype, path, ws, nbytes, None)
+def _lin(W, K=4, x=FAKE, y=FAKE, dtype=vq.DTYPE_F32):
+    return vq.lib.vq_verify_linear(ctypes.byref(W), x, K, y, dtype, None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(K=0), vq.ERR_ARG),
     (dict(K=17), vq.ERR_ARG),
-    (dict(K=9, path=vq.PATH_VALU), vq.ERR_UNSUPPORTED),
-    (dict(path=7), vq.ERR_ARG),
     (dict(dtype=5), vq.ERR_ARG),
     (dict(x=None), vq.ERR_ARG),
     (dict(y=None), vq.ERR_ARG),
     (dict(x=FAKE + 8), vq.ERR_ARG),
-    (dict(), vq.ERR_WORKSPACE),
-    (dict(ws=FAKE, nbytes=16), vq.ERR_WORKSPACE),
+    (dict(y=FAKE + 2), vq.ERR_ARG),
+    (dict(y=FAKE + 1, dtype=vq.DTYPE_F16), vq.ERR_ARG),
 ])
 def test_linear_argument_errors(kw, code):
     assert _lin(_mat(), **kw) == code
@@ -78,22 +76,14 @@ def test_linear_bad_matrix(W):
 def test_linear_zero_rows_is_a_no_op():
     W = _mat(rows=0, qs=None, scales=None, mins=None)
     assert _lin(W, x=None, y=None) == vq.OK
-    assert vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), 4) == 0
 
 
-def test_linear_workspace_query():
-    W = _mat(rows=5120, cols=5120)
-    n = vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), 4)
-    # at least the split-K partials: 5 chunks x K x rows floats
-    assert n >= 5 * 4 * 5120 * 4
-    assert vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), 0) == 0
-    assert vq.lib.vq_workspace_bytes(9, ctypes.byref(W), 4) == 0
-    # one partial per 1024-column chunk and K column, whatever run length a kernel picks
-    for rows, cols in ((5120, 17408), (151936, 5120), (64, 1056)):
+def test_linear_needs_no_workspace():
+    for rows, cols in ((5120, 5120), (5120, 17408), (151936, 5120), (64, 1056)):
         W = _mat(rows=rows, cols=cols)
         for K in (1, 4, 16):
-            n = vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), K)
-            assert n >= -(-cols // 1024) * K * rows * 4, (rows, cols, K)
+            assert vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), K) == 0
+    assert vq.lib.vq_workspace_bytes(9, ctypes.byref(_mat()), 4) == 0
 
 
 def _acc(**kw):
@@ -142,19 +132,32 @@ def _model(L=2, H=256, KV=64, FF=512, V=1000, fmt=vq.FMT_Q4_MIN, bad=None):
     return vq.VqModel(L, 0, ctypes.cast(arr, ctypes.POINTER(vq.VqLayer)), _mat(fmt, V, H)), arr
 
 
+def _dec(M, K=4, x=FAKE, logits=FAKE, ws=FAKE, nbytes=0):
+    return vq.lib.vq_decode_pass(ctypes.byref(M), x, K, logits, ws, nbytes, None)
+
+
 def test_decode_validation_and_layout():
     M, keep = _model()
     n1 = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 1)
     n4 = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 4)
     assert 0 < n1 < n4
-    assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, 4, FAKE, 0, None, 0, None) == vq.ERR_WORKSPACE
-    assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, 0, FAKE, 0, FAKE, n4, None) == vq.ERR_ARG
-    assert vq.lib.vq_decode_pass(ctypes.byref(M), None, 4, FAKE, 0, FAKE, n4, None) == vq.ERR_ARG
+    assert _dec(M, ws=None, nbytes=0) == vq.ERR_WORKSPACE
+    assert _dec(M, nbytes=n4 - 1) == vq.ERR_WORKSPACE
+    assert _dec(M, ws=FAKE + 64, nbytes=n4) == vq.ERR_WORKSPACE          # not 256-byte aligned
+    assert _dec(M, K=0, nbytes=n4) == vq.ERR_ARG
+    assert _dec(M, K=17, nbytes=n4) == vq.ERR_ARG
+    assert _dec(M, x=None, nbytes=n4) == vq.ERR_ARG
+    assert _dec(M, x=FAKE + 8, nbytes=n4) == vq.ERR_ARG
+    assert _dec(M, logits=None, nbytes=n4) == vq.ERR_ARG
     Mb, kb = _model(bad=(1, "down"))
-    assert vq.lib.vq_decode_pass(ctypes.byref(Mb), FAKE, 4, FAKE, 0, FAKE, n4, None) == vq.ERR_ARG
+    assert _dec(Mb, nbytes=n4) == vq.ERR_ARG
     assert vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(Mb), 4) == 0
     Mu, ku = _model(H=96 * 4 + 32)   # hidden not a multiple of 64
-    assert vq.lib.vq_decode_pass(ctypes.byref(Mu), FAKE, 4, FAKE, 0, FAKE, n4, None) == vq.ERR_UNSUPPORTED
+    assert _dec(Mu, nbytes=n4) == vq.ERR_UNSUPPORTED
+    Mf, kf = _model(fmt=vq.FMT_Q4_MIN)
+    Mf.lm_head.format = vq.FMT_Q4
+    Mf.lm_head.mins = None
+    assert _dec(Mf, nbytes=n4) == vq.ERR_ARG                               # one format per stack
     # stage pointers: distinct, ordered, inside the workspace
     seen = []
     for s in range(9):
@@ -169,40 +172,6 @@ def test_decode_validation_and_layout():
     assert seen == sorted(seen) and len(set(seen)) == 9
     a, b = ctypes.c_void_p(), ctypes.c_void_p()
     assert vq.lib.vq_decode_stage_ptr(ctypes.byref(M), 4, FAKE, 9, ctypes.byref(a), ctypes.byref(b)) == vq.ERR_ARG
-
-
-@pytest.mark.parametrize("path,code", [
-    (vq.PATH_ROWS, vq.ERR_UNSUPPORTED),                           # row-strip stops at K = 4
-    (vq.LAUNCH_STAGED | vq.LAUNCH_PERSISTENT, vq.ERR_ARG),         # two launch modes
-    (32, vq.ERR_ARG),
-    (-4, vq.ERR_ARG),
-    (vq.PATH_VALU | vq.LAUNCH_PERSISTENT, vq.ERR_UNSUPPORTED),     # VALU stops at K = 8
-])
-def test_decode_path_and_launch_mode_errors(path, code):
-    M, keep = _model()
-    n9 = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 9)
-    assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, 9, FAKE, path, FAKE, n9, None) == code
-    assert vq.lib.vq_last_error()
-
-
-def test_stream_launch_limits():
-    M, keep = _model()
-    for K, path in ((3, vq.LAUNCH_STREAM), (1, vq.LAUNCH_STREAM | vq.PATH_MFMA),
-                    (1, vq.LAUNCH_STREAM | vq.PATH_ROWS), (1, vq.LAUNCH_STREAM)):
-        n = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), K)
-        assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, K, FAKE, path, FAKE, n, None) == vq.ERR_UNSUPPORTED
-    n = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 1)
-    assert vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, 1, FAKE, vq.LAUNCH_STREAM | vq.LAUNCH_STAGED, FAKE, n,
-                                 None) == vq.ERR_ARG
-
-
-def test_persistent_launch_rejects_the_row_strip_kernel():
-    M, keep = _model()
-    for K in (1, 4):
-        n = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), K)
-        rc = vq.lib.vq_decode_pass(ctypes.byref(M), FAKE, K, FAKE, vq.PATH_ROWS | vq.LAUNCH_PERSISTENT, FAKE, n, None)
-        assert rc == vq.ERR_UNSUPPORTED
-        assert b"row-strip" in vq.lib.vq_last_error()
 
 
 def test_decode_error_word_lies_in_the_workspace():
@@ -220,14 +189,19 @@ def test_decode_error_word_lies_in_the_workspace():
     assert vq.lib.vq_decode_error_word(ctypes.byref(M), 4, FAKE, None) == vq.ERR_ARG
 
 
-def test_decode_timed_needs_events():
+def test_decode_timed_argument_errors():
     M, keep = _model()
     n4 = vq.lib.vq_workspace_bytes(vq.OP_DECODE, ctypes.byref(M), 4)
-    ev = (ctypes.c_void_p * 17)(*([FAKE] * 17))
     nl = ctypes.c_int32(-1)
-    assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, 0, FAKE, n4, None, ev, 17,
-                                       ctypes.byref(nl), None) == vq.ERR_ARG   # 18 needed for 9 stages
-    ev2 = (ctypes.c_void_p * 18)(*([FAKE] * 17 + [None]))
-    assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, 0, FAKE, n4, None, ev2, 18,
-                                       ctypes.byref(nl), None) == vq.ERR_ARG   # a NULL event
+    ev = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    for launch in (1, 12, 16, -4):
+        assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, launch, FAKE, n4, None, ev, 2,
+                                           ctypes.byref(nl)) == vq.ERR_ARG
+    assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, 0, FAKE, n4, None, ev, 1,
+                                       ctypes.byref(nl)) == vq.ERR_ARG      # a pair is needed
+    ev2 = (ctypes.c_void_p * 2)(FAKE, None)
+    assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, 0, FAKE, n4, None, ev2, 2,
+                                       ctypes.byref(nl)) == vq.ERR_ARG      # a NULL event
+    assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, 0, FAKE, n4, None, None, 0,
+                                       ctypes.byref(nl)) == vq.ERR_ARG
     assert nl.value == -1

@@ -1,6 +1,9 @@
-"""GPU parity of vq_decode_pass: every stage's output against the oracle's linear map of
-the GPU's own stage input (the per-stage tolerance 1e-3 * sum|w x|), and every stage input
-against the oracle's glue of the previous GPU output (within one fp16 ulp)."""
+"""GPU parity of vq_decode_pass.  Every checked stage's input is compared with the oracle's
+glue applied to the GPU's previous output (bit-exact where the glue is a plain fp16
+rounding; within one fp16 ulp for silu(gate) * up, which the GPU evaluates in fp32), and
+its output with rho * (W x) of the oracle on the GPU's own stage input, rho in fp64 from
+the GPU's previous output, to the per-row tolerance 1e-3 * rho * sum|w x|.  The staged
+launch (one launch per stage) and the persistent one give identical bits."""
 import numpy as np
 import pytest
 
@@ -47,135 +50,118 @@ def _stage_io(model, shape, K, ws, logits, stage):
     return xin, out
 
 
-def _expected_input(shape, stage, prev_out):
-    """The oracle's glue applied to the previous stage's GPU output (double)."""
-    H, FF = shape.hidden, shape.ffn
-    j = stage % 4 if stage < 4 * shape.n_layers else 0
-    if j == 1:                                   # rho(q part of q|k|v)
-        return oracle.rho(prev_out[:, :H])
-    if j == 3:                                   # rho(silu(gate) * up)
-        K = prev_out.shape[0]
-        s = np.stack([oracle.silu_mul(prev_out[k, :FF], prev_out[k, FF:]) for k in range(K)])
-        return oracle.rho(s)
-    return oracle.rho(prev_out)                  # rho(o), rho(down)
+def _check_glue(shape, stage, xin, prev_out, what):
+    """The stage's fp16 input against the oracle's glue of the previous GPU output; returns
+    the oracle's rho for the stage's outputs."""
+    pk = (stage - 1) % 4
+    v, rho = oracle.stage_glue(prev_out, pk, shape.hidden, shape.ffn)
+    e16 = v.astype(np.float16)
+    if pk != oracle.STAGE_GU:
+        bad = int((xin.view(np.uint16) != e16.view(np.uint16)).sum())
+        assert bad == 0, f"{what}: {bad} inputs differ from the fp16 rounding of the previous output"
+    else:
+        diff = np.abs(xin.astype(np.float64) - e16.astype(np.float64))
+        ulp = np.spacing(np.abs(e16)).astype(np.float64)
+        off = int((diff > 0).sum())
+        assert not (diff > ulp).any(), f"{what}: silu(gate)*up inputs beyond one fp16 ulp ({off} differ)"
+        if off:
+            say(f"{what}: {off} of {diff.size} silu(gate)*up inputs one fp16 ulp off the oracle's rounding")
+    return rho
 
 
-def _check_glue(xin, expect, what):
-    e16 = expect.astype(np.float16)
-    diff = np.abs(xin.astype(np.float64) - e16.astype(np.float64))
-    ulp = np.spacing(np.abs(e16)).astype(np.float64)
-    bad = diff > ulp
-    say(f"{what}: glue inputs off the rounded oracle value: {int((diff > 0).sum())} "
-        f"(one ulp), beyond one ulp: {int(bad.sum())}")
-    assert not bad.any()
+def _check_stage(model, shape, fmt, seed, K, ws, logits, s, x0=None, prev=None, W=None, rows_pick=None, what=""):
+    xin, out = _stage_io(model, shape, K, ws, logits, s)
+    if s == 0:
+        assert np.array_equal(xin.view(np.uint16), x0.view(np.uint16)), f"{what}: stage 0 input is not x0"
+        rho = np.ones(K)
+    else:
+        if prev is None:
+            _, prev = _stage_io(model, shape, K, ws, logits, s - 1)
+        rho = _check_glue(shape, s, xin, prev, f"{what} stage {s}")
+    if W is None:
+        W = _stage_mats(shape, fmt, seed, s, rows_pick)
+    y_ref, a_ref = oracle.linear(W, xin, threads=8)
+    got = out if rows_pick is None else out[:, rows_pick]
+    check_rows(got, y_ref * rho[:, None], a_ref * rho[:, None], f"{what} stage {s}")
+    return out
 
 
-def _every_stage(shape, seed, fmt, K, path):
-    """One pass over the stack; every row of every stage checked against the oracle, the
-    workspace and the logits guarded against writes past their ends."""
+def _pass(model, shape, K, x0, launch):
+    """One pass into guarded workspace and logits buffers; returns (logits, ws)."""
     torch = need_gpu()
     import speculative_decoding_verification_bit_amd as vq
-    model = upload_model(shape, fmt, seed)
-    x0 = synth.activations(seed, K, shape.hidden)
     nws = model.workspace_bytes(K)
     ws, ws_whole = guarded_buffer(nws)
     nlg = K * shape.vocab * 4
     lg, lg_whole = guarded_buffer(nlg)
     logits = lg.view(torch.float32).view(K, shape.vocab)
-    say(f"every stage: {shape} fmt {fmt} K {K} path {path}")
-    vq.decode_pass(model, torch.from_numpy(x0).cuda(), logits, path=path, ws=ws)
+    _, _, nl = vq.decode_pass_launch(model, torch.from_numpy(x0).cuda(), logits, ws=ws, launch=launch)
     torch.cuda.synchronize()
-    check_guard(ws_whole, nws, "decode workspace")
-    check_guard(lg_whole, nlg, "logits")
-    assert model.barrier_error(K, ws) == 0
+    check_guard(ws_whole, nws, f"K {K} launch {launch}: decode workspace")
+    check_guard(lg_whole, nlg, f"K {K} launch {launch}: logits")
+    assert model.barrier_error(K, ws) == 0, f"K {K} launch {launch}: a wait timed out"
+    return logits, ws, nl
+
+
+def _every_stage(shape, seed, fmt, K):
+    """One pass per launch mode; every row of every stage against the oracle; the two
+    launch modes bitwise equal."""
+    import speculative_decoding_verification_bit_amd as vq
+    model = upload_model(shape, fmt, seed)
+    x0 = synth.activations(seed, K, shape.hidden)
+    say(f"every stage: {shape} fmt {fmt} K {K}")
+    lp, wp, nlp = _pass(model, shape, K, x0, vq.LAUNCH_AUTO)
+    ls, wsg, nls = _pass(model, shape, K, x0, vq.LAUNCH_STAGED)
+    assert nls == 4 * shape.n_layers + 1
     prev = None
     for s in range(4 * shape.n_layers + 1):
-        xin, out = _stage_io(model, shape, K, ws, logits, s)
-        if s == 0:
-            assert np.array_equal(xin.view(np.uint16), x0.view(np.uint16))
-        else:
-            _check_glue(xin, _expected_input(shape, s, prev), f"stage {s}")
-        W = _stage_mats(shape, fmt, seed, s)
-        y_ref, a_ref = oracle.linear(W, xin, threads=8)
-        check_rows(out, y_ref, a_ref, f"fmt {fmt} K {K} path {path} stage {s}")
-        prev = out
-    assert np.isfinite(logits.cpu().numpy()).all()
+        prev = _check_stage(model, shape, fmt, seed, K, wp, lp, s, x0=x0, prev=prev, what=f"fmt {fmt} K {K}")
+        for u, v in zip(_stage_io(model, shape, K, wp, lp, s), _stage_io(model, shape, K, wsg, ls, s)):
+            assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), f"stage {s}: staged and persistent differ"
+    assert np.isfinite(lp.cpu().numpy()).all()
 
 
-LAUNCHES = [4, 8]          # staged, persistent
-
-
-@pytest.mark.parametrize("launch", LAUNCHES)
 @pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_MXFP4])
-@pytest.mark.parametrize("K,path", [(1, 1), (2, 1), (3, 1), (4, 1), (8, 1), (4, 2), (16, 2), (1, 3), (4, 3)])
-def test_mini_model_every_stage(fmt, K, path, launch):
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 8, 16])
+def test_mini_model_every_stage(fmt, K):
     """A 2-layer stack (hidden 256, kv 64, ffn 512, vocab 1000): all rows of all stages."""
-    if path == 3 and launch == 8:
-        pytest.skip("the persistent launch rejects the row-strip kernel: run inside the cooperative "
-                    "pass kernel it made an illegal memory access at K = 4 whose cause was not found, "
-                    "so that combination is switched off (VQ_ERR_UNSUPPORTED, checked in test_abi)")
-    _every_stage(synth.SHAPE_MINI, 4, fmt, K, path | launch)
+    _every_stage(synth.SHAPE_MINI, 4, fmt, K)
 
 
-# Two layers whose stages split into several 1024-column chunks (split-K partials, tile
-# arrival counters), small enough for every row of every stage to be checked.
+# Two layers whose rows split into 5 and 16 column groups per compute wave
 SHAPE_MID = synth.ModelShape(n_layers=2, hidden=2048, kv_dim=256, ffn=5120, vocab=4000)
 
 
-@pytest.mark.parametrize("launch", LAUNCHES)
-@pytest.mark.parametrize("K,path", [(1, 0), (2, 1), (3, 0), (4, 1), (8, 1), (8, 2), (16, 2), (2, 3)])
-def test_mid_model_every_stage_split_k(K, path, launch):
-    """hidden 2048, kv 256, ffn 5120, vocab 4000: 2 and 5 column chunks per row."""
-    if path == 3 and launch == 8:
-        pytest.skip("the persistent launch does not run the row-strip kernel")
-    _every_stage(SHAPE_MID, 9, synth.FMT_Q4_MIN, K, path | launch)
+@pytest.mark.parametrize("K", [1, 4, 8, 16])
+def test_mid_model_every_stage(K):
+    """hidden 2048, kv 256, ffn 5120, vocab 4000 (a partial last lm_head tile)."""
+    _every_stage(SHAPE_MID, 9, synth.FMT_Q4_MIN, K)
 
 
-STREAM_OFF = ("the stream launch is switched off: its first GPU run (mini stack, K = 1, Q4 with mins) "
-              "made a memory fault whose cause is not found; host emulation of its addressing finds "
-              "every access in bounds")
+# More layers than one persistent launch carries (16): launch boundaries inside the pass
+SHAPE_DEEP = synth.ModelShape(n_layers=20, hidden=256, kv_dim=64, ffn=512, vocab=1000)
 
 
-@pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_MXFP4])
-@pytest.mark.parametrize("K", [1, 2])
-def test_stream_every_stage(fmt, K):
-    """The stream launch on the 2-layer mini stack and on the split-K one (hidden 2048,
-    ffn 5120): every row of every stage against the oracle."""
-    pytest.skip(STREAM_OFF)
+def test_deep_model_across_launches():
     import speculative_decoding_verification_bit_amd as vq
-    _every_stage(synth.SHAPE_MINI, 4, fmt, K, vq.LAUNCH_STREAM)
-    _every_stage(SHAPE_MID, 9, fmt, K, vq.LAUNCH_STREAM)
+    shape, seed, fmt, K = SHAPE_DEEP, 13, synth.FMT_Q4_MIN, 4
+    model = upload_model(shape, fmt, seed)
+    x0 = synth.activations(seed, K, shape.hidden)
+    lp, wp, nlp = _pass(model, shape, K, x0, vq.LAUNCH_AUTO)
+    ls, wsg, _ = _pass(model, shape, K, x0, vq.LAUNCH_STAGED)
+    assert nlp == 2, f"20 layers run as {nlp} persistent launches"
+    prev = None
+    for s in range(4 * shape.n_layers + 1):
+        prev = _check_stage(model, shape, fmt, seed, K, wp, lp, s, x0=x0, prev=prev, what="deep")
+    assert np.array_equal(lp.cpu().numpy(), ls.cpu().numpy())
 
 
-def test_stream_reproducible_and_close_to_staged():
-    """Two stream passes give identical bits; staged and stream logits agree to rounding."""
-    pytest.skip(STREAM_OFF)
-    torch = need_gpu()
-    import speculative_decoding_verification_bit_amd as vq
-    shape, seed, K = SHAPE_MID, 11, 1
-    model = upload_model(shape, synth.FMT_Q4_MIN, seed)
-    x0 = torch.from_numpy(synth.activations(seed, K, shape.hidden)).cuda()
-    a, _ = vq.decode_pass(model, x0, path=vq.LAUNCH_STREAM)
-    b, _ = vq.decode_pass(model, x0, path=vq.LAUNCH_STREAM)
-    c, _ = vq.decode_pass(model, x0, path=vq.LAUNCH_STAGED)
-    torch.cuda.synchronize()
-    assert torch.equal(a, b)
-    rel = float((a - c).abs().max() / c.abs().max())
-    say(f"stream vs staged logits: max |diff| / max |logit| = {rel:.2e}")
-    assert rel < 1e-3
-
-
-def test_27b_stack_stream_sampled_rows():
-    """The 27B-class stack through the stream launch, sampled rows against the oracle."""
-    pytest.skip(STREAM_OFF)
-
-
-@pytest.mark.parametrize("fmt,runs", [(synth.FMT_Q4_MIN, ((1, 0), (4, 0), (8, 0), (1, 3))),
-                                      (synth.FMT_MXFP4, ((16, 0),))])
-def test_27b_stack_sampled_rows(fmt, runs):
+@pytest.mark.parametrize("fmt,Ks", [(synth.FMT_Q4_MIN, (1, 4, 8)), (synth.FMT_MXFP4, (16,))])
+def test_27b_stack_sampled_rows(fmt, Ks):
     """The full 27B-class stack (64 layers, 5120 / 1024 / 17408, vocab 151936) in one pass;
     stages of layers 0, 31, 63 and the lm_head checked on 24 sampled rows each, every
-    checked stage's input against the glue of the previous output."""
+    checked stage's input against the glue of the previous output; at K = 1 the staged
+    launch gives the same bits."""
     torch = need_gpu()
     import speculative_decoding_verification_bit_amd as vq
     shape, seed = synth.SHAPE_27B, 0
@@ -192,48 +178,22 @@ def test_27b_stack_sampled_rows(fmt, runs):
         mats[s] = synth.Q4Matrix(fmt, len(pick), full.cols, full.qs[pick], full.scales[pick],
                                  None if full.mins is None else full.mins[pick])
         del full
-    runs_ws = []
-    for K, path in runs:
+    for K in Ks:
         x0 = synth.activations(seed, K, shape.hidden)
-        nws = model.workspace_bytes(K)
-        ws, ws_whole = guarded_buffer(nws)
-        logits, _ = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=path, ws=ws)
-        torch.cuda.synchronize()
-        check_guard(ws_whole, nws, f"K {K} path {path}: decode workspace")
-        if path not in (vq.PATH_ROWS, vq.LAUNCH_STREAM):   # persistent: tile kernels, same sums
-            # the other launch mode computes the same sums in the same order: identical bits
-            other = vq.LAUNCH_PERSISTENT | path
-            ws_st, st_whole = guarded_buffer(nws)
-            logits_st, _ = vq.decode_pass(model, torch.from_numpy(x0).cuda(), path=other, ws=ws_st)
-            torch.cuda.synchronize()
-            check_guard(st_whole, nws, f"K {K} path {other}: decode workspace")
-            assert model.barrier_error(K, ws_st) == 0
-            assert model.barrier_error(K, ws) == 0
-            if K < 4:
-                # VALU tile kernel in both modes: the same sums in the same order
-                assert torch.equal(logits, logits_st), f"K {K}: staged and persistent logits differ"
-                for s in stages:
-                    assert all(np.array_equal(u.view(np.uint8), v.view(np.uint8)) for u, v in
-                               zip(_stage_io(model, shape, K, ws, logits, s),
-                                   _stage_io(model, shape, K, ws_st, logits_st, s)))
-            else:
-                # MFMA: the staged launches convert each stage's input once, in workgroups
-                # of their own; their per-column input scales have been seen to differ from
-                # the persistent pass's by a few fp32 ulps, which flips an occasional fp16
-                # input and then grows along the 257-stage chain.  Each mode is checked
-                # stage by stage against the oracle instead.
-                runs_ws.append((ws_st, logits_st, "persistent"))
-            del st_whole
-        for w_, l_, nm in [(ws, logits, "staged")] + runs_ws:
+        logits, ws, nl = _pass(model, shape, K, x0, vq.LAUNCH_AUTO)
+        say(f"K {K}: {nl} persistent launches")
+        for s in stages:
+            _check_stage(model, shape, fmt, seed, K, ws, logits, s, x0=x0, W=mats[s], rows_pick=picks[s],
+                         what=f"27B fmt {fmt} K {K}")
+        if K in (1, 16):
+            ls, wsg, nls = _pass(model, shape, K, x0, vq.LAUNCH_STAGED)
+            assert nls == 4 * L + 1
+            assert torch.equal(logits, ls), f"K {K}: staged and persistent logits differ"
             for s in stages:
-                xin, out = _stage_io(model, shape, K, w_, l_, s)
-                if s > 0:
-                    _, prev = _stage_io(model, shape, K, w_, l_, s - 1)
-                    _check_glue(xin, _expected_input(shape, s, prev), f"K {K} {nm} stage {s}")
-                y_ref, a_ref = oracle.linear(mats[s], xin, threads=8)
-                check_rows(out[:, picks[s]], y_ref, a_ref, f"27B fmt {fmt} K {K} path {path} {nm} stage {s}")
-        runs_ws = []
-        del ws, ws_whole, logits
+                for u, v in zip(_stage_io(model, shape, K, ws, logits, s), _stage_io(model, shape, K, wsg, ls, s)):
+                    assert np.array_equal(u.view(np.uint8), v.view(np.uint8)), f"K {K} stage {s}"
+            del wsg, ls
+        del ws, logits
         torch.cuda.empty_cache()
 
 
@@ -280,25 +240,24 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(logits, ref_logits), f"replay {rep}: logits differ"
         assert torch.equal(out["tokens"], ref_tokens), f"replay {rep}: tokens differ"
+        assert model.barrier_error(K, ws) == 0
         del scratch
 
 
-@pytest.mark.parametrize("launch", LAUNCHES)
-def test_workspace_reuse_with_new_inputs(launch):
+def test_workspace_reuse_with_new_inputs():
     """A pass over a workspace that still holds another input's pass gives the same bits
-    as a pass in the same launch mode over a fresh workspace: nothing stale is read back
-    from the previous pass."""
+    as a pass over a fresh workspace: nothing stale is read back from the previous pass."""
     torch = need_gpu()
     import speculative_decoding_verification_bit_amd as vq
     shape, seed, K = synth.SHAPE_MINI, 7, 4
     model = upload_model(shape, synth.FMT_Q4_MIN, seed)
     xa = torch.from_numpy(synth.activations(seed, K, shape.hidden)).cuda()
     xb = torch.from_numpy(synth.activations(seed + 1, K, shape.hidden)).cuda()
-    logits, ws = vq.decode_pass(model, xa, path=launch)
+    logits, ws = vq.decode_pass(model, xa)
     for _ in range(3):
-        vq.decode_pass(model, xb, logits, path=launch, ws=ws)
+        vq.decode_pass(model, xb, logits, ws=ws)
         torch.cuda.synchronize()
-        ref, ws_ref = vq.decode_pass(model, xb, path=launch)
+        ref, ws_ref = vq.decode_pass(model, xb)
         torch.cuda.synchronize()
         assert torch.equal(logits, ref)
         for s in range(4 * shape.n_layers + 1):
