@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 2
+#define VQ_ABI_VERSION 3
 
 /* ------------------------------------------------------------------ status */
 #define VQ_OK 0
@@ -71,6 +71,43 @@ typedef struct vq_matrix {
     const void* mins;     /* device or NULL */
 } vq_matrix;
 
+/* --------------------------------------------------------------- tiled layout */
+/* The streaming kernels read weights in a tiled layout made once, at load time, from the
+ * plain planes above by vq_tile.  It keeps every 16-row x 128-column piece (a chunk) of
+ * a matrix contiguous, with its codes in the order the matrix cores take them and its
+ * rows' block scales (and mins) beside them, so that a chunk is two 16-byte loads per
+ * lane; the layout is private to the library and may change with VQ_ABI_VERSION.
+ * Rows past the matrix and columns past a multiple of 128 are stored as zero weights.
+ *   order VQ_ROWS_PLAIN : tile t holds rows 16t .. 16t+15
+ *   order VQ_ROWS_PAIR8 : rows [0, R/2) and [R/2, R) are two matrices of equal shape
+ *                         (gate and up); tile t holds rows 8t..8t+7 of each, so that a
+ *                         tile's outputs give silu(gate) * up directly.  R % 16 == 0. */
+#define VQ_ROWS_PLAIN 0
+#define VQ_ROWS_PAIR8 1
+
+typedef struct vq_tiled {
+    int32_t format;       /* VQ_FMT_*                                              */
+    int32_t rows;         /* output features, >= 0                                 */
+    int32_t cols;         /* input features, > 0, multiple of 32                   */
+    int32_t order;        /* VQ_ROWS_*                                             */
+    const void* data;     /* device, vq_tiled_bytes() bytes, 256-byte aligned      */
+} vq_tiled;
+
+/* Bytes of a tiled matrix (0 for invalid arguments). */
+size_t vq_tiled_bytes(int32_t format, int32_t rows, int32_t cols);
+
+/*
+ * vq_tile -- write the plain matrix `src` into rows [row0, row0 + src->rows) of the tiled
+ * matrix `dst` (same format and cols).  One call fills a whole matrix (row0 = 0); a
+ * stacked matrix such as q|k|v is filled by one call per part (row0 = 0, H, H + KV;
+ * every part but the last a multiple of 16 rows), a VQ_ROWS_PAIR8 one by a call for each
+ * half (row0 = 0 and rows / 2).  Rows of dst outside the range are left as they are,
+ * except the zero rows past dst->rows in the last tile, which every call writes.
+ * Errors: VQ_ERR_ARG for bad descriptors, mismatched format or cols, a range outside
+ * dst, a misaligned row0 or a NULL pointer; VQ_ERR_HIP.
+ */
+int vq_tile(const vq_matrix* src, const vq_tiled* dst, int32_t row0, void* stream);
+
 /* Output element type of vq_verify_linear. */
 #define VQ_DTYPE_F32 0
 #define VQ_DTYPE_F16 1
@@ -86,21 +123,24 @@ typedef struct vq_matrix {
  * "How speculative decoding gets past a per-token wall"); streaming the weights is what
  * bounds the pass (same page, section "The wall").
  *
- *   W       : host descriptor of a device matrix (see above)
+ *   W       : host descriptor of a tiled device matrix (order VQ_ROWS_PLAIN)
  *   x_f16   : device fp16 [K][cols]  (row k = activation column k of the window)
  *   K       : 1..16
  *   y       : device [K][rows], fp32 or fp16 (y_dtype); y[k][r] = sum_j w[r][j] x[k][j]
+ *   ws      : device workspace >= vq_workspace_bytes(VQ_OP_LINEAR, W, K), 256-byte
+ *             aligned: partial sums of tiles that several workgroups share
  * Arithmetic: codes widen exactly to fp16 (q = n - 8, or the E2M1 value), products with
  * the fp16 activations are exact, sums are fp32; the block scale multiplies the fp32 sum
  * of its block and the min the fp32 sum of the block's activations, so no weight is
- * rounded.  The result is deterministic (fixed summation order).
- * Needs no workspace.  Errors: VQ_ERR_ARG for NULL pointers, K outside 1..16, cols not a
- * positive multiple of 32, rows < 0, misaligned pointers (x and qs/scales/mins 16-byte,
- * y its element size), an unknown format/dtype or mins inconsistent with the format;
- * VQ_ERR_HIP.  rows == 0 is valid and enqueues nothing.
+ * rounded.  Summation orders depend only on the shapes and the device's compute-unit
+ * count, so results are reproducible bit for bit.
+ * Errors: VQ_ERR_ARG for NULL pointers, K outside 1..16, cols not a positive multiple of
+ * 32, rows < 0, misaligned pointers (x 16-byte, y its element size), an unknown
+ * format/dtype/order; VQ_ERR_UNSUPPORTED for a shape the split cannot handle;
+ * VQ_ERR_WORKSPACE; VQ_ERR_HIP.  rows == 0 is valid and enqueues nothing.
  */
-int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y,
-                     int32_t y_dtype, void* stream);
+int vq_verify_linear(const vq_tiled* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- acceptance */
 #define VQ_MODE_GREEDY 0      /* accept x_i while it equals the target argmax            */
@@ -162,14 +202,17 @@ int vq_verify_accept(const vq_accept_desc* d, void* ws, size_t ws_bytes, void* s
 
 /* ------------------------------------------------------------- decode pass */
 typedef struct vq_layer {
-    vq_matrix q, k, v, o, gate, up, down;
+    vq_tiled qkv;              /* [H + 2 KV][H]: q, k, v stacked (VQ_ROWS_PLAIN)        */
+    vq_tiled o;                /* [H][H]                                                */
+    vq_tiled gu;               /* [2 FF][H]: gate, up (VQ_ROWS_PAIR8)                    */
+    vq_tiled down;             /* [H][FF]                                               */
 } vq_layer;
 
 typedef struct vq_model {
     int32_t n_layers;          /* >= 1                                                  */
     int32_t reserved;          /* must be 0                                             */
     const vq_layer* layers;    /* HOST array [n_layers] of device-matrix descriptors    */
-    vq_matrix lm_head;         /* [vocab][hidden]                                       */
+    vq_tiled lm_head;          /* [vocab][hidden]                                       */
 } vq_model;
 
 /*
@@ -186,9 +229,10 @@ typedef struct vq_model {
  * that every output is what a unit-RMS input would give.  The first x_attn is x0 and
  * stage 0 is not scaled.
  *
- *   M      : host model descriptor; hidden = q.cols, every layer the same shapes;
- *            q: [H][H], k, v: [KV][H], o: [H][H], gate, up: [FF][H], down: [H][FF],
- *            lm_head: [V][H]; all matrices of one format; H, KV, FF multiples of 64
+ *   M      : host model descriptor; H = qkv.cols, FF = down.cols, every layer the same
+ *            shapes (qkv: [H + 2 KV][H], o: [H][H], gu: [2 FF][H] in VQ_ROWS_PAIR8 order,
+ *            down: [H][FF], lm_head: [V][H]); all matrices of one format; H, KV, FF
+ *            multiples of 64
  *   x0_f16 : device fp16 [K][H]
  *   logits : device f32 [K][V]
  *   ws     : device workspace >= vq_workspace_bytes(VQ_OP_DECODE, M, K); after the call
@@ -246,12 +290,11 @@ int vq_decode_stage_ptr(const vq_model* M, int32_t K, void* ws, int32_t stage,
                         void** in_f16, void** out_f32);
 
 /* ---------------------------------------------------------------- queries */
-#define VQ_OP_LINEAR 0         /* desc = const vq_matrix*       */
+#define VQ_OP_LINEAR 0         /* desc = const vq_tiled*        */
 #define VQ_OP_ACCEPT 1         /* desc = const vq_accept_desc*  */
 #define VQ_OP_DECODE 2         /* desc = const vq_model*        */
 
-/* Workspace bytes needed by an op for the given descriptor and K (0 on bad input; 0 for
- * VQ_OP_LINEAR, which needs none). */
+/* Workspace bytes needed by an op for the given descriptor and K (0 on bad input). */
 size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K);
 
 /* Static text for a status code. */

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "vq_internal.h"
 
 namespace vq {
@@ -43,6 +45,106 @@ int check_matrix(const vq_matrix* W, const char* name) {
     return VQ_OK;
 }
 
+int check_tiled(const vq_tiled* W, const char* name) {
+    if (!W) return fail(VQ_ERR_ARG, "%s: NULL matrix descriptor", name);
+    if (W->format < VQ_FMT_Q4 || W->format > VQ_FMT_MXFP4)
+        return fail(VQ_ERR_ARG, "%s: unknown format %d", name, W->format);
+    if (W->order != VQ_ROWS_PLAIN && W->order != VQ_ROWS_PAIR8)
+        return fail(VQ_ERR_ARG, "%s: unknown row order %d", name, W->order);
+    if (W->rows < 0) return fail(VQ_ERR_ARG, "%s: rows %d < 0", name, W->rows);
+    if (W->cols <= 0 || W->cols % 32)
+        return fail(VQ_ERR_ARG, "%s: cols %d is not a positive multiple of 32", name, W->cols);
+    if (W->order == VQ_ROWS_PAIR8 && W->rows % 16)
+        return fail(VQ_ERR_ARG, "%s: a VQ_ROWS_PAIR8 matrix needs rows %% 16 == 0 (rows %d)", name, W->rows);
+    if (tiled_bytes(W->format, W->rows, W->cols) >= ((size_t)1 << 32))
+        return fail(VQ_ERR_UNSUPPORTED, "%s: tiled matrix of 4 GiB or more", name);
+    if (W->rows == 0) return VQ_OK;
+    if (!W->data) return fail(VQ_ERR_ARG, "%s: NULL data", name);
+    if (!aligned(W->data, 256)) return fail(VQ_ERR_ARG, "%s: data must be 256-byte aligned", name);
+    return VQ_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ the split
+
+void lds_plan(int K, int* nsp, int* pbytes, int* ring_off, int* xcap) {
+    *pbytes = 256 * ((K + 3) / 4);
+    *nsp = K <= 8 ? 4 : 2;
+    const int ring = *nsp * FLOW_NCW * *pbytes;
+    *ring_off = (FLOW_CTRL_OFF - ring) & ~255;
+    *xcap = *ring_off;
+}
+
+namespace {
+int wg_of_host(const KindPlan& P, long c) {
+    const long big = (long)P.r * (P.q + 1);
+    return (int)(c < big ? c / (P.q + 1) : P.r + (c - big) / P.q);
+}
+int window_of(const KindPlan& P, long c) {
+    const long span = (long)P.T * P.gw;
+    const long w = c / span;
+    return (int)(w < P.nwin - 1 ? w : P.nwin - 1);
+}
+}  // namespace
+
+bool make_plan(KindPlan& P, int fmt, int K, int rows, int cols, int tiles, int nwg, int xcap) {
+    P = KindPlan{};
+    P.rows = rows;
+    P.cols = cols;
+    P.T = tiles;
+    P.G = (cols + GROUP_COLS - 1) / GROUP_COLS;
+    P.cb = chunk_bytes(fmt);
+    const int xs1 = P.G * 256 + 16;
+    if ((long)K * xs1 <= xcap) {
+        P.nwin = 1;
+        P.gw = P.glast = P.G;
+        P.xs = xs1;
+    } else {
+        const int half = (xcap / 2) & ~15;
+        const int gmax = (half / K - 16) / 256;
+        if (gmax < 1) return false;
+        P.nwin = (P.G + gmax - 1) / gmax;
+        P.gw = (P.G + P.nwin - 1) / P.nwin;
+        P.glast = P.G - (P.nwin - 1) * P.gw;
+        P.xs = P.gw * 256 + 16;
+        if (P.glast < 1) return false;
+    }
+    const long N = (long)P.T * P.G;
+    if (N <= 0 || N >= (1L << 31)) return false;
+    // every workgroup's range holds at least a whole unit (a tile's chunks in one window),
+    // so a unit is shared by two workgroups at most
+    P.nwe = (int)std::max(1L, std::min((long)nwg, N / P.gw));
+    P.q = (int)(N / P.nwe);
+    P.r = (int)(N % P.nwe);
+    // a range spans at most two windows (two activation buffers)
+    if (P.nwin > 1) {
+        for (int w = 0; w < P.nwe; ++w) {
+            const long lo = (long)w * P.q + std::min(w, P.r);
+            const long hi = lo + P.q + (w < P.r ? 1 : 0);
+            if (window_of(P, hi - 1) - window_of(P, lo) > 1) return false;
+        }
+        // split tiles each workgroup finishes: the holder of the last chunk of the tile's
+        // unit in window t mod nwin
+        std::vector<int> pend(P.nwe, 0);
+        for (int t = 0; t < P.T; ++t) {
+            const int wf = t % P.nwin;
+            const int gl = wf == P.nwin - 1 ? P.glast : P.gw;
+            const long lf = (long)wf * P.T * P.gw + (long)(t + 1) * gl - 1;
+            if (++pend[wg_of_host(P, lf)] > FLOW_PEND_MAX) return false;
+        }
+    }
+    return true;
+}
+
+size_t plan_parts_floats(const KindPlan& P, int pbytes) {
+    const size_t slots = P.nwin == 1 ? 2 * (size_t)P.nwe : 2 * (size_t)P.nwin * P.T;
+    return slots * (size_t)(pbytes / 4);
+}
+size_t plan_counters(const KindPlan& P) { return P.nwin == 1 ? (size_t)P.nwe : (size_t)P.T; }
+
+namespace {
+
 // ---------------------------------------------------------------- decode layout
 
 struct Shapes {
@@ -54,78 +156,111 @@ int check_model(const vq_model* M, Shapes* s) {
     if (M->n_layers < 1 || !M->layers) return fail(VQ_ERR_ARG, "model needs n_layers >= 1 and layers");
     if (M->reserved != 0) return fail(VQ_ERR_ARG, "model reserved field must be 0");
     const vq_layer& l0 = M->layers[0];
-    s->H = l0.q.cols;
-    s->KV = l0.k.rows;
-    s->FF = l0.gate.rows;
+    s->H = l0.qkv.cols;
+    s->KV = (l0.qkv.rows - s->H) / 2;
+    s->FF = l0.down.cols;
     s->V = M->lm_head.rows;
     s->L = M->n_layers;
-    s->fmt = l0.q.format;
-    if (s->H % 64 || s->KV % 64 || s->FF % 64 || s->H <= 0 || s->KV <= 0 || s->FF <= 0)
+    s->fmt = l0.qkv.format;
+    if (s->H % 64 || s->KV % 64 || s->FF % 64 || s->H <= 0 || s->KV <= 0 || s->FF <= 0 ||
+        l0.qkv.rows != s->H + 2 * s->KV)
         return fail(VQ_ERR_UNSUPPORTED, "decode pass needs hidden, kv and ffn sizes that are multiples of 64");
     if (s->V < 1) return fail(VQ_ERR_ARG, "lm_head needs rows >= 1");
     for (int l = 0; l < M->n_layers; ++l) {
         const vq_layer& y = M->layers[l];
-        const vq_matrix* ms[7] = {&y.q, &y.k, &y.v, &y.o, &y.gate, &y.up, &y.down};
-        const int rr[7] = {s->H, s->KV, s->KV, s->H, s->FF, s->FF, s->H};
-        const int cc[7] = {s->H, s->H, s->H, s->H, s->H, s->H, s->FF};
-        static const char* nm[7] = {"q", "k", "v", "o", "gate", "up", "down"};
-        for (int i = 0; i < 7; ++i) {
+        const vq_tiled* ms[4] = {&y.qkv, &y.o, &y.gu, &y.down};
+        const int rr[4] = {s->H + 2 * s->KV, s->H, 2 * s->FF, s->H};
+        const int cc[4] = {s->H, s->H, s->H, s->FF};
+        const int oo[4] = {VQ_ROWS_PLAIN, VQ_ROWS_PLAIN, VQ_ROWS_PAIR8, VQ_ROWS_PLAIN};
+        static const char* nm[4] = {"qkv", "o", "gu", "down"};
+        for (int i = 0; i < 4; ++i) {
             char buf[48];
             snprintf(buf, sizeof buf, "layer %d %s", l, nm[i]);
-            int rc = check_matrix(ms[i], buf);
+            int rc = check_tiled(ms[i], buf);
             if (rc) return rc;
-            if (ms[i]->rows != rr[i] || ms[i]->cols != cc[i] || ms[i]->format != s->fmt)
-                return fail(VQ_ERR_ARG, "%s: shape %dx%d fmt %d, expected %dx%d fmt %d", buf, ms[i]->rows,
-                            ms[i]->cols, ms[i]->format, rr[i], cc[i], s->fmt);
+            if (ms[i]->rows != rr[i] || ms[i]->cols != cc[i] || ms[i]->format != s->fmt || ms[i]->order != oo[i])
+                return fail(VQ_ERR_ARG, "%s: shape %dx%d fmt %d order %d, expected %dx%d fmt %d order %d", buf,
+                            ms[i]->rows, ms[i]->cols, ms[i]->format, ms[i]->order, rr[i], cc[i], s->fmt, oo[i]);
         }
     }
-    int rc = check_matrix(&M->lm_head, "lm_head");
+    int rc = check_tiled(&M->lm_head, "lm_head");
     if (rc) return rc;
-    if (M->lm_head.cols != s->H || M->lm_head.format != s->fmt)
-        return fail(VQ_ERR_ARG, "lm_head: shape or format inconsistent with the layers");
+    if (M->lm_head.cols != s->H || M->lm_head.format != s->fmt || M->lm_head.order != VQ_ROWS_PLAIN)
+        return fail(VQ_ERR_ARG, "lm_head: shape, format or order inconsistent with the layers");
+    return VQ_OK;
+}
+
+// The split of every stage kind of a pass with K columns.
+struct PassPlan {
+    KindPlan kp[5];
+    int nsp, pbytes, ring_off, xcap;
+    size_t parts_floats, counters;
+};
+
+int pass_plan(const Shapes& s, int K, int nwg, PassPlan* pp) {
+    lds_plan(K, &pp->nsp, &pp->pbytes, &pp->ring_off, &pp->xcap);
+    const int rows[5] = {s.H + 2 * s.KV, s.H, 2 * s.FF, s.H, s.V};
+    const int cols[5] = {s.H, s.H, s.H, s.FF, s.H};
+    pp->parts_floats = 0;
+    pp->counters = 0;
+    for (int k = 0; k < 5; ++k) {
+        const int tiles = (rows[k] + TILE_ROWS - 1) / TILE_ROWS;
+        if (!make_plan(pp->kp[k], s.fmt, K, rows[k], cols[k], tiles, nwg, pp->xcap))
+            return fail(VQ_ERR_UNSUPPORTED, "stage kind %d (%dx%d) cannot be split over %d workgroups at K %d", k,
+                        rows[k], cols[k], nwg, K);
+        // rho of stage kind k normalises the previous stage's output; the first stage's is set per stage
+        pp->kp[k].n_in = k == SK_DOWN ? s.FF : s.H;
+        pp->kp[k].stats = k == SK_LM ? 0 : 1;
+        pp->parts_floats = std::max(pp->parts_floats, plan_parts_floats(pp->kp[k], pp->pbytes));
+        pp->counters = std::max(pp->counters, plan_counters(pp->kp[k]));
+    }
     return VQ_OK;
 }
 
 // Workspace of a decode pass.  Every buffer a later stage reads is written once per pass
-// at its own 256-byte aligned place: per layer and stage the fp16 input in natural order
-// (xn, kept for inspection), the same input in the MFMA pair order (xp, what the next
-// stage reads for the Q4 formats) and the fp32 output (y); the lm_head's input; per stage
-// the per-workgroup sums of squares; the completion counters and the error word.
+// at its own 256-byte aligned place: per layer and stage the fp16 input (x) and the fp32
+// output (y); the lm_head's input; per stage the per-workgroup sums of squares; the
+// split-tile partial sums; then, zeroed at the start of every pass, the split-tile
+// counters, the completion counters and the error word.
 struct DecodeLayout {
-    size_t off_xn[4], off_xp[4], off_y[4];
+    size_t off_x[4], off_y[4];
     size_t layer_bytes;
-    size_t off_fxn, off_fxp;
+    size_t off_fx;
     size_t off_stats, stats_stride;
+    size_t off_parts;
+    size_t off_cnt;
     size_t off_sync;
-    int sync_words;            // completion counters, then the error word
+    size_t zero_words;         // from off_cnt: counters, completion counters, error word
+    int sync_words;
     size_t total;
 };
 
-DecodeLayout decode_layout(const Shapes& s, int K) {
+DecodeLayout decode_layout(const Shapes& s, int K, const PassPlan& pp) {
     DecodeLayout d{};
     size_t p = 0;
     const int rows[4] = {s.H + 2 * s.KV, s.H, 2 * s.FF, s.H};
     const int cols[4] = {s.H, s.H, s.H, s.FF};
     for (int j = 0; j < 4; ++j) {
-        d.off_xn[j] = p;
-        p += align_up((size_t)K * cols[j] * 2, 256);
-        d.off_xp[j] = p;
+        d.off_x[j] = p;
         p += align_up((size_t)K * cols[j] * 2, 256);
         d.off_y[j] = p;
         p += align_up((size_t)K * rows[j] * 4, 256);
     }
     d.layer_bytes = p;
     p = d.layer_bytes * s.L;
-    d.off_fxn = p;
-    p += align_up((size_t)K * s.H * 2, 256);
-    d.off_fxp = p;
+    d.off_fx = p;
     p += align_up((size_t)K * s.H * 2, 256);
     d.off_stats = p;
     d.stats_stride = align_up((size_t)FLOW_MAX_WG * K, 64);
     p += d.stats_stride * 4 * (size_t)(4 * s.L);
+    d.off_parts = p;
+    p += align_up(pp.parts_floats * 4, 256);
+    d.off_cnt = p;
+    p += align_up(pp.counters * 4, 256);
     d.off_sync = p;
     d.sync_words = (4 * s.L + 1) * DONE_WORDS + DONE_STRIDE;
     p += align_up((size_t)d.sync_words * 4, 256);
+    d.zero_words = (p - d.off_cnt) / 4;
     d.total = p;
     return d;
 }
@@ -134,50 +269,67 @@ int* err_word(const DecodeLayout& d, char* ws) {
     return (int*)(ws + d.off_sync) + (d.sync_words - DONE_STRIDE);
 }
 
-// Tiles of 16 rows per stage (gate|up: 8 gate + 8 up rows).
-int stage_tiles(const Shapes& s, int st) {
-    if (st == 4 * s.L) return (s.V + 15) / 16;
-    switch (st & 3) {
-        case 0: return (s.H + 2 * s.KV) / 16;
-        case 1: return s.H / 16;
-        case 2: return s.FF / 8;
-        default: return s.H / 16;
-    }
-}
-
-void fill_common(FlowArgs& A, const vq_model* M, const Shapes& s, const DecodeLayout& d, int K,
-                 const void* x0, float* logits, char* ws) {
+void fill_common(FlowArgs& A, const Shapes& s, const DecodeLayout& d, const PassPlan& pp, int K, int nwg,
+                 const vq_model* M, const void* x0, float* logits, char* ws) {
     A = FlowArgs{};
     A.fmt = s.fmt;
     A.K = K;
     A.H = s.H; A.KV = s.KV; A.FF = s.FF; A.V = s.V; A.L = s.L;
-    A.nwg = flow_grid();
+    A.nwg = nwg;
+    A.nsp = pp.nsp;
+    A.pbytes = pp.pbytes;
+    A.ring_off = pp.ring_off;
+    A.xoff1 = (pp.xcap / 2) & ~15;
     A.x0 = (const uint16_t*)x0;
     A.out = logits;
     A.ws = ws;
     A.layer_bytes = d.layer_bytes;
     for (int j = 0; j < 4; ++j) {
-        A.off_xn[j] = d.off_xn[j];
-        A.off_xp[j] = d.off_xp[j];
+        A.off_x[j] = d.off_x[j];
         A.off_y[j] = d.off_y[j];
     }
-    A.off_fxn = d.off_fxn;
-    A.off_fxp = d.off_fxp;
+    A.off_fx = d.off_fx;
     A.off_stats = d.off_stats;
     A.stats_stride = d.stats_stride;
+    A.parts = (float*)(ws + d.off_parts);
+    A.cnt = (unsigned*)(ws + d.off_cnt);
     A.done = (unsigned*)(ws + d.off_sync);
     A.err = err_word(d, ws);
-    A.lm = MatPtr{(const uint8_t*)M->lm_head.qs, M->lm_head.scales, (const uint16_t*)M->lm_head.mins};
+    for (int k = 0; k < 5; ++k) A.kp[k] = pp.kp[k];
+    A.lm = (const uint8_t*)M->lm_head.data;
 }
 
 void fill_layers(FlowArgs& A, const vq_model* M, int l0) {
     A.l0 = l0;
     for (int i = 0; i < FLOW_MAX_LAYERS && l0 + i < M->n_layers; ++i) {
         const vq_layer& y = M->layers[l0 + i];
-        const vq_matrix* ms[7] = {&y.q, &y.k, &y.v, &y.o, &y.gate, &y.up, &y.down};
-        for (int m = 0; m < 7; ++m)
-            A.m[i][m] = MatPtr{(const uint8_t*)ms[m]->qs, ms[m]->scales, (const uint16_t*)ms[m]->mins};
+        A.w[i][0] = (const uint8_t*)y.qkv.data;
+        A.w[i][1] = (const uint8_t*)y.o.data;
+        A.w[i][2] = (const uint8_t*)y.gu.data;
+        A.w[i][3] = (const uint8_t*)y.down.data;
     }
+}
+
+// Workspace of a linear map: split-tile partials, then the counters and an error word
+// (zeroed by every call).
+struct LinearLayout {
+    KindPlan kp;
+    int nsp, pbytes, ring_off, xcap;
+    size_t off_cnt, zero_words, total;
+};
+
+int linear_layout(const vq_tiled* W, int K, int nwg, LinearLayout* L) {
+    lds_plan(K, &L->nsp, &L->pbytes, &L->ring_off, &L->xcap);
+    if (!make_plan(L->kp, W->format, K, W->rows, W->cols, (W->rows + TILE_ROWS - 1) / TILE_ROWS, nwg, L->xcap))
+        return fail(VQ_ERR_UNSUPPORTED, "a %dx%d matrix cannot be split over %d workgroups at K %d", W->rows, W->cols,
+                    nwg, K);
+    L->kp.n_in = 0;
+    L->kp.stats = 0;
+    L->off_cnt = align_up(plan_parts_floats(L->kp, L->pbytes) * 4, 256);
+    const size_t words = plan_counters(L->kp) + DONE_STRIDE;
+    L->zero_words = words;
+    L->total = L->off_cnt + align_up(words * 4, 256);
+    return VQ_OK;
 }
 
 }  // namespace
@@ -204,7 +356,15 @@ const char* vq_status_string(int32_t status) {
 
 size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K) {
     if (!desc) return 0;
-    if (op == VQ_OP_LINEAR) return 0;            // the linear map needs no workspace
+    if (K < 1 || K > VQ_MAX_K) return 0;
+    if (op == VQ_OP_LINEAR) {
+        const vq_tiled* W = (const vq_tiled*)desc;
+        if (check_tiled(W, "W")) return 0;
+        if (W->rows == 0) return 256;
+        LinearLayout L;
+        if (linear_layout(W, K, flow_grid(), &L)) return 0;
+        return L.total;
+    }
     if (op == VQ_OP_ACCEPT) {
         const vq_accept_desc* d = (const vq_accept_desc*)desc;
         if (d->W < 0 || d->K < 1 || d->K > VQ_MAX_K) return 0;
@@ -212,22 +372,63 @@ size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K) {
     }
     if (op == VQ_OP_DECODE) {
         Shapes s;
-        if (check_model((const vq_model*)desc, &s) || K < 1 || K > VQ_MAX_K) return 0;
-        return decode_layout(s, K).total;
+        PassPlan pp;
+        if (check_model((const vq_model*)desc, &s) || pass_plan(s, K, flow_grid(), &pp)) return 0;
+        return decode_layout(s, K, pp).total;
     }
     return 0;
 }
 
-int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype, void* stream) {
+size_t vq_tiled_bytes(int32_t format, int32_t rows, int32_t cols) {
+    if (format < VQ_FMT_Q4 || format > VQ_FMT_MXFP4 || rows < 0 || cols <= 0 || cols % 32) return 0;
+    return tiled_bytes(format, rows, cols);
+}
+
+int vq_tile(const vq_matrix* src, const vq_tiled* dst, int32_t row0, void* stream) {
     g_err[0] = 0;
-    int rc = check_matrix(W, "W");
+    int rc = check_matrix(src, "src");
     if (rc) return rc;
+    rc = check_tiled(dst, "dst");
+    if (rc) return rc;
+    if (src->format != dst->format || src->cols != dst->cols)
+        return fail(VQ_ERR_ARG, "src and dst differ in format or cols");
+    if (row0 < 0 || (long)row0 + src->rows > dst->rows)
+        return fail(VQ_ERR_ARG, "rows [%d, %d) outside dst (%d rows)", row0, row0 + src->rows, dst->rows);
+    if (dst->order == VQ_ROWS_PAIR8) {
+        const int half = dst->rows / 2;
+        if (!((row0 == 0 || row0 == half) && src->rows == half))
+            return fail(VQ_ERR_ARG, "a VQ_ROWS_PAIR8 matrix is filled one half (%d rows) at a time", half);
+    } else if (row0 % TILE_ROWS) {
+        return fail(VQ_ERR_ARG, "row0 %d is not a multiple of %d", row0, TILE_ROWS);
+    }
+    if (src->rows == 0) return VQ_OK;
+    hipError_t e = launch_tile(*src, (uint8_t*)dst->data, dst->rows, dst->order, row0, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "tile launch");
+    return VQ_OK;
+}
+
+int vq_verify_linear(const vq_tiled* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype, void* ws,
+                     size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = check_tiled(W, "W");
+    if (rc) return rc;
+    if (W->order != VQ_ROWS_PLAIN) return fail(VQ_ERR_ARG, "W must be in VQ_ROWS_PLAIN order");
     if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
     if (y_dtype != VQ_DTYPE_F32 && y_dtype != VQ_DTYPE_F16) return fail(VQ_ERR_ARG, "unknown y_dtype %d", y_dtype);
     if (W->rows == 0) return VQ_OK;
     if (!x_f16 || !y) return fail(VQ_ERR_ARG, "NULL x or y");
     if (!aligned(x_f16, 16)) return fail(VQ_ERR_ARG, "x must be 16-byte aligned");
     if (!aligned(y, y_dtype == VQ_DTYPE_F32 ? 4 : 2)) return fail(VQ_ERR_ARG, "y is misaligned");
+    const int nwg = flow_grid();
+    LinearLayout L;
+    rc = linear_layout(W, K, nwg, &L);
+    if (rc) return rc;
+    if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+        return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", L.total, ws_bytes);
+    char* base = (char*)ws;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_zero_u32((unsigned*)(base + L.off_cnt), L.zero_words, st);
+    if (e != hipSuccess) return hip_fail(e, "counter reset launch");
     FlowArgs A{};
     A.fmt = W->format;
     A.K = K;
@@ -238,11 +439,19 @@ int vq_verify_linear(const vq_matrix* W, const void* x_f16, int32_t K, void* y, 
     A.y_dtype = y_dtype;
     A.s_begin = 0;
     A.s_end = 1;
-    A.nwg = std::min(flow_grid(), (W->rows + 15) / 16);
+    A.nwg = L.kp.nwe;
+    A.nsp = L.nsp;
+    A.pbytes = L.pbytes;
+    A.ring_off = L.ring_off;
+    A.xoff1 = (L.xcap / 2) & ~15;
     A.x0 = (const uint16_t*)x_f16;
     A.out = y;
-    A.lm = MatPtr{(const uint8_t*)W->qs, W->scales, (const uint16_t*)W->mins};
-    const hipError_t e = launch_flow(A, (hipStream_t)stream);
+    A.parts = (float*)base;
+    A.cnt = (unsigned*)(base + L.off_cnt);
+    A.err = (int*)(base + L.off_cnt) + (L.zero_words - 1);
+    A.kp[SK_LIN] = L.kp;
+    A.lm = (const uint8_t*)W->data;
+    e = launch_flow(A, st);
     if (e != hipSuccess) return hip_fail(e, "linear launch");
     return VQ_OK;
 }
@@ -293,14 +502,17 @@ int vq_decode_stage_ptr(const vq_model* M, int32_t K, void* ws, int32_t stage, v
     if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
     if (stage < 0 || stage > 4 * s.L) return fail(VQ_ERR_ARG, "stage %d outside 0..%d", stage, 4 * s.L);
     if (!ws || !in_f16 || !out_f32) return fail(VQ_ERR_ARG, "NULL pointer");
-    const DecodeLayout d = decode_layout(s, K);
+    PassPlan pp;
+    rc = pass_plan(s, K, flow_grid(), &pp);
+    if (rc) return rc;
+    const DecodeLayout d = decode_layout(s, K, pp);
     char* base = (char*)ws;
     if (stage == 4 * s.L) {
-        *in_f16 = base + d.off_fxn;
+        *in_f16 = base + d.off_fx;
         *out_f32 = nullptr;
     } else {
         const size_t lb = (size_t)(stage / 4) * d.layer_bytes;
-        *in_f16 = base + lb + d.off_xn[stage % 4];
+        *in_f16 = base + lb + d.off_x[stage % 4];
         *out_f32 = base + lb + d.off_y[stage % 4];
     }
     return VQ_OK;
@@ -313,7 +525,10 @@ int vq_decode_error_word(const vq_model* M, int32_t K, void* ws, int32_t** word)
     if (rc) return rc;
     if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
     if (!ws || !word) return fail(VQ_ERR_ARG, "NULL pointer");
-    *word = err_word(decode_layout(s, K), (char*)ws);
+    PassPlan pp;
+    rc = pass_plan(s, K, flow_grid(), &pp);
+    if (rc) return rc;
+    *word = err_word(decode_layout(s, K, pp), (char*)ws);
     return VQ_OK;
 }
 
@@ -329,18 +544,22 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
         return fail(VQ_ERR_ARG, "unknown launch mode %d", launch);
     if (!x0_f16 || !logits) return fail(VQ_ERR_ARG, "NULL x0 or logits");
     if (!aligned(x0_f16, 16) || !aligned(logits, 4)) return fail(VQ_ERR_ARG, "x0 or logits misaligned");
-    const DecodeLayout d = decode_layout(s, K);
+    const int nwg = flow_grid();
+    PassPlan pp;
+    rc = pass_plan(s, K, nwg, &pp);
+    if (rc) return rc;
+    const DecodeLayout d = decode_layout(s, K, pp);
     if (!ws || ws_bytes < d.total || !aligned(ws, 256))
         return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", d.total, ws_bytes);
     hipStream_t st = (hipStream_t)stream;
     char* base = (char*)ws;
-    hipError_t e = launch_zero_u32((unsigned*)(base + d.off_sync), d.sync_words, st);
+    hipError_t e = launch_zero_u32((unsigned*)(base + d.off_cnt), d.zero_words, st);
     if (e != hipSuccess) return hip_fail(e, "sync reset launch");
     FlowArgs A;
-    fill_common(A, M, s, d, K, x0_f16, logits, base);
+    fill_common(A, s, d, pp, K, nwg, M, x0_f16, logits, base);
     const int S = 4 * s.L + 1;
     const bool staged = launch == VQ_LAUNCH_STAGED;
-    int nl = 0, base0 = 0, s0 = 0;
+    int nl = 0, s0 = 0;
     while (s0 < S) {
         int s1;
         if (staged) {
@@ -354,10 +573,6 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
         fill_layers(A, M, std::min(s0 / 4, s.L - 1));
         A.s_begin = s0;
         A.s_end = s1;
-        for (int t = s0, b = base0; t < s1; ++t) {
-            A.base[t - s0] = b;
-            b = (b + stage_tiles(s, t)) % A.nwg;
-        }
         if (events && 2 * nl + 1 < n_events) {
             e = hipEventRecord((hipEvent_t)events[2 * nl], st);
             if (e != hipSuccess) return hip_fail(e, "event record");
@@ -368,7 +583,6 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
             e = hipEventRecord((hipEvent_t)events[2 * nl + 1], st);
             if (e != hipSuccess) return hip_fail(e, "event record");
         }
-        for (int t = s0; t < s1; ++t) base0 = (base0 + stage_tiles(s, t)) % A.nwg;
         ++nl;
         s0 = s1;
     }

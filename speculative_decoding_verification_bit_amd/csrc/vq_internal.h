@@ -12,12 +12,34 @@ namespace vq {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// One block-quantised matrix as the kernels address it.
-struct MatPtr {
-    const uint8_t* qs;
-    const void* sc;
-    const uint16_t* mn;
-};
+// ------------------------------------------------------------------ tiled weights
+// A matrix in the tiled layout is a sequence of chunks, tile-major: tile t (16 rows),
+// group g (4 blocks = 128 columns) at byte (t * G + g) * chunk_bytes.  A chunk is
+//   codes  1024 B: lane l = n + 16 q (n = row in the tile, q = quarter of a block)
+//                  holds 16 B, dword j = the 8 codes of block 4g + j, columns 8q..8q+7,
+//                  of row n, nibble p holding column 8q + kPairSrc[p] (so that the Q4
+//                  widening yields natural column order); MXFP4 keeps natural nibbles
+//   scales       : per row n, the 4 block scales of the group (fp16: 8 B, E8M0: 4 B),
+//                  and for Q4 with mins the 4 fp16 mins after them (16 B per row)
+// Rows past the matrix and blocks past its columns are zero (codes, scales and mins), so
+// they contribute exactly 0.
+constexpr int TILE_ROWS = 16;
+constexpr int GROUP_COLS = 128;
+inline int chunk_bytes(int fmt) {
+    return 1024 + (fmt == VQ_FMT_Q4_MIN ? 256 : fmt == VQ_FMT_Q4 ? 128 : 64);
+}
+inline int row_scale_bytes(int fmt) { return (chunk_bytes(fmt) - 1024) / 16; }
+inline size_t tiled_bytes(int fmt, int rows, int cols) {
+    const size_t T = (size_t)(rows + TILE_ROWS - 1) / TILE_ROWS;
+    const size_t G = (size_t)(cols + GROUP_COLS - 1) / GROUP_COLS;
+    return T * G * (size_t)chunk_bytes(fmt);
+}
+
+// Writes rows [row0, row0 + W.rows) of a tiled matrix (rows `dst_rows`, cols W.cols,
+// row order `order`) from the plain planes of W.
+hipError_t launch_tile(const vq_matrix& W, uint8_t* dst, int dst_rows, int order, int row0, hipStream_t st);
+
+// ------------------------------------------------------------------ the flow kernel
 
 // What a stage computes and where its output goes.
 enum StageKind {
@@ -29,80 +51,88 @@ enum StageKind {
     SK_LIN = 5     // a single linear map (vq_verify_linear)
 };
 
-// Layers whose pointers one launch of the pass kernel carries in its arguments.
-constexpr int FLOW_MAX_LAYERS = 16;
-// Largest grid the workspace layout provides per-workgroup statistics for.
-constexpr int FLOW_MAX_WG = 1024;
+constexpr int FLOW_MAX_LAYERS = 16;      // layers one launch of the pass kernel carries
+constexpr int FLOW_MAX_WG = 1024;        // largest grid the workspace layout provides for
+constexpr int FLOW_NCW = 11;             // compute waves per workgroup (plus one conductor)
+constexpr int FLOW_LDS = 163840;         // LDS per workgroup (gfx950: 160 KB)
+constexpr int FLOW_NSP_MAX = 8;          // slots of the partial-sum ring
+constexpr int FLOW_PEND_MAX = 64;        // split tiles one workgroup finishes per stage
 // Completion counters of a stage: one per XCD group of workgroups (blockIdx mod 8), each
 // on its own 128-byte line.
 constexpr int DONE_REPL = 8;
 constexpr int DONE_STRIDE = 32;
 constexpr int DONE_WORDS = DONE_REPL * DONE_STRIDE;
 
+// Control block at the top of the workgroup's LDS.
+struct FlowCtrl {
+    unsigned pcnt[FLOW_NSP_MAX];     // wave partials written into ring slot i (cumulative)
+    unsigned pfree[FLOW_NSP_MAX];    // times ring slot i has been reduced
+    unsigned xready;                 // stages (launch-relative, + 1) whose activations are in LDS
+    unsigned abort;                  // set by the first wait that times out
+    unsigned pad_[2];
+    float rho[VQ_MAX_K];
+    int pend_t[FLOW_PEND_MAX];
+    float pend_stat[FLOW_PEND_MAX][VQ_MAX_K];
+};
+constexpr int FLOW_CTRL_OFF = (FLOW_LDS - (int)sizeof(FlowCtrl)) & ~255;
+
+// How one kind of stage is split over the grid (computed on the host).  The chunks of a
+// stage are ordered window-major: window w (columns of groups [w gw, ...)), then tile,
+// then group; workgroup i < nwe takes the contiguous range [i q + min(i, r), ... + q +
+// (i < r)), which holds at least one whole unit (a tile's chunks in one window).
+struct KindPlan {
+    int rows, cols;     // output features (gate|up: 2 FF), input features
+    int T, G;           // tiles of 16 rows, groups of 128 columns
+    int nwin, gw, glast;// windows: nwin - 1 of gw groups, then one of glast
+    int cb;             // chunk bytes
+    int nwe, q, r;      // workgroups with work; chunks per workgroup
+    int xs;             // LDS row stride of the activation window (bytes)
+    int n_in;           // elements rho normalises (0: no rho)
+    int stats;          // 1: the stage reports sums of squares of what it feeds on
+};
+
 // Everything one launch of the pass kernel reads.  A launch runs the global stages
 // [s_begin, s_end) of a pass (4 per layer + the lm_head), or one linear map.
 struct FlowArgs {
     int fmt, K;
-    int H, KV, FF, V, L;      // decode shapes; a linear map keeps rows in V and cols in H
+    int H, KV, FF, V, L;      // decode shapes
     int s_begin, s_end;
     int nwg;                  // grid size
-    int base0;                // (unused: see base)
     int linear;               // 1: one plain linear map (stage kind SK_LIN)
     int y_dtype;              // linear: VQ_DTYPE_F32 / VQ_DTYPE_F16
-    int l0;                   // layer of m[0]
+    int l0;                   // layer of w[0]
+    int nsp, pbytes;          // ring slots; bytes of one wave's partial
+    int xoff1;                // LDS offset of the second activation window
+    int ring_off;             // LDS offset of the partial-sum ring
     int pad_;
-    const uint16_t* x0;       // natural-order fp16 input of stage 0 [K][cols]
+    const uint16_t* x0;       // fp16 input of stage 0 [K][cols]
     void* out;                // logits [K][V] (decode) or y [K][rows] (linear)
     char* ws;                 // decode workspace (NULL for a linear map)
-    size_t layer_bytes;       // per layer: [xn, xp, y] of its 4 stages
-    size_t off_xn[4], off_xp[4], off_y[4];
-    size_t off_fxn, off_fxp;  // lm_head input
+    size_t layer_bytes;       // per layer: [x, y] of its 4 stages
+    size_t off_x[4], off_y[4];
+    size_t off_fx;            // lm_head input
     size_t off_stats;         // per stage s < 4L: [FLOW_MAX_WG][K] floats
     size_t stats_stride;      // floats per stage
+    float* parts;             // split-tile partial sums
+    unsigned* cnt;            // split-tile arrival counters (zero between launches)
     unsigned* done;           // [stages][DONE_WORDS] completion counters (NULL: linear)
-    int* err;                 // raised when a bounded wait times out (NULL: linear)
-    // tile t of stage s_begin + i belongs to workgroup (base[i] + t) mod nwg
-    int base[4 * FLOW_MAX_LAYERS + 1];
-    MatPtr lm;
-    MatPtr m[FLOW_MAX_LAYERS][7];   // q, k, v, o, gate, up, down of layers l0 ..
+    int* err;                 // raised when a bounded wait times out
+    KindPlan kp[6];           // by StageKind
+    const uint8_t* lm;        // lm_head, or the linear map
+    const uint8_t* w[FLOW_MAX_LAYERS][4];   // q|k|v, o, gate|up, down of layers l0 ..
 };
 
-// Geometry of one stage.
-struct StageGeo {
-    int kind, rows, cols, nb, G, T;
-    int n_in;                 // elements of the previous output that rho normalises (0: none)
-};
+// Host side of the split: fills a KindPlan, or returns false if the shape cannot be split
+// (a workgroup's chunks would span more than two windows, or it would finish more than
+// FLOW_PEND_MAX split tiles).
+bool make_plan(KindPlan& P, int fmt, int K, int rows, int cols, int tiles, int nwg, int xcap);
+// LDS bytes left for the activation windows with K columns, and the ring geometry.
+void lds_plan(int K, int* nsp, int* pbytes, int* ring_off, int* xcap);
+// Floats of split-tile partials and words of counters a plan needs.
+size_t plan_parts_floats(const KindPlan& P, int pbytes);
+size_t plan_counters(const KindPlan& P);
 
-template <class FA>
-__host__ __device__ inline StageGeo stage_geo(const FA& A, int s) {
-    StageGeo g;
-    if (A.linear) {
-        g.kind = SK_LIN; g.rows = A.V; g.cols = A.H;
-    } else if (s == 4 * A.L) {
-        g.kind = SK_LM; g.rows = A.V; g.cols = A.H;
-    } else {
-        g.kind = s & 3;
-        switch (g.kind) {
-            case SK_QKV: g.rows = A.H + 2 * A.KV; g.cols = A.H; break;
-            case SK_O: g.rows = A.H; g.cols = A.H; break;
-            case SK_GU: g.rows = 2 * A.FF; g.cols = A.H; break;
-            default: g.rows = A.H; g.cols = A.FF; break;
-        }
-    }
-    g.nb = g.cols >> 5;
-    g.G = (g.nb + 3) >> 2;
-    g.T = g.kind == SK_GU ? (A.FF >> 3) : (g.rows + 15) >> 4;
-    if (A.linear || s == 0) {
-        g.n_in = 0;
-    } else {
-        const int pk = (s - 1) & 3;       // kind of the previous stage
-        g.n_in = pk == SK_GU ? A.FF : A.H;
-    }
-    return g;
-}
-
-size_t flow_stage_ws_end(const FlowArgs& A);
-hipError_t launch_zero_u32(unsigned* p, int n, hipStream_t st);
+hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
 // One launch of the pass kernel over A.s_begin .. A.s_end (cooperative when it spans more
 // than one stage, so that every workgroup is resident for the grid barriers).
 hipError_t launch_flow(const FlowArgs& A, hipStream_t st);

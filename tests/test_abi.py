@@ -44,8 +44,14 @@ def _mat(fmt=vq.FMT_Q4_MIN, rows=64, cols=256, qs=FAKE, scales=FAKE, mins=FAKE):
     return vq.VqMatrix(fmt, rows, cols, 0, qs, scales, mins if fmt == vq.FMT_Q4_MIN else None)
 
 
-def _lin(W, K=4, x=FAKE, y=FAKE, dtype=vq.DTYPE_F32):
-    return vq.lib.vq_verify_linear(ctypes.byref(W), x, K, y, dtype, None)
+def _til(fmt=vq.FMT_Q4_MIN, rows=64, cols=256, order=vq.ROWS_PLAIN, data=FAKE):
+    return vq.VqTiled(fmt, rows, cols, order, data)
+
+
+def _lin(W, K=4, x=FAKE, y=FAKE, dtype=vq.DTYPE_F32, ws=FAKE, nbytes=None):
+    if nbytes is None:
+        nbytes = 1 << 40
+    return vq.lib.vq_verify_linear(ctypes.byref(W), x, K, y, dtype, ws, nbytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -57,33 +63,70 @@ def _lin(W, K=4, x=FAKE, y=FAKE, dtype=vq.DTYPE_F32):
     (dict(x=FAKE + 8), vq.ERR_ARG),
     (dict(y=FAKE + 2), vq.ERR_ARG),
     (dict(y=FAKE + 1, dtype=vq.DTYPE_F16), vq.ERR_ARG),
+    (dict(ws=None), vq.ERR_WORKSPACE),
+    (dict(ws=FAKE + 64), vq.ERR_WORKSPACE),
+    (dict(nbytes=0), vq.ERR_WORKSPACE),
 ])
 def test_linear_argument_errors(kw, code):
-    assert _lin(_mat(), **kw) == code
+    assert _lin(_til(), **kw) == code
     assert vq.lib.vq_last_error()
 
 
 @pytest.mark.parametrize("W", [
-    _mat(cols=48), _mat(cols=0), _mat(rows=-1), _mat(fmt=3), _mat(qs=None), _mat(scales=None),
-    _mat(qs=FAKE + 4), _mat(fmt=vq.FMT_Q4, mins=FAKE), vq.VqMatrix(vq.FMT_Q4_MIN, 64, 256, 0, FAKE, FAKE, None),
+    _til(cols=48), _til(cols=0), _til(rows=-1), _til(fmt=3), _til(data=None), _til(data=FAKE + 16),
+    _til(order=2), _til(order=vq.ROWS_PAIR8),
 ])
 def test_linear_bad_matrix(W):
-    if W.format == vq.FMT_Q4 and W.mins is None:
-        W.mins = FAKE
     assert _lin(W) == vq.ERR_ARG
 
 
 def test_linear_zero_rows_is_a_no_op():
-    W = _mat(rows=0, qs=None, scales=None, mins=None)
-    assert _lin(W, x=None, y=None) == vq.OK
+    W = _til(rows=0, data=None)
+    assert _lin(W, x=None, y=None, ws=None, nbytes=0) == vq.OK
 
 
-def test_linear_needs_no_workspace():
-    for rows, cols in ((5120, 5120), (5120, 17408), (151936, 5120), (64, 1056)):
-        W = _mat(rows=rows, cols=cols)
+def test_linear_workspace_is_small_and_exact():
+    for rows, cols in ((5120, 5120), (5120, 17408), (151936, 5120), (64, 1056), (77, 32)):
+        W = _til(rows=rows, cols=cols)
         for K in (1, 4, 16):
-            assert vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), K) == 0
-    assert vq.lib.vq_workspace_bytes(9, ctypes.byref(_mat()), 4) == 0
+            n = vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(W), K)
+            assert 0 < n
+            if K == 1:
+                assert n < 1 << 20, (rows, cols, n)     # one window: two partials per workgroup
+            assert _lin(W, K=K, nbytes=n - 1) == vq.ERR_WORKSPACE
+    assert vq.lib.vq_workspace_bytes(9, ctypes.byref(_til()), 4) == 0
+    assert vq.lib.vq_workspace_bytes(vq.OP_LINEAR, ctypes.byref(_til()), 0) == 0
+
+
+def test_tiled_bytes():
+    for fmt, per in ((vq.FMT_Q4, 1152), (vq.FMT_Q4_MIN, 1280), (vq.FMT_MXFP4, 1088)):
+        assert vq.lib.vq_tiled_bytes(fmt, 16, 128) == per
+        # partial tiles and groups are padded to whole chunks
+        assert vq.lib.vq_tiled_bytes(fmt, 77, 1056) == 5 * 9 * per
+        assert vq.lib.vq_tiled_bytes(fmt, 5120, 17408) == 320 * 136 * per
+        # every weight's 4 bits and its block's scale (and min) are stored once, no more
+        if fmt == vq.FMT_Q4_MIN:
+            assert vq.lib.vq_tiled_bytes(fmt, 5120, 5120) == 5120 * 5120 * 5 // 8
+    assert vq.lib.vq_tiled_bytes(3, 16, 128) == 0
+    assert vq.lib.vq_tiled_bytes(vq.FMT_Q4, 16, 100) == 0
+    assert vq.lib.vq_tiled_bytes(vq.FMT_Q4, -1, 128) == 0
+
+
+def _tile(src, dst, row0=0):
+    return vq.lib.vq_tile(ctypes.byref(src), ctypes.byref(dst), row0, None)
+
+
+def test_tile_argument_errors():
+    assert _tile(_mat(rows=0, qs=None, scales=None, mins=None), _til()) == vq.OK     # nothing to write
+    assert _tile(_mat(fmt=vq.FMT_Q4), _til()) == vq.ERR_ARG                          # format differs
+    assert _tile(_mat(cols=512), _til()) == vq.ERR_ARG                                # cols differ
+    assert _tile(_mat(rows=64), _til(rows=64), 16) == vq.ERR_ARG                     # past dst
+    assert _tile(_mat(rows=16), _til(rows=64), 8) == vq.ERR_ARG                      # row0 % 16
+    assert _tile(_mat(rows=16), _til(rows=64), -16) == vq.ERR_ARG
+    assert _tile(_mat(rows=16), _til(rows=64, order=vq.ROWS_PAIR8), 16) == vq.ERR_ARG  # pair8: halves only
+    assert _tile(_mat(rows=32), _til(rows=64, order=vq.ROWS_PAIR8), 16) == vq.ERR_ARG
+    assert _tile(_mat(rows=16), _til(rows=64, data=None)) == vq.ERR_ARG
+    assert _tile(_mat(rows=16, qs=None), _til(rows=64)) == vq.ERR_ARG
 
 
 def _acc(**kw):
@@ -122,14 +165,15 @@ def test_accept_workspace_errors_and_empty():
 
 
 def _model(L=2, H=256, KV=64, FF=512, V=1000, fmt=vq.FMT_Q4_MIN, bad=None):
-    shapes = dict(q=(H, H), k=(KV, H), v=(KV, H), o=(H, H), gate=(FF, H), up=(FF, H), down=(H, FF))
+    shapes = dict(qkv=(H + 2 * KV, H, vq.ROWS_PLAIN), o=(H, H, vq.ROWS_PLAIN), gu=(2 * FF, H, vq.ROWS_PAIR8),
+                  down=(H, FF, vq.ROWS_PLAIN))
     arr = (vq.VqLayer * L)()
     for i in range(L):
-        for n, (r, c) in shapes.items():
+        for n, (r, c, order) in shapes.items():
             if bad == (i, n):
                 r += 64
-            setattr(arr[i], n, _mat(fmt, r, c))
-    return vq.VqModel(L, 0, ctypes.cast(arr, ctypes.POINTER(vq.VqLayer)), _mat(fmt, V, H)), arr
+            setattr(arr[i], n, _til(fmt, r, c, order))
+    return vq.VqModel(L, 0, ctypes.cast(arr, ctypes.POINTER(vq.VqLayer)), _til(fmt, V, H)), arr
 
 
 def _dec(M, K=4, x=FAKE, logits=FAKE, ws=FAKE, nbytes=0):
@@ -156,8 +200,10 @@ def test_decode_validation_and_layout():
     assert _dec(Mu, nbytes=n4) == vq.ERR_UNSUPPORTED
     Mf, kf = _model(fmt=vq.FMT_Q4_MIN)
     Mf.lm_head.format = vq.FMT_Q4
-    Mf.lm_head.mins = None
     assert _dec(Mf, nbytes=n4) == vq.ERR_ARG                               # one format per stack
+    Mo, ko = _model()
+    ko[1].gu.order = vq.ROWS_PLAIN
+    assert _dec(Mo, nbytes=n4) == vq.ERR_ARG                               # gate|up must be paired
     # stage pointers: distinct, ordered, inside the workspace
     seen = []
     for s in range(9):

@@ -31,8 +31,11 @@ def test_c1_tiny_step():
 
 
 # rows not a multiple of 16 (partial tile), cols with 33, 1 and 3 blocks (partial group of
-# 4 blocks), and column counts that split into 5, 16 and 40 groups
-SHAPES = [(1000, 1056), (77, 32), (64, 2048), (300, 5120), (129, 256), (16, 96), (5, 4096)]
+# 4 blocks), and column counts that split into 5, 16 and 40 groups; more tiles than
+# workgroups, so that tiles are split between workgroups (and, at K = 16 with 5120
+# columns, between column windows of the activations)
+SHAPES = [(1000, 1056), (77, 32), (64, 2048), (300, 5120), (129, 256), (16, 96), (5, 4096),
+          (4200, 256), (4136, 1056), (4400, 5120)]
 
 
 @pytest.mark.parametrize("fmt", [synth.FMT_Q4, synth.FMT_Q4_MIN, synth.FMT_MXFP4])
