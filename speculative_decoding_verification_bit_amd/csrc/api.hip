@@ -93,21 +93,21 @@ bool make_plan(KindPlan& P, int fmt, int K, int rows, int cols, int tiles, int n
     P.rows = rows;
     P.cols = cols;
     P.T = tiles;
-    P.G = (cols + GROUP_COLS - 1) / GROUP_COLS;
-    P.cb = chunk_bytes(fmt);
-    const int xs1 = P.G * 256 + 16;
+    P.G = (cols + STEP_COLS - 1) / STEP_COLS;
+    P.cb = 2 * chunk_bytes(fmt);
+    const int xs1 = P.G * 512 + 16;
     if ((long)K * xs1 <= xcap) {
         P.nwin = 1;
         P.gw = P.glast = P.G;
         P.xs = xs1;
     } else {
         const int half = (xcap / 2) & ~15;
-        const int gmax = (half / K - 16) / 256;
+        const int gmax = (half / K - 16) / 512;
         if (gmax < 1) return false;
         P.nwin = (P.G + gmax - 1) / gmax;
         P.gw = (P.G + P.nwin - 1) / P.nwin;
         P.glast = P.G - (P.nwin - 1) * P.gw;
-        P.xs = P.gw * 256 + 16;
+        P.xs = P.gw * 512 + 16;
         if (P.glast < 1) return false;
     }
     const long N = (long)P.T * P.G;

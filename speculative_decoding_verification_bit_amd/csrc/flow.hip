@@ -42,7 +42,7 @@ namespace {
 
 constexpr int NCW = FLOW_NCW;
 constexpr int NTHR = 64 * (NCW + 1);
-constexpr int DEPTH = 12;               // chunks in flight per compute wave
+constexpr int DEPTH = 6;                // steps (two chunks each) in flight per compute wave
 constexpr unsigned SPIN_LDS = 1u << 23; // bounded waits (about a second)
 constexpr unsigned SPIN_GLOBAL = 1u << 22;
 
@@ -109,6 +109,15 @@ __device__ __forceinline__ h8_t widen8(uint32_t w) {
     r[0] = p[0][0]; r[1] = p[0][1]; r[2] = p[1][0]; r[3] = p[1][1];
     r[4] = p[2][0]; r[5] = p[2][1]; r[6] = p[3][0]; r[7] = p[3][1];
     return r;
+}
+
+// v with lane j replaced by the scalar x (v_writelane_b32; j and x wave-uniform).
+__device__ __forceinline__ int writelane(int x, int j, int v) {
+    x = __builtin_amdgcn_readfirstlane(x);
+    j = __builtin_amdgcn_readfirstlane(j);
+    // the lane select goes through M0: two SGPR operands would exceed the constant bus
+    asm("s_mov_b32 m0, %2\n\tv_writelane_b32 %0, %1, m0" : "+v"(v) : "s"(x), "s"(j) : "m0");
+    return v;
 }
 
 // Sum over the 16 lanes of a row of 16 (every lane gets the sum; fixed order).
@@ -242,6 +251,94 @@ __device__ __forceinline__ const uint16_t* input_of(KArgs& A, int s) {
     return (const uint16_t*)(A.ws + (size_t)(s >> 2) * A.layer_bytes + A.off_x[s & 3]);
 }
 
+// ------------------------------------------------------------------ chunk cursors
+
+// Fields of a row of the per-kind sequence table in LDS.
+enum {
+    KT_N, KT_LENA, KT_WLO, KT_AW, KT_AT, KT_AI, KT_BW, KT_BT, KT_BI, KT_BK1,
+    KT_T, KT_G, KT_GW, KT_GLAST, KT_NWIN, KT_CB, KT_XS
+};
+static_assert(KT_XS < FLOW_KTAB, "sequence table row");
+
+__device__ __forceinline__ int ktab(const FlowCtrl& C, int kind, int f) { return uni(C.ktab[kind][f]); }
+
+// A walk over one wave's chunks of the launch: positions cw, cw + 11, ... of the
+// workgroup's sequence in every stage.  It keeps the stage, the position k, the current
+// span [k0, k1) (a run of chunks inside one unit) with the span's unit (window w, tile t)
+// and the group i0 of its first chunk.  A consume walk also counts the units it has left
+// behind (pclose) and whether it has entered a stage (pnew).  All fields are wave-uniform.
+struct Cur {
+    int s, kind, n, k, k0, k1, w, t, i0;
+    int done, pclose, pnew;
+};
+
+__device__ __forceinline__ Cur span_first(const FlowCtrl& C, Cur c) {
+    const int lenA = ktab(C, c.kind, KT_LENA);
+    c.k0 = 0;
+    if (lenA > 0) {
+        c.w = ktab(C, c.kind, KT_AW); c.t = ktab(C, c.kind, KT_AT); c.i0 = ktab(C, c.kind, KT_AI);
+        c.k1 = lenA;
+    } else {
+        c.w = ktab(C, c.kind, KT_BW); c.t = ktab(C, c.kind, KT_BT); c.i0 = ktab(C, c.kind, KT_BI);
+        c.k1 = ktab(C, c.kind, KT_BK1);
+    }
+    return c;
+}
+
+__device__ __forceinline__ Cur span_next(const FlowCtrl& C, Cur c) {
+    const int lenA = ktab(C, c.kind, KT_LENA);
+    if (lenA > 0 && c.k0 == 0) {
+        c.w = ktab(C, c.kind, KT_BW); c.t = ktab(C, c.kind, KT_BT); c.i0 = ktab(C, c.kind, KT_BI);
+        c.k0 = lenA;
+        c.k1 = ktab(C, c.kind, KT_BK1);
+    } else {
+        c.t = uni(c.t + 1);
+        if (c.t == ktab(C, c.kind, KT_T)) {
+            c.t = 0;
+            c.w = uni(c.w + 1);
+        }
+        const int gU = c.w == ktab(C, c.kind, KT_NWIN) - 1 ? ktab(C, c.kind, KT_GLAST) : ktab(C, c.kind, KT_GW);
+        c.k0 = c.k1;
+        c.k1 = uni(min(c.k0 + gU, c.n));
+        c.i0 = 0;
+    }
+    return c;
+}
+
+// Moves a walk to its next chunk at or after its position (new_stage: enter stage c.s).
+// The issue walk skips a stage as soon as its position passes the stage's chunks; the
+// consume walk steps through every span, so that it counts each unit it leaves.
+template <bool CONSUME>
+__device__ __forceinline__ Cur seek(KArgs& A, const FlowCtrl& C, Cur c, int cw, int new_stage) {
+    for (;;) {
+        if (new_stage) {
+            if (c.s >= A.s_end) {
+                c.done = 1;
+                return c;
+            }
+            c.kind = kind_of(A, c.s);
+            c.n = ktab(C, c.kind, KT_N);
+            c.k = cw;
+            if (c.n == 0 || (!CONSUME && c.k >= c.n)) {
+                c.s = uni(c.s + 1);
+                continue;
+            }
+            c = span_first(C, c);
+            if (CONSUME && c.k < c.n) c.pnew = 1;
+            new_stage = 0;
+        }
+        if (c.k < c.k1) break;
+        if (CONSUME) c.pclose = uni(c.pclose + 1);
+        if (CONSUME ? c.k1 >= c.n : c.k >= c.n) {
+            c.s = uni(c.s + 1);
+            new_stage = 1;
+            continue;
+        }
+        c = span_next(C, c);
+    }
+    return c;
+}
+
 // ------------------------------------------------------------------------ kernel
 
 template <int FMT, int KC>
@@ -268,6 +365,33 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         C.xready = 0;
         C.abort = 0;
     }
+    // The workgroup's chunk sequence for each stage kind: chunk count, segment A, and the
+    // first span (a run of chunks inside one unit) of each segment, with the plan values
+    // the cursors need.  Computed once by the conductor wave.
+    if (wave == NCW) {
+        for (int kind = 0; kind < 6; ++kind) {
+            const Plan P = plan_of(A, kind);
+            const Seq q = seq_of(P, w);
+            int aw = 0, at = 0, ai = 0, bw = 0, bt = 0, bi = 0, bk1 = 0;
+            if (q.lenA > 0) {
+                const Pos pa = locate(P, q.a0);
+                aw = pa.w; at = pa.t; ai = pa.i;
+            }
+            if (q.n - q.lenA > 0) {
+                const Pos pb = locate(P, q.lo);
+                bw = pb.w; bt = pb.t; bi = pb.i;
+                bk1 = q.lenA + min(pb.gl - pb.i, q.n - q.lenA);
+            }
+            if (lane == 0) {
+                int* r = C.ktab[kind];
+                r[KT_N] = q.n; r[KT_LENA] = q.lenA; r[KT_WLO] = q.wlo;
+                r[KT_AW] = aw; r[KT_AT] = at; r[KT_AI] = ai;
+                r[KT_BW] = bw; r[KT_BT] = bt; r[KT_BI] = bi; r[KT_BK1] = bk1;
+                r[KT_T] = P.T; r[KT_G] = P.G; r[KT_GW] = P.gw; r[KT_GLAST] = P.glast;
+                r[KT_NWIN] = P.nwin; r[KT_CB] = P.cb; r[KT_XS] = P.xs;
+            }
+        }
+    }
     __syncthreads();
 
     if (wave < NCW) {
@@ -276,177 +400,192 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         using scale_t = typename std::conditional<FMT == VQ_FMT_Q4_MIN, u4_t,
                         typename std::conditional<FMT == VQ_FMT_Q4, u2_t, uint32_t>::type>::type;
         constexpr int SB = FMT == VQ_FMT_Q4_MIN ? 16 : FMT == VQ_FMT_Q4 ? 8 : 4;
-
-        // ---- issue cursor: walks this wave's chunks of every stage of the launch
-        int is = A.s_begin;
-        Plan iP = plan_of(A, kind_of(A, is));
-        Seq iq = seq_of(iP, w);
-        int ik = cw;
-        Pos ip{0, 0, 0, 1};
-        const uint8_t* iW = mat_of(A, is, kind_of(A, is));
-        const uint8_t* iaddr = iW;
-        bool idone = false;
-        auto i_enter = [&]() {
-            // first stage >= is in which this wave has a chunk
-            for (;;) {
-                if (is >= A.s_end) {
-                    idone = true;
-                    return;
-                }
-                const int kd = kind_of(A, is);
-                iP = plan_of(A, kd);
-                iq = seq_of(iP, w);
-                ik = cw;
-                iW = mat_of(A, is, kd);
-                if (ik < iq.n) {
-                    ip = locate(iP, seq_chunk(iq, ik));
-                    return;
-                }
-                is = uni(is + 1);
-            }
-        };
-        auto i_addr = [&]() {
-            const int g = ip.w * iP.gw + ip.i;
-            iaddr = iW + (size_t)(uint32_t)((ip.t * iP.G + g) * iP.cb);
-        };
-        auto i_next = [&]() {
-            if (idone) return;
-            const int k2 = ik + NCW;
-            if (k2 < iq.n) {
-                if (ik < iq.lenA && k2 >= iq.lenA) ip = locate(iP, seq_chunk(iq, k2));
-                else step_pos(iP, ip, NCW);
-                ik = k2;
-            } else {
-                is = uni(is + 1);
-                i_enter();
-                if (idone) return;       // keep the last address: the tail re-reads it
-            }
-            i_addr();
-        };
-        i_enter();
-        if (!idone) i_addr();
-
-        u4_t rq[DEPTH];
-        scale_t rs[DEPTH];
-        auto issue = [&](int u) {
-            rq[u] = ld_global_nt<u4_t>(iaddr + 16 * lane);
-            rs[u] = ld_global_nt<scale_t>(iaddr + 1024 + SB * n16);
-        };
-
-        // ---- consume cursor
-        int cs = A.s_begin;
-        Plan P = plan_of(A, kind_of(A, cs));
-        Seq q = seq_of(P, w);
-        int ck = cw;
-        Pos cp{0, 0, 0, 1};
-        int open = 0;                   // unit position accumulating
-        unsigned useq = 0;              // ring sequence number of unit position 0 of the stage
-        bool cdone = false;
-        uint32_t xlane = 0;             // LDS byte address of this lane's A operand in window wlo
-        int xoff1 = A.xoff1;
-        f4_t acc = {0.f, 0.f, 0.f, 0.f};
+        const int xoff1 = A.xoff1;
         uint8_t* const ring = lds + A.ring_off;
 
-        // one unit's partial into the ring (zero if the wave had no chunk in it)
-        auto close_unit = [&]() {
-            const unsigned sq_ = useq + (unsigned)open;
-            const unsigned slot = sq_ & (unsigned)(nsp - 1), round = sq_ / (unsigned)nsp;
+        // Two walks over this wave's chunks: the issue walk DEPTH chunks ahead of the
+        // consume walk.  Once per round of DEPTH chunks both are advanced in one loop that
+        // leaves a descriptor per step in the lanes of four VGPRs; the unrolled steps only
+        // read them:
+        //   di0/di1: address of the chunk to issue;  dc0: LDS activation offset of the chunk
+        //   to consume;  dc1: 0 (nothing to consume), or units to close first (bits 0..7),
+        //   opens a stage (bit 8), valid (bit 9), stage kind (bits 10..12), launch stage + 1
+        //   (bits 16..)
+        Cur ic = {};
+        ic.s = A.s_begin;
+        ic = seek<false>(A, C, ic, cw, 1);
+        const uint8_t* iW = A.lm;
+        uint32_t ioff = 0, istep = 0;
+        auto i_set = [&]() __attribute__((always_inline)) {
+            iW = mat_of(A, ic.s, ic.kind);
+            const int cb = ktab(C, ic.kind, KT_CB);
+            istep = (uint32_t)uni(NCW * cb);
+            const int g = ic.w * ktab(C, ic.kind, KT_GW) + ic.i0 + (ic.k - ic.k0);
+            ioff = (uint32_t)uni((ic.t * ktab(C, ic.kind, KT_G) + g) * cb);
+        };
+        if (!ic.done) i_set();
+        Cur cc = {};
+        cc.s = A.s_begin;
+        cc = seek<true>(A, C, cc, cw, 1);
+        uint32_t coff = 0;
+        auto c_set = [&]() __attribute__((always_inline)) {
+            coff = (uint32_t)uni((cc.w - ktab(C, cc.kind, KT_WLO)) * xoff1 + (cc.i0 + (cc.k - cc.k0)) * 512);
+        };
+        if (!cc.done) c_set();
+
+        int di0 = 0, di1 = 0, dc0 = 0, dc1 = 0;
+        auto gen_issue = [&](int j) __attribute__((always_inline)) {
+            const uint64_t a = (uint64_t)(uintptr_t)(iW + ioff);
+            di0 = writelane((int)(uint32_t)a, j, di0);
+            di1 = writelane((int)(uint32_t)(a >> 32), j, di1);
+            if (!ic.done) {
+                const uint32_t last = ioff;
+                ic.k = uni(ic.k + NCW);
+                ioff = (uint32_t)uni((int)(ioff + istep));
+                if (ic.k >= ic.k1) {
+                    ic = seek<false>(A, C, ic, cw, 0);
+                    if (!ic.done) i_set();
+                    else ioff = last;                // the tail re-reads the last chunk
+                }
+            }
+        };
+        auto gen_consume = [&](int j) __attribute__((always_inline)) {
+            int f = 0;
+            if (!cc.done) {
+                dc0 = writelane((int)coff, j, dc0);
+                f = cc.pclose | (cc.pnew ? 0x100 : 0) | 0x200 | (cc.kind << 10) | ((cc.s - A.s_begin + 1) << 16);
+                cc.pclose = 0;
+                cc.pnew = 0;
+                cc.k = uni(cc.k + NCW);
+                coff = (uint32_t)uni((int)(coff + NCW * 512));
+                if (cc.k >= cc.k1) {
+                    cc = seek<true>(A, C, cc, cw, 0);
+                    if (!cc.done) c_set();
+                }
+            }
+            dc1 = writelane(f, j, dc1);
+        };
+
+        f4_t acc = {0.f, 0.f, 0.f, 0.f};
+        uint32_t xlane = 0;                // this lane's A-operand byte offset in a window
+        unsigned useq = 0;                 // ring sequence number of the next unit to close
+        // this wave's partial of the current unit into the ring (zero if it had no chunk there)
+        auto close_unit = [&]() __attribute__((always_inline)) {
+            const unsigned slot = useq & (unsigned)(nsp - 1), round = useq / (unsigned)nsp;
             wait_ge(&C.pfree[slot], round, err, &C.abort);
             if (lane < plane) *(f4_t*)(ring + ((int)slot * NCW + cw) * pbytes + 16 * lane) = acc;
             if (lane == 0) __hip_atomic_fetch_add(&C.pcnt[slot], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
             acc = f4_t{0.f, 0.f, 0.f, 0.f};
-            ++open;
+            useq = (unsigned)uni((int)useq + 1);
         };
-        // enter stage cs: set up, close the units of stages where this wave has no chunk
-        auto c_enter = [&]() {
-            for (;;) {
-                if (cs >= A.s_end) {
-                    cdone = true;
-                    return;
-                }
-                P = plan_of(A, kind_of(A, cs));
-                q = seq_of(P, w);
-                ck = cw;
-                open = 0;
-                if (ck < q.n) {
-                    cp = locate(P, seq_chunk(q, ck));
-                    // the stage's activations are in LDS once the conductor says so
-                    wait_ge(&C.xready, (unsigned)(cs - A.s_begin) + 1u, err, &C.abort);
-                    const int mrow = n16 < K ? n16 : 0;
-                    xlane = (uint32_t)(mrow * P.xs + 16 * q4);
-                    return;
-                }
-                while (open < q.nU) close_unit();
-                useq += (unsigned)q.nU;
-                cs = uni(cs + 1);
+
+        // One step: two chunks (groups 2g, 2g + 1 of a tile), each 1 KB of codes and the
+        // rows' scales; the second chunk follows the first.
+        constexpr int CB1 = FMT == VQ_FMT_Q4_MIN ? 1280 : FMT == VQ_FMT_Q4 ? 1152 : 1088;
+        u4_t rq[DEPTH][2];
+        scale_t rs[DEPTH][2];
+        auto issue = [&](int u) __attribute__((always_inline)) {
+            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(di0, u);
+            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(di1, u);
+            const uint8_t* p = (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                rq[u][h] = ld_global_nt<u4_t>(p + h * CB1 + 16 * lane);
+                rs[u][h] = ld_global_nt<scale_t>(p + h * CB1 + 1024 + SB * n16);
             }
         };
-        auto c_next = [&]() {
-            const int k2 = ck + NCW;
-            if (k2 < q.n) {
-                if (ck < q.lenA && k2 >= q.lenA) cp = locate(P, seq_chunk(q, k2));
-                else step_pos(P, cp, NCW);
-                ck = k2;
-                return;
+
+        // Q4 widening constants held in registers, so that each masked OR is one
+        // v_and_or_b32 (a VOP3 operand cannot be a literal)
+        uint32_t m_lo, m_hi, magic;
+        asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(m_lo));
+        asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(m_hi));
+        asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+        // Eight codes -> the MFMA B operand (8 fp16 in column order; the tiled layout stores
+        // the Q4 nibbles so that this order comes out).  A nibble OR-ed into the mantissa of
+        // 1024.0 gives 1024 + n (low nibbles) or 1024 + 16 n (high nibbles); both map
+        // exactly to n - 8.
+        auto widen = [&](uint32_t w) __attribute__((always_inline)) -> h8_t {
+            if constexpr (FMT == VQ_FMT_MXFP4) {
+                return widen8<FMT>(w);
+            } else {
+                const uint32_t w8 = w >> 8;
+                const h2_t k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+                const h2_t k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
+                const h2_t k72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+                const h2_t p0 = as_h2((w & m_lo) | magic) - k1032;
+                const h2_t p1 = as_h2((w & m_hi) | magic) * k16 + k72;
+                const h2_t p2 = as_h2((w8 & m_lo) | magic) - k1032;
+                const h2_t p3 = as_h2((w8 & m_hi) | magic) * k16 + k72;
+                // pairs (c0, c4), (c1, c5), (c2, c6), (c3, c7) of the dword's nibbles: the
+                // tiled layout puts columns 0..7 of the block quarter in that nibble order
+                const u4_t r = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+                return as_h8(r);
             }
-            while (open < q.nU) close_unit();
-            useq += (unsigned)q.nU;
-            cs = uni(cs + 1);
-            c_enter();
         };
-        c_enter();
 
         const h8_t ONES = {(_Float16)1, (_Float16)1, (_Float16)1, (_Float16)1,
                            (_Float16)1, (_Float16)1, (_Float16)1, (_Float16)1};
         constexpr int NF = KC < 4 ? KC : 4;     // accumulator elements that can hold a column < K
 
-        auto consume = [&](int u) {
-            // close the units before this chunk's
-            const int upos = unit_pos(q, cp.w * P.T + cp.t);
-            while (open < upos) close_unit();
-            // activations: window buffer, group inside the window, block j, quarter q4
-            const uint32_t xa = xlane + (uint32_t)((cp.w - q.wlo) * xoff1 + cp.i * 256);
-            h8_t a[4];
+        auto consume = [&](int u) __attribute__((always_inline)) {
+            const int f = __builtin_amdgcn_readlane(dc1, u);
+            if (!(f & 0x200)) return;
+            if (__builtin_expect((f & 0xff) != 0, 0)) {
+                for (int i = 0; i < (f & 0xff); ++i) close_unit();
+            }
+            if (__builtin_expect((f & 0x100) != 0, 0)) {
+                // the stage's activations are in LDS once the conductor says so
+                wait_ge(&C.xready, (unsigned)(f >> 16), err, &C.abort);
+                const int mrow = n16 < K ? n16 : 0;
+                xlane = (uint32_t)(mrow * ktab(C, (f >> 10) & 7, KT_XS) + 16 * q4);
+            }
+            const uint32_t xa = xlane + (uint32_t)__builtin_amdgcn_readlane(dc0, u);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                a[j] = as_h8(*(const u4_t*)(lds + xa + 64 * j));
-            const u4_t raw = rq[u];
-            const scale_t sc = rs[u];
+            for (int h = 0; h < 2; ++h) {
+                h8_t a[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const h8_t b = widen8<FMT>(raw[j]);
-                const f4_t z = {0.f, 0.f, 0.f, 0.f};
-                const f4_t cj = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], b, z, 0, 0, 0);
-                float d;
-                if constexpr (FMT == VQ_FMT_MXFP4) d = e8m0_to_float((sc >> (8 * j)) & 0xffu);
-                else d = half_bits_to_float((sc[j >> 1] >> ((j & 1) * 16)) & 0xffffu);
+                for (int j = 0; j < 4; ++j) a[j] = as_h8(*(const u4_t*)(lds + xa + 256 * h + 64 * j));
+                const u4_t raw = rq[u][h];
+                const scale_t sc = rs[u][h];
 #pragma unroll
-                for (int i = 0; i < NF; ++i) acc[i] = __builtin_fmaf(d, cj[i], acc[i]);
-                if constexpr (FMT == VQ_FMT_Q4_MIN) {
-                    const f4_t sj = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], ONES, z, 0, 0, 0);
-                    const float mm = half_bits_to_float((sc[2 + (j >> 1)] >> ((j & 1) * 16)) & 0xffffu);
+                for (int j = 0; j < 4; ++j) {
+                    const h8_t b = widen(raw[j]);
+                    const f4_t z = {0.f, 0.f, 0.f, 0.f};
+                    const f4_t cj = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], b, z, 0, 0, 0);
+                    float d;
+                    if constexpr (FMT == VQ_FMT_MXFP4) d = e8m0_to_float((sc >> (8 * j)) & 0xffu);
+                    else d = half_bits_to_float((sc[j >> 1] >> ((j & 1) * 16)) & 0xffffu);
 #pragma unroll
-                    for (int i = 0; i < NF; ++i) acc[i] = __builtin_fmaf(mm, sj[i], acc[i]);
+                    for (int i = 0; i < NF; ++i) acc[i] = __builtin_fmaf(d, cj[i], acc[i]);
+                    if constexpr (FMT == VQ_FMT_Q4_MIN) {
+                        const f4_t sj = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], ONES, z, 0, 0, 0);
+                        const float mm = half_bits_to_float((sc[2 + (j >> 1)] >> ((j & 1) * 16)) & 0xffffu);
+#pragma unroll
+                        for (int i = 0; i < NF; ++i) acc[i] = __builtin_fmaf(mm, sj[i], acc[i]);
+                    }
                 }
             }
         };
 
+        for (int j = 0; j < DEPTH; ++j) gen_issue(j);
 #pragma unroll
-        for (int u = 0; u < DEPTH; ++u) {
-            issue(u);
-            i_next();
-        }
-        while (!cdone) {
+        for (int u = 0; u < DEPTH; ++u) issue(u);
+        for (;;) {
+            const int last = cc.done;
+            for (int j = 0; j < DEPTH; ++j) {
+                gen_issue(j);
+                gen_consume(j);
+            }
 #pragma unroll
             for (int u = 0; u < DEPTH; ++u) {
-                if (!cdone) {
-                    consume(u);
-                    c_next();
-                }
+                consume(u);
                 issue(u);
-                i_next();
             }
+            if (last || cc.done) break;
         }
+        for (int i = 0; i < cc.pclose; ++i) close_unit();
         return;
     }
 
@@ -515,9 +654,9 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
                 uint8_t* xb = lds + (win - q.wlo) * A.xoff1;
                 const int g0 = win * P.gw;
                 const int gl = win == P.nwin - 1 ? P.glast : P.gw;
-                const int c0 = g0 * GROUP_COLS;
-                const int cend = min(P.cols, (g0 + gl) * GROUP_COLS);
-                const int Rb = (cend - c0) * 2, Wb = gl * 256;
+                const int c0 = g0 * STEP_COLS;
+                const int cend = min(P.cols, (g0 + gl) * STEP_COLS);
+                const int Rb = (cend - c0) * 2, Wb = gl * 512;
                 for (int m = 0; m < K; ++m) {
                     const char* src = (const char*)(X + (size_t)m * P.cols + c0);
                     uint8_t* dst = xb + m * P.xs;
@@ -544,7 +683,7 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
 
         // -------- units: reduce the 11 partials, then epilogue or part
         const float* rho = C.rho;
-        auto epilogue = [&](int t, const f4_t& sum) {
+        auto epilogue = [&](int t, const f4_t& sum) __attribute__((always_inline)) {
             float sq[4] = {0.f, 0.f, 0.f, 0.f};
             const bool chain = kind != SK_LIN && kind != SK_LM;
             const bool last_down = kind == SK_DOWN && s + 1 == 4 * A.L;
@@ -592,11 +731,11 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             }
         };
         // split-tile bookkeeping
-        auto part_slot = [&](int U, int t, int side) -> float* {
+        auto part_slot = [&](int U, int t, int side) __attribute__((always_inline)) -> float* {
             const int sl = P.nwin == 1 ? 2 * (side == 0 ? w : w - 1) + side : 2 * U + side;
             return A.parts + (size_t)sl * (pbytes >> 2);
         };
-        auto counter = [&](int t, int side) -> unsigned* {
+        auto counter = [&](int t, int side) __attribute__((always_inline)) -> unsigned* {
             return A.cnt + (P.nwin == 1 ? (side == 0 ? w : w - 1) : t);
         };
 
@@ -817,7 +956,7 @@ hipError_t launch_f(const FlowArgs& A, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_tile(const vq_matrix& W, uint8_t* dst, int dst_rows, int order, int row0, hipStream_t st) {
-    const int G = (W.cols + GROUP_COLS - 1) / GROUP_COLS;
+    const int G = 2 * ((W.cols + STEP_COLS - 1) / STEP_COLS);   // even: zero chunks pad the last step
     int t0, t1;
     if (order == VQ_ROWS_PAIR8) {
         const int half = dst_rows / 2;

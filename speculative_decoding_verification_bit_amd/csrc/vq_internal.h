@@ -14,7 +14,8 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // ------------------------------------------------------------------ tiled weights
 // A matrix in the tiled layout is a sequence of chunks, tile-major: tile t (16 rows),
-// group g (4 blocks = 128 columns) at byte (t * G + g) * chunk_bytes.  A chunk is
+// group g (4 blocks = 128 columns) at byte (t * G + g) * chunk_bytes, with G the group
+// count rounded up to even (the kernels take two groups of a tile per step).  A chunk is
 //   codes  1024 B: lane l = n + 16 q (n = row in the tile, q = quarter of a block)
 //                  holds 16 B, dword j = the 8 codes of block 4g + j, columns 8q..8q+7,
 //                  of row n, nibble p holding column 8q + kPairSrc[p] (so that the Q4
@@ -25,13 +26,14 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // they contribute exactly 0.
 constexpr int TILE_ROWS = 16;
 constexpr int GROUP_COLS = 128;
+constexpr int STEP_COLS = 2 * GROUP_COLS;   // columns of one step of the streaming kernel
 inline int chunk_bytes(int fmt) {
     return 1024 + (fmt == VQ_FMT_Q4_MIN ? 256 : fmt == VQ_FMT_Q4 ? 128 : 64);
 }
 inline int row_scale_bytes(int fmt) { return (chunk_bytes(fmt) - 1024) / 16; }
 inline size_t tiled_bytes(int fmt, int rows, int cols) {
     const size_t T = (size_t)(rows + TILE_ROWS - 1) / TILE_ROWS;
-    const size_t G = (size_t)(cols + GROUP_COLS - 1) / GROUP_COLS;
+    const size_t G = 2 * ((size_t)(cols + STEP_COLS - 1) / STEP_COLS);
     return T * G * (size_t)chunk_bytes(fmt);
 }
 
@@ -57,6 +59,7 @@ constexpr int FLOW_NCW = 11;             // compute waves per workgroup (plus on
 constexpr int FLOW_LDS = 163840;         // LDS per workgroup (gfx950: 160 KB)
 constexpr int FLOW_NSP_MAX = 8;          // slots of the partial-sum ring
 constexpr int FLOW_PEND_MAX = 64;        // split tiles one workgroup finishes per stage
+constexpr int FLOW_KTAB = 20;            // ints per stage kind in the sequence table
 // Completion counters of a stage: one per XCD group of workgroups (blockIdx mod 8), each
 // on its own 128-byte line.
 constexpr int DONE_REPL = 8;
@@ -72,19 +75,20 @@ struct FlowCtrl {
     unsigned pad_[2];
     float rho[VQ_MAX_K];
     int pend_t[FLOW_PEND_MAX];
-    float pend_stat[FLOW_PEND_MAX][VQ_MAX_K];
+    int ktab[6][FLOW_KTAB];          // per stage kind: the workgroup's chunk sequence (see k_flow)
 };
 constexpr int FLOW_CTRL_OFF = (FLOW_LDS - (int)sizeof(FlowCtrl)) & ~255;
 
-// How one kind of stage is split over the grid (computed on the host).  The chunks of a
-// stage are ordered window-major: window w (columns of groups [w gw, ...)), then tile,
+// How one kind of stage is split over the grid (computed on the host), in steps: a step
+// is the two chunks of groups 2g, 2g + 1 of a tile (16 rows x 256 columns); below, a
+// "chunk" of a plan is such a step.  The chunks of a stage are ordered window-major: window w (columns of groups [w gw, ...)), then tile,
 // then group; workgroup i < nwe takes the contiguous range [i q + min(i, r), ... + q +
 // (i < r)), which holds at least one whole unit (a tile's chunks in one window).
 struct KindPlan {
     int rows, cols;     // output features (gate|up: 2 FF), input features
-    int T, G;           // tiles of 16 rows, groups of 128 columns
+    int T, G;           // tiles of 16 rows, steps of 256 columns per tile
     int nwin, gw, glast;// windows: nwin - 1 of gw groups, then one of glast
-    int cb;             // chunk bytes
+    int cb;             // bytes of a step (two chunks)
     int nwe, q, r;      // workgroups with work; chunks per workgroup
     int xs;             // LDS row stride of the activation window (bytes)
     int n_in;           // elements rho normalises (0: no rho)

@@ -100,9 +100,11 @@ def test_linear_workspace_is_small_and_exact():
 
 def test_tiled_bytes():
     for fmt, per in ((vq.FMT_Q4, 1152), (vq.FMT_Q4_MIN, 1280), (vq.FMT_MXFP4, 1088)):
-        assert vq.lib.vq_tiled_bytes(fmt, 16, 128) == per
+        # groups of 128 columns come in pairs (one step of the streaming kernel)
+        assert vq.lib.vq_tiled_bytes(fmt, 16, 128) == 2 * per
+        assert vq.lib.vq_tiled_bytes(fmt, 16, 256) == 2 * per
         # partial tiles and groups are padded to whole chunks
-        assert vq.lib.vq_tiled_bytes(fmt, 77, 1056) == 5 * 9 * per
+        assert vq.lib.vq_tiled_bytes(fmt, 77, 1056) == 5 * 10 * per
         assert vq.lib.vq_tiled_bytes(fmt, 5120, 17408) == 320 * 136 * per
         # every weight's 4 bits and its block's scale (and min) are stored once, no more
         if fmt == vq.FMT_Q4_MIN:
