@@ -137,8 +137,10 @@ bool make_plan(KindPlan& P, int fmt, int K, int rows, int cols, int tiles, int n
     return true;
 }
 
-size_t plan_parts_floats(const KindPlan& P, int pbytes) {
-    const size_t slots = P.nwin == 1 ? 2 * (size_t)P.nwe : 2 * (size_t)P.nwin * P.T;
+size_t plan_parts_floats(const KindPlan& P, int pbytes, int nwg, int stages) {
+    // one window: two slots per workgroup boundary and stage of a launch; several: two per
+    // unit, reused by every stage
+    const size_t slots = P.nwin == 1 ? 2 * (size_t)nwg * stages : 2 * (size_t)P.nwin * P.T;
     return slots * (size_t)(pbytes / 4);
 }
 size_t plan_counters(const KindPlan& P) { return P.nwin == 1 ? (size_t)P.nwe : (size_t)P.T; }
@@ -211,7 +213,7 @@ int pass_plan(const Shapes& s, int K, int nwg, PassPlan* pp) {
         // rho of stage kind k normalises the previous stage's output; the first stage's is set per stage
         pp->kp[k].n_in = k == SK_DOWN ? s.FF : s.H;
         pp->kp[k].stats = k == SK_LM ? 0 : 1;
-        pp->parts_floats = std::max(pp->parts_floats, plan_parts_floats(pp->kp[k], pp->pbytes));
+        pp->parts_floats = std::max(pp->parts_floats, plan_parts_floats(pp->kp[k], pp->pbytes, nwg, 4 * FLOW_MAX_LAYERS + 1));
         pp->counters = std::max(pp->counters, plan_counters(pp->kp[k]));
     }
     return VQ_OK;
@@ -325,7 +327,7 @@ int linear_layout(const vq_tiled* W, int K, int nwg, LinearLayout* L) {
                     nwg, K);
     L->kp.n_in = 0;
     L->kp.stats = 0;
-    L->off_cnt = align_up(plan_parts_floats(L->kp, L->pbytes) * 4, 256);
+    L->off_cnt = align_up(plan_parts_floats(L->kp, L->pbytes, L->kp.nwe, 1) * 4, 256);
     const size_t words = plan_counters(L->kp) + DONE_STRIDE;
     L->zero_words = words;
     L->total = L->off_cnt + align_up(words * 4, 256);

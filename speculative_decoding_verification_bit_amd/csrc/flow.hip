@@ -266,38 +266,48 @@ __device__ __forceinline__ int ktab(const FlowCtrl& C, int kind, int f) { return
 // workgroup's sequence in every stage.  It keeps the stage, the position k, the current
 // span [k0, k1) (a run of chunks inside one unit) with the span's unit (window w, tile t)
 // and the group i0 of its first chunk.  A consume walk also counts the units it has left
-// behind (pclose) and whether it has entered a stage (pnew).  All fields are wave-uniform.
+// behind (pclose) and whether it has entered a stage (pnew).  The stage's row of the
+// sequence table is copied into the walk when it enters the stage (one burst of LDS
+// reads), so that stepping needs no memory access.  All fields are wave-uniform.
 struct Cur {
     int s, kind, n, k, k0, k1, w, t, i0;
     int done, pclose, pnew;
+    int lenA, bw, bt, bi, bk1, T, G, gw, glast, nwin, cb, wlo;
 };
 
-__device__ __forceinline__ Cur span_first(const FlowCtrl& C, Cur c) {
-    const int lenA = ktab(C, c.kind, KT_LENA);
+__device__ __forceinline__ Cur load_row(const FlowCtrl& C, Cur c) {
+    const int4* r = (const int4*)C.ktab[c.kind];
+    const int4 a = r[0], b = r[1], d = r[2], e = r[3], f = r[4];
+    // KT_N, KT_LENA, KT_WLO, KT_AW | KT_AT, KT_AI, KT_BW, KT_BT | KT_BI, KT_BK1, KT_T, KT_G |
+    // KT_GW, KT_GLAST, KT_NWIN, KT_CB | KT_XS
+    c.n = uni(a.x); c.lenA = uni(a.y); c.wlo = uni(a.z);
+    c.bw = uni(b.z); c.bt = uni(b.w); c.bi = uni(d.x); c.bk1 = uni(d.y);
+    c.T = uni(d.z); c.G = uni(d.w); c.gw = uni(e.x); c.glast = uni(e.y); c.nwin = uni(e.z); c.cb = uni(e.w);
+    (void)f;
+    // the first span: segment A's, else segment B's
     c.k0 = 0;
-    if (lenA > 0) {
-        c.w = ktab(C, c.kind, KT_AW); c.t = ktab(C, c.kind, KT_AT); c.i0 = ktab(C, c.kind, KT_AI);
-        c.k1 = lenA;
+    if (c.lenA > 0) {
+        c.w = uni(a.w); c.t = uni(b.x); c.i0 = uni(b.y); c.k1 = c.lenA;
     } else {
-        c.w = ktab(C, c.kind, KT_BW); c.t = ktab(C, c.kind, KT_BT); c.i0 = ktab(C, c.kind, KT_BI);
-        c.k1 = ktab(C, c.kind, KT_BK1);
+        c.w = c.bw; c.t = c.bt; c.i0 = c.bi; c.k1 = c.bk1;
     }
     return c;
 }
+static_assert(KT_N == 0 && KT_AW == 3 && KT_AT == 4 && KT_BW == 6 && KT_BI == 8 && KT_T == 10 &&
+              KT_GW == 12 && KT_CB == 15 && KT_XS == 16, "sequence table row layout");
 
-__device__ __forceinline__ Cur span_next(const FlowCtrl& C, Cur c) {
-    const int lenA = ktab(C, c.kind, KT_LENA);
-    if (lenA > 0 && c.k0 == 0) {
-        c.w = ktab(C, c.kind, KT_BW); c.t = ktab(C, c.kind, KT_BT); c.i0 = ktab(C, c.kind, KT_BI);
-        c.k0 = lenA;
-        c.k1 = ktab(C, c.kind, KT_BK1);
+__device__ __forceinline__ Cur span_next(Cur c) {
+    if (c.lenA > 0 && c.k0 == 0) {
+        c.w = c.bw; c.t = c.bt; c.i0 = c.bi;
+        c.k0 = c.lenA;
+        c.k1 = c.bk1;
     } else {
         c.t = uni(c.t + 1);
-        if (c.t == ktab(C, c.kind, KT_T)) {
+        if (c.t == c.T) {
             c.t = 0;
             c.w = uni(c.w + 1);
         }
-        const int gU = c.w == ktab(C, c.kind, KT_NWIN) - 1 ? ktab(C, c.kind, KT_GLAST) : ktab(C, c.kind, KT_GW);
+        const int gU = c.w == c.nwin - 1 ? c.glast : c.gw;
         c.k0 = c.k1;
         c.k1 = uni(min(c.k0 + gU, c.n));
         c.i0 = 0;
@@ -317,13 +327,12 @@ __device__ __forceinline__ Cur seek(KArgs& A, const FlowCtrl& C, Cur c, int cw, 
                 return c;
             }
             c.kind = kind_of(A, c.s);
-            c.n = ktab(C, c.kind, KT_N);
+            c = load_row(C, c);
             c.k = cw;
             if (c.n == 0 || (!CONSUME && c.k >= c.n)) {
                 c.s = uni(c.s + 1);
                 continue;
             }
-            c = span_first(C, c);
             if (CONSUME && c.k < c.n) c.pnew = 1;
             new_stage = 0;
         }
@@ -334,7 +343,7 @@ __device__ __forceinline__ Cur seek(KArgs& A, const FlowCtrl& C, Cur c, int cw, 
             new_stage = 1;
             continue;
         }
-        c = span_next(C, c);
+        c = span_next(c);
     }
     return c;
 }
@@ -418,10 +427,9 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         uint32_t ioff = 0, istep = 0;
         auto i_set = [&]() __attribute__((always_inline)) {
             iW = mat_of(A, ic.s, ic.kind);
-            const int cb = ktab(C, ic.kind, KT_CB);
-            istep = (uint32_t)uni(NCW * cb);
-            const int g = ic.w * ktab(C, ic.kind, KT_GW) + ic.i0 + (ic.k - ic.k0);
-            ioff = (uint32_t)uni((ic.t * ktab(C, ic.kind, KT_G) + g) * cb);
+            istep = (uint32_t)uni(NCW * ic.cb);
+            const int g = ic.w * ic.gw + ic.i0 + (ic.k - ic.k0);
+            ioff = (uint32_t)uni((ic.t * ic.G + g) * ic.cb);
         };
         if (!ic.done) i_set();
         Cur cc = {};
@@ -429,7 +437,7 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         cc = seek<true>(A, C, cc, cw, 1);
         uint32_t coff = 0;
         auto c_set = [&]() __attribute__((always_inline)) {
-            coff = (uint32_t)uni((cc.w - ktab(C, cc.kind, KT_WLO)) * xoff1 + (cc.i0 + (cc.k - cc.k0)) * 512);
+            coff = (uint32_t)uni((cc.w - cc.wlo) * xoff1 + (cc.i0 + (cc.k - cc.k0)) * 512);
         };
         if (!cc.done) c_set();
 
@@ -601,49 +609,27 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         const int n_in = s == 0 ? 0 : uni(A.kp[kind].n_in);   // stage 0 is not scaled
         const bool stats_on = A.kp[kind].stats != 0;
 
-        // -------- rho of the previous output (after every workgroup completed it)
-        if (n_in > 0) {
-            if (idx > 0) {
-                const unsigned* dn = A.done + (size_t)(s - 1) * DONE_WORDS;
-                unsigned spins = 0;
-                for (;;) {
-                    unsigned v = 0;
-                    if (lane < DONE_REPL) v = ld_dev_u32(dn + lane * DONE_STRIDE);
-                    unsigned sum = 0;
+        // -------- the previous stage complete on every workgroup
+        if (n_in > 0 && idx > 0) {
+            const unsigned* dn = A.done + (size_t)(s - 1) * DONE_WORDS;
+            unsigned spins = 0;
+            for (;;) {
+                unsigned v = 0;
+                if (lane < DONE_REPL) v = ld_dev_u32(dn + lane * DONE_STRIDE);
+                unsigned sum = 0;
 #pragma unroll
-                    for (int r = 0; r < DONE_REPL; ++r) sum += __builtin_amdgcn_readlane(v, r);
-                    if (sum >= (unsigned)A.nwg) break;
-                    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
-                        __hip_atomic_load(&C.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
-                        break;
-                    __builtin_amdgcn_s_sleep(2);
-                    if (++spins > SPIN_GLOBAL) {
-                        __hip_atomic_store(&C.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                        __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
+                for (int r = 0; r < DONE_REPL; ++r) sum += __builtin_amdgcn_readlane(v, r);
+                if (sum >= (unsigned)A.nwg) break;
+                if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
+                    __hip_atomic_load(&C.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
+                    break;
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins > SPIN_GLOBAL) {
+                    __hip_atomic_store(&C.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
                 }
             }
-            // sum over workgroups in a fixed order: lane l adds workgroups l, l + 64, ...,
-            // then the wave's fixed tree
-            const float* st = (const float*)(A.ws + A.off_stats) + (size_t)(s - 1) * A.stats_stride;
-            float a[VQ_MAX_K];
-#pragma unroll
-            for (int m = 0; m < VQ_MAX_K; ++m) a[m] = 0.f;
-            for (int ww = lane; ww < A.nwg; ww += 64) {
-#pragma unroll
-                for (int m = 0; m < VQ_MAX_K; ++m)
-                    if (m < K) a[m] += ld_dev_f32(st + (size_t)ww * K + m);
-            }
-#pragma unroll
-            for (int m = 0; m < VQ_MAX_K; ++m) {
-                if (m < K) {
-                    const float t = wave_sum(a[m]);
-                    if (lane == 0) C.rho[m] = __frcp_rn(__fsqrt_rn(__fdiv_rn(t, (float)n_in)));
-                }
-            }
-        } else if (lane < VQ_MAX_K) {
-            C.rho[lane] = 1.0f;
         }
 
         // -------- the stage's activation windows into LDS
@@ -680,6 +666,40 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             for (int i = lane; i < K * A.H; i += 64) keep[i] = A.x0[i];
         }
         if (lane == 0) st_rel(&C.xready, (unsigned)idx + 1u);
+
+        // -------- rho of the previous output (only the epilogues need it: after the
+        // activations are released to the compute waves)
+        if (n_in > 0) {
+            // sum over workgroups in a fixed order: lane l adds workgroups 4l .. 4l + 3 (and
+            // 256 on), then the wave's fixed tree; the sums of one column are contiguous, so
+            // every load of the stage's figures is in flight at once
+            const float* st = (const float*)(A.ws + A.off_stats) + (size_t)(s - 1) * A.stats_stride;
+            float a[VQ_MAX_K];
+#pragma unroll
+            for (int m = 0; m < VQ_MAX_K; ++m) a[m] = 0.f;
+            for (int b = 0; b < A.nwg; b += 256) {
+                f4_t v[VQ_MAX_K];
+#pragma unroll
+                for (int m = 0; m < VQ_MAX_K; ++m)
+                    v[m] = *(const f4_t*)(st + (size_t)min(m, K - 1) * FLOW_MAX_WG + b + 4 * lane);
+#pragma unroll
+                for (int m = 0; m < VQ_MAX_K; ++m) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (b + 4 * lane + i < A.nwg) a[m] += v[m][i];
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < VQ_MAX_K; ++m) {
+                if (m < K) {
+                    const float t = wave_sum(a[m]);
+                    if (lane == 0) C.rho[m] = __frcp_rn(__fsqrt_rn(__fdiv_rn(t, (float)n_in)));
+                }
+            }
+        } else if (lane < VQ_MAX_K) {
+            C.rho[lane] = 1.0f;
+        }
+
 
         // -------- units: reduce the 11 partials, then epilogue or part
         const float* rho = C.rho;
@@ -732,7 +752,7 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         };
         // split-tile bookkeeping
         auto part_slot = [&](int U, int t, int side) __attribute__((always_inline)) -> float* {
-            const int sl = P.nwin == 1 ? 2 * (side == 0 ? w : w - 1) + side : 2 * U + side;
+            const int sl = P.nwin == 1 ? (idx * A.nwg + (side == 0 ? w : w - 1)) * 2 + side : 2 * U + side;
             return A.parts + (size_t)sl * (pbytes >> 2);
         };
         auto counter = [&](int t, int side) __attribute__((always_inline)) -> unsigned* {
@@ -757,7 +777,11 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
 #pragma unroll
                 for (int c = 0; c < NCW; ++c) sum += *(const f4_t*)(lds + A.ring_off + ((int)slot * NCW + c) * pbytes + 16 * lane);
             }
-            if (lane == 0) st_rel(&C.pfree[slot], round + 1u);
+            // free the slot once the ring reads are done (an LDS wait only: a release here
+            // would also wait for every epilogue store in flight)
+            __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0)
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (lane == 0) __hip_atomic_store(&C.pfree[slot], round + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             // where this unit's chunks lie
             const int gl = uw == P.nwin - 1 ? P.glast : P.gw;
             const int f = uw * P.T * P.gw + ut * gl;
@@ -827,12 +851,13 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             f4_t sum = zero4;
             if (lane < plane) {
                 if (P.nwin == 1) {
-                    const float* p0 = A.parts + (size_t)(2 * (w - 1)) * (pbytes >> 2);
+                    // written once in the launch, after this workgroup last read the lines
+                    // (a fresh launch starts with clean caches): plain loads see them
+                    const float* p0 = A.parts + (size_t)((idx * A.nwg + w - 1) * 2) * (pbytes >> 2);
                     const float* p1 = p0 + (pbytes >> 2);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sum[i] = ld_dev_f32(p0 + 4 * lane + i);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sum[i] += ld_dev_f32(p1 + 4 * lane + i);
+                    const f4_t v0 = *(const f4_t*)(p0 + 4 * lane);
+                    const f4_t v1 = *(const f4_t*)(p1 + 4 * lane);
+                    sum = v0 + v1;
                 } else {
                     for (int win = 0; win < P.nwin; ++win) {
                         const int gl = win == P.nwin - 1 ? P.glast : P.gw;
@@ -853,11 +878,11 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
 
         // -------- report the stage: sums of squares, then the completion counter
         if (stats_on && n16 == 0) {
-            float* st = (float*)(A.ws + A.off_stats) + (size_t)s * A.stats_stride + (size_t)w * K;
+            float* st = (float*)(A.ws + A.off_stats) + (size_t)s * A.stats_stride + w;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * q4 + i;
-                if (m < K) st_dev_f32(st + m, stat[i]);
+                if (m < K) st_dev_f32(st + (size_t)m * FLOW_MAX_WG, stat[i]);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);

@@ -76,6 +76,7 @@ struct FlowCtrl {
     float rho[VQ_MAX_K];
     int pend_t[FLOW_PEND_MAX];
     int ktab[6][FLOW_KTAB];          // per stage kind: the workgroup's chunk sequence (see k_flow)
+    uint8_t junk[1024];              // destination of cache-warming loads (never read)
 };
 constexpr int FLOW_CTRL_OFF = (FLOW_LDS - (int)sizeof(FlowCtrl)) & ~255;
 
@@ -115,7 +116,7 @@ struct FlowArgs {
     size_t layer_bytes;       // per layer: [x, y] of its 4 stages
     size_t off_x[4], off_y[4];
     size_t off_fx;            // lm_head input
-    size_t off_stats;         // per stage s < 4L: [FLOW_MAX_WG][K] floats
+    size_t off_stats;         // per stage s < 4L: [K][FLOW_MAX_WG] floats
     size_t stats_stride;      // floats per stage
     float* parts;             // split-tile partial sums
     unsigned* cnt;            // split-tile arrival counters (zero between launches)
@@ -133,7 +134,7 @@ bool make_plan(KindPlan& P, int fmt, int K, int rows, int cols, int tiles, int n
 // LDS bytes left for the activation windows with K columns, and the ring geometry.
 void lds_plan(int K, int* nsp, int* pbytes, int* ring_off, int* xcap);
 // Floats of split-tile partials and words of counters a plan needs.
-size_t plan_parts_floats(const KindPlan& P, int pbytes);
+size_t plan_parts_floats(const KindPlan& P, int pbytes, int nwg, int stages);
 size_t plan_counters(const KindPlan& P);
 
 hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
