@@ -2,23 +2,24 @@
 """Verify-pass benchmark on one MI355X.
 
 One step = one pass of the whole hot path over one batch: vq_decode_pass streams every
-weight of the 27B-class stack (64 layers of hidden 5120, kv 1024, ffn 17408, plus a
+weight of the 27B-class stack once (64 layers of hidden 5120, kv 1024, ffn 17408, plus a
 151936-row lm_head; 4-bit block-32 codes with fp16 scale and fp16 min, 13,698,252,800
-bytes) once for a K-wide window, then vq_verify_accept turns the logits into tokens.
-The headline line is K = 1 (plain decode, sampled with temperature 0.6, top-p 0.95,
-min-p 0.05); K = 4 (greedy, drafts agreeing with the target argmax at alpha 0.7),
-K = 8 (the sampling path over 1,000 synthetic windows) and K = 16 (MXFP4 stack) are
-reported in the same JSON line under "sweep".
+bytes) for a K-wide window, then vq_verify_accept turns the logits into tokens.  The
+headline line is K = 1 (plain decode; the bonus token sampled with temperature 0.6,
+top-p 0.95, min-p 0.05).  K = 4 (greedy, drafts agreeing with the target argmax at
+alpha 0.7), K = 8 (the sampling path over 1,000 synthetic windows) and K = 16 (MXFP4
+stack) are reported in the same JSON line under "sweep".
 
-Inputs are synthetic and seeded (synth): weights are generated on the host and copied
-to HBM before timing.  Timed steps replay a captured HIP graph of the step; the weight
-stream is HBM-bound, so "value" is weight bytes per pass / seconds per step.
+Inputs are synthetic and seeded (synth): weights are generated on the host, copied to
+HBM and tiled before timing.  Timed steps replay a captured HIP graph of the step; the
+weight stream is HBM-bound, so "value" is weight bytes per pass / seconds per step.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--sweep 4,8,16] [--no-cpu]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,8 +31,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak
+STREAM_CEILING_GBPS = 7150.0    # one launch streaming-reading the stack's 13.7 GB on this GPU
 METRIC = "verify-pass weight GB/s (% of ~8 TB/s HBM) and passes/s at K=1,4,8,16"
 SAMPLER = dict(T=0.6, top_p=0.95, min_p=0.05)
+ALPHAS = (0.5, 0.7, 0.9)
+PROFILE = os.path.join(ROOT, "profiles", "k_flow_q4min_k1_27b_decode.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "speculative_decoding_verification_bit_amd", "csrc", f)
+                  for f in ("flow.hip", "vq_device.h", "vq_internal.h")]
 
 
 def log(*a):
@@ -39,8 +45,29 @@ def log(*a):
 
 
 def tau(alpha: float, k: int) -> float:
-    """Expected tokens per pass with k drafts accepted independently with prob. alpha."""
+    """Expected tokens per pass with k drafts each accepted independently with prob. alpha."""
     return (1 - alpha ** (k + 1)) / (1 - alpha)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def profiled_traffic():
+    """HBM bytes per launch of k_flow<Q4_MIN, K 1> from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None when the
+    kernel sources have changed since the counters were taken."""
+    try:
+        fields = dict(line.split(": ", 1) for line in open(PROFILE).read().splitlines()
+                      if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ")))
+    except OSError:
+        return None
+    if fields.get("source_sha256") != source_hash():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def upload_stack(vq, synth, fmt, seed, threads):
@@ -53,13 +80,12 @@ def upload_stack(vq, synth, fmt, seed, threads):
             r, c = shape.mat_shape(mid)
             L[name] = vq.DeviceMatrix.from_host(synth.weight_matrix(fmt, seed, l, mid, r, c, threads=threads))
         layers.append(L)
-        if l % 16 == 15:
-            log(f"uploaded {l + 1}/{shape.n_layers} layers ({time.time() - t0:.1f} s)")
     r, c = shape.mat_shape(synth.MAT_LM_HEAD)
     lm = vq.DeviceMatrix.from_host(synth.weight_matrix(fmt, seed, shape.n_layers, synth.MAT_LM_HEAD, r, c,
                                                        threads=threads))
     model = vq.DeviceModel(layers, lm)
-    log(f"stack fmt {fmt}: {model.nbytes} bytes on the device in {time.time() - t0:.1f} s")
+    del layers, lm
+    log(f"stack fmt {fmt}: {model.nbytes} bytes tiled on the device in {time.time() - t0:.1f} s")
     return model
 
 
@@ -86,124 +112,103 @@ def time_graph(torch, step, steps, warmup):
     return t0.elapsed_time(t1) / steps, g
 
 
-def time_eager(torch, step, steps):
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
-
-
-PROFILE = os.path.join(ROOT, "profiles", "k_stage_valu_q4min_k1_27b_decode.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "speculative_decoding_verification_bit_amd", "csrc", f)
-                  for f in ("linear.hip", "vq_device.h", "vq_internal.h")]
-
-
-def profiled_traffic(kernel_key):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the summary
-    covers another kernel or the kernel sources have changed since the counters were taken."""
-    import hashlib
-    try:
-        fields = dict(line.split(": ", 1) for line in open(PROFILE).read().splitlines()
-                      if line.startswith(("traffic_bytes_per_launch: ", "source_sha256: ", "kernel_key: ")))
-    except OSError:
-        return None
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
-    if fields.get("source_sha256") != h.hexdigest() or fields.get("kernel_key") != kernel_key:
-        return None
-    return int(fields["traffic_bytes_per_launch"])
-
-
-def stage_weight_bytes(shape, synth, fmt):
-    """Weight bytes of each stage of a pass: q|k|v, o, gate|up, down per layer, lm_head."""
-    H, KV, FF, V = shape.hidden, shape.kv_dim, shape.ffn, shape.vocab
-    per = [(H + 2 * KV) * H, H * H, 2 * FF * H, H * FF]
-    w = [per[i % 4] for i in range(4 * shape.n_layers)] + [V * H]
-    return [n * synth.bytes_per_weight(fmt) for n in w]
-
-
-def time_stream_kernel(torch, vq, model, x0, logits, ws, passes, path, stage_bytes):
-    """Per-launch durations of the weight-streaming kernels, from HIP events that the
-    library records around each launch on the stream it launches on, grouped by kernel
-    instantiation (single- or multi-chunk items).  The event brackets themselves
-    serialise the launches (about 2 us each), so every group's time is scaled by the
-    ratio of an unbracketed pass (two events on the same stream around decode_pass) to
-    the sum of the bracketed launch times.  Returns {name: (launches per pass, ms per pass,
-    weight bytes per pass, raw bracketed ms per pass)} and the launches per pass."""
-    n_st = 4 * len(model.layers) + 1
-    events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_st)]
+def launch_times(torch, vq, model, x0, logits, ws, passes):
+    """Durations of the pass kernel's launches (one cooperative launch per 16 layers, the
+    last with the lm_head), from HIP events that the library records on the stream it
+    launches on, and the weight bytes each launch streams."""
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(16)]
     for ev in events:
         ev.record()                     # creates the HIP event handles
     torch.cuda.synchronize()
-    groups = {}
-    n = 0
-    bracketed = 0.0
+    tot, n = None, 0
     for _ in range(passes):
-        runs = vq.decode_pass_timed(model, x0, events, logits, ws, path=path)
+        _, _, n = vq.decode_pass_launch(model, x0, logits, ws, vq.LAUNCH_AUTO, events)
         torch.cuda.synchronize()
-        n = len(runs)
-        for i, r in enumerate(runs):
-            key = "persistent" if r == 0 else "stream" if r == -1 else "rows" if r < 0 else "multi" if r > 1 else "single"
-            ms = events[2 * i].elapsed_time(events[2 * i + 1])
-            bracketed += ms
-            b = stage_bytes[i] if r > 0 or r < -1 else sum(stage_bytes) / n
-            c, t, bb = groups.get(key, (0, 0.0, 0.0))
-            groups[key] = (c + 1, t + ms, bb + b)
-    # the same passes without per-launch events
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    plain = 0.0
-    for _ in range(passes):
-        e0.record()
-        vq.decode_pass(model, x0, logits, path=path, ws=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        plain += e0.elapsed_time(e1)
-    scale = min(1.0, plain / bracketed) if bracketed > 0 else 1.0
-    return {k: (c / passes, t * scale / passes, b / passes, t / passes) for k, (c, t, b) in groups.items()}, n
+        ms = np.array([events[2 * i].elapsed_time(events[2 * i + 1]) for i in range(n)])
+        tot = ms if tot is None else tot + ms
+    b = []
+    for i in range(n):
+        layers = model.tiled[16 * i:16 * (i + 1)]
+        nb = sum(m.nbytes for L in layers for m in L.values())
+        if i == n - 1:
+            nb += model.lm_head.nbytes
+        b.append(nb)
+    return tot / passes, np.array(b, dtype=np.float64)
 
 
 def cpu_baseline(synth, oracle_mod, budget_s: float):
-    """The fp64 oracle on host cores: whole layers of the stack at K = 1 until `budget_s`
-    of oracle time, scaled to the full pass; plus acceptance of C4 windows."""
+    """The fp64 oracle on the host's cores (test infrastructure, timed as a baseline).
+
+    Linear: whole layers of the 27B stack at K = 1 on all threads until budget_s of oracle
+    time, scaled to the pass; the same on one thread for one o matrix; one layer at K =
+    4, 8, 16 on all threads.  Acceptance: a few windows of the K = 8 sampling workload."""
     threads = min(16, len(os.sched_getaffinity(0)))
+    model_name = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model_name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     shape = synth.SHAPE_27B
+    total_w = shape.n_weights()
+    bpw = synth.bytes_per_weight(synth.FMT_Q4_MIN)
+    mats = {}
+
+    def mat(l, mid):
+        key = (l, mid)
+        if key not in mats:
+            r, c = shape.mat_shape(mid)
+            mats[key] = synth.weight_matrix(synth.FMT_Q4_MIN, 0, l, mid, r, c, threads=threads)
+        return mats[key]
+
     x = {c: synth.activations(0, 1, c) for c in (shape.hidden, shape.ffn)}
     weights, spent, layers = 0, 0.0, 0
     for l in range(shape.n_layers):
         for mid in range(7):
-            r, c = shape.mat_shape(mid)
-            m = synth.weight_matrix(synth.FMT_Q4_MIN, 0, l, mid, r, c, threads=threads)
+            m = mat(l, mid)
             t0 = time.time()
-            oracle_mod.linear(m, x[c], threads=threads)
+            oracle_mod.linear(m, x[m.cols], threads=threads)
             spent += time.time() - t0
-            weights += r * c
+            weights += m.rows * m.cols
         layers += 1
         if spent >= budget_s:
             break
     w_per_s = weights / spent
-    total_w = shape.n_weights()
-    gbps = w_per_s * synth.bytes_per_weight(synth.FMT_Q4_MIN) / 1e9
+    m = mat(0, synth.MAT_O)
+    t0 = time.time()
+    oracle_mod.linear(m, x[m.cols], threads=1)
+    one_thread = m.rows * m.cols / (time.time() - t0)
+    per_k = {}
+    layer_w = sum(r * c for r, c in (shape.mat_shape(mid) for mid in range(7)))
+    for K in (4, 8, 16):
+        xk = synth.activations(0, K, m.cols)
+        t0 = time.time()
+        oracle_mod.linear(m, xk, threads=threads)
+        per_k[f"K{K}_one_layer_s"] = round((time.time() - t0) * layer_w / (m.rows * m.cols), 3)
+    mats.clear()
     c4 = synth.C4
-    nwin = 2
+    nwin = 4
     t, d = synth.logits_batch(c4["logits"], 0, nwin, threads=threads)
     f32 = lambda v: float(np.float32(v))
     t0 = time.time()
-    oracle_mod.accept(oracle_mod.MODE_SAMPLE, t, d, None, oracle_mod.DRAFT_Q_SAMPLE, f32(c4["T"]),
-                      f32(c4["top_p"]), f32(c4["min_p"]), 0.0, c4["philox_seed"], 0, threads=threads)
+    r = oracle_mod.accept(oracle_mod.MODE_SAMPLE, t, d, None, oracle_mod.DRAFT_Q_SAMPLE, f32(c4["T"]),
+                          f32(c4["top_p"]), f32(c4["min_p"]), 0.0, c4["philox_seed"], 0, threads=threads)
     acc_s = time.time() - t0
     return {
-        "value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "value": round(w_per_s * bpw / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "cpu_model": model_name,
         "passes_per_s": w_per_s / total_w,
+        "single_thread_gbps": round(one_thread * bpw / 1e9, 4),
         "sample": (f"{layers} of 64 layers (7 matrices each, {weights} weights) of the 27B stack at "
                    f"K=1, {spent:.1f} s of fp64 oracle time on {threads} threads, scaled to the "
-                   f"{total_w}-weight pass; plus {nwin} C4 acceptance windows (K 8, V 151936)"),
-        "accept_windows_per_s": nwin / acc_s,
+                   f"{total_w}-weight pass; one 5120x5120 matrix on 1 thread; one layer at K=4/8/16 on "
+                   f"{threads} threads (the o matrix timed, scaled by weights); {nwin} C4 acceptance windows (K 8, V 151936)"),
+        **per_k,
+        "accept_windows_per_s": round(nwin / acc_s, 3),
+        "accept_near_threshold_windows": int(np.count_nonzero(r["near"])),
+        "accept_windows_checked": nwin,
     }
 
 
@@ -214,17 +219,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--sweep", default="4,8,16", help="other K values to time ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time to sample")
+    ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle time to sample")
     ap.add_argument("--threads", type=int, default=16, help="host threads for input generation")
-    ap.add_argument("--no-compare", action="store_true",
-                    help="skip timing the other launch mode (e.g. under a profiler)")
+    ap.add_argument("--no-compare", action="store_true", help="skip timing the staged launch mode")
     ap.add_argument("--calib-copy", action="store_true",
-                    help="also run a 1 GiB device copy (reference for HBM counter scaling)")
+                    help="first copy 1 GiB with torch (the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the verify pass on one GPU; runs on more than one GPU are not "
-              "part of this benchmark (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures the verify pass on one GPU: runs on more than one GPU are not part "
+              "of this benchmark (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -234,6 +238,13 @@ def main():
     dev = torch.device("cuda:0")
     shape = synth.SHAPE_27B
     H, V = shape.hidden, shape.vocab
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     # ---------------------------------------------------------------- K = 1
     model = upload_stack(vq, synth, synth.FMT_Q4_MIN, 0, args.threads)
@@ -267,31 +278,21 @@ def main():
     step1, x0_1, logits1, ws1 = make_step(model, 1, sampled_bonus)
     log("K=1: capture and time")
     ms1, g1 = time_graph(torch, step1, args.steps, args.warmup)
-    eager1 = time_eager(torch, step1, max(3, args.steps // 4))
-    sbytes = stage_weight_bytes(shape, synth, synth.FMT_Q4_MIN)
-    groups, n_launch = time_stream_kernel(torch, vq, model, x0_1, logits1, ws1, args.steps, vq.PATH_AUTO, sbytes)
-    # the dominant kernel: the instantiation with the most time per pass
-    dom = max(groups, key=lambda k: groups[k][1])
-    n_dom, ms_dom, b_dom, raw_dom = groups[dom]
-    avg_launch_ms = ms_dom / n_dom
-    bytes_per_launch = b_dom / n_dom
-    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
-    kname = {"single": "k_stage_valu<1, 1, false, false> (Q4_MIN, K 1, one chunk per item)",
-             "multi": "k_stage_valu<1, 1, true, false> (Q4_MIN, K 1, chunk runs per item)",
-             "rows": "k_rows_s<1, 1, NSG> (Q4_MIN, K 1, row strips)",
-             "stream": "k_stream<1, 1> (Q4_MIN, K 1, stream-ahead)",
-             "persistent": "k_pass<1, 1, false> (Q4_MIN, K 1, persistent)"}[dom]
-    value = wbytes / (ms1 * 1e-3) / 1e9
-    log(f"K=1 step {ms1:.3f} ms ({value:.0f} GB/s), eager {eager1:.3f} ms; launches per pass {n_launch}; "
-        + "; ".join(f"{k}: {c:.0f} launches {t:.3f} ms ({r:.3f} ms bracketed) {b / t / 1e6:.0f} GB/s"
-                    for k, (c, t, b, r) in groups.items()))
     del g1
-    other1 = None
+    assert model.barrier_error(1, ws1) == 0, "a grid wait of the pass timed out"
+    per_launch_ms, per_launch_bytes = launch_times(torch, vq, model, x0_1, logits1, ws1, args.steps)
+    assert model.barrier_error(1, ws1) == 0, "a grid wait of the pass timed out"
+    achieved = float(per_launch_bytes.sum() / (per_launch_ms.sum() * 1e-3) / 1e9)
+    value = wbytes / (ms1 * 1e-3) / 1e9
+    log(f"K=1 step {ms1:.3f} ms ({value:.0f} GB/s); launches "
+        + ", ".join(f"{m * 1e3:.0f} us" for m in per_launch_ms) + f"; kernel {achieved:.0f} GB/s")
+    staged1 = None
     if not args.no_compare:
-        other = vq.LAUNCH_PERSISTENT if n_launch > 16 else vq.LAUNCH_STAGED
-        other1 = time_graph(torch, lambda: vq.decode_pass(model, x0_1, logits1, path=other, ws=ws1),
-                            args.steps, args.warmup)[0]
-        log(f"K=1 pass with the other launch mode ({'persistent' if n_launch > 16 else 'staged'}): {other1:.3f} ms")
+        staged1 = time_graph(torch, lambda: vq.decode_pass_launch(model, x0_1, logits1, ws1, vq.LAUNCH_STAGED),
+                             max(3, args.steps // 4), 1)[0]
+        log(f"K=1 pass with one launch per stage: {staged1:.3f} ms")
+    traffic = profiled_traffic()
+    pps1 = 1000.0 / ms1
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms1, 4), "higher_is_better": True, "scaling": "weak",
@@ -301,18 +302,19 @@ def main():
                    "kv": shape.kv_dim, "ffn": shape.ffn, "vocab": V, "K": 1,
                    "format": "q4 block-32 + fp16 scale + fp16 min", "weight_bytes": wbytes,
                    "accept": "sample T 0.6 top-p 0.95 min-p 0.05"},
-        "passes_per_s": round(1000.0 / ms1, 2),
+        "passes_per_s": round(pps1, 2),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
-        "implied_tok_s": round(1000.0 / ms1, 2),
-        "eager_ms_per_step": round(eager1, 4),
-        ("persistent_pass_ms" if n_launch > 16 else "staged_pass_ms"): other1 and round(other1, 4),
+        "frac_of_stream_ceiling": round(value / STREAM_CEILING_GBPS, 4),
+        "implied_tok_s": {f"alpha_{a}": round(pps1 * tau(a, 0), 2) for a in ALPHAS},
+        "staged_pass_ms": staged1 and round(staged1, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": profiled_traffic(dom),
-                     "kernel": kname, "launches_per_pass": round(n_dom),
-                     "avg_launch_us": round(avg_launch_ms * 1e3, 3),
-                     "event_bracketed_avg_launch_us": round(raw_dom / n_dom * 1e3, 3),
-                     "bytes_per_launch": round(bytes_per_launch)},
+                     "traffic": None if traffic is None else round(traffic / per_launch_bytes.mean(), 4),
+                     "traffic_bytes_per_launch": traffic,
+                     "kernel": "k_flow<Q4_MIN, K 1> (persistent, 16 layers per launch)",
+                     "launches_per_pass": len(per_launch_ms),
+                     "avg_launch_us": round(float(per_launch_ms.mean()) * 1e3, 3),
+                     "bytes_per_launch": round(float(per_launch_bytes.mean()))},
     }
 
     # ------------------------------------------------------------------ sweep
@@ -328,12 +330,12 @@ def main():
             def acc():
                 vq.verify_accept(vq.MODE_GREEDY, t, draft_tokens=probe["draft_tokens"],
                                  draft_mode=vq.DRAFT_AGREE, alpha=alpha, seed=0, out=probe)
-            acc.probe = probe
             return acc
 
         step4, x0_4, logits4, ws4 = make_step(model, 4, agree)
         ms4, g4 = time_graph(torch, step4, args.steps, args.warmup)
         del g4
+        assert model.barrier_error(4, ws4) == 0
         # measured acceptance on the pass's own logits, fresh Philox windows
         t = logits4.view(1, 4, V).expand(2000, 4, V).contiguous()
         r = vq.verify_accept(vq.MODE_GREEDY, t, draft_mode=vq.DRAFT_AGREE, alpha=alpha, seed=0)
@@ -341,28 +343,23 @@ def main():
         agree_rate = float((r["draft_tokens"] == am.view(1, 3)).float().mean())
         tau_meas = float((r["n_accepted"] + 1).float().mean())
         del t, r
-        ms4v = time_graph(torch, lambda: vq.decode_pass(model, x0_4, logits4, path=vq.PATH_VALU, ws=ws4),
-                          args.steps, args.warmup)[0]
-        ms4m = time_graph(torch, lambda: vq.decode_pass(model, x0_4, logits4, path=vq.PATH_MFMA, ws=ws4),
-                          args.steps, args.warmup)[0]
+        pps = 1000 / ms4
         sweep["K4"] = {"workload": synth.C3["name"], "ms_per_step": round(ms4, 4),
-                       "gbps": round(wbytes / ms4 / 1e6, 2), "passes_per_s": round(1000 / ms4, 2),
+                       "gbps": round(wbytes / ms4 / 1e6, 2), "passes_per_s": round(pps, 2),
                        "frac_of_hbm_peak": round(wbytes / ms4 / 1e6 / HBM_PEAK_GBPS, 4),
-                       "pass_ms_valu": round(ms4v, 4), "pass_ms_mfma": round(ms4m, 4),
+                       "ratio_to_K1_pass": round(ms4 / ms1, 4),
                        "accept": "greedy, drafts agree with the target argmax at alpha 0.7",
                        "measured_alpha": round(agree_rate, 4), "measured_tau": round(tau_meas, 4),
-                       "tau_at_alpha": round(tau(alpha, 3), 4),
-                       "implied_tok_s": round(1000 / ms4 * tau_meas, 2)}
+                       "implied_tok_s": {f"alpha_{a}": round(pps * tau(a, 3), 2) for a in ALPHAS},
+                       "implied_tok_s_measured": round(pps * tau_meas, 2)}
         log("K=4", sweep["K4"])
         del ws4
     if 8 in Ks:
         x0_8 = torch.from_numpy(synth.activations(0, 8, H)).to(dev)
         logits8 = torch.empty((8, V), dtype=torch.float32, device=dev)
         ws8 = torch.empty(model.workspace_bytes(8), dtype=torch.uint8, device=dev)
-        ms8 = {}
-        for name, path in (("auto", vq.PATH_AUTO), ("valu", vq.PATH_VALU), ("mfma", vq.PATH_MFMA)):
-            ms8[name] = time_graph(torch, lambda: vq.decode_pass(model, x0_8, logits8, path=path, ws=ws8),
-                                   args.steps, args.warmup)[0]
+        ms8 = time_graph(torch, lambda: vq.decode_pass(model, x0_8, logits8, ws=ws8), args.steps, args.warmup)[0]
+        assert model.barrier_error(8, ws8) == 0
         del ws8
         # the sampling path over the C4 windows
         c4 = synth.C4
@@ -377,24 +374,30 @@ def main():
         kw = dict(draft_mode=vq.DRAFT_Q_SAMPLE, T=c4["T"], top_p=c4["top_p"], min_p=c4["min_p"],
                   seed=c4["philox_seed"])
         r = vq.verify_accept(vq.MODE_SAMPLE, td, dd, **kw)
-        acc_ms = time_eager(torch, lambda: vq.verify_accept(vq.MODE_SAMPLE, td, dd, out=r, **kw), 3)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            vq.verify_accept(vq.MODE_SAMPLE, td, dd, out=r, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        acc_ms = e0.elapsed_time(e1) / 3
         n_acc = r["n_accepted"].cpu().numpy()
         beta = [float((n_acc >= i).mean()) for i in range(1, 8)]
         tau8 = float((n_acc + 1).mean())
         del td, dd, r
         torch.cuda.empty_cache()
-        best = min(ms8.values())
-        sweep["K8"] = {"workload": synth.C4["name"], "ms_per_step": round(ms8["auto"], 4),
-                       "gbps": round(wbytes / ms8["auto"] / 1e6, 2),
-                       "passes_per_s": round(1000 / ms8["auto"], 2),
-                       "frac_of_hbm_peak": round(wbytes / ms8["auto"] / 1e6 / HBM_PEAK_GBPS, 4),
-                       "pass_ms_valu": round(ms8["valu"], 4), "pass_ms_mfma": round(ms8["mfma"], 4),
-                       "ratio_to_K1_pass": round(best / ms1, 4),
+        pps = 1000 / ms8
+        sweep["K8"] = {"workload": synth.C4["name"], "ms_per_step": round(ms8, 4),
+                       "gbps": round(wbytes / ms8 / 1e6, 2), "passes_per_s": round(pps, 2),
+                       "frac_of_hbm_peak": round(wbytes / ms8 / 1e6 / HBM_PEAK_GBPS, 4),
+                       "ratio_to_K1_pass": round(ms8 / ms1, 4),
                        "accept_ms_1000_windows": round(acc_ms, 4),
                        "accept_us_per_window": round(acc_ms * 1000 / W, 3),
                        "measured_tau": round(tau8, 4),
                        "reach_position": [round(b, 4) for b in beta],
-                       "implied_tok_s": round(1000 / best * tau8, 2)}
+                       "implied_tok_s": {f"alpha_{a}": round(pps * tau(a, 7), 2) for a in ALPHAS},
+                       "implied_tok_s_measured": round(pps * tau8, 2)}
         log("K=8", sweep["K8"])
     if 16 in Ks:
         del model
@@ -406,28 +409,17 @@ def main():
         ws16 = torch.empty(mx.workspace_bytes(16), dtype=torch.uint8, device=dev)
         ms16 = time_graph(torch, lambda: vq.decode_pass(mx, x0_16, logits16, ws=ws16), args.steps,
                           args.warmup)[0]
-        x0_1m = torch.from_numpy(synth.activations(0, 1, H)).to(dev)
-        logits1m = torch.empty((1, V), dtype=torch.float32, device=dev)
-        ws1m = torch.empty(mx.workspace_bytes(1), dtype=torch.uint8, device=dev)
-        ms1m = time_graph(torch, lambda: vq.decode_pass(mx, x0_1m, logits1m, ws=ws1m), args.steps,
-                          args.warmup)[0]
-        sweep["K16"] = {"workload": synth.C5["name"], "weight_bytes": mbytes, "path": "mfma",
+        assert mx.barrier_error(16, ws16) == 0
+        pps = 1000 / ms16
+        sweep["K16"] = {"workload": synth.C5["name"], "weight_bytes": mbytes, "path": "f16 mfma",
                         "ms_per_step": round(ms16, 4), "gbps": round(mbytes / ms16 / 1e6, 2),
-                        "passes_per_s": round(1000 / ms16, 2),
+                        "passes_per_s": round(pps, 2),
                         "frac_of_hbm_peak": round(mbytes / ms16 / 1e6 / HBM_PEAK_GBPS, 4),
-                        "mxfp4_K1_pass_ms": round(ms1m, 4)}
+                        "implied_tok_s": {f"alpha_{a}": round(pps * tau(a, 15), 2) for a in ALPHAS}}
         log("K=16", sweep["K16"])
-        del mx, ws16, ws1m
+        del mx, ws16
         torch.cuda.empty_cache()
     out["sweep"] = sweep
-
-    if args.calib_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        out["calib_copy_bytes"] = 1 << 30
 
     if not args.no_cpu:
         import oracle as oracle_mod

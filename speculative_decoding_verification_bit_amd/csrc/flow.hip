@@ -42,7 +42,7 @@ namespace {
 
 constexpr int NCW = FLOW_NCW;
 constexpr int NTHR = 64 * (NCW + 1);
-constexpr int DEPTH = 6;                // steps (two chunks each) in flight per compute wave
+constexpr int DEPTH = 4;                // steps (two chunks each) in flight per compute wave
 constexpr unsigned SPIN_LDS = 1u << 23; // bounded waits (about a second)
 constexpr unsigned SPIN_GLOBAL = 1u << 22;
 
