@@ -5,8 +5,12 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
+#include "steps.h"
 #include "vq_internal.h"
 
 namespace vq {
@@ -334,6 +338,69 @@ int linear_layout(const vq_tiled* W, int K, int nwg, LinearLayout* L) {
     return VQ_OK;
 }
 
+// ---------------------------------------------------------------- work-list cache
+
+// The compute waves' work lists depend only on the shapes, K, the grid and the launch
+// split.  They are built on the host at the first call with a shape and kept in device
+// memory, one table per device and shape, until the process ends.
+struct StepKey {
+    int dev, fmt, K, nwg, staged, linear;
+    int H, KV, FF, V, L;       // decode shapes (a linear map: rows in V, cols in H)
+    bool operator<(const StepKey& o) const { return memcmp(this, &o, sizeof *this) < 0; }
+};
+struct StepDev {
+    uint32_t* buf = nullptr;            // the entries, then every launch's start indices
+    std::vector<size_t> launch_start;   // per launch: its start indices, in words from buf
+};
+std::mutex g_steps_mu;
+std::map<StepKey, StepDev>* g_steps = new std::map<StepKey, StepDev>();   // never freed
+
+int get_steps(const StepKey& key, const KindPlan kp[6], const std::vector<std::pair<int, int>>& launches, int L,
+              bool linear, int nwg, int xoff1, hipStream_t st, const StepDev** out) {
+    std::lock_guard<std::mutex> g(g_steps_mu);
+    auto it = g_steps->find(key);
+    if (it != g_steps->end()) {
+        *out = &it->second;
+        return VQ_OK;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+        return fail(VQ_ERR_UNSUPPORTED, "the first call with these shapes builds the work lists (an allocation "
+                                        "and a copy) and cannot be captured: call it once before capturing");
+    StepTable T;
+    std::vector<size_t> hdr;
+    for (const auto& l : launches) {
+        hdr.push_back(T.start.size());
+        if (!build_steps(T, kp, l.first, l.second, L, linear, nwg, xoff1))
+            return fail(VQ_ERR_UNSUPPORTED, "work lists of stages %d..%d do not fit their encoding", l.first,
+                        l.second - 1);
+    }
+    const size_t ne = T.ent.size(), ns = T.start.size();
+    std::vector<uint32_t> h(ne + ns);
+    memcpy(h.data(), T.ent.data(), ne * 4);
+    memcpy(h.data() + ne, T.start.data(), ns * 4);
+    void* d = nullptr;
+    hipError_t e = hipMalloc(&d, h.size() * 4);
+    if (e != hipSuccess) return hip_fail(e, "work list allocation");
+    e = hipMemcpyAsync(d, h.data(), h.size() * 4, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return hip_fail(e, "work list upload");
+    }
+    StepDev sd;
+    sd.buf = (uint32_t*)d;
+    for (size_t o : hdr) sd.launch_start.push_back(ne + o);
+    *out = &g_steps->emplace(key, std::move(sd)).first->second;
+    return VQ_OK;
+}
+
+int current_device() {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    return dev;
+}
+
 }  // namespace
 }  // namespace vq
 
@@ -429,8 +496,6 @@ int vq_verify_linear(const vq_tiled* W, const void* x_f16, int32_t K, void* y, i
         return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", L.total, ws_bytes);
     char* base = (char*)ws;
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_zero_u32((unsigned*)(base + L.off_cnt), L.zero_words, st);
-    if (e != hipSuccess) return hip_fail(e, "counter reset launch");
     FlowArgs A{};
     A.fmt = W->format;
     A.K = K;
@@ -453,6 +518,14 @@ int vq_verify_linear(const vq_tiled* W, const void* x_f16, int32_t K, void* y, i
     A.err = (int*)(base + L.off_cnt) + (L.zero_words - 1);
     A.kp[SK_LIN] = L.kp;
     A.lm = (const uint8_t*)W->data;
+    const StepKey key{current_device(), W->format, K, A.nwg, 0, 1, W->cols, 0, 0, W->rows, 0};
+    const StepDev* sd = nullptr;
+    rc = get_steps(key, A.kp, {{0, 1}}, 0, true, A.nwg, A.xoff1, st, &sd);
+    if (rc) return rc;
+    A.steps = sd->buf;
+    A.step_start = sd->buf + sd->launch_start[0];
+    hipError_t e = launch_zero_u32((unsigned*)(base + L.off_cnt), L.zero_words, st);
+    if (e != hipSuccess) return hip_fail(e, "counter reset launch");
     e = launch_flow(A, st);
     if (e != hipSuccess) return hip_fail(e, "linear launch");
     return VQ_OK;
@@ -555,14 +628,12 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
         return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", d.total, ws_bytes);
     hipStream_t st = (hipStream_t)stream;
     char* base = (char*)ws;
-    hipError_t e = launch_zero_u32((unsigned*)(base + d.off_cnt), d.zero_words, st);
-    if (e != hipSuccess) return hip_fail(e, "sync reset launch");
     FlowArgs A;
     fill_common(A, s, d, pp, K, nwg, M, x0_f16, logits, base);
     const int S = 4 * s.L + 1;
     const bool staged = launch == VQ_LAUNCH_STAGED;
-    int nl = 0, s0 = 0;
-    while (s0 < S) {
+    std::vector<std::pair<int, int>> launches;
+    for (int s0 = 0; s0 < S;) {
         int s1;
         if (staged) {
             s1 = s0 + 1;
@@ -572,9 +643,23 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
             s1 = std::min(S, 4 * (l0 + FLOW_MAX_LAYERS));
             if (s1 == 4 * s.L) s1 = S;
         }
+        launches.emplace_back(s0, s1);
+        s0 = s1;
+    }
+    const StepKey key{current_device(), s.fmt, K, nwg, staged ? 1 : 0, 0, s.H, s.KV, s.FF, s.V, s.L};
+    const StepDev* sd = nullptr;
+    rc = get_steps(key, A.kp, launches, s.L, false, nwg, A.xoff1, st, &sd);
+    if (rc) return rc;
+    A.steps = sd->buf;
+    hipError_t e = launch_zero_u32((unsigned*)(base + d.off_cnt), d.zero_words, st);
+    if (e != hipSuccess) return hip_fail(e, "sync reset launch");
+    int nl = 0;
+    for (const auto& l : launches) {
+        const int s0 = l.first, s1 = l.second;
         fill_layers(A, M, std::min(s0 / 4, s.L - 1));
         A.s_begin = s0;
         A.s_end = s1;
+        A.step_start = sd->buf + sd->launch_start[nl];
         if (events && 2 * nl + 1 < n_events) {
             e = hipEventRecord((hipEvent_t)events[2 * nl], st);
             if (e != hipSuccess) return hip_fail(e, "event record");
@@ -586,7 +671,6 @@ static int decode_impl(const vq_model* M, const void* x0_f16, int32_t K, float* 
             if (e != hipSuccess) return hip_fail(e, "event record");
         }
         ++nl;
-        s0 = s1;
     }
     if (n_launches) *n_launches = nl;
     return VQ_OK;

@@ -7,9 +7,10 @@
 // One kernel, k_flow, one workgroup per compute unit, 12 waves:
 //  * waves 0..10 compute.  A stage's chunks (16 rows x 128 columns of the tiled layout:
 //    1 KB of codes and the rows' block scales / mins) are split into one contiguous range
-//    per workgroup, equal to within a chunk; compute wave c takes every 11th chunk of its
-//    workgroup's range, keeping DEPTH chunks of loads in flight in registers (the loads
-//    run on across stage boundaries: weights never wait for activations).  The 32 codes
+//    per workgroup, equal to within a chunk; compute wave c takes every 11th step (two
+//    chunks) of its workgroup's range, keeping DEPTH steps of loads in flight in registers
+//    (the loads run on across stage boundaries: weights never wait for activations).  A
+//    wave's steps come from a work list built on the host (steps.h).  The 32 codes
 //    of a block widen exactly to fp16 (a Q4 code n to n - 8, an E2M1 code to its value),
 //    one v_mfma_f32_16x16x32_f16 per block multiplies them with the fp16 activations
 //    read from LDS (products exact, fp32 sums); the block scale multiplies the fp32
@@ -36,13 +37,14 @@
 
 #include "vq_device.h"
 #include "vq_internal.h"
+#include "steps.h"
 
 namespace vq {
 namespace {
 
 constexpr int NCW = FLOW_NCW;
 constexpr int NTHR = 64 * (NCW + 1);
-constexpr int DEPTH = 4;                // steps (two chunks each) in flight per compute wave
+constexpr int DEPTH = ST_ROUND;         // steps (two chunks each) in flight per compute wave
 constexpr unsigned SPIN_LDS = 1u << 23; // bounded waits (about a second)
 constexpr unsigned SPIN_GLOBAL = 1u << 22;
 
@@ -251,103 +253,6 @@ __device__ __forceinline__ const uint16_t* input_of(KArgs& A, int s) {
     return (const uint16_t*)(A.ws + (size_t)(s >> 2) * A.layer_bytes + A.off_x[s & 3]);
 }
 
-// ------------------------------------------------------------------ chunk cursors
-
-// Fields of a row of the per-kind sequence table in LDS.
-enum {
-    KT_N, KT_LENA, KT_WLO, KT_AW, KT_AT, KT_AI, KT_BW, KT_BT, KT_BI, KT_BK1,
-    KT_T, KT_G, KT_GW, KT_GLAST, KT_NWIN, KT_CB, KT_XS
-};
-static_assert(KT_XS < FLOW_KTAB, "sequence table row");
-
-__device__ __forceinline__ int ktab(const FlowCtrl& C, int kind, int f) { return uni(C.ktab[kind][f]); }
-
-// A walk over one wave's chunks of the launch: positions cw, cw + 11, ... of the
-// workgroup's sequence in every stage.  It keeps the stage, the position k, the current
-// span [k0, k1) (a run of chunks inside one unit) with the span's unit (window w, tile t)
-// and the group i0 of its first chunk.  A consume walk also counts the units it has left
-// behind (pclose) and whether it has entered a stage (pnew).  The stage's row of the
-// sequence table is copied into the walk when it enters the stage (one burst of LDS
-// reads), so that stepping needs no memory access.  All fields are wave-uniform.
-struct Cur {
-    int s, kind, n, k, k0, k1, w, t, i0;
-    int done, pclose, pnew;
-    int lenA, bw, bt, bi, bk1, T, G, gw, glast, nwin, cb, wlo;
-};
-
-__device__ __forceinline__ Cur load_row(const FlowCtrl& C, Cur c) {
-    const int4* r = (const int4*)C.ktab[c.kind];
-    const int4 a = r[0], b = r[1], d = r[2], e = r[3], f = r[4];
-    // KT_N, KT_LENA, KT_WLO, KT_AW | KT_AT, KT_AI, KT_BW, KT_BT | KT_BI, KT_BK1, KT_T, KT_G |
-    // KT_GW, KT_GLAST, KT_NWIN, KT_CB | KT_XS
-    c.n = uni(a.x); c.lenA = uni(a.y); c.wlo = uni(a.z);
-    c.bw = uni(b.z); c.bt = uni(b.w); c.bi = uni(d.x); c.bk1 = uni(d.y);
-    c.T = uni(d.z); c.G = uni(d.w); c.gw = uni(e.x); c.glast = uni(e.y); c.nwin = uni(e.z); c.cb = uni(e.w);
-    (void)f;
-    // the first span: segment A's, else segment B's
-    c.k0 = 0;
-    if (c.lenA > 0) {
-        c.w = uni(a.w); c.t = uni(b.x); c.i0 = uni(b.y); c.k1 = c.lenA;
-    } else {
-        c.w = c.bw; c.t = c.bt; c.i0 = c.bi; c.k1 = c.bk1;
-    }
-    return c;
-}
-static_assert(KT_N == 0 && KT_AW == 3 && KT_AT == 4 && KT_BW == 6 && KT_BI == 8 && KT_T == 10 &&
-              KT_GW == 12 && KT_CB == 15 && KT_XS == 16, "sequence table row layout");
-
-__device__ __forceinline__ Cur span_next(Cur c) {
-    if (c.lenA > 0 && c.k0 == 0) {
-        c.w = c.bw; c.t = c.bt; c.i0 = c.bi;
-        c.k0 = c.lenA;
-        c.k1 = c.bk1;
-    } else {
-        c.t = uni(c.t + 1);
-        if (c.t == c.T) {
-            c.t = 0;
-            c.w = uni(c.w + 1);
-        }
-        const int gU = c.w == c.nwin - 1 ? c.glast : c.gw;
-        c.k0 = c.k1;
-        c.k1 = uni(min(c.k0 + gU, c.n));
-        c.i0 = 0;
-    }
-    return c;
-}
-
-// Moves a walk to its next chunk at or after its position (new_stage: enter stage c.s).
-// The issue walk skips a stage as soon as its position passes the stage's chunks; the
-// consume walk steps through every span, so that it counts each unit it leaves.
-template <bool CONSUME>
-__device__ __forceinline__ Cur seek(KArgs& A, const FlowCtrl& C, Cur c, int cw, int new_stage) {
-    for (;;) {
-        if (new_stage) {
-            if (c.s >= A.s_end) {
-                c.done = 1;
-                return c;
-            }
-            c.kind = kind_of(A, c.s);
-            c = load_row(C, c);
-            c.k = cw;
-            if (c.n == 0 || (!CONSUME && c.k >= c.n)) {
-                c.s = uni(c.s + 1);
-                continue;
-            }
-            if (CONSUME && c.k < c.n) c.pnew = 1;
-            new_stage = 0;
-        }
-        if (c.k < c.k1) break;
-        if (CONSUME) c.pclose = uni(c.pclose + 1);
-        if (CONSUME ? c.k1 >= c.n : c.k >= c.n) {
-            c.s = uni(c.s + 1);
-            new_stage = 1;
-            continue;
-        }
-        c = span_next(c);
-    }
-    return c;
-}
-
 // ------------------------------------------------------------------------ kernel
 
 template <int FMT, int KC>
@@ -374,33 +279,6 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         C.xready = 0;
         C.abort = 0;
     }
-    // The workgroup's chunk sequence for each stage kind: chunk count, segment A, and the
-    // first span (a run of chunks inside one unit) of each segment, with the plan values
-    // the cursors need.  Computed once by the conductor wave.
-    if (wave == NCW) {
-        for (int kind = 0; kind < 6; ++kind) {
-            const Plan P = plan_of(A, kind);
-            const Seq q = seq_of(P, w);
-            int aw = 0, at = 0, ai = 0, bw = 0, bt = 0, bi = 0, bk1 = 0;
-            if (q.lenA > 0) {
-                const Pos pa = locate(P, q.a0);
-                aw = pa.w; at = pa.t; ai = pa.i;
-            }
-            if (q.n - q.lenA > 0) {
-                const Pos pb = locate(P, q.lo);
-                bw = pb.w; bt = pb.t; bi = pb.i;
-                bk1 = q.lenA + min(pb.gl - pb.i, q.n - q.lenA);
-            }
-            if (lane == 0) {
-                int* r = C.ktab[kind];
-                r[KT_N] = q.n; r[KT_LENA] = q.lenA; r[KT_WLO] = q.wlo;
-                r[KT_AW] = aw; r[KT_AT] = at; r[KT_AI] = ai;
-                r[KT_BW] = bw; r[KT_BT] = bt; r[KT_BI] = bi; r[KT_BK1] = bk1;
-                r[KT_T] = P.T; r[KT_G] = P.G; r[KT_GW] = P.gw; r[KT_GLAST] = P.glast;
-                r[KT_NWIN] = P.nwin; r[KT_CB] = P.cb; r[KT_XS] = P.xs;
-            }
-        }
-    }
     __syncthreads();
 
     if (wave < NCW) {
@@ -412,67 +290,21 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         const int xoff1 = A.xoff1;
         uint8_t* const ring = lds + A.ring_off;
 
-        // Two walks over this wave's chunks: the issue walk DEPTH chunks ahead of the
-        // consume walk.  Once per round of DEPTH chunks both are advanced in one loop that
-        // leaves a descriptor per step in the lanes of four VGPRs; the unrolled steps only
-        // read them:
-        //   di0/di1: address of the chunk to issue;  dc0: LDS activation offset of the chunk
-        //   to consume;  dc1: 0 (nothing to consume), or units to close first (bits 0..7),
-        //   opens a stage (bit 8), valid (bit 9), stage kind (bits 10..12), launch stage + 1
-        //   (bits 16..)
-        Cur ic = {};
-        ic.s = A.s_begin;
-        ic = seek<false>(A, C, ic, cw, 1);
-        const uint8_t* iW = A.lm;
-        uint32_t ioff = 0, istep = 0;
-        auto i_set = [&]() __attribute__((always_inline)) {
-            iW = mat_of(A, ic.s, ic.kind);
-            istep = (uint32_t)uni(NCW * ic.cb);
-            const int g = ic.w * ic.gw + ic.i0 + (ic.k - ic.k0);
-            ioff = (uint32_t)uni((ic.t * ic.G + g) * ic.cb);
+        // The wave's work list (built on the host for this launch and grid): per step the
+        // byte offset of its two chunks in the stage's matrix and a flags word (LDS offset of
+        // the activations, units to close first, stage entry, valid, launch stage).  It is
+        // read a round of DEPTH entries at a time with scalar loads, two rounds ahead: the
+        // issue side runs one round ahead of the consume side.
+        typedef const __attribute__((address_space(4))) uint32_t CU32;
+        const uint32_t first = ((CU32*)A.step_start)[w * NCW + cw];
+        CU32* const tab = (CU32*)A.steps + 2 * (size_t)first;
+        uint32_t e0[2 * DEPTH], e1[2 * DEPTH], e2[2 * DEPTH];
+        auto load_round = [&](uint32_t* e, int r) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 2 * DEPTH; ++i) e[i] = tab[2 * DEPTH * r + i];
         };
-        if (!ic.done) i_set();
-        Cur cc = {};
-        cc.s = A.s_begin;
-        cc = seek<true>(A, C, cc, cw, 1);
-        uint32_t coff = 0;
-        auto c_set = [&]() __attribute__((always_inline)) {
-            coff = (uint32_t)uni((cc.w - cc.wlo) * xoff1 + (cc.i0 + (cc.k - cc.k0)) * 512);
-        };
-        if (!cc.done) c_set();
-
-        int di0 = 0, di1 = 0, dc0 = 0, dc1 = 0;
-        auto gen_issue = [&](int j) __attribute__((always_inline)) {
-            const uint64_t a = (uint64_t)(uintptr_t)(iW + ioff);
-            di0 = writelane((int)(uint32_t)a, j, di0);
-            di1 = writelane((int)(uint32_t)(a >> 32), j, di1);
-            if (!ic.done) {
-                const uint32_t last = ioff;
-                ic.k = uni(ic.k + NCW);
-                ioff = (uint32_t)uni((int)(ioff + istep));
-                if (ic.k >= ic.k1) {
-                    ic = seek<false>(A, C, ic, cw, 0);
-                    if (!ic.done) i_set();
-                    else ioff = last;                // the tail re-reads the last chunk
-                }
-            }
-        };
-        auto gen_consume = [&](int j) __attribute__((always_inline)) {
-            int f = 0;
-            if (!cc.done) {
-                dc0 = writelane((int)coff, j, dc0);
-                f = cc.pclose | (cc.pnew ? 0x100 : 0) | 0x200 | (cc.kind << 10) | ((cc.s - A.s_begin + 1) << 16);
-                cc.pclose = 0;
-                cc.pnew = 0;
-                cc.k = uni(cc.k + NCW);
-                coff = (uint32_t)uni((int)(coff + NCW * 512));
-                if (cc.k >= cc.k1) {
-                    cc = seek<true>(A, C, cc, cw, 0);
-                    if (!cc.done) c_set();
-                }
-            }
-            dc1 = writelane(f, j, dc1);
-        };
+        int ib_idx = -1;                   // launch stage whose matrix ibase is
+        const uint8_t* ibase = A.lm;
 
         f4_t acc = {0.f, 0.f, 0.f, 0.f};
         uint32_t xlane = 0;                // this lane's A-operand byte offset in a window
@@ -492,10 +324,15 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         constexpr int CB1 = FMT == VQ_FMT_Q4_MIN ? 1280 : FMT == VQ_FMT_Q4 ? 1152 : 1088;
         u4_t rq[DEPTH][2];
         scale_t rs[DEPTH][2];
-        auto issue = [&](int u) __attribute__((always_inline)) {
-            const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(di0, u);
-            const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(di1, u);
-            const uint8_t* p = (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+        auto issue = [&](int u, uint32_t off, uint32_t f) __attribute__((always_inline)) {
+            if (!(f & ST_VALID)) return;
+            const int idx = (int)((f >> ST_STAGE_SHIFT) & 127u);
+            if (idx != ib_idx) {
+                ib_idx = idx;
+                const int s = A.s_begin + idx;
+                ibase = mat_of(A, s, kind_of(A, s));
+            }
+            const uint8_t* p = ibase + off;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 rq[u][h] = ld_global_nt<u4_t>(p + h * CB1 + 16 * lane);
@@ -537,19 +374,20 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
                            (_Float16)1, (_Float16)1, (_Float16)1, (_Float16)1};
         constexpr int NF = KC < 4 ? KC : 4;     // accumulator elements that can hold a column < K
 
-        auto consume = [&](int u) __attribute__((always_inline)) {
-            const int f = __builtin_amdgcn_readlane(dc1, u);
-            if (!(f & 0x200)) return;
-            if (__builtin_expect((f & 0xff) != 0, 0)) {
-                for (int i = 0; i < (f & 0xff); ++i) close_unit();
+        auto consume = [&](int u, uint32_t f) __attribute__((always_inline)) {
+            const uint32_t nclose = (f >> ST_CLOSE_SHIFT) & ST_CLOSE_MAX;
+            if (__builtin_expect(nclose != 0, 0)) {
+                for (uint32_t i = 0; i < nclose; ++i) close_unit();
             }
-            if (__builtin_expect((f & 0x100) != 0, 0)) {
+            if (!(f & ST_VALID)) return;
+            if (__builtin_expect((f & ST_OPEN) != 0, 0)) {
                 // the stage's activations are in LDS once the conductor says so
-                wait_ge(&C.xready, (unsigned)(f >> 16), err, &C.abort);
+                const int idx = (int)((f >> ST_STAGE_SHIFT) & 127u);
+                wait_ge(&C.xready, (unsigned)idx + 1u, err, &C.abort);
                 const int mrow = n16 < K ? n16 : 0;
-                xlane = (uint32_t)(mrow * ktab(C, (f >> 10) & 7, KT_XS) + 16 * q4);
+                xlane = (uint32_t)(mrow * uni(A.kp[kind_of(A, A.s_begin + idx)].xs) + 16 * q4);
             }
-            const uint32_t xa = xlane + (uint32_t)__builtin_amdgcn_readlane(dc0, u);
+            const uint32_t xa = xlane + ((f & ST_XOFF_MASK) << 4);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 h8_t a[4];
@@ -577,23 +415,24 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             }
         };
 
-        for (int j = 0; j < DEPTH; ++j) gen_issue(j);
+        load_round(e0, 0);
+        load_round(e1, 1);
 #pragma unroll
-        for (int u = 0; u < DEPTH; ++u) issue(u);
-        for (;;) {
-            const int last = cc.done;
-            for (int j = 0; j < DEPTH; ++j) {
-                gen_issue(j);
-                gen_consume(j);
-            }
+        for (int u = 0; u < DEPTH; ++u) issue(u, e0[2 * u], e0[2 * u + 1]);
+        for (int r = 0;; ++r) {
+            load_round(e2, r + 2);
 #pragma unroll
             for (int u = 0; u < DEPTH; ++u) {
-                consume(u);
-                issue(u);
+                consume(u, e0[2 * u + 1]);
+                issue(u, e1[2 * u], e1[2 * u + 1]);
             }
-            if (last || cc.done) break;
+            if (e0[2 * DEPTH - 1] & ST_END) break;
+#pragma unroll
+            for (int i = 0; i < 2 * DEPTH; ++i) {
+                e0[i] = e1[i];
+                e1[i] = e2[i];
+            }
         }
-        for (int i = 0; i < cc.pclose; ++i) close_unit();
         return;
     }
 

@@ -59,7 +59,6 @@ constexpr int FLOW_NCW = 11;             // compute waves per workgroup (plus on
 constexpr int FLOW_LDS = 163840;         // LDS per workgroup (gfx950: 160 KB)
 constexpr int FLOW_NSP_MAX = 8;          // slots of the partial-sum ring
 constexpr int FLOW_PEND_MAX = 64;        // split tiles one workgroup finishes per stage
-constexpr int FLOW_KTAB = 20;            // ints per stage kind in the sequence table
 // Completion counters of a stage: one per XCD group of workgroups (blockIdx mod 8), each
 // on its own 128-byte line.
 constexpr int DONE_REPL = 8;
@@ -75,8 +74,6 @@ struct FlowCtrl {
     unsigned pad_[2];
     float rho[VQ_MAX_K];
     int pend_t[FLOW_PEND_MAX];
-    int ktab[6][FLOW_KTAB];          // per stage kind: the workgroup's chunk sequence (see k_flow)
-    uint8_t junk[1024];              // destination of cache-warming loads (never read)
 };
 constexpr int FLOW_CTRL_OFF = (FLOW_LDS - (int)sizeof(FlowCtrl)) & ~255;
 
@@ -123,6 +120,8 @@ struct FlowArgs {
     unsigned* done;           // [stages][DONE_WORDS] completion counters (NULL: linear)
     int* err;                 // raised when a bounded wait times out
     KindPlan kp[6];           // by StageKind
+    const uint32_t* steps;    // the compute waves' work lists (pairs, see steps.h)
+    const uint32_t* step_start;  // per workgroup and compute wave: its first pair in steps
     const uint8_t* lm;        // lm_head, or the linear map
     const uint8_t* w[FLOW_MAX_LAYERS][4];   // q|k|v, o, gate|up, down of layers l0 ..
 };
