@@ -121,6 +121,20 @@ bool make_plan(KindPlan& P, int fmt, int K, int rows, int cols, int tiles, int n
     P.nwe = (int)std::max(1L, std::min((long)nwg, N / P.gw));
     P.q = (int)(N / P.nwe);
     P.r = (int)(N % P.nwe);
+    // Whole tiles per workgroup when that costs little: no tile is then split over two
+    // workgroups, which saves the exchange of partial sums at the end of the stage.  Taken
+    // when k = ceil(T / nwg) tiles per workgroup divide T, and the largest range is within
+    // 25% of the balanced one or the stage is small (its chunks are already in flight when
+    // it starts, so its time is the reduction's, not the stream's).
+    if (P.nwin == 1) {
+        const long k = (P.T + nwg - 1) / nwg;
+        const bool small = (long)P.T * P.G * P.cb <= (32L << 20);
+        if (P.T % k == 0 && (4 * k * nwg <= 5L * P.T || small)) {
+            P.nwe = (int)(P.T / k);
+            P.q = (int)(k * P.G);
+            P.r = 0;
+        }
+    }
     // a range spans at most two windows (two activation buffers)
     if (P.nwin > 1) {
         for (int w = 0; w < P.nwe; ++w) {

@@ -293,15 +293,25 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         // The wave's work list (built on the host for this launch and grid): per step the
         // byte offset of its two chunks in the stage's matrix and a flags word (LDS offset of
         // the activations, units to close first, stage entry, valid, launch stage).  It is
-        // read a round of DEPTH entries at a time with scalar loads, two rounds ahead: the
-        // issue side runs one round ahead of the consume side.
+        // read a round of DEPTH entries at a time, two rounds ahead, with vector loads (a
+        // scalar load in flight would make every LDS wait also wait for it); the issue side
+        // runs one round ahead of the consume side.
         typedef const __attribute__((address_space(4))) uint32_t CU32;
         const uint32_t first = ((CU32*)A.step_start)[w * NCW + cw];
-        CU32* const tab = (CU32*)A.steps + 2 * (size_t)first;
-        uint32_t e0[2 * DEPTH], e1[2 * DEPTH], e2[2 * DEPTH];
-        auto load_round = [&](uint32_t* e, int r) __attribute__((always_inline)) {
+        const u4_t* const tab = (const u4_t*)(A.steps + 2 * (size_t)first);
+        constexpr int RV = DEPTH / 2;           // u4 words per round
+        static_assert(DEPTH % 2 == 0, "a round is whole 16-byte words");
+        u4_t e0[RV], e1[RV], e2[RV];
+        auto load_round = [&](u4_t* e, int r) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 2 * DEPTH; ++i) e[i] = tab[2 * DEPTH * r + i];
+            for (int i = 0; i < RV; ++i) e[i] = tab[RV * r + i];
+        };
+        // entry u of a round: (offset, flags)
+        auto ent_off = [&](const u4_t* e, int u) __attribute__((always_inline)) -> uint32_t {
+            return (uint32_t)uni((int)e[u >> 1][2 * (u & 1)]);
+        };
+        auto ent_flags = [&](const u4_t* e, int u) __attribute__((always_inline)) -> uint32_t {
+            return (uint32_t)uni((int)e[u >> 1][2 * (u & 1) + 1]);
         };
         int ib_idx = -1;                   // launch stage whose matrix ibase is
         const uint8_t* ibase = A.lm;
@@ -324,8 +334,9 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         constexpr int CB1 = FMT == VQ_FMT_Q4_MIN ? 1280 : FMT == VQ_FMT_Q4 ? 1152 : 1088;
         u4_t rq[DEPTH][2];
         scale_t rs[DEPTH][2];
+        // every entry names a chunk in its matrix, with or without ST_VALID: the loads are
+        // unconditional, so that the wait counts of the unrolled rounds are exact
         auto issue = [&](int u, uint32_t off, uint32_t f) __attribute__((always_inline)) {
-            if (!(f & ST_VALID)) return;
             const int idx = (int)((f >> ST_STAGE_SHIFT) & 127u);
             if (idx != ib_idx) {
                 ib_idx = idx;
@@ -418,17 +429,17 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         load_round(e0, 0);
         load_round(e1, 1);
 #pragma unroll
-        for (int u = 0; u < DEPTH; ++u) issue(u, e0[2 * u], e0[2 * u + 1]);
+        for (int u = 0; u < DEPTH; ++u) issue(u, ent_off(e0, u), ent_flags(e0, u));
         for (int r = 0;; ++r) {
             load_round(e2, r + 2);
 #pragma unroll
             for (int u = 0; u < DEPTH; ++u) {
-                consume(u, e0[2 * u + 1]);
-                issue(u, e1[2 * u], e1[2 * u + 1]);
+                consume(u, ent_flags(e0, u));
+                issue(u, ent_off(e1, u), ent_flags(e1, u));
             }
-            if (e0[2 * DEPTH - 1] & ST_END) break;
+            if (ent_flags(e0, DEPTH - 1) & ST_END) break;
 #pragma unroll
-            for (int i = 0; i < 2 * DEPTH; ++i) {
+            for (int i = 0; i < RV; ++i) {
                 e0[i] = e1[i];
                 e1[i] = e2[i];
             }
@@ -437,6 +448,9 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
     }
 
     // ================================================================ conductor
+    // The conductor's work (reductions, epilogues, the stage hand-over) is on the critical
+    // path of every stage: it takes issue slots ahead of the compute waves on its SIMD.
+    __builtin_amdgcn_s_setprio(3);
     const f4_t zero4 = {0.f, 0.f, 0.f, 0.f};
     unsigned useq = 0;
     float stat[4];

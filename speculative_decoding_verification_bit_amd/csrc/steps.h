@@ -19,7 +19,8 @@ constexpr int ST_CLOSE_SHIFT = 14;           // bits 14..21: units to close befo
 constexpr uint32_t ST_CLOSE_MAX = 255u;
 constexpr uint32_t ST_OPEN = 1u << 22;       // first step of the wave in its stage
 constexpr uint32_t ST_VALID = 1u << 23;      // a step with chunks (else: closes only)
-constexpr int ST_STAGE_SHIFT = 24;           // bits 24..30: stage - s_begin of the launch
+constexpr int ST_STAGE_SHIFT = 24;           // bits 24..30: stage - s_begin of the launch (of the
+                                             // chunk's matrix, also without ST_VALID)
 constexpr uint32_t ST_END = 1u << 31;        // the wave's last entry (closes only) and padding
 constexpr int ST_ROUND = 4;                  // entries a wave reads per round
 
@@ -113,11 +114,22 @@ inline bool build_steps(StepTable& T, const KindPlan kp[6], int s_begin, int s_e
             T.start.push_back((uint32_t)(T.ent.size() / 2));
             const size_t first = T.ent.size();
             uint32_t pending = 0;        // units left behind, not yet closed
+            // An entry without chunks still names a chunk (the last valid one, else the first
+            // of the launch's first matrix): the waves load every entry's chunks, so that the
+            // number of loads in flight is the same in every round.
+            uint32_t last_off = 0, last_stage = 0;
             auto emit = [&](uint32_t off, uint32_t flags) {
                 while (pending > ST_CLOSE_MAX) {
-                    T.ent.push_back(0);
-                    T.ent.push_back(ST_CLOSE_MAX << ST_CLOSE_SHIFT);
+                    T.ent.push_back(last_off);
+                    T.ent.push_back((ST_CLOSE_MAX << ST_CLOSE_SHIFT) | (last_stage << ST_STAGE_SHIFT));
                     pending -= ST_CLOSE_MAX;
+                }
+                if (flags & ST_VALID) {
+                    last_off = off;
+                    last_stage = (flags >> ST_STAGE_SHIFT) & 127u;
+                } else {
+                    off = last_off;
+                    flags |= last_stage << ST_STAGE_SHIFT;
                 }
                 T.ent.push_back(off);
                 T.ent.push_back(flags | (pending << ST_CLOSE_SHIFT));
