@@ -464,24 +464,27 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
 
         // -------- the previous stage complete on every workgroup
         if (n_in > 0 && idx > 0) {
-            const unsigned* dn = A.done + (size_t)(s - 1) * DONE_WORDS;
+            // one poll in flight (more would contend for the counters' lines); the error word
+            // and the abort flag are looked at every 16 polls
+            const unsigned* dn = A.done + (size_t)(s - 1) * DONE_WORDS + lane * DONE_STRIDE;
             unsigned spins = 0;
             for (;;) {
-                unsigned v = 0;
-                if (lane < DONE_REPL) v = ld_dev_u32(dn + lane * DONE_STRIDE);
+                const unsigned v = lane < DONE_REPL ? ld_dev_u32(dn) : 0u;
                 unsigned sum = 0;
 #pragma unroll
                 for (int r = 0; r < DONE_REPL; ++r) sum += __builtin_amdgcn_readlane(v, r);
                 if (sum >= (unsigned)A.nwg) break;
-                if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
-                    __hip_atomic_load(&C.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
-                    break;
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins > SPIN_GLOBAL) {
-                    __hip_atomic_store(&C.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
+                if ((++spins & 15u) == 0u) {
+                    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
+                        __hip_atomic_load(&C.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
+                        break;
+                    if (spins > SPIN_GLOBAL) {
+                        __hip_atomic_store(&C.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
                 }
+                __builtin_amdgcn_s_sleep(2);
             }
         }
 
@@ -615,6 +618,15 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) stat[i] = 0.f;
         int npend = 0;
+        // one window: a split tile's second part is this workgroup's (kept in registers, it
+        // is the first unit of its range); the first part comes from the previous workgroup.
+        // Half-way through the units its counter is read once (the load stays in flight while
+        // the other units are reduced), so that a part already there needs no polling.
+        f4_t own = zero4;
+        int own_t = -1;
+        bool early = false;
+        unsigned cload = 0;
+        unsigned* const pcn = A.cnt + (w > 0 ? w - 1 : 0);
         int uw = 0, ut = 0;                      // window and tile of the unit at position pos
         for (int pos = 0; pos < q.nU; ++pos) {
             int U;
@@ -624,6 +636,10 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             ut = U - uw * P.T;
             const unsigned sq_ = useq + (unsigned)pos;
             const unsigned slot = sq_ & (unsigned)(nsp - 1), round = sq_ / (unsigned)nsp;
+            if (own_t >= 0 && !early && 2 * pos >= q.nU) {
+                cload = ld_dev_u32(pcn);
+                early = true;
+            }
             wait_ge(&C.pcnt[slot], (unsigned)NCW * (round + 1u), err, &C.abort);
             f4_t sum = zero4;
             if (lane < plane) {
@@ -642,6 +658,9 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             const bool has_first = f >= q.lo, has_last = l < q.hi;
             if (P.nwin == 1 && has_first && has_last) {
                 epilogue(ut, sum);
+            } else if (P.nwin == 1 && !has_first) {
+                own = sum;
+                own_t = ut;
             } else {
                 const int side = has_first ? 0 : 1;
                 float* ps = part_slot(U, ut, side);
@@ -652,76 +671,70 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
                 __builtin_amdgcn_s_waitcnt(0);
                 if (lane == 0)
                     __hip_atomic_fetch_add(counter(ut, side), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                // the finisher: for one window, the workgroup holding the tile's last chunk;
-                // for several, the one holding the last chunk of the tile's unit in window
-                // t mod nwin
-                bool mine;
-                if (P.nwin == 1) {
-                    mine = side == 1;
-                } else {
+                // several windows: the finisher of a tile is the workgroup holding the last
+                // chunk of the tile's unit in window t mod nwin
+                if (P.nwin > 1) {
                     const int wf = ut % P.nwin;
                     const int glf = wf == P.nwin - 1 ? P.glast : P.gw;
                     const int lf = wf * P.T * P.gw + (ut + 1) * glf - 1;
-                    mine = lf >= q.lo && lf < q.hi && wf == uw;
-                }
-                if (mine && npend < FLOW_PEND_MAX) {
-                    if (lane == 0) C.pend_t[npend] = ut;
-                    ++npend;
+                    if (lf >= q.lo && lf < q.hi && wf == uw && npend < FLOW_PEND_MAX) {
+                        if (lane == 0) C.pend_t[npend] = ut;
+                        ++npend;
+                    }
                 }
             }
         }
         useq += (unsigned)q.nU;
 
-        // -------- finish the split tiles this workgroup owns, in list order
-        for (int j = 0; j < npend; ++j) {
-            const int t = uni(C.pend_t[j]);
-            unsigned expect;
-            unsigned* cn;
-            if (P.nwin == 1) {
-                expect = 2u;
-                cn = A.cnt + (w - 1);
-            } else {
-                expect = 0u;
-                for (int win = 0; win < P.nwin; ++win) {
-                    const int gl = win == P.nwin - 1 ? P.glast : P.gw;
-                    const int f = win * P.T * P.gw + t * gl;
-                    expect += wg_of(P, f) != wg_of(P, f + gl - 1) ? 2u : 1u;
-                }
-                cn = A.cnt + t;
-            }
+        // -------- finish the split tiles this workgroup owns
+        auto poll = [&](const unsigned* cn, unsigned expect) __attribute__((always_inline)) {
             unsigned spins = 0;
             while (ld_dev_u32(cn) < expect) {
-                if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
-                    __hip_atomic_load(&C.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
+                if ((++spins & 15u) == 0u &&
+                    (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
+                     __hip_atomic_load(&C.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)))
                     break;
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins > SPIN_GLOBAL) {
+                __builtin_amdgcn_s_sleep(1);
+                if (spins > SPIN_GLOBAL) {
                     __hip_atomic_store(&C.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                     __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
             }
+        };
+        if (own_t >= 0) {
+            // the previous workgroup's part (slot side 0 of its boundary), then this one's
+            if (!early || (unsigned)uni((int)cload) < 1u) poll(pcn, 1u);
             f4_t sum = zero4;
             if (lane < plane) {
-                if (P.nwin == 1) {
-                    // written once in the launch, after this workgroup last read the lines
-                    // (a fresh launch starts with clean caches): plain loads see them
-                    const float* p0 = A.parts + (size_t)((idx * A.nwg + w - 1) * 2) * (pbytes >> 2);
-                    const float* p1 = p0 + (pbytes >> 2);
-                    const f4_t v0 = *(const f4_t*)(p0 + 4 * lane);
-                    const f4_t v1 = *(const f4_t*)(p1 + 4 * lane);
-                    sum = v0 + v1;
-                } else {
-                    for (int win = 0; win < P.nwin; ++win) {
-                        const int gl = win == P.nwin - 1 ? P.glast : P.gw;
-                        const int f = win * P.T * P.gw + t * gl;
-                        const int U = win * P.T + t;
-                        const int np = wg_of(P, f) != wg_of(P, f + gl - 1) ? 2 : 1;
-                        for (int side = 0; side < np; ++side) {
-                            const float* ps = A.parts + (size_t)(2 * U + side) * (pbytes >> 2);
+                const float* p0 = A.parts + (size_t)((idx * A.nwg + w - 1) * 2) * (pbytes >> 2);
+                sum = *(const f4_t*)(p0 + 4 * lane) + own;
+            }
+            epilogue(own_t, sum);
+            if (lane == 0) __hip_atomic_store(pcn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // several windows: the tiles listed above, in list order
+        for (int j = 0; j < npend; ++j) {
+            const int t = uni(C.pend_t[j]);
+            unsigned expect = 0u;
+            for (int win = 0; win < P.nwin; ++win) {
+                const int gl = win == P.nwin - 1 ? P.glast : P.gw;
+                const int f = win * P.T * P.gw + t * gl;
+                expect += wg_of(P, f) != wg_of(P, f + gl - 1) ? 2u : 1u;
+            }
+            unsigned* cn = A.cnt + t;
+            poll(cn, expect);
+            f4_t sum = zero4;
+            if (lane < plane) {
+                for (int win = 0; win < P.nwin; ++win) {
+                    const int gl = win == P.nwin - 1 ? P.glast : P.gw;
+                    const int f = win * P.T * P.gw + t * gl;
+                    const int U = win * P.T + t;
+                    const int np = wg_of(P, f) != wg_of(P, f + gl - 1) ? 2 : 1;
+                    for (int side = 0; side < np; ++side) {
+                        const float* ps = A.parts + (size_t)(2 * U + side) * (pbytes >> 2);
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) sum[i] += ld_dev_f32(ps + 4 * lane + i);
-                        }
+                        for (int i = 0; i < 4; ++i) sum[i] += ld_dev_f32(ps + 4 * lane + i);
                     }
                 }
             }
