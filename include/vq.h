@@ -142,6 +142,26 @@ int vq_tile(const vq_matrix* src, const vq_tiled* dst, int32_t row0, void* strea
 int vq_verify_linear(const vq_tiled* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype,
                      void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * vq_verify_linear_noalloc -- vq_verify_linear for callers that cannot allocate memory
+ * (code under stream capture, tight serving loops, hosts that forbid allocation): no
+ * workspace argument, and the call allocates nothing, on the device or the host.
+ *
+ * The partial sums, counters and work lists live in a fixed array of the library's own
+ * device data (4.5 MiB + 16 KiB; each device the library runs on holds one copy until
+ * the process ends).  Limits: the shape must need no column windows (K * cols small
+ * enough for the activations to stay in LDS, e.g. cols <= 8704 at K = 8), at most 512 KiB
+ * of split-tile partial sums and 4 MiB of work lists (a 151936 x 5120 matrix fits); other
+ * shapes return VQ_ERR_UNSUPPORTED.  The first call with a shape on a device copies that
+ * shape's work lists into the array (and waits for the stream), so it cannot be captured;
+ * later calls with the same shape enqueue two kernels only.  Every call on a device uses
+ * the same array: calls that overlap on one device (several streams or threads) race.
+ * Results are bit-identical to vq_verify_linear's.
+ * Errors: as vq_verify_linear, without VQ_ERR_WORKSPACE; VQ_ERR_UNSUPPORTED for the limits.
+ */
+int vq_verify_linear_noalloc(const vq_tiled* W, const void* x_f16, int32_t K, void* y,
+                             int32_t y_dtype, void* stream);
+
 /* ---------------------------------------------------------------- acceptance */
 #define VQ_MODE_GREEDY 0      /* accept x_i while it equals the target argmax            */
 #define VQ_MODE_SAMPLE 1      /* accept x_i with prob. min(1, p(x_i)/q(x_i)), else resample */

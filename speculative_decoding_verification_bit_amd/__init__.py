@@ -66,7 +66,7 @@ class VqAcceptDesc(ctypes.Structure):
                 ("n_accepted", _P), ("tokens", _P), ("status", _P)]
 
 
-EXPORTS = ("vq_tiled_bytes", "vq_tile", "vq_verify_linear", "vq_verify_accept", "vq_decode_pass", "vq_decode_pass_timed",
+EXPORTS = ("vq_tiled_bytes", "vq_tile", "vq_verify_linear", "vq_verify_linear_noalloc", "vq_verify_accept", "vq_decode_pass", "vq_decode_pass_timed",
            "vq_decode_stage_ptr", "vq_decode_error_word",
            "vq_workspace_bytes", "vq_status_string", "vq_last_error", "vq_abi_version")
 
@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.vq_tile.argtypes = [ctypes.POINTER(VqMatrix), ctypes.POINTER(VqTiled), I32, _P]
     L.vq_verify_linear.restype = I32
     L.vq_verify_linear.argtypes = [ctypes.POINTER(VqTiled), _P, I32, _P, I32, _P, SZ, _P]
+    L.vq_verify_linear_noalloc.restype = I32
+    L.vq_verify_linear_noalloc.argtypes = [ctypes.POINTER(VqTiled), _P, I32, _P, I32, _P]
     L.vq_verify_accept.restype = I32
     L.vq_verify_accept.argtypes = [ctypes.POINTER(VqAcceptDesc), _P, SZ, _P]
     L.vq_decode_pass.restype = I32
@@ -216,6 +218,20 @@ def verify_linear(W, x, y=None, y_dtype: int = DTYPE_F32, ws=None, stream=None):
         ws = _empty(workspace_bytes(OP_LINEAR, W.desc, K), x.device)
     _check(lib.vq_verify_linear(ctypes.byref(W.desc), _ptr(x), K, _ptr(y), y_dtype, _ptr(ws), ws.numel(),
                                 _stream(stream)), "vq_verify_linear")
+    return y
+
+
+def verify_linear_noalloc(W, x, y=None, y_dtype: int = DTYPE_F32, stream=None):
+    """verify_linear through the entry point that allocates nothing (library scratch)."""
+    import torch
+    if isinstance(W, DeviceMatrix):
+        W = W.tiled
+    K = x.shape[0]
+    if y is None:
+        y = torch.empty((K, W.rows), dtype=torch.float32 if y_dtype == DTYPE_F32 else torch.float16,
+                        device=x.device)
+    _check(lib.vq_verify_linear_noalloc(ctypes.byref(W.desc), _ptr(x), K, _ptr(y), y_dtype, _stream(stream)),
+           "vq_verify_linear_noalloc")
     return y
 
 

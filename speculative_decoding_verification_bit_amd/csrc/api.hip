@@ -490,26 +490,34 @@ int vq_tile(const vq_matrix* src, const vq_tiled* dst, int32_t row0, void* strea
     return VQ_OK;
 }
 
-int vq_verify_linear(const vq_tiled* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype, void* ws,
-                     size_t ws_bytes, void* stream) {
-    g_err[0] = 0;
+}  // extern "C"
+
+namespace vq {
+namespace {
+
+// Argument checks shared by the linear entry points; fills the plan.
+int linear_check(const vq_tiled* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype, LinearLayout* L,
+                 bool* empty) {
+    *empty = false;
     int rc = check_tiled(W, "W");
     if (rc) return rc;
     if (W->order != VQ_ROWS_PLAIN) return fail(VQ_ERR_ARG, "W must be in VQ_ROWS_PLAIN order");
     if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
     if (y_dtype != VQ_DTYPE_F32 && y_dtype != VQ_DTYPE_F16) return fail(VQ_ERR_ARG, "unknown y_dtype %d", y_dtype);
-    if (W->rows == 0) return VQ_OK;
+    if (W->rows == 0) {
+        *empty = true;
+        return VQ_OK;
+    }
     if (!x_f16 || !y) return fail(VQ_ERR_ARG, "NULL x or y");
     if (!aligned(x_f16, 16)) return fail(VQ_ERR_ARG, "x must be 16-byte aligned");
     if (!aligned(y, y_dtype == VQ_DTYPE_F32 ? 4 : 2)) return fail(VQ_ERR_ARG, "y is misaligned");
-    const int nwg = flow_grid();
-    LinearLayout L;
-    rc = linear_layout(W, K, nwg, &L);
-    if (rc) return rc;
-    if (!ws || ws_bytes < L.total || !aligned(ws, 256))
-        return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", L.total, ws_bytes);
-    char* base = (char*)ws;
-    hipStream_t st = (hipStream_t)stream;
+    return linear_layout(W, K, flow_grid(), L);
+}
+
+// The launch of a linear map with its scratch memory: split-tile parts, counters (zeroed
+// here, with a kernel), error word, and the work lists.
+int linear_launch(const vq_tiled* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype, const LinearLayout& L,
+                  float* parts, unsigned* cnt, const uint32_t* steps, const uint32_t* step_start, hipStream_t st) {
     FlowArgs A{};
     A.fmt = W->format;
     A.K = K;
@@ -527,22 +535,125 @@ int vq_verify_linear(const vq_tiled* W, const void* x_f16, int32_t K, void* y, i
     A.xoff1 = (L.xcap / 2) & ~15;
     A.x0 = (const uint16_t*)x_f16;
     A.out = y;
-    A.parts = (float*)base;
-    A.cnt = (unsigned*)(base + L.off_cnt);
-    A.err = (int*)(base + L.off_cnt) + (L.zero_words - 1);
+    A.parts = parts;
+    A.cnt = cnt;
+    A.err = (int*)cnt + (L.zero_words - 1);
     A.kp[SK_LIN] = L.kp;
     A.lm = (const uint8_t*)W->data;
-    const StepKey key{current_device(), W->format, K, A.nwg, 0, 1, W->cols, 0, 0, W->rows, 0};
-    const StepDev* sd = nullptr;
-    rc = get_steps(key, A.kp, {{0, 1}}, 0, true, A.nwg, A.xoff1, st, &sd);
-    if (rc) return rc;
-    A.steps = sd->buf;
-    A.step_start = sd->buf + sd->launch_start[0];
-    hipError_t e = launch_zero_u32((unsigned*)(base + L.off_cnt), L.zero_words, st);
+    A.steps = steps;
+    A.step_start = step_start;
+    hipError_t e = launch_zero_u32(cnt, L.zero_words, st);
     if (e != hipSuccess) return hip_fail(e, "counter reset launch");
     e = launch_flow(A, st);
     if (e != hipSuccess) return hip_fail(e, "linear launch");
     return VQ_OK;
+}
+
+// ------------------------------------------------ the entry point that allocates nothing
+
+// Scratch memory of vq_verify_linear_noalloc in the library's own device data: the work
+// lists, the split-tile parts, and the counters with the error word.  Each device that
+// runs the library holds one copy until the process ends; every call on a device uses
+// it, so calls that overlap on one device race.
+constexpr size_t NA_TABLE_BYTES = 4u << 20;
+constexpr size_t NA_PARTS_BYTES = 512u << 10;
+constexpr size_t NA_CNT_WORDS = 4096;
+constexpr size_t NA_BYTES = NA_TABLE_BYTES + NA_PARTS_BYTES + 4 * NA_CNT_WORDS;
+static __device__ __align__(256) uint8_t scratch[NA_BYTES];
+
+constexpr int NA_MAX_DEV = 64;
+struct NoAllocDev {
+    uint8_t* ptr = nullptr;       // device address of scratch on this device
+    bool has_key = false;
+    StepKey key{};                // shape whose work lists scratch holds
+};
+std::mutex g_na_mu;
+NoAllocDev g_na[NA_MAX_DEV];
+// host image of the work lists (static: building them allocates nothing either)
+uint32_t g_na_host[NA_TABLE_BYTES / 4];
+
+}  // namespace
+}  // namespace vq
+
+extern "C" {
+
+int vq_verify_linear(const vq_tiled* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype, void* ws,
+                     size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    LinearLayout L;
+    bool empty = false;
+    int rc = linear_check(W, x_f16, K, y, y_dtype, &L, &empty);
+    if (rc || empty) return rc;
+    if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+        return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", L.total, ws_bytes);
+    char* base = (char*)ws;
+    hipStream_t st = (hipStream_t)stream;
+    FlowArgs A{};
+    A.kp[SK_LIN] = L.kp;
+    const StepKey key{current_device(), W->format, K, L.kp.nwe, 0, 1, W->cols, 0, 0, W->rows, 0};
+    const StepDev* sd = nullptr;
+    rc = get_steps(key, A.kp, {{0, 1}}, 0, true, L.kp.nwe, (L.xcap / 2) & ~15, st, &sd);
+    if (rc) return rc;
+    return linear_launch(W, x_f16, K, y, y_dtype, L, (float*)base, (unsigned*)(base + L.off_cnt), sd->buf,
+                         sd->buf + sd->launch_start[0], st);
+}
+
+int vq_verify_linear_noalloc(const vq_tiled* W, const void* x_f16, int32_t K, void* y, int32_t y_dtype,
+                             void* stream) {
+    g_err[0] = 0;
+    LinearLayout L;
+    bool empty = false;
+    int rc = linear_check(W, x_f16, K, y, y_dtype, &L, &empty);
+    if (rc || empty) return rc;
+    const size_t parts_bytes = plan_parts_floats(L.kp, L.pbytes, L.kp.nwe, 1) * 4;
+    if (L.kp.nwin != 1 || parts_bytes > NA_PARTS_BYTES || L.zero_words > NA_CNT_WORDS)
+        return fail(VQ_ERR_UNSUPPORTED,
+                    "vq_verify_linear_noalloc: a %dx%d matrix at K %d needs column windows or more than its "
+                    "%zu bytes of partial sums; use vq_verify_linear", W->rows, W->cols, K, NA_PARTS_BYTES);
+    const int dev = current_device();
+    if (dev < 0 || dev >= NA_MAX_DEV) return fail(VQ_ERR_UNSUPPORTED, "device %d beyond %d", dev, NA_MAX_DEV);
+    hipStream_t st = (hipStream_t)stream;
+    std::lock_guard<std::mutex> g(g_na_mu);
+    NoAllocDev& D = g_na[dev];
+    if (!D.ptr) {
+        // the array's device address on this (current) device; the host-side name of the
+        // array is not a device address
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e, "scratch symbol address");
+        D.ptr = (uint8_t*)p;
+    }
+    uint32_t* const tab = (uint32_t*)D.ptr;
+    const StepKey key{dev, W->format, K, L.kp.nwe, 0, 1, W->cols, 0, 0, W->rows, 0};
+    const size_t nstart = (size_t)L.kp.nwe * FLOW_NCW;
+    const size_t words = NA_TABLE_BYTES / 4;
+    if (!D.has_key || memcmp(&D.key, &key, sizeof key) != 0) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+            return fail(VQ_ERR_UNSUPPORTED, "vq_verify_linear_noalloc: the first call with a shape copies its work "
+                                            "lists and cannot be captured: call it once before capturing");
+        KindPlan kp[6] = {};
+        kp[SK_LIN] = L.kp;
+        // start indices at the front, entries after them (a multiple of 8 words: entries stay
+        // 32-byte aligned)
+        const size_t soff = (nstart + 7) / 8 * 8;
+        if (soff >= words) return fail(VQ_ERR_UNSUPPORTED, "vq_verify_linear_noalloc: grid too large");
+        FixedStepTable T{g_na_host + soff, words - soff, 0, g_na_host, nstart, 0, false};
+        if (!build_steps(T, kp, 0, 1, 0, true, L.kp.nwe, (L.xcap / 2) & ~15))
+            return fail(VQ_ERR_UNSUPPORTED,
+                        "vq_verify_linear_noalloc: the work lists of a %dx%d matrix exceed its %zu bytes; use "
+                        "vq_verify_linear", W->rows, W->cols, NA_TABLE_BYTES);
+        for (size_t i = 0; i < nstart; ++i) g_na_host[i] += (uint32_t)(soff / 2);   // pairs from tab
+        D.has_key = false;
+        hipError_t e = hipMemcpyAsync(tab, g_na_host, (soff + T.n_ent()) * 4, hipMemcpyHostToDevice, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e, "work list copy");
+        D.key = key;
+        D.has_key = true;
+    }
+    uint8_t* const parts = D.ptr + NA_TABLE_BYTES;
+    unsigned* const cnt = (unsigned*)(parts + NA_PARTS_BYTES);
+    return linear_launch(W, x_f16, K, y, y_dtype, L, (float*)parts, cnt, tab, tab, st);
 }
 
 int vq_verify_accept(const vq_accept_desc* d, void* ws, size_t ws_bytes, void* stream) {

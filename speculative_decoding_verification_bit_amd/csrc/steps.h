@@ -27,6 +27,31 @@ constexpr int ST_ROUND = 4;                  // entries a wave reads per round
 struct StepTable {
     std::vector<uint32_t> ent;     // pairs (offset, flags)
     std::vector<uint32_t> start;   // per workgroup and compute wave: index of its first pair
+    void put_ent(uint32_t v) { ent.push_back(v); }
+    void put_start(uint32_t v) { start.push_back(v); }
+    size_t n_ent() const { return ent.size(); }
+    size_t n_start() const { return start.size(); }
+    bool ok() const { return true; }
+};
+
+// The same in caller-owned fixed storage (no allocation); ok() turns false once full.
+struct FixedStepTable {
+    uint32_t* ent;
+    size_t ent_cap, ne = 0;
+    uint32_t* start;
+    size_t start_cap, ns = 0;
+    bool full = false;
+    void put_ent(uint32_t v) {
+        if (ne < ent_cap) ent[ne++] = v;
+        else full = true;
+    }
+    void put_start(uint32_t v) {
+        if (ns < start_cap) start[ns++] = v;
+        else full = true;
+    }
+    size_t n_ent() const { return ne; }
+    size_t n_start() const { return ns; }
+    bool ok() const { return !full; }
 };
 
 namespace steps {
@@ -102,17 +127,17 @@ inline int stage_kind(int s, int L, bool linear) {
 
 // Appends the work lists of one launch (stages [s_begin, s_end), grid nwg) to T.  Returns
 // false if an entry would not fit its fields or an address would leave its matrix.
-inline bool build_steps(StepTable& T, const KindPlan kp[6], int s_begin, int s_end, int L, bool linear, int nwg,
-                        int xoff1) {
+template <class Table>
+bool build_steps(Table& T, const KindPlan kp[6], int s_begin, int s_end, int L, bool linear, int nwg, int xoff1) {
     using namespace steps;
-    if (s_end - s_begin > 127 || xoff1 % 16) return false;
-    std::vector<Seq> seqs((size_t)(s_end - s_begin));
+    if (s_end - s_begin > 127 || s_end <= s_begin || xoff1 % 16) return false;
+    Seq seqs[127];
     for (int w = 0; w < nwg; ++w) {
         for (int s = s_begin; s < s_end; ++s)
             seqs[s - s_begin] = seq_of(kp[stage_kind(s, L, linear)], w);
         for (int cw = 0; cw < FLOW_NCW; ++cw) {
-            T.start.push_back((uint32_t)(T.ent.size() / 2));
-            const size_t first = T.ent.size();
+            T.put_start((uint32_t)(T.n_ent() / 2));
+            const size_t first = T.n_ent();
             uint32_t pending = 0;        // units left behind, not yet closed
             // An entry without chunks still names a chunk (the last valid one, else the first
             // of the launch's first matrix): the waves load every entry's chunks, so that the
@@ -120,8 +145,8 @@ inline bool build_steps(StepTable& T, const KindPlan kp[6], int s_begin, int s_e
             uint32_t last_off = 0, last_stage = 0;
             auto emit = [&](uint32_t off, uint32_t flags) {
                 while (pending > ST_CLOSE_MAX) {
-                    T.ent.push_back(last_off);
-                    T.ent.push_back((ST_CLOSE_MAX << ST_CLOSE_SHIFT) | (last_stage << ST_STAGE_SHIFT));
+                    T.put_ent(last_off);
+                    T.put_ent((ST_CLOSE_MAX << ST_CLOSE_SHIFT) | (last_stage << ST_STAGE_SHIFT));
                     pending -= ST_CLOSE_MAX;
                 }
                 if (flags & ST_VALID) {
@@ -131,8 +156,8 @@ inline bool build_steps(StepTable& T, const KindPlan kp[6], int s_begin, int s_e
                     off = last_off;
                     flags |= last_stage << ST_STAGE_SHIFT;
                 }
-                T.ent.push_back(off);
-                T.ent.push_back(flags | (pending << ST_CLOSE_SHIFT));
+                T.put_ent(off);
+                T.put_ent(flags | (pending << ST_CLOSE_SHIFT));
                 pending = 0;
             };
             for (int s = s_begin; s < s_end; ++s) {
@@ -160,11 +185,11 @@ inline bool build_steps(StepTable& T, const KindPlan kp[6], int s_begin, int s_e
             }
             emit(0, ST_END);
             // whole rounds, and two more rounds of padding: the waves read two rounds ahead
-            while ((T.ent.size() - first) / 2 % ST_ROUND) emit(0, ST_END);
+            while ((T.n_ent() - first) / 2 % ST_ROUND && T.ok()) emit(0, ST_END);
             for (int i = 0; i < 2 * ST_ROUND; ++i) emit(0, ST_END);
         }
     }
-    return T.ent.size() / 2 < (1ul << 32);
+    return T.ok() && T.n_ent() / 2 < (1ul << 32);
 }
 
 }  // namespace vq
