@@ -37,7 +37,7 @@ SAMPLER = dict(T=0.6, top_p=0.95, min_p=0.05)
 ALPHAS = (0.5, 0.7, 0.9)
 PROFILE = os.path.join(ROOT, "profiles", "k_flow_q4min_k1_27b_decode.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "speculative_decoding_verification_bit_amd", "csrc", f)
-                  for f in ("flow.hip", "vq_device.h", "vq_internal.h")]
+                  for f in ("flow.hip", "vq_device.h", "vq_internal.h", "steps.h", "api.hip")]
 
 
 def log(*a):
@@ -309,8 +309,9 @@ def main():
         "staged_pass_ms": staged1 and round(staged1, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None if traffic is None else round(traffic / per_launch_bytes.mean(), 4),
-                     "traffic_bytes_per_launch": traffic,
+                     "traffic": traffic,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "traffic_over_algorithmic": None if traffic is None else round(traffic / per_launch_bytes.mean(), 4),
                      "kernel": "k_flow<Q4_MIN, K 1> (persistent, 16 layers per launch)",
                      "launches_per_pass": len(per_launch_ms),
                      "avg_launch_us": round(float(per_launch_ms.mean()) * 1e3, 3),
