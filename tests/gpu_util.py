@@ -19,6 +19,13 @@ def say(*a):
     sys.stdout.flush()
 
 
+def report(line: str):
+    """say(), and keep the line for the end-of-session summary (shown by quiet runs too)."""
+    say(line)
+    import conftest
+    conftest.REPORT.append(line)
+
+
 def f32(v: float) -> float:
     """The float32 value the C ABI receives for a sampler setting, as a double."""
     return float(np.float32(v))

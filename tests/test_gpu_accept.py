@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import f32, need_gpu, say
+from gpu_util import f32, need_gpu, report, say
 
 pytestmark = pytest.mark.gpu
 
@@ -32,24 +32,27 @@ def _oracle(mode, t, d=None, dtok=None, draft_mode=0, T=1.0, top_p=1.0, min_p=0.
                          window_base, threads=8)
 
 
-def _compare(g, o, exact: bool, what: str, max_near_frac=0.05, max_near_mismatch=0.25):
+def _compare(g, o, exact: bool, what: str, max_near_frac=0.05):
+    """Exact: every window agrees.  Otherwise every window agrees except those with an
+    oracle decision within 1e-6 of its threshold (flagged), of which at most max_near_frac
+    may exist; flagged windows are counted and reported whether or not they agree."""
     W = len(o["n_accepted"])
     same = ((g["n_accepted"] == o["n_accepted"]) & (g["status"] == o["status"])
             & np.all(g["tokens"] == o["tokens"], axis=1))
     if g.get("draft_tokens") is not None and o["draft_tokens"].size:
         same &= np.all(g["draft_tokens"] == o["draft_tokens"], axis=1)
     near = o["near"] != 0
-    say(f"{what}: {W} windows, near-threshold {int(near.sum())}, mismatches {int((~same).sum())} "
-        f"(of which near {int((~same & near).sum())})")
+    n_near, n_bad = int(near.sum()), int((~same).sum())
+    n_bad_far = int((~same & ~near).sum())
+    line = (f"{what}: {W} windows, flagged (within 1e-6 of a threshold) {n_near}, mismatches {n_bad} "
+            f"(flagged {n_bad - n_bad_far}, unflagged {n_bad_far})")
+    report(line)
     if exact:
-        assert same.all(), f"{what}: windows {np.nonzero(~same)[0][:10]} differ"
+        assert same.all(), f"{line}; windows {np.nonzero(~same)[0][:10]} differ"
     else:
-        assert (same | near).all(), f"{what}: windows {np.nonzero(~same & ~near)[0][:10]} differ"
-        assert near.mean() <= max_near_frac
-        # flagged windows are excluded from the exact check, but the GPU should still
-        # agree on most of them (its kept-set sums are exact in fixed point)
-        assert (~same & near).sum() <= max(1, max_near_mismatch * near.sum())
-    return int(near.sum())
+        assert n_bad_far == 0, f"{line}; unflagged windows {np.nonzero(~same & ~near)[0][:10]} differ"
+        assert n_near <= max_near_frac * W, f"{line}; more than {max_near_frac:.0%} of the windows flagged"
+    return n_near
 
 
 def test_c1_greedy_and_sampling():
@@ -78,20 +81,18 @@ def test_c4_sampler_settings_reduced_windows():
     _compare(g, o, False, "C4 first 48 windows", max_near_frac=0.05)
 
 
-@pytest.mark.parametrize("T,top_p,min_p", [(1.0, 0.9, 0.0), (0.6, 0.5, 0.0), (2.0, 0.99, 0.0),
+@pytest.mark.parametrize("T,top_p,min_p", [(0.6, 0.9, 0.0), (0.6, 0.5, 0.0), (0.8, 0.9, 0.0),
                                             (1.0, 1.0, 0.1), (0.6, 0.95, 0.05)])
 def test_top_p_radix_select_and_min_p(T, top_p, min_p):
-    """Top-p without min-p needs the exact cut over the whole vocabulary."""
-    spec = synth.LogitSpec(seed=7, K=3, vocab=151936, target_sigma=2.0, noise_sigma=0.7)
-    t, d = synth.logits_batch(spec, 0, 12, threads=12)
+    """Top-p without min-p needs the exact cut over the whole vocabulary (V = 151936).  The
+    settings keep the cut's cumulative mass away from top_p on at least 95% of the windows
+    (target logits ~N(0, 3)), so that the radix select is checked window by window."""
+    spec = synth.LogitSpec(seed=7, K=3, vocab=151936, target_sigma=3.0, noise_sigma=1.0)
+    t, d = synth.logits_batch(spec, 0, 40, threads=12)
     kw = dict(draft_mode=oracle.DRAFT_Q_SAMPLE, T=T, top_p=top_p, min_p=min_p, seed=5)
     o = _oracle(oracle.MODE_SAMPLE, t, d, **kw)
     g = _gpu(1, t, d, **kw)
-    # Top-p alone at T >= 1 keeps thousands of tokens of ~1e-6 mass each, so the
-    # cumulative mass at the cut is almost always within 1e-6 of top_p: most windows
-    # are flagged by construction and only their agreement rate is checked.
-    frac = 1.0 if (min_p == 0.0 and top_p < 1.0) else 0.2
-    _compare(g, o, False, f"T {T} top-p {top_p} min-p {min_p}", max_near_frac=frac)
+    _compare(g, o, False, f"V 151936 T {T} top-p {top_p} min-p {min_p}", max_near_frac=0.05)
 
 
 def test_single_window_k1_sampled_full_vocab():
@@ -110,7 +111,7 @@ def test_single_window_k1_sampled_full_vocab():
             os_.setdefault(k, []).append(o[k])
     gs = {k: np.concatenate(v) for k, v in gs.items()}
     os_ = {k: np.concatenate(v) for k, v in os_.items()}
-    _compare(gs, os_, False, "K=1 single windows, T 0.6 top-p 0.95 min-p 0.05", max_near_frac=0.25)
+    _compare(gs, os_, False, "K=1 single windows, T 0.6 top-p 0.95 min-p 0.05", max_near_frac=0.05)
     for w in range(8):
         g = _gpu(0, t[w:w + 1])
         assert g["tokens"][0, 0] == int(np.argmax(t[w, 0]))
@@ -125,7 +126,7 @@ def test_top_p_ties_resolved_by_index():
     kw = dict(draft_mode=oracle.DRAFT_Q_SAMPLE, T=1.0, top_p=0.6, seed=2)
     o = _oracle(oracle.MODE_SAMPLE, base, d, **kw)
     g = _gpu(1, base, d, **kw)
-    _compare(g, o, False, "integer logits (ties) top-p 0.6", max_near_frac=0.2)
+    _compare(g, o, False, "integer logits (ties) top-p 0.6", max_near_frac=0.05)
 
 
 def test_agree_drafter_greedy_full_vocab():
@@ -140,7 +141,7 @@ def test_agree_drafter_greedy_full_vocab():
     t2, d2 = synth.logits_batch(synth.LogitSpec(3, 4, 151936, 3.0, 1.0), 100, 116, threads=16)
     o = _oracle(oracle.MODE_GREEDY, t2, d2, **kw)
     g = _gpu(0, t2, d2, **kw)
-    _compare(g, o, False, "greedy verify of sampled drafts", max_near_frac=0.2)
+    _compare(g, o, False, "greedy verify of sampled drafts", max_near_frac=0.05)
 
 
 def test_edge_cases():
@@ -184,8 +185,9 @@ def test_edge_cases():
     assert out["tokens"].shape == (0, 3)
 
 
-def test_c4_full_size_sampled_windows():
-    """All 1,000 C4 windows on the GPU (9.1 GB of logits); 40 sampled windows checked."""
+def test_c4_full_size_all_windows():
+    """All 1,000 C4 windows (K 8, V 151936, 9.1 GB of logits) on the GPU in one call, every
+    window against the oracle (which consumes the same counter-based uniforms)."""
     torch = need_gpu()
     import speculative_decoding_verification_bit_amd as vq
     c = synth.C4
@@ -193,30 +195,26 @@ def test_c4_full_size_sampled_windows():
     W = c["windows"]
     td = torch.empty((W, spec.K, spec.vocab), dtype=torch.float32, device="cuda")
     dd = torch.empty((W, spec.K - 1, spec.vocab), dtype=torch.float32, device="cuda")
+    okw = dict(draft_mode=oracle.DRAFT_Q_SAMPLE, T=c["T"], top_p=c["top_p"], min_p=c["min_p"],
+               seed=c["philox_seed"])
+    o = {}
     for w0 in range(0, W, 100):
         t, d = synth.logits_batch(spec, w0, w0 + 100, threads=16)
         td[w0:w0 + 100].copy_(torch.from_numpy(t))
         dd[w0:w0 + 100].copy_(torch.from_numpy(d))
-    say("C4 logits uploaded")
-    kw = dict(draft_mode=2, T=c["T"], top_p=c["top_p"], min_p=c["min_p"], seed=c["philox_seed"])
-    out = vq.verify_accept(1, td, dd, **kw)
+        r = oracle.accept(oracle.MODE_SAMPLE, t, d, None, window_base=w0, threads=16,
+                          **{k: (f32(v) if k in ("T", "top_p", "min_p") else v) for k, v in okw.items()})
+        for k, v in r.items():
+            o.setdefault(k, []).append(v)
+        say(f"C4 windows {w0}..{w0 + 99}: uploaded, oracle done")
+    o = {k: np.concatenate(v) for k, v in o.items()}
+    out = vq.verify_accept(1, td, dd, **okw)
     torch.cuda.synchronize()
     g = {k: v.cpu().numpy() for k, v in out.items()}
     del td, dd
     torch.cuda.empty_cache()
     assert np.all(g["status"] == 0)
-    pick = np.sort(np.random.default_rng(0).choice(W, 40, replace=False))
-    t = np.stack([synth.window_logits(spec, int(w))[0] for w in pick])
-    d = np.stack([synth.window_logits(spec, int(w))[1] for w in pick])
-    okw = dict(draft_mode=oracle.DRAFT_Q_SAMPLE, T=c["T"], top_p=c["top_p"], min_p=c["min_p"],
-               seed=c["philox_seed"])
-    o = {}
-    for i, w in enumerate(pick):      # each sampled window keeps its own counter
-        r = _oracle(oracle.MODE_SAMPLE, t[i:i + 1], d[i:i + 1], window_base=int(w), **okw)
-        for k, v in r.items():
-            o.setdefault(k, []).append(v)
-    o = {k: np.concatenate(v) for k, v in o.items()}
-    gs = {k: v[pick] for k, v in g.items()}
-    _compare(gs, o, False, "C4 full size, 40 sampled windows", max_near_frac=0.1)
+    _compare(g, o, False, "C4 all 1000 windows (K 8, V 151936, T 0.6, top-p 0.95, min-p 0.05)",
+             max_near_frac=0.05)
     emitted = g["n_accepted"] + 1
-    say(f"C4 mean tokens per pass {emitted.mean():.3f}")
+    report(f"C4 mean tokens per pass {emitted.mean():.3f} (oracle {(o['n_accepted'] + 1).mean():.3f})")

@@ -528,3 +528,105 @@ def test_k1_is_plain_decode():
     p, _ = oracle.warp(t[0], 1.0)
     counts = np.bincount(s["tokens"][:, 0], minlength=V)
     assert scipy.stats.chisquare(counts, W * p).pvalue > 1e-3
+
+
+# ------------------------------------------------ tolerance base and near-threshold flags
+
+@pytest.mark.parametrize("fmt", [synth.FMT_Q4, synth.FMT_Q4_MIN, synth.FMT_MXFP4])
+def test_tolerance_base_is_sum_of_abs_products(fmt):
+    """a[k][r] = sum_j |w_rj x_kj| exactly (numpy on the dequantised matrix), so that the
+    parity bound 1e-3 * a is neither loosened (e.g. sum|w| * sum|x|) nor tightened."""
+    W = _small_matrix(fmt, rows=23, cols=160)
+    x = synth.activations(3, 4, W.cols)
+    x[0, :7] = -x[0, :7]                       # mixed signs inside a block
+    _, a = oracle.linear(W, x)
+    Wd = oracle.dequant(W)
+    for k in range(x.shape[0]):
+        ref = np.abs(Wd * x[k].astype(np.float64)[None, :]).sum(axis=1)
+        assert np.allclose(a[k], ref, rtol=1e-13, atol=0), f"column {k}"
+    # a strict bound: a row with cancelling terms has |y| < a
+    y, _ = oracle.linear(W, x)
+    assert np.any(np.abs(y) < 0.5 * a)
+
+
+def _softmax64(l):
+    z = l.astype(np.float64)
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+# six distinct logits: masses in decreasing order, cumulative sums C_1..C_6
+_L6 = np.array([2.0, 1.5, 1.0, 0.5, 0.0, -0.5], np.float32)
+_P6 = _softmax64(_L6)
+_C6 = np.cumsum(_P6)
+
+
+@pytest.mark.parametrize("delta,near,m_p", [(5e-7, 1, 3), (2e-6, 0, 3), (-5e-7, 1, 2), (-2e-6, 0, 2)])
+def test_near_top_p_flag_straddles_1e6(delta, near, m_p):
+    """The top-p flag: cumulative mass at the cut (C_m) or before it (C_{m-1}) within 1e-6
+    of top_p.  top_p = C_2 + delta: the cut is token 3 and C_2 is the mass before it
+    (delta > 0), or token 2 with C_2 the mass at it (delta < 0)."""
+    _, info = oracle.warp(_L6, 1.0, top_p=float(_C6[1] + delta))
+    assert info.m_p == m_p and info.n_keep == m_p
+    assert info.near_top_p == near, (delta, info.near_top_p)
+    assert info.near_min_p == 0
+
+
+@pytest.mark.parametrize("delta,near,m_m", [(5e-7, 1, 3), (2e-6, 0, 3), (-5e-7, 1, 4), (-2e-6, 0, 4)])
+def test_near_min_p_flag_straddles_1e6(delta, near, m_m):
+    """The min-p flag: the last kept or the first dropped token within 1e-6 * pi_max of
+    min_p * pi_max.  min_p = pi_4 / pi_max + delta drops token 4 just below the cut
+    (delta > 0) or keeps it just above (delta < 0); the margin scales with pi_max."""
+    _, info = oracle.warp(_L6, 1.0, min_p=float(_P6[3] / _P6[0] + delta))
+    assert info.m_m == m_m and info.n_keep == m_m
+    assert info.near_min_p == near, (delta, info.near_min_p)
+    assert info.near_top_p == 0
+
+
+def test_near_flags_only_where_the_cut_binds():
+    """A near top-p cut is not flagged when min-p keeps fewer tokens, and a near min-p cut
+    is not flagged when top-p keeps fewer."""
+    _, info = oracle.warp(_L6, 1.0, top_p=float(_C6[1] + 5e-7), min_p=0.99)
+    assert info.m_p == 3 and info.m_m == 1 and info.n_keep == 1
+    assert info.near_top_p == 0 and info.near_min_p == 0
+    _, info = oracle.warp(_L6, 1.0, top_p=float(_C6[1] + 5e-7), min_p=0.01)
+    assert info.n_keep == 3 and info.near_top_p == 1
+    _, info = oracle.warp(_L6, 1.0, top_p=float(_C6[0] - 0.01), min_p=float(_P6[3] / _P6[0] + 5e-7))
+    assert info.m_p == 1 and info.m_m == 3 and info.n_keep == 1
+    assert info.near_min_p == 0 and info.near_top_p == 0
+    _, info = oracle.warp(_L6, 1.0, top_p=0.999, min_p=float(_P6[3] / _P6[0] + 5e-7))
+    assert info.n_keep == 3 and info.near_min_p == 1
+
+
+@pytest.mark.parametrize("scale", [1.0, 4.0])
+def test_near_cat_flag_straddles_1e6_of_the_total(scale):
+    """The draw's flag: u * S within 1e-6 * S of C_j (the mass up to the drawn token) or of
+    C_{j-1} (the mass before it).  Weights summing to 4 check that the margin scales with S."""
+    w = scale * np.array([0.25, 0.25, 0.5])
+    assert oracle.cat(w, 0.25 + 5e-7) == (1, True)      # just past C_0
+    assert oracle.cat(w, 0.25 + 2e-6) == (1, False)
+    assert oracle.cat(w, 0.5 - 5e-7) == (1, True)       # just short of C_1
+    assert oracle.cat(w, 0.5 - 2e-6) == (1, False)
+    assert oracle.cat(w, 0.75) == (2, False)
+
+
+@pytest.mark.parametrize("delta", [5e-7, -5e-7, 2e-6, -2e-6])
+def test_near_ratio_flag_straddles_1e6(delta):
+    """The ratio test's flag: |u_A - p(x)/q(x)| < 1e-6.  One draft (token 0) over two
+    tokens; the target logits are set so that p(x)/q(x) = u_A + delta, with u_A the
+    window's first uniform at position 1."""
+    seed, win = 21, 0
+    uA = float(oracle.uniforms(seed, win, 1)[0])
+    dl = np.array([0.0, np.log(0.25)], np.float32)
+    q0 = float(_softmax64(dl)[0])
+    target_p0 = q0 * (uA + delta)
+    assert 0.0 < target_p0 < 1.0
+    d = np.float32(np.log(1.0 / target_p0 - 1.0))
+    tl = np.array([0.0, d], np.float32)
+    r = float(_softmax64(tl)[0]) / q0                  # what the oracle computes, in double
+    assert abs((r - uA) - delta) < 1e-7
+    out = oracle.accept(oracle.MODE_SAMPLE, np.stack([tl, tl])[None], dl[None, None],
+                        np.zeros((1, 1), np.int32), oracle.DRAFT_GIVEN, T=1.0, seed=seed)
+    near = int(out["near"][0])
+    assert bool(near & oracle.NEAR_RATIO) == (abs(delta) < 1e-6), (delta, near)
+    assert out["n_accepted"][0] == (1 if uA < r else 0)
