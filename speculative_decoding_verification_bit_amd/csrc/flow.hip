@@ -618,6 +618,13 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) stat[i] = 0.f;
         int npend = 0;
+        int nrel = 0;                            // parts stored whose counters are not yet raised
+        auto flush_rel = [&]() __attribute__((always_inline)) {
+            __builtin_amdgcn_s_waitcnt(0);
+            for (int j = lane; j < nrel; j += 64)
+                __hip_atomic_fetch_add(A.cnt + C.rel_t[j], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            nrel = 0;
+        };
         // one window: a split tile's second part is this workgroup's (kept in registers, it
         // is the first unit of its range); the first part comes from the previous workgroup.
         // Half-way through the units its counter is read once (the load stays in flight while
@@ -668,9 +675,17 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) st_dev_f32(ps + 4 * lane + i, sum[i]);
                 }
-                __builtin_amdgcn_s_waitcnt(0);
-                if (lane == 0)
-                    __hip_atomic_fetch_add(counter(ut, side), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (P.nwin == 1) {
+                    // one window: the next workgroup's finisher waits for this part early
+                    __builtin_amdgcn_s_waitcnt(0);
+                    if (lane == 0)
+                        __hip_atomic_fetch_add(counter(ut, side), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    // several windows: the counters are raised together after the unit loop
+                    // (one wait for the stores instead of one per unit)
+                    if (lane == 0) C.rel_t[nrel] = ut;
+                    if (++nrel == FLOW_REL_MAX) flush_rel();
+                }
                 // several windows: the finisher of a tile is the workgroup holding the last
                 // chunk of the tile's unit in window t mod nwin
                 if (P.nwin > 1) {
@@ -685,6 +700,7 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             }
         }
         useq += (unsigned)q.nU;
+        if (nrel > 0) flush_rel();
 
         // -------- finish the split tiles this workgroup owns
         auto poll = [&](const unsigned* cn, unsigned expect) __attribute__((always_inline)) {

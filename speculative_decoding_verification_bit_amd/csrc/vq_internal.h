@@ -59,6 +59,7 @@ constexpr int FLOW_NCW = 11;             // compute waves per workgroup (plus on
 constexpr int FLOW_LDS = 163840;         // LDS per workgroup (gfx950: 160 KB)
 constexpr int FLOW_NSP_MAX = 8;          // slots of the partial-sum ring
 constexpr int FLOW_PEND_MAX = 64;        // split tiles one workgroup finishes per stage
+constexpr int FLOW_REL_MAX = 256;        // parts whose counters are raised in one batch
 // Completion counters of a stage: one per XCD group of workgroups (blockIdx mod 8), each
 // on its own 128-byte line.
 constexpr int DONE_REPL = 8;
@@ -74,6 +75,7 @@ struct FlowCtrl {
     unsigned pad_[2];
     float rho[VQ_MAX_K];
     int pend_t[FLOW_PEND_MAX];
+    int rel_t[FLOW_REL_MAX];         // tiles whose part counters the conductor raises next
 };
 constexpr int FLOW_CTRL_OFF = (FLOW_LDS - (int)sizeof(FlowCtrl)) & ~255;
 
