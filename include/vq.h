@@ -13,17 +13,25 @@
  *
  * Conventions for every entry point:
  *   - Buffers are caller-owned DEVICE pointers unless stated otherwise; descriptors are
- *     HOST structs, read only during the call.  The library never allocates device or
- *     host memory; scratch space is a caller-provided workspace sized by
- *     vq_workspace_bytes().
- *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).  No call
- *     synchronises the host, copies to the host or allocates.  Buffers must stay alive
- *     until the stream has executed the work.
+ *     HOST structs, read only during the call.  Per-call scratch space is a caller-provided
+ *     workspace sized by vq_workspace_bytes().
+ *   - Work lists: the weight-streaming kernel follows, per compute wave, a list of steps
+ *     that depends only on the shapes, K and the device's compute-unit count.  The first
+ *     vq_verify_linear or vq_decode_pass call with a new (device, shapes, K, launch mode)
+ *     builds that list on the host, allocates device memory for it, copies it and waits
+ *     for `stream`; the library keeps it until the process ends (about 44 MB for a
+ *     27B-class pass at one K) and reuses it in every later call with the same key.  Such
+ *     a first call cannot be captured into a graph (it returns VQ_ERR_UNSUPPORTED under
+ *     capture): call once before capturing.  vq_verify_linear_noalloc keeps its lists in
+ *     static device memory instead.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).  Apart from
+ *     the first call with a new key above, no call synchronises the host, copies to the
+ *     host or allocates.  Buffers must stay alive until the stream has executed the work.
  *   - Return value: VQ_OK (0) or a negative VQ_ERR_* code.  Arguments are validated on
  *     the host before anything is launched; on an argument error nothing is enqueued.
  *     vq_last_error() returns a thread-local text for the last failure.
- *   - No C++ exception crosses this interface; the library keeps no global mutable
- *     state besides that thread-local text.
+ *   - No C++ exception crosses this interface.  Global state: the work lists above (behind
+ *     a mutex) and that thread-local text.
  *   - Calls that share a workspace must not overlap on the device.
  */
 #ifndef VQ_H
