@@ -298,20 +298,21 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         // runs one round ahead of the consume side.
         typedef const __attribute__((address_space(4))) uint32_t CU32;
         const uint32_t first = ((CU32*)A.step_start)[w * NCW + cw];
-        const u4_t* const tab = (const u4_t*)(A.steps + 2 * (size_t)first);
-        constexpr int RV = DEPTH / 2;           // u4 words per round
-        static_assert(DEPTH % 2 == 0, "a round is whole 16-byte words");
-        u4_t e0[RV], e1[RV], e2[RV];
-        auto load_round = [&](u4_t* e, int r) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < RV; ++i) e[i] = tab[RV * r + i];
+        const uint32_t* const tab = A.steps + 2 * (size_t)first;
+        // a round's 2 DEPTH words sit in lanes 0 .. 2 DEPTH - 1 of one register (one
+        // dword load per lane; the other lanes load a copy)
+        const int tl = lane % (2 * DEPTH);
+        static_assert(2 * DEPTH <= 64, "a round fits the lanes of one register");
+        uint32_t e0, e1, e2;
+        auto load_round = [&](int r) __attribute__((always_inline)) -> uint32_t {
+            return tab[2 * DEPTH * r + tl];
         };
         // entry u of a round: (offset, flags)
-        auto ent_off = [&](const u4_t* e, int u) __attribute__((always_inline)) -> uint32_t {
-            return (uint32_t)uni((int)e[u >> 1][2 * (u & 1)]);
+        auto ent_off = [&](uint32_t e, int u) __attribute__((always_inline)) -> uint32_t {
+            return (uint32_t)__builtin_amdgcn_readlane((int)e, 2 * u);
         };
-        auto ent_flags = [&](const u4_t* e, int u) __attribute__((always_inline)) -> uint32_t {
-            return (uint32_t)uni((int)e[u >> 1][2 * (u & 1) + 1]);
+        auto ent_flags = [&](uint32_t e, int u) __attribute__((always_inline)) -> uint32_t {
+            return (uint32_t)__builtin_amdgcn_readlane((int)e, 2 * u + 1);
         };
         int ib_idx = -1;                   // launch stage whose matrix ibase is
         const uint8_t* ibase = A.lm;
@@ -426,23 +427,20 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             }
         };
 
-        load_round(e0, 0);
-        load_round(e1, 1);
+        e0 = load_round(0);
+        e1 = load_round(1);
 #pragma unroll
         for (int u = 0; u < DEPTH; ++u) issue(u, ent_off(e0, u), ent_flags(e0, u));
         for (int r = 0;; ++r) {
-            load_round(e2, r + 2);
+            e2 = load_round(r + 2);
 #pragma unroll
             for (int u = 0; u < DEPTH; ++u) {
                 consume(u, ent_flags(e0, u));
                 issue(u, ent_off(e1, u), ent_flags(e1, u));
             }
             if (ent_flags(e0, DEPTH - 1) & ST_END) break;
-#pragma unroll
-            for (int i = 0; i < RV; ++i) {
-                e0[i] = e1[i];
-                e1[i] = e2[i];
-            }
+            e0 = e1;
+            e1 = e2;
         }
         return;
     }
