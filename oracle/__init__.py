@@ -56,6 +56,14 @@ def lib():
         L.or_e8m0.restype = D
         L.or_e8m0.argtypes = [ctypes.c_uint8]
         L.or_dequant.argtypes = [I32, P, P, P, I64, I64, P]
+        L.or_linear_x64.restype = I32
+        L.or_linear_x64.argtypes = [I32, P, P, P, I64, I64, P, I32, P, P, I32]
+        L.or_e4m3.restype = D
+        L.or_e4m3.argtypes = [I32]
+        L.or_e4m3_code.restype = I32
+        L.or_e4m3_code.argtypes = [D]
+        L.or_mx_quant.restype = I32
+        L.or_mx_quant.argtypes = [P, I64, I64, P, P]
         L.or_linear.restype = I32
         L.or_linear.argtypes = [I32, P, P, P, I64, I64, P, I32, P, P, I32]
         L.or_rho.argtypes = [P, I32, I64, P]
@@ -123,6 +131,50 @@ def linear(m, x: np.ndarray, threads: int = 1):
     if rc:
         raise RuntimeError(f"or_linear failed ({rc})")
     return y, a
+
+
+def linear_x64(m, x: np.ndarray, threads: int = 1):
+    """linear() with double activations x [K][cols] (e.g. MX-dequantised ones)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    K = x.shape[0]
+    assert x.shape[1] == m.cols
+    y = np.empty((K, m.rows), np.float64)
+    a = np.empty((K, m.rows), np.float64)
+    qs = np.ascontiguousarray(m.qs)
+    sc = np.ascontiguousarray(m.scales)
+    mn = None if m.mins is None else np.ascontiguousarray(m.mins)
+    rc = lib().or_linear_x64(m.fmt, _p(qs), _p(sc), _p(mn), m.rows, m.cols, _p(x), K, _p(y), _p(a), threads)
+    if rc:
+        raise RuntimeError(f"or_linear_x64 failed ({rc})")
+    return y, a
+
+
+def e4m3(code: int) -> float:
+    """Value of an OCP E4M3 code."""
+    return float(lib().or_e4m3(int(code)))
+
+
+def e4m3_code(v: float) -> int:
+    return int(lib().or_e4m3_code(float(v)))
+
+
+def mx_quant(x: np.ndarray):
+    """fp16 activations [K][cols] -> (E4M3 codes [K][cols] u8, E8M0 scales [K][cols/32] u8)."""
+    x = np.ascontiguousarray(x, dtype=np.float16)
+    K, cols = x.shape
+    codes = np.empty((K, cols), np.uint8)
+    scales = np.empty((K, cols // 32), np.uint8)
+    rc = lib().or_mx_quant(_p(x.view(np.uint16)), K, cols, _p(codes), _p(scales))
+    if rc:
+        raise RuntimeError(f"or_mx_quant failed ({rc})")
+    return codes, scales
+
+
+def mx_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The activations an MX-quantised block stands for, in double: e4m3(code) * 2^(s - 127)."""
+    table = np.array([e4m3(c) for c in range(256)], np.float64)
+    sc = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return table[codes] * np.repeat(sc, 32, axis=1)
 
 
 def rho(v: np.ndarray) -> np.ndarray:

@@ -173,6 +173,96 @@ int or_linear(int fmt, const uint8_t* qs, const void* scales, const uint16_t* mi
     return 0;
 }
 
+/* Same, with the activations given in double ([K][cols]), for inputs that are not fp16
+ * values (the MX-quantised activations below). */
+int or_linear_x64(int fmt, const uint8_t* qs, const void* scales, const uint16_t* mins,
+                  int64_t rows, int64_t cols, const double* x, int K,
+                  double* y, double* a, int nthreads) {
+    if (cols % 32 || K < 1 || rows < 0) return -1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > rows) nthreads = rows > 0 ? (int)rows : 1;
+    pthread_t th[256];
+    lin_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        lin_job J = {fmt, qs, scales, mins, rows, cols, x, K, y, a,
+                     rows * t / nthreads, rows * (t + 1) / nthreads};
+        jobs[t] = J;
+    }
+    for (int t = 1; t < nthreads; ++t) pthread_create(&th[t], NULL, lin_worker, &jobs[t]);
+    lin_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
+
+/* ------------------------------------------------------- MX-quantised activations */
+
+/* The CDNA4 scaled matrix instructions multiply MXFP4 weights with activations in an
+ * 8-bit MX format; this is the activation side of that (approximate) path, following
+ * the OCP Microscaling Formats v1.0 specification.
+ *
+ * E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is subnormal
+ * (m/8 * 2^-6); S.1111.111 is NaN; there are no infinities; the largest finite value is
+ * 448. */
+double or_e4m3(int code) {
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double mag = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + (double)m, e - 10);
+    return s ? -mag : mag;
+}
+
+/* The E4M3 code of v: the finite value nearest to |v|, ties to the code with an even
+ * mantissa, saturating at 448 (a search over the 127 non-negative finite codes); the
+ * sign bit is v's. */
+static int e4m3_code(double v) {
+    double a = fabs(v);
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double d = fabs(or_e4m3(c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            bd = d;
+            best = c;
+        }
+    }
+    return signbit(v) ? (best | 0x80) : best;
+}
+
+int or_e4m3_code(double v) { return e4m3_code(v); }
+
+/* One block of 32 activations -> a shared E8M0 scale and 32 E4M3 codes, as the OCP MX
+ * specification converts a block: the shared exponent is floor(log2(max |x|)) minus the
+ * largest exponent of the element type (8 for E4M3), and each element is x / 2^shared
+ * converted to E4M3 (to nearest, ties to even, saturating).  An all-zero block gets
+ * shared exponent -127 (scale byte 0).  x fp16 [K][cols]; codes [K][cols], scales
+ * [K][cols / 32]. */
+int or_mx_quant(const uint16_t* x, int64_t K, int64_t cols, uint8_t* codes, uint8_t* scales) {
+    if (cols % 32 || K < 1) return -1;
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t b = 0; b < cols / 32; ++b) {
+            const uint16_t* xb = x + k * cols + 32 * b;
+            double amax = 0.0;
+            for (int j = 0; j < 32; ++j) {
+                double v = or_half(xb[j]);
+                if (!isfinite(v)) return -2;
+                if (fabs(v) > amax) amax = fabs(v);
+            }
+            int E = -127;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);           /* amax = f * 2^ex, 0.5 <= f < 1 */
+                E = (ex - 1) - 8;
+                if (E < -127) E = -127;
+                if (E > 127) E = 127;
+            }
+            scales[k * (cols / 32) + b] = (uint8_t)(E + 127);
+            for (int j = 0; j < 32; ++j)
+                codes[k * cols + 32 * b + j] = (uint8_t)e4m3_code(ldexp(or_half(xb[j]), -E));
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ stage glue */
 
 /* rho: out[k][j] = v[k][j] / sqrt(mean_j v[k][j]^2), per activation column k. */

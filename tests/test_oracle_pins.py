@@ -630,3 +630,80 @@ def test_near_ratio_flag_straddles_1e6(delta):
     near = int(out["near"][0])
     assert bool(near & oracle.NEAR_RATIO) == (abs(delta) < 1e-6), (delta, near)
     assert out["n_accepted"][0] == (1 if uA < r else 0)
+
+
+# -------------------------------------------- MX-quantised activations (scaled MFMA path)
+
+def test_e4m3_table_ocp_mx():
+    """OCP MX v1.0 E4M3: subnormals m/8 * 2^-6, 1.0 = 0x38, largest 448 = 0x7E, NaN at
+    S.1111.111, sign symmetric; magnitudes strictly increasing over codes 0..0x7E."""
+    v = np.array([oracle.e4m3(c) for c in range(256)])
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    assert v[0x38] == 1.0 and v[0x39] == 1.125 and v[0x7E] == 448.0 and v[0x77] == 240.0 and v[0x78] == 256.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.all(np.diff(v[:0x7F]) > 0)
+    assert np.array_equal(v[0x80:0xFF], -v[0x00:0x7F]) and np.signbit(v[0x80])
+
+
+def test_e4m3_rounding_ties_even_and_saturation():
+    """Nearest value, ties to the even mantissa, saturation at 448, the sign of -0."""
+    assert oracle.e4m3_code(1.0625) == 0x38          # halfway 1.0 / 1.125 -> even (1.0)
+    assert oracle.e4m3_code(1.1875) == 0x3A          # halfway 1.125 / 1.25 -> even (1.25)
+    assert oracle.e4m3_code(1.07) == 0x39
+    assert oracle.e4m3_code(3 * 2.0 ** -10) == 0x02  # halfway 1/512 and 2/512 -> even (2)
+    assert oracle.e4m3_code(480.0) == 0x7E and oracle.e4m3_code(1e6) == 0x7E
+    assert oracle.e4m3_code(-0.0) == 0x80 and oracle.e4m3_code(-1.0) == 0xB8
+    rng = np.random.default_rng(4)
+    for x in rng.uniform(-440, 440, 2000):
+        c = oracle.e4m3_code(x)
+        vals = np.array([oracle.e4m3(k) for k in range(0x7F)])
+        assert abs(abs(oracle.e4m3(c)) - abs(x)) == np.min(np.abs(vals - abs(x)))
+
+
+def test_mx_quant_block_rules():
+    """Shared exponent: the block's largest magnitude lands in [256, 512) before rounding;
+    representable blocks are recovered exactly; every element within half a step of
+    its E4M3 neighbourhood; an all-zero block has scale byte 0."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((3, 256)) * np.exp(rng.uniform(-6, 6, (3, 256)))).astype(np.float16)
+    x[2, 32:64] = 0
+    codes, scales = oracle.mx_quant(x)
+    xh = oracle.mx_dequant(codes, scales)
+    xd = x.astype(np.float64)
+    for k in range(3):
+        for b in range(8):
+            blk = xd[k, 32 * b:32 * b + 32]
+            E = int(scales[k, b]) - 127
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert scales[k, b] == 0 and np.all(codes[k, 32 * b:32 * b + 32] & 0x7F == 0)
+                continue
+            assert 256 <= amax / 2.0 ** E < 512
+            v = blk / 2.0 ** E
+            err = np.abs(xh[k, 32 * b:32 * b + 32] / 2.0 ** E - v)
+            # half the spacing of the E4M3 values around |v| (1/16 of the binade, 2^-10
+            # below 2^-6), or the saturation above 448
+            step = np.where(np.abs(v) < 2.0 ** -6, 2.0 ** -9,
+                            2.0 ** np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6))) / 8)
+            ok = (err <= step / 2) | ((np.abs(v) > 448) & (np.abs(xh[k, 32 * b:32 * b + 32] / 2.0 ** E) == 448))
+            assert ok.all(), (k, b)
+    # a block made of E4M3 values times 2^-3 whose largest is 448 * 2^-3 is recovered exactly
+    vals = np.array([oracle.e4m3(c) for c in rng.integers(0, 0x7E, 32)])
+    vals[7] = 448.0
+    xb = (vals * 2.0 ** -3).astype(np.float16)[None]
+    assert np.array_equal(xb.astype(np.float64), (vals * 2.0 ** -3)[None])
+    c2, s2 = oracle.mx_quant(xb)
+    assert s2[0, 0] == 127 - 3
+    assert np.array_equal(oracle.mx_dequant(c2, s2), xb.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", [synth.FMT_MXFP4, synth.FMT_Q4_MIN])
+def test_linear_x64_vs_numpy(fmt):
+    """W x with double activations agrees with numpy's fp64 matmul of the dequantised matrix."""
+    W = _small_matrix(fmt)
+    codes, scales = oracle.mx_quant(synth.activations(8, 5, W.cols))
+    xh = oracle.mx_dequant(codes, scales)
+    y, a = oracle.linear_x64(W, xh)
+    ref = xh @ oracle.dequant(W).T
+    assert np.all(np.abs(y - ref) <= 1e-12 * a + 1e-300)
+    assert np.allclose(a, np.abs(xh[:, None, :] * oracle.dequant(W)[None]).sum(axis=2), rtol=1e-13)
