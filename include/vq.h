@@ -170,6 +170,32 @@ int vq_verify_linear(const vq_tiled* W, const void* x_f16, int32_t K, void* y, i
 int vq_verify_linear_noalloc(const vq_tiled* W, const void* x_f16, int32_t K, void* y,
                              int32_t y_dtype, void* stream);
 
+/*
+ * vq_verify_linear_mx -- y ~= W x for MXFP4 weights on CDNA4's scaled matrix instruction,
+ * an APPROXIMATION offered beside vq_verify_linear (which is exact).
+ *
+ * The activations are first converted to the 8-bit MX format E4M3 with one E8M0 scale per
+ * 32 values (OCP Microscaling Formats v1.0: shared exponent floor(log2 max|x|) - 8, each
+ * value to nearest E4M3, ties to even, saturating at 448); the E2M1 weight codes and their
+ * E8M0 scales go into v_mfma_scale_f32_16x16x128_f8f6f4 as they are, with fp32 sums.  This
+ * is the K = 16 MXFP4 window's case for the CDNA4 MXFP4 instructions (Hacker News thread
+ * 49596054 names MXFP4-native checkpoints); the result is W applied to the E4M3-rounded
+ * activations, not to x.
+ *
+ *   W     : host descriptor of PLAIN device planes (vq_matrix), format VQ_FMT_MXFP4,
+ *           cols a positive multiple of 128
+ *   x_f16 : device fp16 [K][cols], K 1..16
+ *   y     : device f32 [K][rows]
+ *   ws    : device workspace >= vq_workspace_bytes(VQ_OP_LINEAR_MX, W, K), 256-byte aligned:
+ *           the converted activations and per-split partial sums
+ * Summation orders depend only on the shapes and the compute-unit count.
+ * Errors: VQ_ERR_ARG for NULL pointers, K outside 1..16, a format other than MXFP4, cols not
+ * a positive multiple of 128, misaligned pointers; VQ_ERR_WORKSPACE; VQ_ERR_HIP.  rows == 0
+ * is valid and enqueues nothing.
+ */
+int vq_verify_linear_mx(const vq_matrix* W, const void* x_f16, int32_t K, float* y, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- acceptance */
 #define VQ_MODE_GREEDY 0      /* accept x_i while it equals the target argmax            */
 #define VQ_MODE_SAMPLE 1      /* accept x_i with prob. min(1, p(x_i)/q(x_i)), else resample */
@@ -321,6 +347,7 @@ int vq_decode_stage_ptr(const vq_model* M, int32_t K, void* ws, int32_t stage,
 #define VQ_OP_LINEAR 0         /* desc = const vq_tiled*        */
 #define VQ_OP_ACCEPT 1         /* desc = const vq_accept_desc*  */
 #define VQ_OP_DECODE 2         /* desc = const vq_model*        */
+#define VQ_OP_LINEAR_MX 3      /* desc = const vq_matrix* (plain MXFP4 planes) */
 
 /* Workspace bytes needed by an op for the given descriptor and K (0 on bad input). */
 size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K);

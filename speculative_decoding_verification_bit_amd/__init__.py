@@ -31,7 +31,7 @@ LAUNCH_AUTO, LAUNCH_STAGED, LAUNCH_PERSISTENT = 0, 4, 8
 ROWS_PLAIN, ROWS_PAIR8 = 0, 1
 MODE_GREEDY, MODE_SAMPLE = 0, 1
 DRAFT_GIVEN, DRAFT_Q_ARGMAX, DRAFT_Q_SAMPLE, DRAFT_AGREE = 0, 1, 2, 3
-OP_LINEAR, OP_ACCEPT, OP_DECODE = 0, 1, 2
+OP_LINEAR, OP_ACCEPT, OP_DECODE, OP_LINEAR_MX = 0, 1, 2, 3
 MAX_K = 16
 
 _P = ctypes.c_void_p
@@ -66,7 +66,8 @@ class VqAcceptDesc(ctypes.Structure):
                 ("n_accepted", _P), ("tokens", _P), ("status", _P)]
 
 
-EXPORTS = ("vq_tiled_bytes", "vq_tile", "vq_verify_linear", "vq_verify_linear_noalloc", "vq_verify_accept", "vq_decode_pass", "vq_decode_pass_timed",
+EXPORTS = ("vq_tiled_bytes", "vq_tile", "vq_verify_linear", "vq_verify_linear_noalloc", "vq_verify_linear_mx",
+           "vq_verify_accept", "vq_decode_pass", "vq_decode_pass_timed",
            "vq_decode_stage_ptr", "vq_decode_error_word",
            "vq_workspace_bytes", "vq_status_string", "vq_last_error", "vq_abi_version")
 
@@ -85,6 +86,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.vq_verify_linear.argtypes = [ctypes.POINTER(VqTiled), _P, I32, _P, I32, _P, SZ, _P]
     L.vq_verify_linear_noalloc.restype = I32
     L.vq_verify_linear_noalloc.argtypes = [ctypes.POINTER(VqTiled), _P, I32, _P, I32, _P]
+    L.vq_verify_linear_mx.restype = I32
+    L.vq_verify_linear_mx.argtypes = [ctypes.POINTER(VqMatrix), _P, I32, _P, _P, SZ, _P]
     L.vq_verify_accept.restype = I32
     L.vq_verify_accept.argtypes = [ctypes.POINTER(VqAcceptDesc), _P, SZ, _P]
     L.vq_decode_pass.restype = I32
@@ -232,6 +235,20 @@ def verify_linear_noalloc(W, x, y=None, y_dtype: int = DTYPE_F32, stream=None):
                         device=x.device)
     _check(lib.vq_verify_linear_noalloc(ctypes.byref(W.desc), _ptr(x), K, _ptr(y), y_dtype, _stream(stream)),
            "vq_verify_linear_noalloc")
+    return y
+
+
+def verify_linear_mx(W, x, y=None, ws=None, stream=None):
+    """y ~= W x on the scaled MXFP4 matrix instruction with E4M3 activations (an
+    approximation; W: DeviceMatrix with its plain MXFP4 planes)."""
+    import torch
+    K = x.shape[0]
+    if y is None:
+        y = torch.empty((K, W.rows), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = _empty(workspace_bytes(OP_LINEAR_MX, W.desc, K), x.device)
+    _check(lib.vq_verify_linear_mx(ctypes.byref(W.desc), _ptr(x), K, _ptr(y), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "vq_verify_linear_mx")
     return y
 
 

@@ -448,6 +448,11 @@ size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K) {
         if (linear_layout(W, K, flow_grid(), &L)) return 0;
         return L.total;
     }
+    if (op == VQ_OP_LINEAR_MX) {
+        const vq_matrix* W = (const vq_matrix*)desc;
+        if (check_matrix(W, "W") || W->format != VQ_FMT_MXFP4 || W->cols % 128) return 0;
+        return mx_workspace_bytes(W->rows, W->cols, K, flow_grid());
+    }
     if (op == VQ_OP_ACCEPT) {
         const vq_accept_desc* d = (const vq_accept_desc*)desc;
         if (d->W < 0 || d->K < 1 || d->K > VQ_MAX_K) return 0;
@@ -654,6 +659,26 @@ int vq_verify_linear_noalloc(const vq_tiled* W, const void* x_f16, int32_t K, vo
     uint8_t* const parts = D.ptr + NA_TABLE_BYTES;
     unsigned* const cnt = (unsigned*)(parts + NA_PARTS_BYTES);
     return linear_launch(W, x_f16, K, y, y_dtype, L, (float*)parts, cnt, tab, tab, st);
+}
+
+int vq_verify_linear_mx(const vq_matrix* W, const void* x_f16, int32_t K, float* y, void* ws, size_t ws_bytes,
+                        void* stream) {
+    g_err[0] = 0;
+    int rc = check_matrix(W, "W");
+    if (rc) return rc;
+    if (W->format != VQ_FMT_MXFP4) return fail(VQ_ERR_ARG, "vq_verify_linear_mx takes MXFP4 weights");
+    if (W->cols % 128) return fail(VQ_ERR_ARG, "vq_verify_linear_mx needs cols a multiple of 128, got %d", W->cols);
+    if (K < 1 || K > VQ_MAX_K) return fail(VQ_ERR_ARG, "K %d outside 1..%d", K, VQ_MAX_K);
+    if (W->rows == 0) return VQ_OK;
+    if (!x_f16 || !y) return fail(VQ_ERR_ARG, "NULL x or y");
+    if (!aligned(x_f16, 16) || !aligned(y, 4)) return fail(VQ_ERR_ARG, "x must be 16-byte and y 4-byte aligned");
+    const int nwg = flow_grid();
+    const size_t need = mx_workspace_bytes(W->rows, W->cols, K, nwg);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+        return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
+    hipError_t e = launch_mx_linear(*W, x_f16, K, y, (uint8_t*)ws, nwg, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "mx linear launch");
+    return VQ_OK;
 }
 
 int vq_verify_accept(const vq_accept_desc* d, void* ws, size_t ws_bytes, void* stream) {

@@ -144,6 +144,11 @@ hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
 hipError_t launch_flow(const FlowArgs& A, hipStream_t st);
 int flow_grid();                 // workgroups of a launch: one per compute unit
 
+// The scaled MXFP4 path (E4M3 activations): y [K][rows] ~= W x for plain MXFP4 planes.
+void mx_plan(int rows, int cols, int nwg, int* T, int* C, int* S, int* cps);
+size_t mx_workspace_bytes(int rows, int cols, int K, int nwg);
+hipError_t launch_mx_linear(const vq_matrix& W, const void* x, int K, float* y, uint8_t* ws, int nwg, hipStream_t st);
+
 // Acceptance.
 size_t accept_ws_bytes(const vq_accept_desc* d);
 hipError_t launch_accept(const vq_accept_desc* d, void* ws, hipStream_t st);
