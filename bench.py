@@ -417,9 +417,49 @@ def main():
                         "passes_per_s": round(pps, 2),
                         "frac_of_hbm_peak": round(mbytes / ms16 / 1e6 / HBM_PEAK_GBPS, 4),
                         "implied_tok_s": {f"alpha_{a}": round(pps * tau(a, 15), 2) for a in ALPHAS}}
-        log("K=16", sweep["K16"])
         del mx, ws16
         torch.cuda.empty_cache()
+        # the scaled MXFP4 instruction (E4M3 activations, an approximation) against the exact
+        # f16 path, matrix by matrix: each distinct shape of the stack timed once through
+        # vq_verify_linear_mx and vq_verify_linear, summed over the 449 matrices of a pass
+        def t_event(f, n):
+            for _ in range(2):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+        per_shape, t_mx, t_ex = {}, 0.0, 0.0
+        counts = {synth.MAT_Q: 64, synth.MAT_K: 128, synth.MAT_O: 64, synth.MAT_GATE: 128, synth.MAT_DOWN: 64,
+                  synth.MAT_LM_HEAD: 1}
+        for mid, cnt in counts.items():
+            r, c = shape.mat_shape(mid)
+            mat = vq.DeviceMatrix.from_host(synth.weight_matrix(synth.FMT_MXFP4, 0, 0, mid, r, c, threads=args.threads))
+            xk = torch.from_numpy(synth.activations(0, 16, c)).to(dev)
+            yk = torch.empty((16, r), dtype=torch.float32, device=dev)
+            wsm = torch.empty(vq.workspace_bytes(vq.OP_LINEAR_MX, mat.desc, 16), dtype=torch.uint8, device=dev)
+            a = t_event(lambda: vq.verify_linear_mx(mat, xk, y=yk, ws=wsm), 10)
+            til = mat.tiled
+            wse = torch.empty(vq.workspace_bytes(vq.OP_LINEAR, til.desc, 16), dtype=torch.uint8, device=dev)
+            b = t_event(lambda: vq.verify_linear(til, xk, y=yk, ws=wse), 10)
+            per_shape[f"{r}x{c}"] = {"scaled_us": round(a * 1e3, 1), "exact_us": round(b * 1e3, 1),
+                                     "scaled_gbps": round(mat.nbytes / a / 1e6, 1),
+                                     "exact_gbps": round(mat.nbytes / b / 1e6, 1)}
+            t_mx += cnt * a
+            t_ex += cnt * b
+            del mat, til, wsm, wse, xk, yk
+            torch.cuda.empty_cache()
+        sweep["K16"]["matrix_by_matrix"] = {
+            "note": "449 separate linear launches per pass, no stage glue; the scaled path rounds the "
+                    "activations to E4M3 with E8M0 block scales (an approximation)",
+            "scaled_mxfp4_mfma_ms": round(t_mx, 3), "exact_f16_mfma_ms": round(t_ex, 3),
+            "scaled_gbps": round(mbytes / t_mx / 1e6, 1), "exact_gbps": round(mbytes / t_ex / 1e6, 1),
+            "per_shape": per_shape}
+        log("K=16", sweep["K16"])
     out["sweep"] = sweep
 
     if not args.no_cpu:

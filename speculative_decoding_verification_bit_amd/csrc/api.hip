@@ -451,7 +451,7 @@ size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K) {
     if (op == VQ_OP_LINEAR_MX) {
         const vq_matrix* W = (const vq_matrix*)desc;
         if (check_matrix(W, "W") || W->format != VQ_FMT_MXFP4 || W->cols % 128) return 0;
-        return mx_workspace_bytes(W->rows, W->cols, K, flow_grid());
+        return mx_workspace_bytes(W->rows, W->cols, K, MX_WG_PER_CU * flow_grid());
     }
     if (op == VQ_OP_ACCEPT) {
         const vq_accept_desc* d = (const vq_accept_desc*)desc;
@@ -672,7 +672,7 @@ int vq_verify_linear_mx(const vq_matrix* W, const void* x_f16, int32_t K, float*
     if (W->rows == 0) return VQ_OK;
     if (!x_f16 || !y) return fail(VQ_ERR_ARG, "NULL x or y");
     if (!aligned(x_f16, 16) || !aligned(y, 4)) return fail(VQ_ERR_ARG, "x must be 16-byte and y 4-byte aligned");
-    const int nwg = flow_grid();
+    const int nwg = MX_WG_PER_CU * flow_grid();
     const size_t need = mx_workspace_bytes(W->rows, W->cols, K, nwg);
     if (!ws || ws_bytes < need || !aligned(ws, 256))
         return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);

@@ -145,6 +145,7 @@ hipError_t launch_flow(const FlowArgs& A, hipStream_t st);
 int flow_grid();                 // workgroups of a launch: one per compute unit
 
 // The scaled MXFP4 path (E4M3 activations): y [K][rows] ~= W x for plain MXFP4 planes.
+constexpr int MX_WG_PER_CU = 1;         // workgroups (of 4 waves) per compute unit
 void mx_plan(int rows, int cols, int nwg, int* T, int* C, int* S, int* cps);
 size_t mx_workspace_bytes(int rows, int cols, int K, int nwg);
 hipError_t launch_mx_linear(const vq_matrix& W, const void* x, int K, float* y, uint8_t* ws, int nwg, hipStream_t st);
