@@ -56,6 +56,8 @@ def lib():
         L.or_e8m0.restype = D
         L.or_e8m0.argtypes = [ctypes.c_uint8]
         L.or_dequant.argtypes = [I32, P, P, P, I64, I64, P]
+        L.or_attention.restype = I32
+        L.or_attention.argtypes = [I32, P, P, I32, P, P, I64, I64, I64, P, I64, I64, P, P]
         L.or_linear_x64.restype = I32
         L.or_linear_x64.argtypes = [I32, P, P, P, I64, I64, P, I32, P, P, I32]
         L.or_e4m3.restype = D
@@ -147,6 +149,39 @@ def linear_x64(m, x: np.ndarray, threads: int = 1):
     if rc:
         raise RuntimeError(f"or_linear_x64 failed ({rc})")
     return y, a
+
+
+KV_Q8_0, KV_Q4_0 = 0, 1
+
+
+def attention(kfmt, kcodes, kscales, vfmt, vcodes, vscales, q: np.ndarray, threads: int = 1):
+    """The window's attention over a quantised KV cache (double).  kcodes/vcodes: uint8
+    [Hkv][L][D] (q8_0, int8 bit patterns) or [Hkv][L][D/2] (q4_0); scales fp16
+    [Hkv][L][D/32]; q fp16 [K][Hq][D].  Returns out [K][Hq][D] and a = sum_j p_j |v_j|."""
+    q = np.ascontiguousarray(q, dtype=np.float16)
+    K, Hq, D = q.shape
+    Hkv, L = kscales.shape[0], kscales.shape[1]
+    out = np.empty((K, Hq, D), np.float64)
+    a = np.empty((K, Hq, D), np.float64)
+    kc, vc = np.ascontiguousarray(kcodes), np.ascontiguousarray(vcodes)
+    ks = np.ascontiguousarray(kscales).view(np.uint16)
+    vs = np.ascontiguousarray(vscales).view(np.uint16)
+    rc = lib().or_attention(kfmt, _p(kc), _p(ks), vfmt, _p(vc), _p(vs), Hkv, L, D, _p(q.view(np.uint16)), K, Hq,
+                            _p(out), _p(a))
+    if rc:
+        raise RuntimeError(f"or_attention failed ({rc})")
+    return out, a
+
+
+def kv_dequant(fmt, codes, scales) -> np.ndarray:
+    """Cache values [Hkv][L][D] in double (q8_0: d * int8; q4_0: d * (n - 8), low nibble first)."""
+    sc = np.repeat(np.ascontiguousarray(scales).astype(np.float64), 32, axis=-1)
+    if fmt == KV_Q8_0:
+        return sc * codes.view(np.int8).astype(np.float64)
+    lo = (codes & 15).astype(np.int64) - 8
+    hi = (codes >> 4).astype(np.int64) - 8
+    v = np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (codes.shape[-1] * 2,))
+    return sc * v
 
 
 def e4m3(code: int) -> float:

@@ -263,6 +263,68 @@ int or_mx_quant(const uint16_t* x, int64_t K, int64_t cols, uint8_t* codes, uint
     return 0;
 }
 
+/* ----------------------------------------------------- attention over a KV cache */
+
+/* The window's attention in one layer, over a block-quantised KV cache ("Decode is
+ * memory-bound ...", section "The ceiling": at long context the cache joins the weights
+ * on every pass; "100 tokens per second ...", section "The wall": the measured
+ * configuration keeps the target's cache at q8_0 / q4_0).
+ *
+ * Cache formats, blocks of 32 along the head dimension, one fp16 scale d per block:
+ *   q8_0: an int8 code c per value, value = d * c
+ *   q4_0: a 4-bit code n per value (low nibble = even index), value = d * (n - 8)
+ * Layout: codes [Hkv][L][D] (q8_0: bytes; q4_0: D/2 bytes per row), scales [Hkv][L][D/32].
+ *
+ * Queries q fp16 [K][Hq][D]; query head h reads kv head h / (Hq / Hkv).  The window's own
+ * K positions are the last K of the cache; query i sees positions 0 .. L - K + i.
+ *   s_j = (q . k_j) / sqrt(D),  p_j = exp(s_j - max s) / sum exp(s - max s),  o = sum p_j v_j
+ * in double, with a[k][h][d] = sum_j p_j |v_j[d]| as the tolerance base. */
+static double kv_value(int fmt, const uint8_t* codes, const uint16_t* scales, int64_t D, int64_t row, int64_t d) {
+    double sc = or_half(scales[row * (D / 32) + d / 32]);
+    if (fmt == 0) return sc * (double)(int8_t)codes[row * D + d];
+    uint8_t b = codes[row * (D / 2) + d / 2];
+    int n = (d & 1) ? (b >> 4) : (b & 15);
+    return sc * (double)(n - 8);
+}
+
+int or_attention(int kfmt, const uint8_t* kc, const uint16_t* ks, int vfmt, const uint8_t* vc, const uint16_t* vs,
+                 int64_t Hkv, int64_t L, int64_t D, const uint16_t* q, int64_t K, int64_t Hq,
+                 double* out, double* a) {
+    if (D % 32 || Hkv < 1 || Hq % Hkv || K < 1 || K > L) return -1;
+    double* sc = (double*)malloc(sizeof(double) * (size_t)L);
+    if (!sc) return -2;
+    const double inv = 1.0 / sqrt((double)D);
+    for (int64_t i = 0; i < K; ++i) {
+        const int64_t n = L - K + i + 1;               /* visible positions */
+        for (int64_t h = 0; h < Hq; ++h) {
+            const int64_t g = h / (Hq / Hkv);
+            const uint16_t* qh = q + (i * Hq + h) * D;
+            double mx = -INFINITY;
+            for (int64_t j = 0; j < n; ++j) {
+                double t = 0.0;
+                for (int64_t d = 0; d < D; ++d) t += or_half(qh[d]) * kv_value(kfmt, kc, ks, D, g * L + j, d);
+                sc[j] = t * inv;
+                if (sc[j] > mx) mx = sc[j];
+            }
+            double Z = 0.0;
+            for (int64_t j = 0; j < n; ++j) Z += exp(sc[j] - mx);
+            for (int64_t d = 0; d < D; ++d) {
+                double o = 0.0, ab = 0.0;
+                for (int64_t j = 0; j < n; ++j) {
+                    double pj = exp(sc[j] - mx) / Z;
+                    double v = kv_value(vfmt, vc, vs, D, g * L + j, d);
+                    o += pj * v;
+                    ab += pj * fabs(v);
+                }
+                out[(i * Hq + h) * D + d] = o;
+                a[(i * Hq + h) * D + d] = ab;
+            }
+        }
+    }
+    free(sc);
+    return 0;
+}
+
 /* ------------------------------------------------------------------ stage glue */
 
 /* rho: out[k][j] = v[k][j] / sqrt(mean_j v[k][j]^2), per activation column k. */

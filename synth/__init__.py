@@ -162,6 +162,49 @@ def activations(seed: int, K: int, cols: int, tag: int = 0) -> np.ndarray:
     return rng.standard_normal((K, cols), dtype=np.float32).astype(np.float16)
 
 
+_TAG_KV = 4
+KV_Q8_0, KV_Q4_0 = 0, 1
+
+
+def kv_cache(fmt: int, seed: int, layer: int, which: int, n_kv_heads: int, length: int, head_dim: int = 128,
+             threads: int = 1):
+    """One layer's key (which = 0) or value (which = 1) cache: codes and fp16 block scales
+    (blocks of 32 along the head dimension), generated in chunks of 1024 positions.
+    q8_0: int8 codes uniform in -127..127, scales ~U(0.01, 0.03);
+    q4_0: nibble bytes uniform over 0..255, scales ~U(0.1, 0.3).
+    Returns codes uint8 [Hkv][L][D] (q8_0, int8 bit patterns) or [Hkv][L][D/2] (q4_0) and
+    scales float16 [Hkv][L][D/32]."""
+    cb = head_dim if fmt == KV_Q8_0 else head_dim // 2
+    codes = np.empty((n_kv_heads, length, cb), np.uint8)
+    scales = np.empty((n_kv_heads, length, head_dim // 32), np.float16)
+    jobs = [(g, c0) for g in range(n_kv_heads) for c0 in range(0, length, 1024)]
+
+    def work(job):
+        g, c0 = job
+        n = min(1024, length - c0)
+        rng = _rng(seed, _TAG_KV, layer, which, fmt, g, c0)
+        if fmt == KV_Q8_0:
+            codes[g, c0:c0 + n] = rng.integers(-127, 128, size=(n, cb)).astype(np.int8).view(np.uint8)
+            scales[g, c0:c0 + n] = rng.uniform(0.01, 0.03, size=(n, head_dim // 32)).astype(np.float16)
+        else:
+            codes[g, c0:c0 + n] = rng.integers(0, 256, size=(n, cb), dtype=np.uint8)
+            scales[g, c0:c0 + n] = rng.uniform(0.1, 0.3, size=(n, head_dim // 32)).astype(np.float16)
+
+    if threads > 1 and len(jobs) > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(work, jobs))
+    else:
+        for j in jobs:
+            work(j)
+    return codes, scales
+
+
+def queries(seed: int, K: int, n_q_heads: int, head_dim: int = 128) -> np.ndarray:
+    """K query rows per head ~N(0,1), fp16: [K][Hq][D]."""
+    rng = _rng(seed, _TAG_KV, 1 << 20, K, n_q_heads, head_dim)
+    return rng.standard_normal((K, n_q_heads, head_dim), dtype=np.float32).astype(np.float16)
+
+
 @dataclasses.dataclass(frozen=True)
 class LogitSpec:
     seed: int
@@ -214,3 +257,7 @@ C4 = dict(name="27b-q4min-K8-sample", seed=0, shape=SHAPE_27B, fmt=FMT_Q4_MIN, K
           logits=LogitSpec(seed=1, K=8, vocab=151936, target_sigma=3.0, noise_sigma=1.0),
           windows=1000, T=0.6, top_p=0.95, min_p=0.05, philox_seed=1)
 C5 = dict(name="27b-mxfp4-K16", seed=0, shape=SHAPE_27B, fmt=FMT_MXFP4, K=16)
+# The window's attention in one layer of the 27B-class stack over a 32K-position cache with
+# keys at q8_0 and values at q4_0 (40 query heads, 8 kv heads, head dimension 128).
+ATTN = dict(name="27b-attn-32k-k8v4", seed=0, n_q_heads=40, n_kv_heads=8, head_dim=128, length=32768,
+            kfmt=KV_Q8_0, vfmt=KV_Q4_0)

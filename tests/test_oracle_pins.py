@@ -707,3 +707,80 @@ def test_linear_x64_vs_numpy(fmt):
     ref = xh @ oracle.dequant(W).T
     assert np.all(np.abs(y - ref) <= 1e-12 * a + 1e-300)
     assert np.allclose(a, np.abs(xh[:, None, :] * oracle.dequant(W)[None]).sum(axis=2), rtol=1e-13)
+
+
+# ------------------------------------------------------ attention over a KV cache
+
+def _kv(kf, vf, Hkv=2, L=200, D=64, seed=3):
+    kc, ks = synth.kv_cache(kf, seed, 0, 0, Hkv, L, D)
+    vc, vs = synth.kv_cache(vf, seed, 0, 1, Hkv, L, D)
+    return kc, ks, vc, vs
+
+
+def _dequant_by_hand(fmt, codes, scales):
+    D = scales.shape[-1] * 32
+    out = np.empty(scales.shape[:-1] + (D,))
+    for idx in np.ndindex(scales.shape[:-1]):
+        for d in range(D):
+            sc = float(scales[idx + (d // 32,)])
+            if fmt == synth.KV_Q8_0:
+                c = int(np.int8(codes[idx + (d,)].view(np.int8)))
+            else:
+                b = int(codes[idx + (d // 2,)])
+                c = ((b >> 4) if d & 1 else (b & 15)) - 8
+            out[idx + (d,)] = sc * c
+    return out
+
+
+@pytest.mark.parametrize("kf,vf", [(synth.KV_Q8_0, synth.KV_Q4_0), (synth.KV_Q4_0, synth.KV_Q8_0)])
+def test_attention_vs_scipy_softmax(kf, vf):
+    """Causal GQA attention over the dequantised cache, against scipy's softmax and numpy
+    matmuls (library routines): 4 query rows, 6 query heads on 2 kv heads."""
+    kc, ks, vc, vs = _kv(kf, vf, Hkv=2, L=70, D=64)
+    q = synth.queries(1, 4, 6, 64)
+    out, a = oracle.attention(kf, kc, ks, vf, vc, vs, q)
+    Kd, Vd = _dequant_by_hand(kf, kc, ks), _dequant_by_hand(vf, vc, vs)
+    assert np.array_equal(Kd, oracle.kv_dequant(kf, kc, ks)) and np.array_equal(Vd, oracle.kv_dequant(vf, vc, vs))
+    for i in range(4):
+        for h in range(6):
+            g = h // 3
+            n = 70 - 4 + i + 1
+            s = Kd[g, :n] @ q[i, h].astype(np.float64) / np.sqrt(64)
+            p = scipy.special.softmax(s)
+            ref = p @ Vd[g, :n]
+            assert np.allclose(out[i, h], ref, rtol=1e-12, atol=1e-14)
+            assert np.allclose(a[i, h], p @ np.abs(Vd[g, :n]), rtol=1e-12)
+
+
+def test_attention_uniform_keys_average_values_and_causality():
+    """Equal keys give equal weights: the output is the mean of the visible values.  A
+    query's output does not depend on the positions after its own."""
+    kc, ks, vc, vs = _kv(synth.KV_Q8_0, synth.KV_Q4_0, Hkv=1, L=50, D=32)
+    kc[:] = kc[0, 0]
+    ks[:] = ks[0, 0]
+    q = synth.queries(2, 3, 2, 32)
+    out, _ = oracle.attention(synth.KV_Q8_0, kc, ks, synth.KV_Q4_0, vc, vs, q)
+    Vd = oracle.kv_dequant(synth.KV_Q4_0, vc, vs)
+    for i in range(3):
+        assert np.allclose(out[i, 0], Vd[0, :50 - 3 + i + 1].mean(axis=0), rtol=1e-12, atol=1e-15)
+    kc2, vc2 = _kv(synth.KV_Q8_0, synth.KV_Q4_0, Hkv=1, L=50, D=32, seed=9)[0], vc.copy()
+    kc3 = kc.copy()
+    kc3[0, 48:] = kc2[0, 48:]            # change positions 48, 49: visible only to queries 1 and 2
+    vc2[0, 48:] = vc2[0, 48:] ^ 0x11
+    out3, _ = oracle.attention(synth.KV_Q8_0, kc3, ks, synth.KV_Q4_0, vc2, vs, q)
+    assert np.array_equal(out3[0], out[0])
+    assert not np.allclose(out3[2], out[2])
+
+
+def test_attention_dominant_key_and_shared_group():
+    """One key far above the rest takes all the weight; query heads of one group with the
+    same query read the same kv head and give the same output."""
+    kc, ks, vc, vs = _kv(synth.KV_Q8_0, synth.KV_Q8_0, Hkv=2, L=40, D=32)
+    q = np.zeros((1, 4, 32), np.float16)
+    q[0, :, :] = 1.0
+    kc[:, 17] = np.int8(127).view(np.uint8)
+    ks[:, 17] = 1.0                      # key 17 scores 127 * 32 / sqrt(32), the others < 3
+    out, _ = oracle.attention(synth.KV_Q8_0, kc, ks, synth.KV_Q8_0, vc, vs, q)
+    Vd = oracle.kv_dequant(synth.KV_Q8_0, vc, vs)
+    assert np.allclose(out[0, 0], Vd[0, 17], rtol=1e-12) and np.allclose(out[0, 3], Vd[1, 17], rtol=1e-12)
+    assert np.array_equal(out[0, 0], out[0, 1])
