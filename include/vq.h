@@ -196,6 +196,52 @@ int vq_verify_linear_noalloc(const vq_tiled* W, const void* x_f16, int32_t K, vo
 int vq_verify_linear_mx(const vq_matrix* W, const void* x_f16, int32_t K, float* y, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------ attention over the cache */
+/* KV-cache formats: blocks of 32 along the head dimension, one fp16 scale d per block.
+ *   VQ_KV_Q8_0 : int8 code c, value d * c;          codes [L][D] per kv head
+ *   VQ_KV_Q4_0 : nibble n (low nibble first), value d * (n - 8); codes [L][D/2] per kv head
+ * The pages name q8_0 (keys) and q4_0 (values) as the target's cache formats without
+ * defining them; this is the block-32 layout the library implements. */
+#define VQ_KV_Q8_0 0
+#define VQ_KV_Q4_0 1
+
+/* One layer's KV cache and the heads that read it (host struct, device planes). */
+typedef struct vq_attention {
+    int32_t k_format, v_format;   /* VQ_KV_*                                             */
+    int32_t n_q_heads;            /* Hq, a multiple of n_kv_heads                        */
+    int32_t n_kv_heads;           /* Hkv; query head h reads kv head h / (Hq / Hkv)      */
+    int32_t head_dim;             /* D, must be 128                                      */
+    int32_t length;               /* L: cached positions, the window's K included       */
+    const void* k_codes;          /* uint8 [Hkv][L][D or D/2], 16-byte aligned           */
+    const void* k_scales;         /* fp16 [Hkv][L][D/32], 16-byte aligned               */
+    const void* v_codes;          /* as k_codes for v_format                             */
+    const void* v_scales;         /* as k_scales                                         */
+} vq_attention;
+
+/*
+ * vq_verify_attention -- the verify window's attention in one layer over a quantised KV
+ * cache.  At long context the cache is read on every pass beside the weights ("Decode is
+ * memory-bound ...", section "The ceiling"); the target's cache is kept at q8_0 keys and
+ * q4_0 values ("100 tokens per second from a 27B model ...", section "The wall").  The K
+ * window tokens are the cache's last K positions (already appended); window row i attends
+ * causally to positions 0 .. L - K + i:
+ *     s_j = q . k_j / sqrt(D),  p = softmax(s) over the visible j,  out = sum_j p_j v_j
+ * with k_j, v_j the dequantised cache rows of the query head's kv head.
+ *   q_f16 : device fp16 [K][Hq][D], 2-byte aligned
+ *   K     : 1..16, K <= L, and (Hq / Hkv) * K <= 128
+ *   out   : device f32 [K][Hq][D], 4-byte aligned
+ *   ws    : device workspace >= vq_workspace_bytes(VQ_OP_ATTENTION, desc, K), 256-byte
+ *           aligned: per-span partial results
+ * Dequantisation is exact in fp32; products, the softmax and the sums are fp32 (the
+ * cache is cut into spans of positions, each reduced in position order, then the spans
+ * are combined in order); the summation order depends only on the shapes and the
+ * compute-unit count.
+ * Errors: VQ_ERR_ARG for NULL pointers, unknown formats, head_dim != 128, heads or K out of
+ * range, misaligned pointers; VQ_ERR_WORKSPACE; VQ_ERR_HIP.
+ */
+int vq_verify_attention(const vq_attention* desc, const void* q_f16, int32_t K, float* out, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- acceptance */
 #define VQ_MODE_GREEDY 0      /* accept x_i while it equals the target argmax            */
 #define VQ_MODE_SAMPLE 1      /* accept x_i with prob. min(1, p(x_i)/q(x_i)), else resample */
@@ -348,6 +394,7 @@ int vq_decode_stage_ptr(const vq_model* M, int32_t K, void* ws, int32_t stage,
 #define VQ_OP_ACCEPT 1         /* desc = const vq_accept_desc*  */
 #define VQ_OP_DECODE 2         /* desc = const vq_model*        */
 #define VQ_OP_LINEAR_MX 3      /* desc = const vq_matrix* (plain MXFP4 planes) */
+#define VQ_OP_ATTENTION 4      /* desc = const vq_attention*    */
 
 /* Workspace bytes needed by an op for the given descriptor and K (0 on bad input). */
 size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K);

@@ -31,7 +31,8 @@ LAUNCH_AUTO, LAUNCH_STAGED, LAUNCH_PERSISTENT = 0, 4, 8
 ROWS_PLAIN, ROWS_PAIR8 = 0, 1
 MODE_GREEDY, MODE_SAMPLE = 0, 1
 DRAFT_GIVEN, DRAFT_Q_ARGMAX, DRAFT_Q_SAMPLE, DRAFT_AGREE = 0, 1, 2, 3
-OP_LINEAR, OP_ACCEPT, OP_DECODE, OP_LINEAR_MX = 0, 1, 2, 3
+OP_LINEAR, OP_ACCEPT, OP_DECODE, OP_LINEAR_MX, OP_ATTENTION = 0, 1, 2, 3, 4
+KV_Q8_0, KV_Q4_0 = 0, 1
 MAX_K = 16
 
 _P = ctypes.c_void_p
@@ -56,6 +57,12 @@ class VqModel(ctypes.Structure):
                 ("layers", ctypes.POINTER(VqLayer)), ("lm_head", VqTiled)]
 
 
+class VqAttention(ctypes.Structure):
+    _fields_ = [("k_format", ctypes.c_int32), ("v_format", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("length", ctypes.c_int32),
+                ("k_codes", _P), ("k_scales", _P), ("v_codes", _P), ("v_scales", _P)]
+
+
 class VqAcceptDesc(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("draft_mode", ctypes.c_int32), ("W", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("reserved", ctypes.c_int32),
@@ -67,7 +74,7 @@ class VqAcceptDesc(ctypes.Structure):
 
 
 EXPORTS = ("vq_tiled_bytes", "vq_tile", "vq_verify_linear", "vq_verify_linear_noalloc", "vq_verify_linear_mx",
-           "vq_verify_accept", "vq_decode_pass", "vq_decode_pass_timed",
+           "vq_verify_attention", "vq_verify_accept", "vq_decode_pass", "vq_decode_pass_timed",
            "vq_decode_stage_ptr", "vq_decode_error_word",
            "vq_workspace_bytes", "vq_status_string", "vq_last_error", "vq_abi_version")
 
@@ -88,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.vq_verify_linear_noalloc.argtypes = [ctypes.POINTER(VqTiled), _P, I32, _P, I32, _P]
     L.vq_verify_linear_mx.restype = I32
     L.vq_verify_linear_mx.argtypes = [ctypes.POINTER(VqMatrix), _P, I32, _P, _P, SZ, _P]
+    L.vq_verify_attention.restype = I32
+    L.vq_verify_attention.argtypes = [ctypes.POINTER(VqAttention), _P, I32, _P, _P, SZ, _P]
     L.vq_verify_accept.restype = I32
     L.vq_verify_accept.argtypes = [ctypes.POINTER(VqAcceptDesc), _P, SZ, _P]
     L.vq_decode_pass.restype = I32
@@ -250,6 +259,39 @@ def verify_linear_mx(W, x, y=None, ws=None, stream=None):
     _check(lib.vq_verify_linear_mx(ctypes.byref(W.desc), _ptr(x), K, _ptr(y), _ptr(ws), ws.numel(),
                                    _stream(stream)), "vq_verify_linear_mx")
     return y
+
+
+class DeviceKV:
+    """One layer's quantised KV cache on the device (torch tensors: codes uint8
+    [Hkv][L][D or D/2], scales fp16 [Hkv][L][D/32]) and the query heads that read it."""
+
+    def __init__(self, k_format: int, kcodes, kscales, v_format: int, vcodes, vscales, n_q_heads: int):
+        self.k_codes, self.k_scales, self.v_codes, self.v_scales = kcodes, kscales, vcodes, vscales
+        Hkv, L = kscales.shape[0], kscales.shape[1]
+        self.desc = VqAttention(k_format, v_format, n_q_heads, Hkv, kscales.shape[2] * 32, L,
+                                _ptr(kcodes), _ptr(kscales), _ptr(vcodes), _ptr(vscales))
+
+    @classmethod
+    def from_host(cls, k_format, kcodes, kscales, v_format, vcodes, vscales, n_q_heads, device="cuda"):
+        import torch
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return cls(k_format, t(kcodes), t(kscales), v_format, t(vcodes), t(vscales), n_q_heads)
+
+    def workspace_bytes(self, K: int) -> int:
+        return int(lib.vq_workspace_bytes(OP_ATTENTION, ctypes.byref(self.desc), K))
+
+
+def verify_attention(C: DeviceKV, q, out=None, ws=None, stream=None):
+    """The window's attention over the cache: q fp16 [K][Hq][D] -> out f32 [K][Hq][D]."""
+    import torch
+    K = q.shape[0]
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _empty(C.workspace_bytes(K), q.device)
+    _check(lib.vq_verify_attention(ctypes.byref(C.desc), _ptr(q), K, _ptr(out), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "vq_verify_attention")
+    return out
 
 
 def accept_desc(mode, target, draft=None, draft_tokens=None, draft_mode=DRAFT_GIVEN, T=1.0,

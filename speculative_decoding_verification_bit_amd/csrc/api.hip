@@ -68,6 +68,24 @@ int check_tiled(const vq_tiled* W, const char* name) {
     return VQ_OK;
 }
 
+int check_attention(const vq_attention* C, int32_t K) {
+    if (!C) return fail(VQ_ERR_ARG, "NULL attention descriptor");
+    for (int f : {C->k_format, C->v_format})
+        if (f != VQ_KV_Q8_0 && f != VQ_KV_Q4_0) return fail(VQ_ERR_ARG, "unknown KV format %d", f);
+    if (C->head_dim != 128) return fail(VQ_ERR_ARG, "head_dim must be 128, got %d", C->head_dim);
+    if (C->n_kv_heads < 1 || C->n_kv_heads > 1024) return fail(VQ_ERR_ARG, "n_kv_heads %d outside 1..1024", C->n_kv_heads);
+    if (C->n_q_heads < 1 || C->n_q_heads % C->n_kv_heads)
+        return fail(VQ_ERR_ARG, "n_q_heads %d is not a positive multiple of n_kv_heads %d", C->n_q_heads, C->n_kv_heads);
+    if (C->length < 1 || C->length > (1 << 24)) return fail(VQ_ERR_ARG, "length %d outside 1..2^24", C->length);
+    if (K < 1 || K > VQ_MAX_K || K > C->length) return fail(VQ_ERR_ARG, "K %d outside 1..min(%d, length)", K, VQ_MAX_K);
+    if ((C->n_q_heads / C->n_kv_heads) * K > 128)
+        return fail(VQ_ERR_ARG, "(n_q_heads / n_kv_heads) * K = %d exceeds 128", (C->n_q_heads / C->n_kv_heads) * K);
+    if (!C->k_codes || !C->k_scales || !C->v_codes || !C->v_scales) return fail(VQ_ERR_ARG, "NULL cache plane");
+    if (!aligned(C->k_codes, 16) || !aligned(C->v_codes, 16) || !aligned(C->k_scales, 16) || !aligned(C->v_scales, 16))
+        return fail(VQ_ERR_ARG, "cache codes and scales must be 16-byte aligned");
+    return VQ_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ the split
@@ -453,6 +471,11 @@ size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K) {
         if (check_matrix(W, "W") || W->format != VQ_FMT_MXFP4 || W->cols % 128) return 0;
         return mx_workspace_bytes(W->rows, W->cols, K, MX_WG_PER_CU * flow_grid());
     }
+    if (op == VQ_OP_ATTENTION) {
+        const vq_attention* C = (const vq_attention*)desc;
+        if (check_attention(C, K)) return 0;
+        return attn_workspace_bytes(C->n_kv_heads, C->n_q_heads, C->length, K, flow_grid());
+    }
     if (op == VQ_OP_ACCEPT) {
         const vq_accept_desc* d = (const vq_accept_desc*)desc;
         if (d->W < 0 || d->K < 1 || d->K > VQ_MAX_K) return 0;
@@ -678,6 +701,22 @@ int vq_verify_linear_mx(const vq_matrix* W, const void* x_f16, int32_t K, float*
         return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
     hipError_t e = launch_mx_linear(*W, x_f16, K, y, (uint8_t*)ws, nwg, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "mx linear launch");
+    return VQ_OK;
+}
+
+int vq_verify_attention(const vq_attention* desc, const void* q_f16, int32_t K, float* out, void* ws,
+                        size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    int rc = check_attention(desc, K);
+    if (rc) return rc;
+    if (!q_f16 || !out) return fail(VQ_ERR_ARG, "NULL q or out");
+    if (!aligned(q_f16, 2) || !aligned(out, 4)) return fail(VQ_ERR_ARG, "q must be 2-byte and out 4-byte aligned");
+    const int nwg = flow_grid();
+    const size_t need = attn_workspace_bytes(desc->n_kv_heads, desc->n_q_heads, desc->length, K, nwg);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+        return fail(VQ_ERR_WORKSPACE, "workspace needs %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
+    hipError_t e = launch_attention(*desc, q_f16, K, out, (uint8_t*)ws, nwg, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
     return VQ_OK;
 }
 

@@ -150,6 +150,12 @@ void mx_plan(int rows, int cols, int nwg, int* T, int* C, int* S, int* cps);
 size_t mx_workspace_bytes(int rows, int cols, int K, int nwg);
 hipError_t launch_mx_linear(const vq_matrix& W, const void* x, int K, float* y, uint8_t* ws, int nwg, hipStream_t st);
 
+// Attention over a quantised KV cache: spans of positions per kv head, then their merge.
+void attn_plan(int Hkv, int L, int M, int nwg, int* S, int* span);
+size_t attn_workspace_bytes(int Hkv, int Hq, int L, int K, int nwg);
+hipError_t launch_attention(const vq_attention& C, const void* q, int K, float* out, uint8_t* ws, int nwg,
+                            hipStream_t st);
+
 // Acceptance.
 size_t accept_ws_bytes(const vq_accept_desc* d);
 hipError_t launch_accept(const vq_accept_desc* d, void* ws, hipStream_t st);

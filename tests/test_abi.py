@@ -253,3 +253,48 @@ def test_decode_timed_argument_errors():
     assert vq.lib.vq_decode_pass_timed(ctypes.byref(M), FAKE, 4, FAKE, 0, FAKE, n4, None, None, 0,
                                        ctypes.byref(nl)) == vq.ERR_ARG
     assert nl.value == -1
+
+
+def _att(kf=vq.KV_Q8_0, vf=vq.KV_Q4_0, Hq=40, Hkv=8, D=128, L=1000, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE):
+    return vq.VqAttention(kf, vf, Hq, Hkv, D, L, kc, ks, vc, vs)
+
+
+def _attn(C, K=4, q=FAKE, out=FAKE, ws=FAKE, nbytes=1 << 40):
+    return vq.lib.vq_verify_attention(ctypes.byref(C), q, K, out, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("C,K,kw,code", [
+    (_att(kf=2), 4, {}, vq.ERR_ARG),
+    (_att(vf=-1), 4, {}, vq.ERR_ARG),
+    (_att(D=64), 4, {}, vq.ERR_ARG),
+    (_att(Hkv=0), 4, {}, vq.ERR_ARG),
+    (_att(Hq=12), 4, {}, vq.ERR_ARG),            # not a multiple of Hkv
+    (_att(L=0), 1, {}, vq.ERR_ARG),
+    (_att(L=3), 4, {}, vq.ERR_ARG),              # K > L
+    (_att(), 0, {}, vq.ERR_ARG),
+    (_att(), 17, {}, vq.ERR_ARG),
+    (_att(Hq=72, Hkv=2), 4, {}, vq.ERR_ARG),     # 36 q heads per kv head x 4 rows > 128
+    (_att(kc=None), 4, {}, vq.ERR_ARG),
+    (_att(vs=None), 4, {}, vq.ERR_ARG),
+    (_att(kc=FAKE + 8), 4, {}, vq.ERR_ARG),
+    (_att(ks=FAKE + 8), 4, {}, vq.ERR_ARG),
+    (_att(), 4, dict(q=None), vq.ERR_ARG),
+    (_att(), 4, dict(out=FAKE + 2), vq.ERR_ARG),
+    (_att(), 4, dict(ws=None), vq.ERR_WORKSPACE),
+    (_att(), 4, dict(ws=FAKE + 64), vq.ERR_WORKSPACE),
+    (_att(), 4, dict(nbytes=0), vq.ERR_WORKSPACE),
+])
+def test_attention_argument_errors(C, K, kw, code):
+    assert _attn(C, K, **kw) == code
+    assert vq.lib.vq_last_error()
+
+
+def test_attention_workspace():
+    for Hq, Hkv, L, K in ((40, 8, 32768, 16), (40, 8, 1, 1), (32, 1, 300, 4), (8, 8, 65, 16)):
+        C = _att(Hq=Hq, Hkv=Hkv, L=L)
+        n = vq.lib.vq_workspace_bytes(vq.OP_ATTENTION, ctypes.byref(C), K)
+        # per-span partials: Hq / Hkv * K rows of D + 2 floats per span and kv head
+        spans = -(-L // 64)
+        assert 0 < n <= Hkv * min(spans, 4 * 256) * (Hq // Hkv) * K * (128 + 2) * 4 + 512, (Hq, Hkv, L, K, n)
+        assert _attn(C, K, nbytes=n - 1) == vq.ERR_WORKSPACE
+    assert vq.lib.vq_workspace_bytes(vq.OP_ATTENTION, ctypes.byref(_att(D=96)), 4) == 0
