@@ -28,7 +28,9 @@ namespace {
 constexpr int AT_THREADS = 256;
 constexpr int AT_WAVES = AT_THREADS / 64;
 constexpr int AT_D = 128;            // head dimension
-constexpr int AT_RING = 4;           // tiles per wave in registers (loaded ahead)
+#ifndef AT_WG_PER_CU
+#define AT_WG_PER_CU 1               // workgroups per compute unit in a launch
+#endif
 
 struct AttnArgs {
     const uint8_t* kc;
@@ -62,6 +64,32 @@ __device__ __forceinline__ h8_t widen_q8(u2_t w) {
 // Dimension (0..7 within the lane's eight) held by slot p of the widened operand.
 __device__ __forceinline__ int slot_dim(bool k8, int p) {
     return k8 ? 4 * (p >> 2) + 2 * (p & 1) + ((p >> 1) & 1) : (p >> 1) + 4 * (p & 1);
+}
+
+// fp16 pair (x, y), each rounded toward zero.
+__device__ __forceinline__ uint32_t pk_rtz(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x, y));
+}
+// x - half H of the fp16 pair hb, in one mixed FMA (exact when that half is x rounded
+// toward zero: the residual has at most 13 significant bits).
+template <int H>
+__device__ __forceinline__ float resid(float x, uint32_t hb) {
+    float r;
+    if constexpr (H == 0) asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hb), "v"(x));
+    else asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hb), "v"(x));
+    return r;
+}
+// Eight fp32 values as fp16 hi + lo operands (hi rounded toward zero, lo the rounded
+// residual): hi + lo equals each value to within 2^-22 of it (2^-25 absolute below 2^-3).
+__device__ __forceinline__ void split8(const float (&x)[8], h8_t& hi, h8_t& lo) {
+    u4_t h, l;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        h[k] = pk_rtz(x[2 * k], x[2 * k + 1]);
+        l[k] = pk_rtz(resid<0>(x[2 * k], h[k]), resid<1>(x[2 * k + 1], h[k]));
+    }
+    hi = as_h8(h);
+    lo = as_h8(l);
 }
 
 // RTM: row tiles of this workgroup (at most); K8 / V8: q8_0 keys / values (else q4_0).
@@ -207,8 +235,7 @@ __global__ void __launch_bounds__(AT_THREADS) k_attn_part(AttnArgs A) {
 #pragma unroll
     for (int mt = 0; mt < RTM; ++mt) vlim[mt] = min(w1 - 1, lim[mt]) - 4 * q4;
 
-    auto step = [&](const Tile& T, int pb) __attribute__((always_inline)) {
-        h8_t ka[4];
+    auto widen_keys = [&](const Tile& T, h8_t (&ka)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             if constexpr (K8) {
@@ -221,12 +248,13 @@ __global__ void __launch_bounds__(AT_THREADS) k_attn_part(AttnArgs A) {
                 ka[b] = as_h8(r);
             }
         }
-        // values of position 4 q4 + t, dimensions 8 n16 + 0..7, exact in fp32
-        float vv[4][8];
+    };
+    // values of position 4 q4 + t, dimensions 8 n16 + 0..7, exact in fp32
+    auto values = [&](const Tile& T, float (&vv)[4][8]) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float d = half_bits_to_float(T.vs[t]);
             if constexpr (V8) {
+                const float d = half_bits_to_float(T.vs[t]);
                 const float off = -128.0f * d;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -247,32 +275,58 @@ __global__ void __launch_bounds__(AT_THREADS) k_attn_part(AttnArgs A) {
                 }
             }
         }
-        float dk[4][4];                                      // [position j][block b]
+    };
+    // scores (log2 units, -inf where not visible) of positions pb + 4 q4 + j for the
+    // lane's row of tile mt
+    auto scores = [&](const Tile& T, const h8_t (&ka)[4], int mt, int pb) __attribute__((always_inline)) -> f4_t {
+        f4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const f4_t z = {0.f, 0.f, 0.f, 0.f};
+            const f4_t part = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[b], as_h8(qr[mt][b]), z, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float dk = half_bits_to_float((T.ks[j][b >> 1] >> (16 * (b & 1))) & 0xFFFFu);
+                sc[j] = __builtin_fmaf(dk, part[j], sc[j]);
+            }
+        }
+        const int rel = vlim[mt] - pb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) dk[j][b] = half_bits_to_float((T.ks[j][b >> 1] >> (16 * (b & 1))) & 0xFFFFu);
+            float v = sc[j] * C;
+            asm volatile("" : "+v"(v));                          // computed for every lane, then selected
+            sc[j] = j <= rel ? v : -INFINITY;
         }
+        return sc;
+    };
+
+    // Two tiles (32 positions) per step.  p v on the f16 matrix instruction: slot s of the
+    // lane's 8 k values is position 4 q4 + s of tile a (s < 4) or 4 q4 + s - 4 of tile b,
+    // which is where the lane's values and scores of those positions already are.  Values
+    // and 2^7 p go in as fp16 hi + lo (hi hi + hi lo + lo hi; the lo lo term is below
+    // 2^-22 of the product); 2^7 p <= 2^15 stays in fp16 range, and the factor cancels
+    // between the sums and the outputs.
+    auto step2 = [&](const Tile& Ta, const Tile& Tb, int pb) __attribute__((always_inline)) {
+        h8_t vh[8], vl[8];
+        {
+            float va[4][8], vb[4][8];
+            values(Ta, va);
+            values(Tb, vb);
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const float x[8] = {va[0][dt], va[1][dt], va[2][dt], va[3][dt], vb[0][dt], vb[1][dt], vb[2][dt], vb[3][dt]};
+                split8(x, vh[dt], vl[dt]);
+            }
+        }
+        h8_t ka[4], kb[4];
+        widen_keys(Ta, ka);
+        widen_keys(Tb, kb);
 #pragma unroll
         for (int mt = 0; mt < RTM; ++mt) {
             if (mt < rt) {
-                f4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const f4_t z = {0.f, 0.f, 0.f, 0.f};
-                    const f4_t part = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[b], as_h8(qr[mt][b]), z, 0, 0, 0);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sc[j] = __builtin_fmaf(dk[j][b], part[j], sc[j]);
-                }
-                float mx = -INFINITY;
-                const int rel = vlim[mt] - pb;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float v = sc[j] * C;
-                    asm volatile("" : "+v"(v));                  // computed for every lane, then selected
-                    sc[j] = j <= rel ? v : -INFINITY;
-                    mx = __builtin_fmaxf(mx, sc[j]);
-                }
+                const f4_t sa = scores(Ta, ka, mt, pb), sb = scores(Tb, kb, mt, pb + 16);
+                float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(sa[0], sa[1]), __builtin_fmaxf(sa[2], sa[3])),
+                                           __builtin_fmaxf(__builtin_fmaxf(sb[0], sb[1]), __builtin_fmaxf(sb[2], sb[3])));
                 mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
                 mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
                 // The reference maximum moves only when a row's scores exceed it by more
@@ -286,43 +340,56 @@ __global__ void __launch_bounds__(AT_THREADS) k_attn_part(AttnArgs A) {
                     for (int dt = 0; dt < 8; ++dt) o[mt][dt] *= alpha;
                     m_run[mt] = mn;
                 }
-                const float mu = m_run[mt] == -INFINITY ? 0.f : m_run[mt];   // no visible position yet
-                f4_t pv;
+                // 2^7 p; a row with no visible position yet has every score -inf (p = 0)
+                const float mu = (m_run[mt] == -INFINITY ? 0.f : m_run[mt]) - 7.0f;
+                float pv[8];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pv[j] = __builtin_amdgcn_exp2f(sc[j] - mu);
-                l_run[mt] += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+                for (int j = 0; j < 4; ++j) {
+                    pv[j] = __builtin_amdgcn_exp2f(sa[j] - mu);
+                    pv[4 + j] = __builtin_amdgcn_exp2f(sb[j] - mu);
+                }
+                l_run[mt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+                h8_t ph, pl;
+                split8(pv, ph, pl);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt)
-                        o[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv[t][dt], pv[t], o[mt][dt], 0, 0, 0);
+                for (int dt = 0; dt < 8; ++dt) {
+                    o[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[dt], ph, o[mt][dt], 0, 0, 0);
+                    o[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[dt], pl, o[mt][dt], 0, 0, 0);
+                    o[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[dt], ph, o[mt][dt], 0, 0, 0);
                 }
             }
         }
     };
 
-    // tiles of the wave's range; only the cache's last tile can run past its end.  A ring
-    // of AT_RING tiles in registers keeps AT_RING - 1 tiles' loads in flight.
+    // tiles of the wave's range in pairs (a pair's second tile may lie past the range: its
+    // positions are masked); only the cache's last pair can run past the cache's end.  A
+    // ring of two pairs in registers keeps the next pair's loads in flight.
     const int nt = (w1 - w0 + 15) / 16;
-    const bool tail = nt > 0 && w0 + 16 * nt > A.L;
-    const int nf = nt - (tail ? 1 : 0);
-    Tile ring[AT_RING];
+    const int np = (nt + 1) / 2;
+    const bool tail = np > 0 && w0 + 32 * np > A.L;
+    const int nf = np - (tail ? 1 : 0);                      // pairs read without clamping
+    Tile ring[4];
+    if (nf > 0) {
+        load_fast(ring[0], w0);
+        load_fast(ring[1], w0 + 16);
+    }
+    for (int q0 = 0; q0 < nf; q0 += 2) {
 #pragma unroll
-    for (int u = 0; u < AT_RING - 1; ++u)
-        if (u < nf) load_fast(ring[u], w0 + 16 * u);
-    for (int t0 = 0; t0 < nf; t0 += AT_RING) {
-#pragma unroll
-        for (int u = 0; u < AT_RING; ++u) {
-            const int t = t0 + u;
-            if (t < nf) {
-                if (t + AT_RING - 1 < nf) load_fast(ring[(u + AT_RING - 1) % AT_RING], w0 + 16 * (t + AT_RING - 1));
-                step(ring[u], w0 + 16 * t);
+        for (int u = 0; u < 2; ++u) {
+            const int q = q0 + u;
+            if (q < nf) {
+                if (q + 1 < nf) {
+                    load_fast(ring[2 * (1 - u)], w0 + 32 * (q + 1));
+                    load_fast(ring[2 * (1 - u) + 1], w0 + 32 * (q + 1) + 16);
+                }
+                step2(ring[2 * u], ring[2 * u + 1], w0 + 32 * q);
             }
         }
     }
     if (tail) {
-        load_tail(ring[0], w0 + 16 * nf);
-        step(ring[0], w0 + 16 * nf);
+        load_tail(ring[0], w0 + 32 * nf);
+        load_tail(ring[1], w0 + 32 * nf + 16);
+        step2(ring[0], ring[1], w0 + 32 * nf);
     }
 
     // merge the 4 waves in wave order: M = max m_w, each wave's l and O times 2^(m_w - M)
@@ -470,11 +537,10 @@ hipError_t launch_part(const AttnArgs& A, int nz, hipStream_t st) {
 }  // namespace
 
 void attn_plan(int Hkv, int L, int M, int nwg, int* S, int* span) {
-    // one round of workgroups: two per compute unit when a workgroup holds one row tile
-    // (the registers allow two waves per SIMD), else one; spans of whole 64-position
-    // quarters (16-position tiles per wave)
+    // one round of workgroups, one per compute unit (a wave's registers fill its SIMD);
+    // spans of whole 64-position quarters (16-position tiles per wave)
     const int rt = (M + 15) / 16, nz = (rt + 3) / 4;
-    const int target = (rt == 1 ? 2 : 1) * nwg;
+    const int target = AT_WG_PER_CU * nwg;
     const int s = std::min(AT_MAX_S, std::max(1, target / std::max(1, Hkv * nz)));
     int sp = (L + s - 1) / s;
     sp = std::max(64, (sp + 63) / 64 * 64);
