@@ -9,7 +9,7 @@
 // reads kv head h / G (G = Hq / Hkv).  The window is the cache's last K positions; window
 // row i sees positions 0 .. L - K + i.
 //
-// k_attn_part: one workgroup of 4 waves per (span of positions, kv head, group of up to 4
+// k_attn_part: one workgroup of 4 waves per (span of positions, kv head, group of up to 3
 // row tiles); each wave takes a quarter of the span in tiles of 16 positions, with the
 // next tiles' loads in flight in registers.  Scores on the f16 matrix instruction over the
 // exactly widened key codes (the key scale applied to each 32-dimension block's fp32
@@ -28,9 +28,9 @@ namespace {
 constexpr int AT_THREADS = 256;
 constexpr int AT_WAVES = AT_THREADS / 64;
 constexpr int AT_D = 128;            // head dimension
-#ifndef AT_WG_PER_CU
-#define AT_WG_PER_CU 1               // workgroups per compute unit in a launch
-#endif
+// Waves per SIMD the registers must allow: two with one row tile (each wave keeps one
+// pair of tiles in flight ahead), one with more (the accumulators take the registers).
+#define AT_WAVES_EU(rtm) ((rtm) == 1 ? 2 : 1)
 
 struct AttnArgs {
     const uint8_t* kc;
@@ -92,7 +92,7 @@ __device__ __forceinline__ void split8(const float (&x)[8], h8_t& hi, h8_t& lo) 
     lo = as_h8(l);
 }
 
-// RTM: row tiles of this workgroup (at most); K8 / V8: q8_0 keys / values (else q4_0).
+// RTM: row tiles of this workgroup (at most, 1..3); K8 / V8: q8_0 keys / values (else q4_0).
 //
 // Wave w of workgroup (s, g) takes positions [w0, w1) (a quarter of the workgroup's span)
 // in tiles of 16, one tile's loads in flight while the previous one is used.  Per tile:
@@ -112,7 +112,8 @@ __device__ __forceinline__ void split8(const float (&x)[8], h8_t& hi, h8_t& lo) 
 // The 4 waves' results are merged in LDS in wave order; the span's partial (m, l, O) of
 // every row goes to memory.
 template <int RTM, bool K8, bool V8>
-__global__ void __launch_bounds__(AT_THREADS) k_attn_part(AttnArgs A) {
+__global__ void __launch_bounds__(AT_THREADS) __attribute__((amdgpu_waves_per_eu(AT_WAVES_EU(RTM), 8)))
+k_attn_part(AttnArgs A) {
     __shared__ u4_t qb[RTM][4][64];                          // scores' B operand per row tile, block
     __shared__ float wm[AT_WAVES][16 * RTM], wl[AT_WAVES][16 * RTM];
     __shared__ __attribute__((aligned(16))) float ob[16 * RTM][AT_D + 4];
@@ -235,55 +236,56 @@ __global__ void __launch_bounds__(AT_THREADS) k_attn_part(AttnArgs A) {
 #pragma unroll
     for (int mt = 0; mt < RTM; ++mt) vlim[mt] = min(w1 - 1, lim[mt]) - 4 * q4;
 
-    auto widen_keys = [&](const Tile& T, h8_t (&ka)[4]) __attribute__((always_inline)) {
+    // A tile's values in a compact exact form: per position t, q4_0 nibbles as fp16 n - 8
+    // in the pairs (c, c + 4) of the lane's 8 dimensions, or q8_0 bytes offset to c + 128;
+    // the scale as fp16.  value(t, dim) is then one (mixed) FMA, exact in fp32.
+    struct Vals {
+        uint32_t w[4][4];
+        uint32_t d[4];
+    };
+    auto vals = [&](const Tile& T, Vals& V) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            V.d[t] = T.vs[t];
+            if constexpr (V8) {
+                V.w[t][0] = T.vc[t][0] ^ 0x80808080u;
+                V.w[t][1] = T.vc[t][1] ^ 0x80808080u;
+            } else {
+                h2_t pp[4];
+                unpack_q4(T.vc[t][0], pp);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) V.w[t][c] = __builtin_bit_cast(uint32_t, pp[c]);
+            }
+        }
+    };
+    auto value = [&](const Vals& V, int t, int dim) __attribute__((always_inline)) -> float {
+        const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)V.d[t]);
+        if constexpr (V8) {
+            const float u = (float)((V.w[t][dim >> 2] >> (8 * (dim & 3))) & 0xFFu);
+            return __builtin_fmaf(u, (float)dh, -128.0f * (float)dh);
+        } else {
+            const h2_t pr = __builtin_bit_cast(h2_t, V.w[t][dim & 3]);
+            return __builtin_fmaf((float)pr[dim >> 2], (float)dh, 0.0f);
+        }
+    };
+    // scores (log2 units, -inf where not visible) of positions pb + 4 q4 + j for the
+    // lane's row of tile mt
+    auto scores = [&](const Tile& T, int mt, int pb) __attribute__((always_inline)) -> f4_t {
+        f4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
+            h8_t ka;
             if constexpr (K8) {
-                ka[b] = widen_q8(T.kc[b]);
+                ka = widen_q8(T.kc[b]);
             } else {
                 h2_t pp[4];
                 unpack_q4(T.kc[b][0], pp);
                 const u4_t r = {__builtin_bit_cast(uint32_t, pp[0]), __builtin_bit_cast(uint32_t, pp[1]),
                                 __builtin_bit_cast(uint32_t, pp[2]), __builtin_bit_cast(uint32_t, pp[3])};
-                ka[b] = as_h8(r);
+                ka = as_h8(r);
             }
-        }
-    };
-    // values of position 4 q4 + t, dimensions 8 n16 + 0..7, exact in fp32
-    auto values = [&](const Tile& T, float (&vv)[4][8]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if constexpr (V8) {
-                const float d = half_bits_to_float(T.vs[t]);
-                const float off = -128.0f * d;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t u = T.vc[t][h] ^ 0x80808080u;
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) vv[t][4 * h + c] = __builtin_fmaf((float)((u >> (8 * c)) & 0xFFu), d, off);
-                }
-            } else {
-                // nibbles widened exactly to fp16 n - 8 (pairs of dimensions (c, c + 4)),
-                // times the fp16 scale in one mixed-precision FMA (the product is exact)
-                h2_t pp[4];
-                unpack_q4(T.vc[t][0], pp);
-                const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)T.vs[t]);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    vv[t][c] = __builtin_fmaf((float)pp[c][0], (float)dh, 0.0f);
-                    vv[t][c + 4] = __builtin_fmaf((float)pp[c][1], (float)dh, 0.0f);
-                }
-            }
-        }
-    };
-    // scores (log2 units, -inf where not visible) of positions pb + 4 q4 + j for the
-    // lane's row of tile mt
-    auto scores = [&](const Tile& T, const h8_t (&ka)[4], int mt, int pb) __attribute__((always_inline)) -> f4_t {
-        f4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
             const f4_t z = {0.f, 0.f, 0.f, 0.f};
-            const f4_t part = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[b], as_h8(qr[mt][b]), z, 0, 0, 0);
+            const f4_t part = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, as_h8(qr[mt][b]), z, 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float dk = half_bits_to_float((T.ks[j][b >> 1] >> (16 * (b & 1))) & 0xFFFFu);
@@ -307,24 +309,26 @@ __global__ void __launch_bounds__(AT_THREADS) k_attn_part(AttnArgs A) {
     // 2^-22 of the product); 2^7 p <= 2^15 stays in fp16 range, and the factor cancels
     // between the sums and the outputs.
     auto step2 = [&](const Tile& Ta, const Tile& Tb, int pb) __attribute__((always_inline)) {
-        h8_t vh[8], vl[8];
-        {
-            float va[4][8], vb[4][8];
-            values(Ta, va);
-            values(Tb, vb);
+        Vals va, vb;
+        vals(Ta, va);
+        vals(Tb, vb);
+        // the values' hi + lo operands of dimension tile dt: made where they are used with
+        // one row tile, once per pair (kept for every row tile) with more
+        auto vsplit = [&](int dt, h8_t& vh, h8_t& vl) __attribute__((always_inline)) {
+            const float x[8] = {value(va, 0, dt), value(va, 1, dt), value(va, 2, dt), value(va, 3, dt),
+                                value(vb, 0, dt), value(vb, 1, dt), value(vb, 2, dt), value(vb, 3, dt)};
+            split8(x, vh, vl);
+        };
+        constexpr int NV = RTM == 1 ? 1 : 8;
+        h8_t vhs[NV], vls[NV];
+        if constexpr (RTM > 1) {
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const float x[8] = {va[0][dt], va[1][dt], va[2][dt], va[3][dt], vb[0][dt], vb[1][dt], vb[2][dt], vb[3][dt]};
-                split8(x, vh[dt], vl[dt]);
-            }
+            for (int dt = 0; dt < 8; ++dt) vsplit(dt, vhs[dt], vls[dt]);
         }
-        h8_t ka[4], kb[4];
-        widen_keys(Ta, ka);
-        widen_keys(Tb, kb);
 #pragma unroll
         for (int mt = 0; mt < RTM; ++mt) {
             if (mt < rt) {
-                const f4_t sa = scores(Ta, ka, mt, pb), sb = scores(Tb, kb, mt, pb + 16);
+                const f4_t sa = scores(Ta, mt, pb), sb = scores(Tb, mt, pb + 16);
                 float mx = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(sa[0], sa[1]), __builtin_fmaxf(sa[2], sa[3])),
                                            __builtin_fmaxf(__builtin_fmaxf(sb[0], sb[1]), __builtin_fmaxf(sb[2], sb[3])));
                 mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
@@ -353,9 +357,16 @@ __global__ void __launch_bounds__(AT_THREADS) k_attn_part(AttnArgs A) {
                 split8(pv, ph, pl);
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt) {
-                    o[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[dt], ph, o[mt][dt], 0, 0, 0);
-                    o[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[dt], pl, o[mt][dt], 0, 0, 0);
-                    o[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[dt], ph, o[mt][dt], 0, 0, 0);
+                    h8_t vh, vl;
+                    if constexpr (RTM == 1) {
+                        vsplit(dt, vh, vl);
+                    } else {
+                        vh = vhs[dt];
+                        vl = vls[dt];
+                    }
+                    o[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, ph, o[mt][dt], 0, 0, 0);
+                    o[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, pl, o[mt][dt], 0, 0, 0);
+                    o[mt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, ph, o[mt][dt], 0, 0, 0);
                 }
             }
         }
@@ -363,24 +374,30 @@ __global__ void __launch_bounds__(AT_THREADS) k_attn_part(AttnArgs A) {
 
     // tiles of the wave's range in pairs (a pair's second tile may lie past the range: its
     // positions are masked); only the cache's last pair can run past the cache's end.  A
-    // ring of two pairs in registers keeps the next pair's loads in flight.
+    // ring of NP pairs in registers keeps the next NP - 1 pairs' loads in flight (as many
+    // as the registers left by the row tiles' accumulators allow).
     const int nt = (w1 - w0 + 15) / 16;
     const int np = (nt + 1) / 2;
     const bool tail = np > 0 && w0 + 32 * np > A.L;
     const int nf = np - (tail ? 1 : 0);                      // pairs read without clamping
-    Tile ring[4];
-    if (nf > 0) {
-        load_fast(ring[0], w0);
-        load_fast(ring[1], w0 + 16);
-    }
-    for (int q0 = 0; q0 < nf; q0 += 2) {
+    constexpr int NP = 2;
+    Tile ring[2 * NP];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NP - 1; ++u) {
+        if (u < nf) {
+            load_fast(ring[2 * u], w0 + 32 * u);
+            load_fast(ring[2 * u + 1], w0 + 32 * u + 16);
+        }
+    }
+    for (int q0 = 0; q0 < nf; q0 += NP) {
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
             const int q = q0 + u;
             if (q < nf) {
-                if (q + 1 < nf) {
-                    load_fast(ring[2 * (1 - u)], w0 + 32 * (q + 1));
-                    load_fast(ring[2 * (1 - u) + 1], w0 + 32 * (q + 1) + 16);
+                const int ahead = q + NP - 1, slot = (u + NP - 1) % NP;
+                if (ahead < nf) {
+                    load_fast(ring[2 * slot], w0 + 32 * ahead);
+                    load_fast(ring[2 * slot + 1], w0 + 32 * ahead + 16);
                 }
                 step2(ring[2 * u], ring[2 * u + 1], w0 + 32 * q);
             }
@@ -537,10 +554,10 @@ hipError_t launch_part(const AttnArgs& A, int nz, hipStream_t st) {
 }  // namespace
 
 void attn_plan(int Hkv, int L, int M, int nwg, int* S, int* span) {
-    // one round of workgroups, one per compute unit (a wave's registers fill its SIMD);
+    // one round of workgroups: as many per compute unit as waves per SIMD fit;
     // spans of whole 64-position quarters (16-position tiles per wave)
-    const int rt = (M + 15) / 16, nz = (rt + 3) / 4;
-    const int target = AT_WG_PER_CU * nwg;
+    const int rt = (M + 15) / 16, nz = (rt + 2) / 3;
+    const int target = AT_WAVES_EU(rt) * nwg;
     const int s = std::min(AT_MAX_S, std::max(1, target / std::max(1, Hkv * nz)));
     int sp = (L + s - 1) / s;
     sp = std::max(64, (sp + 63) / 64 * 64);
@@ -577,15 +594,15 @@ hipError_t launch_attention(const vq_attention& C, const void* q, int K, float* 
     A.part_o = (float*)ws;
     A.part_ml = (float*)(ws + attn_part_o_bytes(A.Hkv, A.S, (size_t)M));
     A.out = out;
-    // row tiles per workgroup: at most 4 (the accumulators of 4 tiles fill the matrix
-    // registers); more rows take several workgroups per span, each reading the span
-    const int rt = (M + 15) / 16, nz = (rt + 3) / 4, per = (rt + nz - 1) / nz;
+    // row tiles per workgroup: at most 3 (their accumulators, the tiles in flight and the
+    // value operands fill the registers); more rows take several workgroups per span,
+    // each reading the span
+    const int rt = (M + 15) / 16, nz = (rt + 2) / 3, per = (rt + nz - 1) / nz;
     hipError_t e;
     if (rt > 8) return hipErrorInvalidValue;
     if (per == 1) e = launch_part<1>(A, nz, st);
     else if (per == 2) e = launch_part<2>(A, nz, st);
-    else if (per == 3) e = launch_part<3>(A, nz, st);
-    else e = launch_part<4>(A, nz, st);
+    else e = launch_part<3>(A, nz, st);
     if (e != hipSuccess) return e;
     k_attn_reduce<<<dim3(M, A.Hkv), AT_THREADS, 0, st>>>(A);
     return hipGetLastError();
