@@ -212,6 +212,39 @@ def cpu_baseline(synth, oracle_mod, budget_s: float):
     }
 
 
+def bench_attention(torch, vq, synth, dev, args):
+    """The window's attention over one layer's q8_0 / q4_0 cache of the 27B model at 32768
+    positions (40 query heads, 8 kv heads, head dim 128), K = 1, 4, 8, 16: time per call
+    (both kernels) on the launch stream, and the cache bytes over that time."""
+    c = synth.ATTN
+    Hkv, Hq, L = c["n_kv_heads"], c["n_q_heads"], c["length"]
+    kc, ks = synth.kv_cache(c["kfmt"], c["seed"], 0, 0, Hkv, L, threads=args.threads)
+    vc, vs = synth.kv_cache(c["vfmt"], c["seed"], 0, 1, Hkv, L, threads=args.threads)
+    C = vq.DeviceKV.from_host(c["kfmt"], kc, ks, c["vfmt"], vc, vs, Hq, dev)
+    cache = kc.nbytes + ks.nbytes + vc.nbytes + vs.nbytes
+    res = {"workload": c["name"], "cache_bytes": cache, "per_K": {}}
+    for K in (1, 4, 8, 16):
+        q = torch.from_numpy(synth.queries(c["seed"], K, Hq)).to(dev)
+        o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        ws = torch.empty(C.workspace_bytes(K), dtype=torch.uint8, device=dev)
+        for _ in range(max(2, args.warmup)):
+            vq.verify_attention(C, q, out=o, ws=ws)
+        torch.cuda.synchronize()
+        n = max(50, 5 * args.steps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            vq.verify_attention(C, q, out=o, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        algo = cache + q.numel() * 2 + o.numel() * 4
+        res["per_K"][f"K{K}"] = {"us_per_call": round(us, 2), "gbps": round(algo / us / 1e3, 1),
+                                 "frac_of_hbm_peak": round(algo / us / 1e3 / HBM_PEAK_GBPS, 4),
+                                 "us_per_pass_64_layers": round(64 * us, 1)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +255,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=8.0, help="seconds of oracle time to sample")
     ap.add_argument("--threads", type=int, default=16, help="host threads for input generation")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the staged launch mode")
+    ap.add_argument("--no-attn", action="store_true", help="skip timing the attention over the KV cache")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first copy 1 GiB with torch (the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
@@ -461,6 +495,11 @@ def main():
             "per_shape": per_shape}
         log("K=16", sweep["K16"])
     out["sweep"] = sweep
+
+    # ---------------------------------------------------------- attention (next row)
+    if not args.no_attn:
+        out["attention"] = bench_attention(torch, vq, synth, dev, args)
+        log("attention", out["attention"])
 
     if not args.no_cpu:
         import oracle as oracle_mod
