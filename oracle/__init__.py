@@ -341,3 +341,44 @@ def accept(mode: int, target: np.ndarray, draft: np.ndarray | None = None,
     return dict(n_accepted=n_acc, tokens=tokens, status=status, near=near,
                 draft_tokens=draft_tokens)
 
+
+
+# ------------------------------------------------------------ adaptive draft depth
+def tau(alpha: float, k: int) -> float:
+    """Expected tokens per verify pass with k drafts, each accepted with probability alpha
+    independently ("Decode is memory-bound ...", section "Speculative decoding"):
+    (1 - alpha^(k+1)) / (1 - alpha), and k + 1 at alpha = 1."""
+    if alpha == 1.0:
+        return float(k + 1)
+    return (1.0 - alpha ** (k + 1)) / (1.0 - alpha)
+
+
+def depth_observe(stats, n_accepted, n_drafted, decay: float):
+    """Fold windows into (accepted, rejected) in window order: accepted = decay * accepted +
+    n; rejected = decay * rejected + (1 if the window ended on a rejected draft, n < drafted).
+    A window with every draft accepted adds no failure (the next draft was never tried);
+    accepted / (accepted + rejected) is then the maximum-likelihood per-draft acceptance."""
+    acc, rej = float(stats[0]), float(stats[1])
+    for n, d in zip(n_accepted, n_drafted):
+        n, d = int(n), int(d)
+        if d < 0 or n < 0 or n > d:
+            raise ValueError("n_accepted outside [0, n_drafted]")
+        acc = decay * acc + n
+        rej = decay * rej + (1.0 if n < d else 0.0)
+    return acc, rej
+
+
+def depth_choose(stats, alpha_prior: float, prior_weight: float, t_pass, t_draft: float):
+    """The depth k in 0 .. len(t_pass) - 1 maximising tau(a, k) / (t_pass[k] + k t_draft),
+    a = (accepted + prior_weight alpha_prior) / (accepted + rejected + prior_weight) ("Decode
+    is memory-bound ...", sections "Speculative decoding" and "Two things the math says to
+    do": pick the depth from measured acceptance).  Ties go to the smaller k.  Returns
+    (k, a, rates)."""
+    acc, rej = float(stats[0]), float(stats[1])
+    a = (acc + prior_weight * alpha_prior) / (acc + rej + prior_weight)
+    rates = [tau(a, k) / (float(t_pass[k]) + k * t_draft) for k in range(len(t_pass))]
+    best = 0
+    for k in range(1, len(rates)):
+        if rates[k] > rates[best]:
+            best = k
+    return best, a, rates

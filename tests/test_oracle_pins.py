@@ -784,3 +784,84 @@ def test_attention_dominant_key_and_shared_group():
     Vd = oracle.kv_dequant(synth.KV_Q8_0, vc, vs)
     assert np.allclose(out[0, 0], Vd[0, 17], rtol=1e-12) and np.allclose(out[0, 3], Vd[1, 17], rtol=1e-12)
     assert np.array_equal(out[0, 0], out[0, 1])
+
+
+# ------------------------------------------------------------ adaptive draft depth
+def test_depth_tau_matches_printed_table():
+    """oracle.tau against the acceptance-by-depth table the page prints (2 d.p.)."""
+    n = 0
+    for line in _golden_rows("tau_table.txt"):
+        f = line.split()
+        a = float(f[0])
+        for k, v in zip((1, 3, 5), f[1:]):
+            assert abs(oracle.tau(a, k) - float(v)) <= 0.005 + 1e-12, (a, k)
+            n += 1
+    assert n == 18
+    assert oracle.tau(1.0, 4) == 5.0 and oracle.tau(0.0, 7) == 1.0
+
+
+def test_depth_observe_hand_case_and_decay():
+    # windows (accepted, drafted): all 3 kept (no failure), none kept, 2 kept then a reject
+    assert oracle.depth_observe((0.0, 0.0), [3, 0, 2], [3, 3, 3], 1.0) == (5.0, 2.0)
+    # decay 0.5 in window order: acc 0.5*(0.5*(0.5*0+3)+0)+2 = 2.75; rej 0.5*(0.5*0+1)+1 = 1.5
+    acc, rej = oracle.depth_observe((0.0, 0.0), [3, 0, 2], [3, 3, 3], 0.5)
+    assert acc == 2.75 and rej == 1.5
+    with pytest.raises(ValueError):
+        oracle.depth_observe((0.0, 0.0), [4], [3], 1.0)
+
+
+@pytest.mark.parametrize("alpha,k", [(0.3, 3), (0.6, 5), (0.9, 7), (0.75, 1)])
+def test_depth_estimate_is_consistent(alpha, k):
+    """Windows simulated with independent per-draft acceptance: accepted / (accepted +
+    rejected) converges to alpha (counting windows instead of rejections, or treating an
+    all-accepted window as a failure, would be biased and fail this)."""
+    rng = np.random.default_rng(7)
+    W = 40000
+    u = rng.random((W, k))
+    n = np.where((u >= alpha).any(axis=1), (u >= alpha).argmax(axis=1), k)
+    acc, rej = oracle.depth_observe((0.0, 0.0), n, np.full(W, k), 1.0)
+    est = acc / (acc + rej)
+    se = np.sqrt(alpha * (1 - alpha) / (acc + rej))
+    assert abs(est - alpha) < 5 * se, (est, alpha)
+
+
+def test_depth_choose_against_exact_rationals():
+    """The chosen depth equals a brute-force argmax over exact rationals (fractions), for
+    random costs and acceptance counts."""
+    from fractions import Fraction
+    rng = np.random.default_rng(3)
+    for _ in range(300):
+        kmax = int(rng.integers(0, 16))
+        t = [Fraction(int(rng.integers(900, 1100)) + 40 * k, 1000) for k in range(kmax + 1)]
+        td = Fraction(int(rng.integers(0, 200)), 1000)
+        acc, rej = int(rng.integers(0, 50)), int(rng.integers(1, 50))
+        a = Fraction(acc, acc + rej)
+        def rate(k):
+            tau = sum(a ** i for i in range(k + 1))
+            return tau / (t[k] + k * td)
+        best = max(range(kmax + 1), key=lambda k: (rate(k), -k))
+        k, ah, _ = oracle.depth_choose((acc, rej), 0.5, 0.0, [float(x) for x in t], float(td))
+        assert abs(ah - float(a)) < 1e-15
+        # ties within rounding may go either way; otherwise the argmax must agree
+        if k != best:
+            assert abs(float(rate(k) - rate(best))) <= 1e-12 * float(rate(best))
+
+
+def test_depth_choose_special_cases():
+    flat = [1.0] * 8
+    # no acceptance at all: no drafts
+    assert oracle.depth_choose((0.0, 10.0), 0.5, 0.0, flat, 0.0)[0] == 0
+    # free drafts and a flat pass time: the deepest window
+    assert oracle.depth_choose((9.0, 1.0), 0.5, 0.0, flat, 0.0)[0] == 7
+    # every draft accepted so far (no rejection): alpha 1, deepest
+    assert oracle.depth_choose((12.0, 0.0), 0.5, 0.0, flat, 0.0)[0] == 7
+    # no statistics: the prior decides
+    assert oracle.depth_choose((0.0, 0.0), 0.0, 1.0, flat, 0.1)[0] == 0
+    # the page's reading of its table: at 0.35 going from three to five drafts buys 0.02
+    # tokens per pass, so any draft cost above 0.01 of a pass prefers three over five
+    r = oracle.depth_choose((35.0, 65.0), 0.5, 0.0, flat[:6], 0.011)[2]
+    assert r[3] > r[5]
+    # the page's speedup formula with a drafter cost c (pass time 1): at 0.9 and c = 0.1,
+    # five drafts beat three (4.69 / 1.5 > 3.44 / 1.3)
+    r = oracle.depth_choose((90.0, 10.0), 0.5, 0.0, flat[:6], 0.1)[2]
+    assert r[5] > r[3] and abs(r[5] - 4.68559 / 1.5) < 1e-12
