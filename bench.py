@@ -212,6 +212,72 @@ def cpu_baseline(synth, oracle_mod, budget_s: float):
     }
 
 
+def bench_depth(torch, vq, model, dev, H, V, args):
+    """Adaptive draft depth on this GPU's own pass times.  t_pass[k] = the measured verify pass
+    with k drafts (K = k + 1 columns, graph replays of vq_decode_pass on the 27B stack); a
+    draft step costs c of a K = 1 pass (the drafter is outside this build: c = 0.05, an MTP
+    head, and c = 0.25, a small draft model, are stated, not measured).  Reported: the depth
+    vq_depth_choose picks at fixed acceptance, and a synthetic trace (acceptance 0.85, 0.3,
+    0.65 for 2,000 windows each; per window 15 seeded uniforms decide the drafts for every
+    policy alike) run with the controller (observe each window, decay 0.98, prior 0.5 of
+    weight 2) against every fixed depth; tokens/s = tokens / (passes + drafts)."""
+    kmax = 8
+    t = []
+    for k in range(kmax + 1):
+        K = k + 1
+        x0 = torch.from_numpy(__import__("synth").activations(0, K, H)).to(dev)
+        logits = torch.empty((K, V), dtype=torch.float32, device=dev)
+        ws = torch.empty(model.workspace_bytes(K), dtype=torch.uint8, device=dev)
+        ms, g = time_graph(torch, lambda: vq.decode_pass(model, x0, logits, ws=ws), max(5, args.steps // 2), 2)
+        del g
+        assert model.barrier_error(K, ws) == 0
+        t.append(ms)
+        del x0, logits, ws
+    t = np.array(t)
+    res = {"t_pass_ms": [round(float(x), 4) for x in t], "k_max": kmax}
+    rng = np.random.default_rng(11)
+    segs = [(0.85, 2000), (0.3, 2000), (0.65, 2000)]
+    U = rng.random((sum(n for _, n in segs), 15))
+    A = np.concatenate([np.full(n, a) for a, n in segs])
+    first_rej = lambda w, k: int(np.argmax(U[w, :k] >= A[w])) if k > 0 and (U[w, :k] >= A[w]).any() else k
+    import time as _time
+    for c in (0.05, 0.25):
+        td = c * t[0]
+        fixed_alpha = {}
+        for a in (0.35, 0.5, 0.7, 0.9):
+            st = vq.VqDepthStats(a * 1e6, (1 - a) * 1e6)
+            k, _, r = vq.depth_choose(st, t, td)
+            fixed_alpha[f"alpha_{a}"] = {"k": k, "tok_per_s": round(r * 1e3, 1),
+                                         "tok_per_s_k3": round(1e3 * (1 - a ** 4) / (1 - a) / (t[3] + 3 * td), 1),
+                                         "tok_per_s_k7": round(1e3 * (1 - a ** 8) / (1 - a) / (t[7] + 7 * td), 1)}
+        # the trace: controller against every fixed depth, same uniforms
+        st = vq.VqDepthStats(0.0, 0.0)
+        k, tok, tim, ks = 3, 0, 0.0, []
+        t0 = _time.perf_counter()
+        for w in range(len(A)):
+            n = first_rej(w, k)
+            tok += n + 1
+            tim += t[k] + k * td
+            ks.append(k)
+            vq.depth_observe(st, [n], [k], 0.98)
+            k = vq.depth_choose(st, t, td, 0.5, 2.0)[0]
+        ctl_us = (_time.perf_counter() - t0) / len(A) * 1e6
+        fixed = {}
+        for kf in range(kmax + 1):
+            tk = sum(first_rej(w, kf) + 1 for w in range(len(A)))
+            fixed[kf] = tk / (len(A) * (t[kf] + kf * td)) * 1e3
+        best = max(fixed, key=fixed.get)
+        ks = np.array(ks)
+        res[f"c_{c}"] = {"fixed_alpha": fixed_alpha,
+                         "trace_adaptive_tok_per_s": round(tok / tim * 1e3, 1),
+                         "trace_best_fixed": {"k": best, "tok_per_s": round(fixed[best], 1)},
+                         "trace_fixed_tok_per_s": {str(kf): round(v, 1) for kf, v in fixed.items()},
+                         "trace_mean_depth_per_segment": [round(float(ks[i:i + 2000].mean()), 2)
+                                                          for i in (0, 2000, 4000)],
+                         "controller_us_per_window": round(ctl_us, 2)}
+    return res
+
+
 def bench_attention(torch, vq, synth, dev, args):
     """The window's attention over one layer's q8_0 / q4_0 cache of the 27B model at 32768
     positions (40 query heads, 8 kv heads, head dim 128), K = 1, 4, 8, 16: time per call
@@ -256,6 +322,7 @@ def main():
     ap.add_argument("--threads", type=int, default=16, help="host threads for input generation")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the staged launch mode")
     ap.add_argument("--no-attn", action="store_true", help="skip timing the attention over the KV cache")
+    ap.add_argument("--no-depth", action="store_true", help="skip the adaptive draft depth measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first copy 1 GiB with torch (the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
@@ -434,6 +501,9 @@ def main():
                        "implied_tok_s": {f"alpha_{a}": round(pps * tau(a, 7), 2) for a in ALPHAS},
                        "implied_tok_s_measured": round(pps * tau8, 2)}
         log("K=8", sweep["K8"])
+    if not args.no_depth:
+        out["adaptive_depth"] = bench_depth(torch, vq, model, dev, H, V, args)
+        log("adaptive depth", {k: v for k, v in out["adaptive_depth"].items() if k != "trace"})
     if 16 in Ks:
         del model
         torch.cuda.empty_cache()

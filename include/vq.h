@@ -242,6 +242,53 @@ typedef struct vq_attention {
 int vq_verify_attention(const vq_attention* desc, const void* q_f16, int32_t K, float* out, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------ adaptive draft depth */
+/* Running acceptance statistics (a HOST struct owned by the caller; zero it to start). */
+typedef struct vq_depth_stats {
+    double accepted;   /* decayed sum of accepted drafts                                 */
+    double rejected;   /* decayed count of windows that ended on a rejected draft        */
+} vq_depth_stats;
+
+/*
+ * vq_depth_observe -- fold W windows' outcomes, in window order, into the statistics:
+ *     accepted = decay * accepted + n_accepted[w]
+ *     rejected = decay * rejected + (n_accepted[w] < n_drafted[w] ? 1 : 0)
+ * A window that ends on a rejected draft is n successes and one failure; a window whose
+ * drafts were all accepted is n successes and no failure (the next draft was never tried),
+ * so accepted / (accepted + rejected) is the maximum-likelihood per-draft acceptance under
+ * independent acceptance (page "Decode is memory-bound ...", section "Speculative
+ * decoding"), older windows weighted down by `decay` per window.
+ *   n_accepted : HOST int32 [W], e.g. vq_verify_accept's n_accepted copied back (windows
+ *                with status != 0 left out by the caller)
+ *   n_drafted  : HOST int32 [W], the drafts of each window (K - 1)
+ *   decay      : (0, 1]
+ * Host arithmetic only (no GPU call).  Errors: VQ_ERR_ARG for NULL pointers (unless W == 0),
+ * W < 0, decay outside (0, 1], n_drafted < 0 or n_accepted outside [0, n_drafted]; on an
+ * error the statistics are left unchanged.
+ */
+int vq_depth_observe(vq_depth_stats* st, const int32_t* n_accepted, const int32_t* n_drafted,
+                     int32_t W, double decay);
+
+/*
+ * vq_depth_choose -- the draft depth k (drafts per window, K = k + 1 columns) for the next
+ * windows: the k in 0 .. k_max that maximises the expected tokens per unit time
+ *     rate(k) = tau(a, k) / (t_pass[k] + k * t_draft),  tau(a, k) = (1 - a^(k+1)) / (1 - a)
+ * (tau = k + 1 at a = 1), with a the statistics' estimate shrunk toward a prior,
+ *     a = (accepted + prior_weight * alpha_prior) / (accepted + rejected + prior_weight)
+ * (page "Decode is memory-bound ...", sections "Speculative decoding": tau and the speedup
+ * with a drafter cost; "Two things the math says to do": adapt the depth to the measured
+ * acceptance, which falls on hard text).  Ties go to the smaller k.
+ *   t_pass  : HOST double [k_max + 1], the measured verify-pass time with k drafts
+ *   t_draft : the time of one draft step (same unit), >= 0
+ *   k_out   : HOST out, the chosen depth; alpha_out, rate_out: HOST out or NULL
+ * Host arithmetic only.  Errors: VQ_ERR_ARG for NULL st / t_pass / k_out, k_max outside
+ * 0 .. VQ_MAX_K - 1, a time that is not finite and > 0 (t_draft: >= 0), alpha_prior outside
+ * [0, 1], prior_weight < 0, or no evidence at all (accepted + rejected + prior_weight == 0).
+ */
+int vq_depth_choose(const vq_depth_stats* st, double alpha_prior, double prior_weight,
+                    const double* t_pass, int32_t k_max, double t_draft, int32_t* k_out,
+                    double* alpha_out, double* rate_out);
+
 /* ---------------------------------------------------------------- acceptance */
 #define VQ_MODE_GREEDY 0      /* accept x_i while it equals the target argmax            */
 #define VQ_MODE_SAMPLE 1      /* accept x_i with prob. min(1, p(x_i)/q(x_i)), else resample */

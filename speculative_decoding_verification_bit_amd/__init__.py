@@ -63,6 +63,10 @@ class VqAttention(ctypes.Structure):
                 ("k_codes", _P), ("k_scales", _P), ("v_codes", _P), ("v_scales", _P)]
 
 
+class VqDepthStats(ctypes.Structure):
+    _fields_ = [("accepted", ctypes.c_double), ("rejected", ctypes.c_double)]
+
+
 class VqAcceptDesc(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("draft_mode", ctypes.c_int32), ("W", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("reserved", ctypes.c_int32),
@@ -74,7 +78,7 @@ class VqAcceptDesc(ctypes.Structure):
 
 
 EXPORTS = ("vq_tiled_bytes", "vq_tile", "vq_verify_linear", "vq_verify_linear_noalloc", "vq_verify_linear_mx",
-           "vq_verify_attention", "vq_verify_accept", "vq_decode_pass", "vq_decode_pass_timed",
+           "vq_verify_attention", "vq_verify_accept", "vq_depth_observe", "vq_depth_choose", "vq_decode_pass", "vq_decode_pass_timed",
            "vq_decode_stage_ptr", "vq_decode_error_word",
            "vq_workspace_bytes", "vq_status_string", "vq_last_error", "vq_abi_version")
 
@@ -97,6 +101,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.vq_verify_linear_mx.argtypes = [ctypes.POINTER(VqMatrix), _P, I32, _P, _P, SZ, _P]
     L.vq_verify_attention.restype = I32
     L.vq_verify_attention.argtypes = [ctypes.POINTER(VqAttention), _P, I32, _P, _P, SZ, _P]
+    L.vq_depth_observe.restype = I32
+    L.vq_depth_observe.argtypes = [ctypes.POINTER(VqDepthStats), _P, _P, I32, ctypes.c_double]
+    L.vq_depth_choose.restype = I32
+    L.vq_depth_choose.argtypes = [ctypes.POINTER(VqDepthStats), ctypes.c_double, ctypes.c_double, _P, I32,
+                                  ctypes.c_double, ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(ctypes.c_double)]
     L.vq_verify_accept.restype = I32
     L.vq_verify_accept.argtypes = [ctypes.POINTER(VqAcceptDesc), _P, SZ, _P]
     L.vq_decode_pass.restype = I32
@@ -292,6 +302,27 @@ def verify_attention(C: DeviceKV, q, out=None, ws=None, stream=None):
     _check(lib.vq_verify_attention(ctypes.byref(C.desc), _ptr(q), K, _ptr(out), _ptr(ws), ws.numel(),
                                    _stream(stream)), "vq_verify_attention")
     return out
+
+
+def depth_observe(stats: VqDepthStats, n_accepted, n_drafted, decay: float = 1.0) -> VqDepthStats:
+    """Fold windows (host int arrays) into the running acceptance statistics (in place)."""
+    a = np.ascontiguousarray(n_accepted, dtype=np.int32)
+    d = np.ascontiguousarray(n_drafted, dtype=np.int32)
+    _check(lib.vq_depth_observe(ctypes.byref(stats), a.ctypes.data, d.ctypes.data, a.size, decay),
+           "vq_depth_observe")
+    return stats
+
+
+def depth_choose(stats: VqDepthStats, t_pass, t_draft: float, alpha_prior: float = 0.5,
+                 prior_weight: float = 0.0):
+    """The draft depth maximising expected tokens per unit time at the measured pass times
+    t_pass[k] (k drafts): returns (k, alpha estimate, rate)."""
+    t = np.ascontiguousarray(t_pass, dtype=np.float64)
+    k = ctypes.c_int32(-1)
+    a, r = ctypes.c_double(), ctypes.c_double()
+    _check(lib.vq_depth_choose(ctypes.byref(stats), alpha_prior, prior_weight, t.ctypes.data, t.size - 1,
+                               t_draft, ctypes.byref(k), ctypes.byref(a), ctypes.byref(r)), "vq_depth_choose")
+    return k.value, a.value, r.value
 
 
 def accept_desc(mode, target, draft=None, draft_tokens=None, draft_mode=DRAFT_GIVEN, T=1.0,

@@ -14,7 +14,6 @@
 #include "vq_internal.h"
 
 namespace vq {
-namespace {
 
 thread_local char g_err[512] = "";
 
@@ -25,6 +24,10 @@ int fail(int code, const char* fmt, ...) {
     va_end(ap);
     return code;
 }
+
+void clear_error() { g_err[0] = 0; }
+
+namespace {
 
 int hip_fail(hipError_t e, const char* what) {
     return fail(VQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

@@ -156,6 +156,11 @@ size_t attn_workspace_bytes(int Hkv, int Hq, int L, int K, int nwg);
 hipError_t launch_attention(const vq_attention& C, const void* q, int K, float* out, uint8_t* ws, int nwg,
                             hipStream_t st);
 
+// The thread-local error text of the C ABI: fail() sets it and returns code.
+extern thread_local char g_err[512];
+int fail(int code, const char* fmt, ...);
+void clear_error();
+
 // Acceptance.
 size_t accept_ws_bytes(const vq_accept_desc* d);
 hipError_t launch_accept(const vq_accept_desc* d, void* ws, hipStream_t st);
