@@ -382,3 +382,37 @@ def depth_choose(stats, alpha_prior: float, prior_weight: float, t_pass, t_draft
         if rates[k] > rates[best]:
             best = k
     return best, a, rates
+
+
+# --------------------------------------------------------------- n-gram map drafter
+class NgramMap:
+    """Prompt lookup generalised ("100 tokens per second ...", section "Lever 3: an n-gram
+    overlay for repetition"): an incremental map from the k-token keys of the sequence so
+    far to the position that followed their latest occurrence; the most recent k tokens
+    look up their continuation, proposed as drafts.  A key enters the map once the token
+    after it exists, so the current last k tokens find an earlier occurrence only."""
+
+    def __init__(self, key_len: int):
+        if key_len < 1:
+            raise ValueError("key_len >= 1")
+        self.k = key_len
+        self.seq: list[int] = []
+        self.map: dict[tuple, int] = {}
+
+    def append(self, tokens):
+        for t in tokens:
+            self.seq.append(int(t))
+            n = len(self.seq)
+            # the key ending just before the new token now has a continuation (position n - 1)
+            if n - 1 >= self.k:
+                key = tuple(self.seq[n - 1 - self.k:n - 1])
+                self.map[key] = n - 1
+
+    def propose(self, max_drafts: int) -> list[int]:
+        n = len(self.seq)
+        if max_drafts <= 0 or n < self.k:
+            return []
+        p = self.map.get(tuple(self.seq[n - self.k:]))
+        if p is None:
+            return []
+        return self.seq[p:min(p + max_drafts, n)]

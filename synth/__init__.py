@@ -261,3 +261,31 @@ C5 = dict(name="27b-mxfp4-K16", seed=0, shape=SHAPE_27B, fmt=FMT_MXFP4, K=16)
 # keys at q8_0 and values at q4_0 (40 query heads, 8 kv heads, head dimension 128).
 ATTN = dict(name="27b-attn-32k-k8v4", seed=0, n_q_heads=40, n_kv_heads=8, head_dim=128, length=32768,
             kfmt=KV_Q8_0, vfmt=KV_Q4_0)
+
+
+_TAG_TOKENS = 5
+
+
+def token_stream(seed: int, n: int, vocab: int = 151936, n_snippets: int = 400, p_novel: float = 0.3,
+                 p_edit: float = 0.05) -> np.ndarray:
+    """A token stream with the repetition of code (identifiers, imports, call signatures and
+    re-emitted spans recur): a library of n_snippets random snippets (lengths 4..40 tokens,
+    uniform over the vocabulary) drawn with Zipf-like weights (rank r at 1/(r+1)), each
+    occurrence with every token replaced with probability p_edit, and runs of 1..20 novel
+    uniform tokens between snippets with probability p_novel.  int32 [n]."""
+    rng = _rng(seed, _TAG_TOKENS, n, vocab, n_snippets)
+    lens = rng.integers(4, 41, n_snippets)
+    lib = [rng.integers(0, vocab, L).astype(np.int32) for L in lens]
+    w = 1.0 / (np.arange(n_snippets) + 1.0)
+    w /= w.sum()
+    out, m = [], 0
+    while m < n:
+        if rng.random() < p_novel:
+            piece = rng.integers(0, vocab, int(rng.integers(1, 21))).astype(np.int32)
+        else:
+            piece = lib[int(rng.choice(n_snippets, p=w))].copy()
+            edit = rng.random(piece.size) < p_edit
+            piece[edit] = rng.integers(0, vocab, int(edit.sum()))
+        out.append(piece)
+        m += piece.size
+    return np.concatenate(out)[:n].astype(np.int32)

@@ -865,3 +865,61 @@ def test_depth_choose_special_cases():
     # five drafts beat three (4.69 / 1.5 > 3.44 / 1.3)
     r = oracle.depth_choose((90.0, 10.0), 0.5, 0.0, flat[:6], 0.1)[2]
     assert r[5] > r[3] and abs(r[5] - 4.68559 / 1.5) < 1e-12
+
+
+# --------------------------------------------------------------- n-gram map drafter
+def test_ngram_hand_cases():
+    m = oracle.NgramMap(2)
+    m.append([1, 2, 3, 4, 1, 2])
+    assert m.propose(3) == [3, 4, 1]
+    assert m.propose(10) == [3, 4, 1, 2]            # clamped at the sequence's end
+    assert m.propose(0) == []
+    m = oracle.NgramMap(2)
+    m.append([5, 6, 7, 5, 6, 8, 5, 6])              # the latest occurrence of (5, 6) wins
+    assert m.propose(3) == [8, 5, 6]
+    m = oracle.NgramMap(2)
+    m.append([1, 2, 3])                             # (2, 3) never seen before: a miss
+    assert m.propose(4) == []
+    m = oracle.NgramMap(1)
+    m.append([7, 7])                                # (7) was followed by 7
+    assert m.propose(2) == [7]
+    m = oracle.NgramMap(3)
+    m.append([1, 2])                                # shorter than the key
+    assert m.propose(2) == []
+
+
+def _scan_propose(seq, k, d):
+    """Brute force: the last earlier occurrence of the final k tokens whose next token
+    exists; its continuation, clamped at the end."""
+    n = len(seq)
+    if d <= 0 or n < k:
+        return []
+    key = seq[n - k:]
+    for s in range(n - 1 - k, -1, -1):
+        if seq[s:s + k] == key:
+            return seq[s + k:min(s + k + d, n)]
+    return []
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 6])
+def test_ngram_against_brute_force(k):
+    rng = np.random.default_rng(k)
+    for trial in range(40):
+        seq = [int(x) for x in rng.integers(0, 4 if trial % 2 else 9, int(rng.integers(1, 120)))]
+        m = oracle.NgramMap(k)
+        for i, t in enumerate(seq):
+            m.append([t])
+            d = int(rng.integers(0, 9))
+            assert m.propose(d) == _scan_propose(seq[:i + 1], k, d)
+
+
+def test_ngram_exact_repeat_is_always_right():
+    """A stream that repeats one block of 50 distinct tokens: once the first period has been
+    seen, every proposal is exactly the true next tokens."""
+    block = list(range(1000, 1050))
+    seq = block * 5
+    m = oracle.NgramMap(6)
+    m.append(seq[:60])
+    for i in range(60, len(seq) - 8):
+        assert m.propose(8) == seq[i:i + 8]
+        m.append([seq[i]])
