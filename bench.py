@@ -278,6 +278,49 @@ def bench_depth(torch, vq, model, dev, H, V, args):
     return res
 
 
+def bench_ngram(vq, synth, t_pass=None, n_tokens=100000, max_drafts=8):
+    """The n-gram map drafter on a synthetic code-like stream (synth.token_stream, 100,000
+    tokens) replayed as the target's output: per window the map proposes up to 8 drafts,
+    the accepted drafts are the prefix that equals the stream's next tokens, and the
+    accepted drafts plus one token are appended.  Per key length: tokens per window (tau),
+    the fraction of windows with a proposal, and the library's cost per window (append +
+    propose through the binding).  With the measured pass times t_pass[k], the implied
+    tokens/s when each window is verified with exactly the proposed drafts."""
+    import time as _time
+    s = synth.token_stream(0, n_tokens)
+    res = {"stream": "synth.token_stream(seed 0, 100000 tokens)", "max_drafts": max_drafts, "per_key_len": {}}
+    for k in (12, 6, 4, 2):
+        m = vq.NgramMap(k)
+        prompt = 2000
+        m.append(s[:prompt])
+        i, windows, hits, acc_sum, t_sec = prompt, 0, 0, 0, 0.0
+        pass_ms = 0.0
+        while i < s.size:
+            t0 = _time.perf_counter()
+            d = m.propose(max_drafts)
+            t_sec += _time.perf_counter() - t0
+            a = 0
+            while a < len(d) and i + a < s.size and d[a] == s[i + a]:
+                a += 1
+            emit = s[i:i + a + 1]
+            t0 = _time.perf_counter()
+            m.append(emit)
+            t_sec += _time.perf_counter() - t0
+            i += emit.size
+            windows += 1
+            hits += len(d) > 0
+            acc_sum += a
+            if t_pass is not None:
+                pass_ms += t_pass[min(len(d), len(t_pass) - 1)]
+        r = {"tokens_per_window": round((s.size - prompt) / windows, 4), "hit_rate": round(hits / windows, 4),
+             "accepted_per_hit": round(acc_sum / max(hits, 1), 3),
+             "us_per_window": round(t_sec / windows * 1e6, 2)}
+        if t_pass is not None:
+            r["implied_tok_per_s"] = round((s.size - prompt) / pass_ms * 1e3, 1)
+        res["per_key_len"][f"k{k}"] = r
+    return res
+
+
 def bench_attention(torch, vq, synth, dev, args):
     """The window's attention over one layer's q8_0 / q4_0 cache of the 27B model at 32768
     positions (40 query heads, 8 kv heads, head dim 128), K = 1, 4, 8, 16: time per call
@@ -323,6 +366,7 @@ def main():
     ap.add_argument("--no-compare", action="store_true", help="skip timing the staged launch mode")
     ap.add_argument("--no-attn", action="store_true", help="skip timing the attention over the KV cache")
     ap.add_argument("--no-depth", action="store_true", help="skip the adaptive draft depth measurement")
+    ap.add_argument("--no-ngram", action="store_true", help="skip the n-gram drafter measurement")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first copy 1 GiB with torch (the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
@@ -504,6 +548,10 @@ def main():
     if not args.no_depth:
         out["adaptive_depth"] = bench_depth(torch, vq, model, dev, H, V, args)
         log("adaptive depth", {k: v for k, v in out["adaptive_depth"].items() if k != "trace"})
+    if not args.no_ngram:
+        tp = out["adaptive_depth"]["t_pass_ms"] if "adaptive_depth" in out else None
+        out["ngram_drafter"] = bench_ngram(vq, synth, tp)
+        log("n-gram drafter", out["ngram_drafter"])
     if 16 in Ks:
         del model
         torch.cuda.empty_cache()

@@ -52,6 +52,7 @@ extern "C" {
 #define VQ_ERR_UNSUPPORTED (-2)  /* valid but not instantiated (format / K / path)      */
 #define VQ_ERR_WORKSPACE (-3)    /* workspace NULL or smaller than vq_workspace_bytes() */
 #define VQ_ERR_HIP (-4)          /* a HIP launch or runtime call failed                 */
+#define VQ_ERR_HOST (-5)         /* a host allocation failed                            */
 
 /* ------------------------------------------------------------ weight format */
 /* Block-quantised weights, row-major, blocks of 32 consecutive input columns.
@@ -288,6 +289,48 @@ int vq_depth_observe(vq_depth_stats* st, const int32_t* n_accepted, const int32_
 int vq_depth_choose(const vq_depth_stats* st, double alpha_prior, double prior_weight,
                     const double* t_pass, int32_t k_max, double t_draft, int32_t* k_out,
                     double* alpha_out, double* rate_out);
+
+/* ------------------------------------------------------------- n-gram map drafter */
+/* An incremental map over one token sequence (an opaque HOST object). */
+typedef struct vq_ngram vq_ngram;
+
+/*
+ * vq_ngram_create -- an empty map with keys of key_len tokens.  Prompt lookup generalised
+ * (page "100 tokens per second ...", section "Lever 3: an n-gram overlay for repetition"):
+ * the map takes every key_len-token key of the sequence so far to the position that
+ * followed its latest occurrence; the most recent key_len tokens look up their
+ * continuation, which is proposed as drafts.  The page found 6 better than 12 (12 matching
+ * tokens almost never occur).  Host memory only; grows with the sequence (4 bytes per token
+ * plus a table of at most 16 bytes per distinct key).
+ * Errors: VQ_ERR_ARG for NULL out or key_len outside 1..64; VQ_ERR_HOST.
+ */
+int vq_ngram_create(int32_t key_len, vq_ngram** out);
+
+/* vq_ngram_destroy -- free the map (NULL is ignored). */
+void vq_ngram_destroy(vq_ngram* m);
+
+/*
+ * vq_ngram_append -- append n tokens (the prompt, or each window's emitted tokens) to the
+ * sequence.  The key that ends just before each new token maps to that token's position
+ * (replacing its earlier occurrence), so a key enters the map only once its continuation
+ * exists.
+ *   tokens : HOST int32 [n], token ids >= 0 (the -1 padding of vq_verify_accept's tokens
+ *            must not be passed)
+ * Errors: VQ_ERR_ARG for NULL m, n < 0, NULL tokens with n > 0, a negative token id or a
+ * sequence past 2^31 - 1 tokens (nothing is appended then); VQ_ERR_HOST.
+ */
+int vq_ngram_append(vq_ngram* m, const int32_t* tokens, int32_t n);
+
+/*
+ * vq_ngram_propose -- the drafts for the next window: if the sequence's last key_len tokens
+ * occurred before with a continuation, the tokens that followed their latest such
+ * occurrence, at most max_drafts of them and none past the end of the sequence; otherwise
+ * none.
+ *   drafts   : HOST int32 [max_drafts] out;  n_drafts : HOST out, 0 .. max_drafts
+ * Errors: VQ_ERR_ARG for NULL m / n_drafts, max_drafts < 0, NULL drafts with max_drafts > 0.
+ * Calls on one map must not overlap; separate maps are independent.
+ */
+int vq_ngram_propose(const vq_ngram* m, int32_t max_drafts, int32_t* drafts, int32_t* n_drafts);
 
 /* ---------------------------------------------------------------- acceptance */
 #define VQ_MODE_GREEDY 0      /* accept x_i while it equals the target argmax            */

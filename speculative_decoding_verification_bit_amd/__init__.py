@@ -24,7 +24,7 @@ import torch  # noqa: F401
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libvq.so")
 
-OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_HOST = 0, -1, -2, -3, -4, -5
 FMT_Q4, FMT_Q4_MIN, FMT_MXFP4 = 0, 1, 2
 DTYPE_F32, DTYPE_F16 = 0, 1
 LAUNCH_AUTO, LAUNCH_STAGED, LAUNCH_PERSISTENT = 0, 4, 8
@@ -78,7 +78,8 @@ class VqAcceptDesc(ctypes.Structure):
 
 
 EXPORTS = ("vq_tiled_bytes", "vq_tile", "vq_verify_linear", "vq_verify_linear_noalloc", "vq_verify_linear_mx",
-           "vq_verify_attention", "vq_verify_accept", "vq_depth_observe", "vq_depth_choose", "vq_decode_pass", "vq_decode_pass_timed",
+           "vq_verify_attention", "vq_verify_accept", "vq_depth_observe", "vq_depth_choose",
+           "vq_ngram_create", "vq_ngram_destroy", "vq_ngram_append", "vq_ngram_propose", "vq_decode_pass", "vq_decode_pass_timed",
            "vq_decode_stage_ptr", "vq_decode_error_word",
            "vq_workspace_bytes", "vq_status_string", "vq_last_error", "vq_abi_version")
 
@@ -107,6 +108,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.vq_depth_choose.argtypes = [ctypes.POINTER(VqDepthStats), ctypes.c_double, ctypes.c_double, _P, I32,
                                   ctypes.c_double, ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(ctypes.c_double)]
+    L.vq_ngram_create.restype = I32
+    L.vq_ngram_create.argtypes = [I32, ctypes.POINTER(_P)]
+    L.vq_ngram_destroy.restype = None
+    L.vq_ngram_destroy.argtypes = [_P]
+    L.vq_ngram_append.restype = I32
+    L.vq_ngram_append.argtypes = [_P, _P, I32]
+    L.vq_ngram_propose.restype = I32
+    L.vq_ngram_propose.argtypes = [_P, I32, _P, ctypes.POINTER(I32)]
     L.vq_verify_accept.restype = I32
     L.vq_verify_accept.argtypes = [ctypes.POINTER(VqAcceptDesc), _P, SZ, _P]
     L.vq_decode_pass.restype = I32
@@ -323,6 +332,35 @@ def depth_choose(stats: VqDepthStats, t_pass, t_draft: float, alpha_prior: float
     _check(lib.vq_depth_choose(ctypes.byref(stats), alpha_prior, prior_weight, t.ctypes.data, t.size - 1,
                                t_draft, ctypes.byref(k), ctypes.byref(a), ctypes.byref(r)), "vq_depth_choose")
     return k.value, a.value, r.value
+
+
+class NgramMap:
+    """The library's n-gram map drafter over one token sequence (host memory)."""
+
+    def __init__(self, key_len: int):
+        h = _P()
+        _check(lib.vq_ngram_create(key_len, ctypes.byref(h)), "vq_ngram_create")
+        self._h = h
+        self._lib = lib
+        self._buf = np.empty(16, dtype=np.int32)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.vq_ngram_destroy(h)
+            self._h = None
+
+    def append(self, tokens):
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        _check(lib.vq_ngram_append(self._h, t.ctypes.data, t.size), "vq_ngram_append")
+
+    def propose(self, max_drafts: int) -> list:
+        if self._buf.size < max_drafts:
+            self._buf = np.empty(max_drafts, dtype=np.int32)
+        n = ctypes.c_int32(-1)
+        _check(lib.vq_ngram_propose(self._h, max_drafts, self._buf.ctypes.data, ctypes.byref(n)),
+               "vq_ngram_propose")
+        return self._buf[:n.value].tolist()
 
 
 def accept_desc(mode, target, draft=None, draft_tokens=None, draft_mode=DRAFT_GIVEN, T=1.0,

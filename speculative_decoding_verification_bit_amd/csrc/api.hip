@@ -454,6 +454,7 @@ const char* vq_status_string(int32_t status) {
         case VQ_ERR_UNSUPPORTED: return "unsupported configuration";
         case VQ_ERR_WORKSPACE: return "workspace missing or too small";
         case VQ_ERR_HIP: return "HIP runtime error";
+        case VQ_ERR_HOST: return "host allocation failed";
         default: return "unknown status";
     }
 }
