@@ -74,7 +74,7 @@ def lib():
         L.or_philox4x64.argtypes = [P, P, P]
         L.or_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64, P]
         L.or_warp.restype = I32
-        L.or_warp.argtypes = [P, I64, D, D, D, P, P]
+        L.or_warp.argtypes = [P, I64, D, D, D, I64, P, P]
         L.or_argmax.restype = I64
         L.or_argmax.argtypes = [P, I64]
         L.or_cat.restype = I64
@@ -271,16 +271,17 @@ def uniforms(seed: int, window: int, position: int) -> np.ndarray:
 
 class WarpInfo(ctypes.Structure):
     _fields_ = [("n_keep", ctypes.c_int64), ("m_p", ctypes.c_int64), ("m_m", ctypes.c_int64),
+                ("m_k", ctypes.c_int64),
                 ("near_top_p", ctypes.c_int), ("near_min_p", ctypes.c_int),
                 ("nonfinite", ctypes.c_int), ("argmax", ctypes.c_int64)]
 
 
-def warp(logits: np.ndarray, T: float, top_p: float = 1.0, min_p: float = 0.0):
+def warp(logits: np.ndarray, T: float, top_p: float = 1.0, min_p: float = 0.0, top_k: int = 0):
     """Warped distribution p[V] (double) and the WarpInfo of one logits row."""
     l = np.ascontiguousarray(logits, dtype=np.float32)
     p = np.empty(l.shape[0], np.float64)
     info = WarpInfo()
-    lib().or_warp(_p(l), l.shape[0], T, top_p, min_p, _p(p), ctypes.byref(info))
+    lib().or_warp(_p(l), l.shape[0], T, top_p, min_p, top_k, _p(p), ctypes.byref(info))
     return p, info
 
 
@@ -305,13 +306,14 @@ class _AcceptArgs(ctypes.Structure):
                 ("min_p", ctypes.c_double), ("alpha", ctypes.c_double),
                 ("seed", ctypes.c_uint64), ("window_base", ctypes.c_uint64),
                 ("n_accepted", ctypes.c_void_p), ("tokens", ctypes.c_void_p),
-                ("status", ctypes.c_void_p), ("near", ctypes.c_void_p)]
+                ("status", ctypes.c_void_p), ("near", ctypes.c_void_p),
+                ("top_k", ctypes.c_int64)]
 
 
 def accept(mode: int, target: np.ndarray, draft: np.ndarray | None = None,
            draft_tokens: np.ndarray | None = None, draft_mode: int = DRAFT_GIVEN,
            T: float = 1.0, top_p: float = 1.0, min_p: float = 0.0, alpha: float = 0.0,
-           seed: int = 0, window_base: int = 0, threads: int = 1) -> dict:
+           seed: int = 0, window_base: int = 0, threads: int = 1, top_k: int = 0) -> dict:
     """Acceptance of W windows.  target [W][K][V] f32, draft [W][K-1][V] f32.
 
     Returns n_accepted [W], tokens [W][K] (-1 padded), status [W], near [W] (bits of
@@ -334,7 +336,7 @@ def accept(mode: int, target: np.ndarray, draft: np.ndarray | None = None,
                        None if draft is None else _p(draft).value,
                        _p(draft_tokens).value if draft_tokens.size else None,
                        T, top_p, min_p, alpha, seed, window_base,
-                       _p(n_acc).value, _p(tokens).value, _p(status).value, _p(near).value)
+                       _p(n_acc).value, _p(tokens).value, _p(status).value, _p(near).value, top_k)
     rc = lib().or_accept(ctypes.byref(args), threads)
     if rc:
         raise RuntimeError(f"or_accept failed ({rc})")

@@ -31,6 +31,8 @@
  *    (probability descending, index ascending); top-p keeps the shortest prefix whose
  *    mass reaches top_p; min-p keeps pi >= min_p * pi_max; keep the shorter prefix;
  *    renormalise over the kept set.  top_p >= 1 or min_p == 0 disables that cut.
+ *    A top-k cut (the first top_k tokens of the same order; 0 or >= V disables it) is a
+ *    third prefix: the kept set is the shortest of the three.
  *  - greedy argmax ties go to the lowest index; greedy ignores T, top-p and min-p.
  *  - the ratio test accepts iff u_A < p/q with IEEE division (q = 0 < p gives +inf and
  *    accepts; p = q = 0 gives NaN and rejects).
@@ -397,6 +399,7 @@ typedef struct {
     int64_t n_keep;   /* tokens in the kept set */
     int64_t m_p;      /* top-p prefix length (V when disabled) */
     int64_t m_m;      /* min-p prefix length (V when disabled) */
+    int64_t m_k;      /* top-k prefix length (V when disabled) */
     int near_top_p;   /* cumulative mass within 1e-6 of top_p at m_p or m_p - 1 */
     int near_min_p;   /* a token at the min-p cut within 1e-6*pi_max of min_p*pi_max */
     int nonfinite;    /* a logit was NaN or infinite */
@@ -420,8 +423,8 @@ int64_t or_argmax(const float* l, int64_t V) {
     return best;
 }
 
-/* p[V] = warp(l; T, top_p, min_p).  T == 0 gives the one-hot argmax. */
-int or_warp(const float* l, int64_t V, double T, double top_p, double min_p,
+/* p[V] = warp(l; T, top_p, min_p, top_k).  T == 0 gives the one-hot argmax. */
+int or_warp(const float* l, int64_t V, double T, double top_p, double min_p, int64_t top_k,
             double* p, or_warp_info* info) {
     memset(info, 0, sizeof(*info));
     for (int64_t j = 0; j < V; ++j)
@@ -435,7 +438,7 @@ int or_warp(const float* l, int64_t V, double T, double top_p, double min_p,
         for (int64_t j = 0; j < V; ++j) p[j] = 0.0;
         p[info->argmax] = 1.0;
         info->n_keep = 1;
-        info->m_p = info->m_m = V;
+        info->m_p = info->m_m = info->m_k = V;
         return 0;
     }
     /* (1) tempered softmax */
@@ -480,12 +483,16 @@ int or_warp(const float* l, int64_t V, double T, double top_p, double min_p,
         if (m_m >= 1 && fabs(ord[m_m - 1].pi - thr) < 1e-6 * pi_max) info->near_min_p = 1;
         if (m_m < V && fabs(ord[m_m].pi - thr) < 1e-6 * pi_max) info->near_min_p = 1;
     }
+    /* (3c) top-k: the first top_k tokens of the order */
+    const int64_t m_k = (top_k > 0 && top_k < V) ? top_k : V;
     int64_t n_keep = m_p < m_m ? m_p : m_m;
+    if (m_k < n_keep) n_keep = m_k;
     /* A near-threshold cut matters only where it decides the kept set: moving the
-     * top-p cut by one token changes min(m_p, m_m) only when m_p <= m_m, and the
-     * min-p cut only when m_m <= m_p. */
-    if (m_p > m_m) info->near_top_p = 0;
-    if (m_m > m_p) info->near_min_p = 0;
+     * top-p cut by one token changes the shortest prefix only when m_p is (one of) the
+     * shortest, and likewise the min-p cut. */
+    const int64_t other_p = m_m < m_k ? m_m : m_k, other_m = m_p < m_k ? m_p : m_k;
+    if (m_p > other_p) info->near_top_p = 0;
+    if (m_m > other_m) info->near_min_p = 0;
     /* (4) renormalise over the kept set */
     double S = 0.0;
     for (int64_t m = 0; m < n_keep; ++m) S += ord[m].pi;
@@ -494,6 +501,7 @@ int or_warp(const float* l, int64_t V, double T, double top_p, double min_p,
     info->n_keep = n_keep;
     info->m_p = m_p;
     info->m_m = m_m;
+    info->m_k = m_k;
     free(ord);
     return 0;
 }
@@ -548,6 +556,7 @@ typedef struct {
     int32_t* tokens;         /* [W][K], -1 padded */
     int32_t* status;         /* [W]: 0 ok, 1 non-finite logit, 2 draft token out of range */
     int32_t* near;           /* [W]: OR_NEAR_* bits */
+    int64_t top_k;           /* top-k cut (0 = none) */
 } or_accept_args;
 
 typedef struct {
@@ -594,7 +603,7 @@ static void accept_window(const or_accept_args* A, int64_t w, double* p, double*
             xi = or_argmax(drf + (i - 1) * V, V);
         } else if (A->draft_mode == OR_DRAFT_Q_SAMPLE) {
             or_warp_info qi;
-            or_warp(drf + (i - 1) * V, V, A->T, A->top_p, A->min_p, q, &qi);
+            or_warp(drf + (i - 1) * V, V, A->T, A->top_p, A->min_p, A->top_k, q, &qi);
             if (qi.near_top_p) near |= OR_NEAR_TOP_P;
             if (qi.near_min_p) near |= OR_NEAR_MIN_P;
             int nc = 0;
@@ -642,7 +651,7 @@ static void accept_window(const or_accept_args* A, int64_t w, double* p, double*
         double u[4];
         or_uniforms(A->seed, win, (uint64_t)i, u);
         or_warp_info pi;
-        or_warp(tgt + (i - 1) * V, V, A->T, A->top_p, A->min_p, p, &pi);
+        or_warp(tgt + (i - 1) * V, V, A->T, A->top_p, A->min_p, A->top_k, p, &pi);
         if (pi.near_top_p) near |= OR_NEAR_TOP_P;
         if (pi.near_min_p) near |= OR_NEAR_MIN_P;
         if (i == K) {             /* every draft accepted: bonus token from p_K */
@@ -653,7 +662,7 @@ static void accept_window(const or_accept_args* A, int64_t w, double* p, double*
             break;
         }
         or_warp_info qi;
-        or_warp(drf + (i - 1) * V, V, A->T, A->top_p, A->min_p, q, &qi);
+        or_warp(drf + (i - 1) * V, V, A->T, A->top_p, A->min_p, A->top_k, q, &qi);
         if (qi.near_top_p) near |= OR_NEAR_TOP_P;
         if (qi.near_min_p) near |= OR_NEAR_MIN_P;
         double r = p[x[i]] / q[x[i]];

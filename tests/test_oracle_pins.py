@@ -923,3 +923,46 @@ def test_ngram_exact_repeat_is_always_right():
     for i in range(60, len(seq) - 8):
         assert m.propose(8) == seq[i:i + 8]
         m.append([seq[i]])
+
+
+# ------------------------------------------------------------------------ top-k cut
+def test_topk_hand_cases():
+    l = np.array([0, 3, 1, 3, 2], np.float32)
+    p, info = oracle.warp(l, 1.0, top_k=2)                 # the two 3s
+    assert info.n_keep == 2 and abs(p[1] - 0.5) < 1e-15 and abs(p[3] - 0.5) < 1e-15
+    p, _ = oracle.warp(l, 1.0, top_k=3)                    # and the 2
+    e = np.exp(np.array([3.0, 3.0, 2.0]))
+    assert np.allclose([p[1], p[3], p[4]], e / e.sum(), rtol=1e-15) and p[0] == p[2] == 0
+    p, _ = oracle.warp(np.array([5, 1, 1, 1, 0], np.float32), 1.0, top_k=2)
+    assert p[0] > 0 and p[1] > 0 and p[2] == p[3] == p[4] == 0   # ties: lowest index first
+    p, _ = oracle.warp(l, 0.7, top_k=1)                    # one-hot on the first maximum
+    assert p[1] == 1.0 and p.sum() == 1.0
+
+
+def test_topk_no_cut_and_composition():
+    rng = np.random.default_rng(4)
+    l = rng.standard_normal(300).astype(np.float32) * 2
+    base, _ = oracle.warp(l, 0.8, top_p=0.9, min_p=0.02)
+    for k in (0, 300, 10**6):
+        p, _ = oracle.warp(l, 0.8, top_p=0.9, min_p=0.02, top_k=k)
+        assert np.array_equal(p, base)
+    _, ip = oracle.warp(l, 0.8, top_p=0.9)
+    m_p = ip.n_keep
+    _, i1 = oracle.warp(l, 0.8, top_p=0.9, top_k=m_p - 3)   # top-k shorter: it decides
+    _, i2 = oracle.warp(l, 0.8, top_p=0.9, top_k=m_p + 3)   # top-p shorter: it decides
+    assert i1.n_keep == m_p - 3 and i2.n_keep == m_p
+
+
+def test_topk_kept_set_against_numpy_ranking():
+    """The kept set is exactly the top_k entries by (logit descending, index ascending),
+    ranked with numpy's lexsort on integer-valued logits full of ties."""
+    rng = np.random.default_rng(9)
+    for _ in range(50):
+        V = int(rng.integers(1, 400))
+        l = rng.integers(-4, 5, V).astype(np.float32)
+        k = int(rng.integers(1, V + 2))
+        p, info = oracle.warp(l, 1.3, top_k=k)
+        order = np.lexsort((np.arange(V), -l.astype(np.float64)))
+        keep = set(order[:min(k, V)].tolist())
+        assert set(np.nonzero(p)[0].tolist()) == keep
+        assert info.n_keep == min(k, V)
