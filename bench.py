@@ -235,6 +235,20 @@ def bench_depth(torch, vq, model, dev, H, V, args):
         del x0, logits, ws
     t = np.array(t)
     res = {"t_pass_ms": [round(float(x), 4) for x in t], "k_max": kmax}
+    # the K columns as a batch of independent one-token sequences: tokens per second
+    tb = {K: float(t[K - 1]) for K in range(1, kmax + 2)}
+    for K in (12, 16):
+        x0 = torch.from_numpy(__import__("synth").activations(0, K, H)).to(dev)
+        logits = torch.empty((K, V), dtype=torch.float32, device=dev)
+        ws = torch.empty(model.workspace_bytes(K), dtype=torch.uint8, device=dev)
+        ms, g = time_graph(torch, lambda: vq.decode_pass(model, x0, logits, ws=ws), max(5, args.steps // 2), 2)
+        del g
+        assert model.barrier_error(K, ws) == 0
+        tb[K] = ms
+        del x0, logits, ws
+    res["batch"] = {"note": "K independent sequences per pass (no speculation): tokens/s = K / t_pass(K)",
+                    "per_K": {f"K{K}": {"ms": round(v, 4), "tok_per_s": round(K / v * 1e3, 1)}
+                              for K, v in sorted(tb.items())}}
     rng = np.random.default_rng(11)
     segs = [(0.85, 2000), (0.3, 2000), (0.65, 2000)]
     U = rng.random((sum(n for _, n in segs), 15))

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 3
+#define VQ_ABI_VERSION 4
 
 /* ------------------------------------------------------------------ status */
 #define VQ_OK 0
@@ -350,7 +350,7 @@ typedef struct vq_accept_desc {
     int32_t W;                 /* windows, >= 0                                          */
     int32_t K;                 /* positions per window (K-1 drafts + 1 bonus), 1..16     */
     int32_t V;                 /* vocabulary size, 1 .. 2^19 (fixed-point mass sums)     */
-    int32_t reserved;          /* must be 0                                              */
+    int32_t top_k;             /* top-k cut, >= 0; 0 (or >= V) disables it               */
     const float* target_logits;/* device f32 [W][K][V]: row i scores position i+1        */
     const float* draft_logits; /* device f32 [W][K-1][V], or NULL when not needed        */
     int32_t* draft_tokens;     /* device i32 [W][K-1]: input (GIVEN) or output           */
@@ -378,7 +378,10 @@ typedef struct vq_accept_desc {
  * SAMPLE: p_i and q_i are the target and drafter rows after the sampler warp
  * (temperature, softmax, top-p and min-p cuts over the order probability-descending /
  * index-ascending, renormalised; page "Decode is memory-bound ...", section "Two things
- * the math says to do").  For i = 1..K-1: accept x_i iff u_A < p_i(x_i)/q_i(x_i); on the
+ * the math says to do"; the optional top-k cut keeps the first top_k entries of the same
+ * order; page "100 tokens per second ...", section "What failed", names top-k sampling;
+ * the kept set is the shortest of the three prefixes, each computed on the full
+ * distribution).  For i = 1..K-1: accept x_i iff u_A < p_i(x_i)/q_i(x_i); on the
  * first rejection draw from the normalised positive part of p_i - q_i (p_i itself if
  * that part is zero) and stop; if all are accepted draw the bonus from p_K.  Draws are
  * inverse-CDF over vocabulary order.

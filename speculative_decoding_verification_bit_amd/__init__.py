@@ -69,7 +69,7 @@ class VqDepthStats(ctypes.Structure):
 
 class VqAcceptDesc(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("draft_mode", ctypes.c_int32), ("W", ctypes.c_int32),
-                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("target_logits", _P), ("draft_logits", _P), ("draft_tokens", _P),
                 ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
                 ("min_p", ctypes.c_float), ("alpha", ctypes.c_float),
@@ -365,16 +365,17 @@ class NgramMap:
 
 def accept_desc(mode, target, draft=None, draft_tokens=None, draft_mode=DRAFT_GIVEN, T=1.0,
                 top_p=1.0, min_p=0.0, alpha=0.0, seed=0, window_base=0, n_accepted=None,
-                tokens=None, status=None) -> VqAcceptDesc:
+                tokens=None, status=None, top_k=0) -> VqAcceptDesc:
     W, K, V = target.shape
-    return VqAcceptDesc(mode, draft_mode, W, K, V, 0, _ptr(target), _ptr(draft), _ptr(draft_tokens),
+    return VqAcceptDesc(mode, draft_mode, W, K, V, top_k, _ptr(target), _ptr(draft), _ptr(draft_tokens),
                         T, top_p, min_p, alpha, seed, window_base, _ptr(n_accepted), _ptr(tokens),
                         _ptr(status))
 
 
 def verify_accept(mode: int, target, draft=None, draft_tokens=None, draft_mode: int = DRAFT_GIVEN,
                   T: float = 1.0, top_p: float = 1.0, min_p: float = 0.0, alpha: float = 0.0,
-                  seed: int = 0, window_base: int = 0, ws=None, out=None, stream=None) -> dict:
+                  seed: int = 0, window_base: int = 0, ws=None, out=None, stream=None,
+                  top_k: int = 0) -> dict:
     """Acceptance over W windows of fp32 target [W][K][V] / drafter [W][K-1][V] logits."""
     import torch
     W, K, V = target.shape
@@ -386,7 +387,7 @@ def verify_accept(mode: int, target, draft=None, draft_tokens=None, draft_mode: 
     if draft_tokens is None and K > 1:
         draft_tokens = torch.full((W, K - 1), -1, dtype=torch.int32, device=dev)
     d = accept_desc(mode, target, draft, draft_tokens, draft_mode, T, top_p, min_p, alpha, seed,
-                    window_base, out["n_accepted"], out["tokens"], out["status"])
+                    window_base, out["n_accepted"], out["tokens"], out["status"], top_k)
     need = int(lib.vq_workspace_bytes(OP_ACCEPT, ctypes.byref(d), K))
     if ws is None:
         ws = _empty(need, dev)

@@ -6,7 +6,10 @@
 // on a 24 GB AMD card", section "How speculative decoding gets past a per-token wall";
 // page "Decode is memory-bound ...", section "Speculative decoding").  p and q are the
 // rows after the sampler warp: temperature, softmax, then the top-p and min-p cuts
-// (page "Decode is memory-bound ...", section "Two things the math says to do").
+// (page "Decode is memory-bound ...", section "Two things the math says to do") and an
+// optional top-k cut (the first top_k entries; page "100 tokens per second ...", section
+// "What failed", names top-k sampling): each cut is a prefix of one order, the kept set
+// the shortest.
 //
 // Kernels:
 //  * k_row_stats: one 512-thread workgroup per logits row.  Pass 1 finds the maximum,
@@ -15,8 +18,9 @@
 //    order-independent, so every run is bitwise identical), pass 3 locates the top-p
 //    cut exactly by a three-level radix select on the order-preserving bit pattern of
 //    the logit (12 + 12 + 8 bits, histograms of probability mass in LDS) and then
-//    resolves equal logits by index, pass 4 sums the kept mass.  The kept set is then
-//    "min-p test passes and (key, index) ranks at or before the cut".
+//    resolves equal logits by index; the top-k cut is the same select over counts; pass 4
+//    sums the kept mass.  The kept set is then "min-p test passes and (key, index) ranks
+//    at or before the earlier cut".
 //  * k_accept: one 512-thread workgroup per window.  Thread 0 runs the sequential
 //    rule; inverse-CDF draws are block-wide: each thread owns a contiguous slice of
 //    the vocabulary, slice masses are scanned, and the slice holding the crossing is
@@ -38,16 +42,17 @@ struct RowStat {
     int32_t argmax;
     int32_t nonfinite;
     float lmax;
-    uint32_t thr_key;    // top-p cut: keys above are kept, equal keys up to thr_idx
+    uint32_t thr_key;    // the cut: keys above are kept, equal keys up to thr_idx
     int32_t thr_idx;
     int32_t n_keep;
     uint64_t z_fx;       // sum of e over the row
     uint64_t keep_fx;    // sum of e over the kept set
 };
 
-// Order-preserving map of a finite float to uint32 (larger float -> larger key).
+// Order-preserving map of a finite float to uint32 (larger float -> larger key; -0 and +0
+// compare equal, so both take the key of +0).
 __device__ __forceinline__ uint32_t fkey(float v) {
-    const uint32_t b = __float_as_uint(v);
+    const uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
@@ -157,6 +162,7 @@ struct StatArgs {
     int V;
     int full;              // 0: argmax and non-finite only
     float T, top_p, min_p;
+    int top_k;             // 0: no top-k cut
     RowStat* out;
     // With few rows, the first two passes run split over SPLIT_S workgroups per row
     // (k_row_part1, k_row_part2) and k_row_stats starts from their partials; NULL: not split.
@@ -335,24 +341,10 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
     }
     st.z_fx = block_sum_u64(z, sh);
 
-    // pass 3: top-p cut
-    if (A.top_p < 1.f) {
-        uint64_t tgt = (uint64_t)ceil((double)A.top_p * (double)st.z_fx);
-        if (tgt < 1) tgt = 1;
-        if (min_p > 0.f) {
-            const uint64_t zm_fx = block_sum_u64(zm, sh);
-            const uint64_t nm_all = block_sum_u64(nm, sh);
-            if (zm_fx < tgt) {
-                // the min-p set holds less than the top-p mass, so every top-p prefix
-                // contains it: the min-p cut is the shorter one and decides alone
-                st.thr_key = 0u;
-                st.thr_idx = 0x7fffffff;
-                st.keep_fx = zm_fx;
-                st.n_keep = (int)nm_all;
-                if (t == 0) A.out[row] = st;
-                return;
-            }
-        }
+    // pass 3: the cuts, each the entry of the order (key descending, index ascending) at
+    // which a running measure first reaches a target: top-p over probability mass,
+    // top-k over counts.  The kept set ends at the earlier one.
+    auto cut_at = [&](bool by_count, uint64_t tgt, uint32_t& kout, int& iout) {
         uint32_t prefix = 0;
         int shift_hi = 32;      // bits already fixed: key >> shift_hi == prefix
         uint64_t above = 0;
@@ -367,7 +359,7 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
                 const uint32_t k = fkey(v);
                 if (shift_hi == 32 || (k >> shift_hi) == prefix)
                     atomicAdd((unsigned long long*)&hist[(k >> shift) & (nbins - 1)],
-                              (unsigned long long)to_fx(e_of(v, lmax, T)));
+                              by_count ? 1ull : (unsigned long long)to_fx(e_of(v, lmax, T)));
             });
             __syncthreads();
             int b;
@@ -379,10 +371,13 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
         }
         const uint32_t kstar = prefix;
         // equal keys: the c-th smallest index among them crosses the target
-        const float lstar = __uint_as_float((kstar & 0x80000000u) ? (kstar & 0x7fffffffu) : ~kstar);
-        const uint64_t estar = to_fx(e_of(lstar, lmax, T));
         const uint64_t need = tgt - above;
-        const uint64_t c = estar ? (need + estar - 1) / estar : 1;
+        uint64_t c = need;
+        if (!by_count) {
+            const float lstar = __uint_as_float((kstar & 0x80000000u) ? (kstar & 0x7fffffffu) : ~kstar);
+            const uint64_t estar = to_fx(e_of(lstar, lmax, T));
+            c = estar ? (need + estar - 1) / estar : 1;
+        }
         // The entries with key kstar: usually a handful.  Up to NT of them are listed in
         // LDS and the cc-th smallest index is found by ranking; more than that (long runs
         // of equal logits) take an ordered scan over contiguous slices.
@@ -423,10 +418,36 @@ __global__ __launch_bounds__(NT) void k_row_stats(StatArgs A) {
             }
         }
         __syncthreads();
-        st.thr_key = kstar;
-        st.thr_idx = s_bin;
+        kout = kstar;
+        iout = s_bin;
         __syncthreads();
+    };
+    bool cut = false;
+    uint32_t ck = 0u;
+    int ci = 0x7fffffff;
+    if (A.top_k > 0 && A.top_k < V) {
+        cut_at(true, (uint64_t)A.top_k, ck, ci);
+        cut = true;
     }
+    if (A.top_p < 1.f) {
+        uint64_t tgt = (uint64_t)ceil((double)A.top_p * (double)st.z_fx);
+        if (tgt < 1) tgt = 1;
+        // a min-p set holding less than the top-p mass lies inside every top-p prefix:
+        // then the top-p cut cannot be the shorter one
+        const bool minp_inside = min_p > 0.f && block_sum_u64(zm, sh) < tgt;
+        if (!minp_inside) {
+            uint32_t pk;
+            int pi;
+            cut_at(false, tgt, pk, pi);
+            if (!cut || pk > ck || (pk == ck && pi < ci)) {
+                ck = pk;
+                ci = pi;
+            }
+            cut = true;
+        }
+    }
+    st.thr_key = ck;
+    st.thr_idx = ci;
 
     // pass 4: kept mass and size
     uint64_t kf = 0, kn = 0;
@@ -987,12 +1008,14 @@ hipError_t launch_accept(const vq_accept_desc* d, void* ws, hipStream_t st) {
     const bool sample = d->mode == VQ_MODE_SAMPLE;
     const bool drafter = sample || d->draft_mode == VQ_DRAFT_Q_ARGMAX || d->draft_mode == VQ_DRAFT_Q_SAMPLE;
     const float T = d->temperature;
-    StatArgs sa{d->target_logits, d->W * d->K, d->V, sample ? 1 : 0, T, d->top_p, d->min_p, st_t, nullptr, nullptr};
+    StatArgs sa{d->target_logits, d->W * d->K, d->V, sample ? 1 : 0, T, d->top_p, d->min_p, d->top_k, st_t,
+                nullptr, nullptr};
     hipError_t e = launch_row_stats(sa, L.split_t, wsb, L.p1_t, L.p2_t, st);
     if (e != hipSuccess) return e;
     if (drafter && d->K > 1) {
         const int full = (sample || d->draft_mode == VQ_DRAFT_Q_SAMPLE) ? 1 : 0;
-        StatArgs sd{d->draft_logits, d->W * (d->K - 1), d->V, full, T, d->top_p, d->min_p, st_d, nullptr, nullptr};
+        StatArgs sd{d->draft_logits, d->W * (d->K - 1), d->V, full, T, d->top_p, d->min_p, d->top_k, st_d,
+                    nullptr, nullptr};
         e = launch_row_stats(sd, L.split_d, wsb, L.p1_d, L.p2_d, st);
         if (e != hipSuccess) return e;
     }

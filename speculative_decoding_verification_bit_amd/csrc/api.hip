@@ -727,7 +727,7 @@ int vq_verify_attention(const vq_attention* desc, const void* q_f16, int32_t K, 
 int vq_verify_accept(const vq_accept_desc* d, void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
     if (!d) return fail(VQ_ERR_ARG, "NULL descriptor");
-    if (d->reserved != 0) return fail(VQ_ERR_ARG, "reserved field must be 0");
+    if (d->top_k < 0) return fail(VQ_ERR_ARG, "top_k %d < 0", d->top_k);
     if (d->mode != VQ_MODE_GREEDY && d->mode != VQ_MODE_SAMPLE) return fail(VQ_ERR_ARG, "unknown mode %d", d->mode);
     if (d->draft_mode < VQ_DRAFT_GIVEN || d->draft_mode > VQ_DRAFT_AGREE)
         return fail(VQ_ERR_ARG, "unknown draft_mode %d", d->draft_mode);

@@ -132,7 +132,7 @@ def test_tile_argument_errors():
 
 
 def _acc(**kw):
-    base = dict(mode=vq.MODE_SAMPLE, draft_mode=vq.DRAFT_GIVEN, W=4, K=4, V=256, reserved=0,
+    base = dict(mode=vq.MODE_SAMPLE, draft_mode=vq.DRAFT_GIVEN, W=4, K=4, V=256, top_k=0,
                 target_logits=FAKE, draft_logits=FAKE, draft_tokens=FAKE, temperature=1.0, top_p=1.0,
                 min_p=0.0, alpha=0.0, seed=0, window_base=0, n_accepted=FAKE, tokens=FAKE, status=FAKE)
     base.update(kw)
@@ -144,7 +144,7 @@ def _acc(**kw):
     dict(V=(1 << 19) + 1), dict(temperature=0.0), dict(temperature=-1.0), dict(top_p=0.0),
     dict(top_p=1.5), dict(min_p=1.0), dict(min_p=-0.1), dict(target_logits=None),
     dict(draft_logits=None), dict(draft_tokens=None), dict(tokens=None), dict(status=None),
-    dict(n_accepted=None), dict(reserved=1), dict(draft_mode=vq.DRAFT_AGREE, mode=vq.MODE_GREEDY, V=1),
+    dict(n_accepted=None), dict(top_k=-1), dict(draft_mode=vq.DRAFT_AGREE, mode=vq.MODE_GREEDY, V=1),
     dict(draft_mode=vq.DRAFT_AGREE, mode=vq.MODE_GREEDY, alpha=1.5),
     dict(temperature=float("nan")),
 ])

@@ -15,21 +15,22 @@ pytestmark = pytest.mark.gpu
 
 
 def _gpu(mode, t, d=None, dtok=None, draft_mode=0, T=1.0, top_p=1.0, min_p=0.0, alpha=0.0, seed=0,
-         window_base=0):
+         window_base=0, top_k=0):
     torch = need_gpu()
     import speculative_decoding_verification_bit_amd as vq
     td = torch.from_numpy(np.ascontiguousarray(t)).cuda()
     dd = None if d is None else torch.from_numpy(np.ascontiguousarray(d)).cuda()
     dt = None if dtok is None else torch.from_numpy(np.ascontiguousarray(dtok)).cuda()
-    out = vq.verify_accept(mode, td, dd, dt, draft_mode, T, top_p, min_p, alpha, seed, window_base)
+    out = vq.verify_accept(mode, td, dd, dt, draft_mode, T, top_p, min_p, alpha, seed, window_base,
+                           top_k=top_k)
     torch.cuda.synchronize()
     return {k: (v.cpu().numpy() if v is not None else None) for k, v in out.items()}
 
 
 def _oracle(mode, t, d=None, dtok=None, draft_mode=0, T=1.0, top_p=1.0, min_p=0.0, alpha=0.0, seed=0,
-            window_base=0):
+            window_base=0, top_k=0):
     return oracle.accept(mode, t, d, dtok, draft_mode, f32(T), f32(top_p), f32(min_p), f32(alpha), seed,
-                         window_base, threads=8)
+                         window_base, threads=8, top_k=top_k)
 
 
 def _compare(g, o, exact: bool, what: str, max_near_frac=0.05):
@@ -218,3 +219,61 @@ def test_c4_full_size_all_windows():
              max_near_frac=0.05)
     emitted = g["n_accepted"] + 1
     report(f"C4 mean tokens per pass {emitted.mean():.3f} (oracle {(o['n_accepted'] + 1).mean():.3f})")
+
+
+# (top-p cuts deep in the tail, where each token adds ~1e-6 of mass, flag most windows as
+# near the threshold; the top-p settings here keep the cut in the head)
+@pytest.mark.parametrize("top_k,top_p,min_p", [(40, 1.0, 0.0), (40, 0.95, 0.05), (2000, 0.6, 0.0),
+                                              (1, 1.0, 0.0), (151936, 0.9, 0.0), (7, 0.5, 0.0)])
+def test_top_k_cut_full_vocab(top_k, top_p, min_p):
+    """The top-k cut (a count radix select) alone and with top-p / min-p, over V = 151936
+    (80 windows): the kept set is the shortest of the prefixes; k = 1 is the argmax; k >= V
+    no cut."""
+    spec = synth.LogitSpec(seed=13, K=3, vocab=151936, target_sigma=3.0, noise_sigma=1.0)
+    t, d = synth.logits_batch(spec, 0, 80, threads=16)
+    kw = dict(draft_mode=oracle.DRAFT_Q_SAMPLE, T=0.7, top_p=top_p, min_p=min_p, seed=6, top_k=top_k)
+    o = _oracle(oracle.MODE_SAMPLE, t, d, **kw)
+    g = _gpu(1, t, d, **kw)
+    _compare(g, o, False, f"V 151936 top-k {top_k} top-p {top_p} min-p {min_p}", max_near_frac=0.05)
+
+
+def test_top_k_ties_at_the_cut():
+    """Integer logits (runs of equal values straddle the k-th entry): lower indices first."""
+    V, K, W = 300, 3, 300
+    rng = np.random.default_rng(8)
+    t = np.round(rng.standard_normal((W, K, V)) * 1.5).astype(np.float32)
+    d = (t[:, :K - 1] + np.round(rng.standard_normal((W, K - 1, V)))).astype(np.float32)
+    for top_k in (3, 17, 150):
+        kw = dict(draft_mode=oracle.DRAFT_Q_SAMPLE, T=1.0, top_k=top_k, seed=9)
+        o = _oracle(oracle.MODE_SAMPLE, t, d, **kw)
+        g = _gpu(1, t, d, **kw)
+        _compare(g, o, False, f"integer logits (ties) top-k {top_k}", max_near_frac=0.05)
+
+
+def test_top_k_single_window_split_stats():
+    """K = 1 single windows over V = 151936 (the row statistics run split over many
+    workgroups) with top-k 50 and the production sampler."""
+    spec = synth.LogitSpec(seed=17, K=1, vocab=151936, target_sigma=3.0, noise_sigma=1.0)
+    t, _ = synth.logits_batch(spec, 0, 6, threads=8)
+    kw = dict(T=0.6, top_p=0.95, min_p=0.05, seed=4, top_k=50)
+    for w in range(6):
+        e = np.zeros((1, 0, spec.vocab), np.float32)
+        g = _gpu(1, t[w:w + 1], e, window_base=w, **kw)
+        o = _oracle(oracle.MODE_SAMPLE, t[w:w + 1], e, window_base=w, **kw)
+        _compare(g, o, False, f"K=1 window {w} top-k 50", max_near_frac=1.0)
+
+
+def test_negative_zero_logits_tie_with_positive_zero():
+    """-0.0 and +0.0 logits are equal: at a cut inside a run of zeros, the lower indices are
+    kept first whichever sign the zeros carry (top-k and top-p)."""
+    V, K, W = 64, 2, 200
+    rng = np.random.default_rng(12)
+    t = np.round(rng.standard_normal((W, K, V))).astype(np.float32)
+    t[np.abs(t) == 0] = np.where(rng.random(int((t == 0).sum())) < 0.5, np.float32(-0.0), np.float32(0.0))
+    d = (t[:, :1] + np.round(rng.standard_normal((W, 1, V)))).astype(np.float32)
+    assert np.signbit(t[t == 0]).any() and (~np.signbit(t[t == 0])).any()
+    for kw in (dict(top_k=30), dict(top_p=0.7)):
+        kw.update(draft_mode=oracle.DRAFT_Q_SAMPLE, T=1.0, seed=3)
+        o = _oracle(oracle.MODE_SAMPLE, t, d, **kw)
+        g = _gpu(1, t, d, **kw)
+        _compare(g, o, False, f"signed zeros {kw}", max_near_frac=0.05)
