@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-FMT_Q4, FMT_Q4_MIN, FMT_MXFP4 = 0, 1, 2
+FMT_Q4, FMT_Q4_MIN, FMT_MXFP4, FMT_Q4_K = 0, 1, 2, 3
 MODE_GREEDY, MODE_SAMPLE = 0, 1
 DRAFT_GIVEN, DRAFT_Q_ARGMAX, DRAFT_Q_SAMPLE, DRAFT_AGREE = 0, 1, 2, 3
 NEAR_RATIO, NEAR_CAT, NEAR_TOP_P, NEAR_MIN_P, NEAR_DRAFT_CAT = 1, 2, 4, 8, 16
@@ -55,11 +55,11 @@ def lib():
         L.or_e2m1.argtypes = [I32]
         L.or_e8m0.restype = D
         L.or_e8m0.argtypes = [ctypes.c_uint8]
-        L.or_dequant.argtypes = [I32, P, P, P, I64, I64, P]
+        L.or_dequant.argtypes = [I32, P, P, P, P, I64, I64, P]
         L.or_attention.restype = I32
         L.or_attention.argtypes = [I32, P, P, I32, P, P, I64, I64, I64, P, I64, I64, P, P]
         L.or_linear_x64.restype = I32
-        L.or_linear_x64.argtypes = [I32, P, P, P, I64, I64, P, I32, P, P, I32]
+        L.or_linear_x64.argtypes = [I32, P, P, P, P, I64, I64, P, I32, P, P, I32]
         L.or_e4m3.restype = D
         L.or_e4m3.argtypes = [I32]
         L.or_e4m3_code.restype = I32
@@ -67,7 +67,7 @@ def lib():
         L.or_mx_quant.restype = I32
         L.or_mx_quant.argtypes = [P, I64, I64, P, P]
         L.or_linear.restype = I32
-        L.or_linear.argtypes = [I32, P, P, P, I64, I64, P, I32, P, P, I32]
+        L.or_linear.argtypes = [I32, P, P, P, P, I64, I64, P, I32, P, P, I32]
         L.or_rho.argtypes = [P, I32, I64, P]
         L.or_rms_scale.argtypes = [P, I32, I64, P]
         L.or_silu_mul.argtypes = [P, P, I64, P]
@@ -108,13 +108,24 @@ def e8m0(e: int) -> float:
     return lib().or_e8m0(e)
 
 
+def _mins_supers(m):
+    """The mins plane (or None) and, for Q4_K, the super-block (d, dmin) plane."""
+    mn = None if m.mins is None else np.ascontiguousarray(m.mins)
+    sp = None
+    if m.fmt == FMT_Q4_K:
+        if m.cols % 256 or m.supers is None:
+            raise ValueError("Q4_K needs cols % 256 == 0 and the super-block plane")
+        sp = np.ascontiguousarray(m.supers).view(np.uint16)
+    return mn, sp
+
+
 def dequant(m) -> np.ndarray:
     """Dequantised weights [rows][cols] in double for a synth.Q4Matrix."""
     out = np.empty((m.rows, m.cols), np.float64)
     qs = np.ascontiguousarray(m.qs)
     sc = np.ascontiguousarray(m.scales)
-    mn = None if m.mins is None else np.ascontiguousarray(m.mins)
-    lib().or_dequant(m.fmt, _p(qs), _p(sc), _p(mn), m.rows, m.cols, _p(out))
+    mn, sp = _mins_supers(m)
+    lib().or_dequant(m.fmt, _p(qs), _p(sc), _p(mn), _p(sp), m.rows, m.cols, _p(out))
     return out
 
 
@@ -127,8 +138,8 @@ def linear(m, x: np.ndarray, threads: int = 1):
     a = np.empty((K, m.rows), np.float64)
     qs = np.ascontiguousarray(m.qs)
     sc = np.ascontiguousarray(m.scales)
-    mn = None if m.mins is None else np.ascontiguousarray(m.mins)
-    rc = lib().or_linear(m.fmt, _p(qs), _p(sc), _p(mn), m.rows, m.cols, _p(x), K,
+    mn, sp = _mins_supers(m)
+    rc = lib().or_linear(m.fmt, _p(qs), _p(sc), _p(mn), _p(sp), m.rows, m.cols, _p(x), K,
                          _p(y), _p(a), threads)
     if rc:
         raise RuntimeError(f"or_linear failed ({rc})")
@@ -144,8 +155,9 @@ def linear_x64(m, x: np.ndarray, threads: int = 1):
     a = np.empty((K, m.rows), np.float64)
     qs = np.ascontiguousarray(m.qs)
     sc = np.ascontiguousarray(m.scales)
-    mn = None if m.mins is None else np.ascontiguousarray(m.mins)
-    rc = lib().or_linear_x64(m.fmt, _p(qs), _p(sc), _p(mn), m.rows, m.cols, _p(x), K, _p(y), _p(a), threads)
+    mn, sp = _mins_supers(m)
+    rc = lib().or_linear_x64(m.fmt, _p(qs), _p(sc), _p(mn), _p(sp), m.rows, m.cols, _p(x), K, _p(y), _p(a),
+                             threads)
     if rc:
         raise RuntimeError(f"or_linear_x64 failed ({rc})")
     return y, a

@@ -22,11 +22,18 @@
  *    once, and outputs a [n_tokens, vocab] logits tensor; the "D E F" worked example.
  *  - Weight formats: 4-bit codes in blocks of 32 with an fp16 scale (and optional fp16
  *    min); MXFP4 = E2M1 codes with an E8M0 scale per 32 (OCP Microscaling Formats v1.0).
+ *    The K-quant 4-bit format the pages name (Q4_K_M, UD-Q4_K_XL) in its public GGML
+ *    definition: super-blocks of 256 weights, each of eight 32-weight sub-blocks with a
+ *    6-bit scale s and a 6-bit min m, under the super-block's fp16 d and dmin; an
+ *    unsigned code n in 0..15 gives w = d*s*n - dmin*m.
  *  - Philox4x64-10: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as
  *    1, 2, 3", SC'11 (round function, multipliers, Weyl key schedule).
  *
  * Readings where the pages are silent (each one is listed in the design notes):
  *  - code n -> q = n - 8; even column = low nibble; w = d*q + m (m = 0 without mins).
+ *  - Q4_K planes: one byte per 6-bit s and m (uint8 [rows][cols/32] each), d and dmin as
+ *    an fp16 pair per super-block (uint16 [rows][cols/256][2]); nibbles as above, but
+ *    the code is taken unsigned.
  *  - warp order: temperature, softmax, then the top-p and min-p cuts over the order
  *    (probability descending, index ascending); top-p keeps the shortest prefix whose
  *    mass reaches top_p; min-p keeps pi >= min_p * pi_max; keep the shorter prefix;
@@ -57,6 +64,7 @@
 #define OR_FMT_Q4 0
 #define OR_FMT_Q4_MIN 1
 #define OR_FMT_MXFP4 2
+#define OR_FMT_Q4_K 3
 
 /* ---------------------------------------------------------------- fp16 -> double */
 
@@ -94,9 +102,10 @@ double or_e8m0(uint8_t e) {
     return e == 255 ? NAN : ldexp(1.0, (int)e - 127);
 }
 
-/* Weight (r, j) of a row-major block-quantised matrix with cols columns. */
-double or_weight(int fmt, const uint8_t* qs, const void* scales, const uint16_t* mins,
-                 int64_t cols, int64_t r, int64_t j) {
+/* Weight (r, j) of a row-major block-quantised matrix with cols columns.  supers is
+ * used by Q4_K only (NULL otherwise). */
+double or_weight(int fmt, const uint8_t* qs, const void* scales, const void* mins,
+                 const uint16_t* supers, int64_t cols, int64_t r, int64_t j) {
     int64_t nb = cols / 32, b = j / 32;
     uint8_t byte = qs[r * (cols / 2) + j / 2];
     int n = (j % 2 == 0) ? (byte & 15) : (byte >> 4);
@@ -104,16 +113,23 @@ double or_weight(int fmt, const uint8_t* qs, const void* scales, const uint16_t*
         uint8_t e = ((const uint8_t*)scales)[r * nb + b];
         return or_e2m1(n) * or_e8m0(e);
     }
+    if (fmt == OR_FMT_Q4_K) {
+        const uint16_t* sup = supers + (r * (cols / 256) + j / 256) * 2;
+        double d = or_half(sup[0]), dmin = or_half(sup[1]);
+        double s = (double)((const uint8_t*)scales)[r * nb + b];
+        double m = (double)((const uint8_t*)mins)[r * nb + b];
+        return d * s * (double)n - dmin * m;
+    }
     double d = or_half(((const uint16_t*)scales)[r * nb + b]);
-    double m = (fmt == OR_FMT_Q4_MIN) ? or_half(mins[r * nb + b]) : 0.0;
+    double m = (fmt == OR_FMT_Q4_MIN) ? or_half(((const uint16_t*)mins)[r * nb + b]) : 0.0;
     return d * (double)(n - 8) + m;
 }
 
-void or_dequant(int fmt, const uint8_t* qs, const void* scales, const uint16_t* mins,
-                int64_t rows, int64_t cols, double* out) {
+void or_dequant(int fmt, const uint8_t* qs, const void* scales, const void* mins,
+                const uint16_t* supers, int64_t rows, int64_t cols, double* out) {
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t j = 0; j < cols; ++j)
-            out[r * cols + j] = or_weight(fmt, qs, scales, mins, cols, r, j);
+            out[r * cols + j] = or_weight(fmt, qs, scales, mins, supers, cols, r, j);
 }
 
 /* --------------------------------------------------------------------- linear */
@@ -124,7 +140,8 @@ typedef struct {
     int fmt;
     const uint8_t* qs;
     const void* scales;
-    const uint16_t* mins;
+    const void* mins;
+    const uint16_t* supers;
     int64_t rows, cols;
     const double* x;     /* decoded activations [K][cols] */
     int K;
@@ -140,7 +157,7 @@ static void* lin_worker(void* p) {
             double acc = 0.0, aacc = 0.0;
             const double* xk = J->x + (int64_t)k * J->cols;
             for (int64_t j = 0; j < J->cols; ++j) {
-                double t = or_weight(J->fmt, J->qs, J->scales, J->mins, J->cols, r, j) * xk[j];
+                double t = or_weight(J->fmt, J->qs, J->scales, J->mins, J->supers, J->cols, r, j) * xk[j];
                 acc += t;
                 aacc += fabs(t);
             }
@@ -151,10 +168,10 @@ static void* lin_worker(void* p) {
     return NULL;
 }
 
-int or_linear(int fmt, const uint8_t* qs, const void* scales, const uint16_t* mins,
-              int64_t rows, int64_t cols, const uint16_t* x_f16, int K,
+int or_linear(int fmt, const uint8_t* qs, const void* scales, const void* mins,
+              const uint16_t* supers, int64_t rows, int64_t cols, const uint16_t* x_f16, int K,
               double* y, double* a, int nthreads) {
-    if (cols % 32 || K < 1 || rows < 0) return -1;
+    if (cols % 32 || K < 1 || rows < 0 || (fmt == OR_FMT_Q4_K && cols % 256)) return -1;
     double* x = (double*)malloc(sizeof(double) * (size_t)K * (size_t)cols);
     if (!x) return -2;
     or_half_array(x_f16, x, (int64_t)K * cols);
@@ -164,7 +181,7 @@ int or_linear(int fmt, const uint8_t* qs, const void* scales, const uint16_t* mi
     pthread_t th[256];
     lin_job jobs[256];
     for (int t = 0; t < nthreads; ++t) {
-        lin_job J = {fmt, qs, scales, mins, rows, cols, x, K, y, a,
+        lin_job J = {fmt, qs, scales, mins, supers, rows, cols, x, K, y, a,
                      rows * t / nthreads, rows * (t + 1) / nthreads};
         jobs[t] = J;
     }
@@ -177,17 +194,17 @@ int or_linear(int fmt, const uint8_t* qs, const void* scales, const uint16_t* mi
 
 /* Same, with the activations given in double ([K][cols]), for inputs that are not fp16
  * values (the MX-quantised activations below). */
-int or_linear_x64(int fmt, const uint8_t* qs, const void* scales, const uint16_t* mins,
-                  int64_t rows, int64_t cols, const double* x, int K,
+int or_linear_x64(int fmt, const uint8_t* qs, const void* scales, const void* mins,
+                  const uint16_t* supers, int64_t rows, int64_t cols, const double* x, int K,
                   double* y, double* a, int nthreads) {
-    if (cols % 32 || K < 1 || rows < 0) return -1;
+    if (cols % 32 || K < 1 || rows < 0 || (fmt == OR_FMT_Q4_K && cols % 256)) return -1;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if (nthreads > rows) nthreads = rows > 0 ? (int)rows : 1;
     pthread_t th[256];
     lin_job jobs[256];
     for (int t = 0; t < nthreads; ++t) {
-        lin_job J = {fmt, qs, scales, mins, rows, cols, x, K, y, a,
+        lin_job J = {fmt, qs, scales, mins, supers, rows, cols, x, K, y, a,
                      rows * t / nthreads, rows * (t + 1) / nthreads};
         jobs[t] = J;
     }

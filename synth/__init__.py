@@ -27,8 +27,10 @@ import numpy as np
 FMT_Q4 = 0          # 4-bit code + fp16 block scale
 FMT_Q4_MIN = 1      # 4-bit code + fp16 block scale + fp16 block min
 FMT_MXFP4 = 2       # E2M1 code + E8M0 block scale
+FMT_Q4_K = 3        # unsigned 4-bit code, 6-bit sub-block scale and min, fp16 super-block d, dmin
 
 BLOCK = 32
+SUPER = 256         # weights per Q4_K super-block (eight blocks)
 ROW_CHUNK = 256     # rows per independently seeded chunk of a weight matrix
 
 _TAG_WEIGHT = 1
@@ -72,7 +74,8 @@ SHAPE_MINI = ModelShape(n_layers=2, hidden=256, kv_dim=64, ffn=512, vocab=1000)
 
 
 def bytes_per_weight(fmt: int) -> float:
-    return {FMT_Q4: 0.5 + 2 / 32, FMT_Q4_MIN: 0.5 + 4 / 32, FMT_MXFP4: 0.5 + 1 / 32}[fmt]
+    return {FMT_Q4: 0.5 + 2 / 32, FMT_Q4_MIN: 0.5 + 4 / 32, FMT_MXFP4: 0.5 + 1 / 32,
+            FMT_Q4_K: 0.5 + 2 / 32 + 4 / 256}[fmt]
 
 
 @dataclasses.dataclass
@@ -81,13 +84,23 @@ class Q4Matrix:
     rows: int
     cols: int
     qs: np.ndarray                 # uint8 [rows][cols/2]
-    scales: np.ndarray             # float16 (Q4) or uint8 E8M0 (MXFP4) [rows][cols/32]
-    mins: np.ndarray | None        # float16 [rows][cols/32] or None
+    scales: np.ndarray             # [rows][cols/32]: float16 (Q4, Q4_MIN), uint8 E8M0 (MXFP4),
+                                   # uint8 6-bit sub-block scale s (Q4_K)
+    mins: np.ndarray | None        # [rows][cols/32]: float16 (Q4_MIN), uint8 6-bit m (Q4_K), else None
+    supers: np.ndarray | None = None   # Q4_K: float16 [rows][cols/256][2] = (d, dmin)
 
     @property
     def nbytes(self) -> int:
         n = self.qs.nbytes + self.scales.nbytes
-        return n + (self.mins.nbytes if self.mins is not None else 0)
+        n += self.mins.nbytes if self.mins is not None else 0
+        return n + (self.supers.nbytes if self.supers is not None else 0)
+
+    def take(self, pick) -> "Q4Matrix":
+        """The listed rows, as a matrix of their own."""
+        pick = np.asarray(pick, dtype=np.int64)
+        return Q4Matrix(self.fmt, len(pick), self.cols, self.qs[pick], self.scales[pick],
+                        None if self.mins is None else self.mins[pick],
+                        None if self.supers is None else self.supers[pick])
 
 
 def _chunk_arrays(fmt: int, seed: int, layer: int, mat: int, chunk: int,
@@ -98,11 +111,19 @@ def _chunk_arrays(fmt: int, seed: int, layer: int, mat: int, chunk: int,
     if fmt == FMT_MXFP4:
         scales = rng.integers(119, 124, size=(nrows, nb), dtype=np.uint8)
         mins = None
+    elif fmt == FMT_Q4_K:
+        ns = cols // SUPER
+        d = rng.uniform(scale_lo, scale_hi, size=(nrows, ns)) / 32
+        dmin = d * rng.uniform(6.0, 12.0, size=(nrows, ns))
+        supers = np.stack([d, dmin], axis=-1).astype(np.float16)
+        scales = rng.integers(16, 64, size=(nrows, nb), dtype=np.uint8)
+        mins = rng.integers(0, 64, size=(nrows, nb), dtype=np.uint8)
+        return qs, scales, mins, supers
     else:
         scales = rng.uniform(scale_lo, scale_hi, size=(nrows, nb)).astype(np.float16)
         mins = (rng.uniform(-0.01, 0.01, size=(nrows, nb)).astype(np.float16)
                 if fmt == FMT_Q4_MIN else None)
-    return qs, scales, mins
+    return qs, scales, mins, None
 
 
 def weight_matrix(fmt: int, seed: int, layer: int, mat: int, rows: int, cols: int,
@@ -115,26 +136,36 @@ def weight_matrix(fmt: int, seed: int, layer: int, mat: int, rows: int, cols: in
     fp16 scales ~U(scale_lo, scale_hi), fp16 mins ~U(-0.01, 0.01).
     MXFP4: nibble bytes uniform (E2M1 codes uniform on 16 codes), E8M0 bytes uniform on
     {119..123}, i.e. block scales 2^-8 .. 2^-4.
+    Q4_K: nibble bytes uniform, super-block d ~ U(scale_lo, scale_hi) / 32 and
+    dmin = d * U(6, 12) (fp16), sub-block s uniform on 16..63 and m on 0..63: the
+    sub-block scale d*s spans the Q4 range and dmin*m sits near the middle of the
+    code range, so the weights are roughly centred.
     """
     if cols % BLOCK:
         raise ValueError("cols must be a multiple of 32")
+    if fmt == FMT_Q4_K and cols % SUPER:
+        raise ValueError("Q4_K cols must be a multiple of 256")
     row_end = rows if row_end is None else row_end
     c0, c1 = row_begin // ROW_CHUNK, (row_end + ROW_CHUNK - 1) // ROW_CHUNK
     nb = cols // BLOCK
     n = row_end - row_begin
     qs = np.empty((n, cols // 2), np.uint8)
-    scales = np.empty((n, nb), np.uint8 if fmt == FMT_MXFP4 else np.float16)
-    mins = np.empty((n, nb), np.float16) if fmt == FMT_Q4_MIN else None
+    scales = np.empty((n, nb), np.uint8 if fmt in (FMT_MXFP4, FMT_Q4_K) else np.float16)
+    mins = (np.empty((n, nb), np.float16) if fmt == FMT_Q4_MIN else
+            np.empty((n, nb), np.uint8) if fmt == FMT_Q4_K else None)
+    supers = np.empty((n, cols // SUPER, 2), np.float16) if fmt == FMT_Q4_K else None
 
     def work(ci: int):
         r0 = ci * ROW_CHUNK
         nr = min(ROW_CHUNK, rows - r0)
-        q, s, m = _chunk_arrays(fmt, seed, layer, mat, ci, nr, cols, scale_lo, scale_hi)
+        q, s, m, sp = _chunk_arrays(fmt, seed, layer, mat, ci, nr, cols, scale_lo, scale_hi)
         a, b = max(r0, row_begin), min(r0 + nr, row_end)
         qs[a - row_begin:b - row_begin] = q[a - r0:b - r0]
         scales[a - row_begin:b - row_begin] = s[a - r0:b - r0]
         if mins is not None:
             mins[a - row_begin:b - row_begin] = m[a - r0:b - r0]
+        if supers is not None:
+            supers[a - row_begin:b - row_begin] = sp[a - r0:b - r0]
 
     if threads > 1 and c1 - c0 > 1:
         with ThreadPoolExecutor(threads) as ex:
@@ -142,7 +173,7 @@ def weight_matrix(fmt: int, seed: int, layer: int, mat: int, rows: int, cols: in
     else:
         for ci in range(c0, c1):
             work(ci)
-    return Q4Matrix(fmt, n, cols, qs, scales, mins)
+    return Q4Matrix(fmt, n, cols, qs, scales, mins, supers)
 
 
 def weight_rows(fmt: int, seed: int, layer: int, mat: int, rows: int, cols: int,
@@ -153,7 +184,8 @@ def weight_rows(fmt: int, seed: int, layer: int, mat: int, rows: int, cols: int,
     return Q4Matrix(fmt, len(row_ids), cols,
                     np.concatenate([p.qs for p in parts]),
                     np.concatenate([p.scales for p in parts]),
-                    None if parts[0].mins is None else np.concatenate([p.mins for p in parts]))
+                    None if parts[0].mins is None else np.concatenate([p.mins for p in parts]),
+                    None if parts[0].supers is None else np.concatenate([p.supers for p in parts]))
 
 
 def activations(seed: int, K: int, cols: int, tag: int = 0) -> np.ndarray:

@@ -112,13 +112,86 @@ def test_mxfp4_values_exact_in_fp16():
         assert np.array_equal(v.astype(np.float16).astype(np.float64), v)
 
 
+def _q4k(rows, cols, codes, s, m, d, dmin):
+    """A Q4_K matrix from unsigned codes [rows][cols], sub-block s and m [rows][cols/32]
+    and super-block d, dmin [rows][cols/256]."""
+    n = np.asarray(codes, np.uint8)
+    qs = (n[:, 0::2] | (n[:, 1::2] << 4)).astype(np.uint8)
+    sup = np.stack([np.asarray(d, np.float64), np.asarray(dmin, np.float64)], axis=-1).astype(np.float16)
+    return synth.Q4Matrix(synth.FMT_Q4_K, rows, cols, qs, np.asarray(s, np.uint8), np.asarray(m, np.uint8), sup)
+
+
+def test_q4k_worked_example():
+    """The hand-computed worked example in tests/golden/q4k_worked_example.txt."""
+    codes = (np.arange(256) % 16)[None, :]
+    W = _q4k(1, 256, codes, [[1, 2, 3, 4, 5, 6, 7, 63]], [[0, 1, 2, 3, 4, 5, 6, 63]], [[0.5]], [[0.125]])
+    w = oracle.dequant(W)[0]
+    seen = 0
+    for line in _golden_rows("q4k_worked_example.txt"):
+        kind, idx, val = line.split()
+        idx, val = int(idx), float(val)
+        got = w[32 * idx:32 * idx + 32].sum() if kind == "sum" else w[idx]
+        assert got == val, (kind, idx, got, val)
+        seen += 1
+    assert seen == 13
+
+
+def test_q4k_super_block_index_and_roles():
+    """Two rows of two super-blocks, all codes 15, s = m = 1: where d = 1, dmin = 0 every
+    weight is 15, where d = 0, dmin = 1 it is -1; the roles swap between the rows."""
+    codes = np.full((2, 512), 15)
+    ones = np.ones((2, 16))
+    W = _q4k(2, 512, codes, ones, ones, [[1, 0], [0, 1]], [[0, 1], [1, 0]])
+    w = oracle.dequant(W)
+    assert np.all(w[0, :256] == 15) and np.all(w[0, 256:] == -1)
+    assert np.all(w[1, :256] == -1) and np.all(w[1, 256:] == 15)
+
+
+def test_q4k_reduces_to_q4_min():
+    """d*s*n - dmin*m = (d*s)*(n - 8) + (8*d*s - dmin*m): a Q4_K matrix equals the Q4_MIN
+    matrix with block scale d*s and block min 8*d*s - dmin*m, same codes.  With d, dmin in
+    {1..4}/1024 and s, m < 64 both are exact in fp16, so the two decodings agree exactly."""
+    rng = np.random.default_rng(11)
+    rows, cols = 7, 768
+    nb, ns = cols // 32, cols // 256
+    codes = rng.integers(0, 16, size=(rows, cols))
+    s = rng.integers(0, 64, size=(rows, nb))
+    m = rng.integers(0, 64, size=(rows, nb))
+    d = rng.integers(1, 5, size=(rows, ns)) / 1024.0
+    dmin = rng.integers(1, 5, size=(rows, ns)) / 1024.0
+    K = _q4k(rows, cols, codes, s, m, d, dmin)
+    ds = np.repeat(d, 8, axis=1) * s
+    mm = 8 * ds - np.repeat(dmin, 8, axis=1) * m
+    assert np.array_equal(ds.astype(np.float16).astype(np.float64), ds)
+    assert np.array_equal(mm.astype(np.float16).astype(np.float64), mm)
+    M = synth.Q4Matrix(synth.FMT_Q4_MIN, rows, cols, K.qs, ds.astype(np.float16), mm.astype(np.float16))
+    assert np.array_equal(oracle.dequant(K), oracle.dequant(M))
+
+
+def test_q4k_synthetic_weights_are_centred():
+    """The generator's Q4_K weights: s in 16..63, m in 0..63, mean weight small beside the spread."""
+    W = synth.weight_matrix(synth.FMT_Q4_K, 3, 0, 0, 64, 1024)
+    assert W.scales.min() >= 16 and W.scales.max() <= 63 and W.mins.max() <= 63
+    w = oracle.dequant(W)
+    assert abs(w.mean()) < 0.1 * w.std()
+
+
+def test_q4k_rejects_cols_not_multiple_of_256():
+    W = synth.Q4Matrix(synth.FMT_Q4_K, 1, 32, np.zeros((1, 16), np.uint8), np.zeros((1, 1), np.uint8),
+                       np.zeros((1, 1), np.uint8), np.zeros((1, 1, 2), np.float16))
+    with pytest.raises(ValueError):
+        oracle.linear(W, np.zeros((1, 32), np.float16))
+
+
 # ------------------------------------------------------------------ linear
 
 def _small_matrix(fmt=synth.FMT_Q4_MIN, rows=40, cols=128, seed=7):
+    if fmt == synth.FMT_Q4_K:
+        cols = 512
     return synth.weight_matrix(fmt, seed, 0, 0, rows, cols)
 
 
-@pytest.mark.parametrize("fmt", [synth.FMT_Q4, synth.FMT_Q4_MIN, synth.FMT_MXFP4])
+@pytest.mark.parametrize("fmt", [synth.FMT_Q4, synth.FMT_Q4_MIN, synth.FMT_MXFP4, synth.FMT_Q4_K])
 def test_linear_vs_numpy_matmul(fmt):
     """W x agrees with numpy's float64 matmul of the dequantised matrix (library routine)."""
     W = _small_matrix(fmt)
@@ -532,7 +605,7 @@ def test_k1_is_plain_decode():
 
 # ------------------------------------------------ tolerance base and near-threshold flags
 
-@pytest.mark.parametrize("fmt", [synth.FMT_Q4, synth.FMT_Q4_MIN, synth.FMT_MXFP4])
+@pytest.mark.parametrize("fmt", [synth.FMT_Q4, synth.FMT_Q4_MIN, synth.FMT_MXFP4, synth.FMT_Q4_K])
 def test_tolerance_base_is_sum_of_abs_products(fmt):
     """a[k][r] = sum_j |w_rj x_kj| exactly (numpy on the dequantised matrix), so that the
     parity bound 1e-3 * a is neither loosened (e.g. sum|w| * sum|x|) nor tightened."""
