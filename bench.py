@@ -292,6 +292,32 @@ def bench_depth(torch, vq, model, dev, H, V, args):
     return res
 
 
+def bench_q4k(torch, vq, synth, dev, args):
+    """The decode pass over the 27B-class stack with Q4_K super-block weights (4.625 bits per
+    weight in the tiled layout) at K = 1 and 8: one graph-replayed pass, as the headline."""
+    shape = synth.SHAPE_27B
+    H, V = shape.hidden, shape.vocab
+    model = upload_stack(vq, synth, synth.FMT_Q4_K, 0, args.threads)
+    nbytes = model.nbytes
+    assert nbytes == shape.n_weights() * 37 // 64
+    res = {"workload": "27b-q4k-decode", "format": "q4_k: 256-weight super-blocks, 6-bit sub-block "
+           "scale and min, fp16 d and dmin", "weight_bytes": nbytes}
+    for K in (1, 8):
+        x0 = torch.from_numpy(synth.activations(0, K, H)).to(dev)
+        logits = torch.empty((K, V), dtype=torch.float32, device=dev)
+        ws = torch.empty(model.workspace_bytes(K), dtype=torch.uint8, device=dev)
+        ms = time_graph(torch, lambda: vq.decode_pass(model, x0, logits, ws=ws), args.steps, args.warmup)[0]
+        assert model.barrier_error(K, ws) == 0, "a grid wait of the pass timed out"
+        gbps = nbytes / ms / 1e6
+        res[f"K{K}"] = {"ms_per_step": round(ms, 4), "gbps": round(gbps, 2),
+                        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "passes_per_s": round(1000 / ms, 2)}
+        del ws, logits, x0
+    res["k8_over_k1"] = round(res["K8"]["ms_per_step"] / res["K1"]["ms_per_step"], 3)
+    del model
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_ngram(vq, synth, t_pass=None, n_tokens=100000, max_drafts=8):
     """The n-gram map drafter on a synthetic code-like stream (synth.token_stream, 100,000
     tokens) replayed as the target's output: per window the map proposes up to 8 drafts,
@@ -381,6 +407,7 @@ def main():
     ap.add_argument("--no-attn", action="store_true", help="skip timing the attention over the KV cache")
     ap.add_argument("--no-depth", action="store_true", help="skip the adaptive draft depth measurement")
     ap.add_argument("--no-ngram", action="store_true", help="skip the n-gram drafter measurement")
+    ap.add_argument("--no-q4k", action="store_true", help="skip the pass over Q4_K super-block weights")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first copy 1 GiB with torch (the known-size kernel that scales HBM counters)")
     args = ap.parse_args()
@@ -627,6 +654,12 @@ def main():
             "per_shape": per_shape}
         log("K=16", sweep["K16"])
     out["sweep"] = sweep
+    if not args.no_q4k:
+        if 16 not in Ks:
+            del model
+            torch.cuda.empty_cache()
+        out["q4_k"] = bench_q4k(torch, vq, synth, dev, args)
+        log("Q4_K", out["q4_k"])
 
     # ---------------------------------------------------------- attention (next row)
     if not args.no_attn:

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define VQ_ABI_VERSION 4
+#define VQ_ABI_VERSION 5
 
 /* ------------------------------------------------------------------ status */
 #define VQ_OK 0
@@ -61,14 +61,22 @@ extern "C" {
  *   VQ_FMT_Q4      : code n in 0..15, q = n - 8, w = d * q          (d: fp16 scale)
  *   VQ_FMT_Q4_MIN  : w = d * q + m                                   (m: fp16 block min)
  *   VQ_FMT_MXFP4   : w = e2m1(n) * 2^(E - 127)  (OCP Microscaling v1.0: E2M1 code, E8M0 E)
- *   scales : fp16 [rows][cols/32] (Q4, Q4_MIN) or uint8 E8M0 [rows][cols/32] (MXFP4)
- *   mins   : fp16 [rows][cols/32] for Q4_MIN, NULL otherwise
- * Alignment: qs 16-byte aligned; scales and mins 16-byte aligned.
+ *   VQ_FMT_Q4_K    : K-quant super-blocks of 256 columns (8 blocks): unsigned code n,
+ *                    w = D * s * n - Dmin * m  (s, m: the block's 6-bit scale and min,
+ *                    D, Dmin: the super-block's fp16 scale and min scale); cols % 256 == 0
+ *   scales : fp16 [rows][cols/32] (Q4, Q4_MIN), uint8 E8M0 [rows][cols/32] (MXFP4),
+ *            uint8 s [rows][cols/32] (Q4_K; K-quant encoders use 0..63, any byte decodes)
+ *   mins   : fp16 [rows][cols/32] for Q4_MIN, uint8 m [rows][cols/32] for Q4_K, NULL
+ *            otherwise
+ *   supers : fp16 pairs (D, Dmin) [rows][cols/256][2] for Q4_K, NULL otherwise
+ * Alignment: qs, scales, mins and supers 16-byte aligned.
  * The pages name 4-bit block formats (Q4_K_M, UD-Q4_K_XL, q4_0) and MXFP4 without
- * defining them; this is the block-32 layout the library implements. */
+ * defining them; these are the layouts the library implements (Q4_K: the public GGML
+ * K-quant arithmetic, with one byte per 6-bit value instead of its packed 12 bytes). */
 #define VQ_FMT_Q4 0
 #define VQ_FMT_Q4_MIN 1
 #define VQ_FMT_MXFP4 2
+#define VQ_FMT_Q4_K 3
 
 typedef struct vq_matrix {
     int32_t format;       /* VQ_FMT_*                                   */
@@ -78,6 +86,7 @@ typedef struct vq_matrix {
     const void* qs;       /* device */
     const void* scales;   /* device */
     const void* mins;     /* device or NULL */
+    const void* supers;   /* device (Q4_K) or NULL */
 } vq_matrix;
 
 /* --------------------------------------------------------------- tiled layout */

@@ -25,7 +25,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libvq.so")
 
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_HOST = 0, -1, -2, -3, -4, -5
-FMT_Q4, FMT_Q4_MIN, FMT_MXFP4 = 0, 1, 2
+FMT_Q4, FMT_Q4_MIN, FMT_MXFP4, FMT_Q4_K = 0, 1, 2, 3
+ABI_VERSION = 5            # the structs below mirror include/vq.h at this version
 DTYPE_F32, DTYPE_F16 = 0, 1
 LAUNCH_AUTO, LAUNCH_STAGED, LAUNCH_PERSISTENT = 0, 4, 8
 ROWS_PLAIN, ROWS_PAIR8 = 0, 1
@@ -40,7 +41,7 @@ _P = ctypes.c_void_p
 
 class VqMatrix(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("qs", _P), ("scales", _P), ("mins", _P)]
+                ("reserved", ctypes.c_int32), ("qs", _P), ("scales", _P), ("mins", _P), ("supers", _P)]
 
 
 class VqTiled(ctypes.Structure):
@@ -136,6 +137,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.vq_last_error.argtypes = []
     L.vq_abi_version.restype = I32
     L.vq_abi_version.argtypes = []
+    if L.vq_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} has ABI version {L.vq_abi_version()}, this binding needs "
+                          f"{ABI_VERSION}; rebuild it")
     return L
 
 
@@ -173,28 +177,28 @@ def _empty(nbytes: int, device):
 class DeviceMatrix:
     """A block-quantised matrix in device memory in the plain planes (torch tensors)."""
 
-    def __init__(self, fmt: int, rows: int, cols: int, qs, scales, mins=None):
+    def __init__(self, fmt: int, rows: int, cols: int, qs, scales, mins=None, supers=None):
         self.fmt, self.rows, self.cols = fmt, rows, cols
-        self.qs, self.scales, self.mins = qs, scales, mins
-        self.desc = VqMatrix(fmt, rows, cols, 0, _ptr(qs), _ptr(scales), _ptr(mins))
+        self.qs, self.scales, self.mins, self.supers = qs, scales, mins, supers
+        self.desc = VqMatrix(fmt, rows, cols, 0, _ptr(qs), _ptr(scales), _ptr(mins), _ptr(supers))
         self._tiled = None
 
     @classmethod
     def from_host(cls, m, device="cuda"):
         """Upload a synth.Q4Matrix (numpy arrays)."""
         import torch
-        qs = torch.from_numpy(np.ascontiguousarray(m.qs)).to(device)
-        sc = np.ascontiguousarray(m.scales)
-        scales = torch.from_numpy(sc.view(np.uint16) if sc.dtype == np.float16 else sc).to(device)
-        mins = None
-        if m.mins is not None:
-            mins = torch.from_numpy(np.ascontiguousarray(m.mins).view(np.uint16)).to(device)
-        return cls(m.fmt, m.rows, m.cols, qs, scales, mins)
+
+        def up(a):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(a)
+            return torch.from_numpy(a.view(np.uint16) if a.dtype == np.float16 else a).to(device)
+        return cls(m.fmt, m.rows, m.cols, up(m.qs), up(m.scales), up(m.mins), up(getattr(m, "supers", None)))
 
     @property
     def nbytes(self) -> int:
-        n = self.qs.numel() + self.scales.numel() * self.scales.element_size()
-        return n + (0 if self.mins is None else self.mins.numel() * 2)
+        return sum(t.numel() * t.element_size() for t in (self.qs, self.scales, self.mins, self.supers)
+                   if t is not None)
 
     @property
     def tiled(self) -> "DeviceTiled":
@@ -205,7 +209,7 @@ class DeviceMatrix:
         return self._tiled
 
     def drop_planes(self):
-        self.qs = self.scales = self.mins = None
+        self.qs = self.scales = self.mins = self.supers = None
 
 
 class DeviceTiled:

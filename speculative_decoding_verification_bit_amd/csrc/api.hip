@@ -37,30 +37,38 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_matrix(const vq_matrix* W, const char* name) {
     if (!W) return fail(VQ_ERR_ARG, "%s: NULL matrix descriptor", name);
-    if (W->format < VQ_FMT_Q4 || W->format > VQ_FMT_MXFP4)
+    if (W->format < VQ_FMT_Q4 || W->format > VQ_FMT_Q4_K)
         return fail(VQ_ERR_ARG, "%s: unknown format %d", name, W->format);
     if (W->reserved != 0) return fail(VQ_ERR_ARG, "%s: reserved field must be 0", name);
     if (W->rows < 0) return fail(VQ_ERR_ARG, "%s: rows %d < 0", name, W->rows);
     if (W->cols <= 0 || W->cols % 32)
         return fail(VQ_ERR_ARG, "%s: cols %d is not a positive multiple of 32", name, W->cols);
+    if (W->format == VQ_FMT_Q4_K && W->cols % 256)
+        return fail(VQ_ERR_ARG, "%s: VQ_FMT_Q4_K needs cols %% 256 == 0 (cols %d)", name, W->cols);
     if (W->rows == 0) return VQ_OK;
     if (!W->qs || !W->scales) return fail(VQ_ERR_ARG, "%s: NULL qs or scales", name);
-    if ((W->format == VQ_FMT_Q4_MIN) != (W->mins != nullptr))
-        return fail(VQ_ERR_ARG, "%s: mins must be given exactly for VQ_FMT_Q4_MIN", name);
-    if (!aligned(W->qs, 16) || !aligned(W->scales, 16) || (W->mins && !aligned(W->mins, 16)))
-        return fail(VQ_ERR_ARG, "%s: qs, scales and mins must be 16-byte aligned", name);
+    const bool has_mins = W->format == VQ_FMT_Q4_MIN || W->format == VQ_FMT_Q4_K;
+    if (has_mins != (W->mins != nullptr))
+        return fail(VQ_ERR_ARG, "%s: mins must be given exactly for VQ_FMT_Q4_MIN and VQ_FMT_Q4_K", name);
+    if ((W->format == VQ_FMT_Q4_K) != (W->supers != nullptr))
+        return fail(VQ_ERR_ARG, "%s: supers must be given exactly for VQ_FMT_Q4_K", name);
+    if (!aligned(W->qs, 16) || !aligned(W->scales, 16) || (W->mins && !aligned(W->mins, 16)) ||
+        (W->supers && !aligned(W->supers, 16)))
+        return fail(VQ_ERR_ARG, "%s: qs, scales, mins and supers must be 16-byte aligned", name);
     return VQ_OK;
 }
 
 int check_tiled(const vq_tiled* W, const char* name) {
     if (!W) return fail(VQ_ERR_ARG, "%s: NULL matrix descriptor", name);
-    if (W->format < VQ_FMT_Q4 || W->format > VQ_FMT_MXFP4)
+    if (W->format < VQ_FMT_Q4 || W->format > VQ_FMT_Q4_K)
         return fail(VQ_ERR_ARG, "%s: unknown format %d", name, W->format);
     if (W->order != VQ_ROWS_PLAIN && W->order != VQ_ROWS_PAIR8)
         return fail(VQ_ERR_ARG, "%s: unknown row order %d", name, W->order);
     if (W->rows < 0) return fail(VQ_ERR_ARG, "%s: rows %d < 0", name, W->rows);
     if (W->cols <= 0 || W->cols % 32)
         return fail(VQ_ERR_ARG, "%s: cols %d is not a positive multiple of 32", name, W->cols);
+    if (W->format == VQ_FMT_Q4_K && W->cols % 256)
+        return fail(VQ_ERR_ARG, "%s: VQ_FMT_Q4_K needs cols %% 256 == 0 (cols %d)", name, W->cols);
     if (W->order == VQ_ROWS_PAIR8 && W->rows % 16)
         return fail(VQ_ERR_ARG, "%s: a VQ_ROWS_PAIR8 matrix needs rows %% 16 == 0 (rows %d)", name, W->rows);
     if (tiled_bytes(W->format, W->rows, W->cols) >= ((size_t)1 << 32))
@@ -495,7 +503,8 @@ size_t vq_workspace_bytes(int32_t op, const void* desc, int32_t K) {
 }
 
 size_t vq_tiled_bytes(int32_t format, int32_t rows, int32_t cols) {
-    if (format < VQ_FMT_Q4 || format > VQ_FMT_MXFP4 || rows < 0 || cols <= 0 || cols % 32) return 0;
+    if (format < VQ_FMT_Q4 || format > VQ_FMT_Q4_K || rows < 0 || cols <= 0 || cols % 32) return 0;
+    if (format == VQ_FMT_Q4_K && cols % 256) return 0;
     return tiled_bytes(format, rows, cols);
 }
 

@@ -285,8 +285,9 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         // ============================================================ compute waves
         const int cw = wave;
         using scale_t = typename std::conditional<FMT == VQ_FMT_Q4_MIN, u4_t,
-                        typename std::conditional<FMT == VQ_FMT_Q4, u2_t, uint32_t>::type>::type;
-        constexpr int SB = FMT == VQ_FMT_Q4_MIN ? 16 : FMT == VQ_FMT_Q4 ? 8 : 4;
+                        typename std::conditional<FMT == VQ_FMT_Q4 || FMT == VQ_FMT_Q4_K, u2_t,
+                                                  uint32_t>::type>::type;
+        constexpr int SB = FMT == VQ_FMT_Q4_MIN ? 16 : FMT == VQ_FMT_Q4 || FMT == VQ_FMT_Q4_K ? 8 : 4;
         const int xoff1 = A.xoff1;
         uint8_t* const ring = lds + A.ring_off;
 
@@ -332,9 +333,10 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
 
         // One step: two chunks (groups 2g, 2g + 1 of a tile), each 1 KB of codes and the
         // rows' scales; the second chunk follows the first.
-        constexpr int CB1 = FMT == VQ_FMT_Q4_MIN ? 1280 : FMT == VQ_FMT_Q4 ? 1152 : 1088;
+        constexpr int CB1 = FMT == VQ_FMT_Q4_MIN ? 1280 : FMT == VQ_FMT_Q4 ? 1152 : FMT == VQ_FMT_Q4_K ? 1184 : 1088;
         u4_t rq[DEPTH][2];
         scale_t rs[DEPTH][2];
+        uint32_t rk[DEPTH][2];             // Q4_K: the row's super-block D (h = 0) and Dmin (h = 1)
         // every entry names a chunk in its matrix, with or without ST_VALID: the loads are
         // unconditional, so that the wait counts of the unrolled rounds are exact
         auto issue = [&](int u, uint32_t off, uint32_t f) __attribute__((always_inline)) {
@@ -349,6 +351,7 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             for (int h = 0; h < 2; ++h) {
                 rq[u][h] = ld_global_nt<u4_t>(p + h * CB1 + 16 * lane);
                 rs[u][h] = ld_global_nt<scale_t>(p + h * CB1 + 1024 + SB * n16);
+                if constexpr (FMT == VQ_FMT_Q4_K) rk[u][h] = ld_global_nt<uint16_t>(p + h * CB1 + 1152 + 2 * n16);
             }
         };
 
@@ -361,15 +364,17 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         // Eight codes -> the MFMA B operand (8 fp16 in column order; the tiled layout stores
         // the Q4 nibbles so that this order comes out).  A nibble OR-ed into the mantissa of
         // 1024.0 gives 1024 + n (low nibbles) or 1024 + 16 n (high nibbles); both map
-        // exactly to n - 8.
+        // exactly to n - 8 (Q4, Q4_MIN) or to n (Q4_K, whose codes are unsigned).
         auto widen = [&](uint32_t w) __attribute__((always_inline)) -> h8_t {
             if constexpr (FMT == VQ_FMT_MXFP4) {
                 return widen8<FMT>(w);
             } else {
+                constexpr float lo_off = FMT == VQ_FMT_Q4_K ? 1024.0f : 1032.0f;
+                constexpr float hi_off = FMT == VQ_FMT_Q4_K ? -64.0f : -72.0f;
                 const uint32_t w8 = w >> 8;
-                const h2_t k1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+                const h2_t k1032 = {(_Float16)lo_off, (_Float16)lo_off};
                 const h2_t k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
-                const h2_t k72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+                const h2_t k72 = {(_Float16)hi_off, (_Float16)hi_off};
                 const h2_t p0 = as_h2((w & m_lo) | magic) - k1032;
                 const h2_t p1 = as_h2((w & m_hi) | magic) * k16 + k72;
                 const h2_t p2 = as_h2((w8 & m_lo) | magic) - k1032;
@@ -400,6 +405,13 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
                 xlane = (uint32_t)(mrow * uni(A.kp[kind_of(A, A.s_begin + idx)].xs) + 16 * q4);
             }
             const uint32_t xa = xlane + ((f & ST_XOFF_MASK) << 4);
+            // Q4_K: the step is one super-block of the row; D * s and Dmin * m are exact in
+            // fp32 (an fp16 times a byte)
+            float kd = 0.f, kdm = 0.f;
+            if constexpr (FMT == VQ_FMT_Q4_K) {
+                kd = half_bits_to_float(rk[u][0]);
+                kdm = -half_bits_to_float(rk[u][1]);
+            }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 h8_t a[4];
@@ -414,12 +426,16 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
                     const f4_t cj = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], b, z, 0, 0, 0);
                     float d;
                     if constexpr (FMT == VQ_FMT_MXFP4) d = e8m0_to_float((sc >> (8 * j)) & 0xffu);
+                    else if constexpr (FMT == VQ_FMT_Q4_K) d = kd * (float)((sc[0] >> (8 * j)) & 0xffu);
                     else d = half_bits_to_float((sc[j >> 1] >> ((j & 1) * 16)) & 0xffffu);
 #pragma unroll
                     for (int i = 0; i < NF; ++i) acc[i] = __builtin_fmaf(d, cj[i], acc[i]);
-                    if constexpr (FMT == VQ_FMT_Q4_MIN) {
+                    if constexpr (FMT == VQ_FMT_Q4_MIN || FMT == VQ_FMT_Q4_K) {
+                        // the block's min term: (sum of the column's activations) * min
                         const f4_t sj = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], ONES, z, 0, 0, 0);
-                        const float mm = half_bits_to_float((sc[2 + (j >> 1)] >> ((j & 1) * 16)) & 0xffffu);
+                        float mm;
+                        if constexpr (FMT == VQ_FMT_Q4_K) mm = kdm * (float)((sc[1] >> (8 * j)) & 0xffu);
+                        else mm = half_bits_to_float((sc[2 + (j >> 1)] >> ((j & 1) * 16)) & 0xffffu);
 #pragma unroll
                         for (int i = 0; i < NF; ++i) acc[i] = __builtin_fmaf(mm, sj[i], acc[i]);
                     }
@@ -803,7 +819,9 @@ __global__ void k_tile(vq_matrix W, uint8_t* dst, int dst_rows, int order, int r
     const int nb = W.cols / 32;
     uint8_t* chunk = dst + ((size_t)t * G + g) * cb;
     u4_t codes = {0u, 0u, 0u, 0u};
-    uint16_t sc[4] = {0, 0, 0, 0}, mn[4] = {0, 0, 0, 0};
+    uint32_t sc[4] = {0, 0, 0, 0}, mn[4] = {0, 0, 0, 0};
+    uint32_t sup = 0;
+    const bool bytes = W.format == VQ_FMT_MXFP4 || W.format == VQ_FMT_Q4_K;   // one-byte scales
     if (mine) {
         const uint8_t* qs = (const uint8_t*)W.qs + (size_t)sr * (W.cols / 2);
 #pragma unroll
@@ -812,11 +830,16 @@ __global__ void k_tile(vq_matrix W, uint8_t* dst, int dst_rows, int order, int r
             if (b < nb) {
                 const uint32_t v = *(const uint32_t*)(qs + 16 * b + 4 * q);
                 codes[j] = W.format == VQ_FMT_MXFP4 ? v : q4_to_pair_order(v);
-                if (W.format == VQ_FMT_MXFP4) sc[j] = ((const uint8_t*)W.scales)[(size_t)sr * nb + b];
+                if (bytes) sc[j] = ((const uint8_t*)W.scales)[(size_t)sr * nb + b];
                 else sc[j] = ((const uint16_t*)W.scales)[(size_t)sr * nb + b];
                 if (W.format == VQ_FMT_Q4_MIN) mn[j] = ((const uint16_t*)W.mins)[(size_t)sr * nb + b];
+                if (W.format == VQ_FMT_Q4_K) mn[j] = ((const uint8_t*)W.mins)[(size_t)sr * nb + b];
             }
         }
+        // Q4_K: cols % 256 == 0, so group g lies in super-block g / 2 of the row; the even
+        // group's chunk carries its D, the odd group's its Dmin
+        if (W.format == VQ_FMT_Q4_K)
+            sup = ((const uint16_t*)W.supers)[((size_t)sr * (W.cols / 256) + g / 2) * 2 + (g & 1)];
     }
     *(u4_t*)(chunk + 16 * l) = codes;
     if (q == 0) {
@@ -827,6 +850,11 @@ __global__ void k_tile(vq_matrix W, uint8_t* dst, int dst_rows, int order, int r
         } else if (W.format == VQ_FMT_Q4) {
             const u2_t v = {sc[0] | ((uint32_t)sc[1] << 16), sc[2] | ((uint32_t)sc[3] << 16)};
             *(u2_t*)(s + 8 * n) = v;
+        } else if (W.format == VQ_FMT_Q4_K) {
+            const u2_t v = {sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24),
+                            mn[0] | (mn[1] << 8) | (mn[2] << 16) | (mn[3] << 24)};
+            *(u2_t*)(s + 8 * n) = v;
+            *(uint16_t*)(s + 128 + 2 * n) = (uint16_t)sup;
         } else {
             const u4_t v = {sc[0] | ((uint32_t)sc[1] << 16), sc[2] | ((uint32_t)sc[3] << 16),
                             mn[0] | ((uint32_t)mn[1] << 16), mn[2] | ((uint32_t)mn[3] << 16)};
@@ -887,6 +915,7 @@ hipError_t launch_flow(const FlowArgs& A, hipStream_t st) {
     switch (A.fmt) {
         case VQ_FMT_Q4: return launch_f<VQ_FMT_Q4>(A, st);
         case VQ_FMT_Q4_MIN: return launch_f<VQ_FMT_Q4_MIN>(A, st);
+        case VQ_FMT_Q4_K: return launch_f<VQ_FMT_Q4_K>(A, st);
         default: return launch_f<VQ_FMT_MXFP4>(A, st);
     }
 }

@@ -21,16 +21,18 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //                  of row n, nibble p holding column 8q + kPairSrc[p] (so that the Q4
 //                  widening yields natural column order); MXFP4 keeps natural nibbles
 //   scales       : per row n, the 4 block scales of the group (fp16: 8 B, E8M0: 4 B),
-//                  and for Q4 with mins the 4 fp16 mins after them (16 B per row)
+//                  and for Q4 with mins the 4 fp16 mins after them (16 B per row);
+//                  Q4_K: per row n at 8n the 4 blocks' scale bytes s then their 4 min
+//                  bytes m, and at 128 + 2n one fp16 of the row's super-block (the
+//                  two groups of a step): D in the even group's chunk, Dmin in the odd
 // Rows past the matrix and blocks past its columns are zero (codes, scales and mins), so
 // they contribute exactly 0.
 constexpr int TILE_ROWS = 16;
 constexpr int GROUP_COLS = 128;
 constexpr int STEP_COLS = 2 * GROUP_COLS;   // columns of one step of the streaming kernel
 inline int chunk_bytes(int fmt) {
-    return 1024 + (fmt == VQ_FMT_Q4_MIN ? 256 : fmt == VQ_FMT_Q4 ? 128 : 64);
+    return 1024 + (fmt == VQ_FMT_Q4_MIN ? 256 : fmt == VQ_FMT_Q4 ? 128 : fmt == VQ_FMT_Q4_K ? 160 : 64);
 }
-inline int row_scale_bytes(int fmt) { return (chunk_bytes(fmt) - 1024) / 16; }
 inline size_t tiled_bytes(int fmt, int rows, int cols) {
     const size_t T = (size_t)(rows + TILE_ROWS - 1) / TILE_ROWS;
     const size_t G = 2 * ((size_t)(cols + STEP_COLS - 1) / STEP_COLS);

@@ -40,8 +40,9 @@ def test_status_strings():
     assert vq.lib.vq_status_string(-99) == b"unknown status"
 
 
-def _mat(fmt=vq.FMT_Q4_MIN, rows=64, cols=256, qs=FAKE, scales=FAKE, mins=FAKE):
-    return vq.VqMatrix(fmt, rows, cols, 0, qs, scales, mins if fmt == vq.FMT_Q4_MIN else None)
+def _mat(fmt=vq.FMT_Q4_MIN, rows=64, cols=256, qs=FAKE, scales=FAKE, mins=FAKE, supers=FAKE):
+    return vq.VqMatrix(fmt, rows, cols, 0, qs, scales, mins if fmt in (vq.FMT_Q4_MIN, vq.FMT_Q4_K) else None,
+                       supers if fmt == vq.FMT_Q4_K else None)
 
 
 def _til(fmt=vq.FMT_Q4_MIN, rows=64, cols=256, order=vq.ROWS_PLAIN, data=FAKE):
@@ -73,8 +74,8 @@ def test_linear_argument_errors(kw, code):
 
 
 @pytest.mark.parametrize("W", [
-    _til(cols=48), _til(cols=0), _til(rows=-1), _til(fmt=3), _til(data=None), _til(data=FAKE + 16),
-    _til(order=2), _til(order=vq.ROWS_PAIR8),
+    _til(cols=48), _til(cols=0), _til(rows=-1), _til(fmt=4), _til(fmt=-1), _til(data=None), _til(data=FAKE + 16),
+    _til(order=2), _til(order=vq.ROWS_PAIR8), _til(fmt=vq.FMT_Q4_K, cols=384),
 ])
 def test_linear_bad_matrix(W):
     assert _lin(W) == vq.ERR_ARG
@@ -99,6 +100,15 @@ def test_linear_workspace_is_small_and_exact():
 
 
 def test_tiled_bytes():
+    # Q4_K: per row of a 128-column group 8 bytes of 6-bit scales and mins, and one fp16
+    # of its super-block (D in the even group, Dmin in the odd): 1024 + 16 * 10 bytes
+    per = 1184
+    assert vq.lib.vq_tiled_bytes(vq.FMT_Q4_K, 16, 256) == 2 * per
+    assert vq.lib.vq_tiled_bytes(vq.FMT_Q4_K, 77, 1024) == 5 * 8 * per
+    assert vq.lib.vq_tiled_bytes(vq.FMT_Q4_K, 5120, 17408) == 320 * 136 * per
+    assert vq.lib.vq_tiled_bytes(vq.FMT_Q4_K, 5120, 5120) == 5120 * 5120 * 37 // 64   # 4.625 bits
+    for cols in (128, 288, 1056):
+        assert vq.lib.vq_tiled_bytes(vq.FMT_Q4_K, 16, cols) == 0
     for fmt, per in ((vq.FMT_Q4, 1152), (vq.FMT_Q4_MIN, 1280), (vq.FMT_MXFP4, 1088)):
         # groups of 128 columns come in pairs (one step of the streaming kernel)
         assert vq.lib.vq_tiled_bytes(fmt, 16, 128) == 2 * per
@@ -109,7 +119,7 @@ def test_tiled_bytes():
         # every weight's 4 bits and its block's scale (and min) are stored once, no more
         if fmt == vq.FMT_Q4_MIN:
             assert vq.lib.vq_tiled_bytes(fmt, 5120, 5120) == 5120 * 5120 * 5 // 8
-    assert vq.lib.vq_tiled_bytes(3, 16, 128) == 0
+    assert vq.lib.vq_tiled_bytes(4, 16, 128) == 0
     assert vq.lib.vq_tiled_bytes(vq.FMT_Q4, 16, 100) == 0
     assert vq.lib.vq_tiled_bytes(vq.FMT_Q4, -1, 128) == 0
 
@@ -129,6 +139,19 @@ def test_tile_argument_errors():
     assert _tile(_mat(rows=32), _til(rows=64, order=vq.ROWS_PAIR8), 16) == vq.ERR_ARG
     assert _tile(_mat(rows=16), _til(rows=64, data=None)) == vq.ERR_ARG
     assert _tile(_mat(rows=16, qs=None), _til(rows=64)) == vq.ERR_ARG
+
+
+def test_tile_q4k_planes():
+    """Q4_K takes exactly qs, scales, mins and supers, with cols a multiple of 256."""
+    K = vq.FMT_Q4_K
+    dst = _til(fmt=K, rows=64)
+    assert _tile(_mat(fmt=K, rows=16, supers=None), dst) == vq.ERR_ARG
+    assert _tile(_mat(fmt=K, rows=16, mins=None), dst) == vq.ERR_ARG
+    assert _tile(_mat(fmt=K, rows=16, supers=FAKE + 8), dst) == vq.ERR_ARG
+    assert _tile(_mat(fmt=K, rows=16, cols=384), _til(fmt=K, rows=64, cols=384)) == vq.ERR_ARG
+    bad = vq.VqMatrix(vq.FMT_Q4_MIN, 16, 256, 0, FAKE, FAKE, FAKE, FAKE)   # supers on another format
+    assert _tile(bad, _til(rows=64)) == vq.ERR_ARG
+    assert _tile(_mat(fmt=K, rows=0, qs=None, scales=None, mins=None, supers=None), dst) == vq.OK
 
 
 def _acc(**kw):

@@ -30,10 +30,9 @@ def _stage_mats(shape, fmt, seed, stage, rows_pick=None):
     qs = np.concatenate([m.qs for m in mats])
     sc = np.concatenate([m.scales for m in mats])
     mn = None if mats[0].mins is None else np.concatenate([m.mins for m in mats])
-    if rows_pick is not None:
-        qs, sc = qs[rows_pick], sc[rows_pick]
-        mn = None if mn is None else mn[rows_pick]
-    return synth.Q4Matrix(fmt, qs.shape[0], mats[0].cols, qs, sc, mn)
+    sp = None if mats[0].supers is None else np.concatenate([m.supers for m in mats])
+    full = synth.Q4Matrix(fmt, qs.shape[0], mats[0].cols, qs, sc, mn, sp)
+    return full if rows_pick is None else full.take(rows_pick)
 
 
 def _stage_io(model, shape, K, ws, logits, stage):
@@ -121,7 +120,7 @@ def _every_stage(shape, seed, fmt, K):
     assert np.isfinite(lp.cpu().numpy()).all()
 
 
-@pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_MXFP4])
+@pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_MXFP4, synth.FMT_Q4_K])
 @pytest.mark.parametrize("K", [1, 2, 3, 4, 8, 16])
 def test_mini_model_every_stage(fmt, K):
     """A 2-layer stack (hidden 256, kv 64, ffn 512, vocab 1000): all rows of all stages."""
@@ -156,7 +155,8 @@ def test_deep_model_across_launches():
     assert np.array_equal(lp.cpu().numpy(), ls.cpu().numpy())
 
 
-@pytest.mark.parametrize("fmt,Ks", [(synth.FMT_Q4_MIN, (1, 4, 8)), (synth.FMT_MXFP4, (16,))])
+@pytest.mark.parametrize("fmt,Ks", [(synth.FMT_Q4_MIN, (1, 4, 8)), (synth.FMT_MXFP4, (16,)),
+                                    (synth.FMT_Q4_K, (1, 8))])
 def test_27b_stack_sampled_rows(fmt, Ks):
     """The full 27B-class stack (64 layers, 5120 / 1024 / 17408, vocab 151936) in one pass;
     stages of layers 0, 31, 63 and the lm_head checked on 24 sampled rows each, every
@@ -175,8 +175,7 @@ def test_27b_stack_sampled_rows(fmt, Ks):
         full = _stage_mats(shape, fmt, seed, s)
         pick = np.unique(np.concatenate([rng.integers(0, full.rows, 22), [0, full.rows - 1]]))
         picks[s] = pick
-        mats[s] = synth.Q4Matrix(fmt, len(pick), full.cols, full.qs[pick], full.scales[pick],
-                                 None if full.mins is None else full.mins[pick])
+        mats[s] = full.take(pick)
         del full
     for K in Ks:
         x0 = synth.activations(seed, K, shape.hidden)

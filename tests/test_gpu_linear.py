@@ -1,6 +1,6 @@
 """GPU parity of vq_verify_linear against the fp64 oracle: |gpu - oracle| <= 1e-3 * sum|w x|
 per output, for every format, K = 1..16 and ragged shapes (partial row tiles, partial
-column groups, a single block)."""
+column groups, a single block; for Q4_K, odd numbers of super-blocks)."""
 import numpy as np
 import pytest
 
@@ -50,6 +50,45 @@ def test_shapes_formats_k(fmt, rows, cols):
     say(f"fmt {fmt} {rows}x{cols}: worst |err| / sum|w x| over K = {worst:.3e}")
 
 
+# Q4_K needs cols % 256 == 0: odd numbers of super-blocks (3, 5, 17, 20) instead of
+# partial groups; partial row tiles and tiles split between workgroups as above
+SHAPES_Q4K = [(1000, 768), (77, 256), (64, 2048), (300, 5120), (129, 1280), (16, 512), (5, 4352),
+              (4200, 256), (4136, 1280), (4400, 5120)]
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES_Q4K)
+def test_q4k_shapes_k(rows, cols):
+    fmt = synth.FMT_Q4_K
+    m = synth.weight_matrix(fmt, 11, 1, 2, rows, cols)
+    worst = 0.0
+    for K in (1, 2, 3, 4, 5, 8, 13, 16):
+        x = synth.activations(12, K, cols)
+        y_ref, a_ref = oracle.linear(m, x, threads=8)
+        worst = max(worst, check_rows(_run(m, x), y_ref, a_ref, f"Q4_K {rows}x{cols} K {K}"))
+    say(f"Q4_K {rows}x{cols}: worst |err| / sum|w x| over K = {worst:.3e}")
+
+
+def test_q4k_degenerate_rows_and_extreme_scales():
+    """Rows whose sub-block scales and mins are all 0, or whose super-block D and Dmin are 0,
+    give exactly 0; 6-bit extremes (s = m = 63, bytes up to 255) and a large D stay within
+    the tolerance."""
+    m = synth.weight_matrix(synth.FMT_Q4_K, 5, 0, 0, 192, 1024)
+    m.scales[7] = 0
+    m.mins[7] = 0
+    m.supers[9] = 0
+    m.scales[11] = 63
+    m.mins[11] = 63
+    m.scales[12] = 255
+    m.mins[12] = 255
+    m.supers[13, :, 0] = np.float16(0.5)
+    for K in (1, 4, 8, 16):
+        x = synth.activations(6, K, 1024)
+        y = _run(m, x)
+        assert np.all(y[:, 7] == 0.0) and np.all(y[:, 9] == 0.0), f"K {K}"
+        y_ref, a_ref = oracle.linear(m, x, threads=8)
+        check_rows(y, y_ref, a_ref, f"Q4_K degenerate K {K}")
+
+
 def test_zero_rows_are_exactly_zero_and_f16_output():
     import speculative_decoding_verification_bit_amd as vq
     m = synth.weight_matrix(synth.FMT_Q4_MIN, 5, 0, 0, 192, 512)
@@ -66,7 +105,7 @@ def test_zero_rows_are_exactly_zero_and_f16_output():
         assert np.array_equal(y16, y.astype(np.float16)), f"K {K}: fp16 output is not the rounded fp32 one"
 
 
-@pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4])
+@pytest.mark.parametrize("fmt", [synth.FMT_Q4_MIN, synth.FMT_Q4, synth.FMT_Q4_K])
 def test_large_same_sign_activations(fmt):
     """A block of 32 large activations of one sign (32 x 4096 sums to 131072, beyond fp16):
     the min term and the block sums stay fp32, finite and within the tolerance."""
@@ -118,13 +157,12 @@ def test_full_size_sampled_rows(mid):
     import speculative_decoding_verification_bit_amd as vq
     shape = synth.SHAPE_27B
     rows, cols = shape.mat_shape(mid)
-    for fmt in (synth.FMT_Q4_MIN, synth.FMT_MXFP4):
+    for fmt in (synth.FMT_Q4_MIN, synth.FMT_MXFP4, synth.FMT_Q4_K):
         m = synth.weight_matrix(fmt, 0, 3, mid, rows, cols, threads=16)
         W = vq.DeviceMatrix.from_host(m)
         rng = np.random.default_rng(mid)
         pick = np.unique(np.concatenate([rng.integers(0, rows, 46), [0, rows - 1]]))
-        sub = synth.Q4Matrix(fmt, len(pick), cols, m.qs[pick], m.scales[pick],
-                             None if m.mins is None else m.mins[pick])
+        sub = m.take(pick)
         del m
         for K in (1, 4, 8, 16):
             x = synth.activations(0, K, cols)
