@@ -743,33 +743,70 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             epilogue(own_t, sum);
             if (lane == 0) __hip_atomic_store(pcn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        // several windows: the tiles listed above, in list order
-        for (int j = 0; j < npend; ++j) {
-            const int t = uni(C.pend_t[j]);
-            unsigned expect = 0u;
-            for (int win = 0; win < P.nwin; ++win) {
-                const int gl = win == P.nwin - 1 ? P.glast : P.gw;
-                const int f = win * P.T * P.gw + t * gl;
-                expect += wg_of(P, f) != wg_of(P, f + gl - 1) ? 2u : 1u;
-            }
-            unsigned* cn = A.cnt + t;
-            poll(cn, expect);
-            f4_t sum = zero4;
-            if (lane < plane) {
+        // several windows: the tiles listed above.  Lane j watches tile j's counter, so one
+        // poll round covers them all.
+        if (npend > 0) {
+            int tl = 0;
+            unsigned el = 0u;
+            if (lane < npend) {
+                tl = C.pend_t[lane];
                 for (int win = 0; win < P.nwin; ++win) {
                     const int gl = win == P.nwin - 1 ? P.glast : P.gw;
-                    const int f = win * P.T * P.gw + t * gl;
-                    const int U = win * P.T + t;
-                    const int np = wg_of(P, f) != wg_of(P, f + gl - 1) ? 2 : 1;
-                    for (int side = 0; side < np; ++side) {
-                        const float* ps = A.parts + (size_t)(2 * U + side) * (pbytes >> 2);
+                    const int f = win * P.T * P.gw + tl * gl;
+                    el += wg_of(P, f) != wg_of(P, f + gl - 1) ? 2u : 1u;
+                }
+            }
+            unsigned spins = 0;
+            for (;;) {
+                const unsigned v = lane < npend ? ld_dev_u32(A.cnt + tl) : el;
+                if (__builtin_amdgcn_ballot_w64(v < el) == 0) break;
+                if ((++spins & 15u) == 0u &&
+                    (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
+                     __hip_atomic_load(&C.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)))
+                    break;
+                __builtin_amdgcn_s_sleep(1);
+                if (spins > SPIN_GLOBAL) {
+                    __hip_atomic_store(&C.abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+            }
+        }
+        // Then each tile in list order.  Its parts are read four windows (eight parts) at a
+        // time with every load in flight together: one round trip per four windows, not one
+        // per part (a missing part is zero, which leaves the sum's bits as they are).
+        constexpr int PW = 4;
+        auto issue_parts = [&](int t, int w0, f4_t (&v)[2 * PW]) __attribute__((always_inline)) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) sum[i] += ld_dev_f32(ps + 4 * lane + i);
+            for (int k = 0; k < 2 * PW; ++k) {
+                v[k] = zero4;
+                const int win = w0 + (k >> 1), side = k & 1;
+                if (win < P.nwin && lane < plane) {
+                    const int gl = win == P.nwin - 1 ? P.glast : P.gw;
+                    const int f = win * P.T * P.gw + t * gl;
+                    const int np = wg_of(P, f) != wg_of(P, f + gl - 1) ? 2 : 1;
+                    if (side < np) {
+                        const float* ps = A.parts + (size_t)(2 * (win * P.T + t) + side) * (pbytes >> 2);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[k][i] = ld_dev_f32(ps + 4 * lane + i);
                     }
                 }
             }
+        };
+        auto add_parts = [&](f4_t& sum, const f4_t (&v)[2 * PW]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int k = 0; k < 2 * PW; ++k) sum += v[k];
+        };
+        for (int j = 0; j < npend; ++j) {
+            const int t = uni(C.pend_t[j]);
+            f4_t sum = zero4;
+            for (int w0 = 0; w0 < P.nwin; w0 += PW) {
+                f4_t v[2 * PW];
+                issue_parts(t, w0, v);
+                add_parts(sum, v);
+            }
             epilogue(t, sum);
-            if (lane == 0) __hip_atomic_store(cn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (lane == 0) __hip_atomic_store(A.cnt + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 
         // -------- report the stage: sums of squares, then the completion counter
