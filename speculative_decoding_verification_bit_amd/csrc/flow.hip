@@ -778,17 +778,23 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
         constexpr int PW = 4;
         auto issue_parts = [&](int t, int w0, f4_t (&v)[2 * PW]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int k = 0; k < 2 * PW; ++k) {
-                v[k] = zero4;
-                const int win = w0 + (k >> 1), side = k & 1;
+            for (int k = 0; k < PW; ++k) {
+                v[2 * k] = zero4;
+                v[2 * k + 1] = zero4;
+                const int win = w0 + k;
                 if (win < P.nwin && lane < plane) {
                     const int gl = win == P.nwin - 1 ? P.glast : P.gw;
                     const int f = win * P.T * P.gw + t * gl;
-                    const int np = wg_of(P, f) != wg_of(P, f + gl - 1) ? 2 : 1;
-                    if (side < np) {
-                        const float* ps = A.parts + (size_t)(2 * (win * P.T + t) + side) * (pbytes >> 2);
+                    // the unit has a second part when it runs past the end of the range of
+                    // the workgroup holding its first chunk (one division, not two)
+                    const int i0 = wg_of(P, f);
+                    const int end = (i0 + 1) * P.q + min(i0 + 1, P.r);
+                    const float* ps = A.parts + (size_t)(2 * (win * P.T + t)) * (pbytes >> 2);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) v[k][i] = ld_dev_f32(ps + 4 * lane + i);
+                    for (int i = 0; i < 4; ++i) v[2 * k][i] = ld_dev_f32(ps + 4 * lane + i);
+                    if (f + gl - 1 >= end) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[2 * k + 1][i] = ld_dev_f32(ps + (pbytes >> 2) + 4 * lane + i);
                     }
                 }
             }
