@@ -414,7 +414,7 @@ int get_steps(const StepKey& key, const KindPlan kp[6], const std::vector<std::p
     std::vector<size_t> hdr;
     for (const auto& l : launches) {
         hdr.push_back(T.start.size());
-        if (!build_steps(T, kp, l.first, l.second, L, linear, nwg, xoff1))
+        if (!build_steps(T, kp, l.first, l.second, L, linear, nwg, xoff1, key.K <= 8))
             return fail(VQ_ERR_UNSUPPORTED, "work lists of stages %d..%d do not fit their encoding", l.first,
                         l.second - 1);
     }
@@ -680,7 +680,7 @@ int vq_verify_linear_noalloc(const vq_tiled* W, const void* x_f16, int32_t K, vo
         const size_t soff = (nstart + 7) / 8 * 8;
         if (soff >= words) return fail(VQ_ERR_UNSUPPORTED, "vq_verify_linear_noalloc: grid too large");
         FixedStepTable T{g_na_host + soff, words - soff, 0, g_na_host, nstart, 0, false};
-        if (!build_steps(T, kp, 0, 1, 0, true, L.kp.nwe, (L.xcap / 2) & ~15))
+        if (!build_steps(T, kp, 0, 1, 0, true, L.kp.nwe, (L.xcap / 2) & ~15, K <= 8))
             return fail(VQ_ERR_UNSUPPORTED,
                         "vq_verify_linear_noalloc: the work lists of a %dx%d matrix exceed its %zu bytes; use "
                         "vq_verify_linear", W->rows, W->cols, NA_TABLE_BYTES);

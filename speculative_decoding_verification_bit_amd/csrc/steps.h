@@ -118,6 +118,42 @@ inline int unit_pos(const Seq& q, int U) {
 
 }  // namespace steps
 
+// How a stage's steps are dealt to the compute waves: step k goes to wave deal()[k % n].
+// Dealt in equal shares, the waves of a SIMD do not finish together: wave i sits on SIMD
+// i % 4 (the conductor on SIMD 3), the SIMD issues for its older waves first, and at K <= 8
+// the last wave of each SIMD finished its steps ~45% later than the first, alone on its
+// SIMD by then.  The weighted deal gives wave i kWaveWeight[i] steps of every 91, the
+// weights following those measured rates, each step to the wave whose share would then be
+// least ahead (ties to the lower wave), so that the steps of a wave are spread evenly.
+constexpr int kWaveWeight[FLOW_NCW] = {10, 10, 10, 9, 8, 8, 8, 7, 7, 7, 7};
+struct Deal {
+    uint8_t wave[128];
+    int n;
+};
+inline Deal make_deal(bool weighted) {
+    Deal d{};
+    int wsum = 0;
+    for (int i = 0; i < FLOW_NCW; ++i) wsum += weighted ? kWaveWeight[i] : 1;
+    int cnt[FLOW_NCW] = {};
+    d.n = wsum;
+    for (int k = 0; k < wsum; ++k) {
+        int best = 0;
+        for (int i = 1; i < FLOW_NCW; ++i) {
+            // (cnt + 1) / weight, compared exactly
+            const long wi = weighted ? kWaveWeight[i] : 1, wb = weighted ? kWaveWeight[best] : 1;
+            if ((long)(cnt[i] + 1) * wb < (long)(cnt[best] + 1) * wi) best = i;
+        }
+        d.wave[k] = (uint8_t)best;
+        ++cnt[best];
+    }
+    return d;
+}
+inline const Deal& deal(bool weighted) {
+    static const Deal w = make_deal(true), e = make_deal(false);
+    return weighted ? w : e;
+}
+static_assert(10 + 10 + 10 + 9 + 8 + 8 + 8 + 7 + 7 + 7 + 7 <= 128, "the pattern fits");
+
 // The kind of launch stage s (the pass: 4 per layer, then the lm_head; or one linear map).
 inline int stage_kind(int s, int L, bool linear) {
     if (linear) return SK_LIN;
@@ -128,9 +164,11 @@ inline int stage_kind(int s, int L, bool linear) {
 // Appends the work lists of one launch (stages [s_begin, s_end), grid nwg) to T.  Returns
 // false if an entry would not fit its fields or an address would leave its matrix.
 template <class Table>
-bool build_steps(Table& T, const KindPlan kp[6], int s_begin, int s_end, int L, bool linear, int nwg, int xoff1) {
+bool build_steps(Table& T, const KindPlan kp[6], int s_begin, int s_end, int L, bool linear, int nwg, int xoff1,
+                 bool weighted) {
     using namespace steps;
     if (s_end - s_begin > 127 || s_end <= s_begin || xoff1 % 16) return false;
+    const Deal& dl = deal(weighted);
     Seq seqs[127];
     for (int w = 0; w < nwg; ++w) {
         for (int s = s_begin; s < s_end; ++s)
@@ -166,7 +204,9 @@ bool build_steps(Table& T, const KindPlan kp[6], int s_begin, int s_end, int L, 
                 if (q.n == 0) continue;
                 const long mat_bytes = (long)P.T * P.G * P.cb;
                 int closed = 0;
-                for (int k = cw; k < q.n; k += FLOW_NCW) {
+                bool first = true;
+                for (int k = 0; k < q.n; ++k) {
+                    if (dl.wave[k % dl.n] != cw) continue;
                     const long c = seq_step(q, k);
                     const Pos p = locate(P, c);
                     const int up = unit_pos(q, p.w * P.T + p.t);
@@ -178,8 +218,9 @@ bool build_steps(Table& T, const KindPlan kp[6], int s_begin, int s_end, int L, 
                     if (off < 0 || off + P.cb > mat_bytes || off > 0xffffffffL) return false;
                     if (p.w - q.wlo < 0 || p.w - q.wlo > 1 || xoff % 16 || (xoff >> 4) > (long)ST_XOFF_MASK) return false;
                     if ((long)p.i * 512 + 512 > (long)P.gw * 512) return false;
-                    emit((uint32_t)off, (uint32_t)(xoff >> 4) | (k == cw ? ST_OPEN : 0u) | ST_VALID |
+                    emit((uint32_t)off, (uint32_t)(xoff >> 4) | (first ? ST_OPEN : 0u) | ST_VALID |
                                             ((uint32_t)(s - s_begin) << ST_STAGE_SHIFT));
+                    first = false;
                 }
                 pending += (uint32_t)(q.nU - closed);
             }
