@@ -152,13 +152,13 @@ bool make_plan(KindPlan& P, int fmt, int K, int rows, int cols, int tiles, int n
     P.r = (int)(N % P.nwe);
     // Whole tiles per workgroup when that costs little: no tile is then split over two
     // workgroups, which saves the exchange of partial sums at the end of the stage.  Taken
-    // when k = ceil(T / nwg) tiles per workgroup divide T, and the largest range is within
-    // 25% of the balanced one or the stage is small (its chunks are already in flight when
-    // it starts, so its time is the reduction's, not the stream's).
+    // when k = ceil(T / nwg) tiles per workgroup divide T and the largest range is within
+    // 25% of the balanced one (the 27B stack's q|k|v: 2 tiles against 1.75).  A stage whose
+    // chunks are all in flight when it starts (the o projection: 1.25 tiles per workgroup)
+    // still ends when its busiest workgroup is done, so it is split evenly too.
     if (P.nwin == 1) {
         const long k = (P.T + nwg - 1) / nwg;
-        const bool small = (long)P.T * P.G * P.cb <= (32L << 20);
-        if (P.T % k == 0 && (4 * k * nwg <= 5L * P.T || small)) {
+        if (P.T % k == 0 && 4 * k * nwg <= 5L * P.T) {
             P.nwe = (int)(P.T / k);
             P.q = (int)(k * P.G);
             P.r = 0;
