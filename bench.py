@@ -364,7 +364,9 @@ def bench_ngram(vq, synth, t_pass=None, n_tokens=100000, max_drafts=8):
 def bench_attention(torch, vq, synth, dev, args):
     """The window's attention over one layer's q8_0 / q4_0 cache of the 27B model at 32768
     positions (40 query heads, 8 kv heads, head dim 128), K = 1, 4, 8, 16: time per call
-    (both kernels) on the launch stream, and the cache bytes over that time."""
+    (both kernels) from a captured graph of 10 calls replayed, as the pass is (the eager
+    time, which adds the binding's per-call cost and launch gaps, beside it), and the cache
+    bytes over that time."""
     c = synth.ATTN
     Hkv, Hq, L = c["n_kv_heads"], c["n_q_heads"], c["length"]
     kc, ks = synth.kv_cache(c["kfmt"], c["seed"], 0, 0, Hkv, L, threads=args.threads)
@@ -386,11 +388,28 @@ def bench_attention(torch, vq, synth, dev, args):
             vq.verify_attention(C, q, out=o, ws=ws)
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / n
+        us_eager = e0.elapsed_time(e1) * 1e3 / n
+        per_graph = 10
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                vq.verify_attention(C, q, out=o, ws=ws)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(5, n // per_graph)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
+        del g
         algo = cache + q.numel() * 2 + o.numel() * 4
         res["per_K"][f"K{K}"] = {"us_per_call": round(us, 2), "gbps": round(algo / us / 1e3, 1),
                                  "frac_of_hbm_peak": round(algo / us / 1e3 / HBM_PEAK_GBPS, 4),
-                                 "us_per_pass_64_layers": round(64 * us, 1)}
+                                 "us_per_pass_64_layers": round(64 * us, 1),
+                                 "us_per_call_eager": round(us_eager, 2)}
     return res
 
 
