@@ -122,10 +122,12 @@ inline int unit_pos(const Seq& q, int U) {
 // Dealt in equal shares, the waves of a SIMD do not finish together: wave i sits on SIMD
 // i % 4 (the conductor on SIMD 3), the SIMD issues for its older waves first, and at K <= 8
 // the last wave of each SIMD finished its steps ~45% later than the first, alone on its
-// SIMD by then.  The weighted deal gives wave i kWaveWeight[i] steps of every 91, the
-// weights following those measured rates, each step to the wave whose share would then be
-// least ahead (ties to the lower wave), so that the steps of a wave are spread evenly.
-constexpr int kWaveWeight[FLOW_NCW] = {10, 10, 10, 9, 8, 8, 8, 7, 7, 7, 7};
+// SIMD by then.  The weighted deal gives wave i kWaveWeight[i] steps of every 86, each step
+// to the wave whose share would then be least ahead (ties to the lower wave), so that the
+// steps of a wave are spread evenly.  The weights were chosen by timing the 27B pass at
+// K = 1 and 8 over several tables: the youngest waves (8..10) do best with clearly less than
+// their rate share (they also start each stage late), waves 4..7 with about an equal one.
+constexpr int kWaveWeight[FLOW_NCW] = {10, 10, 10, 9, 9, 9, 9, 8, 6, 6, 6};
 struct Deal {
     uint8_t wave[128];
     int n;
@@ -152,7 +154,7 @@ inline const Deal& deal(bool weighted) {
     static const Deal w = make_deal(true), e = make_deal(false);
     return weighted ? w : e;
 }
-static_assert(10 + 10 + 10 + 9 + 8 + 8 + 8 + 7 + 7 + 7 + 7 <= 128, "the pattern fits");
+static_assert(10 + 10 + 10 + 9 + 9 + 9 + 9 + 8 + 6 + 6 + 6 <= 128, "the pattern fits");
 
 // The kind of launch stage s (the pass: 4 per layer, then the lm_head; or one linear map).
 inline int stage_kind(int s, int L, bool linear) {
