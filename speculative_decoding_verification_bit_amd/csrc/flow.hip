@@ -483,10 +483,10 @@ __global__ void __launch_bounds__(NTHR, 1) k_flow(const FlowArgs args) {
             const unsigned* dn = A.done + (size_t)(s - 1) * DONE_WORDS + lane * DONE_STRIDE;
             unsigned spins = 0;
             for (;;) {
+                static_assert(DONE_REPL <= 64, "one counter per lane");
                 const unsigned v = lane < DONE_REPL ? ld_dev_u32(dn) : 0u;
-                unsigned sum = 0;
-#pragma unroll
-                for (int r = 0; r < DONE_REPL; ++r) sum += __builtin_amdgcn_readlane(v, r);
+                // a count of workgroups (<= 1024): exact as a float sum
+                const unsigned sum = (unsigned)wave_sum((float)v);
                 if (sum >= (unsigned)A.nwg) break;
                 if ((++spins & 15u) == 0u) {
                     if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
